@@ -1,0 +1,303 @@
+"""Plain fp64 CPU oracle of the two-tier sparse attention of a DeepSeek-V4.1 Flash layer.
+
+TEST INFRASTRUCTURE ONLY. It is imported by tests/, __graft_entry__.smoke() and
+bench.py's cpu_baseline leg, never by the library. It shares no code with the
+HIP path: it decodes bf16 and e4m3 from their definitions, and every step below
+is the definition written out in NumPy float64, one query at a time, with no
+blocking or fusion.
+
+Sources (the pages):
+  [P2] "DeepSeek-V4.1 Flash" (Miles docs), section 1 Model Introduction: one
+       512-wide latent per position used as both key and value by all 64 query
+       heads with no value projection; compressed latents collapse 2 positions
+       into 1 (ratio 2) or 1-to-1 (ratio 1); a 128-position sliding window;
+       each retrieving layer picks a top-512 set.
+  [P3] "deepseek-ai/DeepSeek-V4.1-Flash" (vLLM recipe, MI355X), Overview, the
+       "Two-tier sparse attention" bullet: every layer attends a 128-token
+       window; compressing layers add latents pooled by a learned softmax gate;
+       an indexer scores those latents and keeps the best 512 per query after
+       a candidate stage that selects 2048 blocks of 8.
+  [OCP] OCP 8-bit Floating Point Specification (OFP8), E4M3 encoding.
+
+Readings where the pages are silent (each is also a stated definition):
+  - indexer: 16 heads x 128 dims on the query side, one 128-d key per
+    compressed position, score I(j) = sum_h w_h * max(0, <qI_h, k_j>), no
+    extra scale; fp8 keys are k_j = s_j * code_j with one fp32 scale per row;
+  - visibility: compressed j covers raw positions r*j .. r*j+r-1 and is visible
+    to a query at raw position p iff r*j + r - 1 <= p, so n = (p+1) // r;
+  - window: raw positions max(0, p-127) .. p, the query's own included;
+  - block score: max of the block's visible scores; blocks are 8 consecutive
+    compressed positions;
+  - ties: one total order (score descending, position ascending) at both
+    selection stages; fewer than 512 visible -> all are taken;
+  - attention: one softmax over [selected latents ++ window rows] with scale
+    1/sqrt(512); output o and natural-log lse per head;
+  - compressor: per channel, softmax over the r slots of (gate logit + slot
+    bias), then the weighted sum of the slot latents; ratio 1 is the identity;
+    the result is stored as bf16 (round to nearest even).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import numpy as np
+
+HEADS = 64
+DIM = 512
+WINDOW = 128
+TOPK = 512
+IDX_HEADS = 16
+IDX_DIM = 128
+BLOCK = 8
+CAND_BLOCKS = 2048
+SCALE = 1.0 / math.sqrt(512.0)
+
+
+# ---------------------------------------------------------------------------
+# Number formats
+# ---------------------------------------------------------------------------
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float64. A bf16 value is the upper 16 bits of
+    an IEEE binary32, so widening is exact."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 to the nearest bfloat16 (ties to even), returned as bit patterns.
+
+    Done from the definition: bf16 has 8 significant bits and the binary32
+    exponent range; values are rounded on the float64 value directly.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros(x.shape, dtype=np.uint16)
+    flat = x.reshape(-1)
+    o = out.reshape(-1)
+    for i, v in enumerate(flat):
+        o[i] = _bf16_bits_of(float(v))
+    return out
+
+
+def _bf16_bits_of(v: float) -> int:
+    if math.isnan(v):
+        return 0x7FC0
+    sign = 0x8000 if (v < 0 or (v == 0 and math.copysign(1.0, v) < 0)) else 0
+    a = abs(v)
+    if a == 0.0:
+        return sign
+    if math.isinf(a):
+        return sign | 0x7F80
+    m, e = math.frexp(a)            # a = m * 2^e, m in [0.5, 1)
+    E = e - 1                       # a in [2^E, 2^(E+1))
+    if E < -126:                    # subnormal: quantum 2^-133
+        q = round(a * 2.0 ** 133)   # Python round: ties to even
+        return sign | q             # q == 128 lands exactly on the smallest normal
+    q = round(a * 2.0 ** (7 - E))   # 8 significant bits: q in [128, 256]
+    if q == 256:
+        q = 128
+        E += 1
+    if E > 127:
+        return sign | 0x7F80
+    return sign | ((E + 127) << 7) | (q - 128)
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one OCP E4M3 code [OCP]: sign, 4 exponent bits (bias 7), 3 mantissa
+    bits; exponent field 0 is subnormal; S.1111.111 is NaN; no infinities."""
+    s = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return s * (m / 8.0) * 2.0 ** -6
+    return s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def index_keys_f64(KI: np.ndarray, KS: Optional[np.ndarray]) -> np.ndarray:
+    """Exact index keys: bf16 keys as stored, or e4m3 code * fp32 row scale."""
+    if KS is None:
+        return bf16_to_f64(KI)
+    return e4m3_to_f64(KI) * np.asarray(KS, dtype=np.float64)[..., None]
+
+
+# ---------------------------------------------------------------------------
+# Stages
+# ---------------------------------------------------------------------------
+
+def visible_count(p: int, r: int) -> int:
+    """Compressed positions visible to a query at raw position p ([P2] 2->1 or 1->1)."""
+    return (int(p) + 1) // int(r)
+
+
+def window_positions(p: int, W: int = WINDOW) -> np.ndarray:
+    """Raw positions of the sliding window of a query at p ([P2], [P3]: 128 positions)."""
+    return np.arange(max(0, int(p) - W + 1), int(p) + 1, dtype=np.int64)
+
+
+def compress(x: np.ndarray, z: np.ndarray, beta: np.ndarray) -> np.ndarray:
+    """Softmax-gate pooling of groups of r raw latents ([P3] "pooled by a learned softmax gate").
+
+    x, z: [G, r, D] raw latents and gate logits; beta: [r, D] slot bias.
+    For each group and channel: pi = softmax over slots of (z + beta); out = sum_slot pi * x.
+    """
+    x = np.asarray(x, np.float64)
+    a = np.asarray(z, np.float64) + np.asarray(beta, np.float64)[None]
+    a = a - a.max(axis=1, keepdims=True)
+    e = np.exp(a)
+    pi = e / e.sum(axis=1, keepdims=True)
+    return (pi * x).sum(axis=1)
+
+
+def index_scores(qI: np.ndarray, w: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """Indexer scores of one query against keys [n, 128]:
+    I(j) = sum_h w_h * max(0, <qI_h, k_j>)   ([P3] the indexer scores the latents)."""
+    dots = keys @ np.asarray(qI, np.float64).T            # [n, 16]
+    return np.maximum(dots, 0.0) @ np.asarray(w, np.float64)
+
+
+def block_scores(I: np.ndarray, blk: int = BLOCK) -> np.ndarray:
+    """Score of each block of `blk` consecutive positions: the max of its visible scores."""
+    n = I.shape[0]
+    nb = -(-n // blk)
+    M = np.full(nb, -np.inf)
+    for b in range(nb):
+        M[b] = I[b * blk:min(n, b * blk + blk)].max()
+    return M
+
+
+def order_desc(values: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """Permutation sorting by value descending, then id ascending."""
+    return np.lexsort((ids, -values))
+
+
+def candidate_blocks(M: np.ndarray, cb: int = CAND_BLOCKS) -> np.ndarray:
+    """Candidate stage ([P3] "a candidate stage that selects 2048 blocks of 8"):
+    the first min(cb, nb) blocks in the order (block score desc, block id asc), ascending."""
+    ids = np.arange(M.shape[0], dtype=np.int64)
+    keep = ids[order_desc(M, ids)[:min(cb, M.shape[0])]]
+    return np.sort(keep)
+
+
+def topk_of(I: np.ndarray, positions: np.ndarray, k: int = TOPK) -> np.ndarray:
+    """The first min(k, len) of `positions` in the order (I desc, position asc), ascending."""
+    positions = np.asarray(positions, np.int64)
+    sel = positions[order_desc(I[positions], positions)[:min(k, positions.shape[0])]]
+    return np.sort(sel)
+
+
+def select(I: np.ndarray, k: int = TOPK, cb: int = CAND_BLOCKS, blk: int = BLOCK):
+    """Two-stage selection over the n visible scores I: candidate blocks, then top-k
+    inside them ([P3] "keeps the best 512 per query, pre-filtered by a candidate stage").
+    Returns (candidate block ids ascending, selected positions ascending)."""
+    n = I.shape[0]
+    if n == 0:
+        return np.zeros(0, np.int64), np.zeros(0, np.int64)
+    cand = candidate_blocks(block_scores(I, blk), cb)
+    pos = (cand[:, None] * blk + np.arange(blk)[None, :]).reshape(-1)
+    pos = pos[pos < n]
+    return cand, topk_of(I, pos, k)
+
+
+def attend(q: np.ndarray, X: np.ndarray, scale: float = SCALE) -> Tuple[np.ndarray, np.ndarray]:
+    """One softmax over the rows of X for every head of q; X is both key and value ([P2]).
+
+    q: [H, D], X: [m, D] -> o [H, D], lse [H] (natural log).
+    """
+    s = scale * (np.asarray(q, np.float64) @ np.asarray(X, np.float64).T)  # [H, m]
+    mu = s.max(axis=1, keepdims=True)
+    e = np.exp(s - mu)
+    Z = e.sum(axis=1, keepdims=True)
+    P = e / Z
+    return P @ X, (mu + np.log(Z))[:, 0]
+
+
+# ---------------------------------------------------------------------------
+# Whole path for one batch
+# ---------------------------------------------------------------------------
+
+class Result:
+    def __init__(self, T: int):
+        self.scores = [None] * T      # fp64 scores of the visible positions
+        self.cand = [None] * T        # candidate blocks, ascending
+        self.idx = [None] * T         # selected positions, ascending
+        self.o = np.zeros((T, HEADS, DIM))
+        self.lse = np.zeros((T, HEADS))
+        self.C_new = {}               # sequence -> fp64 compressed latent written this step
+
+
+def compressed_store(wl, b: int, n: int, C_new_bits: Optional[np.ndarray] = None) -> np.ndarray:
+    """fp64 compressed store rows 0..n-1 of sequence b; the row written this step
+    (if any) replaces row n-1."""
+    C = bf16_to_f64(wl.C[b, :n])
+    if C_new_bits is not None and n > 0:
+        C[n - 1] = bf16_to_f64(C_new_bits)
+    return C
+
+
+def step_compress(wl) -> dict:
+    """Compressor for the group completed by each sequence's query (ratio 2 decode).
+
+    Returns sequence -> (fp64 value, bf16 bits as stored)."""
+    out = {}
+    for b in wl.compress_groups():
+        v = compress(bf16_to_f64(wl.Xp[b])[None], bf16_to_f64(wl.Zp[b])[None], wl.beta)[0]
+        out[int(b)] = (v, f64_to_bf16(v))
+    return out
+
+
+def run_query(wl, t: int, keys_f64: Optional[np.ndarray] = None, C_new: Optional[dict] = None,
+              idx_override: Optional[np.ndarray] = None):
+    """The whole path for query t of workload `wl` (see workloads.Workload).
+
+    Returns (scores [n], cand, idx, o [64,512], lse [64]). `idx_override` feeds a
+    given selection into the attention stage instead of the oracle's own.
+    """
+    b = int(wl.seq[t])
+    p = int(wl.pos[t])
+    n = visible_count(p, wl.ratio)
+    if keys_f64 is None:
+        keys_f64 = index_keys_f64(wl.KI[b, :n], None if wl.KS is None else wl.KS[b, :n])
+    I = index_scores(bf16_to_f64(wl.qI[t]), wl.w[t], keys_f64[:n])
+    cand, idx = select(I)
+    use = idx if idx_override is None else np.asarray(idx_override, np.int64)
+    new_bits = None
+    if C_new is not None and b in C_new and n > 0:
+        new_bits = C_new[b][1]
+    rows = compressed_store(wl, b, n, new_bits)[use] if use.size else np.zeros((0, DIM))
+    win = window_positions(p)
+    Xw = bf16_to_f64(wl.R[b, win % wl.wcap])
+    X = np.concatenate([rows, Xw], axis=0)
+    o, lse = attend(bf16_to_f64(wl.q[t]), X)
+    return I, cand, idx, o, lse
+
+
+def run(wl, queries=None, idx_override=None) -> Result:
+    """Oracle over the queries `queries` (default all) of a workload, compressor first."""
+    T = wl.T
+    queries = range(T) if queries is None else list(queries)
+    res = Result(T)
+    C_new = step_compress(wl)
+    res.C_new = C_new
+    key_cache = {}
+    for t in queries:
+        b = int(wl.seq[t])
+        if b not in key_cache:
+            nmax = int(max(visible_count(int(wl.pos[u]), wl.ratio)
+                           for u in range(T) if int(wl.seq[u]) == b))
+            key_cache = {b: index_keys_f64(wl.KI[b, :nmax],
+                                           None if wl.KS is None else wl.KS[b, :nmax])}
+        ov = None if idx_override is None else idx_override[t]
+        I, cand, idx, o, lse = run_query(wl, t, key_cache[b], C_new, ov)
+        res.scores[t], res.cand[t], res.idx[t] = I, cand, idx
+        res.o[t], res.lse[t] = o, lse
+    return res

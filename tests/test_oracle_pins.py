@@ -1,0 +1,430 @@
+"""Pins of the fp64 oracle to things other than itself.
+
+Each test ties one oracle function to a hand-derived worked example
+(tests/golden), a library routine on a special case, a closed form, an
+invariant, or the independent pure-Python brute force on tiny inputs. The set
+is chosen so that a dropped term, wrong sign, wrong index or transposed
+operand in any stage fails at least one test.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import brute
+from oracle import oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- formats
+
+def test_e4m3_anchors_from_spec():
+    g = _gold("e4m3_anchors.json")
+    for code, val in g["anchors"]:
+        v = O.e4m3_value(int(code, 16))
+        assert v == val and math.copysign(1, v) == math.copysign(1, val), code
+    for code in g["nan_codes"]:
+        assert math.isnan(O.e4m3_value(int(code, 16)))
+
+
+def test_e4m3_table_matches_torch_float8():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = O.E4M3_TABLE
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(ours))
+    assert np.array_equal(ref[~nan], ours[~nan])
+
+
+def test_e4m3_structure():
+    t = O.E4M3_TABLE
+    pos = t[0x00:0x7F]
+    assert np.all(np.diff(pos) > 0)                          # strictly increasing
+    assert np.array_equal(t[0x80:0xFF], -t[0x00:0x7F])       # sign symmetry
+    finite = t[~np.isnan(t)]
+    assert np.array_equal(finite.astype(np.float32).astype(np.float64), finite)
+    assert len(np.unique(finite)) == 253                     # +-0 coincide, 2 NaNs
+
+
+def test_bf16_matches_torch():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 10 ** rng.uniform(-30, 30, 20000).astype(np.float32),
+                        np.array([0.0, -0.0, 1.0, -1.0, 3.3895314e38, 1e-40, -1e-41], np.float32)])
+    x = x[np.isfinite(x)]
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ours = O.f64_to_bf16(x.astype(np.float64))
+    assert np.array_equal(ref, ours)
+    back = torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(back, O.bf16_to_f64(ref))
+
+
+def test_bf16_ties_to_even():
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: ties to the even mantissa (1.0)
+    assert O.f64_to_bf16(np.array([1.0 + 2 ** -8]))[0] == 0x3F80
+    # 1 + 3*2^-8 is halfway between 1+2^-7 (odd) and 1+2^-6 (even)
+    assert O.f64_to_bf16(np.array([1.0 + 3 * 2 ** -8]))[0] == 0x3F82
+
+
+# ---------------------------------------------------------------- visibility, window
+
+def test_visibility_and_window_counts():
+    g = _gold("layer_shapes.json")
+    for c in g["derived"]["cases"]:
+        p = c["N"] - 1
+        n = O.visible_count(p, c["r"])
+        assert n == c["n"], c
+        assert -(-n // g["block"]) == c["blocks"], c
+        assert len(O.window_positions(p, g["window"])) == c["window_rows"], c
+    assert (O.HEADS, O.DIM, O.WINDOW, O.TOPK, O.CAND_BLOCKS, O.BLOCK) == (
+        g["heads"], g["latent_dim"], g["window"], g["topk"], g["cand_blocks"], g["block"])
+
+
+def test_window_edges():
+    w = O.window_positions(1000)
+    assert w[0] == 1000 - 127 and w[-1] == 1000 and 1000 - 128 not in w
+
+
+def test_ratio2_group_visibility():
+    # group j covers raw positions 2j, 2j+1; visible only once both are <= p
+    assert O.visible_count(0, 2) == 0
+    assert O.visible_count(1, 2) == 1
+    assert O.visible_count(2, 2) == 1
+    assert O.visible_count(3, 2) == 2
+    # ratio 1 includes the diagonal
+    assert O.visible_count(0, 1) == 1
+
+
+# ---------------------------------------------------------------- indexer
+
+def _worked_keys(g):
+    n = len(g["a"])
+    keys = np.zeros((n, 128))
+    keys[:, 0] = g["a"]
+    keys[:, 1] = g["b"]
+    qI = np.zeros((16, 128))
+    qI[0, 0] = 1.0
+    qI[1, 1] = -1.0
+    w = np.zeros(16)
+    w[:2] = g["w01"]
+    return qI, w, keys
+
+
+def test_worked_indexer_and_selection():
+    g = _gold("worked_tiny.json")["indexer_select"]
+    qI, w, keys = _worked_keys(g)
+    I = O.index_scores(qI, w, keys)
+    assert np.array_equal(I, np.array(g["scores"], float))
+    assert np.array_equal(O.block_scores(I), np.array(g["block_max"], float))
+    cand, idx = O.select(I, k=g["k"], cb=2)
+    assert cand.tolist() == g["cb2"]["cand"] and idx.tolist() == g["cb2"]["idx"]
+    cand, idx = O.select(I, k=g["k"], cb=3)
+    assert cand.tolist() == g["cb3"]["cand"] and idx.tolist() == g["cb3"]["idx"]
+    cand, idx = O.select(I)
+    assert idx.tolist() == list(range(20))
+
+
+def test_indexer_brute_force_tiny():
+    rng = np.random.default_rng(7)
+    for n in (1, 7, 8, 9, 23, 40):
+        qI = rng.standard_normal((16, 128))
+        w = rng.uniform(0, 1, 16)
+        keys = rng.standard_normal((n, 128))
+        ref = brute.scores(qI.tolist(), w.tolist(), keys.tolist())
+        got = O.index_scores(qI, w, keys)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_indexer_one_hot_and_relu():
+    qI = np.zeros((16, 128))
+    w = np.zeros(16)
+    qI[5, 17] = 2.0
+    w[5] = 0.25
+    keys = np.zeros((3, 128))
+    keys[0, 17] = 3.0     # positive dot: 0.25 * 6
+    keys[1, 17] = -3.0    # negative dot clipped to 0
+    keys[2, 18] = 9.0     # orthogonal
+    assert O.index_scores(qI, w, keys).tolist() == [1.5, 0.0, 0.0]
+
+
+def test_indexer_head_weights_not_transposed():
+    # head h uses weight w[h] and query row h: distinct values catch a swap
+    qI = np.zeros((16, 128))
+    for h in range(16):
+        qI[h, h] = h + 1.0
+    w = np.arange(16) / 16.0
+    keys = np.eye(128)[:16]
+    I = O.index_scores(qI, w, keys)
+    assert np.allclose(I, (np.arange(16) + 1.0) * np.arange(16) / 16.0, rtol=0, atol=0)
+
+
+def test_indexer_scale_homogeneity_and_zero_weights():
+    rng = np.random.default_rng(3)
+    qI = rng.standard_normal((16, 128))
+    w = rng.uniform(0, 1, 16)
+    codes = rng.integers(0, 0x7E, (50, 128)).astype(np.uint8)
+    s = np.float32(0.0078125)        # a power of two keeps the product exact
+    k1 = O.index_keys_f64(codes, np.full(50, s, np.float32))
+    k0 = O.index_keys_f64(codes, np.ones(50, np.float32))
+    assert np.array_equal(O.index_scores(qI, w, k1), float(s) * O.index_scores(qI, w, k0))
+    assert np.all(O.index_scores(qI, np.zeros(16), k1) == 0.0)
+
+
+# ---------------------------------------------------------------- selection
+
+def _lemma_case(I, k, cb, blk):
+    cand, idx = O.select(I, k=k, cb=cb, blk=blk)
+    direct = O.topk_of(I, np.arange(I.shape[0]), k)
+    assert np.array_equal(idx, direct)
+    return cand, idx
+
+
+def test_two_stage_equals_global_topk_random_and_ties():
+    rng = np.random.default_rng(11)
+    for trial in range(30):
+        n = int(rng.integers(1, 3000))
+        blk = int(rng.choice([1, 2, 4, 8]))
+        k = int(rng.integers(1, 200))
+        cb = int(rng.integers(k, k + 50))       # cb >= k: lossless
+        if trial % 2:
+            I = rng.integers(0, 6, n).astype(float)     # many ties
+        else:
+            I = rng.standard_normal(n)
+        _lemma_case(I, k, cb, blk)
+
+
+def test_two_stage_production_sizes():
+    rng = np.random.default_rng(12)
+    n = 40000                                  # 5000 blocks > 2048: the stage prunes
+    I = rng.standard_normal(n)
+    cand, idx = _lemma_case(I, O.TOPK, O.CAND_BLOCKS, O.BLOCK)
+    assert cand.shape[0] == O.CAND_BLOCKS and idx.shape[0] == O.TOPK
+    assert np.all(np.diff(idx) > 0) and np.all(np.diff(cand) > 0)
+
+
+def test_selection_brute_force_tiny():
+    rng = np.random.default_rng(5)
+    for n in (1, 5, 8, 17, 40):
+        I = rng.integers(0, 4, n).astype(float)
+        for k, cb in ((3, 1), (3, 2), (5, 8), (40, 40)):
+            kept_b, idx_b = brute.select(I.tolist(), k=k, cb=cb, blk=8)
+            cand, idx = O.select(I, k=k, cb=cb, blk=8)
+            assert cand.tolist() == kept_b and idx.tolist() == idx_b
+
+
+def test_selection_all_ties_takes_lowest_positions():
+    for n in (100, 511, 512, 513, 20000):
+        cand, idx = O.select(np.zeros(n))
+        assert idx.tolist() == list(range(min(512, n)))
+
+
+def test_selection_monotone_takes_last_positions_with_partial_block():
+    n = 20003                                   # last block holds 3 positions
+    cand, idx = O.select(np.arange(n, dtype=float))
+    assert idx.tolist() == list(range(n - 512, n))
+    nb = -(-n // 8)
+    assert cand.tolist() == list(range(nb - 2048, nb))
+
+
+def test_selection_small_takes_everything():
+    rng = np.random.default_rng(2)
+    for n in (0, 1, 300, 512):
+        cand, idx = O.select(rng.standard_normal(n))
+        assert idx.tolist() == list(range(n))
+
+
+# ---------------------------------------------------------------- attention
+
+def test_worked_attention():
+    g = _gold("worked_tiny.json")["attention"]
+    q = np.zeros((1, 512))
+    q[0, 0] = math.log(2.0) / O.SCALE
+    X = np.zeros((3, 512))
+    X[:, 0] = [0, 1, 2]
+    X[:, 1] = [0, 10, 40]
+    o, lse = O.attend(q, X)
+    assert abs(o[0, 0] - g["o0"]) < 1e-12 and abs(o[0, 1] - g["o1"]) < 1e-12
+    assert abs(lse[0] - g["lse"]) < 1e-12
+
+
+def test_attention_matches_torch_sdpa_fp64():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((64, 512))
+    X = rng.standard_normal((300, 512))
+    o, lse = O.attend(q, X)
+    qt = torch.from_numpy(q)[None, :, None, :]            # [1, H, 1, D]
+    kt = torch.from_numpy(X)[None, None].expand(1, 64, 300, 512)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, kt, scale=O.SCALE)
+    assert np.allclose(o, ref[0, :, 0].numpy(), rtol=1e-12, atol=1e-12)
+    s = O.SCALE * (torch.from_numpy(q) @ torch.from_numpy(X).T)
+    assert np.allclose(lse, torch.logsumexp(s, dim=1).numpy(), rtol=1e-13, atol=1e-13)
+
+
+def test_attention_brute_force_tiny():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((3, 16))
+    X = rng.standard_normal((7, 16))
+    ob, lb = brute.attend(q.tolist(), X.tolist(), 0.3)
+    o, lse = O.attend(q, X, 0.3)
+    assert np.allclose(o, ob, rtol=1e-12, atol=1e-13) and np.allclose(lse, lb, rtol=1e-13)
+
+
+def test_attention_invariants():
+    rng = np.random.default_rng(8)
+    X = rng.standard_normal((640, 512))
+    q = rng.standard_normal((64, 512)) * 3
+    o, lse = O.attend(q, X)
+    assert np.all(o <= X.max(0) + 1e-12) and np.all(o >= X.min(0) - 1e-12)   # convex hull
+    perm = rng.permutation(640)
+    o2, lse2 = O.attend(q, X[perm])
+    assert np.allclose(o, o2, atol=1e-12) and np.allclose(lse, lse2, atol=1e-12)
+    o0, l0 = O.attend(np.zeros((64, 512)), X)
+    assert np.allclose(o0, X.mean(0)[None], atol=1e-12) and np.allclose(l0, math.log(640))
+    o1, l1 = O.attend(q, X[:1])
+    assert np.allclose(o1, X[:1], atol=0) and np.allclose(l1, O.SCALE * (q @ X[0]))
+    # one key 30 nats above the rest dominates
+    Y = X[:5].copy()
+    Y[:, 0] = [0.0, 1.0, 0.0, 0.0, 0.0]
+    qs = np.zeros((1, 512))
+    qs[0, 0] = 30.0 / O.SCALE
+    oo, ll = O.attend(qs, Y)
+    assert np.allclose(oo[0], Y[1], atol=1e-11) and abs(ll[0] - 30.0) < 1e-11
+
+
+# ---------------------------------------------------------------- compressor
+
+def test_worked_compress():
+    g = _gold("worked_tiny.json")["compress"]
+    x = np.array([[[g["x"][0]], [g["x"][1]]]])
+    out = O.compress(x, np.array([[[math.log(3.0)], [0.0]]]), np.zeros((2, 1)))
+    assert abs(out[0, 0] - g["gap_ln3"]) < 1e-12
+    out = O.compress(x, np.array([[[1.7], [1.7]]]), np.zeros((2, 1)))
+    assert abs(out[0, 0] - g["equal"]) < 1e-12
+
+
+def test_compress_matches_torch_softmax_and_brute():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((5, 2, 512))
+    z = rng.standard_normal((5, 2, 512)) * 4
+    beta = rng.standard_normal((2, 512))
+    out = O.compress(x, z, beta)
+    pi = torch.softmax(torch.from_numpy(z + beta[None]), dim=1).numpy()
+    assert np.allclose(out, (pi * x).sum(1), rtol=1e-13, atol=1e-13)
+    for g in range(5):
+        ref = brute.compress_pair(x[g, 0].tolist(), x[g, 1].tolist(), z[g, 0].tolist(),
+                                  z[g, 1].tolist(), beta[0].tolist(), beta[1].tolist())
+        assert np.allclose(out[g], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_compress_invariants():
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((9, 2, 64))
+    z = rng.standard_normal((9, 2, 64))
+    beta = rng.standard_normal((2, 64))
+    out = O.compress(x, z, beta)
+    assert np.all(out <= x.max(1) + 1e-12) and np.all(out >= x.min(1) - 1e-12)
+    assert np.allclose(O.compress(x, z + 5.0, beta), out, atol=1e-12)     # shift invariance
+    zz = np.zeros_like(z)
+    zz[:, 0] = 40.0
+    assert np.allclose(O.compress(x, zz, np.zeros((2, 64))), x[:, 0], atol=1e-15)
+    # slot bias is per slot: a bias on slot 1 only favours slot 1
+    b1 = np.zeros((2, 64))
+    b1[1] = 40.0
+    assert np.allclose(O.compress(x, np.zeros_like(z), b1), x[:, 1], atol=1e-15)
+
+
+# ---------------------------------------------------------------- whole path
+
+class _TinyWL:
+    """A tiny hand-built workload (no generator) for whole-path checks."""
+
+    def __init__(self, rng, B, n_raw, ratio, fp8=False, wcap=128):
+        self.ratio, self.B, self.T, self.wcap = ratio, B, B, wcap
+        self.seq = np.arange(B, dtype=np.int32)
+        self.pos = (np.asarray(n_raw) - 1).astype(np.int32)
+        nc = max(1, int(((self.pos + 1) // ratio).max()))
+        self.nc_cap = nc
+
+        def bf(shape):
+            return O.f64_to_bf16(rng.standard_normal(shape).astype(np.float32).astype(np.float64))
+        self.q = bf((B, 64, 512))
+        self.qI = bf((B, 16, 128))
+        self.w = rng.uniform(0, 1, (B, 16)).astype(np.float32)
+        self.C = bf((B, nc, 512))
+        self.R = bf((B, wcap, 512))
+        if fp8:
+            self.KI = rng.integers(0, 0x7F, (B, nc, 128)).astype(np.uint8) | (
+                rng.integers(0, 2, (B, nc, 128)).astype(np.uint8) << 7)
+            self.KI[self.KI == 0xFF] = 0xFE
+            self.KS = rng.uniform(0.001, 0.01, (B, nc)).astype(np.float32)
+        else:
+            self.KI, self.KS = bf((B, nc, 128)), None
+        self.Xp = bf((B, 2, 512)) if ratio == 2 else None
+        self.Zp = bf((B, 2, 512)) if ratio == 2 else None
+        self.beta = rng.standard_normal((2, 512)).astype(np.float32) if ratio == 2 else None
+
+    def compress_groups(self):
+        if self.ratio != 2:
+            return np.zeros(0, np.int64)
+        return self.seq[((self.pos.astype(np.int64) + 1) % 2) == 0].astype(np.int64)
+
+
+def test_whole_path_small_context_is_dense_attention():
+    """n <= 512: everything is selected, so the output is dense attention over all
+    compressed rows plus the window rows (library SDPA in fp64)."""
+    rng = np.random.default_rng(20)
+    wl = _TinyWL(rng, B=2, n_raw=[600, 901], ratio=2)
+    res = O.run(wl)
+    for t in range(2):
+        b, p = int(wl.seq[t]), int(wl.pos[t])
+        n = (p + 1) // 2
+        assert res.idx[t].tolist() == list(range(n))
+        C = O.bf16_to_f64(wl.C[b, :n])
+        if (p + 1) % 2 == 0:                      # this query completes group n-1
+            C[n - 1] = O.bf16_to_f64(res.C_new[b][1])
+        else:
+            assert b not in res.C_new
+        X = np.concatenate([C, O.bf16_to_f64(wl.R[b, np.arange(p - 127, p + 1) % 128])])
+        qt = torch.from_numpy(O.bf16_to_f64(wl.q[t]))[None, :, None, :]
+        kt = torch.from_numpy(X)[None, None].expand(1, 64, X.shape[0], 512)
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, kt, scale=O.SCALE)
+        assert np.allclose(res.o[t], ref[0, :, 0].numpy(), atol=1e-12)
+
+
+def test_whole_path_fp8_keys_equal_decoded_bf16_path():
+    """An e4m3 key with a power-of-two scale is exactly a bf16 key; both stores must
+    give identical scores and selections."""
+    rng = np.random.default_rng(21)
+    wl = _TinyWL(rng, B=1, n_raw=[3000], ratio=2, fp8=True)
+    wl.KS[:] = 0.0078125
+    k = O.index_keys_f64(wl.KI, wl.KS)
+    wl2 = _TinyWL(np.random.default_rng(21), B=1, n_raw=[3000], ratio=2)
+    wl2.qI, wl2.w = wl.qI, wl.w
+    wl2.KI, wl2.KS = O.f64_to_bf16(k), None
+    r1, r2 = O.run(wl), O.run(wl2)
+    assert np.array_equal(r1.scores[0], r2.scores[0])
+    assert np.array_equal(r1.idx[0], r2.idx[0])
+
+
+def test_compressor_row_feeds_attention():
+    """The compressed latent written this step is the one attention reads at n-1."""
+    rng = np.random.default_rng(22)
+    wl = _TinyWL(rng, B=1, n_raw=[64], ratio=2)
+    res = O.run(wl)
+    n = 32
+    expect = O.compress(O.bf16_to_f64(wl.Xp[0])[None], O.bf16_to_f64(wl.Zp[0])[None], wl.beta)[0]
+    assert np.array_equal(res.C_new[0][1], O.f64_to_bf16(expect))
+    q = O.bf16_to_f64(wl.q[0])
+    C = O.bf16_to_f64(wl.C[0, :n])
+    C[n - 1] = O.bf16_to_f64(res.C_new[0][1])
+    X = np.concatenate([C, O.bf16_to_f64(wl.R[0, np.arange(0, 64) % 128])])
+    o, lse = O.attend(q, X)
+    assert np.allclose(res.o[0], o, atol=0) and np.allclose(res.lse[0], lse, atol=0)

@@ -1,0 +1,43 @@
+"""Input generator: determinism, independence of streams, value recipe."""
+import numpy as np
+
+import workloads as W
+from oracle import oracle as O
+
+
+def test_streams_are_deterministic_and_distinct():
+    a = W.normal_bf16(0, "C", 3, (1000,))
+    b = W.normal_bf16(0, "C", 3, (1000,))
+    c = W.normal_bf16(0, "C", 4, (1000,))
+    d = W.normal_bf16(1, "C", 3, (1000,))
+    assert np.array_equal(a, b) and not np.array_equal(a, c) and not np.array_equal(a, d)
+    # a prefix of a longer draw is the shorter draw
+    assert np.array_equal(W.normal_bf16(0, "C", 3, (4000,))[:1000], a)
+
+
+def test_normal_moments():
+    x = W.normal_f32(0, "q", 0, (1 << 20,)).astype(np.float64)
+    assert abs(x.mean()) < 5e-3 and abs(x.std() - 1) < 5e-3
+    u = W.uniform_f32(0, "w", 0, (1 << 16,))
+    assert u.min() >= 0 and u.max() < 1 and abs(u.mean() - 0.5) < 1e-2
+
+
+def test_e4m3_rows_roundtrip_within_half_quantum():
+    x = W.normal_f32(0, "KI", 0, (300, 128))
+    codes, scale = W.quant_e4m3_rows(x)
+    dec = O.e4m3_to_f64(codes)
+    assert not np.isnan(dec).any()
+    assert np.all(np.abs(dec).max(axis=1) == 448.0)      # each row's amax maps to 448
+    y = x.astype(np.float64) / scale[:, None].astype(np.float64)
+    ay = np.maximum(np.abs(y), 2.0 ** -6)
+    quantum = 2.0 ** (np.floor(np.log2(ay)) - 3)
+    assert np.all(np.abs(dec - y) <= quantum / 2 * (1 + 1e-6))
+
+
+def test_decode_workload_shapes():
+    wl = W.make_decode(B=3, n_raw=[50, 61, 2], ratio=2, key_dtype="fp8")
+    assert wl.nc_cap == 30 and wl.KI.dtype == np.uint8 and wl.KS.shape == (3, 30)
+    assert wl.pos.tolist() == [49, 60, 1] and wl.visible().tolist() == [25, 30, 1]
+    assert wl.compress_groups().tolist() == [0, 2]
+    wp = W.make_prefill(T=10, offset=100, ratio=1)
+    assert wp.nc_cap == 110 and wp.wcap == 138 and wp.pos[0] == 100
