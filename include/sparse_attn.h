@@ -1,0 +1,181 @@
+/*
+ * sparse_attn.h -- C ABI of the two-tier sparse-attention hot path of a
+ * DeepSeek-V4.1 Flash layer, for AMD MI355X (gfx950).
+ *
+ * What is computed (per query t of sequence b at raw position p):
+ *   S0  compressor: a group of r raw latents is pooled into one compressed
+ *       latent by a learned softmax gate ("deepseek-ai/DeepSeek-V4.1-Flash"
+ *       vLLM recipe, Overview, two-tier sparse attention bullet: latents
+ *       "pooled by a learned softmax gate"; "DeepSeek-V4.1 Flash" Miles docs,
+ *       section 1: 2 positions into 1, or 1-to-1).
+ *   S1  indexer: every visible compressed latent j < n = (p+1)/r gets the score
+ *       I(j) = s_j * sum_h w_h * max(0, <qI_h, kI_j>) over 16 index heads of
+ *       128 dims (recipe Overview: an indexer scores the latents).
+ *   S2  candidate stage: the 2048 blocks of 8 consecutive positions with the
+ *       highest block score (max of the block's visible scores) are kept
+ *       (recipe Overview: "a candidate stage that selects 2048 blocks of 8").
+ *   S3  top-512: the 512 best positions inside the candidates (recipe
+ *       Overview: keeps the best 512 per query; Miles docs section 1).
+ *   S4  attention: 64 query heads, one softmax over the selected latents plus
+ *       the 128-position window [p-127, p]; each 512-wide latent is both key
+ *       and value (Miles docs section 1).
+ * Ties at S2 and S3 are broken by the lower position / block id.
+ *
+ * Conventions for every call:
+ *   - Pointers marked "device" are GPU memory owned by the caller; the library
+ *     never allocates, frees or synchronises inside these calls, so each call
+ *     only enqueues kernels on `stream` (a hipStream_t, or NULL for the null
+ *     stream) and may be captured in a HIP graph. Outputs are valid once the
+ *     stream reaches the enqueued work.
+ *   - bf16 is bfloat16 (upper half of IEEE binary32). e4m3 is OCP FP8 E4M3
+ *     ("e4m3fn": bias 7, max 448, no infinities).
+ *   - Strides are in elements. Rows (the last dimension) are contiguous.
+ *   - Every device pointer must be 16-byte aligned, and every stride a
+ *     multiple of 8 elements (16 for e4m3 keys).
+ *   - Return value: SA_OK, or an error code with a message available from
+ *     sparse_attn_last_error() on the calling thread. All argument checks run
+ *     on the host before any HIP call; an invalid call enqueues nothing.
+ *     Device faults are asynchronous and surface at the caller's next sync.
+ *   - Device metadata (seq_id, pos, topk entries) is not read on the host.
+ *     Kernels clamp it so that memory stays in bounds: a query with seq_id
+ *     outside [0, num_seqs) or pos < 0 gets n = 0; n is capped at
+ *     max_visible and compressed_cap; attention skips topk entries outside
+ *     [0, n). Results for such queries are unspecified but memory-safe.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sa_status {
+  SA_OK = 0,
+  SA_EINVAL = 1,        /* null pointer, misalignment, size or shape mismatch */
+  SA_EUNSUPPORTED = 2,  /* dimensions other than the ones the kernels are built for */
+  SA_EWORKSPACE = 3,    /* workspace missing or smaller than the plan requires */
+  SA_EHIP = 4           /* a HIP runtime call or kernel launch failed */
+} sa_status;
+
+typedef enum sa_key_dtype {
+  SA_KEY_BF16 = 0,      /* index keys bf16 [.][128] */
+  SA_KEY_FP8_E4M3 = 1   /* index keys e4m3 [.][128] plus one fp32 scale per key */
+} sa_key_dtype;
+
+/* Fixed at plan time. The kernels support exactly num_heads 64, latent_dim 512,
+ * window 128, topk 512, idx_heads 16, idx_dim 128, block 8, cand_blocks 2048,
+ * ratio 1 or 2; anything else returns SA_EUNSUPPORTED. */
+typedef struct sa_params {
+  int32_t num_heads;
+  int32_t latent_dim;
+  int32_t window;
+  int32_t topk;
+  int32_t idx_heads;
+  int32_t idx_dim;
+  int32_t block;
+  int32_t cand_blocks;
+  int32_t ratio;
+  int32_t idx_key_dtype;   /* sa_key_dtype */
+  float softmax_scale;     /* multiplies <q_h, x>; 1/sqrt(512) for this layer */
+  int64_t max_queries;     /* largest T of any call made with this plan */
+  int64_t max_compressed;  /* largest visible compressed count of any query */
+} sa_params;
+
+typedef struct sa_plan sa_plan;
+
+/* A batch of T queries. */
+typedef struct sa_queries {
+  int64_t T;               /* 1 <= T <= plan max_queries */
+  const int32_t* seq_id;   /* device [T]: sequence of query t */
+  const int32_t* pos;      /* device [T]: raw position p of query t */
+  int64_t max_visible;     /* host: >= (pos[t]+1)/ratio for every t, <= plan max_compressed.
+                              Sizes the grids and the score rows. */
+} sa_queries;
+
+/* Per-sequence stores, all device memory. */
+typedef struct sa_cache {
+  int64_t num_seqs;
+  int64_t compressed_cap;        /* rows per sequence in latents / idx_keys / idx_scales */
+  const void* latents;           /* bf16 [num_seqs][compressed_cap][512] compressed latents */
+  int64_t latents_seq_stride;    /* >= compressed_cap * 512 */
+  const void* window;            /* bf16 [num_seqs][window_cap][512]; raw position u is row u % window_cap */
+  int64_t window_seq_stride;     /* >= window_cap * 512 */
+  int32_t window_cap;            /* >= 128 */
+  const void* idx_keys;          /* bf16 or e4m3 [num_seqs][compressed_cap][128] */
+  int64_t idx_keys_seq_stride;   /* >= compressed_cap * 128 */
+  const float* idx_scales;       /* fp32 [num_seqs][compressed_cap] for e4m3 keys, NULL for bf16 */
+  int64_t idx_scales_seq_stride; /* >= compressed_cap (e4m3 only) */
+} sa_cache;
+
+/* Validate `params` and create a plan (host memory owned by the library,
+ * immutable, shareable across threads and streams). `*workspace_bytes`
+ * receives the device workspace size that select_topk and sparse_attn_fwd
+ * need for T = max_queries; concurrent calls need separate workspaces. */
+sa_status sparse_attn_plan(const sa_params* params, sa_plan** plan, size_t* workspace_bytes);
+
+void sparse_attn_plan_destroy(sa_plan* plan);
+
+/* Message of the last non-OK status returned on this thread ("" if none). */
+const char* sparse_attn_last_error(void);
+
+/* S1. Indexer scores and block maxima.
+ *   q_idx      device bf16 [T][16][128]   index query of each query
+ *   w          device fp32 [T][16]        index head weights
+ *   scores     device fp32 [T][ld_scores] out: scores[t][j] = I(j) for j < n_t,
+ *              -inf for n_t <= j < E, with E = max_visible rounded up to 8;
+ *              entries at j >= E are not written.  ld_scores >= E.
+ *   block_max  device fp32 [T][ld_block_max] or NULL. out: the max of block
+ *              b's visible scores for b < ceil(n_t/8), -inf for the rest of
+ *              the first E/8 entries. ld_block_max >= E/8. */
+sa_status indexer_score(const sa_plan* plan, const sa_queries* queries, const sa_cache* cache,
+                        const void* q_idx, const float* w, float* scores, int64_t ld_scores,
+                        float* block_max, int64_t ld_block_max, void* stream);
+
+/* S2 + S3. Candidate blocks, then the top-512 positions inside them.
+ *   scores, ld_scores      as written by indexer_score
+ *   block_max              as written by indexer_score, or NULL (then the block
+ *                          maxima are recomputed from scores)
+ *   cand       device int32 [T][2048] or NULL: out, the kept block ids of each
+ *              query in ascending order, -1 after the last one (ceil(n_t/8)
+ *              blocks are kept when there are at most 2048). NULL keeps them
+ *              in the workspace only.
+ *   topk       device int32 [T][512]: out, the selected positions in ascending
+ *              order, -1 after the last one (min(512, n_t) are selected).
+ *   workspace  device, >= the size reported by sparse_attn_plan. */
+sa_status select_topk(const sa_plan* plan, const sa_queries* queries, const float* scores,
+                      int64_t ld_scores, const float* block_max, int64_t ld_block_max,
+                      int32_t* cand, int32_t* topk, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* S4. Joint-softmax attention over the selected latents and the window.
+ *   q      device bf16 [T][64][512]
+ *   topk   device int32 [T][512]: positions into the sequence's compressed store;
+ *          entries outside [0, n_t) are skipped
+ *   out    device bf16 [T][64][512]: out, per-head attention output
+ *   lse    device fp32 [T][64] or NULL: out, natural-log sum of exp of the
+ *          scaled logits (max + log of the normaliser)
+ *   workspace  device, >= the size reported by sparse_attn_plan. */
+sa_status sparse_attn_fwd(const sa_plan* plan, const sa_queries* queries, const sa_cache* cache,
+                          const void* q, const int32_t* topk, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* S0. Softmax-gate compressor over G groups of `ratio` raw latents.
+ * Group g reads raw rows raw + g*raw_group_stride + k*512 and gate logits
+ * gate + g*gate_group_stride + k*512 (k < ratio, bf16), and writes
+ * out + g*out_group_stride (bf16, round to nearest even):
+ *   out[c] = sum_k softmax_k(gate[k][c] + slot_bias[k][c]) * raw[k][c].
+ * slot_bias: device fp32 [ratio][512]. For ratio 1 the output is the raw row.
+ * Output rows must not overlap input rows. */
+sa_status sparse_attn_compress(const sa_plan* plan, const void* raw, int64_t raw_group_stride,
+                               const void* gate, int64_t gate_group_stride,
+                               const float* slot_bias, void* out, int64_t out_group_stride,
+                               int64_t G, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

@@ -1,0 +1,251 @@
+"""Python binding of libsparse_attn.so: the two-tier sparse-attention hot path on MI355X.
+
+Argument marshalling only. Every stage runs in the library's HIP kernels; torch is used
+for device memory and the current stream. The entry points have the names of the C ABI
+(include/sparse_attn.h): sparse_attn_plan, indexer_score, select_topk, sparse_attn_fwd,
+sparse_attn_compress. If the built library is missing, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsparse_attn.so")
+
+SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_EWORKSPACE, SA_EHIP = 0, 1, 2, 3, 4
+SA_KEY_BF16, SA_KEY_FP8_E4M3 = 0, 1
+STATUS_NAMES = {0: "SA_OK", 1: "SA_EINVAL", 2: "SA_EUNSUPPORTED", 3: "SA_EWORKSPACE", 4: "SA_EHIP"}
+
+EXPORTS = ("sparse_attn_plan", "sparse_attn_plan_destroy", "sparse_attn_last_error",
+           "indexer_score", "select_topk", "sparse_attn_fwd", "sparse_attn_compress")
+
+
+class sa_params(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("latent_dim", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32),
+                ("block", ctypes.c_int32), ("cand_blocks", ctypes.c_int32),
+                ("ratio", ctypes.c_int32), ("idx_key_dtype", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float), ("max_queries", ctypes.c_int64),
+                ("max_compressed", ctypes.c_int64)]
+
+
+class sa_queries(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("seq_id", ctypes.c_void_p), ("pos", ctypes.c_void_p),
+                ("max_visible", ctypes.c_int64)]
+
+
+class sa_cache(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int64), ("compressed_cap", ctypes.c_int64),
+                ("latents", ctypes.c_void_p), ("latents_seq_stride", ctypes.c_int64),
+                ("window", ctypes.c_void_p), ("window_seq_stride", ctypes.c_int64),
+                ("window_cap", ctypes.c_int32),
+                ("idx_keys", ctypes.c_void_p), ("idx_keys_seq_stride", ctypes.c_int64),
+                ("idx_scales", ctypes.c_void_p), ("idx_scales_seq_stride", ctypes.c_int64)]
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                          f"python -m sparse_attention_score_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    lib.sparse_attn_plan.argtypes = [ctypes.POINTER(sa_params), ctypes.POINTER(vp), ctypes.POINTER(sz)]
+    lib.sparse_attn_plan.restype = ctypes.c_int
+    lib.sparse_attn_plan_destroy.argtypes = [vp]
+    lib.sparse_attn_plan_destroy.restype = None
+    lib.sparse_attn_last_error.argtypes = []
+    lib.sparse_attn_last_error.restype = ctypes.c_char_p
+    lib.indexer_score.argtypes = [vp, ctypes.POINTER(sa_queries), ctypes.POINTER(sa_cache), vp, vp,
+                                  vp, i64, vp, i64, vp]
+    lib.indexer_score.restype = ctypes.c_int
+    lib.select_topk.argtypes = [vp, ctypes.POINTER(sa_queries), vp, i64, vp, i64, vp, vp, vp, sz, vp]
+    lib.select_topk.restype = ctypes.c_int
+    lib.sparse_attn_fwd.argtypes = [vp, ctypes.POINTER(sa_queries), ctypes.POINTER(sa_cache), vp, vp,
+                                    vp, vp, vp, sz, vp]
+    lib.sparse_attn_fwd.restype = ctypes.c_int
+    lib.sparse_attn_compress.argtypes = [vp, vp, i64, vp, i64, vp, vp, i64, i64, vp]
+    lib.sparse_attn_compress.restype = ctypes.c_int
+    return lib
+
+
+lib = _load()
+
+
+def _check(status: int):
+    if status != SA_OK:
+        msg = lib.sparse_attn_last_error()
+        raise SparseAttnError(status, msg.decode() if msg else "")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _need(t: torch.Tensor, name: str, dtype, cuda: bool = True):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if cuda and not t.is_cuda:
+        raise TypeError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+class Plan:
+    """sparse_attn_plan: fixed layer shape, ratio, key dtype and maximum sizes."""
+
+    _destroy = lib.sparse_attn_plan_destroy
+
+    def __init__(self, ratio: int, key_dtype: str = "bf16", max_queries: int = 1,
+                 max_compressed: int = 0, softmax_scale: float = 1.0 / math.sqrt(512.0),
+                 **dims):
+        p = sa_params(num_heads=dims.get("num_heads", 64), latent_dim=dims.get("latent_dim", 512),
+                      window=dims.get("window", 128), topk=dims.get("topk", 512),
+                      idx_heads=dims.get("idx_heads", 16), idx_dim=dims.get("idx_dim", 128),
+                      block=dims.get("block", 8), cand_blocks=dims.get("cand_blocks", 2048),
+                      ratio=ratio,
+                      idx_key_dtype=SA_KEY_FP8_E4M3 if key_dtype == "fp8" else SA_KEY_BF16,
+                      softmax_scale=softmax_scale, max_queries=max_queries,
+                      max_compressed=max_compressed)
+        h = ctypes.c_void_p()
+        ws = ctypes.c_size_t()
+        _check(lib.sparse_attn_plan(ctypes.byref(p), ctypes.byref(h), ctypes.byref(ws)))
+        self.handle = h
+        self.params = p
+        self.workspace_bytes = ws.value
+        self.key_dtype = key_dtype
+        self.ratio = ratio
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            Plan._destroy(h)
+            self.handle = None
+
+
+def sparse_attn_plan(**kw) -> Plan:
+    return Plan(**kw)
+
+
+class Queries:
+    """sa_queries from device int32 tensors seq_id[T], pos[T] and a host max_visible."""
+
+    def __init__(self, seq_id: torch.Tensor, pos: torch.Tensor, max_visible: int):
+        _need(seq_id, "seq_id", torch.int32)
+        _need(pos, "pos", torch.int32)
+        self._keep = (seq_id, pos)
+        self.c = sa_queries(T=seq_id.shape[0], seq_id=seq_id.data_ptr(), pos=pos.data_ptr(),
+                            max_visible=int(max_visible))
+
+    @property
+    def T(self) -> int:
+        return self.c.T
+
+
+class Cache:
+    """sa_cache from device tensors: latents [S,cap,512] bf16, window [S,wcap,512] bf16,
+    idx_keys [S,cap,128] bf16 or uint8 (e4m3 codes), idx_scales [S,cap] fp32 or None.
+    Any of them may be None when the call at hand does not read it."""
+
+    def __init__(self, latents=None, window=None, idx_keys=None, idx_scales=None,
+                 num_seqs: Optional[int] = None, compressed_cap: Optional[int] = None):
+        ref = latents if latents is not None else idx_keys
+        if num_seqs is None:
+            num_seqs = ref.shape[0]
+        if compressed_cap is None:
+            compressed_cap = ref.shape[1]
+        c = sa_cache(num_seqs=num_seqs, compressed_cap=compressed_cap)
+        if latents is not None:
+            _need(latents, "latents", torch.bfloat16)
+            c.latents, c.latents_seq_stride = latents.data_ptr(), latents.stride(0)
+        if window is not None:
+            _need(window, "window", torch.bfloat16)
+            c.window, c.window_seq_stride, c.window_cap = window.data_ptr(), window.stride(0), window.shape[1]
+        if idx_keys is not None:
+            if idx_keys.dtype not in (torch.bfloat16, torch.uint8):
+                raise TypeError("idx_keys must be bfloat16 or uint8 (e4m3 codes)")
+            _need(idx_keys, "idx_keys", idx_keys.dtype)
+            c.idx_keys, c.idx_keys_seq_stride = idx_keys.data_ptr(), idx_keys.stride(0)
+        if idx_scales is not None:
+            _need(idx_scales, "idx_scales", torch.float32)
+            c.idx_scales, c.idx_scales_seq_stride = idx_scales.data_ptr(), idx_scales.stride(0)
+        self._keep = (latents, window, idx_keys, idx_scales)
+        self.c = c
+
+
+def indexer_score(plan: Plan, queries: Queries, cache: Cache, q_idx: torch.Tensor, w: torch.Tensor,
+                  scores: torch.Tensor, block_max: Optional[torch.Tensor] = None, stream=None):
+    _need(q_idx, "q_idx", torch.bfloat16)
+    _need(w, "w", torch.float32)
+    _need(scores, "scores", torch.float32)
+    if block_max is not None:
+        _need(block_max, "block_max", torch.float32)
+    _check(lib.indexer_score(plan.handle, ctypes.byref(queries.c), ctypes.byref(cache.c),
+                             _ptr(q_idx), _ptr(w), _ptr(scores), scores.stride(0),
+                             _ptr(block_max), 0 if block_max is None else block_max.stride(0),
+                             _stream(stream)))
+
+
+def select_topk(plan: Plan, queries: Queries, scores: torch.Tensor,
+                block_max: Optional[torch.Tensor], topk: torch.Tensor,
+                cand: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                stream=None):
+    _need(scores, "scores", torch.float32)
+    _need(topk, "topk", torch.int32)
+    if block_max is not None:
+        _need(block_max, "block_max", torch.float32)
+    if cand is not None:
+        _need(cand, "cand", torch.int32)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.select_topk(plan.handle, ctypes.byref(queries.c), _ptr(scores), scores.stride(0),
+                           _ptr(block_max), 0 if block_max is None else block_max.stride(0),
+                           _ptr(cand), _ptr(topk), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def sparse_attn_fwd(plan: Plan, queries: Queries, cache: Cache, q: torch.Tensor, topk: torch.Tensor,
+                    out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None):
+    _need(q, "q", torch.bfloat16)
+    _need(topk, "topk", torch.int32)
+    _need(out, "out", torch.bfloat16)
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.sparse_attn_fwd(plan.handle, ctypes.byref(queries.c), ctypes.byref(cache.c), _ptr(q),
+                               _ptr(topk), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
+                               _stream(stream)))
+
+
+def sparse_attn_compress(plan: Plan, raw: torch.Tensor, raw_group_stride: int, gate: Optional[torch.Tensor],
+                         gate_group_stride: int, slot_bias: Optional[torch.Tensor], out: torch.Tensor,
+                         out_group_stride: int, G: int, stream=None):
+    """Tensors are passed as base pointers; groups are addressed by the given element strides."""
+    for t, name in ((raw, "raw"), (out, "out")):
+        if t.dtype != torch.bfloat16 or not t.is_cuda:
+            raise TypeError(f"{name}: expected a bfloat16 device tensor")
+    if gate is not None and (gate.dtype != torch.bfloat16 or not gate.is_cuda):
+        raise TypeError("gate: expected a bfloat16 device tensor")
+    if slot_bias is not None:
+        _need(slot_bias, "slot_bias", torch.float32)
+    _check(lib.sparse_attn_compress(plan.handle, _ptr(raw), raw_group_stride, _ptr(gate),
+                                    gate_group_stride, _ptr(slot_bias), _ptr(out), out_group_stride,
+                                    G, _stream(stream)))

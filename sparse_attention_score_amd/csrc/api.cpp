@@ -1,0 +1,305 @@
+// C ABI of the sparse-attention library: argument checks, plan and workspace sizing,
+// kernel dispatch. Every check runs on the host before any HIP call, no C++ exception
+// leaves this file, and nothing here allocates device memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <new>
+
+#include "../../include/sparse_attn.h"
+#include "sa_launch.h"
+
+struct sa_plan {
+  sa_params p;
+  size_t workspace;
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sa_status fail(sa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+sa_status ok() {
+  g_err[0] = '\0';
+  return SA_OK;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+constexpr int64_t kMaxVisible = 2048LL * 8 * 32;  // 524288: largest block set a select WG holds
+
+size_t cand_bytes(int64_t T) { return (size_t)T * 2048 * sizeof(int32_t); }
+
+sa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define SA_REQUIRE(cond, st, ...)              \
+  do {                                         \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+sa_status check_plan(const sa_plan* plan) {
+  SA_REQUIRE(plan != nullptr, SA_EINVAL, "plan is NULL");
+  return SA_OK;
+}
+
+sa_status check_queries(const sa_plan* plan, const sa_queries* q) {
+  SA_REQUIRE(q != nullptr, SA_EINVAL, "queries is NULL");
+  SA_REQUIRE(q->T >= 1 && q->T <= plan->p.max_queries, SA_EINVAL,
+             "queries->T = %lld outside [1, max_queries = %lld]", (long long)q->T,
+             (long long)plan->p.max_queries);
+  SA_REQUIRE(q->T <= 65535LL * 1024, SA_EUNSUPPORTED, "T = %lld too large", (long long)q->T);
+  SA_REQUIRE(q->seq_id != nullptr && q->pos != nullptr, SA_EINVAL, "queries seq_id/pos is NULL");
+  SA_REQUIRE(q->max_visible >= 0 && q->max_visible <= plan->p.max_compressed, SA_EINVAL,
+             "queries->max_visible = %lld outside [0, max_compressed = %lld]",
+             (long long)q->max_visible, (long long)plan->p.max_compressed);
+  return SA_OK;
+}
+
+sa_status check_cache(const sa_plan* plan, const sa_queries* q, const sa_cache* c, bool keys,
+                      bool latents) {
+  SA_REQUIRE(c != nullptr, SA_EINVAL, "cache is NULL");
+  SA_REQUIRE(c->num_seqs >= 1, SA_EINVAL, "cache->num_seqs must be >= 1");
+  SA_REQUIRE(c->compressed_cap >= 0, SA_EINVAL, "cache->compressed_cap < 0");
+  SA_REQUIRE(q->max_visible <= c->compressed_cap, SA_EINVAL,
+             "queries->max_visible = %lld exceeds cache->compressed_cap = %lld",
+             (long long)q->max_visible, (long long)c->compressed_cap);
+  if (keys) {
+    SA_REQUIRE(c->idx_keys != nullptr && aligned16(c->idx_keys), SA_EINVAL,
+               "cache->idx_keys is NULL or not 16-byte aligned");
+    const int64_t rowmul = plan->p.idx_key_dtype == SA_KEY_FP8_E4M3 ? 16 : 8;
+    SA_REQUIRE(c->idx_keys_seq_stride >= c->compressed_cap * 128 && c->idx_keys_seq_stride % rowmul == 0,
+               SA_EINVAL, "cache->idx_keys_seq_stride = %lld invalid", (long long)c->idx_keys_seq_stride);
+    if (plan->p.idx_key_dtype == SA_KEY_FP8_E4M3) {
+      SA_REQUIRE(c->idx_scales != nullptr && aligned16(c->idx_scales), SA_EINVAL,
+                 "cache->idx_scales is NULL or misaligned (required for e4m3 keys)");
+      SA_REQUIRE(c->idx_scales_seq_stride >= c->compressed_cap, SA_EINVAL,
+                 "cache->idx_scales_seq_stride = %lld < compressed_cap",
+                 (long long)c->idx_scales_seq_stride);
+    }
+  }
+  if (latents) {
+    SA_REQUIRE(c->latents != nullptr && aligned16(c->latents), SA_EINVAL,
+               "cache->latents is NULL or not 16-byte aligned");
+    SA_REQUIRE(c->latents_seq_stride >= c->compressed_cap * 512 && c->latents_seq_stride % 8 == 0,
+               SA_EINVAL, "cache->latents_seq_stride = %lld invalid", (long long)c->latents_seq_stride);
+    SA_REQUIRE(c->window != nullptr && aligned16(c->window), SA_EINVAL,
+               "cache->window is NULL or not 16-byte aligned");
+    SA_REQUIRE(c->window_cap >= plan->p.window, SA_EINVAL, "cache->window_cap = %d < window %d",
+               c->window_cap, plan->p.window);
+    SA_REQUIRE(c->window_seq_stride >= (int64_t)c->window_cap * 512 && c->window_seq_stride % 8 == 0,
+               SA_EINVAL, "cache->window_seq_stride = %lld invalid", (long long)c->window_seq_stride);
+  }
+  return SA_OK;
+}
+
+sa::QueryMeta meta(const sa_plan* plan, const sa_queries* q, int64_t num_seqs, int64_t cap) {
+  sa::QueryMeta m;
+  m.seq_id = q->seq_id;
+  m.pos = q->pos;
+  m.T = q->T;
+  m.max_visible = q->max_visible;
+  m.num_seqs = num_seqs;
+  m.compressed_cap = cap;
+  m.ratio = plan->p.ratio;
+  return m;
+}
+
+int64_t round8(int64_t v) { return (v + 7) / 8 * 8; }
+
+}  // namespace
+
+extern "C" {
+
+const char* sparse_attn_last_error(void) { return g_err; }
+
+sa_status sparse_attn_plan(const sa_params* p, sa_plan** plan, size_t* workspace_bytes) {
+  SA_REQUIRE(p != nullptr && plan != nullptr, SA_EINVAL, "params or plan is NULL");
+  *plan = nullptr;
+  SA_REQUIRE(p->num_heads == 64 && p->latent_dim == 512 && p->window == 128 && p->topk == 512 &&
+                 p->idx_heads == 16 && p->idx_dim == 128 && p->block == 8 && p->cand_blocks == 2048,
+             SA_EUNSUPPORTED,
+             "unsupported dims (need heads 64, latent 512, window 128, topk 512, idx 16x128, "
+             "block 8, cand_blocks 2048)");
+  SA_REQUIRE(p->ratio == 1 || p->ratio == 2, SA_EUNSUPPORTED, "ratio %d not in {1, 2}", p->ratio);
+  SA_REQUIRE(p->idx_key_dtype == SA_KEY_BF16 || p->idx_key_dtype == SA_KEY_FP8_E4M3,
+             SA_EUNSUPPORTED, "idx_key_dtype %d unknown", p->idx_key_dtype);
+  SA_REQUIRE(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f, SA_EINVAL,
+             "softmax_scale must be finite and > 0");
+  SA_REQUIRE(p->max_queries >= 1, SA_EINVAL, "max_queries must be >= 1");
+  SA_REQUIRE(p->max_compressed >= 0, SA_EINVAL, "max_compressed must be >= 0");
+  SA_REQUIRE(p->max_compressed <= kMaxVisible, SA_EUNSUPPORTED,
+             "max_compressed %lld above the supported %lld", (long long)p->max_compressed,
+             (long long)kMaxVisible);
+  sa_plan* pl = new (std::nothrow) sa_plan;
+  SA_REQUIRE(pl != nullptr, SA_EINVAL, "out of host memory");
+  pl->p = *p;
+  pl->workspace = cand_bytes(p->max_queries);
+  *plan = pl;
+  if (workspace_bytes) *workspace_bytes = pl->workspace;
+  return ok();
+}
+
+void sparse_attn_plan_destroy(sa_plan* plan) { delete plan; }
+
+sa_status indexer_score(const sa_plan* plan, const sa_queries* q, const sa_cache* c,
+                        const void* q_idx, const float* w, float* scores, int64_t ld_scores,
+                        float* block_max, int64_t ld_block_max, void* stream) {
+  sa_status st;
+  if ((st = check_plan(plan)) != SA_OK) return st;
+  if ((st = check_queries(plan, q)) != SA_OK) return st;
+  if ((st = check_cache(plan, q, c, true, false)) != SA_OK) return st;
+  SA_REQUIRE(q_idx && aligned16(q_idx) && w && aligned16(w), SA_EINVAL,
+             "q_idx / w NULL or not 16-byte aligned");
+  SA_REQUIRE(scores && aligned16(scores), SA_EINVAL, "scores NULL or not 16-byte aligned");
+  const int64_t E = round8(q->max_visible);
+  SA_REQUIRE(ld_scores >= E && ld_scores % 4 == 0, SA_EINVAL,
+             "ld_scores = %lld must be >= %lld (max_visible rounded up to 8) and a multiple of 4",
+             (long long)ld_scores, (long long)E);
+  if (block_max) {
+    SA_REQUIRE(aligned16(block_max), SA_EINVAL, "block_max not 16-byte aligned");
+    SA_REQUIRE(ld_block_max >= E / 8, SA_EINVAL, "ld_block_max = %lld must be >= %lld",
+               (long long)ld_block_max, (long long)(E / 8));
+  }
+  if (E == 0) return ok();
+  sa::IndexerArgs a;
+  a.seq_id = q->seq_id;
+  a.pos = q->pos;
+  a.T = q->T;
+  a.max_visible = q->max_visible;
+  a.num_seqs = c->num_seqs;
+  a.compressed_cap = c->compressed_cap;
+  a.ratio = plan->p.ratio;
+  a.fp8 = plan->p.idx_key_dtype == SA_KEY_FP8_E4M3;
+  a.q_idx = q_idx;
+  a.w = w;
+  a.keys = c->idx_keys;
+  a.keys_seq_stride = c->idx_keys_seq_stride;
+  a.scales = c->idx_scales;
+  a.scales_seq_stride = c->idx_scales_seq_stride;
+  a.scores = scores;
+  a.ld_scores = ld_scores;
+  a.block_max = block_max;
+  a.ld_block_max = ld_block_max;
+  a.E = E;
+  // Queries that share a sequence in one call (a prefill chunk) reuse each key tile
+  // across many queries; independent decode queries each stream their own keys.
+  const bool prefill = c->num_seqs == 1 && q->T > 1;
+  SA_REQUIRE(prefill || q->T <= 65535, SA_EUNSUPPORTED,
+             "T = %lld queries over several sequences: at most 65535 per call", (long long)q->T);
+  return hip_status(sa::launch_indexer(a, prefill, (hipStream_t)stream), "indexer_score launch");
+}
+
+sa_status select_topk(const sa_plan* plan, const sa_queries* q, const float* scores,
+                      int64_t ld_scores, const float* block_max, int64_t ld_block_max,
+                      int32_t* cand, int32_t* topk, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  sa_status st;
+  if ((st = check_plan(plan)) != SA_OK) return st;
+  if ((st = check_queries(plan, q)) != SA_OK) return st;
+  const int64_t E = round8(q->max_visible);
+  SA_REQUIRE(scores && aligned16(scores), SA_EINVAL, "scores NULL or not 16-byte aligned");
+  SA_REQUIRE(ld_scores >= E && ld_scores % 4 == 0, SA_EINVAL, "ld_scores = %lld must be >= %lld",
+             (long long)ld_scores, (long long)E);
+  if (block_max) {
+    SA_REQUIRE(aligned16(block_max), SA_EINVAL, "block_max not 16-byte aligned");
+    SA_REQUIRE(ld_block_max >= E / 8, SA_EINVAL, "ld_block_max = %lld must be >= %lld",
+               (long long)ld_block_max, (long long)(E / 8));
+  }
+  SA_REQUIRE(topk && aligned16(topk), SA_EINVAL, "topk NULL or not 16-byte aligned");
+  if (cand) {
+    SA_REQUIRE(aligned16(cand), SA_EINVAL, "cand not 16-byte aligned");
+  } else {
+    SA_REQUIRE(workspace != nullptr && aligned16(workspace), SA_EWORKSPACE,
+               "workspace NULL or misaligned (needed when cand is NULL)");
+    SA_REQUIRE(workspace_bytes >= cand_bytes(q->T), SA_EWORKSPACE,
+               "workspace_bytes = %zu < %zu", workspace_bytes, cand_bytes(q->T));
+    cand = static_cast<int32_t*>(workspace);
+  }
+  sa::SelectArgs a;
+  // num_seqs / compressed_cap are not known here: the per-query n is capped by max_visible.
+  a.m = meta(plan, q, INT32_MAX, q->max_visible);
+  a.scores = scores;
+  a.ld_scores = ld_scores;
+  a.block_max = block_max;
+  a.ld_block_max = ld_block_max;
+  a.cand = cand;
+  a.topk = topk;
+  return hip_status(sa::launch_select(a, (hipStream_t)stream), "select_topk launch");
+}
+
+sa_status sparse_attn_fwd(const sa_plan* plan, const sa_queries* q, const sa_cache* c,
+                          const void* qv, const int32_t* topk, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  sa_status st;
+  if ((st = check_plan(plan)) != SA_OK) return st;
+  if ((st = check_queries(plan, q)) != SA_OK) return st;
+  if ((st = check_cache(plan, q, c, false, true)) != SA_OK) return st;
+  SA_REQUIRE(qv && aligned16(qv), SA_EINVAL, "q NULL or not 16-byte aligned");
+  SA_REQUIRE(topk && aligned16(topk), SA_EINVAL, "topk NULL or not 16-byte aligned");
+  SA_REQUIRE(out && aligned16(out), SA_EINVAL, "out NULL or not 16-byte aligned");
+  SA_REQUIRE(lse == nullptr || aligned16(lse), SA_EINVAL, "lse not 16-byte aligned");
+  sa::AttnArgs a;
+  a.m = meta(plan, q, c->num_seqs, c->compressed_cap);
+  a.q = qv;
+  a.topk = topk;
+  a.latents = c->latents;
+  a.latents_seq_stride = c->latents_seq_stride;
+  a.window = c->window;
+  a.window_seq_stride = c->window_seq_stride;
+  a.window_cap = c->window_cap;
+  a.scale = plan->p.softmax_scale;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(sa::launch_attn(a, (hipStream_t)stream), "sparse_attn_fwd launch");
+}
+
+sa_status sparse_attn_compress(const sa_plan* plan, const void* raw, int64_t raw_group_stride,
+                               const void* gate, int64_t gate_group_stride,
+                               const float* slot_bias, void* out, int64_t out_group_stride,
+                               int64_t G, void* stream) {
+  sa_status st;
+  if ((st = check_plan(plan)) != SA_OK) return st;
+  const int r = plan->p.ratio;
+  SA_REQUIRE(G >= 0, SA_EINVAL, "G = %lld < 0", (long long)G);
+  SA_REQUIRE(raw && aligned16(raw) && out && aligned16(out), SA_EINVAL,
+             "raw / out NULL or not 16-byte aligned");
+  SA_REQUIRE(raw_group_stride >= (int64_t)r * 512 && raw_group_stride % 8 == 0, SA_EINVAL,
+             "raw_group_stride = %lld invalid", (long long)raw_group_stride);
+  SA_REQUIRE(out_group_stride >= 512 && out_group_stride % 8 == 0, SA_EINVAL,
+             "out_group_stride = %lld invalid", (long long)out_group_stride);
+  if (r == 2) {
+    SA_REQUIRE(gate && aligned16(gate) && slot_bias && aligned16(slot_bias), SA_EINVAL,
+               "gate / slot_bias NULL or not 16-byte aligned");
+    SA_REQUIRE(gate_group_stride >= 1024 && gate_group_stride % 8 == 0, SA_EINVAL,
+               "gate_group_stride = %lld invalid", (long long)gate_group_stride);
+  }
+  if (G == 0) return ok();
+  sa::CompressArgs a;
+  a.raw = raw;
+  a.raw_stride = raw_group_stride;
+  a.gate = gate;
+  a.gate_stride = gate_group_stride;
+  a.bias = slot_bias;
+  a.out = out;
+  a.out_stride = out_group_stride;
+  a.G = G;
+  a.ratio = r;
+  return hip_status(sa::launch_compress(a, (hipStream_t)stream), "sparse_attn_compress launch");
+}
+
+}  // extern "C"

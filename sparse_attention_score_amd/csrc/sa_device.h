@@ -1,0 +1,58 @@
+// Device helpers shared by the gfx950 kernels of the sparse-attention library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+
+constexpr int kHeads = 64;
+constexpr int kDim = 512;
+constexpr int kWindow = 128;
+constexpr int kTopK = 512;
+constexpr int kIdxHeads = 16;
+constexpr int kIdxDim = 128;
+constexpr int kBlock = 8;
+constexpr int kCandBlocks = 2048;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+
+// bf16 bits <-> fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// Round fp32 to bf16 (nearest, ties to even). Inputs here are finite.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Four OCP e4m3 codes (one dword) -> four bf16 values in two dwords. Exact: every
+// e4m3 value is a bf16 value, so the fp32 result of the hardware conversion
+// is truncated to its upper half.
+__device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t codes, uint32_t& lo, uint32_t& hi) {
+  auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(codes, false);
+  auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(codes, true);
+  lo = __builtin_amdgcn_perm(__float_as_uint(f01[1]), __float_as_uint(f01[0]), 0x07060302u);
+  hi = __builtin_amdgcn_perm(__float_as_uint(f23[1]), __float_as_uint(f23[0]), 0x07060302u);
+}
+
+// Order-preserving map fp32 -> u32 (larger float -> larger key); -0 maps to +0.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Cross-lane helpers (wave64).
+__device__ __forceinline__ float shfl_xor_f(float v, int m) {
+  return __shfl_xor(v, m, 64);
+}
+
+}  // namespace sa

@@ -1,0 +1,81 @@
+// Kernel argument blocks and launchers (host <-> device boundary inside the library).
+// Every launcher assumes the host-side checks in api.cpp have passed.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+struct QueryMeta {
+  const int32_t* seq_id;
+  const int32_t* pos;
+  int64_t T;
+  int64_t max_visible;     // host hint, caps n
+  int64_t num_seqs;
+  int64_t compressed_cap;  // caps n
+  int32_t ratio;
+};
+
+struct IndexerArgs {
+  const int32_t* seq_id;
+  const int32_t* pos;
+  int64_t T;
+  int64_t max_visible;
+  int64_t num_seqs;
+  int64_t compressed_cap;
+  int32_t ratio;
+  bool fp8;
+  const void* q_idx;        // bf16 [T][16][128]
+  const float* w;           // [T][16]
+  const void* keys;         // bf16 / e4m3 [seq][cap][128]
+  int64_t keys_seq_stride;  // elements
+  const float* scales;      // e4m3 only
+  int64_t scales_seq_stride;
+  float* scores;            // [T][ld_scores]
+  int64_t ld_scores;
+  float* block_max;         // [T][ld_block_max] or null
+  int64_t ld_block_max;
+  int64_t E;                // score row extent: max_visible rounded up to 8
+};
+hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream);
+
+struct SelectArgs {
+  QueryMeta m;
+  const float* scores;
+  int64_t ld_scores;
+  const float* block_max;   // may be null
+  int64_t ld_block_max;
+  int32_t* cand;            // [T][2048]
+  int32_t* topk;            // [T][512]
+};
+hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+
+struct AttnArgs {
+  QueryMeta m;
+  const void* q;            // bf16 [T][64][512]
+  const int32_t* topk;      // [T][512]
+  const void* latents;      // bf16 [seq][cap][512]
+  int64_t latents_seq_stride;
+  const void* window;       // bf16 [seq][wcap][512]
+  int64_t window_seq_stride;
+  int32_t window_cap;
+  float scale;
+  void* out;                // bf16 [T][64][512]
+  float* lse;               // [T][64] or null
+};
+hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
+
+struct CompressArgs {
+  const void* raw;
+  int64_t raw_stride;
+  const void* gate;
+  int64_t gate_stride;
+  const float* bias;        // [ratio][512]
+  void* out;
+  int64_t out_stride;
+  int64_t G;
+  int32_t ratio;
+};
+hipError_t launch_compress(const CompressArgs& a, hipStream_t stream);
+
+}  // namespace sa

@@ -1,0 +1,149 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments on the host before any HIP call.
+
+No call here passes validation: every device pointer below is either NULL or paired
+with an argument the host check refuses, so no kernel is ever launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_score_amd as S
+
+HDR = os.path.join(os.path.dirname(__file__), "..", "include", "sparse_attn.h")
+
+
+def _declared():
+    src = open(HDR).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted(S.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(S.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def _plan(**kw):
+    args = dict(ratio=2, key_dtype="bf16", max_queries=8, max_compressed=4096)
+    args.update(kw)
+    return S.Plan(**args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ratio=3), S.SA_EUNSUPPORTED),
+    (dict(ratio=0), S.SA_EUNSUPPORTED),
+    (dict(num_heads=32), S.SA_EUNSUPPORTED),
+    (dict(topk=256), S.SA_EUNSUPPORTED),
+    (dict(cand_blocks=1024), S.SA_EUNSUPPORTED),
+    (dict(max_queries=0), S.SA_EINVAL),
+    (dict(max_compressed=-1), S.SA_EINVAL),
+    (dict(max_compressed=524289), S.SA_EUNSUPPORTED),
+    (dict(softmax_scale=float("nan")), S.SA_EINVAL),
+    (dict(softmax_scale=0.0), S.SA_EINVAL),
+])
+def test_plan_rejects(kw, status):
+    with pytest.raises(S.SparseAttnError) as ei:
+        _plan(**kw)
+    assert ei.value.status == status
+    assert S.lib.sparse_attn_last_error()
+
+
+def test_plan_workspace_and_last_error_reset():
+    p = _plan(max_queries=100)
+    assert p.workspace_bytes == 100 * 2048 * 4
+    assert S.lib.sparse_attn_last_error() == b""
+
+
+def _q(T=4, max_visible=100, seq=0x1000, pos=0x2000):
+    return S.sa_queries(T=T, seq_id=seq, pos=pos, max_visible=max_visible)
+
+
+def _c(**kw):
+    c = S.sa_cache(num_seqs=4, compressed_cap=1000, latents=0x10000, latents_seq_stride=1000 * 512,
+                   window=0x20000, window_seq_stride=128 * 512, window_cap=128,
+                   idx_keys=0x30000, idx_keys_seq_stride=1000 * 128, idx_scales=None,
+                   idx_scales_seq_stride=0)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _indexer(p, q, c, qi=0x40000, w=0x50000, scores=0x60000, ld=104, bm=None, ldb=0):
+    return S.lib.indexer_score(p.handle, ctypes.byref(q), ctypes.byref(c), qi, w, scores, ld, bm, ldb, None)
+
+
+@pytest.mark.parametrize("case", [
+    "T0", "Tbig", "seq_null", "maxvis_big", "cap_small", "keys_null", "keys_misaligned",
+    "qidx_null", "scores_null", "ld_small", "ldb_small", "fp8_no_scales", "stride_small",
+])
+def test_indexer_rejects(case):
+    p = _plan()
+    q, c = _q(), _c()
+    kw = {}
+    if case == "T0": q.T = 0
+    if case == "Tbig": q.T = 9
+    if case == "seq_null": q.seq_id = None
+    if case == "maxvis_big": q.max_visible = 5000
+    if case == "cap_small": c.compressed_cap = 50
+    if case == "keys_null": c.idx_keys = None
+    if case == "keys_misaligned": c.idx_keys = 0x30008
+    if case == "qidx_null": kw["qi"] = None
+    if case == "scores_null": kw["scores"] = None
+    if case == "ld_small": kw["ld"] = 100   # max_visible 100 -> rows of 104
+    if case == "ldb_small": kw.update(bm=0x70000, ldb=12)
+    if case == "stride_small": c.idx_keys_seq_stride = 999 * 128
+    if case == "fp8_no_scales":
+        p = _plan(key_dtype="fp8")
+    st = _indexer(p, q, c, **kw)
+    assert st == S.SA_EINVAL, (case, st, S.lib.sparse_attn_last_error())
+    assert S.lib.sparse_attn_last_error()
+
+
+def test_select_rejects():
+    p = _plan()
+    q = _q()
+    lib = S.lib
+    # topk NULL
+    assert lib.select_topk(p.handle, ctypes.byref(q), 0x60000, 104, None, 0, 0x80000, None,
+                           0x90000, 1 << 20, None) == S.SA_EINVAL
+    # no cand and no workspace
+    assert lib.select_topk(p.handle, ctypes.byref(q), 0x60000, 104, None, 0, None, 0xA0000,
+                           None, 0, None) == S.SA_EWORKSPACE
+    # workspace too small for T queries
+    assert lib.select_topk(p.handle, ctypes.byref(q), 0x60000, 104, None, 0, None, 0xA0000,
+                           0x90000, 4 * 2048 * 4 - 1, None) == S.SA_EWORKSPACE
+    # ld_scores below max_visible
+    assert lib.select_topk(p.handle, ctypes.byref(q), 0x60000, 96, None, 0, 0x80000, 0xA0000,
+                           0x90000, 1 << 20, None) == S.SA_EINVAL
+
+
+def test_attn_rejects():
+    p = _plan()
+    q = _q()
+    lib = S.lib
+    for c in (_c(window_cap=127), _c(latents=None), _c(window=None), _c(latents_seq_stride=512 * 999)):
+        assert lib.sparse_attn_fwd(p.handle, ctypes.byref(q), ctypes.byref(c), 0x40000, 0x50000,
+                                   0x60000, None, None, 0, None) == S.SA_EINVAL
+    c = _c()
+    assert lib.sparse_attn_fwd(p.handle, ctypes.byref(q), ctypes.byref(c), None, 0x50000, 0x60000,
+                               None, None, 0, None) == S.SA_EINVAL
+    assert lib.sparse_attn_fwd(p.handle, ctypes.byref(q), ctypes.byref(c), 0x40000, 0x50000, 0x60000,
+                               0x70004, None, 0, None) == S.SA_EINVAL
+
+
+def test_compress_rejects():
+    p = _plan()
+    lib = S.lib
+    assert lib.sparse_attn_compress(p.handle, None, 1024, 0x1000, 1024, 0x2000, 0x3000, 512, 4, None) == S.SA_EINVAL
+    assert lib.sparse_attn_compress(p.handle, 0x1000, 1000, 0x1000, 1024, 0x2000, 0x3000, 512, 4, None) == S.SA_EINVAL
+    assert lib.sparse_attn_compress(p.handle, 0x1000, 1024, None, 1024, 0x2000, 0x3000, 512, 4, None) == S.SA_EINVAL
+    assert lib.sparse_attn_compress(p.handle, 0x1000, 1024, 0x1000, 1024, 0x2000, 0x3000, 512, -1, None) == S.SA_EINVAL
+    assert lib.sparse_attn_compress(None, 0x1000, 1024, 0x1000, 1024, 0x2000, 0x3000, 512, 4, None) == S.SA_EINVAL

@@ -1,0 +1,257 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on small and ragged
+batches that span several tiles, per stage and end to end, plus edge cases."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import oracle as O
+from parity_util import (LSE_TOL, SCORE_REL, bf16_dev_to_f64, bf16_ulp, check_index_row,
+                         check_outputs, kth_score)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import sparse_attention_score_amd  # noqa: F401  (raises if the library is not built)
+
+
+def _run(wl, stages=("compress", "index", "select", "attend")):
+    from sparse_attention_score_amd.step import DeviceBatch
+    print(f"[case] {wl.name} T={wl.T} B={wl.B} ratio={wl.ratio} keys={wl.key_dtype} "
+          f"n={wl.visible().min()}..{wl.visible().max()}", flush=True)
+    d = DeviceBatch(wl)
+    for s in stages:
+        getattr(d, s)()
+    torch.cuda.synchronize()
+    return d
+
+
+def _scores_check(d, res, wl, t):
+    n = int(wl.visible()[t])
+    got = d.scores[t].cpu().numpy()
+    I = res.scores[t]
+    if n:
+        Ik = kth_score(I, 512)
+        tol = SCORE_REL * np.maximum(np.abs(I), abs(Ik))
+        err = np.abs(got[:n].astype(np.float64) - I)
+        assert np.all(err <= tol + 1e-30), f"t={t}: score err {err.max():.3g} > tol at j={err.argmax()}"
+    assert np.all(np.isneginf(got[n:d.E])), f"t={t}: masked scores not -inf"
+    # block maxima equal the max of the GPU's own scores, bit for bit
+    bm = d.block_max[t].cpu().numpy()
+    nb = -(-n // 8)
+    for b in range(nb):
+        assert bm[b] == got[8 * b:min(n, 8 * b + 8)].max(), f"t={t} block {b}"
+    assert np.all(np.isneginf(bm[nb:d.E // 8]))
+
+
+def _e2e(wl, check_scores=True):
+    d = _run(wl)
+    res = O.run(wl)
+    topk = d.topk.cpu().numpy()
+    cand = d.cand.cpu().numpy()
+    o_gpu = bf16_dev_to_f64(d.out)
+    lse_gpu = d.lse.cpu().numpy()
+    idx_gpu = [topk[t][topk[t] >= 0] for t in range(wl.T)]
+    res2 = O.run(wl, idx_override=idx_gpu)   # oracle attention on the GPU's selection
+    for t in range(wl.T):
+        if check_scores:
+            _scores_check(d, res, wl, t)
+        check_index_row(topk[t], res.idx[t], res.scores[t], 512, f"{wl.name} t={t} topk")
+        n = int(wl.visible()[t])
+        if n:
+            M = O.block_scores(res.scores[t])
+            check_index_row(cand[t], res.cand[t], M, 2048, f"{wl.name} t={t} cand")
+        check_outputs(o_gpu[t], res2.o[t], f"{wl.name} t={t} out")
+        assert np.abs(lse_gpu[t] - res2.lse[t]).max() <= LSE_TOL, f"t={t} lse"
+    return d, res
+
+
+# ------------------------------------------------------------------ end to end, small
+
+def test_decode_small_bf16():
+    _e2e(W.make("decode-b4-ctx2k"))
+
+
+def test_decode_ragged_fp8_mixed_positions():
+    wl = W.make_decode(B=3, n_raw=[3001, 1022, 20001], ratio=2, key_dtype="fp8",
+                       name="ragged-fp8", with_compress=False, seed=3)
+    _e2e(wl)
+
+
+@pytest.mark.parametrize("kd", ["bf16", "fp8"])
+def test_decode_candidate_stage_prunes(kd):
+    # n = 20003 -> 2501 blocks, 2048 kept; the last block holds 3 positions
+    wl = W.make_decode(B=2, n_raw=40006, ratio=2, key_dtype=kd, name=f"prune-{kd}", seed=5)
+    d, res = _e2e(wl)
+    cand = d.cand.cpu().numpy()
+    assert np.all(cand >= 0)  # exactly 2048 kept
+
+
+def test_decode_tiny_contexts():
+    # n = 0 (window only), 1, 1, 8, 65 visible compressed latents
+    wl = W.make_decode(B=5, n_raw=[1, 2, 3, 17, 130], ratio=2, key_dtype="bf16", name="tiny",
+                       with_compress=False, seed=7)
+    d, res = _e2e(wl)
+    assert np.all(d.topk[0].cpu().numpy() == -1)
+
+
+def test_decode_uniform_with_compressor_ratio2_small():
+    wl = W.make_decode(B=6, n_raw=1234, ratio=2, key_dtype="fp8", name="compress-step", seed=9)
+    d, res = _e2e(wl)
+    # the compressed row written this step matches the oracle within one bf16 ulp
+    n = 617
+    got = d.C[:, n - 1].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    for b in range(6):
+        ref = res.C_new[b][0]
+        g = O.bf16_to_f64(got[b])
+        assert np.all(np.abs(g - ref) <= bf16_ulp(ref)), b
+
+
+def test_prefill_small_ratio1():
+    wl = W.make_prefill(T=200, offset=900, ratio=1, key_dtype="bf16", name="prefill-small", seed=11)
+    _e2e(wl)
+
+
+def test_prefill_prunes_ratio1():
+    wl = W.make_prefill(T=40, offset=20000, ratio=1, key_dtype="bf16", name="prefill-prune", seed=12)
+    _e2e(wl)
+
+
+def test_prefill_fp8_ratio2():
+    wl = W.make_prefill(T=70, offset=3001, ratio=2, key_dtype="fp8", name="prefill-fp8-r2", seed=13)
+    _e2e(wl)
+
+
+# ------------------------------------------------------------------ stage isolated
+
+def test_select_exact_on_given_scores_with_ties():
+    """Selection fed fixed fp32 scores (many exact ties) must equal the oracle's selection on
+    the same fp32 values exactly: this is integer work."""
+    from sparse_attention_score_amd.step import DeviceBatch
+    rng = np.random.default_rng(21)
+    wl = W.make_decode(B=4, n_raw=[2 * 20003, 2 * 9000, 2 * 700, 2 * 60000], ratio=2,
+                       name="select-ties", with_compress=False, seed=21)
+    d = DeviceBatch(wl)
+    n = wl.visible()
+    S = np.full((wl.T, d.scores.shape[1]), -np.inf, np.float32)
+    for t in range(wl.T):
+        S[t, :n[t]] = rng.integers(0, 50, n[t]).astype(np.float32) * np.float32(0.25)
+    d.scores.copy_(torch.from_numpy(S))
+    for use_bm in (False, True):
+        if use_bm:
+            bm = np.full(d.block_max.shape, -np.inf, np.float32)
+            for t in range(wl.T):
+                bm[t, :-(-n[t] // 8)] = O.block_scores(S[t, :n[t]].astype(np.float64))
+            d.block_max.copy_(torch.from_numpy(bm))
+        d.select(use_block_max=use_bm)
+        torch.cuda.synchronize()
+        topk, cand = d.topk.cpu().numpy(), d.cand.cpu().numpy()
+        for t in range(wl.T):
+            c_ref, i_ref = O.select(S[t, :n[t]].astype(np.float64))
+            assert np.array_equal(topk[t][topk[t] >= 0], i_ref), t
+            assert np.array_equal(cand[t][cand[t] >= 0], c_ref), t
+
+
+def test_select_all_ties_takes_lowest():
+    from sparse_attention_score_amd.step import DeviceBatch
+    wl = W.make_decode(B=2, n_raw=[2 * 30000, 2 * 300], ratio=2, name="zero-w", with_compress=False, seed=2)
+    wl.w[:] = 0.0
+    d = DeviceBatch(wl)
+    d.index()
+    d.select()
+    torch.cuda.synchronize()
+    assert np.all(d.scores[0, :30000].cpu().numpy() == 0.0)
+    assert d.topk[0].cpu().numpy().tolist() == list(range(512))
+    assert d.cand[0].cpu().numpy().tolist() == list(range(2048))
+    assert d.topk[1].cpu().numpy().tolist() == list(range(300)) + [-1] * 212
+
+
+def test_attention_stage_isolated_and_permutation():
+    """K4 fed the oracle's selection, then the same selection reversed (order must not matter)."""
+    wl = W.make_decode(B=3, n_raw=[2 * 5000, 2 * 40, 2 * 3000 + 1], ratio=2, key_dtype="bf16",
+                       name="attn-iso", with_compress=False, seed=31)
+    res = O.run(wl)
+    from sparse_attention_score_amd.step import DeviceBatch
+    d = DeviceBatch(wl)
+    tk = np.full((wl.T, 512), -1, np.int32)
+    for t in range(wl.T):
+        tk[t, :len(res.idx[t])] = res.idx[t]
+    for order in ("asc", "rev"):
+        tt = tk.copy()
+        if order == "rev":
+            for t in range(wl.T):
+                m = int((tt[t] >= 0).sum())
+                tt[t, :m] = tt[t, :m][::-1]
+        d.attend(topk=torch.from_numpy(tt).cuda())
+        torch.cuda.synchronize()
+        o = bf16_dev_to_f64(d.out)
+        lse = d.lse.cpu().numpy()
+        for t in range(wl.T):
+            check_outputs(o[t], res.o[t], f"iso t={t} {order}")
+            assert np.abs(lse[t] - res.lse[t]).max() <= LSE_TOL
+
+
+def test_attention_window_edges_and_dominant_key():
+    """Make one window row dominate every head (+~30 logit); it must be attended when it
+    is at p-127 and not when it is at p-128 (window_cap 256 so the rows do not alias)."""
+    from sparse_attention_score_amd.step import DeviceBatch
+    B = 2
+    wl = W.make_decode(B=B, n_raw=1000, ratio=2, key_dtype="bf16", name="edges",
+                       with_compress=False, wcap=256, seed=41)
+    p = 999
+    rng = np.random.default_rng(41)
+    for b, u in enumerate((p - 127, p - 128)):
+        v = np.zeros(512)
+        v[:8] = 4.0
+        wl.R[b, u % 256] = O.f64_to_bf16(v)
+        qv = np.zeros((64, 512))
+        qv[:, :8] = 30.0 / (O.SCALE * 4.0 * 8)
+        wl.q[b] = O.f64_to_bf16(qv)
+    res = O.run(wl)
+    d = _run(wl)
+    o = bf16_dev_to_f64(d.out)
+    for b in range(B):
+        check_outputs(o[b], res.o[b], f"edge b={b}")
+    assert np.allclose(o[0][:, :8], 4.0, atol=1e-2)        # dominated by the p-127 row
+    assert not np.allclose(o[1][:, :8], 4.0, atol=0.5)     # p-128 row is outside the window
+
+
+def test_compress_standalone_one_ulp():
+    from sparse_attention_score_amd import Plan, sparse_attn_compress
+    from sparse_attention_score_amd.step import to_device_bf16
+    X, Z, beta = W.make_compress_input(B=3, n_raw=2 * 777, seed=51)
+    big = O.f64_to_bf16(np.full(512, 60.0))
+    Z[0, 0], Z[0, 1] = big, big ^ 0x8000       # gate gap of +120: slot 0 only
+    Z[0, 2], Z[0, 3] = big ^ 0x8000, big       # gap of -120: slot 1 only
+    plan = Plan(ratio=2, max_queries=1, max_compressed=1)
+    Xd, Zd = to_device_bf16(X), to_device_bf16(Z)
+    bd = torch.from_numpy(beta).cuda()
+    out = torch.empty((3, 777, 512), dtype=torch.bfloat16, device="cuda")
+    sparse_attn_compress(plan, Xd, 1024, Zd, 1024, bd, out, 512, 3 * 777)
+    torch.cuda.synchronize()
+    got = bf16_dev_to_f64(out).reshape(-1, 512)
+    ref = O.compress(O.bf16_to_f64(X).reshape(-1, 2, 512), O.bf16_to_f64(Z).reshape(-1, 2, 512), beta)
+    err = np.abs(got - ref)
+    ulp = bf16_ulp(ref)
+    assert np.all(err <= ulp), f"max err/ulp {np.max(err / ulp):.3f}"
+    # ratio 1 is the identity copy
+    plan1 = Plan(ratio=1, max_queries=1, max_compressed=1)
+    out1 = torch.empty((3 * 777, 512), dtype=torch.bfloat16, device="cuda")
+    sparse_attn_compress(plan1, Xd, 512, None, 0, None, out1, 512, 3 * 777)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16).cpu(), Xd.reshape(-1, 512).view(torch.int16).cpu())
+
+
+def test_deterministic_bitwise():
+    wl = W.make_decode(B=3, n_raw=2 * 20003, ratio=2, key_dtype="fp8", name="determinism", seed=61)
+    d = _run(wl)
+    a = (d.scores.clone(), d.topk.clone(), d.out.clone(), d.lse.clone())
+    d.run()
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], d.scores) and torch.equal(a[1], d.topk)
+    assert torch.equal(a[2].view(torch.int16), d.out.view(torch.int16)) and torch.equal(a[3], d.lse)
