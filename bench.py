@@ -1,0 +1,236 @@
+"""Throughput of the two-tier sparse-attention hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: compressor for the group each
+query completes, indexer scores, candidate-block + top-512 selection, gather attention.
+Default workload: decode, 128 sequences at 131072 raw tokens (65536 compressed latents
+at ratio 2), fp8-e4m3 index keys. Inputs are synthetic (seeded) and resident in HBM
+before timing starts.
+
+Prints one JSON line with queries/s, the indexer kernel's HBM roofline fraction (HIP
+events on the launch stream), the step's fraction of HBM, a prefill chunk's fraction of
+bf16 MFMA peak, and the fp64 CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-prefill] [--no-cpu-baseline] [--profile]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+BF16_PEAK = 2.5e15         # flop/s, MI355X dense bf16 MFMA
+IDX_BYTES_PER_QUERY_FIXED = 16 * 128 * 2 + 16 * 4        # index query + head weights
+LATENT_ROW = 512 * 2
+
+
+def key_row_bytes(key_dtype: str) -> int:
+    return 128 + 4 if key_dtype == "fp8" else 256
+
+
+def indexer_bytes(wl) -> float:
+    """Algorithmic bytes of one indexer launch: every visible index key (and its fp8 row
+    scale) of every query, plus the index queries and weights."""
+    n = wl.visible().astype(np.float64)
+    return float((n * key_row_bytes(wl.key_dtype)).sum() + wl.T * IDX_BYTES_PER_QUERY_FIXED)
+
+
+def step_bytes(wl) -> float:
+    """Algorithmic bytes of one whole step: index keys, selected latents, window rows,
+    q, output, index query/weights, selected ids (materialised scores excluded)."""
+    n = wl.visible().astype(np.float64)
+    k = np.minimum(512, n)
+    win = np.minimum(128, wl.pos.astype(np.float64) + 1)
+    per_q = (n * key_row_bytes(wl.key_dtype) + k * LATENT_ROW + win * LATENT_ROW
+             + 64 * 512 * 2 * 2 + IDX_BYTES_PER_QUERY_FIXED + 512 * 4)
+    groups = len(wl.compress_groups())
+    return float(per_q.sum() + groups * (2 * 2 * 512 * 2 + 512 * 2) + 2 * 512 * 4)
+
+
+def step_flops(wl) -> tuple:
+    n = wl.visible().astype(np.float64)
+    k = np.minimum(512, n)
+    win = np.minimum(128, wl.pos.astype(np.float64) + 1)
+    idx = float((n * 16 * 128 * 2).sum())
+    attn = float((64 * (k + win) * 512 * 4).sum())
+    return idx, attn
+
+
+class Timer:
+    """HIP events recorded on the launch stream around each stage of every timed step."""
+
+    def __init__(self, torch, names):
+        self.torch = torch
+        self.names = names
+        self.ev = []
+
+    def step(self, fns):
+        t = self.torch
+        evs = [t.cuda.Event(enable_timing=True)]
+        evs[0].record()
+        for f in fns:
+            f()
+            e = t.cuda.Event(enable_timing=True)
+            e.record()
+            evs.append(e)
+        self.ev.append(evs)
+
+    def mean_ms(self):
+        out = {n: 0.0 for n in self.names}
+        for evs in self.ev:
+            for i, n in enumerate(self.names):
+                out[n] += evs[i].elapsed_time(evs[i + 1])
+        return {n: v / max(1, len(self.ev)) for n, v in out.items()}
+
+
+def run_batch(torch, d, steps, warmup):
+    stages = ["compress", "indexer", "select", "attention"]
+    fns = [d.compress, d.index, d.select, d.attend]
+    for _ in range(warmup):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    timer = Timer(torch, stages)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        timer.step(fns)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    return (t1 - t0) / steps, timer.mean_ms()
+
+
+def cpu_baseline(wl, budget_s=20.0, max_queries=None):
+    """The fp64 oracle, as it stands, over the first queries of the batch until the time
+    budget is spent (at least one query). Returns queries/s and the sample description."""
+    from oracle import oracle as O
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max([i.get("num_threads", 1) for i in info if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = 1
+    t0 = time.perf_counter()
+    C_new = O.step_compress(wl)
+    done = 0
+    keys = {}
+    limit = wl.T if max_queries is None else min(wl.T, max_queries)
+    for t in range(limit):
+        b = int(wl.seq[t])
+        if b not in keys:
+            nn = int(wl.visible()[wl.seq == b].max())
+            keys = {b: O.index_keys_f64(wl.KI[b, :nn], None if wl.KS is None else wl.KS[b, :nn])}
+        O.run_query(wl, t, keys[b], C_new)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return done / dt, done, dt, cores
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="decode-b128-ctx128k-fp8")
+    ap.add_argument("--prefill-workload", default="prefill-4096-at-61440")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--profile", action="store_true", help="timed steps only (for rocprofv3)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(batch- or context-sharding is a design note only). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    from sparse_attention_score_amd.step import DeviceBatch
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    torch.cuda.set_device(0)
+    log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)  # noqa: E731
+
+    t0 = time.perf_counter()
+    wl = W.make(args.workload)
+    log(f"generated {args.workload} in {time.perf_counter() - t0:.1f}s")
+    d = DeviceBatch(wl)
+    torch.cuda.synchronize()
+    log("uploaded")
+    sec_per_step, stage_ms = run_batch(torch, d, args.steps, args.warmup)
+    log(f"decode: {sec_per_step * 1e3:.3f} ms/step, stages {stage_ms}")
+
+    idx_bytes = indexer_bytes(wl)
+    idx_s = stage_ms["indexer"] * 1e-3
+    sbytes = step_bytes(wl)
+    result = {
+        "metric": "sparse-attn decode queries/s at 128K ctx",
+        "value": wl.T / sec_per_step,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec_per_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": int(wl.B), "queries": int(wl.T),
+                   "raw_context": int(wl.pos.max()) + 1, "compressed": int(wl.visible().max()),
+                   "ratio": int(wl.ratio), "index_keys": "fp8-e4m3" if wl.key_dtype == "fp8" else "bf16",
+                   "heads": 64, "latent": 512, "window": 128, "topk": 512, "cand_blocks": 2048,
+                   "block": 8, "index_heads": 16, "index_dim": 128},
+        "roofline": {"kernel": "indexer_score (S1)", "bound": "hbm",
+                     "achieved": idx_bytes / idx_s / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                     "frac": idx_bytes / idx_s / HBM_PEAK, "traffic": None,
+                     "algorithmic_bytes_per_launch": idx_bytes, "avg_launch_ms": stage_ms["indexer"]},
+        "step": {"stage_ms": stage_ms, "algorithmic_bytes": sbytes,
+                 "hbm_frac": sbytes / sec_per_step / HBM_PEAK,
+                 "tokens_per_s": wl.T / sec_per_step},
+    }
+    del d
+    torch.cuda.empty_cache()
+
+    if not args.no_prefill and not args.profile:
+        t0 = time.perf_counter()
+        wp = W.make(args.prefill_workload)
+        dp = DeviceBatch(wp)
+        torch.cuda.synchronize()
+        log(f"prefill inputs ready in {time.perf_counter() - t0:.1f}s")
+        sp, sms = run_batch(torch, dp, max(3, args.steps // 2), args.warmup)
+        fi, fa = step_flops(wp)
+        result["prefill"] = {
+            "workload": args.prefill_workload, "ms_per_chunk": sp * 1e3, "tokens_per_s": wp.T / sp,
+            "stage_ms": sms, "algorithmic_tflop": (fi + fa) / 1e12,
+            "mfma_frac": (fi + fa) / sp / BF16_PEAK,
+            "indexer_mfma_frac": fi / (sms["indexer"] * 1e-3) / BF16_PEAK,
+            "attention_mfma_frac": fa / (sms["attention"] * 1e-3) / BF16_PEAK,
+        }
+        log(f"prefill: {sp * 1e3:.3f} ms/chunk, stages {sms}")
+        del dp, wp
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline and not args.profile:
+        qps, done, dt, cores = cpu_baseline(wl, args.cpu_budget)
+        result["cpu_baseline"] = {
+            "value": qps, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {done} of the {wl.T} queries of {args.workload}, whole path "
+                      f"(compressor, indexer, selection, attention) in fp64, {dt:.1f}s"}
+        log(f"cpu oracle: {done} queries in {dt:.1f}s on {cores} BLAS threads")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -169,10 +169,9 @@ def block_scores(I: np.ndarray, blk: int = BLOCK) -> np.ndarray:
     """Score of each block of `blk` consecutive positions: the max of its visible scores."""
     n = I.shape[0]
     nb = -(-n // blk)
-    M = np.full(nb, -np.inf)
-    for b in range(nb):
-        M[b] = I[b * blk:min(n, b * blk + blk)].max()
-    return M
+    padded = np.full(nb * blk, -np.inf)      # positions past n are not visible
+    padded[:n] = I
+    return padded.reshape(nb, blk).max(axis=1)
 
 
 def order_desc(values: np.ndarray, ids: np.ndarray) -> np.ndarray:
@@ -235,13 +234,15 @@ class Result:
         self.C_new = {}               # sequence -> fp64 compressed latent written this step
 
 
-def compressed_store(wl, b: int, n: int, C_new_bits: Optional[np.ndarray] = None) -> np.ndarray:
-    """fp64 compressed store rows 0..n-1 of sequence b; the row written this step
-    (if any) replaces row n-1."""
-    C = bf16_to_f64(wl.C[b, :n])
+def compressed_rows(wl, b: int, n: int, rows: np.ndarray,
+                    C_new_bits: Optional[np.ndarray] = None) -> np.ndarray:
+    """fp64 values of compressed rows `rows` (< n) of sequence b; the row written this
+    step (if any) stands in for row n-1."""
+    rows = np.asarray(rows, np.int64)
+    X = bf16_to_f64(wl.C[b, rows])
     if C_new_bits is not None and n > 0:
-        C[n - 1] = bf16_to_f64(C_new_bits)
-    return C
+        X[rows == n - 1] = bf16_to_f64(C_new_bits)
+    return X
 
 
 def step_compress(wl) -> dict:
@@ -273,7 +274,7 @@ def run_query(wl, t: int, keys_f64: Optional[np.ndarray] = None, C_new: Optional
     new_bits = None
     if C_new is not None and b in C_new and n > 0:
         new_bits = C_new[b][1]
-    rows = compressed_store(wl, b, n, new_bits)[use] if use.size else np.zeros((0, DIM))
+    rows = compressed_rows(wl, b, n, use, new_bits) if use.size else np.zeros((0, DIM))
     win = window_positions(p)
     Xw = bf16_to_f64(wl.R[b, win % wl.wcap])
     X = np.concatenate([rows, Xw], axis=0)

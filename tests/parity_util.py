@@ -61,3 +61,10 @@ def bf16_dev_to_f64(t) -> np.ndarray:
 def bf16_ulp(ref: np.ndarray) -> np.ndarray:
     """One bf16 ulp at each value of ref (8 significant bits)."""
     return 2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+
+
+def compress_tol(ref: np.ndarray, x0: np.ndarray, x1: np.ndarray) -> np.ndarray:
+    """Error bound of the fp32 compressor after rounding to bf16: one bf16 ulp of the result
+    plus 16 fp32 unit roundoffs of the slot magnitudes (the gate exp, reciprocal and blend
+    are evaluated in fp32, so near cancellation the absolute error scales with |x|)."""
+    return bf16_ulp(ref) + 2.0 ** -20 * (np.abs(x0) + np.abs(x1))

@@ -9,7 +9,7 @@ import torch
 import workloads as W
 from oracle import oracle as O
 from parity_util import (LSE_TOL, SCORE_REL, bf16_dev_to_f64, bf16_ulp, check_index_row,
-                         check_outputs, kth_score)
+                         check_outputs, compress_tol, kth_score)
 
 pytestmark = pytest.mark.gpu
 
@@ -109,7 +109,8 @@ def test_decode_uniform_with_compressor_ratio2_small():
     for b in range(6):
         ref = res.C_new[b][0]
         g = O.bf16_to_f64(got[b])
-        assert np.all(np.abs(g - ref) <= bf16_ulp(ref)), b
+        x = O.bf16_to_f64(wl.Xp[b])
+        assert np.all(np.abs(g - ref) <= compress_tol(ref, x[0], x[1])), b
 
 
 def test_prefill_small_ratio1():
@@ -237,14 +238,18 @@ def test_compress_standalone_one_ulp():
     got = bf16_dev_to_f64(out).reshape(-1, 512)
     ref = O.compress(O.bf16_to_f64(X).reshape(-1, 2, 512), O.bf16_to_f64(Z).reshape(-1, 2, 512), beta)
     err = np.abs(got - ref)
-    ulp = bf16_ulp(ref)
-    assert np.all(err <= ulp), f"max err/ulp {np.max(err / ulp):.3f}"
+    xs = O.bf16_to_f64(X).reshape(-1, 2, 512)
+    tol = compress_tol(ref, xs[:, 0], xs[:, 1])
+    assert np.all(err <= tol), f"max err/tol {np.max(err / tol):.3f}"
+    # away from cancellation the result is within one bf16 ulp
+    far = np.abs(ref) > 0.25 * (np.abs(xs[:, 0]) + np.abs(xs[:, 1]))
+    assert np.all(err[far] <= bf16_ulp(ref[far]))
     # ratio 1 is the identity copy
     plan1 = Plan(ratio=1, max_queries=1, max_compressed=1)
     out1 = torch.empty((3 * 777, 512), dtype=torch.bfloat16, device="cuda")
     sparse_attn_compress(plan1, Xd, 512, None, 0, None, out1, 512, 3 * 777)
     torch.cuda.synchronize()
-    assert torch.equal(out1.view(torch.int16).cpu(), Xd.reshape(-1, 512).view(torch.int16).cpu())
+    assert torch.equal(out1.view(torch.int16).cpu(), Xd.reshape(-1, 512)[:3 * 777].view(torch.int16).cpu())
 
 
 def test_deterministic_bitwise():
