@@ -7,31 +7,36 @@
 // Flash" Miles docs, section 1 Model Introduction; one softmax over both tiers, recipe
 // Overview, two-tier sparse attention bullet).
 //
-// One work-group per query; wave w owns heads 16w..16w+15. Keys are gathered 32 at a time
-// into an LDS tile (double-buffered through registers) that all four waves share.
-//   S^T = K Q^T : v_mfma_f32_16x16x32_bf16, A = 16 keys from LDS, B = the wave's 16 heads
-//                 (kept in registers), 16 k-steps over the 512 dims.
-//   O^T += V^T P^T : A = V^T, built from LDS rows with byte permutes (8 keys x 1 dim per
-//                 lane), B = P^T taken straight from the S^T accumulators.
-// In both results a lane's column is its head, so the online-softmax max, sum and
-// rescale are per lane; only the tile max needs two cross-lane steps.
+// One work-group (8 waves) per query. Keys are gathered 32 per step into an LDS tile
+// (rows staged through registers one step ahead, two LDS buffers).
+//   scores: wave (hg, kh) computes S^T for keys 16kh..16kh+15 of the step and heads
+//           16hg..16hg+15 with v_mfma_f32_16x16x32_bf16 (A = keys from LDS, B = the
+//           wave's query heads held in registers, 16 k-steps over the 512 dims).
+//   softmax: per head, online in the log2 domain; the two key halves exchange their
+//           tile maxima through LDS; P (bf16) and the rescale factors go to LDS.
+//   values: wave w owns output dims 64w..64w+63 for all 64 heads: O^T += V^T P^T with
+//           A = V^T built from LDS rows by byte permutes (8 keys x 1 dim per lane) and
+//           B = P^T read from LDS. Each value element is read from LDS once per step.
 #include "sa_device.h"
 #include "sa_launch.h"
 
 namespace sa {
 namespace {
 
-constexpr int kAW = 4;              // waves, 16 heads each
+constexpr int kAW = 8;              // waves
 constexpr int kAThreads = 64 * kAW;
 constexpr int kKT = 32;             // keys per step
-constexpr int kRow = kDim * 2 + 16; // padded LDS row bytes
+constexpr int kRow = kDim * 2 + 16; // padded LDS row bytes (bank offset 4 dwords per row)
 constexpr int kMaxKeys = kTopK + kWindow;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 struct AttnShared {
-  uint8_t tile[2][kKT * kRow];
-  const uint16_t* rows[kMaxKeys];
+  uint8_t tile[2][kKT * kRow];         // 66,560 B
+  u32x4 P[4][64];                      // P^T B operands: [head group][lane], 8 bf16 each
+  float tmax[2][kHeads];               // per key half: tile max of each head
+  float alpha[kHeads];                 // rescale factor of each head this step
+  const uint16_t* rows[kMaxKeys];      // global row of every key slot
   int wave_cnt[kAW];
 };
 
@@ -41,8 +46,16 @@ __device__ __forceinline__ uint32_t perm_lo(uint32_t hi_src, uint32_t lo_src) {
 __device__ __forceinline__ uint32_t perm_hi(uint32_t hi_src, uint32_t lo_src) {
   return __builtin_amdgcn_perm(hi_src, lo_src, 0x07060302u);  // (hi16 of lo_src, hi16 of hi_src)
 }
+__device__ __forceinline__ float max_xor16(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
-__global__ __launch_bounds__(kAThreads) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAThreads, 2) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) AttnShared sh;
   const int t = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -58,12 +71,12 @@ __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnArgs a) {
   }
 
   // ---- key list: selected latents in topk order, then the window ----
-  int nsel = 0, m = 0;
+  int m = 0;
   if (valid_q) {
     const int32_t* tk = a.topk + (int64_t)t * kTopK;
-    const int j0 = tk[2 * tid], j1 = tk[2 * tid + 1];
-    const bool v0 = j0 >= 0 && j0 < n, v1 = j1 >= 0 && j1 < n;
-    int cnt = (int)v0 + (int)v1;
+    const int j = tk[tid];  // 512 threads, one entry each
+    const bool v = j >= 0 && j < n;
+    const int cnt = (int)v;
     int incl = cnt;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -72,15 +85,13 @@ __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnArgs a) {
     }
     if (lane == 63) sh.wave_cnt[wave] = incl;
     __syncthreads();
-    int before = 0;
+    int nsel = 0, before = 0;
     for (int w = 0; w < kAW; ++w) {
       nsel += sh.wave_cnt[w];
       before += (w < wave) ? sh.wave_cnt[w] : 0;
     }
-    int off = before + incl - cnt;
     const uint16_t* lat = reinterpret_cast<const uint16_t*>(a.latents) + (int64_t)seq * a.latents_seq_stride;
-    if (v0) sh.rows[off++] = lat + (int64_t)j0 * kDim;
-    if (v1) sh.rows[off] = lat + (int64_t)j1 * kDim;
+    if (v) sh.rows[before + incl - cnt] = lat + (int64_t)j * kDim;
     const int u0 = p - kWindow + 1 > 0 ? p - kWindow + 1 : 0;
     const int nwin = p - u0 + 1;
     const uint16_t* win = reinterpret_cast<const uint16_t*>(a.window) + (int64_t)seq * a.window_seq_stride;
@@ -89,154 +100,176 @@ __global__ __launch_bounds__(kAThreads) void attn_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  const int head = wave * 16 + c;
-  uint16_t* outp = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * kHeads + head) * kDim;
   if (m == 0) {  // invalid query: zero output, lse = -inf
-    for (int i = g; i < kDim / 8; i += 4)
-      *reinterpret_cast<u32x4*>(outp + 8 * i) = u32x4{0u, 0u, 0u, 0u};
-    if (a.lse && g == 0) a.lse[(int64_t)t * kHeads + head] = neg_inf();
+    uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (int64_t)t * kHeads * kDim;
+    for (int i = tid; i < kHeads * kDim / 8; i += kAThreads)
+      *reinterpret_cast<u32x4*>(o + 8 * i) = u32x4{0u, 0u, 0u, 0u};
+    if (a.lse && tid < kHeads) a.lse[(int64_t)t * kHeads + tid] = neg_inf();
     return;
   }
 
-  // ---- the wave's 16 query heads as the B operand (k-step s: dims (4s+g)*8 .. +8) ----
+  // roles
+  const int hg = wave & 3, kh = wave >> 2;   // scores: head group, key half
+  const int d0 = wave * 64;                   // values: output dims d0..d0+63
+
+  // ---- query heads 16hg..16hg+15 as the B operand (k-step s: dims (4s+g)*8 .. +8) ----
   bf16x8 qb[16];
   {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)t * kHeads + head) * kDim;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)t * kHeads + 16 * hg + c) * kDim;
 #pragma unroll
     for (int s = 0; s < 16; ++s) qb[s] = *reinterpret_cast<const bf16x8*>(qrow + (4 * s + g) * 8);
   }
 
-  // ---- tile loader: thread (wave w, lane l) moves 16 bytes of rows w*8 .. w*8+7 ----
-  u32x4 stage[8];
+  // ---- tile loader: wave w moves rows 4w..4w+3 of a step, 16 bytes per lane ----
+  u32x4 stage[4];
   auto fetch = [&](int step) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k = step * kKT + wave * 8 + i;
+    for (int i = 0; i < 4; ++i) {
+      const int k = step * kKT + wave * 4 + i;
       if (k < m) stage[i] = *reinterpret_cast<const u32x4*>(sh.rows[k] + lane * 8);
       else stage[i] = u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto commit = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4*>(&sh.tile[buf][(wave * 8 + i) * kRow + lane * 16]) = stage[i];
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(&sh.tile[buf][(wave * 4 + i) * kRow + lane * 16]) = stage[i];
   };
 
-  f32x4 O[4][8];
+  // O^T accumulators: [dim tile e (4 of them: dims d0 + 4c' + e)][head group]
+  f32x4 O[4][4];
 #pragma unroll
-  for (int bk = 0; bk < 4; ++bk)
+  for (int e = 0; e < 4; ++e)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) O[bk][e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = neg_inf(), l_run = 0.f;
+    for (int h = 0; h < 4; ++h) O[e][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = neg_inf();   // running max of head 16hg + c (log2 domain), scores role
+  float l_run = 0.f;         // partial normaliser of that head over this wave's keys
   const float sc2 = a.scale * kLog2e;
-
   const int nsteps = (m + kKT - 1) / kKT;
+
   fetch(0);
   commit(0);
+  if (nsteps > 1) fetch(1);
   __syncthreads();
+
   for (int step = 0; step < nsteps; ++step) {
     const int buf = step & 1;
-    if (step + 1 < nsteps) fetch(step + 1);
     const uint8_t* T = sh.tile[buf];
 
-    // S^T for keys 16st + 4g + i of this step, head c.
-    f32x4 sacc[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const uint8_t* krow = T + (16 * st + c) * kRow;
+    // -- scores: S^T[keys 16kh + 4g + i][head 16hg + c]
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    {
+      const uint8_t* krow = T + (16 * kh + c) * kRow;
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
         bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + (4 * s + g) * 16);
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[s], acc, 0, 0, 0);
       }
-      sacc[st] = acc;
     }
-
-    // Online softmax in the log2 domain.
-    float x[8];
+    float x[4];
     float mt = neg_inf();
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k = step * kKT + 16 * st + 4 * g + i;
-        float v = k < m ? sacc[st][i] * sc2 : neg_inf();
-        x[4 * st + i] = v;
-        mt = fmaxf(mt, v);
-      }
-    mt = fmaxf(mt, shfl_xor_f(mt, 16));
-    mt = fmaxf(mt, shfl_xor_f(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float psum = 0.f;
-    float pv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pv[j] = __builtin_amdgcn_exp2f(x[j] - m_new);
-      psum += pv[j];
+    for (int i = 0; i < 4; ++i) {
+      const int k = step * kKT + 16 * kh + 4 * g + i;
+      x[i] = k < m ? acc[i] * sc2 : neg_inf();
+      mt = fmaxf(mt, x[i]);
     }
-    if (__ballot(m_new > m_run) != 0) {
+    mt = max_xor32(max_xor16(mt));
+    if (g == 0) sh.tmax[kh][16 * hg + c] = mt;
+    __syncthreads();  // (1) tile maxima visible; every wave is done with the previous step
+
+    if (step + 1 < nsteps) commit(buf ^ 1);   // buffer last read in the previous step
+    const float m_new = fmaxf(m_run, fmaxf(sh.tmax[0][16 * hg + c], sh.tmax[1][16 * hg + c]));
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float pv[4];
+    float psum = 0.f;
 #pragma unroll
-      for (int bk = 0; bk < 4; ++bk)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) O[bk][e] *= alpha;
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
+      psum += pv[i];
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-
-    // P^T as the B operand: k-slots 0..3 = keys 4g+i, 4..7 = keys 16+4g+i.
-    u32x4 pu = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, pu);
-
-    // O^T[dim 128bk + 8(4g+i) + e][head c] += V^T P^T.
-#pragma unroll
-    for (int bk = 0; bk < 4; ++bk) {
-      u32x4 R[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4));
-        R[j] = *reinterpret_cast<const u32x4*>(T + key * kRow + (128 * bk + 8 * c) * 2);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        u32x4 va;
-        if (e & 1) {
-          va = u32x4{perm_hi(R[1][w], R[0][w]), perm_hi(R[3][w], R[2][w]),
-                     perm_hi(R[5][w], R[4][w]), perm_hi(R[7][w], R[6][w])};
-        } else {
-          va = u32x4{perm_lo(R[1][w], R[0][w]), perm_lo(R[3][w], R[2][w]),
-                     perm_lo(R[5][w], R[4][w]), perm_lo(R[7][w], R[6][w])};
-        }
-        O[bk][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, va), pb,
-                                                            O[bk][e], 0, 0, 0);
-      }
+    // P^T operand of head group hg: k-slots 0..3 from key half 0, 4..7 from key half 1.
+    {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(&sh.P[hg][lane]) + 2 * kh;
+      dst[0] = pack_bf16x2(pv[0], pv[1]);
+      dst[1] = pack_bf16x2(pv[2], pv[3]);
     }
+    if (kh == 0 && g == 0) sh.alpha[16 * hg + c] = alpha;
+    if (step + 2 < nsteps) fetch(step + 2);
+    __syncthreads();  // (2) P, alpha and the next tile visible
 
-    if (step + 1 < nsteps) {
-      commit(buf ^ 1);  // the other buffer was last read in the previous step
-      __syncthreads();
+    // -- values: O^T[dims d0 + 4c + e][heads 16h + c'] += V^T P^T
+    float al[4];
+    bool any = false;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      al[h] = sh.alpha[16 * h + c];
+      any |= al[h] != 1.0f;
+    }
+    if (__ballot(any) != 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int h = 0; h < 4; ++h) O[e][h] *= al[h];
+    }
+    bf16x8 pb[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) pb[h] = __builtin_bit_cast(bf16x8, sh.P[h][lane]);
+    uint32_t R[8][2];   // key slot j: dims d0 + 4c .. +3 (two dwords)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int key = (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4));
+      const uint2 v = *reinterpret_cast<const uint2*>(T + key * kRow + (d0 + 4 * c) * 2);
+      R[j][0] = v.x;
+      R[j][1] = v.y;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int w = e >> 1;
+      u32x4 va;
+      if (e & 1) {
+        va = u32x4{perm_hi(R[1][w], R[0][w]), perm_hi(R[3][w], R[2][w]),
+                   perm_hi(R[5][w], R[4][w]), perm_hi(R[7][w], R[6][w])};
+      } else {
+        va = u32x4{perm_lo(R[1][w], R[0][w]), perm_lo(R[3][w], R[2][w]),
+                   perm_lo(R[5][w], R[4][w]), perm_lo(R[7][w], R[6][w])};
+      }
+      const bf16x8 A = __builtin_bit_cast(bf16x8, va);
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        O[e][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pb[h], O[e][h], 0, 0, 0);
     }
   }
 
-  // ---- normalise and store ----
-  float l = l_run + shfl_xor_f(l_run, 16);
-  l = l + shfl_xor_f(l, 32);
-  const float inv = 1.0f / l;
+  // ---- normaliser per head: sum of the partial sums of both key halves ----
+  {
+    float l = add_xor32(add_xor16(l_run));
+    if (g == 0) sh.tmax[kh][16 * hg + c] = l;   // reuse: partial normaliser
+    __syncthreads();
+    if (kh == 0 && g == 0) {
+      const float L = sh.tmax[0][16 * hg + c] + sh.tmax[1][16 * hg + c];
+      sh.alpha[16 * hg + c] = L;
+      if (a.lse) a.lse[(int64_t)t * kHeads + 16 * hg + c] = (m_run + __log2f(L)) * kLn2;
+    }
+    __syncthreads();
+  }
+  // ---- normalise and store: lane (c', g) holds dims d0 + 4(4g+i) + e of heads 16h + c' ----
+  uint16_t* outp = reinterpret_cast<uint16_t*>(a.out) + (int64_t)t * kHeads * kDim;
 #pragma unroll
-  for (int bk = 0; bk < 4; ++bk)
+  for (int h = 0; h < 4; ++h) {
+    const float inv = 1.0f / sh.alpha[16 * h + c];
+    uint16_t* orow = outp + (int64_t)(16 * h + c) * kDim + d0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int d0 = 128 * bk + 8 * (4 * g + i);
-      u32x4 o = {pack_bf16x2(O[bk][0][i] * inv, O[bk][1][i] * inv),
-                 pack_bf16x2(O[bk][2][i] * inv, O[bk][3][i] * inv),
-                 pack_bf16x2(O[bk][4][i] * inv, O[bk][5][i] * inv),
-                 pack_bf16x2(O[bk][6][i] * inv, O[bk][7][i] * inv)};
-      *reinterpret_cast<u32x4*>(outp + d0) = o;
+      const int r = 4 * g + i;  // row of the MFMA result = dim group
+      uint2 o;
+      o.x = pack_bf16x2(O[0][h][i] * inv, O[1][h][i] * inv);
+      o.y = pack_bf16x2(O[2][h][i] * inv, O[3][h][i] * inv);
+      *reinterpret_cast<uint2*>(orow + 4 * r) = o;
     }
-  if (a.lse && g == 0) a.lse[(int64_t)t * kHeads + head] = (m_run + __log2f(l)) * kLn2;
+  }
 }
 
 }  // namespace

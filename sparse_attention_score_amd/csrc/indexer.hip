@@ -98,9 +98,7 @@ __device__ __forceinline__ float head_sum(const QueryRegs& Q, f32x4 acc) {
   v = fmaf(Q.w[1], fmaxf(acc[1], 0.f), v);
   v = fmaf(Q.w[2], fmaxf(acc[2], 0.f), v);
   v = fmaf(Q.w[3], fmaxf(acc[3], 0.f), v);
-  v += shfl_xor_f(v, 16);
-  v += shfl_xor_f(v, 32);
-  return v;
+  return add_xor32(add_xor16(v));
 }
 
 // Store a tile's 16 scores and its two block maxima. `valid` = number of visible keys in
@@ -110,9 +108,7 @@ __device__ __forceinline__ void store_tile(float v, int valid, int64_t lim, int 
                                            float* brow) {
   const int c = lane & 15;
   if (c >= valid) v = neg_inf();
-  float m = fmaxf(v, shfl_xor_f(v, 1));
-  m = fmaxf(m, shfl_xor_f(m, 2));
-  m = fmaxf(m, shfl_xor_f(m, 4));
+  const float m = max8_lanes(v);
   if (lane < 16 && c < lim) srow[c] = v;
   if (brow != nullptr && (lane == 0 || lane == 8) && lane < lim) brow[lane >> 3] = m;
 }
@@ -199,8 +195,8 @@ __global__ __launch_bounds__(kThreads) void indexer_decode_kernel(IndexerArgs a)
 // kQPW queries in registers and streams 16-key tiles; every tile feeds 4*kQPW MFMAs.
 // Grid (key chunks of kPKeys, query groups of kWaves*kQPW).
 // ---------------------------------------------------------------------------------------
-constexpr int kQPW = 8;
-constexpr int kPKeys = 512;
+constexpr int kQPW = 4;
+constexpr int kPKeys = 1024;
 
 template <bool FP8>
 __global__ __launch_bounds__(kThreads) void indexer_prefill_kernel(IndexerArgs a) {

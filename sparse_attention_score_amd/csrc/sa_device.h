@@ -55,4 +55,23 @@ __device__ __forceinline__ float shfl_xor_f(float v, int m) {
   return __shfl_xor(v, m, 64);
 }
 
+// v[l] + v[l ^ 16] and v[l] + v[l ^ 32] with the gfx950 row-swap instructions (VALU, no
+// LDS round trip). Both lanes of a pair add the same two values, so they agree bitwise.
+__device__ __forceinline__ float add_xor16(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Max over each aligned group of 8 lanes (DPP quad permutes, then the half-row mirror).
+__device__ __forceinline__ float max8_lanes(float v) {
+  float m = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
+  m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xF, 0xF, false)));
+  return m;
+}
+
 }  // namespace sa
