@@ -129,7 +129,8 @@ const char* sparse_attn_last_error(void);
  *              entries at j >= E are not written.  ld_scores >= E.
  *   block_max  device fp32 [T][ld_block_max] or NULL. out: the max of block
  *              b's visible scores for b < ceil(n_t/8), -inf for the rest of
- *              the first E/8 entries. ld_block_max >= E/8. */
+ *              the first E/8 entries. ld_block_max >= E/8, a multiple of 4.
+ *   ld_scores must be a multiple of 4 (rows start 16-byte aligned). */
 sa_status indexer_score(const sa_plan* plan, const sa_queries* queries, const sa_cache* cache,
                         const void* q_idx, const float* w, float* scores, int64_t ld_scores,
                         float* block_max, int64_t ld_block_max, void* stream);

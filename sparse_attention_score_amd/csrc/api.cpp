@@ -170,7 +170,8 @@ sa_status indexer_score(const sa_plan* plan, const sa_queries* q, const sa_cache
              (long long)ld_scores, (long long)E);
   if (block_max) {
     SA_REQUIRE(aligned16(block_max), SA_EINVAL, "block_max not 16-byte aligned");
-    SA_REQUIRE(ld_block_max >= E / 8, SA_EINVAL, "ld_block_max = %lld must be >= %lld",
+    SA_REQUIRE(ld_block_max >= E / 8 && ld_block_max % 4 == 0, SA_EINVAL,
+               "ld_block_max = %lld must be >= %lld and a multiple of 4",
                (long long)ld_block_max, (long long)(E / 8));
   }
   if (E == 0) return ok();
@@ -215,7 +216,8 @@ sa_status select_topk(const sa_plan* plan, const sa_queries* q, const float* sco
              (long long)ld_scores, (long long)E);
   if (block_max) {
     SA_REQUIRE(aligned16(block_max), SA_EINVAL, "block_max not 16-byte aligned");
-    SA_REQUIRE(ld_block_max >= E / 8, SA_EINVAL, "ld_block_max = %lld must be >= %lld",
+    SA_REQUIRE(ld_block_max >= E / 8 && ld_block_max % 4 == 0, SA_EINVAL,
+               "ld_block_max = %lld must be >= %lld and a multiple of 4",
                (long long)ld_block_max, (long long)(E / 8));
   }
   SA_REQUIRE(topk && aligned16(topk), SA_EINVAL, "topk NULL or not 16-byte aligned");

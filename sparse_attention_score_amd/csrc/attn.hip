@@ -30,6 +30,7 @@ constexpr int kRow = kDim * 2 + 16; // padded LDS row bytes (bank offset 4 dword
 constexpr int kMaxKeys = kTopK + kWindow;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.0f;
 
 struct AttnShared {
   uint8_t tile[2][kKT * kRow];         // 66,560 B
@@ -58,7 +59,7 @@ __device__ __forceinline__ float max_xor32(float v) {
 __global__ __launch_bounds__(kAThreads, 2) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) AttnShared sh;
   const int t = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int c = lane & 15, g = lane >> 4;
 
   const int seq = a.m.seq_id[t], p = a.m.pos[t];
@@ -179,7 +180,11 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_kernel(AttnArgs a) {
     __syncthreads();  // (1) tile maxima visible; every wave is done with the previous step
 
     if (step + 1 < nsteps) commit(buf ^ 1);   // buffer last read in the previous step
-    const float m_new = fmaxf(m_run, fmaxf(sh.tmax[0][16 * hg + c], sh.tmax[1][16 * hg + c]));
+    // Lazy running max: it only moves when the tile max exceeds it by more than kLazy
+    // (log2 units), so most steps need no rescale; P stays below 2^kLazy. Both key halves
+    // read the same maxima and take the same decision for a head.
+    const float mt2 = fmaxf(sh.tmax[0][16 * hg + c], sh.tmax[1][16 * hg + c]);
+    const float m_new = mt2 > m_run + kLazy ? mt2 : m_run;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float pv[4];
     float psum = 0.f;

@@ -7,6 +7,7 @@ namespace sa {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
 
 constexpr int kHeads = 64;
@@ -42,6 +43,17 @@ __device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t codes, uint32_t& lo, u
   auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(codes, true);
   lo = __builtin_amdgcn_perm(__float_as_uint(f01[1]), __float_as_uint(f01[0]), 0x07060302u);
   hi = __builtin_amdgcn_perm(__float_as_uint(f23[1]), __float_as_uint(f23[0]), 0x07060302u);
+}
+
+// max(x, 0) as one integer max: negative floats (sign bit set) are negative int32s, and
+// +0, positive floats and +inf keep their bits. Exact for every non-NaN input.
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// The wave index as a scalar (uniform) value.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
 // Order-preserving map fp32 -> u32 (larger float -> larger key); -0 maps to +0.
