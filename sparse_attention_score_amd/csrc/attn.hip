@@ -7,14 +7,16 @@
 // Flash" Miles docs, section 1 Model Introduction; one softmax over both tiers, recipe
 // Overview, two-tier sparse attention bullet).
 //
-// One work-group (8 waves) per query. Keys are gathered 32 per step into an LDS tile
-// (rows staged through registers one step ahead, two LDS buffers).
-//   scores: wave (hg, kh) computes S^T for keys 16kh..16kh+15 of the step and heads
-//           16hg..16hg+15 with v_mfma_f32_16x16x32_bf16 (A = keys from LDS, B = the
-//           wave's query heads held in registers, 16 k-steps over the 512 dims).
-//   softmax: per head, online in the log2 domain; the two key halves exchange their
-//           tile maxima through LDS; P (bf16) and the rescale factors go to LDS.
-//   values: wave w owns output dims 64w..64w+63 for all 64 heads: O^T += V^T P^T with
+// One work-group (4 waves) per (query, half of the heads); the two halves of a query are
+// placed on the same XCD so the second gather of each row hits that XCD's L2, and two
+// work-groups fit on a CU. Keys are gathered 32 per step into an LDS tile (rows staged
+// through registers one step ahead, two LDS buffers).
+//   scores: wave (hg, kh) computes S^T for keys 16kh..16kh+15 of the step and the 16 heads of
+//           head group hg with v_mfma_f32_16x16x32_bf16 (A = keys from LDS, B = the wave's
+//           query heads held in registers, 16 k-steps over the 512 dims).
+//   softmax: per head, online in the log2 domain with a lazy running max; the two key halves
+//           exchange their tile maxima through LDS; P (bf16) and the rescale factors go to LDS.
+//   values: wave w owns output dims 128w..128w+127 of the 32 heads: O^T += V^T P^T with
 //           A = V^T built from LDS rows by byte permutes (8 keys x 1 dim per lane) and
 //           B = P^T read from LDS. Each value element is read from LDS once per step.
 #include "sa_device.h"
@@ -23,20 +25,21 @@
 namespace sa {
 namespace {
 
-constexpr int kAW = 8;              // waves
+constexpr int kAW = 4;              // waves
 constexpr int kAThreads = 64 * kAW;
+constexpr int kHH = 32;             // heads per work-group
 constexpr int kKT = 32;             // keys per step
-constexpr int kRow = kDim * 2 + 16; // padded LDS row bytes (bank offset 4 dwords per row)
+constexpr int kRow = kDim * 2 + 32; // padded LDS row bytes (+32: conflict-free 16-row reads)
 constexpr int kMaxKeys = kTopK + kWindow;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazy = 8.0f;
+constexpr float kLazy = 8.0f;       // running-max slack, log2 units
 
 struct AttnShared {
   uint8_t tile[2][kKT * kRow];         // 66,560 B
-  u32x4 P[4][64];                      // P^T B operands: [head group][lane], 8 bf16 each
-  float tmax[2][kHeads];               // per key half: tile max of each head
-  float alpha[kHeads];                 // rescale factor of each head this step
+  u32x4 P[2][64];                      // P^T B operands: [head group][lane], 8 bf16 each
+  float tmax[2][kHH];                  // per key half: tile max of each head
+  float alpha[kHH];                    // rescale factor of each head this step
   const uint16_t* rows[kMaxKeys];      // global row of every key slot
   int wave_cnt[kAW];
 };
@@ -58,7 +61,12 @@ __device__ __forceinline__ float max_xor32(float v) {
 
 __global__ __launch_bounds__(kAThreads, 2) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) AttnShared sh;
-  const int t = blockIdx.x;
+  // work-group -> (query, head half): 16 consecutive ids hold 8 queries x 2 halves with both
+  // halves of a query on the same XCD (ids are dealt round-robin over 8 XCDs).
+  const int bid = blockIdx.x;
+  const int t = (bid >> 4) * 8 + (bid & 7);
+  const int hh = (bid >> 3) & 1;
+  if (t >= a.m.T) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int c = lane & 15, g = lane >> 4;
 
@@ -75,9 +83,9 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_kernel(AttnArgs a) {
   int m = 0;
   if (valid_q) {
     const int32_t* tk = a.topk + (int64_t)t * kTopK;
-    const int j = tk[tid];  // 512 threads, one entry each
-    const bool v = j >= 0 && j < n;
-    const int cnt = (int)v;
+    const int2 jj = *reinterpret_cast<const int2*>(tk + 2 * tid);
+    const bool v0 = jj.x >= 0 && jj.x < n, v1 = jj.y >= 0 && jj.y < n;
+    const int cnt = (int)v0 + (int)v1;
     int incl = cnt;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -92,7 +100,9 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_kernel(AttnArgs a) {
       before += (w < wave) ? sh.wave_cnt[w] : 0;
     }
     const uint16_t* lat = reinterpret_cast<const uint16_t*>(a.latents) + (int64_t)seq * a.latents_seq_stride;
-    if (v) sh.rows[before + incl - cnt] = lat + (int64_t)j * kDim;
+    int off = before + incl - cnt;
+    if (v0) sh.rows[off++] = lat + (int64_t)jj.x * kDim;
+    if (v1) sh.rows[off] = lat + (int64_t)jj.y * kDim;
     const int u0 = p - kWindow + 1 > 0 ? p - kWindow + 1 : 0;
     const int nwin = p - u0 + 1;
     const uint16_t* win = reinterpret_cast<const uint16_t*>(a.window) + (int64_t)seq * a.window_seq_stride;
@@ -101,48 +111,49 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_kernel(AttnArgs a) {
   }
   __syncthreads();
 
+  const int head0 = kHH * hh;
   if (m == 0) {  // invalid query: zero output, lse = -inf
-    uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (int64_t)t * kHeads * kDim;
-    for (int i = tid; i < kHeads * kDim / 8; i += kAThreads)
+    uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * kHeads + head0) * kDim;
+    for (int i = tid; i < kHH * kDim / 8; i += kAThreads)
       *reinterpret_cast<u32x4*>(o + 8 * i) = u32x4{0u, 0u, 0u, 0u};
-    if (a.lse && tid < kHeads) a.lse[(int64_t)t * kHeads + tid] = neg_inf();
+    if (a.lse && tid < kHH) a.lse[(int64_t)t * kHeads + head0 + tid] = neg_inf();
     return;
   }
 
   // roles
-  const int hg = wave & 3, kh = wave >> 2;   // scores: head group, key half
-  const int d0 = wave * 64;                   // values: output dims d0..d0+63
+  const int hg = wave & 1, kh = wave >> 1;   // scores: head group, key half
+  const int d0 = wave * 128;                  // values: output dims d0..d0+127
 
-  // ---- query heads 16hg..16hg+15 as the B operand (k-step s: dims (4s+g)*8 .. +8) ----
+  // ---- query heads head0 + 16hg + c as the B operand (k-step s: dims (4s+g)*8 .. +8) ----
   bf16x8 qb[16];
   {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)t * kHeads + 16 * hg + c) * kDim;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)t * kHeads + head0 + 16 * hg + c) * kDim;
 #pragma unroll
     for (int s = 0; s < 16; ++s) qb[s] = *reinterpret_cast<const bf16x8*>(qrow + (4 * s + g) * 8);
   }
 
-  // ---- tile loader: wave w moves rows 4w..4w+3 of a step, 16 bytes per lane ----
-  u32x4 stage[4];
+  // ---- tile loader: wave w moves rows 8w..8w+7 of a step, 16 bytes per lane ----
+  u32x4 stage[8];
   auto fetch = [&](int step) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = step * kKT + wave * 4 + i;
+    for (int i = 0; i < 8; ++i) {
+      const int k = step * kKT + wave * 8 + i;
       if (k < m) stage[i] = *reinterpret_cast<const u32x4*>(sh.rows[k] + lane * 8);
       else stage[i] = u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto commit = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(&sh.tile[buf][(wave * 4 + i) * kRow + lane * 16]) = stage[i];
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<u32x4*>(&sh.tile[buf][(wave * 8 + i) * kRow + lane * 16]) = stage[i];
   };
 
-  // O^T accumulators: [dim tile e (4 of them: dims d0 + 4c' + e)][head group]
-  f32x4 O[4][4];
+  // O^T accumulators: [e][head group]: dims d0 + 8r + e (r = MFMA row), heads 16h + c'
+  f32x4 O[8][2];
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
+  for (int e = 0; e < 8; ++e)
 #pragma unroll
-    for (int h = 0; h < 4; ++h) O[e][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < 2; ++h) O[e][h] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = neg_inf();   // running max of head 16hg + c (log2 domain), scores role
   float l_run = 0.f;         // partial normaliser of that head over this wave's keys
   const float sc2 = a.scale * kLog2e;
@@ -205,46 +216,51 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_kernel(AttnArgs a) {
     if (step + 2 < nsteps) fetch(step + 2);
     __syncthreads();  // (2) P, alpha and the next tile visible
 
-    // -- values: O^T[dims d0 + 4c + e][heads 16h + c'] += V^T P^T
-    float al[4];
+    // -- values: O^T[dims d0 + 8r + e][heads 16h + c'] += V^T P^T
+    float al[2];
     bool any = false;
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
+    for (int h = 0; h < 2; ++h) {
       al[h] = sh.alpha[16 * h + c];
       any |= al[h] != 1.0f;
     }
     if (__ballot(any) != 0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+      for (int e = 0; e < 8; ++e)
 #pragma unroll
-        for (int h = 0; h < 4; ++h) O[e][h] *= al[h];
+        for (int h = 0; h < 2; ++h) O[e][h] *= al[h];
     }
-    bf16x8 pb[4];
+    bf16x8 pb[2];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) pb[h] = __builtin_bit_cast(bf16x8, sh.P[h][lane]);
-    uint32_t R[8][2];   // key slot j: dims d0 + 4c .. +3 (two dwords)
+    for (int h = 0; h < 2; ++h) pb[h] = __builtin_bit_cast(bf16x8, sh.P[h][lane]);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int key = (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4));
-      const uint2 v = *reinterpret_cast<const uint2*>(T + key * kRow + (d0 + 4 * c) * 2);
-      R[j][0] = v.x;
-      R[j][1] = v.y;
-    }
+    for (int half = 0; half < 2; ++half) {
+      // key slot j: dims d0 + 8c + 4*half .. +3 (two dwords)
+      uint32_t R[8][2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int w = e >> 1;
-      u32x4 va;
-      if (e & 1) {
-        va = u32x4{perm_hi(R[1][w], R[0][w]), perm_hi(R[3][w], R[2][w]),
-                   perm_hi(R[5][w], R[4][w]), perm_hi(R[7][w], R[6][w])};
-      } else {
-        va = u32x4{perm_lo(R[1][w], R[0][w]), perm_lo(R[3][w], R[2][w]),
-                   perm_lo(R[5][w], R[4][w]), perm_lo(R[7][w], R[6][w])};
+      for (int j = 0; j < 8; ++j) {
+        const int key = (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4));
+        const uint2 v = *reinterpret_cast<const uint2*>(T + key * kRow + (d0 + 8 * c + 4 * half) * 2);
+        R[j][0] = v.x;
+        R[j][1] = v.y;
       }
-      const bf16x8 A = __builtin_bit_cast(bf16x8, va);
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
-        O[e][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pb[h], O[e][h], 0, 0, 0);
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int w = e4 >> 1;
+        u32x4 va;
+        if (e4 & 1) {
+          va = u32x4{perm_hi(R[1][w], R[0][w]), perm_hi(R[3][w], R[2][w]),
+                     perm_hi(R[5][w], R[4][w]), perm_hi(R[7][w], R[6][w])};
+        } else {
+          va = u32x4{perm_lo(R[1][w], R[0][w]), perm_lo(R[3][w], R[2][w]),
+                     perm_lo(R[5][w], R[4][w]), perm_lo(R[7][w], R[6][w])};
+        }
+        const bf16x8 A = __builtin_bit_cast(bf16x8, va);
+        const int e = 4 * half + e4;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          O[e][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pb[h], O[e][h], 0, 0, 0);
+      }
     }
   }
 
@@ -256,23 +272,25 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_kernel(AttnArgs a) {
     if (kh == 0 && g == 0) {
       const float L = sh.tmax[0][16 * hg + c] + sh.tmax[1][16 * hg + c];
       sh.alpha[16 * hg + c] = L;
-      if (a.lse) a.lse[(int64_t)t * kHeads + 16 * hg + c] = (m_run + __log2f(L)) * kLn2;
+      if (a.lse) a.lse[(int64_t)t * kHeads + head0 + 16 * hg + c] = (m_run + __log2f(L)) * kLn2;
     }
     __syncthreads();
   }
-  // ---- normalise and store: lane (c', g) holds dims d0 + 4(4g+i) + e of heads 16h + c' ----
-  uint16_t* outp = reinterpret_cast<uint16_t*>(a.out) + (int64_t)t * kHeads * kDim;
+  // ---- normalise and store: lane (c', g) holds dims d0 + 8(4g+i) + e of heads 16h + c' ----
+  uint16_t* outp = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * kHeads + head0) * kDim;
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
+  for (int h = 0; h < 2; ++h) {
     const float inv = 1.0f / sh.alpha[16 * h + c];
     uint16_t* orow = outp + (int64_t)(16 * h + c) * kDim + d0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 4 * g + i;  // row of the MFMA result = dim group
-      uint2 o;
-      o.x = pack_bf16x2(O[0][h][i] * inv, O[1][h][i] * inv);
-      o.y = pack_bf16x2(O[2][h][i] * inv, O[3][h][i] * inv);
-      *reinterpret_cast<uint2*>(orow + 4 * r) = o;
+      const int r = 4 * g + i;  // row of the MFMA result = group of 8 dims
+      u32x4 o;
+      o[0] = pack_bf16x2(O[0][h][i] * inv, O[1][h][i] * inv);
+      o[1] = pack_bf16x2(O[2][h][i] * inv, O[3][h][i] * inv);
+      o[2] = pack_bf16x2(O[4][h][i] * inv, O[5][h][i] * inv);
+      o[3] = pack_bf16x2(O[6][h][i] * inv, O[7][h][i] * inv);
+      *reinterpret_cast<u32x4*>(orow + 8 * r) = o;
     }
   }
 }
@@ -280,7 +298,8 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)a.m.T), dim3(kAThreads), 0, stream, a);
+  const int64_t groups = (a.m.T + 7) / 8;  // 8 queries x 2 head halves per 16 ids
+  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)(groups * 16)), dim3(kAThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -291,22 +291,28 @@ __global__ __launch_bounds__(kPThreads, 2) void indexer_prefill_kernel(IndexerAr
   const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys) + (int64_t)sq * a.keys_seq_stride * (FP8 ? 1 : 2);
   const float* scales = FP8 ? a.scales + (int64_t)sq * a.scales_seq_stride : nullptr;
 
-  // staging: thread -> key row tid/8, bytes (tid%8) * RB/8 of it
-  constexpr int PART = RB / 8;                          // 32 (bf16) or 16 (e4m3)
-  const int srow_k = tid >> 3, spart = tid & 7;
-  u32x4 stg[PART / 16];
+  // staging: 16-byte chunk q = tid + kPThreads*h of the tile (h < CPT) is row q / CPR,
+  // chunk q % CPR: each wave loads whole rows (contiguous 1 KiB per instruction) and
+  // each group of CPR lanes writes one padded LDS row contiguously.
+  constexpr int CPR = RB / 16;                          // chunks per row: 16 (bf16) or 8 (e4m3)
+  constexpr int CPT = kPKT * CPR / kPThreads;           // chunks per thread: 2 or 1
+  u32x4 stg[CPT];
   float stg_scale = 1.f;
   auto fetch = [&](int i) {
-    const int row = min(k0 + i * kPKT + srow_k, klive - 1);
-    const uint8_t* src = keys + (int64_t)row * RB + spart * PART;
 #pragma unroll
-    for (int h = 0; h < PART / 16; ++h) stg[h] = *reinterpret_cast<const u32x4*>(src + 16 * h);
+    for (int h = 0; h < CPT; ++h) {
+      const int q = tid + kPThreads * h;
+      const int row = min(k0 + i * kPKT + q / CPR, klive - 1);
+      stg[h] = *reinterpret_cast<const u32x4*>(keys + (int64_t)row * RB + (q % CPR) * 16);
+    }
     if (FP8 && tid < kPKT) stg_scale = scales[min(k0 + i * kPKT + tid, klive - 1)];
   };
   auto commit = [&](int buf) {
 #pragma unroll
-    for (int h = 0; h < PART / 16; ++h)
-      *reinterpret_cast<u32x4*>(&sh.tile[buf][srow_k * RS + spart * PART + 16 * h]) = stg[h];
+    for (int h = 0; h < CPT; ++h) {
+      const int q = tid + kPThreads * h;
+      *reinterpret_cast<u32x4*>(&sh.tile[buf][(q / CPR) * RS + (q % CPR) * 16]) = stg[h];
+    }
     if (FP8 && tid < kPKT) sh.scale[buf][tid] = stg_scale;
   };
 
