@@ -130,13 +130,14 @@ const char* sparse_attn_last_error(void);
  *   block_max  device fp32 [T][ld_block_max] or NULL. out: the max of block
  *              b's visible scores for b < ceil(n_t/8), -inf for the rest of
  *              the first E/8 entries. ld_block_max >= E/8, a multiple of 4.
- *   ld_scores must be a multiple of 4 (rows start 16-byte aligned). */
+ *   ld_scores and ld_block_max must be multiples of 4 (rows start 16-byte
+ *   aligned) and at most 2^26. */
 sa_status indexer_score(const sa_plan* plan, const sa_queries* queries, const sa_cache* cache,
                         const void* q_idx, const float* w, float* scores, int64_t ld_scores,
                         float* block_max, int64_t ld_block_max, void* stream);
 
 /* S2 + S3. Candidate blocks, then the top-512 positions inside them.
- *   scores, ld_scores      as written by indexer_score
+ *   scores, ld_scores      as written by indexer_score (same limits on the strides)
  *   block_max              as written by indexer_score, or NULL (then the block
  *                          maxima are recomputed from scores)
  *   cand       device int32 [T][2048] or NULL: out, the kept block ids of each

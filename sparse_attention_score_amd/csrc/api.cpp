@@ -37,6 +37,8 @@ sa_status ok() {
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
 constexpr int64_t kMaxVisible = 2048LL * 8 * 32;  // 524288: largest block set a select WG holds
+constexpr int64_t kMaxLd = 1LL << 26;              // row strides of scores / block maxima: two rows
+                                                   // stay addressable by 32-bit buffer offsets
 
 size_t cand_bytes(int64_t T) { return (size_t)T * 2048 * sizeof(int32_t); }
 
@@ -165,14 +167,14 @@ sa_status indexer_score(const sa_plan* plan, const sa_queries* q, const sa_cache
              "q_idx / w NULL or not 16-byte aligned");
   SA_REQUIRE(scores && aligned16(scores), SA_EINVAL, "scores NULL or not 16-byte aligned");
   const int64_t E = round8(q->max_visible);
-  SA_REQUIRE(ld_scores >= E && ld_scores % 4 == 0, SA_EINVAL,
-             "ld_scores = %lld must be >= %lld (max_visible rounded up to 8) and a multiple of 4",
-             (long long)ld_scores, (long long)E);
+  SA_REQUIRE(ld_scores >= E && ld_scores % 4 == 0 && ld_scores <= kMaxLd, SA_EINVAL,
+             "ld_scores = %lld must be >= %lld (max_visible rounded up to 8), <= %lld and a multiple of 4",
+             (long long)ld_scores, (long long)E, (long long)kMaxLd);
   if (block_max) {
     SA_REQUIRE(aligned16(block_max), SA_EINVAL, "block_max not 16-byte aligned");
-    SA_REQUIRE(ld_block_max >= E / 8 && ld_block_max % 4 == 0, SA_EINVAL,
-               "ld_block_max = %lld must be >= %lld and a multiple of 4",
-               (long long)ld_block_max, (long long)(E / 8));
+    SA_REQUIRE(ld_block_max >= E / 8 && ld_block_max % 4 == 0 && ld_block_max <= kMaxLd, SA_EINVAL,
+               "ld_block_max = %lld must be >= %lld, <= %lld and a multiple of 4",
+               (long long)ld_block_max, (long long)(E / 8), (long long)kMaxLd);
   }
   if (E == 0) return ok();
   sa::IndexerArgs a;
@@ -212,13 +214,14 @@ sa_status select_topk(const sa_plan* plan, const sa_queries* q, const float* sco
   if ((st = check_queries(plan, q)) != SA_OK) return st;
   const int64_t E = round8(q->max_visible);
   SA_REQUIRE(scores && aligned16(scores), SA_EINVAL, "scores NULL or not 16-byte aligned");
-  SA_REQUIRE(ld_scores >= E && ld_scores % 4 == 0, SA_EINVAL, "ld_scores = %lld must be >= %lld",
-             (long long)ld_scores, (long long)E);
+  SA_REQUIRE(ld_scores >= E && ld_scores % 4 == 0 && ld_scores <= kMaxLd, SA_EINVAL,
+             "ld_scores = %lld must be >= %lld, <= %lld and a multiple of 4", (long long)ld_scores,
+             (long long)E, (long long)kMaxLd);
   if (block_max) {
     SA_REQUIRE(aligned16(block_max), SA_EINVAL, "block_max not 16-byte aligned");
-    SA_REQUIRE(ld_block_max >= E / 8 && ld_block_max % 4 == 0, SA_EINVAL,
-               "ld_block_max = %lld must be >= %lld and a multiple of 4",
-               (long long)ld_block_max, (long long)(E / 8));
+    SA_REQUIRE(ld_block_max >= E / 8 && ld_block_max % 4 == 0 && ld_block_max <= kMaxLd, SA_EINVAL,
+               "ld_block_max = %lld must be >= %lld, <= %lld and a multiple of 4",
+               (long long)ld_block_max, (long long)(E / 8), (long long)kMaxLd);
   }
   SA_REQUIRE(topk && aligned16(topk), SA_EINVAL, "topk NULL or not 16-byte aligned");
   if (cand) {

@@ -209,24 +209,27 @@ constexpr int kPairsPerWave = 2;
 constexpr int kQPerWG = kPWaves * kPairsPerWave * 2;   // 16 queries
 constexpr int kPKT = 32;                                // keys per tile
 constexpr int kPChunk = 2048;                           // keys per work-group
+constexpr int kPST = 2 * kPKT;                          // keys per LDS stage (two tiles)
 constexpr int kPBufs = 3;
 
-template <bool FP8>
+// LDS key tile: 32 keys as bf16 rows (e4m3 keys are widened once, while staging), padded
+// to 272 bytes so the B-operand reads of 32 rows are bank-conflict free.
+constexpr int kPRS = 2 * kIdxDim + 16;
 struct PrefillShared {
-  static constexpr int RB = FP8 ? kIdxDim : 2 * kIdxDim;
-  static constexpr int RS = RB + 16;                   // padded row stride
-  uint8_t tile[kPBufs][kPKT * RS];
-  float scale[kPBufs][kPKT];
+  uint8_t tile[kPBufs][kPST * kPRS];
+  float scale[kPBufs][kPST];
 };
 
 // Dims of k-step s (0..7) for lane half hh: (2s + hh) * 8 .. +8 (32x32x16 operands).
 __device__ __forceinline__ int pdim(int hh, int s) { return (2 * s + hh) * 8; }
 
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer resource, 32-bit data (gfx9 family)
+constexpr uint32_t kDrop = 0x80000000u;  // buffer offset past every extent: store dropped
+
 template <bool FP8>
 __global__ __launch_bounds__(kPThreads, 2) void indexer_prefill_kernel(IndexerArgs a) {
-  using SH = PrefillShared<FP8>;
-  constexpr int RB = SH::RB, RS = SH::RS;
-  __shared__ __attribute__((aligned(16))) SH sh;
+  constexpr int RB = FP8 ? kIdxDim : 2 * kIdxDim;   // key row bytes in HBM
+  __shared__ __attribute__((aligned(16))) PrefillShared sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int r32 = lane & 31, hh = lane >> 5;
   const int E = (int)a.E;
@@ -239,35 +242,25 @@ __global__ __launch_bounds__(kPThreads, 2) void indexer_prefill_kernel(IndexerAr
   // queries of this wave: q0 + 4*wave + j, j = 0..3 (pair p = j/2); the WG's queries must
   // read one sequence (queries of another sequence, or invalid ones, get n = 0).
   const int seq = a.seq_id[q0];
-  int nq[4];
+  auto n_of = [&](int tq) { return tq < T && a.seq_id[tq] == seq ? query_n(a, tq) : 0; };
   int nmax_wg = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) nq[j] = 0;
-  for (int j = 0; j < kQPerWG; ++j) {
-    const int tq = q0 + j;
-    int nj = 0;
-    if (tq < T && a.seq_id[tq] == seq) nj = query_n(a, tq);
-    nmax_wg = max(nmax_wg, nj);
-    if ((j >> 2) == wave) nq[j & 3] = nj;
-  }
-  int nmin_w = INT32_MAX;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (q0 + 4 * wave + j < T) nmin_w = min(nmin_w, nq[j]);
+  for (int j = 0; j < kQPerWG; ++j) nmax_wg = max(nmax_wg, n_of(q0 + j));
   const int klive = min(kend, nmax_wg);   // keys past every query's n are masked
-  const int ntiles = klive > k0 ? (klive - k0 + kPKT - 1) / kPKT : 0;
+  // tiles covering [k0, klive), rounded up to an even count (steps run in pairs); keys of
+  // the extra tile are past klive, so they come out masked like the rest
+  const int nsteps = klive > k0 ? ((klive - k0 + 2 * kPKT - 1) / (2 * kPKT)) * 2 : 0;
 
-  // masked part of the chunk (tiles past klive), for every valid query of the wave
+  // part of the chunk past the steps' tiles, for every valid query of the wave
   for (int j = 0; j < 4; ++j) {
     const int tq = q0 + 4 * wave + j;
     if (tq >= T) break;
     float* srow = a.scores + (int64_t)tq * a.ld_scores;
     float* brow = a.block_max ? a.block_max + (int64_t)tq * a.ld_block_max : nullptr;
-    for (int k = k0 + ntiles * kPKT + lane; k < kend; k += 64) srow[k] = neg_inf();
+    for (int k = k0 + nsteps * kPKT + lane; k < kend; k += 64) srow[k] = neg_inf();
     if (brow)
-      for (int b = (k0 + ntiles * kPKT) / 8 + lane; b < kend / 8; b += 64) brow[b] = neg_inf();
+      for (int b = (k0 + nsteps * kPKT) / 8 + lane; b < kend / 8; b += 64) brow[b] = neg_inf();
   }
-  if (ntiles == 0) return;
+  if (nsteps == 0) return;
 
   // A operands and head weights of the wave's two query pairs.
   bf16x8 qa[kPairsPerWave][8];
@@ -287,106 +280,182 @@ __global__ __launch_bounds__(kPThreads, 2) void indexer_prefill_kernel(IndexerAr
     }
   }
 
-  const int sq = (seq >= 0 && seq < a.num_seqs) ? seq : 0;
-  const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys) + (int64_t)sq * a.keys_seq_stride * (FP8 ? 1 : 2);
-  const float* scales = FP8 ? a.scales + (int64_t)sq * a.scales_seq_stride : nullptr;
-
-  // staging: 16-byte chunk q = tid + kPThreads*h of the tile (h < CPT) is row q / CPR,
-  // chunk q % CPR: each wave loads whole rows (contiguous 1 KiB per instruction) and
-  // each group of CPR lanes writes one padded LDS row contiguously.
-  constexpr int CPR = RB / 16;                          // chunks per row: 16 (bf16) or 8 (e4m3)
-  constexpr int CPT = kPKT * CPR / kPThreads;           // chunks per thread: 2 or 1
-  u32x4 stg[CPT];
-  float stg_scale = 1.f;
-  auto fetch = [&](int i) {
+  // Outputs. After the head sum of pair p, lanes 0-31 hold query 2p's score of key r32 and
+  // lanes 32-63 query 2p+1's. Each pair stores through buffer resources based at its first
+  // query's rows, covering the pair's valid rows; a lane whose entry is not to be written
+  // gets offset kDrop, which the hardware discards, so the epilogue needs no branches.
+  __amdgpu_buffer_rsrc_t srs[kPairsPerWave], brs[kPairsPerWave];
+  int nl[kPairsPerWave];
+  const uint32_t soff_hh = (uint32_t)hh * (uint32_t)a.ld_scores * 4u;
+  const uint32_t boff_hh = (uint32_t)hh * (uint32_t)a.ld_block_max * 4u;
 #pragma unroll
-    for (int h = 0; h < CPT; ++h) {
-      const int q = tid + kPThreads * h;
-      const int row = min(k0 + i * kPKT + q / CPR, klive - 1);
-      stg[h] = *reinterpret_cast<const u32x4*>(keys + (int64_t)row * RB + (q % CPR) * 16);
-    }
-    if (FP8 && tid < kPKT) stg_scale = scales[min(k0 + i * kPKT + tid, klive - 1)];
-  };
-  auto commit = [&](int buf) {
-#pragma unroll
-    for (int h = 0; h < CPT; ++h) {
-      const int q = tid + kPThreads * h;
-      *reinterpret_cast<u32x4*>(&sh.tile[buf][(q / CPR) * RS + (q % CPR) * 16]) = stg[h];
-    }
-    if (FP8 && tid < kPKT) sh.scale[buf][tid] = stg_scale;
-  };
-
-  fetch(0);
-  commit(0);
-  if (ntiles > 1) {
-    fetch(1);
-    commit(1);
+  for (int p = 0; p < kPairsPerWave; ++p) {
+    const int tp = q0 + 4 * wave + 2 * p;
+    const int rows = tp + 1 < T ? 2 : (tp < T ? 1 : 0);
+    const int tpc = min(tp, T - 1);
+    srs[p] = __builtin_amdgcn_make_buffer_rsrc(a.scores + (int64_t)tpc * a.ld_scores, (short)0,
+                                               rows * (int)a.ld_scores * 4, kRsrcWord3);
+    brs[p] = __builtin_amdgcn_make_buffer_rsrc(a.block_max ? a.block_max + (int64_t)tpc * a.ld_block_max : a.scores,
+                                               (short)0, a.block_max ? rows * (int)a.ld_block_max * 4 : 0,
+                                               kRsrcWord3);
+    nl[p] = n_of(tp + hh);
   }
-  if (ntiles > 2) fetch(2);
-  __syncthreads();
 
-  for (int i = 0; i < ntiles; ++i) {
-    const int buf = i % kPBufs;
-    const int k = k0 + i * kPKT;
-    const uint8_t* T8 = sh.tile[buf] + r32 * RS;
-    bf16x8 b[8];
+  // Keys and scales through buffer resources over rows [k0, klive) of the sequence: loads
+  // past klive read zeros (their scores are masked), so the loads need no clamping. The
+  // whole offset goes in the VGPR operand, which the range check covers.
+  const int sq = (seq >= 0 && seq < a.num_seqs) ? seq : 0;
+  const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys) + (int64_t)sq * a.keys_seq_stride * (FP8 ? 1 : 2) +
+                        (int64_t)k0 * RB;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(keys), (short)0, (klive - k0) * RB, kRsrcWord3);
+  const float* scales = FP8 ? a.scales + (int64_t)sq * a.scales_seq_stride + k0 : a.w;
+  const __amdgpu_buffer_rsrc_t scrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(scales), (short)0, FP8 ? (klive - k0) * 4 : 0, kRsrcWord3);
+
+  // staging, one stage (64 keys) at a time: 16-byte chunk q = tid + kPThreads*h of a stage
+  // (h < CPT) is row q / CPR, chunk q % CPR: each wave loads whole rows (contiguous 1 KiB
+  // per instruction) and each group of CPR lanes writes one padded LDS row contiguously
+  // (e4m3 chunks are widened to 32 bytes of bf16 on the way).
+  constexpr int CPR = RB / 16;                          // chunks per row: 16 (bf16) or 8 (e4m3)
+  constexpr int CPT = kPST * CPR / kPThreads;           // chunks per thread: 4 or 2
+  uint32_t kvoff[CPT], ldsoff[CPT];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+  for (int h = 0; h < CPT; ++h) {
+    const int q = tid + kPThreads * h;
+    kvoff[h] = (uint32_t)((q / CPR) * RB + (q % CPR) * 16);
+    ldsoff[h] = (uint32_t)((q / CPR) * kPRS + (q % CPR) * (FP8 ? 32 : 16));
+  }
+  const uint32_t scoff = tid < kPST ? (uint32_t)tid * 4u : kDrop;
+  struct Stage {
+    u32x4 v[CPT];
+    float scale;
+  };
+  auto fetch = [&](Stage& st, int S) {
+#pragma unroll
+    for (int h = 0; h < CPT; ++h)
+      st.v[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, kvoff[h] + S * kPST * RB, 0, 0));
+    if (FP8) st.scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(scrs, scoff + S * kPST * 4, 0, 0));
+  };
+  auto commit = [&](const Stage& st, int buf) {
+#pragma unroll
+    for (int h = 0; h < CPT; ++h) {
+      uint8_t* dst = &sh.tile[buf][ldsoff[h]];
       if constexpr (FP8) {
-        const uint2 v = *reinterpret_cast<const uint2*>(T8 + pdim(hh, s));
-        b[s] = e4m3x8_to_bf16x8(v.x, v.y);
+        uint32_t u[8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) e4m3x4_to_bf16x4(st.v[h][c], u[2 * c], u[2 * c + 1]);
+        *reinterpret_cast<u32x4*>(dst) = u32x4{u[0], u[1], u[2], u[3]};
+        *reinterpret_cast<u32x4*>(dst + 16) = u32x4{u[4], u[5], u[6], u[7]};
       } else {
-        b[s] = *reinterpret_cast<const bf16x8*>(T8 + 2 * pdim(hh, s));
+        *reinterpret_cast<u32x4*>(dst) = st.v[h];
       }
     }
-    const float sc = FP8 ? sh.scale[buf][r32] : 1.f;
-    const bool full = k + kPKT <= nmin_w;   // every key of the tile visible to all 4 queries
-    // both pairs' MFMA chains first (independent accumulators), then the epilogues, so
-    // the second chain runs under the first epilogue
-    f32x16 acc[kPairsPerWave];
+    if (FP8 && tid < kPST) sh.scale[buf][tid] = st.scale;
+  };
+  // B operands of tile i (stage i/2, half i%2): lane (r32, hh) reads key row r32, dims pdim(hh, s).
+  auto load_b = [&](bf16x8 (&b)[8], float& sc, int i) {
+    const int buf = (i >> 1) % kPBufs, row = (i & 1) * kPKT + r32;
+    const uint8_t* T8 = sh.tile[buf] + row * kPRS;
 #pragma unroll
-    for (int p = 0; p < kPairsPerWave; ++p) {
-      acc[p] = f32x16{};
+    for (int s = 0; s < 8; ++s) b[s] = *reinterpret_cast<const bf16x8*>(T8 + 2 * pdim(hh, s));
+    sc = FP8 ? sh.scale[buf][row] : 1.f;
+  };
+
+  // Epilogue of pair p for the tile at key k: ReLU and head weights in-lane over the
+  // lane's 8 heads of each query, one 32-lane swap to finish both 16-head sums, key scale,
+  // mask past the query's n, block max over 8 lanes, two stores.
+  const uint32_t sbase = soff_hh + (uint32_t)r32 * 4u;
+  const uint32_t bbase = boff_hh + (uint32_t)(r32 >> 3) * 4u;
+  const bool bstore = (lane & 7) == 0;
+  auto epilogue = [&](int p, const f32x16& acc, int k, float sc) {
+    float x = wt[p][0][0] * relu(acc[0]);
+    float y = wt[p][1][0] * relu(acc[8]);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) acc[p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[p][s], b[s], acc[p], 0, 0, 0);
+    for (int ii = 1; ii < 8; ++ii) {
+      x = fmaf(wt[p][0][ii], relu(acc[ii]), x);
+      y = fmaf(wt[p][1][ii], relu(acc[8 + ii]), y);
     }
+    // lanes 32-63 of x trade places with lanes 0-31 of y: the low half then adds its own
+    // and the high half's partial of query 2p, the high half both partials of query 2p+1
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    float v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    if (FP8) v *= sc;
+    v = r32 < nl[p] - k ? v : neg_inf();
+    const float m = max8_lanes(v);
+    const bool in = r32 < kend - k;            // keys of later chunks belong to other WGs
+    const uint32_t so = in ? sbase + (uint32_t)k * 4u : kDrop;
+    const uint32_t bo = in && bstore ? bbase + (uint32_t)(k >> 3) * 4u : kDrop;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srs[p], so, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), brs[p], bo, 0, 0);
+  };
+
+  // One tile: B operands of the next tile are read from LDS while this one's MFMAs run.
+  // Pair 1's epilogue of tile i-1 runs in step i (in step 0 on zeros, every store dropped).
+  // After every second step (one stage) the next stages move up; staging, loads and barriers
+  // are unconditional (past the last stage, loads read zeros and commits fill buffers
+  // nobody reads), so the compiler's wait counts stay exact.
+  // Issue order, fixed with scheduling barriers: pair 0's MFMA chain with pair 1's previous
+  // epilogue, then pair 1's chain with pair 0's epilogue, each MFMA followed by a few VALU
+  // ops so one wave keeps the matrix core and the VALU busy together.
+  Stage st;
+  f32x16 acc0, acc1 = {};
+  int kprev = E;
+  float scprev = 1.f;
+  auto step = [&](int i, const bf16x8 (&bc)[8], float sc, bf16x8 (&bn)[8], float& scn, bool stage_end) {
+    const int k = k0 + i * kPKT;
+    load_b(bn, scn, i + 1);   // stale past the last tile, never used then
+    __builtin_amdgcn_sched_barrier(0);
+    acc0 = f32x16{};
 #pragma unroll
-    for (int p = 0; p < kPairsPerWave; ++p) {
+    for (int s = 0; s < 8; ++s) acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0][s], bc[s], acc0, 0, 0, 0);
+    epilogue(1, acc1, kprev, scprev);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int jq = 2 * p + j;
-        const int tq = q0 + 4 * wave + jq;
-        float v = wt[p][j][0] * relu(acc[p][8 * j + 0]);
-#pragma unroll
-        for (int ii = 1; ii < 8; ++ii) v = fmaf(wt[p][j][ii], relu(acc[p][8 * j + ii]), v);
-        v = add_xor32(v);
-        if (FP8) v *= sc;
-        if (tq < T) {
-          float* srow = a.scores + (int64_t)tq * a.ld_scores;
-          float* brow = a.block_max ? a.block_max + (int64_t)tq * a.ld_block_max : nullptr;
-          if (full) {
-            const float m = max8_lanes(v);
-            if (lane < 32) srow[k + lane] = v;
-            if (brow && lane < 32 && (lane & 7) == 0) brow[(k >> 3) + (lane >> 3)] = m;
-          } else {
-            if (k + r32 >= nq[jq]) v = neg_inf();
-            const float m = max8_lanes(v);
-            if (lane < 32 && k + lane < E) srow[k + lane] = v;
-            if (brow && lane < 32 && (lane & 7) == 0 && k + lane < E) brow[(k >> 3) + (lane >> 3)] = m;
-          }
-        }
-      }
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
     }
-    if (i + 1 < ntiles) {
-      // buffer (i+2)%3 was last read in step i-1, which every wave finished before the
-      // barrier at the end of step i-1
-      if (i + 2 < ntiles) {
-        commit((i + 2) % kPBufs);
-        if (i + 3 < ntiles) fetch(i + 3);
-      }
+    __builtin_amdgcn_sched_barrier(0);
+    acc1 = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[1][s], bc[s], acc1, 0, 0, 0);
+    epilogue(0, acc0, k, sc);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    kprev = k;
+    scprev = sc;
+    if (stage_end) {
+      // end of stage S = i/2: stage S+2 goes to buffer (S+2)%3, which held stage S-1, last
+      // read in stage S-1 (before the previous barrier); stage S+3 starts loading
+      const int S = i >> 1;
+      commit(st, (S + 2) % kPBufs);
+      fetch(st, S + 3);
       __syncthreads();
     }
+  };
+
+  fetch(st, 0);
+  commit(st, 0);
+  fetch(st, 1);
+  commit(st, 1);
+  // Nothing loaded so far is still in flight past here, so the waits the compiler places
+  // inside the loop only cover the loop's own loads.
+  __builtin_amdgcn_s_waitcnt(0);
+  fetch(st, 2);
+  __syncthreads();
+
+  bf16x8 b0[8], b1[8];
+  float sc0, sc1;
+  load_b(b0, sc0, 0);
+  for (int i = 0; i < nsteps; i += 2) {
+    step(i, b0, sc0, b1, sc1, false);
+    step(i + 1, b1, sc1, b0, sc0, true);
   }
+  epilogue(1, acc1, kprev, scprev);
 }
 
 }  // namespace
