@@ -140,13 +140,26 @@ class Timer:
         return {n: v / max(1, len(self.ev)) for n, v in out.items()}
 
 
-def run_batch(torch, d, steps, warmup):
-    stages = ["compress", "indexer", "select", "attention"]
-    fns = [d.compress, d.index, d.select, d.attend]
-    for _ in range(warmup):
+def warm_up(torch, fns, warmup, min_seconds):
+    """W untimed steps, then more until `min_seconds` of GPU work have run, so the clocks
+    have left their idle state before anything is timed."""
+    t0 = time.perf_counter()
+    done = 0
+    while done < warmup or time.perf_counter() - t0 < min_seconds:
         for f in fns:
             f()
+        done += 1
+        if done % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+
+
+def run_batch(torch, d, steps, warmup, min_warm_s=0.5):
+    """Eager steps with HIP events on the launch stream around every stage.
+    Returns (seconds per step, mean stage milliseconds)."""
+    stages = ["compress", "indexer", "select", "attention"]
+    fns = [d.compress, d.index, d.select, d.attend]
+    warm_up(torch, fns, warmup, min_warm_s)
     timer = Timer(torch, stages)
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -154,6 +167,25 @@ def run_batch(torch, d, steps, warmup):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     return (t1 - t0) / steps, timer.mean_ms()
+
+
+def run_graph(torch, d, steps):
+    """The same step captured once in a HIP graph and replayed `steps` times: the timed
+    region holds exactly those replays, bracketed by device synchronisation."""
+    g = d.capture()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    del g
+    return (t1 - t0) / steps, e0.elapsed_time(e1) * 1e-3 / steps
 
 
 def cpu_baseline(wl, budget_s=20.0, max_queries=None):
@@ -217,8 +249,13 @@ def main():
     d = DeviceBatch(wl)
     torch.cuda.synchronize()
     log("uploaded")
-    sec_per_step, stage_ms = run_batch(torch, d, args.steps, args.warmup)
-    log(f"decode: {sec_per_step * 1e3:.3f} ms/step, stages {stage_ms}")
+    eager_s, stage_ms = run_batch(torch, d, args.steps, args.warmup, 0.0 if args.profile else 0.5)
+    log(f"decode eager: {eager_s * 1e3:.3f} ms/step, stages {stage_ms}")
+    if args.profile:
+        sec_per_step, graph_gpu_s = eager_s, None
+    else:
+        sec_per_step, graph_gpu_s = run_graph(torch, d, args.steps)
+        log(f"decode graph replay: {sec_per_step * 1e3:.3f} ms/step (events {graph_gpu_s * 1e3:.3f})")
 
     idx_bytes = indexer_bytes(wl)
     idx_s = stage_ms["indexer"] * 1e-3
@@ -247,7 +284,9 @@ def main():
                      "frac": idx_bytes / idx_s / HBM_PEAK, "traffic": stored_traffic(args.workload),
                      "algorithmic_bytes_per_launch": idx_bytes, "avg_launch_ms": stage_ms["indexer"],
                      "measured_copy_GBps": copy_bw / 1e9},
-        "step": {"stage_ms": stage_ms, "algorithmic_bytes": sbytes,
+        "step": {"stage_ms": stage_ms, "eager_ms_per_step": eager_s * 1e3,
+                 "timing": "HIP graph replays of the whole step" if graph_gpu_s else "eager launches",
+                 "algorithmic_bytes": sbytes,
                  "hbm_frac": sbytes / sec_per_step / HBM_PEAK,
                  "tokens_per_s": wl.T / sec_per_step},
     }
@@ -260,10 +299,12 @@ def main():
         dp = DeviceBatch(wp)
         torch.cuda.synchronize()
         log(f"prefill inputs ready in {time.perf_counter() - t0:.1f}s")
-        sp, sms = run_batch(torch, dp, max(3, args.steps // 2), args.warmup)
+        sp_eager, sms = run_batch(torch, dp, max(3, args.steps // 2), args.warmup)
+        sp, _ = run_graph(torch, dp, max(3, args.steps // 2))
         fi, fa = step_flops(wp)
         result["prefill"] = {
             "workload": args.prefill_workload, "ms_per_chunk": sp * 1e3, "tokens_per_s": wp.T / sp,
+            "eager_ms_per_chunk": sp_eager * 1e3,
             "stage_ms": sms, "algorithmic_tflop": (fi + fa) / 1e12,
             "mfma_frac": (fi + fa) / sp / BF16_PEAK,
             "indexer_mfma_frac": fi / (sms["indexer"] * 1e-3) / BF16_PEAK,

@@ -96,3 +96,20 @@ class DeviceBatch:
         self.index(stream)
         self.select(stream)
         self.attend(stream)
+
+    def capture(self):
+        """One whole step (the four stage launches) captured in a HIP graph. The library
+        enqueues kernels only (no allocation, copy, memset or synchronisation), so every
+        launch is recorded; replaying the graph re-runs the step on the same buffers."""
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.run()          # first launches outside capture (lazy initialisation)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run()
+        torch.cuda.synchronize()
+        return g
