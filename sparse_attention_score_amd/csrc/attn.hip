@@ -7,41 +7,54 @@
 // Flash" Miles docs, section 1 Model Introduction; one softmax over both tiers, recipe
 // Overview, two-tier sparse attention bullet).
 //
-// One work-group (4 waves) per (query, half of the heads); the two halves of a query are
-// placed on the same XCD so the second gather of each row hits that XCD's L2, and two
-// work-groups fit on a CU. Keys are gathered 32 per step into an LDS tile (rows staged
-// through registers one step ahead, two LDS buffers).
-//   scores: wave (hg, kh) computes S^T for keys 16kh..16kh+15 of the step and the 16 heads of
-//           head group hg with v_mfma_f32_16x16x32_bf16 (A = keys from LDS, B = the wave's
-//           query heads held in registers, 16 k-steps over the 512 dims).
-//   softmax: per head, online in the log2 domain with a lazy running max; the two key halves
-//           exchange their tile maxima through LDS; P (bf16) and the rescale factors go to LDS.
-//   values: wave w owns output dims 128w..128w+127 of the 32 heads: O^T += V^T P^T with
-//           A = V^T built from LDS rows by byte permutes (8 keys x 1 dim per lane) and
-//           B = P^T read from LDS. Each value element is read from LDS once per step.
+// One work-group (4 waves) per query, so every gathered row is read from memory once for
+// all 64 heads. Rows are gathered 32 per step into LDS tiles by direct global-to-LDS loads
+// (no registers), kDepth steps ahead of the step being computed.
+//   scores: wave w owns heads 16w..16w+15: S^T[32 keys][16 heads] with
+//           v_mfma_f32_16x16x32_bf16, A = key rows from LDS, B = the wave's query heads held
+//           in registers (16 k-steps over the 512 dims); lane (c, g) ends with keys 4g..4g+3
+//           and 16+4g..16+4g+3 of head c.
+//   softmax: in the log2 domain against a fixed reference per head, the max of the first
+//           step's scores (softmax does not depend on the reference, and P and the fp32 sums
+//           have the range of fp32), so the output is never rescaled. If a later score
+//           exceeds the reference by more than kSafe, the query is run again with the true
+//           max as reference. The max over a step's keys of a head is an in-lane max plus
+//           two lane swaps. The lane's 8 probabilities, packed, are exactly the P^T operand
+//           of its head group (the MFMA k order is free as long as A uses the same one);
+//           they go to LDS.
+//   values: wave w owns output dims 128w..128w+127 of all 64 heads: O^T += V^T P^T with
+//           A = V^T built from LDS rows by byte permutes (8 keys x 1 dim per lane), each value
+//           element read from LDS once per step, and B = P^T of each head group.
 #include "sa_device.h"
 #include "sa_launch.h"
 
 namespace sa {
 namespace {
 
-constexpr int kAW = 4;              // waves
+constexpr int kAW = 4;              // waves; wave w owns heads 16w..16w+15
 constexpr int kAThreads = 64 * kAW;
-constexpr int kHH = 32;             // heads per work-group
 constexpr int kKT = 32;             // keys per step
 constexpr int kRow = kDim * 2 + 32; // padded LDS row bytes (+32: conflict-free 16-row reads)
 constexpr int kMaxKeys = kTopK + kWindow;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazy = 8.0f;       // running-max slack, log2 units
+constexpr float kSafe = 64.0f;      // largest score above the reference a pass accepts (log2)
+constexpr int kDepth = 3;           // steps whose rows are in flight ahead of the current one
+constexpr int kBufs = kDepth + 1;   // LDS tiles
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8;
+// expcnt and lgkmcnt left at their maxima = no wait)
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLater = waitcnt_vm(8 * (kDepth - 1));   // all but the kDepth-1 later steps' loads
+constexpr int kWaitNext = waitcnt_vm(8 * (kDepth - 2));    // ... all but kDepth-2 of them
+constexpr int kWaitAll = waitcnt_vm(0);
 
 struct AttnShared {
-  uint8_t tile[2][kKT * kRow];         // 66,560 B
-  u32x4 P[2][64];                      // P^T B operands: [head group][lane], 8 bf16 each
-  float tmax[2][kHH];                  // per key half: tile max of each head
-  float alpha[kHH];                    // rescale factor of each head this step
+  uint8_t tile[kBufs][kKT * kRow];     // 135,168 B
   const uint16_t* rows[kMaxKeys];      // global row of every key slot
+  u32x4 P[2][kAW][64];                 // P^T operand of each head group per lane, two steps
+  float norm[kHeads];                  // final normaliser of each head
   int wave_cnt[kAW];
+  int redo[kAW];                       // per wave: a score exceeded its reference by > kSafe
 };
 
 __device__ __forceinline__ uint32_t perm_lo(uint32_t hi_src, uint32_t lo_src) {
@@ -59,14 +72,23 @@ __device__ __forceinline__ float max_xor32(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-__global__ __launch_bounds__(kAThreads, 2) void attn_kernel(AttnArgs a) {
+// One 1 KB latent row from global memory straight into LDS: lane l moves bytes 16l..16l+15
+// to LDS byte address lds + 16l. The compiler does not see this load, so completion is
+// tracked by hand with s_waitcnt vmcnt (the kernel issues no other vector-memory
+// operations between the first of these and the final wait).
+__device__ __forceinline__ void row_to_lds(const uint16_t* row, uint32_t lds, int lane) {
+  // s_nop: an LDS-DMA load must not directly follow the write of M0 (one wait state)
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(row + lane * 8), "{m0}"(lds) : "memory");
+}
+
+__global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) AttnShared sh;
-  // work-group -> (query, head half): 16 consecutive ids hold 8 queries x 2 halves with both
-  // halves of a query on the same XCD (ids are dealt round-robin over 8 XCDs).
-  const int bid = blockIdx.x;
-  const int t = (bid >> 4) * 8 + (bid & 7);
-  const int hh = (bid >> 3) & 1;
-  if (t >= a.m.T) return;
+  // work-group -> query: ids are dealt round-robin over the 8 XCDs, so XCD x gets the
+  // contiguous query range x*Q8 .. x*Q8+Q8-1 (neighbouring queries share window rows).
+  const int T = (int)a.m.T;
+  const int q8 = (T + 7) >> 3;
+  const int t = (blockIdx.x & 7) * q8 + (blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= q8 || t >= T) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int c = lane & 15, g = lane >> 4;
 
@@ -111,136 +133,100 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  const int head0 = kHH * hh;
+  const int head0 = 16 * wave;   // this wave's heads
   if (m == 0) {  // invalid query: zero output, lse = -inf
-    uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * kHeads + head0) * kDim;
-    for (int i = tid; i < kHH * kDim / 8; i += kAThreads)
+    uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (int64_t)t * kHeads * kDim;
+    for (int i = tid; i < kHeads * kDim / 8; i += kAThreads)
       *reinterpret_cast<u32x4*>(o + 8 * i) = u32x4{0u, 0u, 0u, 0u};
-    if (a.lse && tid < kHH) a.lse[(int64_t)t * kHeads + head0 + tid] = neg_inf();
+    if (a.lse && tid < kHeads) a.lse[(int64_t)t * kHeads + tid] = neg_inf();
     return;
   }
 
-  // roles
-  const int hg = wave & 1, kh = wave >> 1;   // scores: head group, key half
-  const int d0 = wave * 128;                  // values: output dims d0..d0+127
-
-  // ---- query heads head0 + 16hg + c as the B operand (k-step s: dims (4s+g)*8 .. +8) ----
+  // ---- query heads head0 + c as the B operand (k-step s: dims (4s+g)*8 .. +8) ----
   bf16x8 qb[16];
   {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)t * kHeads + head0 + 16 * hg + c) * kDim;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)t * kHeads + head0 + c) * kDim;
 #pragma unroll
     for (int s = 0; s < 16; ++s) qb[s] = *reinterpret_cast<const bf16x8*>(qrow + (4 * s + g) * 8);
   }
 
-  // ---- tile loader: wave w moves rows 8w..8w+7 of a step, 16 bytes per lane ----
-  u32x4 stage[8];
-  auto fetch = [&](int step) {
+  // ---- tile loader: wave w moves rows 8w..8w+7 of a step (8 row loads). Rows past the
+  // key list repeat the last real row (finite data; their scores are masked), so every
+  // wave issues exactly 8 loads per step and the wait counts below are constants.
+  const uint32_t tile0 = (uint32_t)(uintptr_t)&sh.tile[0][0];
+  auto issue = [&](int step) {
+    const uint32_t base = tile0 + (uint32_t)((step % kBufs) * (kKT * kRow) + wave * 8 * kRow);
+    const uint16_t* r[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int k = step * kKT + wave * 8 + i;
-      if (k < m) stage[i] = *reinterpret_cast<const u32x4*>(sh.rows[k] + lane * 8);
-      else stage[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto commit = [&](int buf) {
+    for (int i = 0; i < 8; ++i) r[i] = sh.rows[min(step * kKT + wave * 8 + i, m - 1)];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4*>(&sh.tile[buf][(wave * 8 + i) * kRow + lane * 16]) = stage[i];
+    for (int i = 0; i < 8; ++i) row_to_lds(r[i], base + i * kRow, lane);
   };
 
-  // O^T accumulators: [e][head group]: dims d0 + 8r + e (r = MFMA row), heads 16h + c'
-  f32x4 O[8][2];
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-#pragma unroll
-    for (int h = 0; h < 2; ++h) O[e][h] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = neg_inf();   // running max of head 16hg + c (log2 domain), scores role
-  float l_run = 0.f;         // partial normaliser of that head over this wave's keys
+  // O^T accumulators [head group][e]: dims d0 + 8r + e (r = MFMA row) of head 16hg + c
+  const int d0 = 128 * wave;
+  f32x4 O[kAW][8];
+  float m_ref = neg_inf();   // reference of head head0 + c (log2 domain)
+  float m_max = neg_inf();   // max score of that head so far
+  float l_run = 0.f;         // this lane's part of that head's normaliser
   const float sc2 = a.scale * kLog2e;
   const int nsteps = (m + kKT - 1) / kKT;
 
-  fetch(0);
-  commit(0);
-  if (nsteps > 1) fetch(1);
-  __syncthreads();
+  // the query loads are complete before the first row load, so the compiler's own waits
+  // (which do not count the row loads) never need to reach past them
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
 
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
-    const uint8_t* T = sh.tile[buf];
-
-    // -- scores: S^T[keys 16kh + 4g + i][head 16hg + c]
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    {
-      const uint8_t* krow = T + (16 * kh + c) * kRow;
+  // Scores and softmax of step `step` (tile in LDS buffer step % kBufs): P goes to LDS
+  // buffer step & 1. Keys past m (and whole steps past the last) come out with P = 0.
+  auto scores = [&](int step, int pass) {
+    const uint8_t* T8 = sh.tile[step % kBufs];
+    // S^T[keys 16kt + 4g + i][head c], kt = 0, 1 (two independent chains)
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    const uint8_t* k0row = T8 + c * kRow;
+    const uint8_t* k1row = T8 + (16 + c) * kRow;
 #pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + (4 * s + g) * 16);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[s], acc, 0, 0, 0);
-      }
+    for (int s = 0; s < 16; ++s) {
+      const bf16x8 ka0 = *reinterpret_cast<const bf16x8*>(k0row + (4 * s + g) * 16);
+      const bf16x8 ka1 = *reinterpret_cast<const bf16x8*>(k1row + (4 * s + g) * 16);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qb[s], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qb[s], acc1, 0, 0, 0);
     }
-    float x[4];
+    // softmax of head c over the step's keys (slot j < 4: key 4g+j; j >= 4: 16+4g+j-4)
+    float x[8];
     float mt = neg_inf();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int k = step * kKT + 16 * kh + 4 * g + i;
-      x[i] = k < m ? acc[i] * sc2 : neg_inf();
-      mt = fmaxf(mt, x[i]);
+      const int k = step * kKT + 4 * g + i;
+      x[i] = k < m ? acc0[i] * sc2 : neg_inf();
+      x[4 + i] = k + 16 < m ? acc1[i] * sc2 : neg_inf();
+      mt = fmaxf(mt, fmaxf(x[i], x[4 + i]));
     }
-    mt = max_xor32(max_xor16(mt));
-    if (g == 0) sh.tmax[kh][16 * hg + c] = mt;
-    __syncthreads();  // (1) tile maxima visible; every wave is done with the previous step
-
-    if (step + 1 < nsteps) commit(buf ^ 1);   // buffer last read in the previous step
-    // Lazy running max: it only moves when the tile max exceeds it by more than kLazy
-    // (log2 units), so most steps need no rescale; P stays below 2^kLazy. Both key halves
-    // read the same maxima and take the same decision for a head.
-    const float mt2 = fmaxf(sh.tmax[0][16 * hg + c], sh.tmax[1][16 * hg + c]);
-    const float m_new = mt2 > m_run + kLazy ? mt2 : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    float pv[4];
-    float psum = 0.f;
+    mt = max_xor32(max_xor16(mt));   // all four lane groups of head c agree
+    if (step == 0 && pass == 0) m_ref = mt;   // step 0 always holds a real key (m >= 1)
+    m_max = fmaxf(m_max, mt);
+    float pv[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pv[i] = __builtin_amdgcn_exp2f(x[i] - m_new);
-      psum += pv[i];
+    for (int j = 0; j < 8; ++j) {
+      pv[j] = __builtin_amdgcn_exp2f(x[j] - m_ref);
+      l_run += pv[j];
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // P^T operand of head group hg: k-slots 0..3 from key half 0, 4..7 from key half 1.
-    {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(&sh.P[hg][lane]) + 2 * kh;
-      dst[0] = pack_bf16x2(pv[0], pv[1]);
-      dst[1] = pack_bf16x2(pv[2], pv[3]);
-    }
-    if (kh == 0 && g == 0) sh.alpha[16 * hg + c] = alpha;
-    if (step + 2 < nsteps) fetch(step + 2);
-    __syncthreads();  // (2) P, alpha and the next tile visible
-
-    // -- values: O^T[dims d0 + 8r + e][heads 16h + c'] += V^T P^T
-    float al[2];
-    bool any = false;
+    sh.P[step & 1][wave][lane] = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                                       pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
+  };
+  // O^T[dims d0 + 8r + 4half + e4][head 16hg + c] += V^T P^T for step `step`
+  auto values = [&](int step) {
+    const uint8_t* T8 = sh.tile[step % kBufs];
+    bf16x8 pb[kAW];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      al[h] = sh.alpha[16 * h + c];
-      any |= al[h] != 1.0f;
-    }
-    if (__ballot(any) != 0) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) O[e][h] *= al[h];
-    }
-    bf16x8 pb[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) pb[h] = __builtin_bit_cast(bf16x8, sh.P[h][lane]);
+    for (int hg = 0; hg < kAW; ++hg) pb[hg] = __builtin_bit_cast(bf16x8, sh.P[step & 1][hg][lane]);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      // key slot j: dims d0 + 8c + 4*half .. +3 (two dwords)
+      // key slot j: dims d0 + 8c + 4half .. +3 (two dwords)
       uint32_t R[8][2];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int key = (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4));
-        const uint2 v = *reinterpret_cast<const uint2*>(T + key * kRow + (d0 + 8 * c + 4 * half) * 2);
+        const uint2 v = *reinterpret_cast<const uint2*>(T8 + key * kRow + (d0 + 8 * c + 4 * half) * 2);
         R[j][0] = v.x;
         R[j][1] = v.y;
       }
@@ -258,38 +244,68 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_kernel(AttnArgs a) {
         const bf16x8 A = __builtin_bit_cast(bf16x8, va);
         const int e = 4 * half + e4;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-          O[e][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pb[h], O[e][h], 0, 0, 0);
+        for (int hg = 0; hg < kAW; ++hg)
+          O[hg][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pb[hg], O[hg][e], 0, 0, 0);
       }
     }
+  };
+
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int hg = 0; hg < kAW; ++hg)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) O[hg][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    l_run = 0.f;
+    if (pass == 1) m_ref = m_max;   // second pass: the true max, so every P <= 1
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) issue(j);
+    __builtin_amdgcn_s_waitcnt(kWaitLater);   // step 0's rows (steps 1, 2 in flight)
+    __syncthreads();
+    scores(0, pass);
+
+    // Software pipeline: step s runs the values of step s and the scores of step s+1,
+    // independent work that the wave interleaves. One barrier per step makes visible the
+    // P of step s, the rows of step s+1 and frees the buffer of step s-1.
+    for (int step = 0; step < nsteps; ++step) {
+      __builtin_amdgcn_s_waitcnt(kWaitNext);   // step s+1's rows (step s+2's in flight)
+      __syncthreads();
+      issue(step + kDepth);
+      values(step);
+      scores(step + 1, pass);                  // past the last step: P = 0, never read
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitAll);  // no row load may outlive the pass (or the LDS)
+    // a second pass only if some head of the query saw a score more than kSafe above its
+    // reference (P up to 2^kSafe and the sums stay far inside fp32 range otherwise)
+    if (pass == 1) break;
+    if (lane == 0) sh.redo[wave] = __ballot(m_max > m_ref + kSafe) != 0;
+    __syncthreads();
+    if (!(sh.redo[0] | sh.redo[1] | sh.redo[2] | sh.redo[3])) break;
+    __syncthreads();   // every wave read the flags and is done with the tiles
   }
 
-  // ---- normaliser per head: sum of the partial sums of both key halves ----
+
+  // ---- normaliser of head head0 + c: the four lane groups' parts ----
   {
-    float l = add_xor32(add_xor16(l_run));
-    if (g == 0) sh.tmax[kh][16 * hg + c] = l;   // reuse: partial normaliser
-    __syncthreads();
-    if (kh == 0 && g == 0) {
-      const float L = sh.tmax[0][16 * hg + c] + sh.tmax[1][16 * hg + c];
-      sh.alpha[16 * hg + c] = L;
-      if (a.lse) a.lse[(int64_t)t * kHeads + head0 + 16 * hg + c] = (m_run + __log2f(L)) * kLn2;
+    const float L = add_xor32(add_xor16(l_run));
+    if (g == 0) {
+      sh.norm[head0 + c] = L;
+      if (a.lse) a.lse[(int64_t)t * kHeads + head0 + c] = (m_ref + __log2f(L)) * kLn2;
     }
-    __syncthreads();
   }
-  // ---- normalise and store: lane (c', g) holds dims d0 + 8(4g+i) + e of heads 16h + c' ----
-  uint16_t* outp = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * kHeads + head0) * kDim;
+  __syncthreads();
+  // ---- store: lane (c, g) holds dims d0 + 8(4g+i) + e of head 16hg + c ----
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const float inv = 1.0f / sh.alpha[16 * h + c];
-    uint16_t* orow = outp + (int64_t)(16 * h + c) * kDim + d0;
+  for (int hg = 0; hg < kAW; ++hg) {
+    const float inv = 1.0f / sh.norm[16 * hg + c];
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * kHeads + 16 * hg + c) * kDim + d0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * g + i;  // row of the MFMA result = group of 8 dims
       u32x4 o;
-      o[0] = pack_bf16x2(O[0][h][i] * inv, O[1][h][i] * inv);
-      o[1] = pack_bf16x2(O[2][h][i] * inv, O[3][h][i] * inv);
-      o[2] = pack_bf16x2(O[4][h][i] * inv, O[5][h][i] * inv);
-      o[3] = pack_bf16x2(O[6][h][i] * inv, O[7][h][i] * inv);
+      o[0] = pack_bf16x2(O[hg][0][i] * inv, O[hg][1][i] * inv);
+      o[1] = pack_bf16x2(O[hg][2][i] * inv, O[hg][3][i] * inv);
+      o[2] = pack_bf16x2(O[hg][4][i] * inv, O[hg][5][i] * inv);
+      o[3] = pack_bf16x2(O[hg][6][i] * inv, O[hg][7][i] * inv);
       *reinterpret_cast<u32x4*>(orow + 8 * r) = o;
     }
   }
@@ -298,8 +314,8 @@ __global__ __launch_bounds__(kAThreads, 2) void attn_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
-  const int64_t groups = (a.m.T + 7) / 8;  // 8 queries x 2 head halves per 16 ids
-  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)(groups * 16)), dim3(kAThreads), 0, stream, a);
+  const int64_t q8 = (a.m.T + 7) / 8;   // queries per XCD
+  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)(8 * q8)), dim3(kAThreads), 0, stream, a);
   return hipGetLastError();
 }
 
