@@ -146,7 +146,10 @@ sa_status indexer_score(const sa_plan* plan, const sa_queries* queries, const sa
  *              in the workspace only.
  *   topk       device int32 [T][512]: out, the selected positions in ascending
  *              order, -1 after the last one (min(512, n_t) are selected).
- *   workspace  device, >= the size reported by sparse_attn_plan. */
+ *   workspace  device, >= the size reported by sparse_attn_plan; used for the
+ *              candidate blocks when cand is NULL and, for queries longer than
+ *              65536 positions, for per-part candidate lists (the candidate stage then
+ *              runs in two levels over parts of 8192 blocks). */
 sa_status select_topk(const sa_plan* plan, const sa_queries* queries, const float* scores,
                       int64_t ld_scores, const float* block_max, int64_t ld_block_max,
                       int32_t* cand, int32_t* topk, void* workspace, size_t workspace_bytes,

@@ -15,7 +15,8 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libsparse_attn.so")
+# SPARSE_ATTN_LIB selects another build of the library (same ABI); default: the in-tree one
+LIB_PATH = os.environ.get("SPARSE_ATTN_LIB") or os.path.join(_PKG, "libsparse_attn.so")
 
 SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_EWORKSPACE, SA_EHIP = 0, 1, 2, 3, 4
 SA_KEY_BF16, SA_KEY_FP8_E4M3 = 0, 1

@@ -41,6 +41,11 @@ constexpr int64_t kMaxLd = 1LL << 26;              // row strides of scores / bl
                                                    // stay addressable by 32-bit buffer offsets
 
 size_t cand_bytes(int64_t T) { return (size_t)T * 2048 * sizeof(int32_t); }
+// Part lists of the two-level candidate stage (queries longer than 8192 blocks).
+size_t part_bytes(int64_t T, int64_t max_visible) {
+  const int parts = sa::select_parts(max_visible);
+  return parts > 1 ? (size_t)T * parts * 2048 * sizeof(int32_t) : 0;
+}
 
 sa_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
@@ -148,7 +153,7 @@ sa_status sparse_attn_plan(const sa_params* p, sa_plan** plan, size_t* workspace
   sa_plan* pl = new (std::nothrow) sa_plan;
   SA_REQUIRE(pl != nullptr, SA_EINVAL, "out of host memory");
   pl->p = *p;
-  pl->workspace = cand_bytes(p->max_queries);
+  pl->workspace = cand_bytes(p->max_queries) + part_bytes(p->max_queries, p->max_compressed);
   *plan = pl;
   if (workspace_bytes) *workspace_bytes = pl->workspace;
   return ok();
@@ -224,15 +229,17 @@ sa_status select_topk(const sa_plan* plan, const sa_queries* q, const float* sco
                (long long)ld_block_max, (long long)(E / 8), (long long)kMaxLd);
   }
   SA_REQUIRE(topk && aligned16(topk), SA_EINVAL, "topk NULL or not 16-byte aligned");
-  if (cand) {
-    SA_REQUIRE(aligned16(cand), SA_EINVAL, "cand not 16-byte aligned");
-  } else {
+  if (cand) SA_REQUIRE(aligned16(cand), SA_EINVAL, "cand not 16-byte aligned");
+  // workspace: [cand_bytes(T)] candidate blocks when cand is NULL, then the part lists
+  const size_t parts_need = part_bytes(q->T, q->max_visible);
+  if (!cand || parts_need) {
+    const size_t need = cand_bytes(q->T) + parts_need;
     SA_REQUIRE(workspace != nullptr && aligned16(workspace), SA_EWORKSPACE,
-               "workspace NULL or misaligned (needed when cand is NULL)");
-    SA_REQUIRE(workspace_bytes >= cand_bytes(q->T), SA_EWORKSPACE,
-               "workspace_bytes = %zu < %zu", workspace_bytes, cand_bytes(q->T));
-    cand = static_cast<int32_t*>(workspace);
+               "workspace NULL or misaligned (needed when cand is NULL or max_visible > %d)",
+               sa::kPartBlocks * 8);
+    SA_REQUIRE(workspace_bytes >= need, SA_EWORKSPACE, "workspace_bytes = %zu < %zu", workspace_bytes, need);
   }
+  if (!cand) cand = static_cast<int32_t*>(workspace);
   sa::SelectArgs a;
   // num_seqs / compressed_cap are not known here: the per-query n is capped by max_visible.
   a.m = meta(plan, q, INT32_MAX, q->max_visible);
@@ -242,6 +249,8 @@ sa_status select_topk(const sa_plan* plan, const sa_queries* q, const float* sco
   a.ld_block_max = ld_block_max;
   a.cand = cand;
   a.topk = topk;
+  a.parts = sa::select_parts(q->max_visible);
+  a.part_ids = a.parts > 1 ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + cand_bytes(q->T)) : nullptr;
   return hip_status(sa::launch_select(a, (hipStream_t)stream), "select_topk launch");
 }
 

@@ -39,6 +39,8 @@ struct IndexerArgs {
 };
 hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream);
 
+constexpr int kPartBlocks = 8192;   // blocks per part of the two-level candidate stage
+
 struct SelectArgs {
   QueryMeta m;
   const float* scores;
@@ -47,7 +49,11 @@ struct SelectArgs {
   int64_t ld_block_max;
   int32_t* cand;            // [T][2048]
   int32_t* topk;            // [T][512]
+  int32_t* part_ids;        // [T][parts][2048] workspace, used when parts > 1
+  int parts;                // select_parts(m.max_visible)
 };
+// Parts of the candidate stage for queries of up to max_visible positions (1: one level).
+int select_parts(int64_t max_visible);
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 
 struct AttnArgs {

@@ -1,9 +1,9 @@
-// S2 candidate blocks and S3 top-512 on gfx950 (one fused kernel).
+// S2 candidate blocks and S3 top-512 on gfx950.
 //
 // Both stages keep the first k elements of a set in the order (value descending, id
 // ascending) and emit their ids in ascending order ("deepseek-ai/DeepSeek-V4.1-Flash"
 // recipe, Overview, two-tier sparse attention bullet: 2048 candidate blocks of 8, then the
-// best 512 positions per query). One work-group handles one query:
+// best 512 positions per query). One work-group (4 waves) handles one query:
 //   S2  elements = block maxima of the query's ceil(n/8) blocks, k = 2048;
 //   S3  elements = scores of the visible positions inside the kept blocks, k = 512.
 // Each thread holds a contiguous run of elements in registers (so id order = thread order),
@@ -11,16 +11,20 @@
 // histograms over linear bins of the remaining key range (each round keeps the bin that
 // holds the k-th key and shrinks the range to it), so a skewed score distribution does not
 // pile onto a few bins. Then every element with key > v is kept, plus the lowest-id
-// elements with key == v until k are taken; two work-group prefix sums place the kept ids
-// in ascending order.
+// elements with key == v until k are taken; work-group prefix sums place the kept ids in
+// ascending order.
+// Above 8192 blocks S2 runs in two levels: parts of 8192 blocks each keep their own best
+// 2048 (a block among the best 2048 of the union is among the best 2048 of its part, with
+// the same order), then one work-group per query selects among the survivors.
 #include "sa_device.h"
 #include "sa_launch.h"
 
 namespace sa {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWavesSel = kThreads / 64;
+// Work-group sizes: 1024 threads when few queries run (latency of one query matters),
+// 256 when many do (more work-groups per CU).
+constexpr int kMaxWaves = 16;
 constexpr int kBins = 2048;
 
 constexpr int kMaxSel = 2;      // selections sharing one histogram (candidate and core blocks)
@@ -28,9 +32,9 @@ constexpr int kColl = 256;      // most elements of a threshold bin the fast pat
 
 struct SelShared {
   uint32_t hist[kBins];
-  uint32_t wmin[kWavesSel], wmax[kWavesSel];
-  int wave_sum[kWavesSel];
-  int wave_sum2[kWavesSel];
+  uint32_t wmin[kMaxWaves], wmax[kMaxWaves];
+  int wave_sum[kMaxWaves];
+  int wave_sum2[kMaxWaves];
   int bin;           // selected bin of the current round (refinement path)
   int above;         // elements in higher bins (refinement path)
   // fast path, per selection
@@ -39,6 +43,7 @@ struct SelShared {
   int32_t vid[kMaxSel];
   uint32_t ckey[kMaxSel][kColl];
   int32_t cid[kMaxSel][kColl];
+  int32_t stage[kCandBlocks + kTopK] __attribute__((aligned(16)));   // kept ids before they go out
 };
 
 __device__ __forceinline__ int64_t visible_n(const QueryMeta& m, int t) {
@@ -50,6 +55,7 @@ __device__ __forceinline__ int64_t visible_n(const QueryMeta& m, int t) {
 }
 
 // Inclusive prefix sum over the work-group; `total` receives the sum over all threads.
+template <int NT>
 __device__ __forceinline__ int wg_inclusive_scan(int v, SelShared& sh, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -61,7 +67,7 @@ __device__ __forceinline__ int wg_inclusive_scan(int v, SelShared& sh, int& tota
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kWavesSel; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     int s = sh.wave_sum[w];
     before += (w < wave) ? s : 0;
     tot += s;
@@ -72,6 +78,7 @@ __device__ __forceinline__ int wg_inclusive_scan(int v, SelShared& sh, int& tota
 }
 
 // Two inclusive prefix sums over the work-group in one pass (one pair of barriers).
+template <int NT>
 __device__ __forceinline__ void wg_inclusive_scan2(int& a, int& b, SelShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -89,7 +96,7 @@ __device__ __forceinline__ void wg_inclusive_scan2(int& a, int& b, SelShared& sh
   __syncthreads();
   int ba = 0, bb = 0;
 #pragma unroll
-  for (int w = 0; w < kWavesSel; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     ba += (w < wave) ? sh.wave_sum[w] : 0;
     bb += (w < wave) ? sh.wave_sum2[w] : 0;
   }
@@ -115,6 +122,7 @@ struct ListIds {
 };
 
 // Work-group min and max of one u32 per thread.
+template <int NT>
 __device__ __forceinline__ void wg_minmax(uint32_t lo, uint32_t hi, SelShared& sh, uint32_t& glo,
                                           uint32_t& ghi) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -131,7 +139,7 @@ __device__ __forceinline__ void wg_minmax(uint32_t lo, uint32_t hi, SelShared& s
   glo = sh.wmin[0];
   ghi = sh.wmax[0];
 #pragma unroll
-  for (int w = 1; w < kWavesSel; ++w) {
+  for (int w = 1; w < NT / 64; ++w) {
     glo = min(glo, sh.wmin[w]);
     ghi = max(ghi, sh.wmax[w]);
   }
@@ -167,13 +175,43 @@ struct Binner {
   }
 };
 
+// Bins of the histogram in LDS, from the top: thread i owns bins kBins-1-kBPT*i down to
+// kBins-kBPT*(i+1). For each selection q, the bin holding its k[q]-th element and the
+// number of elements in the bins above it are stored to tb[q] / tabove[q] by the thread
+// that owns that bin (a k beyond the total leaves them untouched).
+template <int NT, int NS>
+__device__ __forceinline__ void find_threshold(const uint32_t* hist, const int (&k)[NS], int* tb,
+                                               int* tabove, SelShared& sh) {
+  constexpr int kBPT = kBins / NT;   // bins per thread
+  const int top = kBins - 1 - kBPT * (int)threadIdx.x;
+  int c[kBPT];
+  int sum = 0;
+#pragma unroll
+  for (int j = 0; j < kBPT; ++j) {
+    c[j] = (int)hist[top - j];
+    sum += c[j];
+  }
+  int tot;
+  int above = wg_inclusive_scan<NT>(sum, sh, tot) - sum;
+#pragma unroll
+  for (int j = 0; j < kBPT; ++j) {
+#pragma unroll
+    for (int q = 0; q < NS; ++q)
+      if (above < k[q] && k[q] <= above + c[j]) {
+        tb[q] = top - j;
+        tabove[q] = above;
+      }
+    above += c[j];
+  }
+}
+
 // The k-th largest key of the valid elements, and through `take_eq` how many elements
 // equal to it are kept. Each round histograms the remaining candidates (keys in [lo, hi])
 // over kBins linear bins of that range, keeps the bin that holds the k-th key, and shrinks
 // [lo, hi] to the keys in that bin; the range strictly shrinks every round (lo and hi
 // always fall in different bins), and spread data needs two or three rounds.
-template <int EPT, class Ids>
-__device__ uint32_t kth_key(const uint32_t (&key)[EPT], const Ids& I, int k, SelShared& sh,
+template <int NT, int EPT, class Ids>
+__device__ __forceinline__ uint32_t kth_key(const uint32_t (&key)[EPT], const Ids& I, int k, SelShared& sh,
                             int& take_eq) {
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
@@ -182,11 +220,11 @@ __device__ uint32_t kth_key(const uint32_t (&key)[EPT], const Ids& I, int k, Sel
       lo = min(lo, key[e]);
       hi = max(hi, key[e]);
     }
-  wg_minmax(lo, hi, sh, lo, hi);
+  wg_minmax<NT>(lo, hi, sh, lo, hi);
   int kk = k;
   while (lo != hi) {
     const Binner bin(lo, hi);
-    for (int i = threadIdx.x; i < kBins; i += kThreads) sh.hist[i] = 0;
+    for (int i = threadIdx.x; i < kBins; i += NT) sh.hist[i] = 0;
     if (threadIdx.x == 0) {
       sh.bin = 0;
       sh.above = 0;
@@ -196,18 +234,9 @@ __device__ uint32_t kth_key(const uint32_t (&key)[EPT], const Ids& I, int k, Sel
     for (int e = 0; e < EPT; ++e)
       if (I.ok(e) && key[e] >= lo && key[e] <= hi) atomicAdd(&sh.hist[bin(key[e])], 1u);
     __syncthreads();
-    // Suffix sums from the top bin: thread i owns bins 2047-2i and 2046-2i.
-    const int d_hi = kBins - 1 - 2 * threadIdx.x, d_lo = d_hi - 1;
-    const int c_hi = (int)sh.hist[d_hi], c_lo = (int)sh.hist[d_lo];
-    int tot;
-    const int incl = wg_inclusive_scan(c_hi + c_lo, sh, tot);
-    const int above_hi = incl - c_hi - c_lo;   // elements in bins above d_hi
-    if (above_hi < kk && kk <= above_hi + c_hi) {
-      sh.bin = d_hi;
-      sh.above = above_hi;
-    } else if (above_hi + c_hi < kk && kk <= above_hi + c_hi + c_lo) {
-      sh.bin = d_lo;
-      sh.above = above_hi + c_hi;
+    {
+      const int kq[1] = {kk};
+      find_threshold<NT, 1>(sh.hist, kq, &sh.bin, &sh.above, sh);
     }
     __syncthreads();
     const uint32_t tb = (uint32_t)sh.bin;
@@ -219,7 +248,7 @@ __device__ uint32_t kth_key(const uint32_t (&key)[EPT], const Ids& I, int k, Sel
         lo2 = min(lo2, key[e]);
         hi2 = max(hi2, key[e]);
       }
-    wg_minmax(lo2, hi2, sh, lo, hi);   // also orders the reads of sh.bin before the next round
+    wg_minmax<NT>(lo2, hi2, sh, lo, hi);   // also orders the reads of sh.bin before the next round
   }
   take_eq = kk;
   return lo;
@@ -228,11 +257,11 @@ __device__ uint32_t kth_key(const uint32_t (&key)[EPT], const Ids& I, int k, Sel
 // Keep the first k of the thread-ordered elements by (key desc, id asc) and write their
 // ids ascending to out[0..k). Every thread's ids must be ascending and precede the next
 // thread's.
-template <int EPT, class Ids>
-__device__ void select_and_emit(const uint32_t (&key)[EPT], const Ids& I, int k, SelShared& sh,
+template <int NT, int EPT, class Ids>
+__device__ __forceinline__ void select_and_emit(const uint32_t (&key)[EPT], const Ids& I, int k, SelShared& sh,
                                 int32_t* out) {
   int take_eq;
-  const uint32_t v = kth_key<EPT, Ids>(key, I, k, sh, take_eq);
+  const uint32_t v = kth_key<NT, EPT, Ids>(key, I, k, sh, take_eq);
   int gt = 0, eq = 0;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
@@ -240,11 +269,11 @@ __device__ void select_and_emit(const uint32_t (&key)[EPT], const Ids& I, int k,
     eq += (I.ok(e) && key[e] == v) ? 1 : 0;
   }
   int tot;
-  int eq_before = wg_inclusive_scan(eq, sh, tot) - eq;
+  int eq_before = wg_inclusive_scan<NT>(eq, sh, tot) - eq;
   int my_eq = take_eq - eq_before;
   my_eq = my_eq < 0 ? 0 : (my_eq > eq ? eq : my_eq);
   int cnt = gt + my_eq;
-  int off = wg_inclusive_scan(cnt, sh, tot) - cnt;
+  int off = wg_inclusive_scan<NT>(cnt, sh, tot) - cnt;
   int seen_eq = 0;
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
@@ -266,8 +295,8 @@ __device__ void select_and_emit(const uint32_t (&key)[EPT], const Ids& I, int k,
 // key > v or (key == v and id <= id_v). Selections whose threshold bin holds more than
 // kColl elements (long runs of equal or clustered keys) fall back to the refinement
 // path above.
-template <int EPT, int NS, class Ids>
-__device__ void multi_select(const uint32_t (&key)[EPT], const Ids& I, const int (&k)[NS],
+template <int NT, int EPT, int NS, class Ids>
+__device__ __forceinline__ void multi_select(const uint32_t (&key)[EPT], const Ids& I, const int (&k)[NS],
                              int32_t* const (&out)[NS], SelShared& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
@@ -277,11 +306,11 @@ __device__ void multi_select(const uint32_t (&key)[EPT], const Ids& I, const int
       lo = min(lo, key[e]);
       hi = max(hi, key[e]);
     }
-  wg_minmax(lo, hi, sh, lo, hi);
+  wg_minmax<NT>(lo, hi, sh, lo, hi);
   bool fast = lo != hi;
   const Binner bin(lo, fast ? hi : lo + 1u);
   if (fast) {
-    for (int i = tid; i < kBins; i += kThreads) sh.hist[i] = 0;
+    for (int i = tid; i < kBins; i += NT) sh.hist[i] = 0;
     if (tid < NS) {
       sh.tb[tid] = 0;
       sh.tabove[tid] = 0;
@@ -292,44 +321,40 @@ __device__ void multi_select(const uint32_t (&key)[EPT], const Ids& I, const int
     for (int e = 0; e < EPT; ++e)
       if (I.ok(e)) atomicAdd(&sh.hist[bin(key[e])], 1u);
     __syncthreads();
-    const int d_hi = kBins - 1 - 2 * tid, d_lo = d_hi - 1;
-    const int c_hi = (int)sh.hist[d_hi], c_lo = (int)sh.hist[d_lo];
-    int tot;
-    const int above_hi = wg_inclusive_scan(c_hi + c_lo, sh, tot) - c_hi - c_lo;
-#pragma unroll
-    for (int q = 0; q < NS; ++q) {
-      if (above_hi < k[q] && k[q] <= above_hi + c_hi) {
-        sh.tb[q] = d_hi;
-        sh.tabove[q] = above_hi;
-      } else if (above_hi + c_hi < k[q] && k[q] <= above_hi + c_hi + c_lo) {
-        sh.tb[q] = d_lo;
-        sh.tabove[q] = above_hi + c_hi;
-      }
-    }
+    find_threshold<NT, NS>(sh.hist, k, sh.tb, sh.tabove, sh);
     __syncthreads();
 #pragma unroll
     for (int q = 0; q < NS; ++q) fast = fast && (int)sh.hist[sh.tb[q]] <= kColl;
   }
   if (!fast) {
 #pragma unroll
-    for (int q = 0; q < NS; ++q) select_and_emit<EPT, Ids>(key, I, k[q], sh, out[q]);
+    for (int q = 0; q < NS; ++q) select_and_emit<NT, EPT, Ids>(key, I, k[q], sh, out[q]);
     return;
   }
   // collect the threshold bins' elements
   int tbq[NS];
 #pragma unroll
   for (int q = 0; q < NS; ++q) tbq[q] = sh.tb[q];
+  // (wave-level compaction: one LDS atomic per wave and element index that has matches)
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
-    if (!I.ok(e)) continue;
-    const int b = (int)bin(key[e]);
+    const int b = I.ok(e) ? (int)bin(key[e]) : -1;
 #pragma unroll
-    for (int q = 0; q < NS; ++q)
-      if (b == tbq[q]) {
-        const int slot = atomicAdd(&sh.ncoll[q], 1);
-        sh.ckey[q][slot] = key[e];
-        sh.cid[q][slot] = I.id(e);
+    for (int q = 0; q < NS; ++q) {
+      const bool match = b == tbq[q];
+      const uint64_t bal = __ballot(match);
+      if (bal != 0) {
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&sh.ncoll[q], __popcll(bal));
+        base = __builtin_amdgcn_readfirstlane(base);
+        if (match) {
+          const int slot = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+          sh.ckey[q][slot] = key[e];
+          sh.cid[q][slot] = I.id(e);
+        }
       }
+    }
   }
   __syncthreads();
   // wave q ranks selection q's collected elements: the one with rank kk-1 is the k-th
@@ -371,128 +396,249 @@ __device__ void multi_select(const uint32_t (&key)[EPT], const Ids& I, const int
   int off[NS];
   if constexpr (NS == 2) {
     int a = cnt[0], b = cnt[1];
-    wg_inclusive_scan2(a, b, sh);
+    wg_inclusive_scan2<NT>(a, b, sh);
     off[0] = a - cnt[0];
     off[1] = b - cnt[1];
   } else {
     int tot;
-    off[0] = wg_inclusive_scan(cnt[0], sh, tot) - cnt[0];
+    off[0] = wg_inclusive_scan<NT>(cnt[0], sh, tot) - cnt[0];
   }
+  // kept ids go to their offsets in an LDS staging area, then out in 16-byte stores
+  int sbase[NS];
+  sbase[0] = 0;
+  if constexpr (NS == 2) sbase[1] = k[0];
 #pragma unroll
   for (int e = 0; e < EPT; ++e) {
     if (!I.ok(e)) continue;
 #pragma unroll
     for (int q = 0; q < NS; ++q)
-      if ((key[e] > v[q] || (key[e] == v[q] && I.id(e) <= vi[q])) && off[q] < k[q]) out[q][off[q]++] = I.id(e);
+      if ((key[e] > v[q] || (key[e] == v[q] && I.id(e) <= vi[q])) && off[q] < k[q])
+        sh.stage[sbase[q] + off[q]++] = I.id(e);
   }
+  __syncthreads();
+  // exactly k[q] ids were kept (the k-th element exists); k and the outputs are 16-byte aligned
+#pragma unroll
+  for (int q = 0; q < NS; ++q)
+    for (int i = 4 * tid; i < k[q]; i += 4 * NT)
+      *reinterpret_cast<int4*>(out[q] + i) = *reinterpret_cast<const int4*>(&sh.stage[sbase[q] + i]);
 }
 
 // ---------------------------------------------------------------------------------------
-// S2 + S3 in one work-group per query.
-//   S2: the 2048 candidate blocks (block maxima from block_max, or recomputed from scores).
-//   S3: the top-512 positions inside the candidates. By the candidate-stage lemma (a
-//       position among the best k of a union of blocks lies in one of the best k blocks,
-//       blocks ranked by (block max desc, block id asc)), the top-512 inside the 2048
-//       candidates lie inside the best 512 blocks, so S3 only reads those 512 "core"
-//       blocks (4096 scores) and returns the same set.
+// S3: the top-512 positions inside the candidates. By the candidate-stage lemma (a
+// position among the best k of a union of blocks lies in one of the best k blocks, blocks
+// ranked by (block max desc, block id asc)), the top-512 inside the 2048 candidates lie
+// inside the best 512 blocks, so S3 only reads those 512 "core" blocks (4096 scores) and
+// returns the same set. Each thread holds 16 (or 4) consecutive positions of the core.
 // ---------------------------------------------------------------------------------------
+template <int NT>
+__device__ __forceinline__ void select_core(const SelectArgs& a, int t, int64_t n, const int32_t* core, SelShared& sh) {
+  int32_t* out = a.topk + (int64_t)t * kTopK;
+  if (n <= kTopK) {  // every visible position is selected
+    for (int i = threadIdx.x; i < kTopK; i += NT) out[i] = i < n ? i : -1;
+    return;
+  }
+  constexpr int E3 = (kTopK * kBlock) / NT;   // positions per thread: 16 (256 threads) or 4
+  const float* row = a.scores + (int64_t)t * a.ld_scores;
+  uint32_t key[E3];
+  ListIds<E3> I;
+  // a block's 8 scores are contiguous and 32-byte aligned inside the row
+  auto load4 = [&](int cb, int half, int e0) {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (cb >= 0) v = *reinterpret_cast<const f32x4*>(row + (int64_t)cb * kBlock + 4 * half);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t p = (int64_t)cb * kBlock + 4 * half + j;
+      I.valid[e0 + j] = cb >= 0 && p < n;
+      I.ids[e0 + j] = (int32_t)p;
+      key[e0 + j] = order_key(v[j]);
+    }
+  };
+  if constexpr (E3 >= kBlock) {   // whole core blocks E3/8 * tid ..
+#pragma unroll
+    for (int u = 0; u < E3 / kBlock; ++u) {
+      const int cb = core[(E3 / kBlock) * threadIdx.x + u];
+      load4(cb, 0, 8 * u);
+      load4(cb, 1, 8 * u + 4);
+    }
+  } else {                        // half of core block tid/2
+    load4(core[threadIdx.x >> 1], threadIdx.x & 1, 0);
+  }
+  const int ks[1] = {kTopK};
+  int32_t* const outs[1] = {out};
+  multi_select<NT, E3, 1>(key, I, ks, outs, sh);
+  // n > 512 here and the core holds at least 512 visible positions: 512 ids written.
+}
+
+// Block max of block b of query t (from block_max, or recomputed from the scores).
+__device__ __forceinline__ float block_value(const SelectArgs& a, int t, int64_t n, int b) {
+  if (a.block_max) return a.block_max[(int64_t)t * a.ld_block_max + b];
+  const float* row = a.scores + (int64_t)t * a.ld_scores + (int64_t)b * kBlock;
+  float m = neg_inf();
+  for (int j = 0; j < kBlock; ++j)
+    if ((int64_t)b * kBlock + j < n) m = fmaxf(m, row[j]);
+  return m;
+}
+
+// Keys of the contiguous blocks I.base .. I.base+EPT-1 (invalid ones 0).
 template <int EPT>
-__global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
+__device__ __forceinline__ void load_block_keys(const SelectArgs& a, int t, int64_t n, const ContigIds<EPT>& I,
+                                                uint32_t (&key)[EPT]) {
+  static_assert(EPT % 4 == 0, "runs of whole 16-byte loads");
+  if (a.block_max) {
+    // rows are 16-byte aligned (ld_block_max % 4 == 0), runs start at multiples of 4
+    const float* row = a.block_max + (int64_t)t * a.ld_block_max + I.base;
+#pragma unroll
+    for (int q = 0; q < EPT / 4; ++q) {
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (I.base + 4 * q < I.limit) v = *reinterpret_cast<const f32x4*>(row + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) key[4 * q + e] = I.ok(4 * q + e) ? order_key(v[e]) : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) key[e] = I.ok(e) ? order_key(block_value(a, t, n, I.base + e)) : 0u;
+  }
+}
+
+// S2 + S3 in one work-group of NT threads per query, for at most NT * EPT blocks.
+template <int NT, int EPT>
+__global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   __shared__ SelShared sh;
-  __shared__ int32_t core[kTopK];
+  __shared__ __attribute__((aligned(16))) int32_t core[kTopK];
   const int t = blockIdx.x;
   const int64_t n = visible_n(a.m, t);
   const int nb = (int)((n + kBlock - 1) / kBlock);
   int32_t* cand = a.cand + (int64_t)t * kCandBlocks;
 
-  // ---- S2: candidate blocks, and the 512 core blocks ----
   if (nb <= kCandBlocks)
-    for (int i = threadIdx.x; i < kCandBlocks; i += kThreads) cand[i] = i < nb ? i : -1;
+    for (int i = threadIdx.x; i < kCandBlocks; i += NT) cand[i] = i < nb ? i : -1;
   if (nb <= kTopK) {
-    for (int i = threadIdx.x; i < kTopK; i += kThreads) core[i] = i < nb ? i : -1;
+    for (int i = threadIdx.x; i < kTopK; i += NT) core[i] = i < nb ? i : -1;
   } else {
     uint32_t key[EPT];
-    ContigIds<EPT> I{(int)threadIdx.x * EPT, nb};
-    if (a.block_max) {
-      // rows are 16-byte aligned (ld_block_max % 4 == 0) and hold at least nb entries
-      const float* row = a.block_max + (int64_t)t * a.ld_block_max + I.base;
-#pragma unroll
-      for (int q = 0; q < EPT / 4; ++q) {
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (I.base + 4 * q < nb) v = *reinterpret_cast<const f32x4*>(row + 4 * q);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) key[4 * q + e] = order_key(v[e]);
-      }
-    } else {
-      const float* row = a.scores + (int64_t)t * a.ld_scores;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        float m = neg_inf();
-        if (I.ok(e)) {
-          for (int j = 0; j < kBlock; ++j) {
-            const int64_t p = (int64_t)(I.base + e) * kBlock + j;
-            if (p < n) m = fmaxf(m, row[p]);
-          }
-        }
-        key[e] = I.ok(e) ? order_key(m) : 0u;
-      }
-    }
+    const ContigIds<EPT> I{(int)threadIdx.x * EPT, nb};
+    load_block_keys<EPT>(a, t, n, I, key);
     if (nb > kCandBlocks) {
       const int ks[2] = {kCandBlocks, kTopK};
       int32_t* const outs[2] = {cand, core};
-      multi_select<EPT, 2>(key, I, ks, outs, sh);
+      multi_select<NT, EPT, 2>(key, I, ks, outs, sh);
     } else {
       const int ks[1] = {kTopK};
       int32_t* const outs[1] = {core};
-      multi_select<EPT, 1>(key, I, ks, outs, sh);
+      multi_select<NT, EPT, 1>(key, I, ks, outs, sh);
     }
   }
   __syncthreads();
+  select_core<NT>(a, t, n, core, sh);
+}
 
-  // ---- S3: top-512 positions; thread i holds 4 positions of core block i/2 ----
-  int32_t* out = a.topk + (int64_t)t * kTopK;
-  if (n <= kTopK) {  // every visible position is selected
-    for (int i = threadIdx.x; i < kTopK; i += kThreads) out[i] = i < n ? i : -1;
+// Two-level S2, first level: work-group (t, p) keeps the best 2048 of blocks
+// [p*kPartBlocks, (p+1)*kPartBlocks) and writes their ids ascending to its part list
+// (-1 after the last).
+template <int NT, int EPT>
+__global__ __launch_bounds__(NT) void select_part_kernel(SelectArgs a) {
+  __shared__ SelShared sh;
+  const int t = blockIdx.y, p = blockIdx.x;
+  const int64_t n = visible_n(a.m, t);
+  const int nb = (int)((n + kBlock - 1) / kBlock);
+  const int b0 = p * kPartBlocks;
+  const int b1 = min(nb, b0 + kPartBlocks);
+  int32_t* out = a.part_ids + ((int64_t)t * a.parts + p) * kCandBlocks;
+  if (b1 - b0 <= kCandBlocks) {
+    for (int i = threadIdx.x; i < kCandBlocks; i += NT) out[i] = b0 + i < b1 ? b0 + i : -1;
     return;
   }
-  constexpr int E3 = 4;
-  const float* row = a.scores + (int64_t)t * a.ld_scores;
-  const int cb = core[threadIdx.x >> 1];
-  const int half = threadIdx.x & 1;
-  uint32_t key[E3];
-  ListIds<E3> I;
-  // a block's 8 scores are contiguous and 32-byte aligned inside the row
-  f32x4 v = {0.f, 0.f, 0.f, 0.f};
-  if (cb >= 0) v = *reinterpret_cast<const f32x4*>(row + (int64_t)cb * kBlock + 4 * half);
+  uint32_t key[EPT];
+  const ContigIds<EPT> I{b0 + (int)threadIdx.x * EPT, b1};
+  load_block_keys<EPT>(a, t, n, I, key);
+  const int ks[1] = {kCandBlocks};
+  int32_t* const outs[1] = {out};
+  multi_select<NT, EPT, 1>(key, I, ks, outs, sh);
+}
+
+// Two-level S2, second level: the union of a query's part lists (ids ascending part after
+// part) holds its best 2048 blocks; select them and the 512 core blocks, then S3.
+template <int NT, int EPT>
+__global__ __launch_bounds__(NT) void select_merge_kernel(SelectArgs a) {
+  __shared__ SelShared sh;
+  __shared__ __attribute__((aligned(16))) int32_t core[kTopK];
+  const int t = blockIdx.x;
+  const int64_t n = visible_n(a.m, t);
+  const int nb = (int)((n + kBlock - 1) / kBlock);
+  int32_t* cand = a.cand + (int64_t)t * kCandBlocks;
+  if (nb <= kCandBlocks) {
+    for (int i = threadIdx.x; i < kCandBlocks; i += NT) cand[i] = i < nb ? i : -1;
+    if (nb <= kTopK) {
+      for (int i = threadIdx.x; i < kTopK; i += NT) core[i] = i < nb ? i : -1;
+    } else {
+      // nb in (512, 2048]: all blocks are candidates, the best 512 are the core
+      constexpr int E = kCandBlocks / NT < 4 ? 4 : kCandBlocks / NT;
+      uint32_t key[E];
+      const ContigIds<E> I{(int)threadIdx.x * E, nb};
+      load_block_keys<E>(a, t, n, I, key);
+      const int ks[1] = {kTopK};
+      int32_t* const outs[1] = {core};
+      multi_select<NT, E, 1>(key, I, ks, outs, sh);
+    }
+  } else {
+    const int32_t* lists = a.part_ids + (int64_t)t * a.parts * kCandBlocks;
+    const int total = a.parts * kCandBlocks;
+    uint32_t key[EPT];
+    ListIds<EPT> I;
 #pragma unroll
-  for (int j = 0; j < E3; ++j) {
-    const int64_t p = (int64_t)cb * kBlock + 4 * half + j;
-    I.valid[j] = cb >= 0 && p < n;
-    I.ids[j] = (int32_t)p;
-    key[j] = order_key(v[j]);
+    for (int e = 0; e < EPT; ++e) {
+      const int i = (int)threadIdx.x * EPT + e;
+      const int32_t b = i < total ? lists[i] : -1;
+      I.valid[e] = b >= 0;
+      I.ids[e] = b;
+      key[e] = b >= 0 ? order_key(block_value(a, t, n, b)) : 0u;
+    }
+    const int ks[2] = {kCandBlocks, kTopK};
+    int32_t* const outs[2] = {cand, core};
+    multi_select<NT, EPT, 2>(key, I, ks, outs, sh);
   }
-  {
-    const int ks[1] = {kTopK};
-    int32_t* const outs[1] = {out};
-    multi_select<E3, 1>(key, I, ks, outs, sh);
+  __syncthreads();
+  select_core<NT>(a, t, n, core, sh);
+}
+
+template <int NT>
+hipError_t launch_select_nt(const SelectArgs& a, hipStream_t stream) {
+  const int64_t nbmax = (a.m.max_visible + kBlock - 1) / kBlock;
+  const dim3 grid((unsigned)a.m.T);
+  // blocks per thread: a multiple of 4 (16-byte loads), at least 4
+  constexpr int E1 = 2048 / NT < 4 ? 4 : 2048 / NT, E2 = 4096 / NT < 4 ? 4 : 4096 / NT;
+  if (a.parts <= 1) {
+    if (nbmax <= NT * E1)
+      hipLaunchKernelGGL((select_kernel<NT, E1>), grid, dim3(NT), 0, stream, a);
+    else if (nbmax <= NT * E2)
+      hipLaunchKernelGGL((select_kernel<NT, E2>), grid, dim3(NT), 0, stream, a);
+    else
+      hipLaunchKernelGGL((select_kernel<NT, kPartBlocks / NT>), grid, dim3(NT), 0, stream, a);
+    return hipGetLastError();
   }
-  // n > 512 here and the core holds at least 512 visible positions: 512 ids written.
+  hipLaunchKernelGGL((select_part_kernel<NT, kPartBlocks / NT>), dim3((unsigned)a.parts, (unsigned)a.m.T),
+                     dim3(NT), 0, stream, a);
+  const int per_thread = a.parts * kCandBlocks / NT;
+  if (per_thread <= 16 * 256 / NT)
+    hipLaunchKernelGGL((select_merge_kernel<NT, 16 * 256 / NT>), grid, dim3(NT), 0, stream, a);
+  else if (per_thread <= 32 * 256 / NT)
+    hipLaunchKernelGGL((select_merge_kernel<NT, 32 * 256 / NT>), grid, dim3(NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((select_merge_kernel<NT, 64 * 256 / NT>), grid, dim3(NT), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
+int select_parts(int64_t max_visible) {
+  const int64_t nb = (max_visible + kBlock - 1) / kBlock;
+  return nb <= kPartBlocks ? 1 : (int)((nb + kPartBlocks - 1) / kPartBlocks);
+}
+
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
-  const int64_t nbmax = (a.m.max_visible + kBlock - 1) / kBlock;
-  const dim3 grid((unsigned)a.m.T);
-  if (nbmax <= 8 * kThreads)
-    hipLaunchKernelGGL(select_kernel<8>, grid, dim3(kThreads), 0, stream, a);
-  else if (nbmax <= 16 * kThreads)
-    hipLaunchKernelGGL(select_kernel<16>, grid, dim3(kThreads), 0, stream, a);
-  else if (nbmax <= 32 * kThreads)
-    hipLaunchKernelGGL(select_kernel<32>, grid, dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(select_kernel<64>, grid, dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  // few queries: one large work-group each (the latency of a query is the kernel time);
+  // many queries: small work-groups, several per CU
+  return a.m.T < 1024 ? launch_select_nt<1024>(a, stream) : launch_select_nt<256>(a, stream);
 }
 
 }  // namespace sa

@@ -175,6 +175,45 @@ def test_select_exact_on_given_scores_with_ties():
             assert np.array_equal(cand[t][cand[t] >= 0], c_ref), t
 
 
+@pytest.mark.parametrize("T,n_lo,n_hi", [(1040, 16500, 24000), (6, 66000, 140000)])
+def test_select_many_queries_and_long_rows(T, n_lo, n_hi):
+    """Selection alone on given fp32 scores with ties: 1040 queries (the small-work-group
+    kernels used for large batches) and rows past 65536 positions (the two-level candidate
+    stage), against the oracle's selection on the same values; exact integer results."""
+    from sparse_attention_score_amd import Plan, Queries, select_topk
+    rng = np.random.default_rng(23 + T)
+    n = rng.integers(n_lo, n_hi, T)
+    n[0] = n_hi   # one row at the maximum
+    E = int(-(-n.max() // 8) * 8)
+    plan = Plan(ratio=1, max_queries=T, max_compressed=int(n.max()))
+    seq = torch.zeros(T, dtype=torch.int32, device="cuda")
+    pos = torch.from_numpy((n - 1).astype(np.int32)).cuda()
+    qs = Queries(seq, pos, int(n.max()))
+    S = np.full((T, E), -np.inf, np.float32)
+    for t in range(T):
+        S[t, :n[t]] = rng.integers(0, 200, n[t]).astype(np.float32) * np.float32(0.5)
+    scores = torch.from_numpy(S).cuda()
+    bm_np = np.full((T, (E // 8 + 3) // 4 * 4), -np.inf, np.float32)
+    for t in range(T):
+        nb = -(-int(n[t]) // 8)
+        pad = np.full(nb * 8, -np.inf, np.float32)
+        pad[:n[t]] = S[t, :n[t]]
+        bm_np[t, :nb] = pad.reshape(nb, 8).max(axis=1)
+    block_max = torch.from_numpy(bm_np).cuda()
+    topk = torch.empty((T, 512), dtype=torch.int32, device="cuda")
+    cand = torch.empty((T, 2048), dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(16, plan.workspace_bytes), dtype=torch.uint8, device="cuda")
+    print(f"[case] select T={T} n={n.min()}..{n.max()} workspace={plan.workspace_bytes}", flush=True)
+    for use_bm in (True, False):
+        select_topk(plan, qs, scores, block_max if use_bm else None, topk, cand=cand, workspace=ws)
+        torch.cuda.synchronize()
+        tk, cd = topk.cpu().numpy(), cand.cpu().numpy()
+        for t in range(0, T, max(1, T // 40)):
+            c_ref, i_ref = O.select(S[t, :n[t]].astype(np.float64))
+            assert np.array_equal(tk[t][tk[t] >= 0], i_ref), (use_bm, t)
+            assert np.array_equal(cd[t][cd[t] >= 0], c_ref), (use_bm, t)
+
+
 def test_select_all_ties_takes_lowest():
     from sparse_attention_score_amd.step import DeviceBatch
     wl = W.make_decode(B=2, n_raw=[2 * 30000, 2 * 300], ratio=2, name="zero-w", with_compress=False, seed=2)
