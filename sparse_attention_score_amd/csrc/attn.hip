@@ -7,33 +7,36 @@
 // Flash" Miles docs, section 1 Model Introduction; one softmax over both tiers, recipe
 // Overview, two-tier sparse attention bullet).
 //
-// One work-group (4 waves) per query, so every gathered row is read from memory once for
-// all 64 heads. Rows are gathered 32 per step into LDS tiles by direct global-to-LDS loads
-// (no registers), kDepth steps ahead of the step being computed.
-//   scores: wave w owns heads 16w..16w+15: S^T[32 keys][16 heads] with
-//           v_mfma_f32_16x16x32_bf16, A = key rows from LDS, B = the wave's query heads held
-//           in registers (16 k-steps over the 512 dims); lane (c, g) ends with keys 4g..4g+3
-//           and 16+4g..16+4g+3 of head c.
+// One work-group (8 waves, two per SIMD) per query, so every gathered row is read from
+// memory once for all 64 heads. Rows are gathered 32 per step into LDS tiles by direct
+// global-to-LDS loads (no registers), kDepth steps ahead of the step being computed.
 //   softmax: in the log2 domain against a fixed reference per head, the max of the first
 //           step's scores (softmax does not depend on the reference, and P and the fp32 sums
-//           have the range of fp32), so the output is never rescaled. If a later score
-//           exceeds the reference by more than kSafe, the query is run again with the true
-//           max as reference. The max over a step's keys of a head is an in-lane max plus
-//           two lane swaps. The lane's 8 probabilities, packed, are exactly the P^T operand
-//           of its head group (the MFMA k order is free as long as A uses the same one);
-//           they go to LDS.
-//   values: wave w owns output dims 128w..128w+127 of all 64 heads: O^T += V^T P^T with
+//           have the range of fp32), so the output is never rescaled and waves holding
+//           different keys of a head need not exchange maxima. If a later score exceeds the
+//           reference by more than kSafe, the query is run again with the true max.
+//   scores: wave (hg, kh) = (w % 4, w / 4) takes heads 16hg..16hg+15 and keys 16kh..16kh+15
+//           of the step: S^T with v_mfma_f32_16x16x32_bf16, A = key rows from LDS, B = the
+//           query heads held in registers (16 k-steps over the 512 dims); lane (c, g) ends
+//           with keys 4g..4g+3 of head c. Its 4 probabilities, packed, are half of the P^T
+//           operand of the head group (the MFMA k order is free as long as A uses the same
+//           one); they go to LDS.
+//   values: wave w owns output dims 64w..64w+63 of all 64 heads: O^T += V^T P^T with
 //           A = V^T built from LDS rows by byte permutes (8 keys x 1 dim per lane), each value
 //           element read from LDS once per step, and B = P^T of each head group.
+// The values of step s and the scores of step s+1 are independent and run in the same
+// loop iteration, with one barrier per step.
 #include "sa_device.h"
 #include "sa_launch.h"
 
 namespace sa {
 namespace {
 
-constexpr int kAW = 4;              // waves; wave w owns heads 16w..16w+15
+constexpr int kAW = 8;              // waves
 constexpr int kAThreads = 64 * kAW;
+constexpr int kHG = 4;              // head groups of 16
 constexpr int kKT = 32;             // keys per step
+constexpr int kRowsPerWave = kKT / kAW;
 constexpr int kRow = kDim * 2 + 32; // padded LDS row bytes (+32: conflict-free 16-row reads)
 constexpr int kMaxKeys = kTopK + kWindow;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -44,14 +47,15 @@ constexpr int kBufs = kDepth + 1;   // LDS tiles
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8;
 // expcnt and lgkmcnt left at their maxima = no wait)
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-constexpr int kWaitLater = waitcnt_vm(8 * (kDepth - 1));   // all but the kDepth-1 later steps' loads
-constexpr int kWaitNext = waitcnt_vm(8 * (kDepth - 2));    // ... all but kDepth-2 of them
+constexpr int kWaitLater = waitcnt_vm(kRowsPerWave * (kDepth - 1));   // all but kDepth-1 later steps
+constexpr int kWaitNext = waitcnt_vm(kRowsPerWave * (kDepth - 2));    // all but kDepth-2 later steps
 constexpr int kWaitAll = waitcnt_vm(0);
 
 struct AttnShared {
   uint8_t tile[kBufs][kKT * kRow];     // 135,168 B
   const uint16_t* rows[kMaxKeys];      // global row of every key slot
-  u32x4 P[2][kAW][64];                 // P^T operand of each head group per lane, two steps
+  u32x4 P[2][kHG][64];                 // P^T operand of each head group per lane, two steps
+  float tmax[2][kHeads];               // step-0 maxima per key half / partial normalisers
   float norm[kHeads];                  // final normaliser of each head
   int wave_cnt[kAW];
   int redo[kAW];                       // per wave: a score exceeded its reference by > kSafe
@@ -91,6 +95,8 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   if ((int)(blockIdx.x >> 3) >= q8 || t >= T) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int c = lane & 15, g = lane >> 4;
+  const int hg = wave & (kHG - 1), kh = wave / kHG;   // scores role
+  const int d0 = 64 * wave;                           // values role
 
   const int seq = a.m.seq_id[t], p = a.m.pos[t];
   const bool valid_q = seq >= 0 && seq < a.m.num_seqs && p >= 0;
@@ -104,11 +110,9 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   // ---- key list: selected latents in topk order, then the window ----
   int m = 0;
   if (valid_q) {
-    const int32_t* tk = a.topk + (int64_t)t * kTopK;
-    const int2 jj = *reinterpret_cast<const int2*>(tk + 2 * tid);
-    const bool v0 = jj.x >= 0 && jj.x < n, v1 = jj.y >= 0 && jj.y < n;
-    const int cnt = (int)v0 + (int)v1;
-    int incl = cnt;
+    const int32_t j = a.topk[(int64_t)t * kTopK + tid];   // kAThreads == kTopK
+    const bool v = j >= 0 && j < n;
+    int incl = (int)v;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       int o = __shfl_up(incl, d, 64);
@@ -122,9 +126,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       before += (w < wave) ? sh.wave_cnt[w] : 0;
     }
     const uint16_t* lat = reinterpret_cast<const uint16_t*>(a.latents) + (int64_t)seq * a.latents_seq_stride;
-    int off = before + incl - cnt;
-    if (v0) sh.rows[off++] = lat + (int64_t)jj.x * kDim;
-    if (v1) sh.rows[off] = lat + (int64_t)jj.y * kDim;
+    if (v) sh.rows[before + incl - 1] = lat + (int64_t)j * kDim;
     const int u0 = p - kWindow + 1 > 0 ? p - kWindow + 1 : 0;
     const int nwin = p - u0 + 1;
     const uint16_t* win = reinterpret_cast<const uint16_t*>(a.window) + (int64_t)seq * a.window_seq_stride;
@@ -133,7 +135,6 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  const int head0 = 16 * wave;   // this wave's heads
   if (m == 0) {  // invalid query: zero output, lse = -inf
     uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (int64_t)t * kHeads * kDim;
     for (int i = tid; i < kHeads * kDim / 8; i += kAThreads)
@@ -142,171 +143,191 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
     return;
   }
 
-  // ---- query heads head0 + c as the B operand (k-step s: dims (4s+g)*8 .. +8) ----
+  // ---- query heads 16hg + c as the B operand (k-step s: dims (4s+g)*8 .. +8) ----
   bf16x8 qb[16];
   {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)t * kHeads + head0 + c) * kDim;
+    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)t * kHeads + 16 * hg + c) * kDim;
 #pragma unroll
     for (int s = 0; s < 16; ++s) qb[s] = *reinterpret_cast<const bf16x8*>(qrow + (4 * s + g) * 8);
   }
 
-  // ---- tile loader: wave w moves rows 8w..8w+7 of a step (8 row loads). Rows past the
-  // key list repeat the last real row (finite data; their scores are masked), so every
-  // wave issues exactly 8 loads per step and the wait counts below are constants.
+  // ---- tile loader: wave w moves rows 4w..4w+3 of a step. Rows past the key list repeat
+  // the last real row (finite data; their scores are masked), so every wave issues exactly
+  // kRowsPerWave loads per step and the wait counts are constants.
   const uint32_t tile0 = (uint32_t)(uintptr_t)&sh.tile[0][0];
   auto issue = [&](int step) {
-    const uint32_t base = tile0 + (uint32_t)((step % kBufs) * (kKT * kRow) + wave * 8 * kRow);
-    const uint16_t* r[8];
+    const uint32_t base = tile0 + (uint32_t)((step % kBufs) * (kKT * kRow) + wave * kRowsPerWave * kRow);
+    const uint16_t* r[kRowsPerWave];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = sh.rows[min(step * kKT + wave * 8 + i, m - 1)];
+    for (int i = 0; i < kRowsPerWave; ++i) r[i] = sh.rows[min(step * kKT + wave * kRowsPerWave + i, m - 1)];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) row_to_lds(r[i], base + i * kRow, lane);
+    for (int i = 0; i < kRowsPerWave; ++i) row_to_lds(r[i], base + i * kRow, lane);
   };
 
-  // O^T accumulators [head group][e]: dims d0 + 8r + e (r = MFMA row) of head 16hg + c
-  const int d0 = 128 * wave;
-  f32x4 O[kAW][8];
-  float m_ref = neg_inf();   // reference of head head0 + c (log2 domain)
-  float m_max = neg_inf();   // max score of that head so far
+  // O^T accumulators [head group][e4]: dims d0 + 4r + e4 (r = MFMA row) of head 16hg' + c
+  f32x4 O[kHG][4];
+  float m_ref = neg_inf();   // reference of head 16hg + c (log2 domain), common to both key halves
+  float m_max = neg_inf();   // max score of that head over this wave's keys so far
   float l_run = 0.f;         // this lane's part of that head's normaliser
   const float sc2 = a.scale * kLog2e;
   const int nsteps = (m + kKT - 1) / kKT;
+
+  // Scores and softmax of step `step` for (hg, kh): P to LDS buffer step & 1. Keys past m
+  // (and whole steps past the last) come out with P = 0. Returns the keys' max.
+  auto scores = [&](int step) -> float {
+    const uint8_t* T8 = sh.tile[step % kBufs];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const uint8_t* krow = T8 + (16 * kh + c) * kRow;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + (4 * s + g) * 16);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[s], acc, 0, 0, 0);
+    }
+    float x[4];
+    float mt = neg_inf();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = step * kKT + 16 * kh + 4 * g + i;
+      x[i] = k < m ? acc[i] * sc2 : neg_inf();
+      mt = fmaxf(mt, x[i]);
+    }
+    mt = max_xor32(max_xor16(mt));   // all four lane groups of head c agree
+    m_max = fmaxf(m_max, mt);
+    float pv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = __builtin_amdgcn_exp2f(x[i] - m_ref);
+      l_run += pv[i];
+    }
+    // k-slots 0..3 of the P^T operand come from key half 0, 4..7 from key half 1
+    uint32_t* dst = reinterpret_cast<uint32_t*>(&sh.P[step & 1][hg][lane]) + 2 * kh;
+    dst[0] = pack_bf16x2(pv[0], pv[1]);
+    dst[1] = pack_bf16x2(pv[2], pv[3]);
+    return mt;
+  };
+  // O^T[dims d0 + 4r + e4][head 16hg' + c] += V^T P^T for step `step`
+  auto values = [&](int step) {
+    const uint8_t* T8 = sh.tile[step % kBufs];
+    bf16x8 pb[kHG];
+#pragma unroll
+    for (int h = 0; h < kHG; ++h) pb[h] = __builtin_bit_cast(bf16x8, sh.P[step & 1][h][lane]);
+    // key slot j: dims d0 + 4c .. +3 (two dwords)
+    uint32_t R[8][2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int key = (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4));
+      const uint2 v = *reinterpret_cast<const uint2*>(T8 + key * kRow + (d0 + 4 * c) * 2);
+      R[j][0] = v.x;
+      R[j][1] = v.y;
+    }
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const int w = e4 >> 1;
+      u32x4 va;
+      if (e4 & 1) {
+        va = u32x4{perm_hi(R[1][w], R[0][w]), perm_hi(R[3][w], R[2][w]),
+                   perm_hi(R[5][w], R[4][w]), perm_hi(R[7][w], R[6][w])};
+      } else {
+        va = u32x4{perm_lo(R[1][w], R[0][w]), perm_lo(R[3][w], R[2][w]),
+                   perm_lo(R[5][w], R[4][w]), perm_lo(R[7][w], R[6][w])};
+      }
+      const bf16x8 A = __builtin_bit_cast(bf16x8, va);
+#pragma unroll
+      for (int h = 0; h < kHG; ++h)
+        O[h][e4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pb[h], O[h][e4], 0, 0, 0);
+    }
+  };
 
   // the query loads are complete before the first row load, so the compiler's own waits
   // (which do not count the row loads) never need to reach past them
   __builtin_amdgcn_s_waitcnt(kWaitAll);
 
-  // Scores and softmax of step `step` (tile in LDS buffer step % kBufs): P goes to LDS
-  // buffer step & 1. Keys past m (and whole steps past the last) come out with P = 0.
-  auto scores = [&](int step, int pass) {
-    const uint8_t* T8 = sh.tile[step % kBufs];
-    // S^T[keys 16kt + 4g + i][head c], kt = 0, 1 (two independent chains)
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    const uint8_t* k0row = T8 + c * kRow;
-    const uint8_t* k1row = T8 + (16 + c) * kRow;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const bf16x8 ka0 = *reinterpret_cast<const bf16x8*>(k0row + (4 * s + g) * 16);
-      const bf16x8 ka1 = *reinterpret_cast<const bf16x8*>(k1row + (4 * s + g) * 16);
-      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka0, qb[s], acc0, 0, 0, 0);
-      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka1, qb[s], acc1, 0, 0, 0);
-    }
-    // softmax of head c over the step's keys (slot j < 4: key 4g+j; j >= 4: 16+4g+j-4)
-    float x[8];
-    float mt = neg_inf();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = step * kKT + 4 * g + i;
-      x[i] = k < m ? acc0[i] * sc2 : neg_inf();
-      x[4 + i] = k + 16 < m ? acc1[i] * sc2 : neg_inf();
-      mt = fmaxf(mt, fmaxf(x[i], x[4 + i]));
-    }
-    mt = max_xor32(max_xor16(mt));   // all four lane groups of head c agree
-    if (step == 0 && pass == 0) m_ref = mt;   // step 0 always holds a real key (m >= 1)
-    m_max = fmaxf(m_max, mt);
-    float pv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pv[j] = __builtin_amdgcn_exp2f(x[j] - m_ref);
-      l_run += pv[j];
-    }
-    sh.P[step & 1][wave][lane] = u32x4{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                                       pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7])};
-  };
-  // O^T[dims d0 + 8r + 4half + e4][head 16hg + c] += V^T P^T for step `step`
-  auto values = [&](int step) {
-    const uint8_t* T8 = sh.tile[step % kBufs];
-    bf16x8 pb[kAW];
-#pragma unroll
-    for (int hg = 0; hg < kAW; ++hg) pb[hg] = __builtin_bit_cast(bf16x8, sh.P[step & 1][hg][lane]);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      // key slot j: dims d0 + 8c + 4half .. +3 (two dwords)
-      uint32_t R[8][2];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4));
-        const uint2 v = *reinterpret_cast<const uint2*>(T8 + key * kRow + (d0 + 8 * c + 4 * half) * 2);
-        R[j][0] = v.x;
-        R[j][1] = v.y;
-      }
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int w = e4 >> 1;
-        u32x4 va;
-        if (e4 & 1) {
-          va = u32x4{perm_hi(R[1][w], R[0][w]), perm_hi(R[3][w], R[2][w]),
-                     perm_hi(R[5][w], R[4][w]), perm_hi(R[7][w], R[6][w])};
-        } else {
-          va = u32x4{perm_lo(R[1][w], R[0][w]), perm_lo(R[3][w], R[2][w]),
-                     perm_lo(R[5][w], R[4][w]), perm_lo(R[7][w], R[6][w])};
-        }
-        const bf16x8 A = __builtin_bit_cast(bf16x8, va);
-        const int e = 4 * half + e4;
-#pragma unroll
-        for (int hg = 0; hg < kAW; ++hg)
-          O[hg][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pb[hg], O[hg][e], 0, 0, 0);
-      }
-    }
-  };
-
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int hg = 0; hg < kAW; ++hg)
+    for (int h = 0; h < kHG; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) O[hg][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 4; ++e) O[h][e] = f32x4{0.f, 0.f, 0.f, 0.f};
     l_run = 0.f;
-    if (pass == 1) m_ref = m_max;   // second pass: the true max, so every P <= 1
 #pragma unroll
     for (int j = 0; j < kDepth; ++j) issue(j);
     __builtin_amdgcn_s_waitcnt(kWaitLater);   // step 0's rows (steps 1, 2 in flight)
     __syncthreads();
-    scores(0, pass);
+    if (pass == 0) {
+      // reference: the max of step 0's keys of the head (step 0 always holds a real key),
+      // from both key halves; step 0's P is then computed against it
+      const uint8_t* T8 = sh.tile[0];
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const uint8_t* krow = T8 + (16 * kh + c) * kRow;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + (4 * s + g) * 16);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[s], acc, 0, 0, 0);
+      }
+      float mt = neg_inf();
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (16 * kh + 4 * g + i < m) mt = fmaxf(mt, acc[i] * sc2);
+      mt = max_xor32(max_xor16(mt));
+      if (g == 0) sh.tmax[kh][16 * hg + c] = mt;
+      __syncthreads();
+      m_ref = fmaxf(sh.tmax[0][16 * hg + c], sh.tmax[1][16 * hg + c]);
+    } else {
+      m_ref = m_max;   // second pass: the true max (both halves), so every P <= 1
+      m_max = neg_inf();
+    }
+    scores(0);
 
     // Software pipeline: step s runs the values of step s and the scores of step s+1,
-    // independent work that the wave interleaves. One barrier per step makes visible the
+    // independent work that the waves interleave. One barrier per step makes visible the
     // P of step s, the rows of step s+1 and frees the buffer of step s-1.
     for (int step = 0; step < nsteps; ++step) {
       __builtin_amdgcn_s_waitcnt(kWaitNext);   // step s+1's rows (step s+2's in flight)
       __syncthreads();
       issue(step + kDepth);
       values(step);
-      scores(step + 1, pass);                  // past the last step: P = 0, never read
+      scores(step + 1);                        // past the last step: P = 0, never read
     }
     __builtin_amdgcn_s_waitcnt(kWaitAll);  // no row load may outlive the pass (or the LDS)
     // a second pass only if some head of the query saw a score more than kSafe above its
     // reference (P up to 2^kSafe and the sums stay far inside fp32 range otherwise)
     if (pass == 1) break;
-    if (lane == 0) sh.redo[wave] = __ballot(m_max > m_ref + kSafe) != 0;
+    const bool wave_redo = __ballot(m_max > m_ref + kSafe) != 0;   // over all lanes (heads)
+    if (lane == 0) sh.redo[wave] = wave_redo;
     __syncthreads();
-    if (!(sh.redo[0] | sh.redo[1] | sh.redo[2] | sh.redo[3])) break;
-    __syncthreads();   // every wave read the flags and is done with the tiles
+    int redo = 0;
+    for (int w = 0; w < kAW; ++w) redo |= sh.redo[w];
+    if (!redo) break;
+    // the second pass's reference: the max over both key halves
+    if (g == 0) sh.tmax[kh][16 * hg + c] = m_max;
+    __syncthreads();
+    m_max = fmaxf(sh.tmax[0][16 * hg + c], sh.tmax[1][16 * hg + c]);
+    __syncthreads();   // every wave read the flags and maxima and is done with the tiles
   }
 
-
-  // ---- normaliser of head head0 + c: the four lane groups' parts ----
+  // ---- normaliser of head 16hg + c: both key halves, four lane groups each ----
   {
     const float L = add_xor32(add_xor16(l_run));
-    if (g == 0) {
-      sh.norm[head0 + c] = L;
-      if (a.lse) a.lse[(int64_t)t * kHeads + head0 + c] = (m_ref + __log2f(L)) * kLn2;
+    if (g == 0) sh.tmax[kh][16 * hg + c] = L;
+    __syncthreads();
+    if (kh == 0 && g == 0) {
+      const float Lh = sh.tmax[0][16 * hg + c] + sh.tmax[1][16 * hg + c];
+      sh.norm[16 * hg + c] = Lh;
+      if (a.lse) a.lse[(int64_t)t * kHeads + 16 * hg + c] = (m_ref + __log2f(Lh)) * kLn2;
     }
+    __syncthreads();
   }
-  __syncthreads();
-  // ---- store: lane (c, g) holds dims d0 + 8(4g+i) + e of head 16hg + c ----
+  // ---- store: lane (c, g) holds dims d0 + 4(4g+i) + e4 of head 16h + c ----
 #pragma unroll
-  for (int hg = 0; hg < kAW; ++hg) {
-    const float inv = 1.0f / sh.norm[16 * hg + c];
-    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * kHeads + 16 * hg + c) * kDim + d0;
+  for (int h = 0; h < kHG; ++h) {
+    const float inv = 1.0f / sh.norm[16 * h + c];
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * kHeads + 16 * h + c) * kDim + d0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 4 * g + i;  // row of the MFMA result = group of 8 dims
-      u32x4 o;
-      o[0] = pack_bf16x2(O[hg][0][i] * inv, O[hg][1][i] * inv);
-      o[1] = pack_bf16x2(O[hg][2][i] * inv, O[hg][3][i] * inv);
-      o[2] = pack_bf16x2(O[hg][4][i] * inv, O[hg][5][i] * inv);
-      o[3] = pack_bf16x2(O[hg][6][i] * inv, O[hg][7][i] * inv);
-      *reinterpret_cast<u32x4*>(orow + 8 * r) = o;
+      const int r = 4 * g + i;  // row of the MFMA result = group of 4 dims
+      uint2 o;
+      o.x = pack_bf16x2(O[h][0][i] * inv, O[h][1][i] * inv);
+      o.y = pack_bf16x2(O[h][2][i] * inv, O[h][3][i] * inv);
+      *reinterpret_cast<uint2*>(orow + 4 * r) = o;
     }
   }
 }
