@@ -6,14 +6,16 @@
 // compressed latents). s_j is the fp32 row scale of e4m3 keys (1 for bf16 keys). e4m3 keys
 // are widened to bf16 exactly in registers; the index query stays bf16.
 //
-// Block maxima (blocks of 8 positions) are taken from the same registers with DPP.
+// Block maxima (blocks of 8 positions) are taken in registers with DPP.
 //
-// Decode (every query has its own key stream, HBM-bound): v_mfma_f32_16x16x32_bf16 with
-// the 16 heads of one query as rows (A, in registers) and 16 keys as columns (B, streamed
-// from HBM, kDepth tiles in flight per wave). In the 16x16 result each lane holds heads
-// 4g..4g+3 (g = lane/16) of key lane%16: ReLU and head weights in-lane, then two row-swap
-// adds finish the 16-head sum. The k order inside an MFMA is free (A and B use the same
-// one), so each lane group reads 64 contiguous bytes of a key row.
+// Decode (every query has its own key stream, HBM-bound): each wave streams 16 tiles of 16
+// keys from HBM straight into its own LDS ring (kDepth tiles in flight, no registers held;
+// every load instruction moves 1 KB of whole rows). v_mfma_f32_16x16x32_bf16 then takes the
+// 16 heads of the query as rows (A, in registers) and the tile's 16 keys as columns (B, from
+// LDS). In the 16x16 result each lane holds heads 4g..4g+3 (g = lane/16) of key lane%16:
+// ReLU and head weights in-lane, then two row-swap adds finish the 16-head sum. The k order
+// inside an MFMA is free (A and B use the same one). Scores are staged in LDS and written
+// at the end with their row scales and block maxima, 64 consecutive keys per store.
 //
 // Prefill (a chunk of queries shares one key stream, MFMA-bound): v_mfma_f32_32x32x16_bf16
 // with two queries x 16 heads as rows and 32 keys as columns. Key tiles are staged once per
@@ -53,32 +55,42 @@ constexpr int kDWaves = 4;
 constexpr int kDThreads = 64 * kDWaves;
 constexpr int kTilesPerWave = SA_IDX_TPW;
 constexpr int kKeysPerWG = kDWaves * kTilesPerWave * 16;
-constexpr int kDepth = SA_IDX_DEPTH;
+constexpr int kRingBytes = SA_IDX_DEPTH * 16 * kIdxDim;   // per wave: kDepth e4m3 tiles
+
+// Decode key tiles (16 keys) travel HBM -> LDS by direct loads (no registers): each load
+// instruction moves 1 KB of whole key rows, so every request is full cache lines. Inside a
+// row the 16-byte chunks are stored rotated (chunk q of row r at position q ^ f(r)), which
+// the loads do for free by choosing each lane's source; the B-operand reads (16 rows, one
+// chunk each per lane group) then hit 16 different bank groups.
+template <bool FP8>
+struct DecodeTile {
+  static constexpr int RB = FP8 ? kIdxDim : 2 * kIdxDim;   // row bytes
+  static constexpr int TB = 16 * RB;                       // tile bytes
+  static constexpr int NK = TB / 1024;                     // loads per tile
+  static constexpr int D = kRingBytes / TB;                // tiles in flight per wave
+  static constexpr int CPR = RB / 16;                      // chunks per row
+  // position of chunk q in row r
+  static __device__ __forceinline__ int pos(int r, int q) {
+    return FP8 ? (q ^ ((r & 7) ^ (r >> 3))) : (q ^ r);
+  }
+};
+
+struct DecodeShared {
+  uint8_t ring[kDWaves][kRingBytes];
+  float stage[kDWaves][kTilesPerWave * 16];   // unscaled scores of the wave's keys
+  uint16_t q[kIdxHeads * kIdxDim];
+  float w[kIdxHeads];
+};
 
 // Dims of k-step s (0..3) held by lane group g, in elements. bf16 keys: chunk 4s+g of
-// 8 dims; e4m3 keys: ksteps (2i, 2i+1) share one 16-byte load at byte (4i+g)*16.
+// 8 dims; e4m3 keys: ksteps (2i, 2i+1) share one 16-byte chunk, 4i+g.
 __device__ __forceinline__ int kdim_bf16(int g, int s) { return (4 * s + g) * 8; }
 __device__ __forceinline__ int kdim_fp8(int g, int s) { return ((s >> 1) * 4 + g) * 16 + (s & 1) * 8; }
 
 template <bool FP8>
 struct KeyRegs {
   u32x4 v[FP8 ? 2 : 4];
-  float scale;
 };
-
-template <bool FP8>
-__device__ __forceinline__ void load_keys(KeyRegs<FP8>& K, const uint8_t* tile, const float* tscale,
-                                          uint32_t lane_off, int c) {
-  if constexpr (FP8) {
-    K.v[0] = *reinterpret_cast<const u32x4*>(tile + lane_off);
-    K.v[1] = *reinterpret_cast<const u32x4*>(tile + lane_off + 64);
-    K.scale = tscale[c];
-  } else {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) K.v[s] = *reinterpret_cast<const u32x4*>(tile + lane_off + 64 * s);
-    K.scale = 1.0f;
-  }
-}
 
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t c0, uint32_t c1) {
   uint32_t u0, u1, u2, u3;
@@ -101,101 +113,144 @@ __device__ __forceinline__ f32x4 tile_dots(const bf16x8 (&qa)[4], const KeyRegs<
   return acc;
 }
 
+// 16 bytes per lane from global memory to LDS byte lds + 16 * lane. The compiler does not
+// see these loads; completion is tracked with explicit vmcnt waits, and the kernel issues
+// no other vector-memory operation between the first of them and the last wait.
+__device__ __forceinline__ void to_lds16(const void* src, uint32_t lds) {
+  // s_nop: an LDS-DMA load must not directly follow the write of M0 (one wait state)
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds) : "memory");
+}
+// Same, after every LDS read of this wave has returned (the slot being refilled was just read).
+__device__ __forceinline__ void to_lds16_after_reads(const void* src, uint32_t lds) {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds) : "memory");
+}
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 template <bool FP8>
 __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a) {
+  using DT = DecodeTile<FP8>;
+  constexpr int RB = DT::RB, TB = DT::TB, NK = DT::NK, D = DT::D;
+  static_assert((D & (D - 1)) == 0 && D >= 2, "ring depth must be a power of two");
+  static_assert(D * NK <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) DecodeShared sh;
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int c = lane & 15, g = lane >> 4;
   const int E = (int)a.E;
-  const int key0 = blockIdx.x * kKeysPerWG + wave * kTilesPerWave * 16;
-  if (key0 >= E) return;
-
+  const int chunk0 = blockIdx.x * kKeysPerWG;
+  const int key0 = chunk0 + wave * kTilesPerWave * 16;   // the keys this wave stores
   const int n = query_n(a, t);
+  const int ntiles = key0 < E ? min(kTilesPerWave, (E - key0 + 15) >> 4) : 0;
+  // tiles of the group's chunk below n, and this wave's share of them
+  const int chunk_live = chunk0 < n ? min(kDWaves * kTilesPerWave, (n - chunk0 + 15) >> 4) : 0;
+  const int live = min(max(chunk_live - wave * kTilesPerWave, 0), kTilesPerWave);
+  auto tile_of = [&](int i) { return wave * kTilesPerWave + i; };
+  const bool wg_live = chunk_live > 0;
+
   float* srow = a.scores + (int64_t)t * a.ld_scores;
   float* brow = a.block_max ? a.block_max + (int64_t)t * a.ld_block_max : nullptr;
-
-  int ntiles = min(kTilesPerWave, (E - key0 + 15) >> 4);
-  int live = key0 < n ? min(ntiles, (n - key0 + 15) >> 4) : 0;
-
-  // Tiles past n: -inf scores and block maxima, no key reads.
-  for (int i = live; i < ntiles; ++i) {
-    const int k = key0 + 16 * i;
-    if (lane < 16 && k + lane < E) srow[k + lane] = neg_inf();
-    if (brow && lane < 2 && k + 8 * lane < E) brow[(k >> 3) + lane] = neg_inf();
-  }
-  if (live == 0) return;
-
   const int seq = a.seq_id[t];
-  bf16x8 qa[4];
-  float wq[4];
-  {
-    const uint16_t* row = reinterpret_cast<const uint16_t*>(a.q_idx) + ((int64_t)t * kIdxHeads + c) * kIdxDim;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      qa[s] = *reinterpret_cast<const bf16x8*>(row + (FP8 ? kdim_fp8(g, s) : kdim_bf16(g, s)));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wq[i] = a.w[(int64_t)t * kIdxHeads + 4 * g + i];
-  }
-  constexpr int RB = FP8 ? kIdxDim : 2 * kIdxDim;  // key row bytes
   const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys) + (int64_t)seq * a.keys_seq_stride * (FP8 ? 1 : 2);
-  const float* scales = FP8 ? a.scales + (int64_t)seq * a.scales_seq_stride : nullptr;
-  // A lane reads row c of a tile: 64 contiguous bytes at 16g (bf16) or 16 at 16g (+64) (e4m3).
-  const uint32_t lane_off = (uint32_t)(c * RB + 16 * g);
 
-  // Rows past n inside the last live tile are clamped to row n-1 (read, then masked).
-  auto tile_ptr = [&](int i, const uint8_t*& tp, const float*& sp, uint32_t& off) {
-    const int k = key0 + 16 * i;
-    if (k + 16 <= n) {
-      tp = keys + (int64_t)k * RB;
-      sp = FP8 ? scales + k : nullptr;
-      off = lane_off;
-    } else {
-      const int row = min(k + c, n - 1);
-      tp = keys;
-      sp = FP8 ? scales + row - c : nullptr;
-      off = (uint32_t)(row * RB + 16 * g);
+  // e4m3 row scales of the keys this lane stores at the end (issued first: the loads
+  // complete in order, so the row waits below also cover them)
+  float scv[kTilesPerWave / 4] = {};
+  if (FP8 && key0 < n) {   // (a query without keys may have no valid sequence)
+    const float* scales = a.scales + (int64_t)seq * a.scales_seq_stride;
+#pragma unroll
+    for (int j = 0; j < kTilesPerWave / 4; ++j) scv[j] = scales[min(key0 + 64 * j + lane, n - 1)];
+  }
+  const uint32_t lds_q = (uint32_t)(uintptr_t)&sh.q[0];
+  const uint32_t lds_w = (uint32_t)(uintptr_t)&sh.w[0];
+  if (wg_live) {
+    // the query's 16 x 128 index heads (4 KB): wave w moves bytes 1024w .. 1024w + 1023
+    static_assert(kDWaves * 1024 == kIdxHeads * kIdxDim * 2, "one KB of the query per wave");
+    const uint8_t* qb = reinterpret_cast<const uint8_t*>(a.q_idx) + (int64_t)t * kIdxHeads * kIdxDim * 2;
+    to_lds16(qb + 1024 * wave + 16 * lane, lds_q + 1024 * wave);
+    if (wave == 0 && lane < kIdxHeads / 4) to_lds16(a.w + (int64_t)t * kIdxHeads + 4 * lane, lds_w);
+  }
+
+  // load j of a tile: lane -> row rr[j], chunk qq[j]; its 16 bytes land at position
+  // pos(row, chunk) of that row in LDS
+  int rr[NK], qq[NK];
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    const int r = j * (64 / DT::CPR) + lane / DT::CPR;
+    const int p = lane % DT::CPR;
+    rr[j] = r;
+    qq[j] = DT::pos(r, p);   // pos is an involution in q for a fixed row
+  }
+  const uint32_t ring0 = (uint32_t)(uintptr_t)&sh.ring[wave][0];
+  auto issue = [&](int i, bool after_reads) {
+    const int k = chunk0 + 16 * tile_of(i);
+    const uint8_t* tb = keys + (int64_t)k * RB;
+    const int last = n - 1 - k;   // rows past n in the last live tile repeat row n - 1
+    const uint32_t lds = ring0 + (uint32_t)((i & (D - 1)) * TB);
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const uint8_t* src = tb + (min(rr[j], last) * RB + qq[j] * 16);
+      if (j == 0 && after_reads) to_lds16_after_reads(src, lds + 1024 * j);
+      else to_lds16(src, lds + 1024 * j);
     }
   };
-
-  KeyRegs<FP8> buf[kDepth];
 #pragma unroll
-  for (int u = 0; u < kDepth; ++u) {
-    if (u < live) {
-      const uint8_t* tp; const float* sp; uint32_t off;
-      tile_ptr(u, tp, sp, off);
-      load_keys<FP8>(buf[u], tp, sp, off, c);
+  for (int u = 0; u < D; ++u)
+    if (u < live) issue(u, false);
+  if (live >= D) __builtin_amdgcn_s_waitcnt(waitcnt_vm(D * NK));   // query, weights, scales
+  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  // every wave's part of the query is in LDS (its loads completed above); a bare barrier,
+  // since a fence here would also wait for the row loads in flight
+  asm volatile("s_barrier" ::: "memory");
+
+  if (live > 0) {
+    bf16x8 qa[4];
+    float wq[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      qa[s] = *reinterpret_cast<const bf16x8*>(&sh.q[c * kIdxDim + (FP8 ? kdim_fp8(g, s) : kdim_bf16(g, s))]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wq[i] = sh.w[4 * g + i];
+    // B-operand reads of lane (c, g): chunk g + 4i (e4m3) or 4i + g (bf16) of row c
+    uint32_t roff[NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int q = FP8 ? g + 4 * i : 4 * i + g;
+      roff[i] = (uint32_t)(c * RB + DT::pos(c, q) * 16);
+    }
+    float* stage = &sh.stage[0][0];
+    for (int i = 0; i < live; ++i) {
+      if (i + D - 1 < live) __builtin_amdgcn_s_waitcnt(waitcnt_vm((D - 1) * NK));   // tile i landed
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      const uint8_t* tile = sh.ring[wave] + (i & (D - 1)) * TB;
+      KeyRegs<FP8> K;
+#pragma unroll
+      for (int j = 0; j < NK; ++j) K.v[j] = *reinterpret_cast<const u32x4*>(tile + roff[j]);
+      const f32x4 acc = tile_dots<FP8>(qa, K);
+      if (i + D < live) issue(i + D, true);
+      float v = wq[0] * relu(acc[0]);
+      v = fmaf(wq[1], relu(acc[1]), v);
+      v = fmaf(wq[2], relu(acc[2]), v);
+      v = fmaf(wq[3], relu(acc[3]), v);
+      v = add_xor32(add_xor16(v));
+      if (lane < 16) stage[16 * tile_of(i) + lane] = v;
     }
   }
-  for (int i0 = 0; i0 < live; i0 += kDepth) {
+
+  // ---- scores and block maxima of the wave's keys: 64 consecutive keys per store ----
+  const float* stage = sh.stage[wave];
 #pragma unroll
-    for (int u = 0; u < kDepth; ++u) {
-      const int i = i0 + u;
-      if (i < live) {
-        const f32x4 acc = tile_dots<FP8>(qa, buf[u]);
-        const float sc = buf[u].scale;
-        if (i + kDepth < live) {
-          const uint8_t* tp; const float* sp; uint32_t off;
-          tile_ptr(i + kDepth, tp, sp, off);
-          load_keys<FP8>(buf[u], tp, sp, off, c);
-        }
-        float v = wq[0] * relu(acc[0]);
-        v = fmaf(wq[1], relu(acc[1]), v);
-        v = fmaf(wq[2], relu(acc[2]), v);
-        v = fmaf(wq[3], relu(acc[3]), v);
-        v = add_xor32(add_xor16(v));
-        if (FP8) v *= sc;
-        const int k = key0 + 16 * i;
-        if (k + 16 <= n) {  // whole tile visible
-          const float m = max8_lanes(v);
-          if (lane < 16) srow[k + lane] = v;
-          if (brow && (lane == 0 || lane == 8)) brow[(k >> 3) + (lane >> 3)] = m;
-        } else {
-          if (k + c >= n) v = neg_inf();
-          const float m = max8_lanes(v);
-          if (lane < 16 && k + lane < E) srow[k + lane] = v;
-          if (brow && (lane == 0 || lane == 8) && k + lane < E) brow[(k >> 3) + (lane >> 3)] = m;
-        }
-      }
+  for (int j = 0; j < kTilesPerWave / 4; ++j) {
+    const int k = key0 + 64 * j + lane;
+    if (64 * j >= 16 * ntiles) break;
+    float v = neg_inf();
+    if (k < n) {
+      v = stage[64 * j + lane];
+      if constexpr (FP8) v *= scv[j];
+    }
+    const float m = max8_lanes(v);   // E is a multiple of 8: groups are all in or all out
+    if (k < E) {
+      srow[k] = v;
+      if (brow && (lane & 7) == 0) brow[k >> 3] = m;
     }
   }
 }
