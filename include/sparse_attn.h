@@ -113,10 +113,21 @@ typedef struct sa_cache {
 /* Validate `params` and create a plan (host memory owned by the library,
  * immutable, shareable across threads and streams). `*workspace_bytes`
  * receives the device workspace size that select_topk and sparse_attn_fwd
- * need for T = max_queries; concurrent calls need separate workspaces. */
+ * need for T = max_queries; concurrent calls need separate workspaces.
+ * A workspace holds a select area (scratch between calls) and an attention
+ * area (used by batches of at most 32 queries) whose per-query counters must
+ * be zero before a call: zero them once with sparse_attn_workspace_init after
+ * allocating; every sparse_attn_fwd call leaves them zero again. */
 sa_status sparse_attn_plan(const sa_params* params, sa_plan** plan, size_t* workspace_bytes);
 
 void sparse_attn_plan_destroy(sa_plan* plan);
+
+/* Zero the attention counters of a workspace of at least the plan's size (a
+ * kernel on `stream`, so the call may be captured in a graph). Needed once per
+ * allocation, before its first use by sparse_attn_fwd. Not a step of the
+ * method: the library's own bookkeeping for sparse_attn_fwd's key splits. */
+sa_status sparse_attn_workspace_init(const sa_plan* plan, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 /* Message of the last non-OK status returned on this thread ("" if none). */
 const char* sparse_attn_last_error(void);
@@ -162,7 +173,13 @@ sa_status select_topk(const sa_plan* plan, const sa_queries* queries, const floa
  *   out    device bf16 [T][64][512]: out, per-head attention output
  *   lse    device fp32 [T][64] or NULL: out, natural-log sum of exp of the
  *          scaled logits (max + log of the normaliser)
- *   workspace  device, >= the size reported by sparse_attn_plan. */
+ *   workspace  device or NULL. With T <= 32 and a workspace of the plan's
+ *          size (counters zeroed, see sparse_attn_workspace_init), each query's
+ *          key list is split over 4 work-groups whose partial softmax results
+ *          are combined at the end (the probabilities are rounded to bf16
+ *          against each part's own reference, so the output may differ from
+ *          the unsplit one by that rounding; it is the same for every call);
+ *          otherwise one work-group takes each query. */
 sa_status sparse_attn_fwd(const sa_plan* plan, const sa_queries* queries, const sa_cache* cache,
                           const void* q, const int32_t* topk, void* out, float* lse,
                           void* workspace, size_t workspace_bytes, void* stream);

@@ -23,7 +23,8 @@ SA_KEY_BF16, SA_KEY_FP8_E4M3 = 0, 1
 STATUS_NAMES = {0: "SA_OK", 1: "SA_EINVAL", 2: "SA_EUNSUPPORTED", 3: "SA_EWORKSPACE", 4: "SA_EHIP"}
 
 EXPORTS = ("sparse_attn_plan", "sparse_attn_plan_destroy", "sparse_attn_last_error",
-           "indexer_score", "select_topk", "sparse_attn_fwd", "sparse_attn_compress")
+           "sparse_attn_workspace_init", "indexer_score", "select_topk", "sparse_attn_fwd",
+           "sparse_attn_compress")
 
 
 class sa_params(ctypes.Structure):
@@ -59,7 +60,7 @@ class SparseAttnError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
-                          f"python -m sparse_attention_score_amd.build")
+                          f"python sparse_attention_score_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
     lib.sparse_attn_plan.argtypes = [ctypes.POINTER(sa_params), ctypes.POINTER(vp), ctypes.POINTER(sz)]
@@ -68,6 +69,8 @@ def _load():
     lib.sparse_attn_plan_destroy.restype = None
     lib.sparse_attn_last_error.argtypes = []
     lib.sparse_attn_last_error.restype = ctypes.c_char_p
+    lib.sparse_attn_workspace_init.argtypes = [vp, vp, sz, vp]
+    lib.sparse_attn_workspace_init.restype = ctypes.c_int
     lib.indexer_score.argtypes = [vp, ctypes.POINTER(sa_queries), ctypes.POINTER(sa_cache), vp, vp,
                                   vp, i64, vp, i64, vp]
     lib.indexer_score.restype = ctypes.c_int
@@ -220,6 +223,20 @@ def select_topk(plan: Plan, queries: Queries, scores: torch.Tensor,
     _check(lib.select_topk(plan.handle, ctypes.byref(queries.c), _ptr(scores), scores.stride(0),
                            _ptr(block_max), 0 if block_max is None else block_max.stride(0),
                            _ptr(cand), _ptr(topk), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def sparse_attn_workspace_init(plan: Plan, workspace: torch.Tensor, stream=None):
+    """Zero the attention counters of a fresh workspace (once per allocation)."""
+    _need(workspace, "workspace", torch.uint8)
+    _check(lib.sparse_attn_workspace_init(plan.handle, _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def workspace_for(plan: Plan, device="cuda") -> torch.Tensor:
+    """A workspace of the plan's size, ready for use by select_topk and sparse_attn_fwd."""
+    ws = torch.empty((max(16, plan.workspace_bytes),), dtype=torch.uint8, device=device)
+    sparse_attn_workspace_init(plan, ws)
+    return ws
 
 
 def sparse_attn_fwd(plan: Plan, queries: Queries, cache: Cache, q: torch.Tensor, topk: torch.Tensor,

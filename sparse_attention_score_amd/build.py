@@ -1,6 +1,6 @@
 """Build libsparse_attn.so (HIP kernels for gfx950 + the C ABI) in-tree with hipcc.
 
-Usage: python -m sparse_attention_score_amd.build [--jobs N]
+Usage: python sparse_attention_score_amd/build.py [--jobs N]   (runs without importing the package)
 """
 from __future__ import annotations
 

@@ -47,6 +47,26 @@ size_t part_bytes(int64_t T, int64_t max_visible) {
   return parts > 1 ? (size_t)T * parts * 2048 * sizeof(int32_t) : 0;
 }
 
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Workspace layout: [select area][attention area]. The select area holds the candidate
+// blocks (when cand is NULL) and the part lists; the attention area holds one counter per
+// query (zero between calls) and the partial results of key splits.
+struct WsLayout {
+  size_t select_bytes, counters_off, ml_off, o_off, total;
+  int64_t units;
+};
+WsLayout ws_layout(const sa_params& p) {
+  WsLayout w;
+  w.select_bytes = cand_bytes(p.max_queries) + part_bytes(p.max_queries, p.max_compressed);
+  w.units = sa::attn_max_units(p.max_queries);
+  w.counters_off = align256(w.select_bytes);
+  w.ml_off = w.counters_off + align256((size_t)p.max_queries * sizeof(uint32_t));
+  w.o_off = w.ml_off + align256((size_t)w.units * 64 * 2 * sizeof(float));
+  w.total = w.units > 0 ? w.o_off + (size_t)w.units * 64 * 512 * sizeof(float) : w.select_bytes;
+  return w;
+}
+
 sa_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(SA_EHIP, "%s: %s", what, hipGetErrorString(e));
@@ -153,7 +173,7 @@ sa_status sparse_attn_plan(const sa_params* p, sa_plan** plan, size_t* workspace
   sa_plan* pl = new (std::nothrow) sa_plan;
   SA_REQUIRE(pl != nullptr, SA_EINVAL, "out of host memory");
   pl->p = *p;
-  pl->workspace = cand_bytes(p->max_queries) + part_bytes(p->max_queries, p->max_compressed);
+  pl->workspace = ws_layout(*p).total;
   *plan = pl;
   if (workspace_bytes) *workspace_bytes = pl->workspace;
   return ok();
@@ -257,8 +277,6 @@ sa_status select_topk(const sa_plan* plan, const sa_queries* q, const float* sco
 sa_status sparse_attn_fwd(const sa_plan* plan, const sa_queries* q, const sa_cache* c,
                           const void* qv, const int32_t* topk, void* out, float* lse,
                           void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   sa_status st;
   if ((st = check_plan(plan)) != SA_OK) return st;
   if ((st = check_queries(plan, q)) != SA_OK) return st;
@@ -279,7 +297,37 @@ sa_status sparse_attn_fwd(const sa_plan* plan, const sa_queries* q, const sa_cac
   a.scale = plan->p.softmax_scale;
   a.out = out;
   a.lse = lse;
+  // key splits need the plan's whole workspace (its counters zeroed once by
+  // sparse_attn_workspace_init); without it every query runs in one work-group
+  const WsLayout wl = ws_layout(plan->p);
+  a.splits = sa::attn_splits(q->T);
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  a.counters = nullptr;
+  if (a.splits > 1 && workspace != nullptr && aligned16(workspace) && workspace_bytes >= wl.total &&
+      q->T * a.splits <= wl.units) {
+    char* ws = static_cast<char*>(workspace);
+    a.counters = reinterpret_cast<uint32_t*>(ws + wl.counters_off);
+    a.part_ml = reinterpret_cast<float*>(ws + wl.ml_off);
+    a.part_o = reinterpret_cast<float*>(ws + wl.o_off);
+  } else {
+    a.splits = 1;
+  }
   return hip_status(sa::launch_attn(a, (hipStream_t)stream), "sparse_attn_fwd launch");
+}
+
+sa_status sparse_attn_workspace_init(const sa_plan* plan, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  sa_status st;
+  if ((st = check_plan(plan)) != SA_OK) return st;
+  SA_REQUIRE(workspace != nullptr && aligned16(workspace), SA_EWORKSPACE, "workspace NULL or misaligned");
+  SA_REQUIRE(workspace_bytes >= plan->workspace, SA_EWORKSPACE, "workspace_bytes = %zu < %zu",
+             workspace_bytes, plan->workspace);
+  const WsLayout wl = ws_layout(plan->p);
+  if (wl.units == 0) return ok();
+  uint32_t* counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + wl.counters_off);
+  return hip_status(sa::launch_zero_u32(counters, plan->p.max_queries, (hipStream_t)stream),
+                    "sparse_attn_workspace_init launch");
 }
 
 sa_status sparse_attn_compress(const sa_plan* plan, const void* raw, int64_t raw_group_stride,

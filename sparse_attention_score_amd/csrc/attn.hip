@@ -33,6 +33,10 @@ namespace sa {
 namespace {
 
 constexpr int kAW = 8;              // waves
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer resource, 32-bit data (gfx9 family)
+constexpr int kCoherent = 16;            // buffer cache policy sc1: device-scope coherent
+constexpr int64_t kAttnPartBytesO = 64 * 512 * 4;   // one partial O
+constexpr int kMaxSplits = 4;
 constexpr int kAThreads = 64 * kAW;
 constexpr int kHG = 4;              // head groups of 16
 constexpr int kKT = 32;             // keys per step
@@ -54,11 +58,13 @@ constexpr int kWaitAll = waitcnt_vm(0);
 struct AttnShared {
   uint8_t tile[kBufs][kKT * kRow];     // 135,168 B
   const uint16_t* rows[kMaxKeys];      // global row of every key slot
+  int32_t topk[kTopK];                 // the query's selection, loaded straight into LDS
   u32x4 P[2][kHG][64];                 // P^T operand of each head group per lane, two steps
   float tmax[2][kHeads];               // step-0 maxima per key half / partial normalisers
   float norm[kHeads];                  // final normaliser of each head
   int wave_cnt[kAW];
   int redo[kAW];                       // per wave: a score exceeded its reference by > kSafe
+  int last;                            // this work-group combines the query's key splits
 };
 
 __device__ __forceinline__ uint32_t perm_lo(uint32_t hi_src, uint32_t lo_src) {
@@ -76,23 +82,38 @@ __device__ __forceinline__ float max_xor32(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// One 1 KB latent row from global memory straight into LDS: lane l moves bytes 16l..16l+15
-// to LDS byte address lds + 16l. The compiler does not see this load, so completion is
-// tracked by hand with s_waitcnt vmcnt (the kernel issues no other vector-memory
-// operations between the first of these and the final wait).
-__device__ __forceinline__ void row_to_lds(const uint16_t* row, uint32_t lds, int lane) {
+// Device-coherent 32-bit store and load (relaxed atomics at device scope): written through
+// to, and read from, the level every XCD shares.
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's land at LDS byte address
+// lds + 16l. The compiler does not see these loads, so completion is tracked by hand with
+// s_waitcnt vmcnt (the kernel issues no other vector-memory load before its output).
+__device__ __forceinline__ void to_lds16(const void* src, uint32_t lds) {
   // s_nop: an LDS-DMA load must not directly follow the write of M0 (one wait state)
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(row + lane * 8), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds) : "memory");
+}
+// One 1 KB latent row: lane l moves bytes 16l..16l+15.
+__device__ __forceinline__ void row_to_lds(const uint16_t* row, uint32_t lds, int lane) {
+  to_lds16(row + lane * 8, lds);
 }
 
 __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) AttnShared sh;
   // work-group -> query: ids are dealt round-robin over the 8 XCDs, so XCD x gets the
   // contiguous query range x*Q8 .. x*Q8+Q8-1 (neighbouring queries share window rows).
-  const int T = (int)a.m.T;
-  const int q8 = (T + 7) >> 3;
-  const int t = (blockIdx.x & 7) * q8 + (blockIdx.x >> 3);
-  if ((int)(blockIdx.x >> 3) >= q8 || t >= T) return;
+  // With key splits the unit is (query, split), split fastest, so the splits of a query
+  // normally share an XCD.
+  const int T = (int)a.m.T, S = a.splits, U = T * S;
+  const int u8 = (U + 7) >> 3;
+  const int u = (blockIdx.x & 7) * u8 + (blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= u8 || u >= U) return;
+  const int t = u / S, split = u - t * S;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int c = lane & 15, g = lane >> 4;
   const int hg = wave & (kHG - 1), kh = wave / kHG;   // scores role
@@ -107,10 +128,32 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
     n = n < a.m.compressed_cap ? n : a.m.compressed_cap;
   }
 
+  // ---- the selection (2 KB) and the query (64 KB) by direct loads: the selection into its
+  // own LDS array, the query's 64 heads into tiles 2 and 3 (one padded row per head) until
+  // step 2's rows replace it. Every load the kernel makes before its output is one of these,
+  // so all waits are explicit vmcnt counts. ----
+  const uint32_t tile0 = (uint32_t)(uintptr_t)&sh.tile[0][0];
+  const uint32_t qlds = tile0 + (uint32_t)(2 * kKT * kRow);
+  static_assert(kBufs >= 4 && kHeads <= 2 * kKT, "the query needs two tiles");
+  if (valid_q) {
+    if (wave < 2) {   // 256 entries per wave
+      const int32_t* src = a.topk + (int64_t)t * kTopK + 256 * wave + 4 * lane;
+      to_lds16(src, (uint32_t)(uintptr_t)&sh.topk[256 * wave]);
+    }
+    const uint16_t* qt = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)t * kHeads * kDim;
+#pragma unroll
+    for (int i = 0; i < kHeads / kAW; ++i) {
+      const int head = (kHeads / kAW) * wave + i;
+      to_lds16(qt + head * kDim + 8 * lane, qlds + head * kRow);
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kHeads / kAW));   // the selection (query loads in flight)
+  }
+  __syncthreads();
+
   // ---- key list: selected latents in topk order, then the window ----
   int m = 0;
   if (valid_q) {
-    const int32_t j = a.topk[(int64_t)t * kTopK + tid];   // kAThreads == kTopK
+    const int32_t j = sh.topk[tid];   // kAThreads == kTopK
     const bool v = j >= 0 && j < n;
     int incl = (int)v;
 #pragma unroll
@@ -135,7 +178,8 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  if (m == 0) {  // invalid query: zero output, lse = -inf
+  if (m == 0) {  // invalid query (no load was issued): zero output, lse = -inf
+    if (split != 0) return;
     uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (int64_t)t * kHeads * kDim;
     for (int i = tid; i < kHeads * kDim / 8; i += kAThreads)
       *reinterpret_cast<u32x4*>(o + 8 * i) = u32x4{0u, 0u, 0u, 0u};
@@ -143,26 +187,42 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
     return;
   }
 
-  // ---- query heads 16hg + c as the B operand (k-step s: dims (4s+g)*8 .. +8) ----
-  bf16x8 qb[16];
-  {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)t * kHeads + 16 * hg + c) * kDim;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) qb[s] = *reinterpret_cast<const bf16x8*>(qrow + (4 * s + g) * 8);
-  }
+  // ---- this work-group's steps of the key list: kb .. kb + mk - 1 ----
+  const int ns_all = (m + kKT - 1) / kKT;
+  const int st0 = split * ns_all / S, st1 = (split + 1) * ns_all / S;
+  const int kb = st0 * kKT;
+  const int mk = min(m, st1 * kKT) - kb;   // 0 for a split without a step
 
   // ---- tile loader: wave w moves rows 4w..4w+3 of a step. Rows past the key list repeat
   // the last real row (finite data; their scores are masked), so every wave issues exactly
   // kRowsPerWave loads per step and the wait counts are constants.
-  const uint32_t tile0 = (uint32_t)(uintptr_t)&sh.tile[0][0];
   auto issue = [&](int step) {
     const uint32_t base = tile0 + (uint32_t)((step % kBufs) * (kKT * kRow) + wave * kRowsPerWave * kRow);
     const uint16_t* r[kRowsPerWave];
 #pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) r[i] = sh.rows[min(step * kKT + wave * kRowsPerWave + i, m - 1)];
+    for (int i = 0; i < kRowsPerWave; ++i) r[i] = sh.rows[kb + min(step * kKT + wave * kRowsPerWave + i, mk - 1)];
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) row_to_lds(r[i], base + i * kRow, lane);
   };
+
+  // ---- query heads 16hg + c as the B operand (k-step s: dims (4s+g)*8 .. +8), from LDS;
+  // steps 0 and 1 are already on their way meanwhile ----
+  if (mk > 0) {
+    issue(0);
+    issue(1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kRowsPerWave));   // the query (steps 0, 1 in flight)
+  } else {
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+  }
+  __syncthreads();
+  bf16x8 qb[16];
+  {
+    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(&sh.tile[0][0]) + 2 * kKT * kRow + (16 * hg + c) * kRow;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) qb[s] = *reinterpret_cast<const bf16x8*>(qrow + (4 * s + g) * 16);
+  }
+  __syncthreads();   // every wave holds its query heads: tile 2 may take step 2's rows
+  if (mk > 0) issue(2);
 
   // O^T accumulators [head group][e4]: dims d0 + 4r + e4 (r = MFMA row) of head 16hg' + c
   f32x4 O[kHG][4];
@@ -170,7 +230,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   float m_max = neg_inf();   // max score of that head over this wave's keys so far
   float l_run = 0.f;         // this lane's part of that head's normaliser
   const float sc2 = a.scale * kLog2e;
-  const int nsteps = (m + kKT - 1) / kKT;
+  const int nsteps = (mk + kKT - 1) / kKT;
 
   // Scores and softmax of step `step` for (hg, kh): P to LDS buffer step & 1. Keys past m
   // (and whole steps past the last) come out with P = 0. Returns the keys' max.
@@ -188,7 +248,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int k = step * kKT + 16 * kh + 4 * g + i;
-      x[i] = k < m ? acc[i] * sc2 : neg_inf();
+      x[i] = k < mk ? acc[i] * sc2 : neg_inf();
       mt = fmaxf(mt, x[i]);
     }
     mt = max_xor32(max_xor16(mt));   // all four lane groups of head c agree
@@ -238,18 +298,24 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
     }
   };
 
-  // the query loads are complete before the first row load, so the compiler's own waits
-  // (which do not count the row loads) never need to reach past them
-  __builtin_amdgcn_s_waitcnt(kWaitAll);
 
-  for (int pass = 0; pass < 2; ++pass) {
+  // (a split without keys leaves O = 0, l = 0 and the reference at -inf)
 #pragma unroll
-    for (int h = 0; h < kHG; ++h)
+  for (int h = 0; h < kHG; ++h)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) O[h][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < 4; ++e) O[h][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int pass = 0; pass < (mk > 0 ? 2 : 0); ++pass) {
+    if (pass == 1) {
+#pragma unroll
+      for (int h = 0; h < kHG; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) O[h][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
     l_run = 0.f;
+    if (pass == 1) {   // (the first pass's rows went out with the query)
 #pragma unroll
-    for (int j = 0; j < kDepth; ++j) issue(j);
+      for (int j = 0; j < kDepth; ++j) issue(j);
+    }
     __builtin_amdgcn_s_waitcnt(kWaitLater);   // step 0's rows (steps 1, 2 in flight)
     __syncthreads();
     if (pass == 0) {
@@ -266,7 +332,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       float mt = neg_inf();
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (16 * kh + 4 * g + i < m) mt = fmaxf(mt, acc[i] * sc2);
+        if (16 * kh + 4 * g + i < mk) mt = fmaxf(mt, acc[i] * sc2);
       mt = max_xor32(max_xor16(mt));
       if (g == 0) sh.tmax[kh][16 * hg + c] = mt;
       __syncthreads();
@@ -311,32 +377,162 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
     __syncthreads();
     if (kh == 0 && g == 0) {
       const float Lh = sh.tmax[0][16 * hg + c] + sh.tmax[1][16 * hg + c];
-      sh.norm[16 * hg + c] = Lh;
-      if (a.lse) a.lse[(int64_t)t * kHeads + 16 * hg + c] = (m_ref + __log2f(Lh)) * kLn2;
+      if (S == 1) {
+        sh.norm[16 * hg + c] = Lh;
+        if (a.lse) a.lse[(int64_t)t * kHeads + 16 * hg + c] = (m_ref + __log2f(Lh)) * kLn2;
+      } else {
+        float* ml = a.part_ml + ((int64_t)u * kHeads + 16 * hg + c) * 2;
+        store_dev(ml, m_ref);
+        store_dev(ml + 1, Lh);
+      }
     }
     __syncthreads();
   }
-  // ---- store: lane (c, g) holds dims d0 + 4(4g+i) + e4 of head 16h + c ----
+  if (S == 1) {
+    // ---- store: lane (c, g) holds dims d0 + 4(4g+i) + e4 of head 16h + c ----
 #pragma unroll
-  for (int h = 0; h < kHG; ++h) {
-    const float inv = 1.0f / sh.norm[16 * h + c];
-    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * kHeads + 16 * h + c) * kDim + d0;
+    for (int h = 0; h < kHG; ++h) {
+      const float inv = 1.0f / sh.norm[16 * h + c];
+      uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * kHeads + 16 * h + c) * kDim + d0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;  // row of the MFMA result = group of 4 dims
+        uint2 o;
+        o.x = pack_bf16x2(O[h][0][i] * inv, O[h][1][i] * inv);
+        o.y = pack_bf16x2(O[h][2][i] * inv, O[h][3][i] * inv);
+        *reinterpret_cast<uint2*>(orow + 4 * r) = o;
+      }
+    }
+    return;
+  }
+
+  // ---- key splits: this work-group's partial O, then the last of the query combines ----
+  // The softmax of the whole key list from the splits' partial ones: with M the largest
+  // reference, o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) L_s.
+  // Partials travel by device-coherent stores and loads (written through to, and read
+  // from, the level all XCDs share), in the lanes' own order so every instruction moves
+  // 1 KB of whole lines; no cache-wide write-back or invalidation is needed. The count is
+  // raised only after every store of the work-group has completed.
+  const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+      a.part_o, (short)0, (int)(U * kAttnPartBytesO), kRsrcWord3);
+  auto part_off = [&](int unit, int h, int i) {   // byte offset of lane 0's f32x4
+    return (uint32_t)((((unit * kAW + wave) * kHG + h) * 4 + i) * 64 * 16);
+  };
+#pragma unroll
+  for (int h = 0; h < kHG; ++h)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 4 * g + i;  // row of the MFMA result = group of 4 dims
+      const u32x4 v = __builtin_bit_cast(u32x4, f32x4{O[h][0][i], O[h][1][i], O[h][2][i], O[h][3][i]});
+      __builtin_amdgcn_raw_buffer_store_b128(v, prs, part_off(u, h, i) + lane * 16, 0, kCoherent);
+    }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's partial is device-visible
+  __syncthreads();
+  if (tid == 0) sh.last = atomicAdd(&a.counters[t], 1u) == (uint32_t)(S - 1);
+  __syncthreads();
+  if (!sh.last) return;
+  if (tid == 0) a.counters[t] = 0u;   // every split of this call has counted: ready for the next
+  const int u0 = t * S;
+  // weights of the splits per head 16h + c, the own partial scaled in place
+  float wgt[kHG][kMaxSplits], Lsum[kHG], Mx[kHG];
+#pragma unroll
+  for (int h = 0; h < kHG; ++h) {
+    const int head = 16 * h + c;
+    float mref[kMaxSplits], lsp[kMaxSplits];
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplits; ++s2) {
+      const float* ml = a.part_ml + ((int64_t)(u0 + min(s2, S - 1)) * kHeads + head) * 2;
+      mref[s2] = s2 < S ? load_dev(ml) : neg_inf();
+      lsp[s2] = s2 < S ? load_dev(ml + 1) : 0.f;
+    }
+    float M = neg_inf();
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplits; ++s2) M = fmaxf(M, mref[s2]);
+    float L = 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < kMaxSplits; ++s2) {
+      wgt[h][s2] = s2 < S ? __builtin_amdgcn_exp2f(mref[s2] - M) : 0.f;   // an empty split: 2^-inf = 0
+      L += wgt[h][s2] * lsp[s2];
+    }
+    Lsum[h] = L;
+    Mx[h] = M;
+  }
+  // sum over the splits in split order, so the result is the same bit for bit whichever
+  // work-group combines: acc = w_0 O_0, then += w_s O_s. O_0 comes from registers when this
+  // is split 0; otherwise every partial (this one's too) is read back, 16 lines of 1 KB per
+  // wave for one split at a time, and O's registers hold the sum.
+#pragma unroll
+  for (int s2 = 0; s2 < kMaxSplits; ++s2) {
+    if (s2 >= S) break;
+    asm volatile("" ::: "memory");   // one split's loads in flight at a time (registers)
+    if (s2 == 0 && split == 0) {
+#pragma unroll
+      for (int h = 0; h < kHG; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) O[h][e] = wgt[h][0] * O[h][e];
+    } else {
+      f32x4 v[kHG][4];
+#pragma unroll
+      for (int h = 0; h < kHG; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[h][i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  prs, part_off(u0 + s2, h, i) + lane * 16, 0, kCoherent));
+#pragma unroll
+      for (int h = 0; h < kHG; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            O[h][e][i] = s2 == 0 ? wgt[h][0] * v[h][i][e] : O[h][e][i] + wgt[h][s2] * v[h][i][e];
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < kHG; ++h) {
+    const int head = 16 * h + c;
+    const float inv = 1.0f / Lsum[h];
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * kHeads + head) * kDim + d0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
       uint2 o;
       o.x = pack_bf16x2(O[h][0][i] * inv, O[h][1][i] * inv);
       o.y = pack_bf16x2(O[h][2][i] * inv, O[h][3][i] * inv);
-      *reinterpret_cast<uint2*>(orow + 4 * r) = o;
+      *reinterpret_cast<uint2*>(orow + 4 * (4 * g + i)) = o;
     }
+    if (a.lse && wave == 0 && g == 0) a.lse[(int64_t)t * kHeads + head] = (Mx[h] + __log2f(Lsum[h])) * kLn2;
   }
+}
+
+__global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
 }
 
 }  // namespace
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
-  const int64_t q8 = (a.m.T + 7) / 8;   // queries per XCD
-  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)(8 * q8)), dim3(kAThreads), 0, stream, a);
+  const int64_t u8 = (a.m.T * a.splits + 7) / 8;   // work units per XCD
+  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+// Small batches (at most 32 queries, an eighth of the CUs): a query's keys are spread over
+// kMaxSplits work-groups (the last to finish reads the others' partials). With more
+// queries the partial traffic costs about what the shorter key lists save.
+int attn_splits(int64_t T) { return T <= 32 ? kMaxSplits : 1; }
+
+int64_t attn_max_units(int64_t max_queries) {
+  int64_t best = 0;
+  const int64_t lim = max_queries < 32 ? max_queries : 32;
+  for (int64_t T = 1; T <= lim; ++T) {
+    const int s = attn_splits(T);
+    if (s > 1 && T * s > best) best = T * s;
+  }
+  return best;
+}
+
+hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n);
   return hipGetLastError();
 }
 

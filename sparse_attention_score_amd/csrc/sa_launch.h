@@ -68,8 +68,21 @@ struct AttnArgs {
   float scale;
   void* out;                // bf16 [T][64][512]
   float* lse;               // [T][64] or null
+  // key splits: splits > 1 spreads each query's keys over that many work-groups, which
+  // leave partial results in part_o / part_ml; the last one of a query to finish (counted
+  // in counters[t], zero before and after the call) combines them
+  int splits;
+  float* part_o;            // [T * splits][64][512] unnormalised outputs
+  float* part_ml;           // [T * splits][64][2] reference (log2 domain) and normaliser
+  uint32_t* counters;       // [T]
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
+// Key splits used for T queries, and the partial slots (T * splits) the largest of them
+// needs for any T up to max_queries.
+int attn_splits(int64_t T);
+int64_t attn_max_units(int64_t max_queries);
+// Zero n 32-bit words (a kernel, so the call may be captured in a graph).
+hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t stream);
 
 struct CompressArgs {
   const void* raw;

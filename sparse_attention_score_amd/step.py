@@ -9,7 +9,7 @@ import numpy as np
 import torch
 
 from . import (Cache, Plan, Queries, indexer_score, select_topk, sparse_attn_compress,
-               sparse_attn_fwd)
+               sparse_attn_fwd, workspace_for)
 
 
 def to_device_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
@@ -62,7 +62,7 @@ class DeviceBatch:
         self.topk = torch.empty((wl.T, 512), dtype=torch.int32, device=dev)
         self.out = torch.empty((wl.T, 64, 512), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((wl.T, 64), dtype=torch.float32, device=dev)
-        self.workspace = torch.empty((max(16, self.plan.workspace_bytes),), dtype=torch.uint8, device=dev)
+        self.workspace = workspace_for(self.plan, dev)
 
     # -- stages -------------------------------------------------------------------------
     def compress(self, stream=None):
@@ -86,10 +86,11 @@ class DeviceBatch:
         select_topk(self.plan, self.queries, self.scores, self.block_max if use_block_max else None,
                     self.topk, cand=self.cand, workspace=self.workspace, stream=stream)
 
-    def attend(self, stream=None, topk: Optional[torch.Tensor] = None):
+    def attend(self, stream=None, topk: Optional[torch.Tensor] = None, split: bool = True):
+        # split=False passes no workspace: one work-group per query, whatever T is
         sparse_attn_fwd(self.plan, self.queries, self.cache, self.q,
                         self.topk if topk is None else topk, self.out, self.lse,
-                        workspace=self.workspace, stream=stream)
+                        workspace=self.workspace if split else None, stream=stream)
 
     def run(self, stream=None):
         self.compress(stream)

@@ -56,10 +56,37 @@ def test_plan_rejects(kw, status):
     assert S.lib.sparse_attn_last_error()
 
 
-def test_plan_workspace_and_last_error_reset():
-    p = _plan(max_queries=100)
-    assert p.workspace_bytes == 100 * 2048 * 4
+def _splits(T):
+    # key splits of the attention for T queries: 4 work-groups per query for T <= 32
+    return 4 if T <= 32 else 1
+
+
+def _expected_workspace(max_queries):
+    a256 = lambda b: (b + 255) // 256 * 256
+    select = max_queries * 2048 * 4                       # candidate blocks
+    units = max([T * _splits(T) for T in range(1, max_queries + 1) if _splits(T) > 1] or [0])
+    if units == 0:
+        return select
+    counters = a256(select)
+    ml = counters + a256(4 * max_queries)
+    o = ml + a256(units * 64 * 2 * 4)
+    return o + units * 64 * 512 * 4
+
+
+@pytest.mark.parametrize("mq", [1, 7, 100, 128, 255, 256, 4096])
+def test_plan_workspace_and_last_error_reset(mq):
+    p = _plan(max_queries=mq)
+    assert p.workspace_bytes == _expected_workspace(mq)
     assert S.lib.sparse_attn_last_error() == b""
+
+
+def test_workspace_init_checks():
+    p = _plan(max_queries=8)
+    assert S.lib.sparse_attn_workspace_init(None, 0x1000, 1 << 30, None) != 0
+    assert S.lib.sparse_attn_workspace_init(p.handle, None, 1 << 30, None) == 3        # SA_EWORKSPACE
+    assert S.lib.sparse_attn_workspace_init(p.handle, 0x1008, 1 << 30, None) == 3      # misaligned
+    assert S.lib.sparse_attn_workspace_init(p.handle, 0x1000, p.workspace_bytes - 1, None) == 3
+    assert b"workspace" in S.lib.sparse_attn_last_error()
 
 
 def _q(T=4, max_visible=100, seq=0x1000, pos=0x2000):

@@ -130,6 +130,52 @@ def test_attention_late_dominant_keys():
     d, res = _e2e(wl, lse_tol=LSE_TOL * 10)
     o = bf16_dev_to_f64(d.out)[:, [5, 37], :]
     assert np.all(o > -0.5) and np.all(o < 1.5), "output must be the window rows' mixture"
+    # the same with one work-group per query (a small batch otherwise splits the key list,
+    # and the window rows then sit at the start of the last split)
+    topk = d.topk.cpu().numpy()
+    res2 = O.run(wl, idx_override=[topk[t][topk[t] >= 0] for t in range(wl.T)])
+    d.attend(split=False)
+    torch.cuda.synchronize()
+    o1, lse1 = bf16_dev_to_f64(d.out), d.lse.cpu().numpy()
+    for t in range(wl.T):
+        check_outputs(o1[t], res2.o[t], f"one group t={t}")
+        assert np.abs(lse1[t] - res2.lse[t]).max() <= LSE_TOL * 10
+
+
+def test_attention_key_splits_match_one_group_per_query():
+    """A small batch spreads each query's key list over several work-groups and the last
+    to finish combines their partial softmax results: the same output as one work-group per
+    query up to fp32 summation order. Includes queries with fewer steps than splits (empty
+    splits). The per-query counters reset themselves: a second call with other queries
+    must be combined as well (a stale count would leave the first call's output)."""
+    from sparse_attention_score_amd.step import DeviceBatch
+    wl = W.make_decode(B=8, n_raw=[6000, 100, 1400, 40000, 3, 3000, 18000, 128], ratio=2,
+                       key_dtype="bf16", name="splits", with_compress=False, seed=71)
+    print(f"[case] {wl.name} T={wl.T}", flush=True)
+    d = DeviceBatch(wl)
+    d.index()
+    d.select()
+    topk = d.topk.cpu().numpy()
+    sel = [topk[t][topk[t] >= 0] for t in range(wl.T)]
+    for it, scale in enumerate((1.0, -0.75)):
+        if it:
+            d.q.mul_(scale)
+            wl.q = d.q.cpu().contiguous().view(torch.int16).numpy().view(np.uint16).reshape(wl.q.shape)
+        d.attend()
+        torch.cuda.synchronize()
+        o_s, l_s = bf16_dev_to_f64(d.out), d.lse.cpu().numpy()
+        d.attend(split=False)
+        torch.cuda.synchronize()
+        o_1, l_1 = bf16_dev_to_f64(d.out), d.lse.cpu().numpy()
+        # the probabilities enter the value products as bf16 relative to each group's own
+        # reference, so the two paths differ by that rounding (well inside the oracle bar)
+        mx, mn = check_outputs(o_s, o_1, f"call {it}: split vs one group")
+        print(f"split vs one group: max {mx:.3g} mean {mn:.3g}", flush=True)
+        assert np.abs(l_s - l_1).max() <= 1e-5, f"call {it}: lse"
+        res = O.run(wl, idx_override=sel)
+        for t in range(wl.T):
+            check_outputs(o_s[t], res.o[t], f"split t={t} call {it}")
+            assert np.abs(l_s[t] - res.lse[t]).max() <= LSE_TOL
 
 
 def test_prefill_small_ratio1():
