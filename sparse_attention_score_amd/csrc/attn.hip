@@ -15,17 +15,20 @@
 //           have the range of fp32), so the output is never rescaled and waves holding
 //           different keys of a head need not exchange maxima. If a later score exceeds the
 //           reference by more than kSafe, the query is run again with the true max.
-//   scores: wave (hg, kh) = (w % 4, w / 4) takes heads 16hg..16hg+15 and keys 16kh..16kh+15
-//           of the step: S^T with v_mfma_f32_16x16x32_bf16, A = key rows from LDS, B = the
-//           query heads held in registers (16 k-steps over the 512 dims); lane (c, g) ends
-//           with keys 4g..4g+3 of head c. Its 4 probabilities, packed, are half of the P^T
-//           operand of the head group (the MFMA k order is free as long as A uses the same
-//           one); they go to LDS.
-//   values: wave w owns output dims 64w..64w+63 of all 64 heads: O^T += V^T P^T with
-//           A = V^T built from LDS rows by byte permutes (8 keys x 1 dim per lane), each value
-//           element read from LDS once per step, and B = P^T of each head group.
+// The waves have two roles; waves w and w+4 share a SIMD, one of each:
+//   score waves 0-3: wave (kh, hp) = (w % 2, w / 2) takes keys 16kh..16kh+15 of the step and
+//           head groups 2hp, 2hp+1 (16 heads each): S^T with v_mfma_f32_16x16x32_bf16, A =
+//           key rows from LDS (read once for both groups), B = the query heads held in
+//           registers (16 k-steps over the 512 dims); lane (c, g) ends with keys 4g..4g+3 of
+//           head c. Its 4 probabilities, packed, are half of the P^T operand of the head
+//           group (the MFMA k order is free as long as A uses the same one); they go to LDS.
+//   value waves 4-7: wave 4+v owns output dims 128v..128v+127 of all 64 heads: O^T += V^T
+//           P^T with A = V^T built from LDS rows by byte permutes (8 keys x 1 dim per lane),
+//           each value element read from LDS once per step, and B = P^T of each head group.
 // The values of step s and the scores of step s+1 are independent and run in the same
 // loop iteration, with one barrier per step.
+// Small batches spread each query's key list over kMaxSplits work-groups; the last to
+// finish combines their partial results.
 #include "sa_device.h"
 #include "sa_launch.h"
 
@@ -33,6 +36,8 @@ namespace sa {
 namespace {
 
 constexpr int kAW = 8;              // waves
+constexpr int kSW = 4;              // score waves (the other four weigh the values)
+constexpr int kVW = kAW - kSW;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer resource, 32-bit data (gfx9 family)
 constexpr int kCoherent = 16;            // buffer cache policy sc1: device-scope coherent
 constexpr int64_t kAttnPartBytesO = 64 * 512 * 4;   // one partial O
@@ -98,6 +103,15 @@ __device__ __forceinline__ void to_lds16(const void* src, uint32_t lds) {
   // s_nop: an LDS-DMA load must not directly follow the write of M0 (one wait state)
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" :: "v"(src), "{m0}"(lds) : "memory");
 }
+// Partial O of key splits: per (query, split) unit, [value wave][half][head group][i][lane]
+// f32x4, so each buffer instruction of a wave moves 1 KB.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const AttnArgs& a, int units) {
+  return __builtin_amdgcn_make_buffer_rsrc(a.part_o, (short)0, (int)(units * kAttnPartBytesO), kRsrcWord3);
+}
+__device__ __forceinline__ uint32_t part_off(int unit, int vw, int hh, int h, int i) {   // lane 0's byte
+  return (uint32_t)(((((unit * kVW + vw) * 2 + hh) * kHG + h) * 4 + i) * 64 * 16);
+}
+
 // One 1 KB latent row: lane l moves bytes 16l..16l+15.
 __device__ __forceinline__ void row_to_lds(const uint16_t* row, uint32_t lds, int lane) {
   to_lds16(row + lane * 8, lds);
@@ -116,8 +130,11 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   const int t = u / S, split = u - t * S;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int c = lane & 15, g = lane >> 4;
-  const int hg = wave & (kHG - 1), kh = wave / kHG;   // scores role
-  const int d0 = 64 * wave;                           // values role
+  // waves 0-3 score (keys 16kh.., head groups 2hp, 2hp+1), waves 4-7 weigh the values
+  // (dims 128vw..128vw+127); waves w and w+4 share a SIMD
+  const bool sw = wave < kSW;
+  const int kh = wave & 1, hp = (wave >> 1) & 1;
+  const int vw = wave & 3;
 
   const int seq = a.m.seq_id[t], p = a.m.pos[t];
   const bool valid_q = seq >= 0 && seq < a.m.num_seqs && p >= 0;
@@ -205,8 +222,8 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
     for (int i = 0; i < kRowsPerWave; ++i) row_to_lds(r[i], base + i * kRow, lane);
   };
 
-  // ---- query heads 16hg + c as the B operand (k-step s: dims (4s+g)*8 .. +8), from LDS;
-  // steps 0 and 1 are already on their way meanwhile ----
+  // ---- score waves: query heads 16(2hp + j) + c as B operands (k-step s: dims
+  // (4s+g)*8 .. +8), from LDS; steps 0 and 1 are already on their way meanwhile ----
   if (mk > 0) {
     issue(0);
     issue(1);
@@ -215,224 +232,288 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitAll);
   }
   __syncthreads();
-  bf16x8 qb[16];
-  {
-    const uint8_t* qrow = reinterpret_cast<const uint8_t*>(&sh.tile[0][0]) + 2 * kKT * kRow + (16 * hg + c) * kRow;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) qb[s] = *reinterpret_cast<const bf16x8*>(qrow + (4 * s + g) * 16);
-  }
-  __syncthreads();   // every wave holds its query heads: tile 2 may take step 2's rows
-  if (mk > 0) issue(2);
-
-  // O^T accumulators [head group][e4]: dims d0 + 4r + e4 (r = MFMA row) of head 16hg' + c
-  f32x4 O[kHG][4];
-  float m_ref = neg_inf();   // reference of head 16hg + c (log2 domain), common to both key halves
-  float m_max = neg_inf();   // max score of that head over this wave's keys so far
-  float l_run = 0.f;         // this lane's part of that head's normaliser
   const float sc2 = a.scale * kLog2e;
   const int nsteps = (mk + kKT - 1) / kKT;
+  const int npass = mk > 0 ? 2 : 0;
 
-  // Scores and softmax of step `step` for (hg, kh): P to LDS buffer step & 1. Keys past m
-  // (and whole steps past the last) come out with P = 0. Returns the keys' max.
-  auto scores = [&](int step) -> float {
-    const uint8_t* T8 = sh.tile[step % kBufs];
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const uint8_t* krow = T8 + (16 * kh + c) * kRow;
+  if (sw) {
+    // ==================================== score waves ====================================
+    bf16x8 qb[2][16];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + (4 * s + g) * 16);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[s], acc, 0, 0, 0);
+    for (int j = 0; j < 2; ++j) {
+      const uint8_t* qrow = reinterpret_cast<const uint8_t*>(&sh.tile[0][0]) + 2 * kKT * kRow +
+                            (16 * (2 * hp + j) + c) * kRow;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) qb[j][s] = *reinterpret_cast<const bf16x8*>(qrow + (4 * s + g) * 16);
     }
-    float x[4];
-    float mt = neg_inf();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = step * kKT + 16 * kh + 4 * g + i;
-      x[i] = k < mk ? acc[i] * sc2 : neg_inf();
-      mt = fmaxf(mt, x[i]);
-    }
-    mt = max_xor32(max_xor16(mt));   // all four lane groups of head c agree
-    m_max = fmaxf(m_max, mt);
-    float pv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pv[i] = __builtin_amdgcn_exp2f(x[i] - m_ref);
-      l_run += pv[i];
-    }
-    // k-slots 0..3 of the P^T operand come from key half 0, 4..7 from key half 1
-    uint32_t* dst = reinterpret_cast<uint32_t*>(&sh.P[step & 1][hg][lane]) + 2 * kh;
-    dst[0] = pack_bf16x2(pv[0], pv[1]);
-    dst[1] = pack_bf16x2(pv[2], pv[3]);
-    return mt;
-  };
-  // O^T[dims d0 + 4r + e4][head 16hg' + c] += V^T P^T for step `step`
-  auto values = [&](int step) {
-    const uint8_t* T8 = sh.tile[step % kBufs];
-    bf16x8 pb[kHG];
-#pragma unroll
-    for (int h = 0; h < kHG; ++h) pb[h] = __builtin_bit_cast(bf16x8, sh.P[step & 1][h][lane]);
-    // key slot j: dims d0 + 4c .. +3 (two dwords)
-    uint32_t R[8][2];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int key = (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4));
-      const uint2 v = *reinterpret_cast<const uint2*>(T8 + key * kRow + (d0 + 4 * c) * 2);
-      R[j][0] = v.x;
-      R[j][1] = v.y;
-    }
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const int w = e4 >> 1;
-      u32x4 va;
-      if (e4 & 1) {
-        va = u32x4{perm_hi(R[1][w], R[0][w]), perm_hi(R[3][w], R[2][w]),
-                   perm_hi(R[5][w], R[4][w]), perm_hi(R[7][w], R[6][w])};
-      } else {
-        va = u32x4{perm_lo(R[1][w], R[0][w]), perm_lo(R[3][w], R[2][w]),
-                   perm_lo(R[5][w], R[4][w]), perm_lo(R[7][w], R[6][w])};
-      }
-      const bf16x8 A = __builtin_bit_cast(bf16x8, va);
-#pragma unroll
-      for (int h = 0; h < kHG; ++h)
-        O[h][e4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pb[h], O[h][e4], 0, 0, 0);
-    }
-  };
+    __syncthreads();   // every wave holds its query heads: tile 2 may take step 2's rows
+    if (mk > 0) issue(2);
 
-
-  // (a split without keys leaves O = 0, l = 0 and the reference at -inf)
-#pragma unroll
-  for (int h = 0; h < kHG; ++h)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) O[h][e] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int pass = 0; pass < (mk > 0 ? 2 : 0); ++pass) {
-    if (pass == 1) {
-#pragma unroll
-      for (int h = 0; h < kHG; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) O[h][e] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    l_run = 0.f;
-    if (pass == 1) {   // (the first pass's rows went out with the query)
-#pragma unroll
-      for (int j = 0; j < kDepth; ++j) issue(j);
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitLater);   // step 0's rows (steps 1, 2 in flight)
-    __syncthreads();
-    if (pass == 0) {
-      // reference: the max of step 0's keys of the head (step 0 always holds a real key),
-      // from both key halves; step 0's P is then computed against it
-      const uint8_t* T8 = sh.tile[0];
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const uint8_t* krow = T8 + (16 * kh + c) * kRow;
+    float m_ref[2] = {neg_inf(), neg_inf()};   // reference of head 16(2hp+j) + c (log2 domain)
+    float m_max[2] = {neg_inf(), neg_inf()};   // its max over this wave's keys so far
+    float l_run[2] = {0.f, 0.f};               // this lane's part of its normaliser
+    // raw S^T of step `step`: keys 16kh + 4g + i (rows), heads 16(2hp + j) + c (columns)
+    auto scores_raw = [&](int step, f32x4 (&acc)[2]) {
+      const uint8_t* krow = sh.tile[step % kBufs] + (16 * kh + c) * kRow;
+      acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + (4 * s + g) * 16);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[s], acc, 0, 0, 0);
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[0][s], acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[1][s], acc[1], 0, 0, 0);
       }
-      float mt = neg_inf();
+    };
+    // softmax of step `step`: P to LDS buffer step & 1 (keys past mk, and whole steps past
+    // the last, come out with P = 0). k-slots 0..3 of a P^T operand hold key half 0, 4..7
+    // key half 1.
+    auto softmax = [&](int step, const f32x4 (&acc)[2]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (16 * kh + 4 * g + i < mk) mt = fmaxf(mt, acc[i] * sc2);
-      mt = max_xor32(max_xor16(mt));
-      if (g == 0) sh.tmax[kh][16 * hg + c] = mt;
-      __syncthreads();
-      m_ref = fmaxf(sh.tmax[0][16 * hg + c], sh.tmax[1][16 * hg + c]);
-    } else {
-      m_ref = m_max;   // second pass: the true max (both halves), so every P <= 1
-      m_max = neg_inf();
-    }
-    scores(0);
+      for (int j = 0; j < 2; ++j) {
+        float x[4];
+        float mt = neg_inf();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int k = step * kKT + 16 * kh + 4 * g + i;
+          x[i] = k < mk ? acc[j][i] * sc2 : neg_inf();
+          mt = fmaxf(mt, x[i]);
+        }
+        mt = max_xor32(max_xor16(mt));   // all four lane groups of head c agree
+        m_max[j] = fmaxf(m_max[j], mt);
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[i] = __builtin_amdgcn_exp2f(x[i] - m_ref[j]);
+          l_run[j] += pv[i];
+        }
+        uint32_t* dst = reinterpret_cast<uint32_t*>(&sh.P[step & 1][2 * hp + j][lane]) + 2 * kh;
+        dst[0] = pack_bf16x2(pv[0], pv[1]);
+        dst[1] = pack_bf16x2(pv[2], pv[3]);
+      }
+    };
 
-    // Software pipeline: step s runs the values of step s and the scores of step s+1,
-    // independent work that the waves interleave. One barrier per step makes visible the
-    // P of step s, the rows of step s+1 and frees the buffer of step s-1.
-    for (int step = 0; step < nsteps; ++step) {
-      __builtin_amdgcn_s_waitcnt(kWaitNext);   // step s+1's rows (step s+2's in flight)
+    for (int pass = 0; pass < npass; ++pass) {
+      if (pass == 1) {   // (the first pass's rows went out with the query)
+#pragma unroll
+        for (int j = 0; j < kDepth; ++j) issue(j);
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitLater);   // step 0's rows (steps 1, 2 in flight)
       __syncthreads();
-      issue(step + kDepth);
-      values(step);
-      scores(step + 1);                        // past the last step: P = 0, never read
+      f32x4 acc[2];
+      scores_raw(0, acc);
+      if (pass == 0) {
+        // reference: the max of step 0's keys of the head (step 0 always holds a real key),
+        // over both key halves
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          float mt = neg_inf();
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * kh + 4 * g + i < mk) mt = fmaxf(mt, acc[j][i] * sc2);
+          mt = max_xor32(max_xor16(mt));
+          if (g == 0) sh.tmax[kh][16 * (2 * hp + j) + c] = mt;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int head = 16 * (2 * hp + j) + c;
+        if (pass == 0) {
+          m_ref[j] = fmaxf(sh.tmax[0][head], sh.tmax[1][head]);
+        } else {
+          m_ref[j] = m_max[j];   // second pass: the true max (both halves), so every P <= 1
+          m_max[j] = neg_inf();
+        }
+        l_run[j] = 0.f;
+      }
+      softmax(0, acc);
+      // one barrier per step makes visible the P of step s, the rows of step s+1 and frees
+      // the buffer of step s-1; the value waves weigh step s meanwhile
+      for (int step = 0; step < nsteps; ++step) {
+        __builtin_amdgcn_s_waitcnt(kWaitNext);   // step s+1's rows (step s+2's in flight)
+        __syncthreads();
+        issue(step + kDepth);
+        scores_raw(step + 1, acc);               // past the last step: P = 0, never read
+        softmax(step + 1, acc);
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitAll);   // no row load may outlive the pass (or the LDS)
+      if (pass == 1) break;
+      // a second pass only if some head saw a score more than kSafe above its reference
+      const bool wave_redo = __ballot(m_max[0] > m_ref[0] + kSafe || m_max[1] > m_ref[1] + kSafe) != 0;
+      if (lane == 0) sh.redo[wave] = wave_redo;
+      __syncthreads();
+      int redo = 0;
+      for (int w = 0; w < kSW; ++w) redo |= sh.redo[w];
+      if (!redo) break;
+      // the second pass's reference: the max over both key halves
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (g == 0) sh.tmax[kh][16 * (2 * hp + j) + c] = m_max[j];
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int head = 16 * (2 * hp + j) + c;
+        m_max[j] = fmaxf(sh.tmax[0][head], sh.tmax[1][head]);
+      }
+      __syncthreads();   // every wave read the flags and maxima and is done with the tiles
     }
-    __builtin_amdgcn_s_waitcnt(kWaitAll);  // no row load may outlive the pass (or the LDS)
-    // a second pass only if some head of the query saw a score more than kSafe above its
-    // reference (P up to 2^kSafe and the sums stay far inside fp32 range otherwise)
-    if (pass == 1) break;
-    const bool wave_redo = __ballot(m_max > m_ref + kSafe) != 0;   // over all lanes (heads)
-    if (lane == 0) sh.redo[wave] = wave_redo;
-    __syncthreads();
-    int redo = 0;
-    for (int w = 0; w < kAW; ++w) redo |= sh.redo[w];
-    if (!redo) break;
-    // the second pass's reference: the max over both key halves
-    if (g == 0) sh.tmax[kh][16 * hg + c] = m_max;
-    __syncthreads();
-    m_max = fmaxf(sh.tmax[0][16 * hg + c], sh.tmax[1][16 * hg + c]);
-    __syncthreads();   // every wave read the flags and maxima and is done with the tiles
-  }
 
-  // ---- normaliser of head 16hg + c: both key halves, four lane groups each ----
-  {
-    const float L = add_xor32(add_xor16(l_run));
-    if (g == 0) sh.tmax[kh][16 * hg + c] = L;
+    // ---- normaliser of head 16(2hp+j) + c: both key halves, four lane groups each ----
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float L = add_xor32(add_xor16(l_run[j]));
+      if (g == 0) sh.tmax[kh][16 * (2 * hp + j) + c] = L;
+    }
     __syncthreads();
     if (kh == 0 && g == 0) {
-      const float Lh = sh.tmax[0][16 * hg + c] + sh.tmax[1][16 * hg + c];
-      if (S == 1) {
-        sh.norm[16 * hg + c] = Lh;
-        if (a.lse) a.lse[(int64_t)t * kHeads + 16 * hg + c] = (m_ref + __log2f(Lh)) * kLn2;
-      } else {
-        float* ml = a.part_ml + ((int64_t)u * kHeads + 16 * hg + c) * 2;
-        store_dev(ml, m_ref);
-        store_dev(ml + 1, Lh);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int head = 16 * (2 * hp + j) + c;
+        const float Lh = sh.tmax[0][head] + sh.tmax[1][head];
+        if (S == 1) {
+          sh.norm[head] = Lh;
+          if (a.lse) a.lse[(int64_t)t * kHeads + head] = (m_ref[j] + __log2f(Lh)) * kLn2;
+        } else {
+          float* ml = a.part_ml + ((int64_t)u * kHeads + head) * 2;
+          store_dev(ml, m_ref[j]);
+          store_dev(ml + 1, Lh);
+        }
       }
     }
     __syncthreads();
-  }
-  if (S == 1) {
-    // ---- store: lane (c, g) holds dims d0 + 4(4g+i) + e4 of head 16h + c ----
+    if (S == 1) return;
+  } else {
+
+    // ==================================== value waves ====================================
+    __syncthreads();   // (the score waves read their query heads)
+    if (mk > 0) issue(2);
+    // O^T accumulators [half][head group][e4]: dims 128vw + 64hh + 4r + e4 (r = MFMA row) of
+    // head 16h + c
+    f32x4 O[2][kHG][4];
 #pragma unroll
-    for (int h = 0; h < kHG; ++h) {
-      const float inv = 1.0f / sh.norm[16 * h + c];
-      uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * kHeads + 16 * h + c) * kDim + d0;
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * g + i;  // row of the MFMA result = group of 4 dims
-        uint2 o;
-        o.x = pack_bf16x2(O[h][0][i] * inv, O[h][1][i] * inv);
-        o.y = pack_bf16x2(O[h][2][i] * inv, O[h][3][i] * inv);
-        *reinterpret_cast<uint2*>(orow + 4 * r) = o;
+      for (int h = 0; h < kHG; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) O[hh][h][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // O^T += V^T P^T for step `step`: A = V^T from LDS rows by byte permutes (8 keys x 1 dim
+    // per lane), B = P^T of each head group
+    auto values = [&](int step) {
+      const uint8_t* T8 = sh.tile[step % kBufs];
+      bf16x8 pb[kHG];
+#pragma unroll
+      for (int h = 0; h < kHG; ++h) pb[h] = __builtin_bit_cast(bf16x8, sh.P[step & 1][h][lane]);
+      // key slot j of half hh: dims 128vw + 64hh + 4c .. +3 (two dwords)
+      uint32_t R[2][8][2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int key = (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4));
+          const uint2 v = *reinterpret_cast<const uint2*>(T8 + key * kRow + (128 * vw + 64 * hh + 4 * c) * 2);
+          R[hh][j][0] = v.x;
+          R[hh][j][1] = v.y;
+        }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int w = e4 >> 1;
+          u32x4 va;
+          if (e4 & 1) {
+            va = u32x4{perm_hi(R[hh][1][w], R[hh][0][w]), perm_hi(R[hh][3][w], R[hh][2][w]),
+                       perm_hi(R[hh][5][w], R[hh][4][w]), perm_hi(R[hh][7][w], R[hh][6][w])};
+          } else {
+            va = u32x4{perm_lo(R[hh][1][w], R[hh][0][w]), perm_lo(R[hh][3][w], R[hh][2][w]),
+                       perm_lo(R[hh][5][w], R[hh][4][w]), perm_lo(R[hh][7][w], R[hh][6][w])};
+          }
+          const bf16x8 A = __builtin_bit_cast(bf16x8, va);
+#pragma unroll
+          for (int h = 0; h < kHG; ++h)
+            O[hh][h][e4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pb[h], O[hh][h][e4], 0, 0, 0);
+        }
+    };
+
+    for (int pass = 0; pass < npass; ++pass) {
+      if (pass == 1) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int h = 0; h < kHG; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) O[hh][h][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kDepth; ++j) issue(j);
       }
+      __builtin_amdgcn_s_waitcnt(kWaitLater);
+      __syncthreads();
+      __syncthreads();   // (the score waves' step-0 maxima)
+      for (int step = 0; step < nsteps; ++step) {
+        __builtin_amdgcn_s_waitcnt(kWaitNext);
+        __syncthreads();
+        issue(step + kDepth);
+        values(step);
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+      if (pass == 1) break;
+      if (lane == 0) sh.redo[wave] = 0;
+      __syncthreads();
+      int redo = 0;
+      for (int w = 0; w < kSW; ++w) redo |= sh.redo[w];
+      if (!redo) break;
+      __syncthreads();
+      __syncthreads();
     }
-    return;
+
+    __syncthreads();   // (the score waves' normalisers)
+    __syncthreads();
+    if (S == 1) {
+      // ---- store: lane (c, g) holds dims 128vw + 64hh + 4(4g+i) + e4 of head 16h + c ----
+#pragma unroll
+      for (int h = 0; h < kHG; ++h) {
+        const float inv = 1.0f / sh.norm[16 * h + c];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * kHeads + 16 * h + c) * kDim +
+                           128 * vw + 64 * hh;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i;  // row of the MFMA result = group of 4 dims
+            uint2 o;
+            o.x = pack_bf16x2(O[hh][h][0][i] * inv, O[hh][h][1][i] * inv);
+            o.y = pack_bf16x2(O[hh][h][2][i] * inv, O[hh][h][3][i] * inv);
+            *reinterpret_cast<uint2*>(orow + 4 * r) = o;
+          }
+        }
+      }
+      return;
+    }
+    // partial O of this split, in the lanes' own order (every instruction: 1 KB of lines)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int h = 0; h < kHG; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 v = __builtin_bit_cast(u32x4, f32x4{O[hh][h][0][i], O[hh][h][1][i], O[hh][h][2][i], O[hh][h][3][i]});
+          __builtin_amdgcn_raw_buffer_store_b128(v, part_rsrc(a, U), part_off(u, vw, hh, h, i) + lane * 16, 0, kCoherent);
+        }
   }
 
-  // ---- key splits: this work-group's partial O, then the last of the query combines ----
+  // ---- key splits: the last work-group of the query to finish combines the partials ----
   // The softmax of the whole key list from the splits' partial ones: with M the largest
-  // reference, o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) L_s.
-  // Partials travel by device-coherent stores and loads (written through to, and read
-  // from, the level all XCDs share), in the lanes' own order so every instruction moves
-  // 1 KB of whole lines; no cache-wide write-back or invalidation is needed. The count is
+  // reference, o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) L_s. Partials travel by
+  // device-coherent stores and loads (written through to, and read from, the level all
+  // XCDs share), so no cache-wide write-back or invalidation is needed; the count is
   // raised only after every store of the work-group has completed.
-  const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
-      a.part_o, (short)0, (int)(U * kAttnPartBytesO), kRsrcWord3);
-  auto part_off = [&](int unit, int h, int i) {   // byte offset of lane 0's f32x4
-    return (uint32_t)((((unit * kAW + wave) * kHG + h) * 4 + i) * 64 * 16);
-  };
-#pragma unroll
-  for (int h = 0; h < kHG; ++h)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4 v = __builtin_bit_cast(u32x4, f32x4{O[h][0][i], O[h][1][i], O[h][2][i], O[h][3][i]});
-      __builtin_amdgcn_raw_buffer_store_b128(v, prs, part_off(u, h, i) + lane * 16, 0, kCoherent);
-    }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's partial is device-visible
   __syncthreads();
   if (tid == 0) sh.last = atomicAdd(&a.counters[t], 1u) == (uint32_t)(S - 1);
   __syncthreads();
   if (!sh.last) return;
   if (tid == 0) a.counters[t] = 0u;   // every split of this call has counted: ready for the next
+  // every wave combines one slice: dims 128cv + 64chh .. +63 of all heads
+  const int cv = wave & 3, chh = wave >> 2;
   const int u0 = t * S;
-  // weights of the splits per head 16h + c, the own partial scaled in place
   float wgt[kHG][kMaxSplits], Lsum[kHG], Mx[kHG];
 #pragma unroll
   for (int h = 0; h < kHG; ++h) {
@@ -456,46 +537,34 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
     Lsum[h] = L;
     Mx[h] = M;
   }
-  // sum over the splits in split order, so the result is the same bit for bit whichever
-  // work-group combines: acc = w_0 O_0, then += w_s O_s. O_0 comes from registers when this
-  // is split 0; otherwise every partial (this one's too) is read back, 16 lines of 1 KB per
-  // wave for one split at a time, and O's registers hold the sum.
+  // sum over the splits in split order (the same bits whichever work-group combines)
+  f32x4 acc[kHG][4];
 #pragma unroll
   for (int s2 = 0; s2 < kMaxSplits; ++s2) {
     if (s2 >= S) break;
     asm volatile("" ::: "memory");   // one split's loads in flight at a time (registers)
-    if (s2 == 0 && split == 0) {
+    f32x4 v[kHG][4];
 #pragma unroll
-      for (int h = 0; h < kHG; ++h)
+    for (int h = 0; h < kHG; ++h)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) O[h][e] = wgt[h][0] * O[h][e];
-    } else {
-      f32x4 v[kHG][4];
+      for (int i = 0; i < 4; ++i)
+        v[h][i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                part_rsrc(a, U), part_off(u0 + s2, cv, chh, h, i) + lane * 16, 0, kCoherent));
 #pragma unroll
-      for (int h = 0; h < kHG; ++h)
+    for (int h = 0; h < kHG; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          v[h][i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  prs, part_off(u0 + s2, h, i) + lane * 16, 0, kCoherent));
-#pragma unroll
-      for (int h = 0; h < kHG; ++h)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            O[h][e][i] = s2 == 0 ? wgt[h][0] * v[h][i][e] : O[h][e][i] + wgt[h][s2] * v[h][i][e];
-    }
+      for (int i = 0; i < 4; ++i) acc[h][i] = s2 == 0 ? wgt[h][0] * v[h][i] : acc[h][i] + wgt[h][s2] * v[h][i];
   }
 #pragma unroll
   for (int h = 0; h < kHG; ++h) {
     const int head = 16 * h + c;
     const float inv = 1.0f / Lsum[h];
-    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * kHeads + head) * kDim + d0;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * kHeads + head) * kDim + 128 * cv + 64 * chh;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint2 o;
-      o.x = pack_bf16x2(O[h][0][i] * inv, O[h][1][i] * inv);
-      o.y = pack_bf16x2(O[h][2][i] * inv, O[h][3][i] * inv);
+      o.x = pack_bf16x2(acc[h][i][0] * inv, acc[h][i][1] * inv);
+      o.y = pack_bf16x2(acc[h][i][2] * inv, acc[h][i][3] * inv);
       *reinterpret_cast<uint2*>(orow + 4 * (4 * g + i)) = o;
     }
     if (a.lse && wave == 0 && g == 0) a.lse[(int64_t)t * kHeads + head] = (Mx[h] + __log2f(Lsum[h])) * kLn2;
