@@ -585,13 +585,27 @@ __global__ __launch_bounds__(NT) void select_merge_kernel(SelectArgs a) {
     const int total = a.parts * kCandBlocks;
     uint32_t key[EPT];
     ListIds<EPT> I;
+    // a thread's EPT entries are contiguous and 16-byte aligned (total is a multiple of 16):
+    // all id loads first, then all block-value loads, so each set is one round trip
+    static_assert(EPT % 4 == 0, "whole 16-byte loads");
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const int i = (int)threadIdx.x * EPT + e;
-      const int32_t b = i < total ? lists[i] : -1;
-      I.valid[e] = b >= 0;
-      I.ids[e] = b;
-      key[e] = b >= 0 ? order_key(block_value(a, t, n, b)) : 0u;
+    for (int q = 0; q < EPT / 4; ++q) {
+      const int i = (int)threadIdx.x * EPT + 4 * q;
+      const int4 v = i < total ? *reinterpret_cast<const int4*>(lists + i) : int4{-1, -1, -1, -1};
+      I.ids[4 * q] = v.x;
+      I.ids[4 * q + 1] = v.y;
+      I.ids[4 * q + 2] = v.z;
+      I.ids[4 * q + 3] = v.w;
+    }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) I.valid[e] = I.ids[e] >= 0;
+    if (a.block_max) {
+      const float* bm = a.block_max + (int64_t)t * a.ld_block_max;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) key[e] = I.valid[e] ? order_key(bm[I.ids[e]]) : 0u;
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) key[e] = I.valid[e] ? order_key(block_value(a, t, n, I.ids[e])) : 0u;
     }
     const int ks[2] = {kCandBlocks, kTopK};
     int32_t* const outs[2] = {cand, core};
