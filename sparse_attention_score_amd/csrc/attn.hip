@@ -172,12 +172,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   if (valid_q) {
     const int32_t j = sh.topk[tid];   // kAThreads == kTopK
     const bool v = j >= 0 && j < n;
-    int incl = (int)v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      int o = __shfl_up(incl, d, 64);
-      if (lane >= d) incl += o;
-    }
+    const int incl = wave_incl_scan((int)v);
     if (lane == 63) sh.wave_cnt[wave] = incl;
     __syncthreads();
     int nsel = 0, before = 0;

@@ -78,6 +78,41 @@ __device__ __forceinline__ float add_xor32(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP (VALU, no LDS round trip):
+// shifts by 1, 2, 4, 8 inside each row of 16 (lanes shifted in from outside the row add
+// 0), then the total of row 0 broadcast into rows 1 and 3 and the total of rows 0-1 into
+// rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, true);    // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, true);    // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, true);    // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, true);    // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+  return x;
+}
+
+// Min and max of a u32 over the 64 lanes of a wave, in every lane (DPP inside rows of 16,
+// then the row-swap instructions across rows).
+__device__ __forceinline__ void wave_minmax_u32(uint32_t& lo, uint32_t& hi) {
+#define SA_DPP_MINMAX(ctrl)                                                                     \
+  lo = min(lo, (uint32_t)__builtin_amdgcn_update_dpp((int)lo, (int)lo, ctrl, 0xF, 0xF, false)); \
+  hi = max(hi, (uint32_t)__builtin_amdgcn_update_dpp((int)hi, (int)hi, ctrl, 0xF, 0xF, false));
+  SA_DPP_MINMAX(0xB1)    // quad_perm 1,0,3,2
+  SA_DPP_MINMAX(0x4E)    // quad_perm 2,3,0,1
+  SA_DPP_MINMAX(0x141)   // row_half_mirror
+  SA_DPP_MINMAX(0x140)   // row_mirror
+#undef SA_DPP_MINMAX
+  auto l16 = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  auto h16 = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  lo = min(l16[0], l16[1]);
+  hi = max(h16[0], h16[1]);
+  auto l32 = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  auto h32 = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  lo = min(l32[0], l32[1]);
+  hi = max(h32[0], h32[1]);
+}
+
 // Max over each aligned group of 8 lanes (DPP quad permutes, then the half-row mirror).
 __device__ __forceinline__ float max8_lanes(float v) {
   float m = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));

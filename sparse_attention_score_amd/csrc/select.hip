@@ -58,11 +58,7 @@ __device__ __forceinline__ int64_t visible_n(const QueryMeta& m, int t) {
 template <int NT>
 __device__ __forceinline__ int wg_inclusive_scan(int v, SelShared& sh, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int o = __shfl_up(v, d, 64);
-    if (lane >= d) v += o;
-  }
+  v = wave_incl_scan(v);
   if (lane == 63) sh.wave_sum[wave] = v;
   __syncthreads();
   int before = 0, tot = 0;
@@ -81,14 +77,8 @@ __device__ __forceinline__ int wg_inclusive_scan(int v, SelShared& sh, int& tota
 template <int NT>
 __device__ __forceinline__ void wg_inclusive_scan2(int& a, int& b, SelShared& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int oa = __shfl_up(a, d, 64), ob = __shfl_up(b, d, 64);
-    if (lane >= d) {
-      a += oa;
-      b += ob;
-    }
-  }
+  a = wave_incl_scan(a);
+  b = wave_incl_scan(b);
   if (lane == 63) {
     sh.wave_sum[wave] = a;
     sh.wave_sum2[wave] = b;
@@ -126,11 +116,7 @@ template <int NT>
 __device__ __forceinline__ void wg_minmax(uint32_t lo, uint32_t hi, SelShared& sh, uint32_t& glo,
                                           uint32_t& ghi) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, d, 64));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, d, 64));
-  }
+  wave_minmax_u32(lo, hi);
   if (lane == 0) {
     sh.wmin[wave] = lo;
     sh.wmax[wave] = hi;
