@@ -62,11 +62,6 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Cross-lane helpers (wave64).
-__device__ __forceinline__ float shfl_xor_f(float v, int m) {
-  return __shfl_xor(v, m, 64);
-}
-
 // v[l] + v[l ^ 16] and v[l] + v[l ^ 32] with the gfx950 row-swap instructions (VALU, no
 // LDS round trip). Both lanes of a pair add the same two values, so they agree bitwise.
 __device__ __forceinline__ float add_xor16(float v) {
