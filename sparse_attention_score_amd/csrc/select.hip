@@ -348,17 +348,34 @@ __device__ __forceinline__ void multi_select(const uint32_t (&key)[EPT], const I
     const int q = wave;
     const int kk = k[q] - sh.tabove[q];
     const int mcol = sh.ncoll[q];
-    for (int i = lane; i < mcol; i += 64) {
-      const uint32_t ki = sh.ckey[q][i];
-      const int32_t ii = sh.cid[q][i];
+    if (mcol <= 64) {
+      // one element per lane; the others arrive by lane reads (no LDS round trips)
+      const uint32_t ki = lane < mcol ? sh.ckey[q][lane] : 0u;
+      const int32_t ii = lane < mcol ? sh.cid[q][lane] : 0;
       int rank = 0;
+#pragma unroll 4
       for (int j = 0; j < mcol; ++j) {
-        const uint32_t kj = sh.ckey[q][j];
-        rank += (kj > ki || (kj == ki && sh.cid[q][j] < ii)) ? 1 : 0;
+        const uint32_t kj = (uint32_t)__builtin_amdgcn_readlane((int)ki, j);
+        const int32_t ij = __builtin_amdgcn_readlane(ii, j);
+        rank += (kj > ki || (kj == ki && ij < ii)) ? 1 : 0;
       }
-      if (rank == kk - 1) {
+      if (lane < mcol && rank == kk - 1) {
         sh.vkey[q] = ki;
         sh.vid[q] = ii;
+      }
+    } else {
+      for (int i = lane; i < mcol; i += 64) {
+        const uint32_t ki = sh.ckey[q][i];
+        const int32_t ii = sh.cid[q][i];
+        int rank = 0;
+        for (int j = 0; j < mcol; ++j) {
+          const uint32_t kj = sh.ckey[q][j];
+          rank += (kj > ki || (kj == ki && sh.cid[q][j] < ii)) ? 1 : 0;
+        }
+        if (rank == kk - 1) {
+          sh.vkey[q] = ki;
+          sh.vid[q] = ii;
+        }
       }
     }
   }
