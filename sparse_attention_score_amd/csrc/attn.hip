@@ -28,7 +28,10 @@
 // The values of step s and the scores of step s+1 are independent and run in the same
 // loop iteration, with one barrier per step.
 // Small batches spread each query's key list over kMaxSplits work-groups; the last to
-// finish combines their partial results.
+// finish combines their partial results. Mid-size batches (33 to 128 queries) split each
+// query's 64 heads over two work-groups instead, which need no combining: both gather the
+// same rows, and as neighbours in the grid they normally share an XCD, so the second
+// read comes from its L2.
 #include "sa_device.h"
 #include "sa_launch.h"
 
@@ -117,16 +120,25 @@ __device__ __forceinline__ void row_to_lds(const uint16_t* row, uint32_t lds, in
   to_lds16(row + lane * 8, lds);
 }
 
+template <int HS>
 __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
+  // HS = 2: the query's heads are split over two work-groups (32 each) that gather the same
+  // rows (normally on one XCD, so the second reads them from L2); no key splits then
+  static_assert(HS == 1 || HS == 2, "one or two head sets");
+  constexpr int NJ = 2 / HS;          // head groups per score wave
+  constexpr int NV = kHG / HS;        // head groups per value wave
+  constexpr int kQPW = kHeads / HS / kAW;   // query heads each wave loads
   __shared__ __attribute__((aligned(16))) AttnShared sh;
   // work-group -> query: ids are dealt round-robin over the 8 XCDs, so XCD x gets the
   // contiguous query range x*Q8 .. x*Q8+Q8-1 (neighbouring queries share window rows).
   // With key splits the unit is (query, split), split fastest, so the splits of a query
   // normally share an XCD.
-  const int T = (int)a.m.T, S = a.splits, U = T * S;
+  const int T = (int)a.m.T, S = HS == 1 ? a.splits : 1, U = T * S * HS;
   const int u8 = (U + 7) >> 3;
-  const int u = (blockIdx.x & 7) * u8 + (blockIdx.x >> 3);
-  if ((int)(blockIdx.x >> 3) >= u8 || u >= U) return;
+  const int uw = (blockIdx.x & 7) * u8 + (blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= u8 || uw >= U) return;
+  const int hs = HS == 2 ? (uw & 1) : 0;
+  const int u = uw / HS;   // (query, split) unit
   const int t = u / S, split = u - t * S;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int c = lane & 15, g = lane >> 4;
@@ -135,6 +147,9 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   const bool sw = wave < kSW;
   const int kh = wave & 1, hp = (wave >> 1) & 1;
   const int vw = wave & 3;
+  // head group of the score wave's j-th set; of the value wave's h-th
+  auto sgrp = [&](int j) { return HS == 1 ? 2 * hp + j : 2 * hs + hp; };
+  auto vgrp = [&](int h) { return hs * NV + h; };
 
   const int seq = a.m.seq_id[t], p = a.m.pos[t];
   const bool valid_q = seq >= 0 && seq < a.m.num_seqs && p >= 0;
@@ -159,11 +174,11 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
     }
     const uint16_t* qt = reinterpret_cast<const uint16_t*>(a.q) + (int64_t)t * kHeads * kDim;
 #pragma unroll
-    for (int i = 0; i < kHeads / kAW; ++i) {
-      const int head = (kHeads / kAW) * wave + i;
+    for (int i = 0; i < kQPW; ++i) {
+      const int head = (kHeads / HS) * hs + kQPW * wave + i;
       to_lds16(qt + head * kDim + 8 * lane, qlds + head * kRow);
     }
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kHeads / kAW));   // the selection (query loads in flight)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kQPW));   // the selection (query loads in flight)
   }
   __syncthreads();
 
@@ -191,7 +206,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   __syncthreads();
 
   if (m == 0) {  // invalid query (no load was issued): zero output, lse = -inf
-    if (split != 0) return;
+    if (split != 0 || hs != 0) return;
     uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (int64_t)t * kHeads * kDim;
     for (int i = tid; i < kHeads * kDim / 8; i += kAThreads)
       *reinterpret_cast<u32x4*>(o + 8 * i) = u32x4{0u, 0u, 0u, 0u};
@@ -233,37 +248,43 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
 
   if (sw) {
     // ==================================== score waves ====================================
-    bf16x8 qb[2][16];
+    bf16x8 qb[NJ][16];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const uint8_t* qrow = reinterpret_cast<const uint8_t*>(&sh.tile[0][0]) + 2 * kKT * kRow +
-                            (16 * (2 * hp + j) + c) * kRow;
+                            (16 * sgrp(j) + c) * kRow;
 #pragma unroll
       for (int s = 0; s < 16; ++s) qb[j][s] = *reinterpret_cast<const bf16x8*>(qrow + (4 * s + g) * 16);
     }
     __syncthreads();   // every wave holds its query heads: tile 2 may take step 2's rows
     if (mk > 0) issue(2);
 
-    float m_ref[2] = {neg_inf(), neg_inf()};   // reference of head 16(2hp+j) + c (log2 domain)
-    float m_max[2] = {neg_inf(), neg_inf()};   // its max over this wave's keys so far
-    float l_run[2] = {0.f, 0.f};               // this lane's part of its normaliser
+    float m_ref[NJ], m_max[NJ], l_run[NJ];   // per head 16 sgrp(j) + c: reference (log2 domain),
+#pragma unroll                                // max over this wave's keys so far, this lane's
+    for (int j = 0; j < NJ; ++j) {            // part of the normaliser
+      m_ref[j] = neg_inf();
+      m_max[j] = neg_inf();
+      l_run[j] = 0.f;
+    }
     // raw S^T of step `step`: keys 16kh + 4g + i (rows), heads 16(2hp + j) + c (columns)
-    auto scores_raw = [&](int step, f32x4 (&acc)[2]) {
+    auto scores_raw = [&](int step, f32x4 (&acc)[NJ]) {
       const uint8_t* krow = sh.tile[step % kBufs] + (16 * kh + c) * kRow;
-      acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + (4 * s + g) * 16);
-        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[0][s], acc[0], 0, 0, 0);
-        acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[1][s], acc[1], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j][s], acc[j], 0, 0, 0);
       }
     };
     // softmax of step `step`: P to LDS buffer step & 1 (keys past mk, and whole steps past
     // the last, come out with P = 0). k-slots 0..3 of a P^T operand hold key half 0, 4..7
     // key half 1.
-    auto softmax = [&](int step, const f32x4 (&acc)[2]) {
+    auto softmax = [&](int step, const f32x4 (&acc)[NJ]) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int j = 0; j < NJ; ++j) {
         float x[4];
         float mt = neg_inf();
 #pragma unroll
@@ -280,7 +301,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
           pv[i] = __builtin_amdgcn_exp2f(x[i] - m_ref[j]);
           l_run[j] += pv[i];
         }
-        uint32_t* dst = reinterpret_cast<uint32_t*>(&sh.P[step & 1][2 * hp + j][lane]) + 2 * kh;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(&sh.P[step & 1][sgrp(j)][lane]) + 2 * kh;
         dst[0] = pack_bf16x2(pv[0], pv[1]);
         dst[1] = pack_bf16x2(pv[2], pv[3]);
       }
@@ -293,25 +314,25 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       }
       __builtin_amdgcn_s_waitcnt(kWaitLater);   // step 0's rows (steps 1, 2 in flight)
       __syncthreads();
-      f32x4 acc[2];
+      f32x4 acc[NJ];
       scores_raw(0, acc);
       if (pass == 0) {
         // reference: the max of step 0's keys of the head (step 0 always holds a real key),
         // over both key halves
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           float mt = neg_inf();
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             if (16 * kh + 4 * g + i < mk) mt = fmaxf(mt, acc[j][i] * sc2);
           mt = max_xor32(max_xor16(mt));
-          if (g == 0) sh.tmax[kh][16 * (2 * hp + j) + c] = mt;
+          if (g == 0) sh.tmax[kh][16 * sgrp(j) + c] = mt;
         }
       }
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int head = 16 * (2 * hp + j) + c;
+      for (int j = 0; j < NJ; ++j) {
+        const int head = 16 * sgrp(j) + c;
         if (pass == 0) {
           m_ref[j] = fmaxf(sh.tmax[0][head], sh.tmax[1][head]);
         } else {
@@ -333,7 +354,10 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       __builtin_amdgcn_s_waitcnt(kWaitAll);   // no row load may outlive the pass (or the LDS)
       if (pass == 1) break;
       // a second pass only if some head saw a score more than kSafe above its reference
-      const bool wave_redo = __ballot(m_max[0] > m_ref[0] + kSafe || m_max[1] > m_ref[1] + kSafe) != 0;
+      bool over = false;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) over = over || m_max[j] > m_ref[j] + kSafe;
+      const bool wave_redo = __ballot(over) != 0;
       if (lane == 0) sh.redo[wave] = wave_redo;
       __syncthreads();
       int redo = 0;
@@ -341,12 +365,12 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       if (!redo) break;
       // the second pass's reference: the max over both key halves
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        if (g == 0) sh.tmax[kh][16 * (2 * hp + j) + c] = m_max[j];
+      for (int j = 0; j < NJ; ++j)
+        if (g == 0) sh.tmax[kh][16 * sgrp(j) + c] = m_max[j];
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int head = 16 * (2 * hp + j) + c;
+      for (int j = 0; j < NJ; ++j) {
+        const int head = 16 * sgrp(j) + c;
         m_max[j] = fmaxf(sh.tmax[0][head], sh.tmax[1][head]);
       }
       __syncthreads();   // every wave read the flags and maxima and is done with the tiles
@@ -354,15 +378,15 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
 
     // ---- normaliser of head 16(2hp+j) + c: both key halves, four lane groups each ----
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const float L = add_xor32(add_xor16(l_run[j]));
-      if (g == 0) sh.tmax[kh][16 * (2 * hp + j) + c] = L;
+      if (g == 0) sh.tmax[kh][16 * sgrp(j) + c] = L;
     }
     __syncthreads();
     if (kh == 0 && g == 0) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int head = 16 * (2 * hp + j) + c;
+      for (int j = 0; j < NJ; ++j) {
+        const int head = 16 * sgrp(j) + c;
         const float Lh = sh.tmax[0][head] + sh.tmax[1][head];
         if (S == 1) {
           sh.norm[head] = Lh;
@@ -383,20 +407,20 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
     if (mk > 0) issue(2);
     // O^T accumulators [half][head group][e4]: dims 128vw + 64hh + 4r + e4 (r = MFMA row) of
     // head 16h + c
-    f32x4 O[2][kHG][4];
+    f32x4 O[2][NV][4];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int h = 0; h < kHG; ++h)
+      for (int h = 0; h < NV; ++h)
 #pragma unroll
         for (int e = 0; e < 4; ++e) O[hh][h][e] = f32x4{0.f, 0.f, 0.f, 0.f};
     // O^T += V^T P^T for step `step`: A = V^T from LDS rows by byte permutes (8 keys x 1 dim
     // per lane), B = P^T of each head group
     auto values = [&](int step) {
       const uint8_t* T8 = sh.tile[step % kBufs];
-      bf16x8 pb[kHG];
+      bf16x8 pb[NV];
 #pragma unroll
-      for (int h = 0; h < kHG; ++h) pb[h] = __builtin_bit_cast(bf16x8, sh.P[step & 1][h][lane]);
+      for (int h = 0; h < NV; ++h) pb[h] = __builtin_bit_cast(bf16x8, sh.P[step & 1][vgrp(h)][lane]);
       // key slot j of half hh: dims 128vw + 64hh + 4c .. +3 (two dwords)
       uint32_t R[2][8][2];
 #pragma unroll
@@ -423,7 +447,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
           }
           const bf16x8 A = __builtin_bit_cast(bf16x8, va);
 #pragma unroll
-          for (int h = 0; h < kHG; ++h)
+          for (int h = 0; h < NV; ++h)
             O[hh][h][e4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pb[h], O[hh][h][e4], 0, 0, 0);
         }
     };
@@ -433,7 +457,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-          for (int h = 0; h < kHG; ++h)
+          for (int h = 0; h < NV; ++h)
 #pragma unroll
             for (int e = 0; e < 4; ++e) O[hh][h][e] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -464,11 +488,11 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
     if (S == 1) {
       // ---- store: lane (c, g) holds dims 128vw + 64hh + 4(4g+i) + e4 of head 16h + c ----
 #pragma unroll
-      for (int h = 0; h < kHG; ++h) {
-        const float inv = 1.0f / sh.norm[16 * h + c];
+      for (int h = 0; h < NV; ++h) {
+        const float inv = 1.0f / sh.norm[16 * vgrp(h) + c];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * kHeads + 16 * h + c) * kDim +
+          uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * kHeads + 16 * vgrp(h) + c) * kDim +
                            128 * vw + 64 * hh;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -483,16 +507,19 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       return;
     }
     // partial O of this split, in the lanes' own order (every instruction: 1 KB of lines)
+    if constexpr (HS == 1) {
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-      for (int h = 0; h < kHG; ++h)
+        for (int h = 0; h < kHG; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const u32x4 v = __builtin_bit_cast(u32x4, f32x4{O[hh][h][0][i], O[hh][h][1][i], O[hh][h][2][i], O[hh][h][3][i]});
-          __builtin_amdgcn_raw_buffer_store_b128(v, part_rsrc(a, U), part_off(u, vw, hh, h, i) + lane * 16, 0, kCoherent);
-        }
+          for (int i = 0; i < 4; ++i) {
+            const u32x4 v = __builtin_bit_cast(u32x4, f32x4{O[hh][h][0][i], O[hh][h][1][i], O[hh][h][2][i], O[hh][h][3][i]});
+            __builtin_amdgcn_raw_buffer_store_b128(v, part_rsrc(a, U), part_off(u, vw, hh, h, i) + lane * 16, 0, kCoherent);
+          }
+    }
   }
+  if constexpr (HS == 1) {
 
   // ---- key splits: the last work-group of the query to finish combines the partials ----
   // The softmax of the whole key list from the splits' partial ones: with M the largest
@@ -564,6 +591,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
     }
     if (a.lse && wave == 0 && g == 0) a.lse[(int64_t)t * kHeads + head] = (Mx[h] + __log2f(Lsum[h])) * kLn2;
   }
+  }   // HS == 1
 }
 
 __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
@@ -573,9 +601,17 @@ __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
 
 }  // namespace
 
+// Batches of 33 to 128 queries (fewer work-groups than CUs) split each query's heads over
+// two work-groups; smaller ones split its keys instead (splits > 1), larger ones neither.
+int attn_head_sets(int64_t T, int splits) { return splits == 1 && T > 32 && T <= 128 ? 2 : 1; }
+
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
-  const int64_t u8 = (a.m.T * a.splits + 7) / 8;   // work units per XCD
-  hipLaunchKernelGGL(attn_kernel, dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
+  const int hs = attn_head_sets(a.m.T, a.splits);
+  const int64_t u8 = (a.m.T * a.splits * hs + 7) / 8;   // work units per XCD
+  if (hs == 2)
+    hipLaunchKernelGGL(attn_kernel<2>, dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_kernel<1>, dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -178,6 +178,16 @@ def test_attention_key_splits_match_one_group_per_query():
             assert np.abs(l_s[t] - res.lse[t]).max() <= LSE_TOL
 
 
+def test_attention_head_sets():
+    """33 to 128 queries: each query's heads are split over two work-groups (32 heads each).
+    Ragged contexts, both key dtypes' paths share this kernel; bf16 keys here."""
+    rng = np.random.default_rng(81)
+    n_raw = [int(x) for x in rng.integers(3, 4000, size=36)]
+    wl = W.make_decode(B=36, n_raw=n_raw, ratio=2, key_dtype="bf16", name="head-sets",
+                       with_compress=False, seed=81)
+    _e2e(wl)
+
+
 def test_prefill_small_ratio1():
     wl = W.make_prefill(T=200, offset=900, ratio=1, key_dtype="bf16", name="prefill-small", seed=11)
     _e2e(wl)
