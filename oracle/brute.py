@@ -46,6 +46,21 @@ def select(I, k=512, cb=2048, blk=8):
     return kept, sorted(j for _, j in cand[:k])
 
 
+def rescore(qI, w, keys, cand, n, k=512, blk=8):
+    """Scores of the visible positions of candidate blocks `cand` only, then the first k by
+    (-score, position), ascending. keys: n lists of floats."""
+    pos = []
+    for b in cand:
+        if b < 0:
+            continue
+        for r in range(blk):
+            if b * blk + r < n:
+                pos.append(b * blk + r)
+    s = scores(qI, w, [keys[p] for p in pos])
+    ranked = sorted(zip([-v for v in s], pos))
+    return sorted(p for _, p in ranked[:k])
+
+
 def attend(q, X, scale):
     """q: H lists of D floats; X: m lists of D floats -> (o: H x D, lse: H)."""
     o, lse = [], []

@@ -207,6 +207,30 @@ def select(I: np.ndarray, k: int = TOPK, cb: int = CAND_BLOCKS, blk: int = BLOCK
     return cand, topk_of(I, pos, k)
 
 
+def candidate_positions(cand: np.ndarray, n: int, blk: int = BLOCK) -> np.ndarray:
+    """Visible positions of the candidate blocks `cand` (ascending block ids, entries < 0
+    ignored), ascending."""
+    cand = np.asarray(cand, np.int64)
+    cand = cand[cand >= 0]
+    pos = (cand[:, None] * blk + np.arange(blk)[None, :]).reshape(-1)
+    return pos[pos < n]
+
+
+def rescore_select(qI: np.ndarray, w: np.ndarray, keys: np.ndarray, cand: np.ndarray, n: int,
+                   k: int = TOPK, blk: int = BLOCK):
+    """Candidate-bounded re-scoring: the indexer scores only the visible positions of a
+    carried candidate-block set (this query's own index query and weights), and the top-k
+    of them by (score desc, position asc) is selected, ascending. This is how layers that
+    only index re-score the candidates an earlier layer's candidate stage kept ([P3] the
+    candidate stage that selects 2048 blocks of 8). `keys` holds the decoded keys of
+    positions 0..n-1. Returns (positions, their scores, selected positions)."""
+    pos = candidate_positions(cand, n, blk)
+    I = index_scores(qI, w, keys[pos]) if pos.size else np.zeros(0)
+    Ifull = np.full(n, -np.inf)
+    Ifull[pos] = I
+    return pos, I, topk_of(Ifull, pos, k)
+
+
 def attend(q: np.ndarray, X: np.ndarray, scale: float = SCALE) -> Tuple[np.ndarray, np.ndarray]:
     """One softmax over the rows of X for every head of q; X is both key and value ([P2]).
 

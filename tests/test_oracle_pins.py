@@ -241,6 +241,52 @@ def test_selection_small_takes_everything():
         assert idx.tolist() == list(range(n))
 
 
+# ---------------------------------------------------------------- candidate-bounded re-scoring
+
+def test_rescore_own_candidates_equals_two_stage_path():
+    """Re-scoring inside the query's own candidate blocks gives the two-stage path's top-512
+    (the candidate-stage lemma): a wrong block-to-position map or a dropped partial block
+    fails it."""
+    rng = np.random.default_rng(91)
+    for n in (20003, 40000):
+        qI = rng.standard_normal((16, 128))
+        w = rng.uniform(0, 1, 16)
+        keys = rng.standard_normal((n, 128))
+        I = O.index_scores(qI, w, keys)
+        cand, idx = O.select(I)
+        pos, Ic, sel = O.rescore_select(qI, w, keys, cand, n)
+        assert np.array_equal(sel, idx)
+        assert pos.shape[0] == sum(min(8, n - 8 * int(b)) for b in cand)
+        assert np.array_equal(Ic, I[pos])
+
+
+def test_rescore_brute_force_tiny():
+    rng = np.random.default_rng(92)
+    for n in (1, 7, 8, 9, 30, 61):
+        nb = -(-n // 8)
+        qI = rng.integers(-2, 3, (16, 128)).astype(float)
+        w = rng.integers(0, 3, 16).astype(float)
+        keys = rng.integers(-1, 2, (n, 128)).astype(float)   # many ties
+        for trial in range(4):
+            m = int(rng.integers(1, nb + 1))
+            cand = np.sort(rng.choice(nb, m, replace=False))
+            cand = np.concatenate([cand, -np.ones(3, np.int64)])   # -1 padding is ignored
+            for k in (1, 3, 16, 512):
+                _, _, sel = O.rescore_select(qI, w, keys, cand, n, k=k)
+                want = brute.rescore(qI.tolist(), w.tolist(), keys.tolist(), cand.tolist(), n, k=k)
+                assert sel.tolist() == want, (n, k, cand)
+
+
+def test_rescore_small_set_takes_everything_and_ignores_invisible():
+    rng = np.random.default_rng(93)
+    n = 1000
+    qI, w, keys = rng.standard_normal((16, 128)), rng.uniform(0, 1, 16), rng.standard_normal((n, 128))
+    cand = np.array([3, 40, 124, 125, -1])      # block 124 holds 992..999, block 125 nothing visible
+    pos, _, sel = O.rescore_select(qI, w, keys, cand, n)
+    want = list(range(24, 32)) + list(range(320, 328)) + list(range(992, 1000))
+    assert pos.tolist() == want and sel.tolist() == want
+
+
 # ---------------------------------------------------------------- attention
 
 def test_worked_attention():
