@@ -10,8 +10,11 @@ Prints one JSON line with queries/s, the indexer kernel's HBM roofline fraction 
 events on the launch stream), the step's fraction of HBM, a prefill chunk's fraction of
 bf16 MFMA peak, and the fp64 CPU oracle timed on a bounded sample.
 
+A second object times a layer that only indexes: it re-scores the 2048 candidate blocks
+the two-stage pass kept (candidate-bounded indexer, selection inside them, attention).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-prefill] [--no-cpu-baseline] [--profile]
+                       [--no-prefill] [--no-rescore] [--no-cpu-baseline] [--profile]
 """
 from __future__ import annotations
 
@@ -36,6 +39,7 @@ LATENT_ROW = 512 * 2
 INDEXER_SOURCES = ("sparse_attention_score_amd/csrc/indexer.hip", "sparse_attention_score_amd/csrc/sa_device.h",
                    "sparse_attention_score_amd/csrc/sa_launch.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_decode-b128-ctx128k-fp8_traffic.json")
+RESCORE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_cand_decode-b128-ctx128k-fp8_traffic.json")
 COPY_BYTES = 1 << 30
 
 
@@ -47,11 +51,11 @@ def indexer_source_hash() -> str:
     return h.hexdigest()
 
 
-def stored_traffic(workload: str):
+def stored_traffic(workload: str, path: str = TRAFFIC_FILE):
     """HBM bytes per indexer launch from the committed rocprofv3 counter summary, or None if
     there is none for this workload or the indexer source changed since it was taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
@@ -102,6 +106,17 @@ def step_bytes(wl) -> float:
              + 64 * 512 * 2 * 2 + IDX_BYTES_PER_QUERY_FIXED + 512 * 4)
     groups = len(wl.compress_groups())
     return float(per_q.sum() + groups * (2 * 2 * 512 * 2 + 512 * 2) + 2 * 512 * 4)
+
+
+def rescore_bytes(wl, carried: np.ndarray) -> float:
+    """Algorithmic bytes of one candidate-bounded indexer launch: the index keys (and fp8
+    row scales) of the visible positions inside every query's carried blocks, the carried
+    block ids, and the index queries and weights."""
+    n = wl.visible().astype(np.int64)[:, None]
+    ids = carried.astype(np.int64)
+    valid = (ids >= 0) & (ids < (n + 7) // 8)
+    rows = np.where(valid, np.minimum(8, n - 8 * ids), 0).sum()
+    return float(rows * key_row_bytes(wl.key_dtype) + wl.T * (IDX_BYTES_PER_QUERY_FIXED + 2048 * 4))
 
 
 def step_flops(wl) -> tuple:
@@ -188,6 +203,64 @@ def run_graph(torch, d, steps):
     return (t1 - t0) / steps, e0.elapsed_time(e1) * 1e-3 / steps
 
 
+def capture(torch, fns):
+    """The launches of `fns` captured once in a HIP graph (first run outside capture)."""
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for f in fns:
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def run_rescore(torch, d, steps, warmup, profile=False):
+    """A layer that only indexes: it re-scores the candidate blocks an earlier layer's
+    candidate stage kept (here the batch's own two-stage pass), selects the top-512 inside
+    them and attends. Eager steps with HIP events on the launch stream around each stage,
+    then the same three launches as graph replays.
+    Returns (carried block ids [T][2048], eager s/layer, graph s/layer or None, stage ms)."""
+    import sparse_attention_score_amd as S
+    d.index()
+    d.select()
+    torch.cuda.synchronize()
+    carried = d.cand.clone()
+    T = d.T
+    sc = torch.empty((T, 2048 * 8), dtype=torch.float32, device="cuda")
+    bm = torch.empty((T, 2048), dtype=torch.float32, device="cuda")
+    tk = torch.empty((T, 512), dtype=torch.int32, device="cuda")
+    fns = [lambda: S.indexer_score_cand(d.plan, d.queries, d.cache, d.qI, d.w, carried, sc, bm),
+           lambda: S.select_topk_cand(d.plan, d.queries, carried, sc, bm, tk),
+           lambda: d.attend(topk=tk)]
+    warm_up(torch, fns, warmup, 0.0 if profile else 0.5)
+    timer = Timer(torch, ["indexer", "select", "attention"])
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        timer.step(fns)
+    torch.cuda.synchronize()
+    eager = (time.perf_counter() - t0) / steps
+    graph = None
+    if not profile:
+        g = capture(torch, fns)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph = (time.perf_counter() - t0) / steps
+        del g
+    return carried.cpu().numpy(), eager, graph, timer.mean_ms()
+
+
 def cpu_baseline(wl, budget_s=20.0, max_queries=None):
     """The fp64 oracle, as it stands, over the first queries of the batch until the time
     budget is spent (at least one query). Returns queries/s and the sample description."""
@@ -224,6 +297,7 @@ def main():
     ap.add_argument("--workload", default="decode-b128-ctx128k-fp8")
     ap.add_argument("--prefill-workload", default="prefill-4096-at-61440")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-rescore", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--profile", action="store_true", help="timed steps only (for rocprofv3)")
@@ -290,6 +364,26 @@ def main():
                  "hbm_frac": sbytes / sec_per_step / HBM_PEAK,
                  "tokens_per_s": wl.T / sec_per_step},
     }
+    if not args.no_rescore:
+        carried, r_eager, r_graph, rms = run_rescore(torch, d, args.steps, args.warmup, args.profile)
+        rb = rescore_bytes(wl, carried)
+        r_s = r_graph or r_eager
+        result["rescore"] = {
+            "what": "layer that re-scores the 2048 candidate blocks carried from the two-stage "
+                    "pass (indexer_score_cand, select_topk_cand, attention)",
+            "ms_per_layer": r_s * 1e3, "queries_per_s": wl.T / r_s,
+            "eager_ms_per_layer": r_eager * 1e3,
+            "timing": "HIP graph replays" if r_graph else "eager launches",
+            "stage_ms": rms,
+            "indexer": {"bound": "hbm", "achieved": rb / (rms["indexer"] * 1e-3) / 1e9,
+                        "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                        "frac": rb / (rms["indexer"] * 1e-3) / HBM_PEAK,
+                        "algorithmic_bytes_per_launch": rb, "avg_launch_ms": rms["indexer"],
+                        "traffic": stored_traffic(args.workload, RESCORE_TRAFFIC_FILE),
+                        "key_bytes_per_query": rb / wl.T,
+                        "full_scan_key_bytes_per_query": idx_bytes / wl.T},
+        }
+        log(f"rescore layer: {r_s * 1e3:.3f} ms, stages {rms}")
     del d
     torch.cuda.empty_cache()
 

@@ -166,6 +166,33 @@ sa_status select_topk(const sa_plan* plan, const sa_queries* queries, const floa
                       int32_t* cand, int32_t* topk, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* Candidate-bounded re-scoring (layers that only index re-score the candidate blocks an
+ * earlier layer's candidate stage kept; the pages' candidate stage selecting 2048 blocks of
+ * 8, "deepseek-ai/DeepSeek-V4.1-Flash" recipe, Overview, two-tier sparse attention bullet).
+ * S1 over the visible positions of the carried blocks only, with this query's own index
+ * heads and weights; one stream of 1 KB (e4m3) or 2 KB (bf16) blocks per query.
+ *   cand       device int32 [T][2048]: carried block ids, ascending, -1 after the last
+ *              (the layout select_topk writes); 16-byte aligned. An entry outside
+ *              [0, ceil(n_t / 8)) is an empty slot (its entries are -inf).
+ *   scores     device fp32 [T][ld_scores] out, slot order: scores[t][8i + r] = I(8 cand[t][i] + r)
+ *              when cand[t][i] >= 0 and that position is visible, -inf otherwise, for
+ *              every i < 2048 (entries past 16384 are not written). ld_scores >= 16384.
+ *   block_max  device fp32 [T][ld_block_max] out: the max of slot i's 8 entries.
+ *              ld_block_max >= 2048. Both strides multiples of 4, at most 2^26.
+ * Other arguments as for indexer_score; T <= 65535. */
+sa_status indexer_score_cand(const sa_plan* plan, const sa_queries* queries, const sa_cache* cache,
+                             const void* q_idx, const float* w, const int32_t* cand, float* scores,
+                             int64_t ld_scores, float* block_max, int64_t ld_block_max, void* stream);
+
+/* S3 inside carried candidates: the min(512, m) best of the m re-scored visible positions by
+ * (score desc, position asc), written ascending to topk[t][0..), -1 after the last. The
+ * 512 best slots by (slot max desc, block id asc) are found first and only their positions
+ * are ranked (they hold the 512 best positions).
+ *   cand, scores, block_max  as passed to / written by indexer_score_cand. */
+sa_status select_topk_cand(const sa_plan* plan, const sa_queries* queries, const int32_t* cand,
+                           const float* scores, int64_t ld_scores, const float* block_max,
+                           int64_t ld_block_max, int32_t* topk, void* stream);
+
 /* S4. Joint-softmax attention over the selected latents and the window.
  *   q      device bf16 [T][64][512]
  *   topk   device int32 [T][512]: positions into the sequence's compressed store;

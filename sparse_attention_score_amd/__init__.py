@@ -23,8 +23,8 @@ SA_KEY_BF16, SA_KEY_FP8_E4M3 = 0, 1
 STATUS_NAMES = {0: "SA_OK", 1: "SA_EINVAL", 2: "SA_EUNSUPPORTED", 3: "SA_EWORKSPACE", 4: "SA_EHIP"}
 
 EXPORTS = ("sparse_attn_plan", "sparse_attn_plan_destroy", "sparse_attn_last_error",
-           "sparse_attn_workspace_init", "indexer_score", "select_topk", "sparse_attn_fwd",
-           "sparse_attn_compress")
+           "sparse_attn_workspace_init", "indexer_score", "select_topk", "indexer_score_cand",
+           "select_topk_cand", "sparse_attn_fwd", "sparse_attn_compress")
 
 
 class sa_params(ctypes.Structure):
@@ -76,6 +76,11 @@ def _load():
     lib.indexer_score.restype = ctypes.c_int
     lib.select_topk.argtypes = [vp, ctypes.POINTER(sa_queries), vp, i64, vp, i64, vp, vp, vp, sz, vp]
     lib.select_topk.restype = ctypes.c_int
+    lib.indexer_score_cand.argtypes = [vp, ctypes.POINTER(sa_queries), ctypes.POINTER(sa_cache), vp, vp,
+                                       vp, vp, i64, vp, i64, vp]
+    lib.indexer_score_cand.restype = ctypes.c_int
+    lib.select_topk_cand.argtypes = [vp, ctypes.POINTER(sa_queries), vp, vp, i64, vp, i64, vp, vp]
+    lib.select_topk_cand.restype = ctypes.c_int
     lib.sparse_attn_fwd.argtypes = [vp, ctypes.POINTER(sa_queries), ctypes.POINTER(sa_cache), vp, vp,
                                     vp, vp, vp, sz, vp]
     lib.sparse_attn_fwd.restype = ctypes.c_int
@@ -207,6 +212,32 @@ def indexer_score(plan: Plan, queries: Queries, cache: Cache, q_idx: torch.Tenso
                              _ptr(q_idx), _ptr(w), _ptr(scores), scores.stride(0),
                              _ptr(block_max), 0 if block_max is None else block_max.stride(0),
                              _stream(stream)))
+
+
+def indexer_score_cand(plan: Plan, queries: Queries, cache: Cache, q_idx: torch.Tensor,
+                       w: torch.Tensor, cand: torch.Tensor, scores: torch.Tensor,
+                       block_max: torch.Tensor, stream=None):
+    """Candidate-bounded re-scoring: scores in slot order of the carried blocks `cand`."""
+    _need(q_idx, "q_idx", torch.bfloat16)
+    _need(w, "w", torch.float32)
+    _need(cand, "cand", torch.int32)
+    _need(scores, "scores", torch.float32)
+    _need(block_max, "block_max", torch.float32)
+    _check(lib.indexer_score_cand(plan.handle, ctypes.byref(queries.c), ctypes.byref(cache.c),
+                                  _ptr(q_idx), _ptr(w), _ptr(cand), _ptr(scores), scores.stride(0),
+                                  _ptr(block_max), block_max.stride(0), _stream(stream)))
+
+
+def select_topk_cand(plan: Plan, queries: Queries, cand: torch.Tensor, scores: torch.Tensor,
+                     block_max: torch.Tensor, topk: torch.Tensor, stream=None):
+    """Top-512 positions inside the carried candidate blocks (after indexer_score_cand)."""
+    _need(cand, "cand", torch.int32)
+    _need(scores, "scores", torch.float32)
+    _need(block_max, "block_max", torch.float32)
+    _need(topk, "topk", torch.int32)
+    _check(lib.select_topk_cand(plan.handle, ctypes.byref(queries.c), _ptr(cand), _ptr(scores),
+                                scores.stride(0), _ptr(block_max), block_max.stride(0), _ptr(topk),
+                                _stream(stream)))
 
 
 def select_topk(plan: Plan, queries: Queries, scores: torch.Tensor,

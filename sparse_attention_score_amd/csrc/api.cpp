@@ -222,12 +222,86 @@ sa_status indexer_score(const sa_plan* plan, const sa_queries* q, const sa_cache
   a.block_max = block_max;
   a.ld_block_max = ld_block_max;
   a.E = E;
+  a.cand = nullptr;
   // Queries that share a sequence in one call (a prefill chunk) reuse each key tile
   // across many queries; independent decode queries each stream their own keys.
   const bool prefill = c->num_seqs == 1 && q->T > 1;
   SA_REQUIRE(prefill || q->T <= 65535, SA_EUNSUPPORTED,
              "T = %lld queries over several sequences: at most 65535 per call", (long long)q->T);
   return hip_status(sa::launch_indexer(a, prefill, (hipStream_t)stream), "indexer_score launch");
+}
+
+sa_status indexer_score_cand(const sa_plan* plan, const sa_queries* q, const sa_cache* c,
+                             const void* q_idx, const float* w, const int32_t* cand, float* scores,
+                             int64_t ld_scores, float* block_max, int64_t ld_block_max, void* stream) {
+  sa_status st;
+  if ((st = check_plan(plan)) != SA_OK) return st;
+  if ((st = check_queries(plan, q)) != SA_OK) return st;
+  if ((st = check_cache(plan, q, c, true, false)) != SA_OK) return st;
+  SA_REQUIRE(q_idx && aligned16(q_idx) && w && aligned16(w), SA_EINVAL,
+             "q_idx / w NULL or not 16-byte aligned");
+  SA_REQUIRE(cand && aligned16(cand), SA_EINVAL, "cand NULL or not 16-byte aligned");
+  SA_REQUIRE(scores && aligned16(scores), SA_EINVAL, "scores NULL or not 16-byte aligned");
+  SA_REQUIRE(block_max && aligned16(block_max), SA_EINVAL, "block_max NULL or not 16-byte aligned");
+  constexpr int64_t E = 2048LL * 8;
+  SA_REQUIRE(ld_scores >= E && ld_scores % 4 == 0 && ld_scores <= kMaxLd, SA_EINVAL,
+             "ld_scores = %lld must be >= %lld, <= %lld and a multiple of 4", (long long)ld_scores,
+             (long long)E, (long long)kMaxLd);
+  SA_REQUIRE(ld_block_max >= 2048 && ld_block_max % 4 == 0 && ld_block_max <= kMaxLd, SA_EINVAL,
+             "ld_block_max = %lld must be >= 2048, <= %lld and a multiple of 4", (long long)ld_block_max,
+             (long long)kMaxLd);
+  SA_REQUIRE(q->T <= 65535, SA_EUNSUPPORTED, "T = %lld: at most 65535 queries per call", (long long)q->T);
+  sa::IndexerArgs a;
+  a.seq_id = q->seq_id;
+  a.pos = q->pos;
+  a.T = q->T;
+  a.max_visible = q->max_visible;
+  a.num_seqs = c->num_seqs;
+  a.compressed_cap = c->compressed_cap;
+  a.ratio = plan->p.ratio;
+  a.fp8 = plan->p.idx_key_dtype == SA_KEY_FP8_E4M3;
+  a.q_idx = q_idx;
+  a.w = w;
+  a.keys = c->idx_keys;
+  a.keys_seq_stride = c->idx_keys_seq_stride;
+  a.scales = c->idx_scales;
+  a.scales_seq_stride = c->idx_scales_seq_stride;
+  a.scores = scores;
+  a.ld_scores = ld_scores;
+  a.block_max = block_max;
+  a.ld_block_max = ld_block_max;
+  a.E = E;
+  a.cand = cand;
+  return hip_status(sa::launch_indexer(a, false, (hipStream_t)stream), "indexer_score_cand launch");
+}
+
+sa_status select_topk_cand(const sa_plan* plan, const sa_queries* q, const int32_t* cand,
+                           const float* scores, int64_t ld_scores, const float* block_max,
+                           int64_t ld_block_max, int32_t* topk, void* stream) {
+  sa_status st;
+  if ((st = check_plan(plan)) != SA_OK) return st;
+  if ((st = check_queries(plan, q)) != SA_OK) return st;
+  SA_REQUIRE(cand && aligned16(cand), SA_EINVAL, "cand NULL or not 16-byte aligned");
+  SA_REQUIRE(scores && aligned16(scores), SA_EINVAL, "scores NULL or not 16-byte aligned");
+  SA_REQUIRE(block_max && aligned16(block_max), SA_EINVAL, "block_max NULL or not 16-byte aligned");
+  SA_REQUIRE(topk && aligned16(topk), SA_EINVAL, "topk NULL or not 16-byte aligned");
+  SA_REQUIRE(ld_scores >= 2048LL * 8 && ld_scores % 4 == 0 && ld_scores <= kMaxLd, SA_EINVAL,
+             "ld_scores = %lld must be >= 16384, <= %lld and a multiple of 4", (long long)ld_scores,
+             (long long)kMaxLd);
+  SA_REQUIRE(ld_block_max >= 2048 && ld_block_max % 4 == 0 && ld_block_max <= kMaxLd, SA_EINVAL,
+             "ld_block_max = %lld must be >= 2048, <= %lld and a multiple of 4", (long long)ld_block_max,
+             (long long)kMaxLd);
+  sa::SelectArgs a;
+  a.m = meta(plan, q, INT32_MAX, q->max_visible);
+  a.scores = scores;
+  a.ld_scores = ld_scores;
+  a.block_max = block_max;
+  a.ld_block_max = ld_block_max;
+  a.cand = const_cast<int32_t*>(cand);   // read only in this mode
+  a.topk = topk;
+  a.part_ids = nullptr;
+  a.parts = 1;
+  return hip_status(sa::launch_select_cand(a, (hipStream_t)stream), "select_topk_cand launch");
 }
 
 sa_status select_topk(const sa_plan* plan, const sa_queries* q, const float* scores,

@@ -80,6 +80,7 @@ struct DecodeShared {
   float stage[kDWaves][kTilesPerWave * 16];   // unscaled scores of the wave's keys
   uint16_t q[kIdxHeads * kIdxDim];
   float w[kIdxHeads];
+  int32_t ids[kDWaves * kTilesPerWave * 2];   // candidate mode: the group's block ids
 };
 
 // Dims of k-step s (0..3) held by lane group g, in elements. bf16 keys: chunk 4s+g of
@@ -128,7 +129,10 @@ __device__ __forceinline__ void to_lds16_after_reads(const void* src, uint32_t l
 }
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <bool FP8>
+// CAND: candidate-bounded re-scoring. The score row is in slot order: entry 8i + r belongs
+// to position 8 cand[i] + r of the query's carried candidate blocks (ascending, -1 padded),
+// and a tile of 16 entries is two candidate blocks; the loads gather those blocks' rows.
+template <bool FP8, bool CAND>
 __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a) {
   using DT = DecodeTile<FP8>;
   constexpr int RB = DT::RB, TB = DT::TB, NK = DT::NK, D = DT::D;
@@ -143,9 +147,11 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
   const int key0 = chunk0 + wave * kTilesPerWave * 16;   // the keys this wave stores
   const int n = query_n(a, t);
   const int ntiles = key0 < E ? min(kTilesPerWave, (E - key0 + 15) >> 4) : 0;
-  // tiles of the group's chunk below n, and this wave's share of them
-  const int chunk_live = chunk0 < n ? min(kDWaves * kTilesPerWave, (n - chunk0 + 15) >> 4) : 0;
-  const int live = min(max(chunk_live - wave * kTilesPerWave, 0), kTilesPerWave);
+  // tiles of the group's chunk below n, and this wave's share of them (candidate mode:
+  // decided once the block ids are in)
+  const int chunk_live = CAND ? (n > 0 ? 1 : 0)
+                              : (chunk0 < n ? min(kDWaves * kTilesPerWave, (n - chunk0 + 15) >> 4) : 0);
+  int live = CAND ? 0 : min(max(chunk_live - wave * kTilesPerWave, 0), kTilesPerWave);
   auto tile_of = [&](int i) { return wave * kTilesPerWave + i; };
   const bool wg_live = chunk_live > 0;
 
@@ -157,7 +163,7 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
   // e4m3 row scales of the keys this lane stores at the end (issued first: the loads
   // complete in order, so the row waits below also cover them)
   float scv[kTilesPerWave / 4] = {};
-  if (FP8 && key0 < n) {   // (a query without keys may have no valid sequence)
+  if (FP8 && !CAND && key0 < n) {   // (a query without keys may have no valid sequence)
     const float* scales = a.scales + (int64_t)seq * a.scales_seq_stride;
 #pragma unroll
     for (int j = 0; j < kTilesPerWave / 4; ++j) scv[j] = scales[min(key0 + 64 * j + lane, n - 1)];
@@ -170,6 +176,32 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
     const uint8_t* qb = reinterpret_cast<const uint8_t*>(a.q_idx) + (int64_t)t * kIdxHeads * kIdxDim * 2;
     to_lds16(qb + 1024 * wave + 16 * lane, lds_q + 1024 * wave);
     if (wave == 0 && lane < kIdxHeads / 4) to_lds16(a.w + (int64_t)t * kIdxHeads + 4 * lane, lds_w);
+    if (CAND && wave == 1 && lane < kDWaves * kTilesPerWave * 2 / 4)   // the group's block ids
+      to_lds16(a.cand + (int64_t)t * kCandBlocks + chunk0 / 8 + 4 * lane, (uint32_t)(uintptr_t)&sh.ids[0]);
+  }
+  // candidate mode: block id of the wave's slot `lane` (lane reads pick one per load). A
+  // slot is valid when its block holds a visible position (0 <= id < ceil(n / 8), compared
+  // without forming 8 id); the wave loads tiles up to its last valid slot, and invalid
+  // slots among them read row n - 1 and are masked.
+  static_assert(2 * kTilesPerWave <= 64, "one slot per lane");
+  constexpr int kSlots = 2 * kTilesPerWave;   // candidate blocks per wave
+  const int nbv = (n + 7) >> 3;
+  auto valid_id = [&](int id) { return id >= 0 && id < nbv; };
+  int idreg = -1;
+  if constexpr (CAND) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    asm volatile("s_barrier" ::: "memory");
+    if (wg_live && lane < kSlots) idreg = sh.ids[kSlots * wave + lane];
+    const uint64_t vm = __ballot(valid_id(idreg));
+    live = vm ? (64 - __builtin_clzll(vm) + 1) >> 1 : 0;
+    if (FP8 && live > 0) {
+      const float* scales = a.scales + (int64_t)seq * a.scales_seq_stride;
+#pragma unroll
+      for (int j = 0; j < kTilesPerWave / 4; ++j) {
+        const int id = sh.ids[kSlots * wave + 8 * j + (lane >> 3)];
+        scv[j] = valid_id(id) ? scales[min(8 * id + (lane & 7), n - 1)] : 0.f;
+      }
+    }
   }
 
   // load j of a tile: lane -> row rr[j], chunk qq[j]; its 16 bytes land at position
@@ -190,7 +222,16 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
     const uint32_t lds = ring0 + (uint32_t)((i & (D - 1)) * TB);
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
-      const uint8_t* src = tb + (min(rr[j], last) * RB + qq[j] * 16);
+      const uint8_t* src;
+      if constexpr (CAND) {
+        // load j covers rows of one slot: 2i + j (e4m3) or 2i + j/2 (bf16); slots past the
+        // valid ones read row n - 1 (masked)
+        const int id = __builtin_amdgcn_readlane(idreg, 2 * i + (j * (64 / DT::CPR)) / 8);
+        const int row = valid_id(id) ? min(8 * id + (rr[j] & 7), n - 1) : n - 1;
+        src = keys + (int64_t)row * RB + qq[j] * 16;
+      } else {
+        src = tb + (min(rr[j], last) * RB + qq[j] * 16);
+      }
       if (j == 0 && after_reads) to_lds16_after_reads(src, lds + 1024 * j);
       else to_lds16(src, lds + 1024 * j);
     }
@@ -198,11 +239,13 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
 #pragma unroll
   for (int u = 0; u < D; ++u)
     if (u < live) issue(u, false);
-  if (live >= D) __builtin_amdgcn_s_waitcnt(waitcnt_vm(D * NK));   // query, weights, scales
-  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  // every wave's part of the query is in LDS (its loads completed above); a bare barrier,
-  // since a fence here would also wait for the row loads in flight
-  asm volatile("s_barrier" ::: "memory");
+  if constexpr (!CAND) {
+    if (live >= D) __builtin_amdgcn_s_waitcnt(waitcnt_vm(D * NK));   // query, weights, scales
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    // every wave's part of the query is in LDS (its loads completed above); a bare barrier,
+    // since a fence here would also wait for the row loads in flight
+    asm volatile("s_barrier" ::: "memory");
+  }
 
   if (live > 0) {
     bf16x8 qa[4];
@@ -245,7 +288,12 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
     const int k = key0 + 64 * j + lane;
     if (64 * j >= 16 * ntiles) break;
     float v = neg_inf();
-    if (k < n) {
+    bool ok = k < n;
+    if constexpr (CAND) {
+      const int id = wg_live ? sh.ids[kSlots * wave + 8 * j + (lane >> 3)] : -1;
+      ok = valid_id(id) && 8 * id + (lane & 7) < n;
+    }
+    if (ok) {
       v = stage[64 * j + lane];
       if constexpr (FP8) v *= scv[j];
     }
@@ -520,10 +568,16 @@ __global__ __launch_bounds__(kPThreads, 2) void indexer_prefill_kernel(IndexerAr
 hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream) {
   if (!prefill) {
     dim3 grid((unsigned)((a.E + kKeysPerWG - 1) / kKeysPerWG), (unsigned)a.T);
-    if (a.fp8)
-      hipLaunchKernelGGL(indexer_decode_kernel<true>, grid, dim3(kDThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL(indexer_decode_kernel<false>, grid, dim3(kDThreads), 0, stream, a);
+    if (a.cand) {
+      if (a.fp8)
+        hipLaunchKernelGGL((indexer_decode_kernel<true, true>), grid, dim3(kDThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL((indexer_decode_kernel<false, true>), grid, dim3(kDThreads), 0, stream, a);
+    } else if (a.fp8) {
+      hipLaunchKernelGGL((indexer_decode_kernel<true, false>), grid, dim3(kDThreads), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((indexer_decode_kernel<false, false>), grid, dim3(kDThreads), 0, stream, a);
+    }
   } else {
     // blockIdx.x (key chunk) varies fastest, so with a multiple of 8 chunks every XCD
     // keeps the same chunks and their keys stay in its L2.

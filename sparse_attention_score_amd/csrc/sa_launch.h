@@ -35,7 +35,8 @@ struct IndexerArgs {
   int64_t ld_scores;
   float* block_max;         // [T][ld_block_max] or null
   int64_t ld_block_max;
-  int64_t E;                // score row extent: max_visible rounded up to 8
+  int64_t E;                // score row extent: max_visible rounded up to 8 (candidate mode: 8 * 2048)
+  const int32_t* cand;      // candidate mode: [T][2048] carried block ids, else null
 };
 hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream);
 
@@ -55,6 +56,9 @@ struct SelectArgs {
 // Parts of the candidate stage for queries of up to max_visible positions (1: one level).
 int select_parts(int64_t max_visible);
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
+// Candidate mode: top-512 positions inside carried candidate blocks (a.cand is the input,
+// scores / block_max in slot order as the candidate-mode indexer writes them).
+hipError_t launch_select_cand(const SelectArgs& a, hipStream_t stream);
 
 struct AttnArgs {
   QueryMeta m;

@@ -618,6 +618,96 @@ __global__ __launch_bounds__(NT) void select_merge_kernel(SelectArgs a) {
   select_core<NT>(a, t, n, core, sh);
 }
 
+// Candidate mode: the top-512 positions inside a query's carried candidate blocks. Slot i
+// is block cand[i] (ascending, -1 padded); the re-scored entries are in slot order (entry
+// 8i + r is position 8 cand[i] + r) with slot maxima in block_max. The 512 best slots by
+// (slot max desc, block id asc) hold the 512 best positions (the candidate-stage lemma),
+// so, as in select_kernel, the final selection reads only those slots. Slot ids ascend
+// with block ids and positions, so ties between slots and between positions resolve as
+// in the two-stage path; the ids passed to the selection are the positions themselves.
+template <int NT>
+__global__ __launch_bounds__(NT) void select_cand_kernel(SelectArgs a) {
+  static_assert(NT == 512, "4 slots and one core slot per thread");
+  constexpr int ES = kCandBlocks / NT;   // slots per thread
+  __shared__ SelShared sh;
+  __shared__ __attribute__((aligned(16))) int32_t core[kTopK];
+  __shared__ int32_t cids[kCandBlocks];  // block id of every valid slot, else -1
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int64_t n = visible_n(a.m, t);
+  const int32_t* crow = a.cand + (int64_t)t * kCandBlocks;
+  int32_t* out = a.topk + (int64_t)t * kTopK;
+  const float* row = a.scores + (int64_t)t * a.ld_scores;
+  const float* bm = a.block_max + (int64_t)t * a.ld_block_max;
+
+  // slots tid*ES .. +ES-1; a slot is valid when its block holds a visible position
+  uint32_t key[ES];
+  ListIds<ES> I;
+  int nv_mine = 0;
+  {
+    const int4 b4 = *reinterpret_cast<const int4*>(crow + tid * ES);
+    const f32x4 m4 = *reinterpret_cast<const f32x4*>(bm + tid * ES);
+    const int b[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+    for (int e = 0; e < ES; ++e) {
+      const bool v = b[e] >= 0 && (int64_t)b[e] * kBlock < n;
+      cids[tid * ES + e] = v ? b[e] : -1;
+      I.valid[e] = v;
+      I.ids[e] = tid * ES + e;
+      key[e] = v ? order_key(m4[e]) : 0u;
+      nv_mine += v ? 1 : 0;
+    }
+  }
+  int nvs;
+  const int vbefore = wg_inclusive_scan<NT>(nv_mine, sh, nvs) - nv_mine;
+  if (nvs <= kTopK) {   // every valid slot, in slot order
+    int o = vbefore;
+#pragma unroll
+    for (int e = 0; e < ES; ++e)
+      if (I.valid[e]) core[o++] = I.ids[e];
+    for (int i = nvs + tid; i < kTopK; i += NT) core[i] = -1;
+  } else {
+    const int ks[1] = {kTopK};
+    int32_t* const outs[1] = {core};
+    multi_select<NT, ES, 1>(key, I, ks, outs, sh);
+  }
+  __syncthreads();
+
+  // positions of core slot `tid`: 8 entries, ids = positions
+  uint32_t pkey[kBlock];
+  ListIds<kBlock> P;
+  int np_mine = 0;
+  {
+    const int cs = core[tid];
+    const int b = cs >= 0 ? cids[cs] : -1;
+    f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
+    if (b >= 0) {
+      v0 = *reinterpret_cast<const f32x4*>(row + (int64_t)cs * kBlock);
+      v1 = *reinterpret_cast<const f32x4*>(row + (int64_t)cs * kBlock + 4);
+    }
+#pragma unroll
+    for (int r = 0; r < kBlock; ++r) {
+      const int64_t p = (int64_t)b * kBlock + r;
+      P.valid[r] = b >= 0 && p < n;
+      P.ids[r] = (int32_t)p;
+      pkey[r] = order_key(r < 4 ? v0[r] : v1[r - 4]);
+      np_mine += P.valid[r] ? 1 : 0;
+    }
+  }
+  int np;
+  const int before = wg_inclusive_scan<NT>(np_mine, sh, np) - np_mine;
+  if (np <= kTopK) {   // every candidate position is selected, in slot (= position) order
+    int o = before;
+#pragma unroll
+    for (int r = 0; r < kBlock; ++r)
+      if (P.valid[r]) out[o++] = P.ids[r];
+    for (int i = np + tid; i < kTopK; i += NT) out[i] = -1;
+    return;
+  }
+  const int ks[1] = {kTopK};
+  int32_t* const outs[1] = {out};
+  multi_select<NT, kBlock, 1>(pkey, P, ks, outs, sh);
+}
+
 template <int NT>
 hipError_t launch_select_nt(const SelectArgs& a, hipStream_t stream) {
   const int64_t nbmax = (a.m.max_visible + kBlock - 1) / kBlock;
@@ -650,6 +740,11 @@ hipError_t launch_select_nt(const SelectArgs& a, hipStream_t stream) {
 int select_parts(int64_t max_visible) {
   const int64_t nb = (max_visible + kBlock - 1) / kBlock;
   return nb <= kPartBlocks ? 1 : (int)((nb + kPartBlocks - 1) / kPartBlocks);
+}
+
+hipError_t launch_select_cand(const SelectArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(select_cand_kernel<512>, dim3((unsigned)a.m.T), dim3(512), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
