@@ -122,8 +122,6 @@ def _need(t: torch.Tensor, name: str, dtype, cuda: bool = True):
 class Plan:
     """sparse_attn_plan: fixed layer shape, ratio, key dtype and maximum sizes."""
 
-    _destroy = lib.sparse_attn_plan_destroy
-
     def __init__(self, ratio: int, key_dtype: str = "bf16", max_queries: int = 1,
                  max_compressed: int = 0, softmax_scale: float = 1.0 / math.sqrt(512.0),
                  **dims):
@@ -144,10 +142,12 @@ class Plan:
         self.key_dtype = key_dtype
         self.ratio = ratio
 
-    def __del__(self):
+    def __del__(self, _destroy=lib.sparse_attn_plan_destroy):
+        # the default argument keeps the function reachable at interpreter exit, when the
+        # module's globals may already be cleared
         h = getattr(self, "handle", None)
         if h is not None and h.value:
-            Plan._destroy(h)
+            _destroy(h)
             self.handle = None
 
 
