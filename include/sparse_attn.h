@@ -93,6 +93,13 @@ typedef struct sa_queries {
   const int32_t* pos;      /* device [T]: raw position p of query t */
   int64_t max_visible;     /* host: >= (pos[t]+1)/ratio for every t, <= plan max_compressed.
                               Sizes the grids and the score rows. */
+  int32_t group;           /* host, 0..8. 0 or 1: no grouping. G > 1: queries
+                              gG .. gG+G-1 (the last group may be shorter) read one
+                              sequence, as the tokens of a multi-token decode step do (a
+                              verified token and the drafted tokens after it); indexer_score
+                              then streams each group's keys once for all its queries. A
+                              query whose seq_id differs from its group's first query gets
+                              -inf scores. Ignored by the other calls. */
 } sa_queries;
 
 /* Per-sequence stores, all device memory. */

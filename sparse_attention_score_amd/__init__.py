@@ -39,7 +39,7 @@ class sa_params(ctypes.Structure):
 
 class sa_queries(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("seq_id", ctypes.c_void_p), ("pos", ctypes.c_void_p),
-                ("max_visible", ctypes.c_int64)]
+                ("max_visible", ctypes.c_int64), ("group", ctypes.c_int32)]
 
 
 class sa_cache(ctypes.Structure):
@@ -156,14 +156,15 @@ def sparse_attn_plan(**kw) -> Plan:
 
 
 class Queries:
-    """sa_queries from device int32 tensors seq_id[T], pos[T] and a host max_visible."""
+    """sa_queries from device int32 tensors seq_id[T], pos[T], a host max_visible and the
+    number of consecutive queries that share a sequence (group; 0 = none)."""
 
-    def __init__(self, seq_id: torch.Tensor, pos: torch.Tensor, max_visible: int):
+    def __init__(self, seq_id: torch.Tensor, pos: torch.Tensor, max_visible: int, group: int = 0):
         _need(seq_id, "seq_id", torch.int32)
         _need(pos, "pos", torch.int32)
         self._keep = (seq_id, pos)
         self.c = sa_queries(T=seq_id.shape[0], seq_id=seq_id.data_ptr(), pos=pos.data_ptr(),
-                            max_visible=int(max_visible))
+                            max_visible=int(max_visible), group=int(group))
 
     @property
     def T(self) -> int:

@@ -37,6 +37,7 @@ sa_status ok() {
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
 constexpr int64_t kMaxVisible = 2048LL * 8 * 32;  // 524288: largest block set a select WG holds
+constexpr int kMaxGroup = 8;                        // queries per group sharing one key stream
 constexpr int64_t kMaxLd = 1LL << 26;              // row strides of scores / block maxima: two rows
                                                    // stay addressable by 32-bit buffer offsets
 
@@ -92,6 +93,8 @@ sa_status check_queries(const sa_plan* plan, const sa_queries* q) {
   SA_REQUIRE(q->max_visible >= 0 && q->max_visible <= plan->p.max_compressed, SA_EINVAL,
              "queries->max_visible = %lld outside [0, max_compressed = %lld]",
              (long long)q->max_visible, (long long)plan->p.max_compressed);
+  SA_REQUIRE(q->group >= 0 && q->group <= kMaxGroup, SA_EUNSUPPORTED,
+             "queries->group = %d outside [0, %d]", (int)q->group, kMaxGroup);
   return SA_OK;
 }
 
@@ -223,11 +226,14 @@ sa_status indexer_score(const sa_plan* plan, const sa_queries* q, const sa_cache
   a.ld_block_max = ld_block_max;
   a.E = E;
   a.cand = nullptr;
+  a.group = q->group > 1 ? q->group : 1;
   // Queries that share a sequence in one call (a prefill chunk) reuse each key tile
-  // across many queries; independent decode queries each stream their own keys.
-  const bool prefill = c->num_seqs == 1 && q->T > 1;
-  SA_REQUIRE(prefill || q->T <= 65535, SA_EUNSUPPORTED,
-             "T = %lld queries over several sequences: at most 65535 per call", (long long)q->T);
+  // across many queries; groups of a multi-token decode step share one key stream per
+  // group; independent decode queries each stream their own keys.
+  const bool prefill = a.group == 1 && c->num_seqs == 1 && q->T > 1;
+  SA_REQUIRE(prefill || (q->T + a.group - 1) / a.group <= 65535, SA_EUNSUPPORTED,
+             "T = %lld queries in groups of %d over several sequences: at most 65535 groups per call",
+             (long long)q->T, (int)a.group);
   return hip_status(sa::launch_indexer(a, prefill, (hipStream_t)stream), "indexer_score launch");
 }
 
@@ -272,6 +278,7 @@ sa_status indexer_score_cand(const sa_plan* plan, const sa_queries* q, const sa_
   a.ld_block_max = ld_block_max;
   a.E = E;
   a.cand = cand;
+  a.group = 1;
   return hip_status(sa::launch_indexer(a, false, (hipStream_t)stream), "indexer_score_cand launch");
 }
 

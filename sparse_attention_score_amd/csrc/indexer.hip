@@ -306,6 +306,201 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
 }
 
 // ======================================================================================
+// Grouped decode
+// ======================================================================================
+// Up to G consecutive queries that read one sequence (a multi-token decode step: a
+// verified token and the drafted tokens after it) share one key stream. Same LDS ring and
+// direct loads as the decode kernel, with every query's 16 heads in registers, so each
+// 16-key tile feeds 4G MFMAs. The arithmetic of each query (MFMA k order, ReLU and head
+// weights in-lane, the 16-head sum as (row 0 + row 1) + (row 2 + row 3)) is the decode
+// kernel's, so a query's scores are the same bits whichever kernel runs it. The head sums
+// of four queries finish together: a row-swap add within each pair of queries, then a
+// half-swap add that leaves query j's totals in row j, so one store instruction writes the
+// tile's 16 keys of four queries. Scores stay in registers until the wave's tiles are done:
+// no store may sit between the ring loads and their explicit vmcnt waits.
+constexpr int kGTilesPerWave = 16;
+constexpr int kGKeysPerWG = kDWaves * kGTilesPerWave * 16;
+
+template <bool FP8, int G>
+__global__ __launch_bounds__(kDThreads, 2) void indexer_group_kernel(IndexerArgs a) {
+  using DT = DecodeTile<FP8>;
+  constexpr int RB = DT::RB, TB = DT::TB, NK = DT::NK, D = DT::D;
+  constexpr int TPW = kGTilesPerWave;
+  constexpr int N4 = G / 4, N2 = (G % 4) / 2;   // four-query chunks, then one pair
+  static_assert(G >= 2 && G <= 8 && G % 2 == 0, "groups of 2, 4, 6 or 8 queries");
+  static_assert((D & (D - 1)) == 0 && D >= 2 && D <= TPW, "ring depth");
+  static_assert(D * NK <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[kDWaves][kRingBytes];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int c = lane & 15, g = lane >> 4;
+  const int E = (int)a.E, T = (int)a.T;
+  const int t0 = blockIdx.y * a.group;
+  const int gs = min(a.group, T - t0);   // queries of this group (a.group <= G)
+  const int key0 = blockIdx.x * kGKeysPerWG + wave * TPW * 16;   // the wave's keys
+  const int seq = a.seq_id[t0];
+
+  // visible count of the group's j-th query; 0 past the group or for another sequence
+  auto n_of = [&](int j) { return j < gs && a.seq_id[t0 + j] == seq ? query_n(a, t0 + j) : 0; };
+  int nmax = 0;
+  for (int j = 0; j < gs; ++j) nmax = max(nmax, n_of(j));
+  const int ntiles = key0 < E ? min(TPW, (E - key0 + 15) >> 4) : 0;
+  const int live = key0 < nmax ? min(TPW, (nmax - key0 + 15) >> 4) : 0;
+  const int sq = nmax > 0 ? seq : 0;   // nmax > 0 implies a valid sequence
+  const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys) + (int64_t)sq * a.keys_seq_stride * (FP8 ? 1 : 2);
+
+  // Head weights, e4m3 row scales (4 consecutive keys per lane) and the A operands, in this
+  // order, before the first ring loads: the compiler waits for the A operands at the first
+  // MFMA, which then also covers the first D tiles (loads complete in order).
+  float wq[G][4];
+  float sv[4] = {1.f, 1.f, 1.f, 1.f};
+  bf16x8 qa[G][4];
+  if (live > 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int tq = t0 + min(j, gs - 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wq[j][i] = a.w[(int64_t)tq * kIdxHeads + 4 * g + i];
+    }
+    if constexpr (FP8) {
+      const float* scales = a.scales + (int64_t)sq * a.scales_seq_stride;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sv[e] = scales[min(key0 + 4 * lane + e, nmax - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int tq = t0 + min(j, gs - 1);
+      const uint16_t* row = reinterpret_cast<const uint16_t*>(a.q_idx) + ((int64_t)tq * kIdxHeads + c) * kIdxDim;
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2)
+        qa[j][s2] = *reinterpret_cast<const bf16x8*>(row + (FP8 ? kdim_fp8(g, s2) : kdim_bf16(g, s2)));
+    }
+  }
+
+  int rr[NK], qq[NK];
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    const int r = j * (64 / DT::CPR) + lane / DT::CPR;
+    rr[j] = r;
+    qq[j] = DT::pos(r, lane % DT::CPR);
+  }
+  const uint32_t ring0 = (uint32_t)(uintptr_t)&ring[wave][0];
+  auto issue = [&](int i, bool after_reads) {
+    const int k = key0 + 16 * i;
+    const uint8_t* tb = keys + (int64_t)k * RB;
+    const int last = nmax - 1 - k;   // rows past the group's last key repeat that row
+    const uint32_t lds = ring0 + (uint32_t)((i & (D - 1)) * TB);
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const uint8_t* src = tb + (min(rr[j], last) * RB + qq[j] * 16);
+      if (j == 0 && after_reads) to_lds16_after_reads(src, lds + 1024 * j);
+      else to_lds16(src, lds + 1024 * j);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+    if (u < live) issue(u, false);
+
+  uint32_t roff[NK];
+#pragma unroll
+  for (int i = 0; i < NK; ++i) {
+    const int q = FP8 ? g + 4 * i : 4 * i + g;
+    roff[i] = (uint32_t)(c * RB + DT::pos(c, q) * 16);
+  }
+  float r4[TPW][N4 > 0 ? N4 : 1];   // tile i, chunk h: query 4h + g's score of key c
+  float r2[TPW];                    // tile i, pair: query 4 N4 + (g & 1)'s score of key c
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    if (i < live) {
+      if (i + D - 1 < live) __builtin_amdgcn_s_waitcnt(waitcnt_vm((D - 1) * NK));   // tile i landed
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      const uint8_t* tile = ring[wave] + (i & (D - 1)) * TB;
+      KeyRegs<FP8> K;
+#pragma unroll
+      for (int j = 0; j < NK; ++j) K.v[j] = *reinterpret_cast<const u32x4*>(tile + roff[j]);
+      if (i + D < live) issue(i + D, true);
+      bf16x8 b[4];
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        if constexpr (FP8) b[s2] = e4m3x8_to_bf16x8(K.v[s2 >> 1][2 * (s2 & 1)], K.v[s2 >> 1][2 * (s2 & 1) + 1]);
+        else b[s2] = __builtin_bit_cast(bf16x8, K.v[s2]);
+      }
+      float p[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j][s2], b[s2], acc, 0, 0, 0);
+        float v = wq[j][0] * relu(acc[0]);
+        v = fmaf(wq[j][1], relu(acc[1]), v);
+        v = fmaf(wq[j][2], relu(acc[2]), v);
+        p[j] = fmaf(wq[j][3], relu(acc[3]), v);
+      }
+      // row-swap adds: rows (0+1) and (2+3) of two queries side by side
+      auto sw16 = [](float x, float y) {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      };
+#pragma unroll
+      for (int h = 0; h < N4; ++h) {
+        const float ab = sw16(p[4 * h], p[4 * h + 1]);       // rows: a01 b01 a23 b23
+        const float cd = sw16(p[4 * h + 2], p[4 * h + 3]);   // rows: c01 d01 c23 d23
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ab), __float_as_uint(cd), false, false);
+        r4[i][h] = __uint_as_float(r[0]) + __uint_as_float(r[1]);   // row j: query 4h + j
+      }
+      if constexpr (N2 > 0) r2[i] = add_xor32(sw16(p[4 * N4], p[4 * N4 + 1]));   // rows 0, 2: e; 1, 3: f
+    }
+  }
+
+  // ---- scores and block maxima: per tile, 16 keys of four queries per store ----
+  float* sc_l = reinterpret_cast<float*>(&ring[wave][0]);   // the ring is idle now
+  if constexpr (FP8) {
+    if (live > 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc_l[4 * lane + e] = sv[e];
+    }
+  }
+  int jq4[N4 > 0 ? N4 : 1], nl4[N4 > 0 ? N4 : 1];
+#pragma unroll
+  for (int h = 0; h < N4; ++h) {
+    jq4[h] = 4 * h + g;
+    nl4[h] = n_of(jq4[h]);
+  }
+  const int jq2 = 4 * N4 + (g & 1);
+  const int nl2 = N2 > 0 ? n_of(jq2) : 0;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    if (i >= ntiles) break;
+    const int k = key0 + 16 * i + c;
+    const float sc = FP8 && i < live ? sc_l[16 * i + c] : 1.f;
+    auto put = [&](float v, int jq, bool mine) {
+      const float m = max8_lanes(v);   // E is a multiple of 8: groups are all in or all out
+      if (mine && jq < gs && k < E) {
+        const int64_t tq = t0 + jq;
+        a.scores[tq * a.ld_scores + k] = v;
+        if (a.block_max && (c & 7) == 0) a.block_max[tq * a.ld_block_max + (k >> 3)] = m;
+      }
+    };
+#pragma unroll
+    for (int h = 0; h < N4; ++h) {
+      float v = neg_inf();
+      if (i < live && k < nl4[h]) {
+        v = r4[i][h];
+        if constexpr (FP8) v *= sc;
+      }
+      put(v, jq4[h], true);
+    }
+    if constexpr (N2 > 0) {
+      float v = neg_inf();
+      if (i < live && k < nl2) {
+        v = r2[i];
+        if constexpr (FP8) v *= sc;
+      }
+      put(v, jq2, g < 2);
+    }
+  }
+}
+
+// ======================================================================================
 // Prefill
 // ======================================================================================
 constexpr int kPWaves = 4;
@@ -563,10 +758,25 @@ __global__ __launch_bounds__(kPThreads, 2) void indexer_prefill_kernel(IndexerAr
   epilogue(1, acc1, kprev, scprev);
 }
 
+template <int G>
+void launch_group(const IndexerArgs& a, hipStream_t stream) {
+  dim3 grid((unsigned)((a.E + kGKeysPerWG - 1) / kGKeysPerWG), (unsigned)((a.T + a.group - 1) / a.group));
+  if (a.fp8)
+    hipLaunchKernelGGL((indexer_group_kernel<true, G>), grid, dim3(kDThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((indexer_group_kernel<false, G>), grid, dim3(kDThreads), 0, stream, a);
+}
+
 }  // namespace
 
 hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream) {
-  if (!prefill) {
+  if (a.group > 1 && !a.cand) {
+    // the smallest even group size that holds a.group (extra queries are masked)
+    if (a.group <= 2) launch_group<2>(a, stream);
+    else if (a.group <= 4) launch_group<4>(a, stream);
+    else if (a.group <= 6) launch_group<6>(a, stream);
+    else launch_group<8>(a, stream);
+  } else if (!prefill) {
     dim3 grid((unsigned)((a.E + kKeysPerWG - 1) / kKeysPerWG), (unsigned)a.T);
     if (a.cand) {
       if (a.fp8)

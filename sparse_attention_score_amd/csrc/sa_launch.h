@@ -37,6 +37,7 @@ struct IndexerArgs {
   int64_t ld_block_max;
   int64_t E;                // score row extent: max_visible rounded up to 8 (candidate mode: 8 * 2048)
   const int32_t* cand;      // candidate mode: [T][2048] carried block ids, else null
+  int32_t group;            // > 1: queries g*group .. g*group+group-1 share a sequence (<= 8)
 };
 hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream);
 

@@ -134,6 +134,15 @@ def test_indexer_rejects(case):
     assert S.lib.sparse_attn_last_error()
 
 
+@pytest.mark.parametrize("group", [-1, 9])
+def test_indexer_rejects_group(group):
+    p = _plan()
+    q, c = _q(), _c()
+    q.group = group
+    assert _indexer(p, q, c) == S.SA_EUNSUPPORTED
+    assert b"group" in S.lib.sparse_attn_last_error()
+
+
 def test_select_rejects():
     p = _plan()
     q = _q()

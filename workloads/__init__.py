@@ -34,7 +34,8 @@ _SRC = os.path.join(_HERE, "synth.c")
 _LIB = os.path.join(_HERE, "libsynth.so")
 
 # Stream tags: stream id = (tag << 32) | sequence.
-TAG = dict(q=1, qI=2, w=3, C=4, KI=5, R=6, Xp=7, Zp=8, beta=9, Xraw=10, Zraw=11)
+TAG = {"q": 1, "qI": 2, "w": 3, "C": 4, "KI": 5, "R": 6, "Xp": 7, "Zp": 8, "beta": 9, "Xraw": 10, "Zraw": 11,
+       "q-mq": 12, "qI-mq": 13, "w-mq": 14}
 
 # Layer shapes the pages fix.
 HEADS = 64          # query heads sharing one latent
@@ -151,6 +152,7 @@ class Workload:
     beta: Optional[np.ndarray] = None
     seed: int = 0
     meta: dict = field(default_factory=dict)
+    group: int = 0       # consecutive queries that share a sequence (multi-token decode)
 
     def visible(self) -> np.ndarray:
         return (self.pos.astype(np.int64) + 1) // self.ratio
@@ -214,6 +216,38 @@ def make_decode(B: int, n_raw, ratio: int = 2, key_dtype: str = "bf16", seed: in
                     KS=KS, R=R, Xp=Xp, Zp=Zp, beta=beta, seed=seed)
 
 
+def make_decode_mq(B: int, n_raw, G: int = 6, ratio: int = 2, key_dtype: str = "bf16",
+                   seed: int = 0, name: str = "decode-mq", nc_cap: Optional[int] = None) -> Workload:
+    """B sequences, G decode queries each at raw positions n_raw-G .. n_raw-1 (a verified
+    token and the G-1 drafted tokens after it). Queries g*G .. g*G+G-1 read sequence g; the
+    block's own latents, index keys and window rows are already in the stores. The window
+    store holds 128 + G rows, so no query's window wraps onto another's rows."""
+    n_raw = np.broadcast_to(np.asarray(n_raw, dtype=np.int64), (B,)).copy()
+    assert np.all(n_raw >= G)
+    T = B * G
+    seq = np.repeat(np.arange(B, dtype=np.int32), G)
+    pos = (np.repeat(n_raw, G) - G + np.tile(np.arange(G), B)).astype(np.int32)
+    vis = (pos.astype(np.int64) + 1) // ratio
+    if nc_cap is None:
+        nc_cap = int(max(1, vis.max()))
+    wcap = WINDOW + G
+    q = np.empty((T, HEADS, DIM), np.uint16)
+    qI = np.empty((T, IDX_HEADS, IDX_DIM), np.uint16)
+    w = np.empty((T, IDX_HEADS), np.float32)
+    C = np.empty((B, nc_cap, DIM), np.uint16)
+    R = np.empty((B, wcap, DIM), np.uint16)
+    for b in range(B):
+        q[b * G:(b + 1) * G] = normal_bf16(seed, "q-mq", b, (G, HEADS, DIM))
+        qI[b * G:(b + 1) * G] = normal_bf16(seed, "qI-mq", b, (G, IDX_HEADS, IDX_DIM))
+        w[b * G:(b + 1) * G] = uniform_f32(seed, "w-mq", b, (G, IDX_HEADS))
+        C[b] = normal_bf16(seed, "C", b, (nc_cap, DIM))
+        R[b] = normal_bf16(seed, "R", b, (wcap, DIM))
+    KI, KS = _keys(seed, key_dtype, B, nc_cap)
+    return Workload(name=name, kind="decode", ratio=ratio, key_dtype=key_dtype, B=B, T=T,
+                    nc_cap=nc_cap, wcap=wcap, seq=seq, pos=pos, q=q, qI=qI, w=w, C=C, KI=KI,
+                    KS=KS, R=R, seed=seed, group=G)
+
+
 def make_prefill(T: int, offset: int, ratio: int = 1, key_dtype: str = "bf16", seed: int = 0,
                  name: str = "prefill", wcap: Optional[int] = None) -> Workload:
     """One sequence; a chunk of T causal queries at raw positions offset .. offset+T-1.
@@ -257,9 +291,20 @@ WORKLOADS = {
 }
 
 
+# Further workloads of the same layer: a multi-token decode step (the verified token and
+# 5 drafted tokens per sequence: 128 x (1 + 5) = 768 queries, the decode capture size the
+# MI355X recipe names for its 5-token draft).
+MORE_WORKLOADS = {
+    "decode-mq6-b128-ctx128k-fp8": dict(kind="decode_mq", B=128, n_raw=131072, G=6, ratio=2,
+                                        key_dtype="fp8"),
+}
+
+
 def make(name: str, seed: int = 0) -> Workload:
-    cfg = dict(WORKLOADS[name])
+    cfg = dict(WORKLOADS[name] if name in WORKLOADS else MORE_WORKLOADS[name])
     kind = cfg.pop("kind")
     if kind == "decode":
         return make_decode(name=name, seed=seed, **cfg)
+    if kind == "decode_mq":
+        return make_decode_mq(name=name, seed=seed, **cfg)
     return make_prefill(name=name, seed=seed, **cfg)
