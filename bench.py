@@ -12,9 +12,12 @@ bf16 MFMA peak, and the fp64 CPU oracle timed on a bounded sample.
 
 A second object times a layer that only indexes: it re-scores the 2048 candidate blocks
 the two-stage pass kept (candidate-bounded indexer, selection inside them, attention).
+A third times a multi-token decode step: 128 sequences x 6 queries (a verified token and
+5 drafted ones) whose indexer streams each sequence's keys once per group.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-prefill] [--no-rescore] [--no-cpu-baseline] [--profile]
+                       [--no-prefill] [--no-rescore] [--no-multiquery] [--no-cpu-baseline]
+                       [--profile]
 """
 from __future__ import annotations
 
@@ -40,6 +43,7 @@ INDEXER_SOURCES = ("sparse_attention_score_amd/csrc/indexer.hip", "sparse_attent
                    "sparse_attention_score_amd/csrc/sa_launch.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_decode-b128-ctx128k-fp8_traffic.json")
 RESCORE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_cand_decode-b128-ctx128k-fp8_traffic.json")
+GROUP_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_group_decode-mq6-b128-ctx128k-fp8_traffic.json")
 COPY_BYTES = 1 << 30
 
 
@@ -106,6 +110,15 @@ def step_bytes(wl) -> float:
              + 64 * 512 * 2 * 2 + IDX_BYTES_PER_QUERY_FIXED + 512 * 4)
     groups = len(wl.compress_groups())
     return float(per_q.sum() + groups * (2 * 2 * 512 * 2 + 512 * 2) + 2 * 512 * 4)
+
+
+def group_indexer_bytes(wl) -> float:
+    """Algorithmic bytes of one grouped indexer launch: each sequence's visible index keys
+    (and fp8 row scales) once, up to the largest n of its queries, plus every query's index
+    query and weights."""
+    nseq = np.zeros(wl.B, dtype=np.float64)
+    np.maximum.at(nseq, wl.seq.astype(np.int64), wl.visible().astype(np.float64))
+    return float((nseq * key_row_bytes(wl.key_dtype)).sum() + wl.T * IDX_BYTES_PER_QUERY_FIXED)
 
 
 def rescore_bytes(wl, carried: np.ndarray) -> float:
@@ -298,6 +311,8 @@ def main():
     ap.add_argument("--prefill-workload", default="prefill-4096-at-61440")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-rescore", action="store_true")
+    ap.add_argument("--mq-workload", default="decode-mq6-b128-ctx128k-fp8")
+    ap.add_argument("--no-multiquery", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--profile", action="store_true", help="timed steps only (for rocprofv3)")
@@ -386,6 +401,34 @@ def main():
         log(f"rescore layer: {r_s * 1e3:.3f} ms, stages {rms}")
     del d
     torch.cuda.empty_cache()
+
+    if not args.no_multiquery:
+        t0 = time.perf_counter()
+        wm = W.make(args.mq_workload)
+        dm = DeviceBatch(wm)
+        torch.cuda.synchronize()
+        log(f"multi-token decode inputs ready in {time.perf_counter() - t0:.1f}s")
+        m_eager, mms = run_batch(torch, dm, args.steps, args.warmup, 0.0 if args.profile else 0.5)
+        m_s = m_eager if args.profile else run_graph(torch, dm, args.steps)[0]
+        gb = group_indexer_bytes(wm)
+        fi, fa = step_flops(wm)
+        mi_s = mms["indexer"] * 1e-3
+        result["multi_query"] = {
+            "workload": args.mq_workload, "queries": int(wm.T), "group": int(wm.group),
+            "ms_per_step": m_s * 1e3, "queries_per_s": wm.T / m_s,
+            "eager_ms_per_step": m_eager * 1e3,
+            "timing": "eager launches" if args.profile else "HIP graph replays of the whole step",
+            "stage_ms": mms,
+            "indexer": {"bound": "hbm", "achieved": gb / mi_s / 1e9, "peak": HBM_PEAK / 1e9,
+                        "unit": "GB/s", "frac": gb / mi_s / HBM_PEAK,
+                        "traffic": stored_traffic(args.mq_workload, GROUP_TRAFFIC_FILE),
+                        "algorithmic_bytes_per_launch": gb, "avg_launch_ms": mms["indexer"],
+                        "key_bytes_per_query": gb / wm.T,
+                        "mfma_tflop": fi / 1e12, "mfma_frac": fi / mi_s / BF16_PEAK},
+        }
+        log(f"multi-token decode: {m_s * 1e3:.3f} ms/step, stages {mms}")
+        del dm, wm
+        torch.cuda.empty_cache()
 
     if not args.no_prefill and not args.profile:
         t0 = time.perf_counter()
