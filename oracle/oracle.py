@@ -18,6 +18,10 @@ Sources (the pages):
        an indexer scores those latents and keeps the best 512 per query after
        a candidate stage that selects 2048 blocks of 8.
   [OCP] OCP 8-bit Floating Point Specification (OFP8), E4M3 encoding.
+  [MX]  OCP Microscaling Formats (MX) Specification v1.0: MXFP4 = blocks of 32
+        FP4 E2M1 elements sharing one E8M0 scale. The pages name the 4-bit
+        indexer cache ("deepseek-ai/DeepSeek-V4.1-Flash" recipe, model table:
+        FP4 indexer cache; both MI355X configurations: indexer_kv_dtype mxfp4).
 
 Readings where the pages are silent (each is also a stated definition):
   - indexer: 16 heads x 128 dims on the query side, one 128-d key per
@@ -123,10 +127,49 @@ def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
     return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
+def e2m1_value(code: int) -> float:
+    """Value of one FP4 E2M1 code [MX]: sign, 2 exponent bits (bias 1), 1 mantissa bit;
+    exponent field 0 is subnormal (0 or 0.5); no infinities and no NaN."""
+    s = -1.0 if code & 0x8 else 1.0
+    e = (code >> 1) & 0x3
+    m = code & 0x1
+    if e == 0:
+        return s * (m / 2.0)
+    return s * (1.0 + m / 2.0) * 2.0 ** (e - 1)
+
+
+E2M1_TABLE = np.array([e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def e8m0_value(code: int) -> float:
+    """Value of one E8M0 scale [MX]: 2^(code - 127), code 255 is NaN."""
+    return float("nan") if code == 255 else 2.0 ** (int(code) - 127)
+
+
+E8M0_TABLE = np.array([e8m0_value(c) for c in range(256)], dtype=np.float64)
+
+MX_BLOCK = 32
+
+
+def mxfp4_to_f64(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP4 rows -> fp64 [..., 128]. codes: uint8 [..., 64], element 2i in the low nibble
+    of byte i and element 2i+1 in the high nibble; scales: uint8 E8M0 [..., 4], scale b for
+    elements 32b .. 32b+31. Element value = E8M0 scale * E2M1 element [MX]."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    lo = E2M1_TABLE[codes & 0xF]
+    hi = E2M1_TABLE[codes >> 4]
+    elem = np.stack([lo, hi], axis=-1).reshape(codes.shape[:-1] + (2 * codes.shape[-1],))
+    sc = E8M0_TABLE[np.asarray(scales, dtype=np.uint8)]
+    return elem * np.repeat(sc, MX_BLOCK, axis=-1)
+
+
 def index_keys_f64(KI: np.ndarray, KS: Optional[np.ndarray]) -> np.ndarray:
-    """Exact index keys: bf16 keys as stored, or e4m3 code * fp32 row scale."""
+    """Exact index keys: bf16 keys as stored, e4m3 code * fp32 row scale, or MXFP4
+    (uint8 codes [.., 64] with uint8 E8M0 block scales [.., 4])."""
     if KS is None:
         return bf16_to_f64(KI)
+    if np.asarray(KS).dtype == np.uint8:
+        return mxfp4_to_f64(KI, KS)
     return e4m3_to_f64(KI) * np.asarray(KS, dtype=np.float64)[..., None]
 
 

@@ -55,6 +55,80 @@ def test_e4m3_structure():
     assert len(np.unique(finite)) == 253                     # +-0 coincide, 2 NaNs
 
 
+def test_e2m1_and_e8m0_anchors_from_spec():
+    g = _gold("mxfp4_anchors.json")
+    for code, val in g["e2m1"]:
+        v = O.e2m1_value(code)
+        assert v == val and math.copysign(1, v) == math.copysign(1, val), code
+    for code, val in g["e8m0"]:
+        assert O.e8m0_value(code) == val, code
+    for code in g["e8m0_nan"]:
+        assert math.isnan(O.e8m0_value(code))
+
+
+def test_e8m0_table_matches_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 1 and np.isnan(O.E8M0_TABLE[255])
+    assert np.array_equal(ref[~nan], O.E8M0_TABLE[~nan])
+
+
+def test_e2m1_values_are_e4m3_values():
+    # every E2M1 value times a power of two in [2^-3, 2^3] is an E4M3 value (torch's
+    # float8_e4m3fn table): E2M1 has one mantissa bit, E4M3 three, and a wider range
+    e4 = set(torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+             .to(torch.float64).numpy().tolist())
+    for k in range(-3, 4):
+        for v in O.E2M1_TABLE:
+            assert v * 2.0 ** k in e4, (v, k)
+    t = O.E2M1_TABLE
+    assert np.all(np.diff(t[:8]) > 0) and np.array_equal(t[8:], -t[:8])
+
+
+def test_mxfp4_worked_row():
+    g = _gold("mxfp4_anchors.json")["worked_row"]
+    codes = np.zeros(64, np.uint8)
+    for i, b in g["bytes"].items():
+        codes[int(i)] = b
+    v = O.mxfp4_to_f64(codes, np.array(g["scales"], np.uint8))
+    want = np.zeros(128)
+    for i, x in g["values"].items():
+        want[int(i)] = x
+    assert np.array_equal(v, want)
+
+
+def test_mxfp4_decode_against_scalar_loops():
+    # the vectorised decode (nibble split, interleave, block repeat) against one element
+    # at a time from the scalar definitions
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 256, (3, 64), dtype=np.uint8)
+    scales = rng.integers(100, 150, (3, 4), dtype=np.uint8)
+    v = O.mxfp4_to_f64(codes, scales)
+    for r in range(3):
+        for d in range(128):
+            byte = int(codes[r, d // 2])
+            nib = byte & 0xF if d % 2 == 0 else byte >> 4
+            assert v[r, d] == O.e2m1_value(nib) * O.e8m0_value(int(scales[r, d // 32])), (r, d)
+
+
+def test_mxfp4_scores_equal_bf16_scores():
+    # MXFP4 keys are exact bf16 values (at most 2 significant bits times a power of two):
+    # scoring the decoded keys equals scoring the same keys stored as bf16
+    rng = np.random.default_rng(6)
+    codes = rng.integers(0, 256, (40, 64), dtype=np.uint8)
+    scales = rng.integers(120, 132, (40, 4), dtype=np.uint8)
+    k = O.mxfp4_to_f64(codes, scales)
+    kb = torch.from_numpy(k).to(torch.bfloat16)
+    assert np.array_equal(kb.to(torch.float64).numpy(), k)
+    bits = kb.view(torch.int16).numpy().view(np.uint16)
+    qI = rng.standard_normal((16, 128))
+    w = rng.uniform(0, 1, 16)
+    a = O.index_scores(qI, w, O.index_keys_f64(codes, scales))
+    b = O.index_scores(qI, w, O.index_keys_f64(bits, None))
+    assert np.array_equal(a, b)
+
+
 def test_bf16_matches_torch():
     rng = np.random.default_rng(1)
     x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 10 ** rng.uniform(-30, 30, 20000).astype(np.float32),

@@ -41,3 +41,31 @@ def test_decode_workload_shapes():
     assert wl.compress_groups().tolist() == [0, 2]
     wp = W.make_prefill(T=10, offset=100, ratio=1)
     assert wp.nc_cap == 110 and wp.wcap == 138 and wp.pos[0] == 100
+
+
+def test_mxfp4_quantiser_follows_the_mx_rule():
+    # block exponent floor(log2 amax) - 2, elements the nearest E2M1 value of x / 2^X
+    # (ties to the even code, saturating at 6), checked one element at a time
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((5, 128)) * 10.0 ** rng.uniform(-2, 2, (5, 1))).astype(np.float32)
+    x[0, 0:32] = 0.0                       # an all-zero block
+    x[1, 32:64] = 0.75                     # exact ties between 0.5 and 1 after scaling
+    codes, scales = W.quant_mxfp4_rows(x)
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for r in range(5):
+        for b in range(4):
+            blk = x[r, 32 * b:32 * b + 32].astype(np.float64)
+            amax = np.abs(blk).max()
+            X = -127 if amax == 0 else int(np.floor(np.log2(amax))) - 2
+            assert scales[r, b] == X + 127, (r, b)
+            for k in range(32):
+                y = abs(blk[k]) / 2.0 ** X
+                d = [abs(y - m) for m in mags]
+                best = min(range(8), key=lambda c: (d[c], c & 1))
+                if y >= 6.0:
+                    best = 7
+                byte = int(codes[r, 16 * b + k // 2])
+                got = byte & 0xF if k % 2 == 0 else byte >> 4
+                assert got & 7 == best, (r, b, k, y, got)
+                if blk[k] < 0:
+                    assert got & 8, (r, b, k)

@@ -73,8 +73,11 @@ def _L():
         lib.synth_uniform_f32.argtypes = [u64, u64, vp, i64]
         lib.synth_quant_e4m3_rows.argtypes = [vp, i64, i64, vp, vp]
         lib.synth_normal_e4m3_rows.argtypes = [u64, u64, i64, i64, vp, vp]
+        lib.synth_quant_mxfp4_rows.argtypes = [vp, i64, i64, vp, vp]
+        lib.synth_normal_mxfp4_rows.argtypes = [u64, u64, i64, i64, vp, vp]
         for f in (lib.synth_normal_f32, lib.synth_normal_bf16, lib.synth_uniform_f32,
-                  lib.synth_quant_e4m3_rows, lib.synth_normal_e4m3_rows):
+                  lib.synth_quant_e4m3_rows, lib.synth_normal_e4m3_rows,
+                  lib.synth_quant_mxfp4_rows, lib.synth_normal_mxfp4_rows):
             f.restype = None
         _lib = lib
     return _lib
@@ -113,6 +116,27 @@ def quant_e4m3_rows(x: np.ndarray):
     return codes, scale
 
 
+def quant_mxfp4_rows(x: np.ndarray):
+    """Row-wise OCP MXFP4 quantisation of fp32 [..., cols] -> (codes u8 [..., cols/2],
+    E8M0 block scales u8 [..., cols/32])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    cols = x.shape[-1]
+    assert cols % 32 == 0
+    rows = x.size // cols
+    codes = np.empty(x.shape[:-1] + (cols // 2,), dtype=np.uint8)
+    scales = np.empty(x.shape[:-1] + (cols // 32,), dtype=np.uint8)
+    _L().synth_quant_mxfp4_rows(x.ctypes.data, rows, cols, codes.ctypes.data, scales.ctypes.data)
+    return codes, scales
+
+
+def normal_mxfp4_rows(seed: int, tag: str, seq: int, rows: int, cols: int):
+    codes = np.empty((rows, cols // 2), dtype=np.uint8)
+    scales = np.empty((rows, cols // 32), dtype=np.uint8)
+    _L().synth_normal_mxfp4_rows(seed, _stream(tag, seq), rows, cols, codes.ctypes.data,
+                                 scales.ctypes.data)
+    return codes, scales
+
+
 def normal_e4m3_rows(seed: int, tag: str, seq: int, rows: int, cols: int):
     codes = np.empty((rows, cols), dtype=np.uint8)
     scale = np.empty((rows,), dtype=np.float32)
@@ -133,7 +157,7 @@ class Workload:
     name: str
     kind: str            # "decode" | "prefill"
     ratio: int
-    key_dtype: str       # "bf16" | "fp8"
+    key_dtype: str       # "bf16" | "fp8" | "mxfp4"
     B: int
     T: int
     nc_cap: int
@@ -176,6 +200,12 @@ def _keys(seed, key_dtype, B, nc_cap):
         KS = np.empty((B, nc_cap), dtype=np.float32)
         for b in range(B):
             KI[b], KS[b] = normal_e4m3_rows(seed, "KI", b, nc_cap, IDX_DIM)
+        return KI, KS
+    if key_dtype == "mxfp4":
+        KI = np.empty((B, nc_cap, IDX_DIM // 2), dtype=np.uint8)
+        KS = np.empty((B, nc_cap, IDX_DIM // 32), dtype=np.uint8)
+        for b in range(B):
+            KI[b], KS[b] = normal_mxfp4_rows(seed, "KI", b, nc_cap, IDX_DIM)
         return KI, KS
     raise ValueError(key_dtype)
 

@@ -17,7 +17,12 @@
  *   bf16  round-to-nearest-even of the fp32 value (upper half of binary32),
  *   e4m3  OCP FP8 E4M3 ("e4m3fn": bias 7, max 448, no infinities) with one
  *         fp32 scale per row, scale = amax / 448 (1 for an all-zero row),
- *         code = RNE(x / scale), saturating at 448.
+ *         code = RNE(x / scale), saturating at 448,
+ *   mxfp4 OCP MX FP4 (E2M1 elements, one E8M0 scale per block of 32): block
+ *         exponent X = floor(log2(amax)) - 2 (E2M1's largest exponent), clamped
+ *         to [-127, 127] (-127 for an all-zero block), element = RNE(x / 2^X)
+ *         on the E2M1 grid, saturating at 6; two elements per byte, the even
+ *         one in the low nibble.
  */
 #include <math.h>
 #include <stdint.h>
@@ -145,6 +150,69 @@ void synth_quant_e4m3_rows(const float* x, int64_t rows, int64_t cols, uint8_t* 
     float s = amax > 0.0f ? amax / 448.0f : 1.0f;
     scale[r] = s;
     for (int64_t c = 0; c < cols; ++c) codes[r * cols + c] = e4m3_encode(xr[c] / s);
+  }
+}
+
+/* Nearest FP4 E2M1 code (ties to the even code) of a finite fp32 value, saturating at 6. */
+static inline uint8_t e2m1_encode(float y) {
+  static const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+  uint8_t sign = 0;
+  if (y < 0.0f || (y == 0.0f && signbit(y))) { sign = 8; y = -y; }
+  if (!(y < 6.0f)) return (uint8_t)(sign | 7);
+  int c = 0;
+  while (c < 7 && mag[c + 1] <= y) ++c;          /* mag[c] <= y < mag[c+1] */
+  const float lo = y - mag[c], hi = mag[c + 1] - y;
+  if (hi < lo || (hi == lo && (c & 1))) ++c;       /* nearest; a tie goes to the even code */
+  return (uint8_t)(sign | c);
+}
+
+/* One row of cols (a multiple of 32) fp32 values -> cols/2 packed E2M1 bytes and cols/32
+   E8M0 block scales. */
+static void mxfp4_row(const float* x, int64_t cols, uint8_t* codes, uint8_t* scales) {
+  for (int64_t b = 0; b < cols / 32; ++b) {
+    const float* xb = x + 32 * b;
+    float amax = 0.0f;
+    for (int k = 0; k < 32; ++k) {
+      float a = fabsf(xb[k]);
+      if (a > amax) amax = a;
+    }
+    int X = -127;
+    if (amax > 0.0f) {
+      int e;
+      frexpf(amax, &e);                      /* floor(log2 amax) = e - 1 */
+      X = e - 1 - 2;
+      if (X < -127) X = -127;
+      if (X > 127) X = 127;
+    }
+    scales[b] = (uint8_t)(X + 127);
+    for (int k = 0; k < 32; k += 2) {
+      uint8_t c0 = e2m1_encode(ldexpf(xb[k], -X));
+      uint8_t c1 = e2m1_encode(ldexpf(xb[k + 1], -X));
+      codes[16 * b + k / 2] = (uint8_t)(c0 | (c1 << 4));
+    }
+  }
+}
+
+/* Row-wise MXFP4 quantisation: x[rows][cols] fp32 -> codes[rows][cols/2], scales[rows][cols/32]. */
+void synth_quant_mxfp4_rows(const float* x, int64_t rows, int64_t cols, uint8_t* codes,
+                            uint8_t* scales) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    mxfp4_row(x + r * cols, cols, codes + r * (cols / 2), scales + r * (cols / 32));
+}
+
+/* Normal draws quantised straight to MXFP4 (same stream layout as synth_normal_e4m3_rows). */
+void synth_normal_mxfp4_rows(uint64_t seed, uint64_t stream, int64_t rows, int64_t cols,
+                             uint8_t* codes, uint8_t* scales) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    float buf[512];
+    for (int64_t c = 0; c < cols; c += 4) {
+      float z[4];
+      block_normals(seed, stream, (uint64_t)((r * cols + c) / 4), z);
+      for (int k = 0; k < 4; ++k) buf[c + k] = z[k];
+    }
+    mxfp4_row(buf, cols, codes + r * (cols / 2), scales + r * (cols / 32));
   }
 }
 
