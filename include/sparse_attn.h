@@ -62,7 +62,14 @@ typedef enum sa_status {
 
 typedef enum sa_key_dtype {
   SA_KEY_BF16 = 0,      /* index keys bf16 [.][128] */
-  SA_KEY_FP8_E4M3 = 1   /* index keys e4m3 [.][128] plus one fp32 scale per key */
+  SA_KEY_FP8_E4M3 = 1,  /* index keys e4m3 [.][128] plus one fp32 scale per key */
+  SA_KEY_MXFP4 = 2      /* index keys OCP MXFP4 (the pages' FP4 indexer cache, "mxfp4"
+                           indexer_kv_dtype of the recipe's MI355X configurations):
+                           [.][64] bytes of FP4 E2M1, element 2i in the low nibble of
+                           byte i, plus [.][4] E8M0 scales, scale b for elements
+                           32b .. 32b+31. Key = 2^(scale-127) * element. Scored per
+                           query (indexer_score ignores queries->group and the chunk
+                           kernel for these keys); not supported by indexer_score_cand */
 } sa_key_dtype;
 
 /* Fixed at plan time. The kernels support exactly num_heads 64, latent_dim 512,
@@ -111,10 +118,15 @@ typedef struct sa_cache {
   const void* window;            /* bf16 [num_seqs][window_cap][512]; raw position u is row u % window_cap */
   int64_t window_seq_stride;     /* >= window_cap * 512 */
   int32_t window_cap;            /* >= 128 */
-  const void* idx_keys;          /* bf16 or e4m3 [num_seqs][compressed_cap][128] */
-  int64_t idx_keys_seq_stride;   /* >= compressed_cap * 128 */
-  const float* idx_scales;       /* fp32 [num_seqs][compressed_cap] for e4m3 keys, NULL for bf16 */
-  int64_t idx_scales_seq_stride; /* >= compressed_cap (e4m3 only) */
+  const void* idx_keys;          /* bf16 or e4m3 [num_seqs][compressed_cap][128], or MXFP4
+                                    bytes [num_seqs][compressed_cap][64]; 16-byte aligned */
+  int64_t idx_keys_seq_stride;   /* in elements of the store (bf16, bytes, bytes):
+                                    >= compressed_cap * 128 (64 for MXFP4) */
+  const void* idx_scales;        /* fp32 [num_seqs][compressed_cap] for e4m3 keys (16-byte
+                                    aligned), E8M0 bytes [num_seqs][compressed_cap][4] for
+                                    MXFP4 keys (4-byte aligned), NULL for bf16 */
+  int64_t idx_scales_seq_stride; /* in scale elements: >= compressed_cap (e4m3) or
+                                    >= 4 * compressed_cap and a multiple of 4 (MXFP4) */
 } sa_cache;
 
 /* Validate `params` and create a plan (host memory owned by the library,

@@ -19,7 +19,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("SPARSE_ATTN_LIB") or os.path.join(_PKG, "libsparse_attn.so")
 
 SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_EWORKSPACE, SA_EHIP = 0, 1, 2, 3, 4
-SA_KEY_BF16, SA_KEY_FP8_E4M3 = 0, 1
+SA_KEY_BF16, SA_KEY_FP8_E4M3, SA_KEY_MXFP4 = 0, 1, 2
+KEY_DTYPES = {"bf16": SA_KEY_BF16, "fp8": SA_KEY_FP8_E4M3, "mxfp4": SA_KEY_MXFP4}
 STATUS_NAMES = {0: "SA_OK", 1: "SA_EINVAL", 2: "SA_EUNSUPPORTED", 3: "SA_EWORKSPACE", 4: "SA_EHIP"}
 
 EXPORTS = ("sparse_attn_plan", "sparse_attn_plan_destroy", "sparse_attn_last_error",
@@ -130,7 +131,7 @@ class Plan:
                       idx_heads=dims.get("idx_heads", 16), idx_dim=dims.get("idx_dim", 128),
                       block=dims.get("block", 8), cand_blocks=dims.get("cand_blocks", 2048),
                       ratio=ratio,
-                      idx_key_dtype=SA_KEY_FP8_E4M3 if key_dtype == "fp8" else SA_KEY_BF16,
+                      idx_key_dtype=KEY_DTYPES[key_dtype],
                       softmax_scale=softmax_scale, max_queries=max_queries,
                       max_compressed=max_compressed)
         h = ctypes.c_void_p()
@@ -173,7 +174,8 @@ class Queries:
 
 class Cache:
     """sa_cache from device tensors: latents [S,cap,512] bf16, window [S,wcap,512] bf16,
-    idx_keys [S,cap,128] bf16 or uint8 (e4m3 codes), idx_scales [S,cap] fp32 or None.
+    idx_keys [S,cap,128] bf16 or uint8 (e4m3 codes), or uint8 [S,cap,64] (MXFP4 codes);
+    idx_scales [S,cap] fp32 (e4m3), uint8 [S,cap,4] (MXFP4 E8M0 scales) or None.
     Any of them may be None when the call at hand does not read it."""
 
     def __init__(self, latents=None, window=None, idx_keys=None, idx_scales=None,
@@ -192,11 +194,13 @@ class Cache:
             c.window, c.window_seq_stride, c.window_cap = window.data_ptr(), window.stride(0), window.shape[1]
         if idx_keys is not None:
             if idx_keys.dtype not in (torch.bfloat16, torch.uint8):
-                raise TypeError("idx_keys must be bfloat16 or uint8 (e4m3 codes)")
+                raise TypeError("idx_keys must be bfloat16 or uint8 (e4m3 or MXFP4 codes)")
             _need(idx_keys, "idx_keys", idx_keys.dtype)
             c.idx_keys, c.idx_keys_seq_stride = idx_keys.data_ptr(), idx_keys.stride(0)
         if idx_scales is not None:
-            _need(idx_scales, "idx_scales", torch.float32)
+            if idx_scales.dtype not in (torch.float32, torch.uint8):
+                raise TypeError("idx_scales must be float32 (e4m3) or uint8 (MXFP4 E8M0)")
+            _need(idx_scales, "idx_scales", idx_scales.dtype)
             c.idx_scales, c.idx_scales_seq_stride = idx_scales.data_ptr(), idx_scales.stride(0)
         self._keep = (latents, window, idx_keys, idx_scales)
         self.c = c

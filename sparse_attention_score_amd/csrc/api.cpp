@@ -109,9 +109,19 @@ sa_status check_cache(const sa_plan* plan, const sa_queries* q, const sa_cache* 
   if (keys) {
     SA_REQUIRE(c->idx_keys != nullptr && aligned16(c->idx_keys), SA_EINVAL,
                "cache->idx_keys is NULL or not 16-byte aligned");
-    const int64_t rowmul = plan->p.idx_key_dtype == SA_KEY_FP8_E4M3 ? 16 : 8;
-    SA_REQUIRE(c->idx_keys_seq_stride >= c->compressed_cap * 128 && c->idx_keys_seq_stride % rowmul == 0,
+    // stride unit: bf16 elements, e4m3 bytes, or MXFP4 bytes (64 per row); 16-byte rows
+    const bool mx = plan->p.idx_key_dtype == SA_KEY_MXFP4;
+    const int64_t rowmul = plan->p.idx_key_dtype == SA_KEY_BF16 ? 8 : 16;
+    const int64_t rowunits = mx ? 64 : 128;
+    SA_REQUIRE(c->idx_keys_seq_stride >= c->compressed_cap * rowunits && c->idx_keys_seq_stride % rowmul == 0,
                SA_EINVAL, "cache->idx_keys_seq_stride = %lld invalid", (long long)c->idx_keys_seq_stride);
+    if (mx) {
+      SA_REQUIRE(c->idx_scales != nullptr && reinterpret_cast<uintptr_t>(c->idx_scales) % 4 == 0, SA_EINVAL,
+                 "cache->idx_scales is NULL or not 4-byte aligned (required for MXFP4 keys)");
+      SA_REQUIRE(c->idx_scales_seq_stride >= c->compressed_cap * 4 && c->idx_scales_seq_stride % 4 == 0,
+                 SA_EINVAL, "cache->idx_scales_seq_stride = %lld must be >= 4 * compressed_cap and a multiple of 4",
+                 (long long)c->idx_scales_seq_stride);
+    }
     if (plan->p.idx_key_dtype == SA_KEY_FP8_E4M3) {
       SA_REQUIRE(c->idx_scales != nullptr && aligned16(c->idx_scales), SA_EINVAL,
                  "cache->idx_scales is NULL or misaligned (required for e4m3 keys)");
@@ -164,7 +174,8 @@ sa_status sparse_attn_plan(const sa_params* p, sa_plan** plan, size_t* workspace
              "unsupported dims (need heads 64, latent 512, window 128, topk 512, idx 16x128, "
              "block 8, cand_blocks 2048)");
   SA_REQUIRE(p->ratio == 1 || p->ratio == 2, SA_EUNSUPPORTED, "ratio %d not in {1, 2}", p->ratio);
-  SA_REQUIRE(p->idx_key_dtype == SA_KEY_BF16 || p->idx_key_dtype == SA_KEY_FP8_E4M3,
+  SA_REQUIRE(p->idx_key_dtype == SA_KEY_BF16 || p->idx_key_dtype == SA_KEY_FP8_E4M3 ||
+                 p->idx_key_dtype == SA_KEY_MXFP4,
              SA_EUNSUPPORTED, "idx_key_dtype %d unknown", p->idx_key_dtype);
   SA_REQUIRE(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f, SA_EINVAL,
              "softmax_scale must be finite and > 0");
@@ -214,11 +225,12 @@ sa_status indexer_score(const sa_plan* plan, const sa_queries* q, const sa_cache
   a.compressed_cap = c->compressed_cap;
   a.ratio = plan->p.ratio;
   a.fp8 = plan->p.idx_key_dtype == SA_KEY_FP8_E4M3;
+  a.mxfp4 = plan->p.idx_key_dtype == SA_KEY_MXFP4;
   a.q_idx = q_idx;
   a.w = w;
   a.keys = c->idx_keys;
   a.keys_seq_stride = c->idx_keys_seq_stride;
-  a.scales = c->idx_scales;
+  a.scales = static_cast<const float*>(c->idx_scales);
   a.scales_seq_stride = c->idx_scales_seq_stride;
   a.scores = scores;
   a.ld_scores = ld_scores;
@@ -230,7 +242,9 @@ sa_status indexer_score(const sa_plan* plan, const sa_queries* q, const sa_cache
   // Queries that share a sequence in one call (a prefill chunk) reuse each key tile
   // across many queries; groups of a multi-token decode step share one key stream per
   // group; independent decode queries each stream their own keys.
-  const bool prefill = a.group == 1 && c->num_seqs == 1 && q->T > 1;
+  // MXFP4 keys: one key stream per query in every case (no chunk or group kernel yet)
+  if (a.mxfp4) a.group = 1;
+  const bool prefill = !a.mxfp4 && a.group == 1 && c->num_seqs == 1 && q->T > 1;
   SA_REQUIRE(prefill || (q->T + a.group - 1) / a.group <= 65535, SA_EUNSUPPORTED,
              "T = %lld queries in groups of %d over several sequences: at most 65535 groups per call",
              (long long)q->T, (int)a.group);
@@ -244,6 +258,8 @@ sa_status indexer_score_cand(const sa_plan* plan, const sa_queries* q, const sa_
   if ((st = check_plan(plan)) != SA_OK) return st;
   if ((st = check_queries(plan, q)) != SA_OK) return st;
   if ((st = check_cache(plan, q, c, true, false)) != SA_OK) return st;
+  SA_REQUIRE(plan->p.idx_key_dtype != SA_KEY_MXFP4, SA_EUNSUPPORTED,
+             "candidate-bounded re-scoring supports bf16 and e4m3 index keys only");
   SA_REQUIRE(q_idx && aligned16(q_idx) && w && aligned16(w), SA_EINVAL,
              "q_idx / w NULL or not 16-byte aligned");
   SA_REQUIRE(cand && aligned16(cand), SA_EINVAL, "cand NULL or not 16-byte aligned");
@@ -266,11 +282,12 @@ sa_status indexer_score_cand(const sa_plan* plan, const sa_queries* q, const sa_
   a.compressed_cap = c->compressed_cap;
   a.ratio = plan->p.ratio;
   a.fp8 = plan->p.idx_key_dtype == SA_KEY_FP8_E4M3;
+  a.mxfp4 = plan->p.idx_key_dtype == SA_KEY_MXFP4;
   a.q_idx = q_idx;
   a.w = w;
   a.keys = c->idx_keys;
   a.keys_seq_stride = c->idx_keys_seq_stride;
-  a.scales = c->idx_scales;
+  a.scales = static_cast<const float*>(c->idx_scales);
   a.scales_seq_stride = c->idx_scales_seq_stride;
   a.scores = scores;
   a.ld_scores = ld_scores;

@@ -127,6 +127,10 @@ __device__ __forceinline__ void to_lds16(const void* src, uint32_t lds) {
 __device__ __forceinline__ void to_lds16_after_reads(const void* src, uint32_t lds) {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" :: "v"(src), "{m0}"(lds) : "memory");
 }
+// 4 bytes per lane to LDS byte lds + 4 * lane (same rules as to_lds16).
+__device__ __forceinline__ void to_lds4(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(src), "{m0}"(lds) : "memory");
+}
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // CAND: candidate-bounded re-scoring. The score row is in slot order: entry 8i + r belongs
@@ -298,6 +302,142 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
       if constexpr (FP8) v *= scv[j];
     }
     const float m = max8_lanes(v);   // E is a multiple of 8: groups are all in or all out
+    if (k < E) {
+      srow[k] = v;
+      if (brow && (lane & 7) == 0) brow[k >> 3] = m;
+    }
+  }
+}
+
+// ======================================================================================
+// Decode, MXFP4 keys
+// ======================================================================================
+// MXFP4 keys (OCP MX: 128 FP4 E2M1 elements in 64 bytes, element 2i in the low nibble of
+// byte i, and one E8M0 scale per block of 32 elements): the decode kernel's stream with
+// 64-byte rows, so one load instruction moves a 16-key tile and the ring holds 16 of them.
+// Lane group g of the MFMA takes block g of its key row: its k-steps s = 0..3 are dims
+// 32g + 8s .. +7 (the query's A operand uses the same dims), so each lane reads one 16-byte
+// chunk per tile and applies one block scale, while widening E2M1 x scale to bf16 exactly
+// (v_cvt_scalef32_pk_bf16_fp4: two elements per instruction). The wave's block scales
+// (4 bytes per key) arrive in LDS by direct loads ahead of the tiles.
+constexpr int kMxRB = kIdxDim / 2;                     // row bytes
+constexpr int kMxD = kRingBytes / (16 * kMxRB);        // tiles in flight per wave
+static_assert(kMxD <= kTilesPerWave && (kMxD & (kMxD - 1)) == 0, "ring depth");
+
+struct MxShared {
+  uint8_t ring[kDWaves][kRingBytes];
+  uint8_t scale[kDWaves][kTilesPerWave * 16 * 4];   // E8M0 scales of the wave's keys
+  float stage[kDWaves][kTilesPerWave * 16];
+  uint16_t q[kIdxHeads * kIdxDim];
+  float w[kIdxHeads];
+};
+
+// Position of chunk q (block q) of row r in LDS: rotated by r/4 so that the 16 rows' reads
+// of one block hit 16 different bank groups.
+__device__ __forceinline__ int mx_pos(int r, int q) { return q ^ ((r >> 2) & 3); }
+__device__ __forceinline__ int kdim_mx(int g, int s) { return 32 * g + 8 * s; }
+
+// E8M0 code -> fp32 scale 2^(e-127) (e = 0 is the fp32 subnormal 2^-127, 255 is NaN).
+__device__ __forceinline__ float e8m0_scale(uint32_t e) {
+  return __uint_as_float(e == 0 ? 0x00400000u : (e == 255 ? 0x7FC00000u : e << 23));
+}
+
+__global__ __launch_bounds__(kDThreads) void indexer_mx_kernel(IndexerArgs a) {
+  constexpr int RB = kMxRB, TB = 16 * kMxRB, D = kMxD;
+  static_assert(TB == 1024, "one load instruction per tile");
+  __shared__ __attribute__((aligned(16))) MxShared sh;
+  const int t = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int c = lane & 15, g = lane >> 4;
+  const int E = (int)a.E;
+  const int chunk0 = blockIdx.x * kKeysPerWG;
+  const int key0 = chunk0 + wave * kTilesPerWave * 16;
+  const int n = query_n(a, t);
+  const int ntiles = key0 < E ? min(kTilesPerWave, (E - key0 + 15) >> 4) : 0;
+  const int chunk_live = chunk0 < n ? min(kDWaves * kTilesPerWave, (n - chunk0 + 15) >> 4) : 0;
+  const int live = min(max(chunk_live - wave * kTilesPerWave, 0), kTilesPerWave);
+  float* srow = a.scores + (int64_t)t * a.ld_scores;
+  float* brow = a.block_max ? a.block_max + (int64_t)t * a.ld_block_max : nullptr;
+  const int seq = a.seq_id[t];
+  const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys) + (int64_t)seq * a.keys_seq_stride;
+  const uint8_t* scales = reinterpret_cast<const uint8_t*>(a.scales) + (int64_t)seq * a.scales_seq_stride;
+
+  const uint32_t lds_q = (uint32_t)(uintptr_t)&sh.q[0];
+  const uint32_t lds_w = (uint32_t)(uintptr_t)&sh.w[0];
+  if (chunk_live > 0) {
+    const uint8_t* qb = reinterpret_cast<const uint8_t*>(a.q_idx) + (int64_t)t * kIdxHeads * kIdxDim * 2;
+    to_lds16(qb + 1024 * wave + 16 * lane, lds_q + 1024 * wave);
+    if (wave == 0 && lane < kIdxHeads / 4) to_lds16(a.w + (int64_t)t * kIdxHeads + 4 * lane, lds_w);
+  }
+  // the wave's block scales, one key (4 bytes) per lane and load (rows past n repeat row n-1)
+  if (live > 0) {
+#pragma unroll
+    for (int j = 0; j < kTilesPerWave / 4; ++j)
+      to_lds4(scales + (int64_t)min(key0 + 64 * j + lane, n - 1) * 4,
+              (uint32_t)(uintptr_t)&sh.scale[wave][256 * j]);
+  }
+
+  // load of a tile: lane -> row r = lane / 4, position p = lane % 4 holds chunk mx_pos(r, p)
+  const int rr = lane >> 2, qq = mx_pos(rr, lane & 3);
+  const uint32_t ring0 = (uint32_t)(uintptr_t)&sh.ring[wave][0];
+  auto issue = [&](int i, bool after_reads) {
+    const int k = key0 + 16 * i;
+    const int row = min(k + rr, n - 1);
+    const uint8_t* src = keys + (int64_t)row * RB + qq * 16;
+    const uint32_t lds = ring0 + (uint32_t)((i & (D - 1)) * TB);
+    if (after_reads) to_lds16_after_reads(src, lds);
+    else to_lds16(src, lds);
+  };
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+    if (u < live) issue(u, false);
+  if (live >= D) __builtin_amdgcn_s_waitcnt(waitcnt_vm(D));   // query, weights, scales
+  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  asm volatile("s_barrier" ::: "memory");
+
+  if (live > 0) {
+    bf16x8 qa[4];
+    float wq[4];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) qa[s2] = *reinterpret_cast<const bf16x8*>(&sh.q[c * kIdxDim + kdim_mx(g, s2)]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wq[i] = sh.w[4 * g + i];
+    const uint32_t roff = (uint32_t)(c * RB + mx_pos(c, g) * 16);
+    float* stage = sh.stage[wave];
+    for (int i = 0; i < live; ++i) {
+      if (i + D - 1 < live) __builtin_amdgcn_s_waitcnt(waitcnt_vm(D - 1));   // tile i landed
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      const uint8_t* tile = sh.ring[wave] + (i & (D - 1)) * TB;
+      const u32x4 K = *reinterpret_cast<const u32x4*>(tile + roff);
+      const float sc = e8m0_scale(sh.scale[wave][(16 * i + c) * 4 + g]);
+      if (i + D < live) issue(i + D, true);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const u32x4 u = {
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(K[s2], sc, 0)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(K[s2], sc, 1)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(K[s2], sc, 2)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(K[s2], sc, 3))};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s2], __builtin_bit_cast(bf16x8, u), acc, 0, 0, 0);
+      }
+      float v = wq[0] * relu(acc[0]);
+      v = fmaf(wq[1], relu(acc[1]), v);
+      v = fmaf(wq[2], relu(acc[2]), v);
+      v = fmaf(wq[3], relu(acc[3]), v);
+      v = add_xor32(add_xor16(v));
+      if (lane < 16) stage[16 * i + lane] = v;
+    }
+  }
+
+  // ---- scores and block maxima of the wave's keys: 64 consecutive keys per store ----
+  const float* stage = sh.stage[wave];
+#pragma unroll
+  for (int j = 0; j < kTilesPerWave / 4; ++j) {
+    const int k = key0 + 64 * j + lane;
+    if (64 * j >= 16 * ntiles) break;
+    const float v = k < n ? stage[64 * j + lane] : neg_inf();
+    const float m = max8_lanes(v);
     if (k < E) {
       srow[k] = v;
       if (brow && (lane & 7) == 0) brow[k >> 3] = m;
@@ -779,7 +919,11 @@ void launch_group(const IndexerArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream) {
-  if (a.group > 1 && !a.cand) {
+  if (a.mxfp4) {
+    // every query streams its own keys (the caller routes no other mode here)
+    dim3 grid((unsigned)((a.E + kKeysPerWG - 1) / kKeysPerWG), (unsigned)a.T);
+    hipLaunchKernelGGL(indexer_mx_kernel, grid, dim3(kDThreads), 0, stream, a);
+  } else if (a.group > 1 && !a.cand) {
     // the smallest even group size that holds a.group (extra queries are masked)
     if (a.group <= 2) launch_group<2>(a, stream);
     else if (a.group <= 4) launch_group<4>(a, stream);

@@ -25,11 +25,12 @@ struct IndexerArgs {
   int64_t compressed_cap;
   int32_t ratio;
   bool fp8;
+  bool mxfp4;               // MXFP4 keys: [seq][cap][64] bytes, E8M0 scales [seq][cap][4]
   const void* q_idx;        // bf16 [T][16][128]
   const float* w;           // [T][16]
   const void* keys;         // bf16 / e4m3 [seq][cap][128]
   int64_t keys_seq_stride;  // elements
-  const float* scales;      // e4m3 only
+  const float* scales;      // e4m3: fp32 per row; MXFP4: the E8M0 bytes (cast back in the kernel)
   int64_t scales_seq_stride;
   float* scores;            // [T][ld_scores]
   int64_t ld_scores;

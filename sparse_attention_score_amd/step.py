@@ -39,7 +39,7 @@ class DeviceBatch:
         self.w = torch.from_numpy(wl.w).to(dev)
         self.C = to_device_bf16(wl.C, dev)
         self.R = to_device_bf16(wl.R, dev)
-        if wl.key_dtype == "fp8":
+        if wl.key_dtype in ("fp8", "mxfp4"):
             self.KI = torch.from_numpy(wl.KI).to(dev)
             self.KS = torch.from_numpy(wl.KS).to(dev)
         else:

@@ -143,6 +143,22 @@ def test_indexer_rejects_group(group):
     assert b"group" in S.lib.sparse_attn_last_error()
 
 
+@pytest.mark.parametrize("case", ["no_scales", "scale_stride", "key_stride", "cand"])
+def test_mxfp4_rejects(case):
+    p = _plan(key_dtype="mxfp4")
+    q = _q()
+    c = _c(idx_keys_seq_stride=1000 * 64, idx_scales=0x70000, idx_scales_seq_stride=4000)
+    if case == "no_scales": c.idx_scales = None
+    if case == "scale_stride": c.idx_scales_seq_stride = 3999
+    if case == "key_stride": c.idx_keys_seq_stride = 999 * 64
+    if case == "cand":
+        st = S.lib.indexer_score_cand(p.handle, ctypes.byref(q), ctypes.byref(c), 0x40000, 0x50000,
+                                      0x80000, 0x60000, 16384, 0x90000, 2048, None)
+        assert st == S.SA_EUNSUPPORTED
+        return
+    assert _indexer(p, q, c) == S.SA_EINVAL, S.lib.sparse_attn_last_error()
+
+
 def test_select_rejects():
     p = _plan()
     q = _q()

@@ -92,6 +92,23 @@ def test_decode_candidate_stage_prunes(kd):
     assert np.all(cand >= 0)  # exactly 2048 kept
 
 
+@pytest.mark.parametrize("n_raw", [[40006, 3001], [1, 2, 17, 130, 1031]])
+def test_decode_mxfp4_keys(n_raw):
+    # MXFP4 index keys (E2M1 elements, E8M0 block scales): pruning and a ragged last
+    # block, then n = 0, 1, 8, 65, 515
+    wl = W.make_decode(B=len(n_raw), n_raw=n_raw, ratio=2, key_dtype="mxfp4",
+                       name=f"mxfp4-{len(n_raw)}", with_compress=False, seed=17)
+    _e2e(wl)
+
+
+def test_mxfp4_keys_in_a_prefill_chunk_and_a_group():
+    # a chunk of one sequence and a multi-token decode batch with MXFP4 keys: both run the
+    # per-query kernel for these keys
+    _e2e(W.make_prefill(T=40, offset=20000, ratio=1, key_dtype="mxfp4", name="prefill-mxfp4", seed=18))
+    _e2e(W.make_decode_mq(B=2, n_raw=[3001, 9000], G=6, ratio=2, key_dtype="mxfp4",
+                          name="mq-mxfp4", seed=19), check_scores=True)
+
+
 def test_decode_tiny_contexts():
     # n = 0 (window only), 1, 1, 8, 65 visible compressed latents
     wl = W.make_decode(B=5, n_raw=[1, 2, 3, 17, 130], ratio=2, key_dtype="bf16", name="tiny",
