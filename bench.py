@@ -13,11 +13,12 @@ bf16 MFMA peak, and the fp64 CPU oracle timed on a bounded sample.
 A second object times a layer that only indexes: it re-scores the 2048 candidate blocks
 the two-stage pass kept (candidate-bounded indexer, selection inside them, attention).
 A third times a multi-token decode step: 128 sequences x 6 queries (a verified token and
-5 drafted ones) whose indexer streams each sequence's keys once per group.
+5 drafted ones) whose indexer streams each sequence's keys once per group. A fourth times
+the headline decode batch with MXFP4 index keys (the 4-bit indexer cache).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-prefill] [--no-rescore] [--no-multiquery] [--no-cpu-baseline]
-                       [--profile]
+                       [--no-prefill] [--no-rescore] [--no-multiquery] [--no-mxfp4]
+                       [--no-cpu-baseline] [--profile]
 """
 from __future__ import annotations
 
@@ -44,6 +45,7 @@ INDEXER_SOURCES = ("sparse_attention_score_amd/csrc/indexer.hip", "sparse_attent
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_decode-b128-ctx128k-fp8_traffic.json")
 RESCORE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_cand_decode-b128-ctx128k-fp8_traffic.json")
 GROUP_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_group_decode-mq6-b128-ctx128k-fp8_traffic.json")
+MX_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_mx_decode-b128-ctx128k-mxfp4_traffic.json")
 COPY_BYTES = 1 << 30
 
 
@@ -90,7 +92,8 @@ def copy_bandwidth(torch):
 
 
 def key_row_bytes(key_dtype: str) -> int:
-    return 128 + 4 if key_dtype == "fp8" else 256
+    """Bytes of one index key row with its scales: e4m3 + fp32 scale, MXFP4 + 4 E8M0, bf16."""
+    return {"fp8": 128 + 4, "mxfp4": 64 + 4}.get(key_dtype, 256)
 
 
 def indexer_bytes(wl) -> float:
@@ -313,6 +316,8 @@ def main():
     ap.add_argument("--no-rescore", action="store_true")
     ap.add_argument("--mq-workload", default="decode-mq6-b128-ctx128k-fp8")
     ap.add_argument("--no-multiquery", action="store_true")
+    ap.add_argument("--mxfp4-workload", default="decode-b128-ctx128k-mxfp4")
+    ap.add_argument("--no-mxfp4", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--profile", action="store_true", help="timed steps only (for rocprofv3)")
@@ -428,6 +433,31 @@ def main():
         }
         log(f"multi-token decode: {m_s * 1e3:.3f} ms/step, stages {mms}")
         del dm, wm
+        torch.cuda.empty_cache()
+
+    if not args.no_mxfp4:
+        t0 = time.perf_counter()
+        wx = W.make(args.mxfp4_workload)
+        dx = DeviceBatch(wx)
+        torch.cuda.synchronize()
+        log(f"MXFP4-key decode inputs ready in {time.perf_counter() - t0:.1f}s")
+        x_eager, xms = run_batch(torch, dx, args.steps, args.warmup, 0.0 if args.profile else 0.5)
+        x_s = x_eager if args.profile else run_graph(torch, dx, args.steps)[0]
+        xb = indexer_bytes(wx)
+        xi_s = xms["indexer"] * 1e-3
+        result["mxfp4_keys"] = {
+            "workload": args.mxfp4_workload, "queries": int(wx.T),
+            "ms_per_step": x_s * 1e3, "queries_per_s": wx.T / x_s,
+            "eager_ms_per_step": x_eager * 1e3,
+            "timing": "eager launches" if args.profile else "HIP graph replays of the whole step",
+            "stage_ms": xms,
+            "indexer": {"bound": "hbm", "achieved": xb / xi_s / 1e9, "peak": HBM_PEAK / 1e9,
+                        "unit": "GB/s", "frac": xb / xi_s / HBM_PEAK,
+                        "traffic": stored_traffic(args.mxfp4_workload, MX_TRAFFIC_FILE),
+                        "algorithmic_bytes_per_launch": xb, "avg_launch_ms": xms["indexer"]},
+        }
+        log(f"MXFP4-key decode: {x_s * 1e3:.3f} ms/step, stages {xms}")
+        del dx, wx
         torch.cuda.empty_cache()
 
     if not args.no_prefill and not args.profile:
