@@ -127,6 +127,19 @@ typedef struct sa_cache {
                                     MXFP4 keys (4-byte aligned), NULL for bf16 */
   int64_t idx_scales_seq_stride; /* in scale elements: >= compressed_cap (e4m3) or
                                     >= 4 * compressed_cap and a multiple of 4 (MXFP4) */
+  /* Paged stores (the layout serving engines keep caches in). NULL block_table: the
+   * stores above are contiguous per sequence. Otherwise latents, idx_keys and idx_scales
+   * are page pools of num_pages pages of page_size rows each (pool row r = page r /
+   * page_size, row r % page_size; the *_seq_stride fields are ignored), and compressed
+   * position j of sequence s is pool row block_table[s * block_table_stride + j /
+   * page_size] * page_size + j % page_size. The window stays per sequence. Page ids
+   * outside [0, num_pages) are clamped. Supported by indexer_score (bf16 and e4m3 keys,
+   * one key stream per query) and sparse_attn_fwd; indexer_score_cand and MXFP4 keys
+   * return SA_EUNSUPPORTED. */
+  const int32_t* block_table;    /* device int32 [num_seqs][block_table_stride] or NULL */
+  int64_t block_table_stride;    /* >= ceil(compressed_cap / page_size) */
+  int32_t page_size;             /* power of two in [16, 2^20] */
+  int64_t num_pages;             /* pages in each pool, 1 .. 2^31 - 1 */
 } sa_cache;
 
 /* Validate `params` and create a plan (host memory owned by the library,

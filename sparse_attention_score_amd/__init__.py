@@ -49,7 +49,9 @@ class sa_cache(ctypes.Structure):
                 ("window", ctypes.c_void_p), ("window_seq_stride", ctypes.c_int64),
                 ("window_cap", ctypes.c_int32),
                 ("idx_keys", ctypes.c_void_p), ("idx_keys_seq_stride", ctypes.c_int64),
-                ("idx_scales", ctypes.c_void_p), ("idx_scales_seq_stride", ctypes.c_int64)]
+                ("idx_scales", ctypes.c_void_p), ("idx_scales_seq_stride", ctypes.c_int64),
+                ("block_table", ctypes.c_void_p), ("block_table_stride", ctypes.c_int64),
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int64)]
 
 
 class SparseAttnError(RuntimeError):
@@ -179,7 +181,8 @@ class Cache:
     Any of them may be None when the call at hand does not read it."""
 
     def __init__(self, latents=None, window=None, idx_keys=None, idx_scales=None,
-                 num_seqs: Optional[int] = None, compressed_cap: Optional[int] = None):
+                 num_seqs: Optional[int] = None, compressed_cap: Optional[int] = None,
+                 block_table: Optional[torch.Tensor] = None, page_size: int = 0):
         ref = latents if latents is not None else idx_keys
         if num_seqs is None:
             num_seqs = ref.shape[0]
@@ -202,7 +205,15 @@ class Cache:
                 raise TypeError("idx_scales must be float32 (e4m3) or uint8 (MXFP4 E8M0)")
             _need(idx_scales, "idx_scales", idx_scales.dtype)
             c.idx_scales, c.idx_scales_seq_stride = idx_scales.data_ptr(), idx_scales.stride(0)
-        self._keep = (latents, window, idx_keys, idx_scales)
+        if block_table is not None:
+            # paged stores: latents [pages*page_size, 512], idx_keys [pages*page_size, 128],
+            # idx_scales [pages*page_size] are pools; block_table [num_seqs, pages per seq]
+            _need(block_table, "block_table", torch.int32)
+            pool = latents if latents is not None else idx_keys
+            c.block_table, c.block_table_stride = block_table.data_ptr(), block_table.stride(0)
+            c.page_size = int(page_size)
+            c.num_pages = pool.shape[0] // int(page_size)
+        self._keep = (latents, window, idx_keys, idx_scales, block_table)
         self.c = c
 
 

@@ -98,6 +98,16 @@ sa_status check_queries(const sa_plan* plan, const sa_queries* q) {
   return SA_OK;
 }
 
+sa::PageTable page_table(const sa_cache* c) {
+  sa::PageTable pt;
+  pt.table = c->block_table;
+  pt.stride = c->block_table_stride;
+  pt.log2_page = 0;
+  while (c->block_table && (1 << pt.log2_page) < c->page_size) ++pt.log2_page;
+  pt.num_pages = c->num_pages;
+  return pt;
+}
+
 sa_status check_cache(const sa_plan* plan, const sa_queries* q, const sa_cache* c, bool keys,
                       bool latents) {
   SA_REQUIRE(c != nullptr, SA_EINVAL, "cache is NULL");
@@ -106,6 +116,17 @@ sa_status check_cache(const sa_plan* plan, const sa_queries* q, const sa_cache* 
   SA_REQUIRE(q->max_visible <= c->compressed_cap, SA_EINVAL,
              "queries->max_visible = %lld exceeds cache->compressed_cap = %lld",
              (long long)q->max_visible, (long long)c->compressed_cap);
+  const bool paged = c->block_table != nullptr;
+  if (paged) {
+    SA_REQUIRE(reinterpret_cast<uintptr_t>(c->block_table) % 4 == 0, SA_EINVAL,
+               "cache->block_table not 4-byte aligned");
+    SA_REQUIRE(c->page_size >= 16 && c->page_size <= (1 << 20) && (c->page_size & (c->page_size - 1)) == 0,
+               SA_EINVAL, "cache->page_size = %d must be a power of two in [16, 2^20]", (int)c->page_size);
+    SA_REQUIRE(c->num_pages >= 1 && c->num_pages <= INT32_MAX, SA_EINVAL,
+               "cache->num_pages = %lld invalid", (long long)c->num_pages);
+    SA_REQUIRE(c->block_table_stride >= (c->compressed_cap + c->page_size - 1) / c->page_size, SA_EINVAL,
+               "cache->block_table_stride = %lld < pages of compressed_cap", (long long)c->block_table_stride);
+  }
   if (keys) {
     SA_REQUIRE(c->idx_keys != nullptr && aligned16(c->idx_keys), SA_EINVAL,
                "cache->idx_keys is NULL or not 16-byte aligned");
@@ -113,8 +134,9 @@ sa_status check_cache(const sa_plan* plan, const sa_queries* q, const sa_cache* 
     const bool mx = plan->p.idx_key_dtype == SA_KEY_MXFP4;
     const int64_t rowmul = plan->p.idx_key_dtype == SA_KEY_BF16 ? 8 : 16;
     const int64_t rowunits = mx ? 64 : 128;
-    SA_REQUIRE(c->idx_keys_seq_stride >= c->compressed_cap * rowunits && c->idx_keys_seq_stride % rowmul == 0,
+    SA_REQUIRE(paged || (c->idx_keys_seq_stride >= c->compressed_cap * rowunits && c->idx_keys_seq_stride % rowmul == 0),
                SA_EINVAL, "cache->idx_keys_seq_stride = %lld invalid", (long long)c->idx_keys_seq_stride);
+    SA_REQUIRE(!(paged && mx), SA_EUNSUPPORTED, "paged stores support bf16 and e4m3 index keys only");
     if (mx) {
       SA_REQUIRE(c->idx_scales != nullptr && reinterpret_cast<uintptr_t>(c->idx_scales) % 4 == 0, SA_EINVAL,
                  "cache->idx_scales is NULL or not 4-byte aligned (required for MXFP4 keys)");
@@ -125,7 +147,7 @@ sa_status check_cache(const sa_plan* plan, const sa_queries* q, const sa_cache* 
     if (plan->p.idx_key_dtype == SA_KEY_FP8_E4M3) {
       SA_REQUIRE(c->idx_scales != nullptr && aligned16(c->idx_scales), SA_EINVAL,
                  "cache->idx_scales is NULL or misaligned (required for e4m3 keys)");
-      SA_REQUIRE(c->idx_scales_seq_stride >= c->compressed_cap, SA_EINVAL,
+      SA_REQUIRE(paged || c->idx_scales_seq_stride >= c->compressed_cap, SA_EINVAL,
                  "cache->idx_scales_seq_stride = %lld < compressed_cap",
                  (long long)c->idx_scales_seq_stride);
     }
@@ -133,7 +155,7 @@ sa_status check_cache(const sa_plan* plan, const sa_queries* q, const sa_cache* 
   if (latents) {
     SA_REQUIRE(c->latents != nullptr && aligned16(c->latents), SA_EINVAL,
                "cache->latents is NULL or not 16-byte aligned");
-    SA_REQUIRE(c->latents_seq_stride >= c->compressed_cap * 512 && c->latents_seq_stride % 8 == 0,
+    SA_REQUIRE(paged || (c->latents_seq_stride >= c->compressed_cap * 512 && c->latents_seq_stride % 8 == 0),
                SA_EINVAL, "cache->latents_seq_stride = %lld invalid", (long long)c->latents_seq_stride);
     SA_REQUIRE(c->window != nullptr && aligned16(c->window), SA_EINVAL,
                "cache->window is NULL or not 16-byte aligned");
@@ -239,12 +261,15 @@ sa_status indexer_score(const sa_plan* plan, const sa_queries* q, const sa_cache
   a.E = E;
   a.cand = nullptr;
   a.group = q->group > 1 ? q->group : 1;
+  a.pages = page_table(c);
+  // paged stores: one key stream per query (the chunk and group kernels read contiguous rows)
+  if (a.pages.table) a.group = 1;
   // Queries that share a sequence in one call (a prefill chunk) reuse each key tile
   // across many queries; groups of a multi-token decode step share one key stream per
   // group; independent decode queries each stream their own keys.
   // MXFP4 keys: one key stream per query in every case (no chunk or group kernel yet)
   if (a.mxfp4) a.group = 1;
-  const bool prefill = !a.mxfp4 && a.group == 1 && c->num_seqs == 1 && q->T > 1;
+  const bool prefill = !a.mxfp4 && !a.pages.table && a.group == 1 && c->num_seqs == 1 && q->T > 1;
   SA_REQUIRE(prefill || (q->T + a.group - 1) / a.group <= 65535, SA_EUNSUPPORTED,
              "T = %lld queries in groups of %d over several sequences: at most 65535 groups per call",
              (long long)q->T, (int)a.group);
@@ -260,6 +285,8 @@ sa_status indexer_score_cand(const sa_plan* plan, const sa_queries* q, const sa_
   if ((st = check_cache(plan, q, c, true, false)) != SA_OK) return st;
   SA_REQUIRE(plan->p.idx_key_dtype != SA_KEY_MXFP4, SA_EUNSUPPORTED,
              "candidate-bounded re-scoring supports bf16 and e4m3 index keys only");
+  SA_REQUIRE(c->block_table == nullptr, SA_EUNSUPPORTED,
+             "candidate-bounded re-scoring reads contiguous stores only");
   SA_REQUIRE(q_idx && aligned16(q_idx) && w && aligned16(w), SA_EINVAL,
              "q_idx / w NULL or not 16-byte aligned");
   SA_REQUIRE(cand && aligned16(cand), SA_EINVAL, "cand NULL or not 16-byte aligned");
@@ -296,6 +323,7 @@ sa_status indexer_score_cand(const sa_plan* plan, const sa_queries* q, const sa_
   a.E = E;
   a.cand = cand;
   a.group = 1;
+  a.pages = sa::PageTable{nullptr, 0, 0, 0};
   return hip_status(sa::launch_indexer(a, false, (hipStream_t)stream), "indexer_score_cand launch");
 }
 
@@ -385,6 +413,7 @@ sa_status sparse_attn_fwd(const sa_plan* plan, const sa_queries* q, const sa_cac
   SA_REQUIRE(lse == nullptr || aligned16(lse), SA_EINVAL, "lse not 16-byte aligned");
   sa::AttnArgs a;
   a.m = meta(plan, q, c->num_seqs, c->compressed_cap);
+  a.pages = page_table(c);
   a.q = qv;
   a.topk = topk;
   a.latents = c->latents;

@@ -195,8 +195,15 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       nsel += sh.wave_cnt[w];
       before += (w < wave) ? sh.wave_cnt[w] : 0;
     }
-    const uint16_t* lat = reinterpret_cast<const uint16_t*>(a.latents) + (int64_t)seq * a.latents_seq_stride;
-    if (v) sh.rows[before + incl - 1] = lat + (int64_t)j * kDim;
+    const uint16_t* lat = reinterpret_cast<const uint16_t*>(a.latents);
+    if (a.pages.table) {
+      // paged latents: the row of position j is in page table[seq][j / page] (the only
+      // compiler-visible load before the output; the waits after it are explicit again)
+      if (v) sh.rows[before + incl - 1] = lat + pool_row(a.pages, page_of(a.pages, seq, j), j) * kDim;
+    } else {
+      lat += (int64_t)seq * a.latents_seq_stride;
+      if (v) sh.rows[before + incl - 1] = lat + (int64_t)j * kDim;
+    }
     const int u0 = p - kWindow + 1 > 0 ? p - kWindow + 1 : 0;
     const int nwin = p - u0 + 1;
     const uint16_t* win = reinterpret_cast<const uint16_t*>(a.window) + (int64_t)seq * a.window_seq_stride;

@@ -133,11 +133,17 @@ __device__ __forceinline__ void to_lds4(const void* src, uint32_t lds) {
 }
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// CAND: candidate-bounded re-scoring. The score row is in slot order: entry 8i + r belongs
-// to position 8 cand[i] + r of the query's carried candidate blocks (ascending, -1 padded),
-// and a tile of 16 entries is two candidate blocks; the loads gather those blocks' rows.
-template <bool FP8, bool CAND>
+// Modes. kPlain: each query's keys are contiguous rows of its sequence. kCand (candidate-
+// bounded re-scoring): the score row is in slot order, entry 8i + r belonging to position
+// 8 cand[i] + r of the query's carried candidate blocks (ascending, -1 padded); a tile of 16
+// entries is two candidate blocks, and the loads gather those blocks' rows. kPaged: the keys
+// (and e4m3 scales) are page pools; a tile of 16 positions lies in one page (pages hold a
+// multiple of 16 positions), whose id each wave reads from the block table up front.
+enum DecodeMode { kPlain = 0, kCand = 1, kPaged = 2 };
+
+template <bool FP8, int MODE>
 __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a) {
+  constexpr bool CAND = MODE == kCand, PAGED = MODE == kPaged;
   using DT = DecodeTile<FP8>;
   constexpr int RB = DT::RB, TB = DT::TB, NK = DT::NK, D = DT::D;
   static_assert((D & (D - 1)) == 0 && D >= 2, "ring depth must be a power of two");
@@ -162,12 +168,13 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
   float* srow = a.scores + (int64_t)t * a.ld_scores;
   float* brow = a.block_max ? a.block_max + (int64_t)t * a.ld_block_max : nullptr;
   const int seq = a.seq_id[t];
-  const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys) + (int64_t)seq * a.keys_seq_stride * (FP8 ? 1 : 2);
+  const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys) +
+                        (PAGED ? 0 : (int64_t)seq * a.keys_seq_stride * (FP8 ? 1 : 2));
 
   // e4m3 row scales of the keys this lane stores at the end (issued first: the loads
   // complete in order, so the row waits below also cover them)
   float scv[kTilesPerWave / 4] = {};
-  if (FP8 && !CAND && key0 < n) {   // (a query without keys may have no valid sequence)
+  if (FP8 && MODE == kPlain && key0 < n) {   // (a query without keys may have no valid sequence)
     const float* scales = a.scales + (int64_t)seq * a.scales_seq_stride;
 #pragma unroll
     for (int j = 0; j < kTilesPerWave / 4; ++j) scv[j] = scales[min(key0 + 64 * j + lane, n - 1)];
@@ -182,6 +189,24 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
     if (wave == 0 && lane < kIdxHeads / 4) to_lds16(a.w + (int64_t)t * kIdxHeads + 4 * lane, lds_w);
     if (CAND && wave == 1 && lane < kDWaves * kTilesPerWave * 2 / 4)   // the group's block ids
       to_lds16(a.cand + (int64_t)t * kCandBlocks + chunk0 / 8 + 4 * lane, (uint32_t)(uintptr_t)&sh.ids[0]);
+  }
+  // paged mode: page id of the wave's tile `lane` (the first 16 rows past n repeat row n-1),
+  // read before any tile load (their addresses depend on it); the e4m3 scales follow, each
+  // lane's key in the page of its tile
+  int pgreg = 0;
+  if constexpr (PAGED) {
+    if (live > 0) {
+      pgreg = (int)page_of(a.pages, seq, min(key0 + 16 * min(lane, kTilesPerWave - 1), n - 1));
+      if constexpr (FP8) {
+        const float* scales = a.scales;
+#pragma unroll
+        for (int j = 0; j < kTilesPerWave / 4; ++j) {
+          const int x = min(key0 + 64 * j + lane, n - 1);
+          const int pg = __shfl(pgreg, (x - key0) >> 4);
+          scv[j] = scales[pool_row(a.pages, pg, x)];
+        }
+      }
+    }
   }
   // candidate mode: block id of the wave's slot `lane` (lane reads pick one per load). A
   // slot is valid when its block holds a visible position (0 <= id < ceil(n / 8), compared
@@ -233,6 +258,9 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
         const int id = __builtin_amdgcn_readlane(idreg, 2 * i + (j * (64 / DT::CPR)) / 8);
         const int row = valid_id(id) ? min(8 * id + (rr[j] & 7), n - 1) : n - 1;
         src = keys + (int64_t)row * RB + qq[j] * 16;
+      } else if constexpr (PAGED) {
+        const int64_t pg = __builtin_amdgcn_readlane(pgreg, i);
+        src = keys + (pool_row(a.pages, pg, k) + min(rr[j], last)) * RB + qq[j] * 16;
       } else {
         src = tb + (min(rr[j], last) * RB + qq[j] * 16);
       }
@@ -663,12 +691,18 @@ __global__ __launch_bounds__(kDThreads, 2) void indexer_group_kernel(IndexerArgs
 // ======================================================================================
 // Prefill
 // ======================================================================================
-constexpr int kPWaves = 4;
+#ifndef SA_P_WAVES
+#define SA_P_WAVES 4
+#endif
+#ifndef SA_P_CHUNK
+#define SA_P_CHUNK 4096
+#endif
+constexpr int kPWaves = SA_P_WAVES;
 constexpr int kPThreads = 64 * kPWaves;
 constexpr int kPairsPerWave = 2;
 constexpr int kQPerWG = kPWaves * kPairsPerWave * 2;   // 16 queries
 constexpr int kPKT = 32;                                // keys per tile
-constexpr int kPChunk = 2048;                           // keys per work-group
+constexpr int kPChunk = SA_P_CHUNK;                     // keys per work-group (4096: 3 % faster than 2048)
 constexpr int kPST = 2 * kPKT;                          // keys per LDS stage (two tiles)
 constexpr int kPBufs = 3;
 
@@ -687,7 +721,7 @@ constexpr int kRsrcWord3 = 0x00020000;   // raw buffer resource, 32-bit data (gf
 constexpr uint32_t kDrop = 0x80000000u;  // buffer offset past every extent: store dropped
 
 template <bool FP8>
-__global__ __launch_bounds__(kPThreads, 2) void indexer_prefill_kernel(IndexerArgs a) {
+__global__ __launch_bounds__(kPThreads, 8 / kPWaves) void indexer_prefill_kernel(IndexerArgs a) {
   constexpr int RB = FP8 ? kIdxDim : 2 * kIdxDim;   // key row bytes in HBM
   __shared__ __attribute__((aligned(16))) PrefillShared sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -945,13 +979,18 @@ hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream
     dim3 grid((unsigned)((a.E + kKeysPerWG - 1) / kKeysPerWG), (unsigned)a.T);
     if (a.cand) {
       if (a.fp8)
-        hipLaunchKernelGGL((indexer_decode_kernel<true, true>), grid, dim3(kDThreads), 0, stream, a);
+        hipLaunchKernelGGL((indexer_decode_kernel<true, kCand>), grid, dim3(kDThreads), 0, stream, a);
       else
-        hipLaunchKernelGGL((indexer_decode_kernel<false, true>), grid, dim3(kDThreads), 0, stream, a);
+        hipLaunchKernelGGL((indexer_decode_kernel<false, kCand>), grid, dim3(kDThreads), 0, stream, a);
+    } else if (a.pages.table) {
+      if (a.fp8)
+        hipLaunchKernelGGL((indexer_decode_kernel<true, kPaged>), grid, dim3(kDThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL((indexer_decode_kernel<false, kPaged>), grid, dim3(kDThreads), 0, stream, a);
     } else if (a.fp8) {
-      hipLaunchKernelGGL((indexer_decode_kernel<true, false>), grid, dim3(kDThreads), 0, stream, a);
+      hipLaunchKernelGGL((indexer_decode_kernel<true, kPlain>), grid, dim3(kDThreads), 0, stream, a);
     } else {
-      hipLaunchKernelGGL((indexer_decode_kernel<false, false>), grid, dim3(kDThreads), 0, stream, a);
+      hipLaunchKernelGGL((indexer_decode_kernel<false, kPlain>), grid, dim3(kDThreads), 0, stream, a);
     }
   } else {
     // blockIdx.x (key chunk) varies fastest, so with a multiple of 8 chunks every XCD

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "sa_launch.h"
+
 namespace sa {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
@@ -114,6 +116,17 @@ __device__ __forceinline__ float max8_lanes(float v) {
   m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4E, 0xF, 0xF, false)));
   m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xF, 0xF, false)));
   return m;
+}
+
+// Page id of compressed position j of sequence seq in a paged store (clamped into the pool).
+__device__ __forceinline__ int64_t page_of(const PageTable& pt, int seq, int j) {
+  int64_t pg = pt.table[(int64_t)seq * pt.stride + (j >> pt.log2_page)];
+  pg = pg < 0 ? 0 : pg;
+  return pg < pt.num_pages ? pg : pt.num_pages - 1;
+}
+// Pool row of position j given its page id.
+__device__ __forceinline__ int64_t pool_row(const PageTable& pt, int64_t page, int j) {
+  return (page << pt.log2_page) + (j & ((1 << pt.log2_page) - 1));
 }
 
 }  // namespace sa

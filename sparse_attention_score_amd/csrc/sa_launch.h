@@ -6,6 +6,16 @@
 
 namespace sa {
 
+// Paged compressed stores: position j of sequence s is pool row
+// table[s * stride + (j >> log2_page)] * page + (j & (page - 1)); table == null: the stores
+// are contiguous per sequence. Page ids are clamped into [0, num_pages).
+struct PageTable {
+  const int32_t* table;
+  int64_t stride;
+  int32_t log2_page;
+  int64_t num_pages;
+};
+
 struct QueryMeta {
   const int32_t* seq_id;
   const int32_t* pos;
@@ -39,6 +49,7 @@ struct IndexerArgs {
   int64_t E;                // score row extent: max_visible rounded up to 8 (candidate mode: 8 * 2048)
   const int32_t* cand;      // candidate mode: [T][2048] carried block ids, else null
   int32_t group;            // > 1: queries g*group .. g*group+group-1 share a sequence (<= 8)
+  PageTable pages;          // keys and scales are page pools when pages.table is set
 };
 hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream);
 
@@ -81,6 +92,7 @@ struct AttnArgs {
   float* part_o;            // [T * splits][64][512] unnormalised outputs
   float* part_ml;           // [T * splits][64][2] reference (log2 domain) and normaliser
   uint32_t* counters;       // [T]
+  PageTable pages;          // latents are a page pool when pages.table is set
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 // Key splits used for T queries, and the partial slots (T * splits) the largest of them
