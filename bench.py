@@ -14,10 +14,11 @@ A second object times a layer that only indexes: it re-scores the 2048 candidate
 the two-stage pass kept (candidate-bounded indexer, selection inside them, attention).
 A third times a multi-token decode step: 128 sequences x 6 queries (a verified token and
 5 drafted ones) whose indexer streams each sequence's keys once per group. A fourth times
-the headline decode batch with MXFP4 index keys (the 4-bit indexer cache).
+the headline decode batch with MXFP4 index keys (the 4-bit indexer cache), and a fifth its
+indexer, selection and attention on paged stores (64-row pages, block tables).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-prefill] [--no-rescore] [--no-multiquery] [--no-mxfp4]
+                       [--no-prefill] [--no-rescore] [--no-multiquery] [--no-mxfp4] [--no-paged]
                        [--no-cpu-baseline] [--profile]
 """
 from __future__ import annotations
@@ -277,6 +278,60 @@ def run_rescore(torch, d, steps, warmup, profile=False):
     return carried.cpu().numpy(), eager, graph, timer.mean_ms()
 
 
+def paged_copy(torch, d, P, seed=0):
+    """The batch's latents, index keys and e4m3 scales as pools of P-row pages in a shuffled
+    order, with the block table that addresses them."""
+    import sparse_attention_score_amd as S
+    B, cap = d.C.shape[0], d.C.shape[1]
+    assert cap % P == 0
+    per = cap // P
+    ids = torch.from_numpy(np.random.default_rng(seed).permutation(B * per).astype(np.int64)).cuda()
+
+    def pool_of(x):
+        pages = x.reshape((B * per, P) + tuple(x.shape[2:]))
+        pool = torch.empty_like(pages)
+        pool[ids] = pages
+        return pool.reshape((B * per * P,) + tuple(x.shape[2:]))
+
+    table = ids.to(torch.int32).reshape(B, per).contiguous()
+    return S.Cache(latents=pool_of(d.C), window=d.R, idx_keys=pool_of(d.KI),
+                   idx_scales=pool_of(d.KS) if d.KS is not None else None, num_seqs=B,
+                   compressed_cap=cap, block_table=table, page_size=P)
+
+
+def run_paged(torch, d, steps, warmup, P=64, profile=False):
+    """Indexer, selection and attention of the batch on paged stores (eager, HIP events),
+    then the same three launches as graph replays."""
+    import sparse_attention_score_amd as S
+    cache = paged_copy(torch, d, P)
+    torch.cuda.synchronize()
+    fns = [lambda: S.indexer_score(d.plan, d.queries, cache, d.qI, d.w, d.scores, d.block_max),
+           d.select,
+           lambda: S.sparse_attn_fwd(d.plan, d.queries, cache, d.q, d.topk, d.out, d.lse,
+                                     workspace=d.workspace)]
+    warm_up(torch, fns, warmup, 0.0 if profile else 0.5)
+    timer = Timer(torch, ["indexer", "select", "attention"])
+    for _ in range(steps):
+        timer.step(fns)
+    torch.cuda.synchronize()
+    graph = None
+    if not profile:
+        g = capture(torch, fns)
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph = (time.perf_counter() - t0) / steps
+        del g
+    ms = timer.mean_ms()
+    del cache
+    torch.cuda.empty_cache()
+    return graph, ms
+
+
 def cpu_baseline(wl, budget_s=20.0, max_queries=None):
     """The fp64 oracle, as it stands, over the first queries of the batch until the time
     budget is spent (at least one query). Returns queries/s and the sample description."""
@@ -318,6 +373,7 @@ def main():
     ap.add_argument("--no-multiquery", action="store_true")
     ap.add_argument("--mxfp4-workload", default="decode-b128-ctx128k-mxfp4")
     ap.add_argument("--no-mxfp4", action="store_true")
+    ap.add_argument("--no-paged", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--profile", action="store_true", help="timed steps only (for rocprofv3)")
@@ -384,6 +440,16 @@ def main():
                  "hbm_frac": sbytes / sec_per_step / HBM_PEAK,
                  "tokens_per_s": wl.T / sec_per_step},
     }
+    if not args.no_paged:
+        p_graph, pms = run_paged(torch, d, args.steps, args.warmup, 64, args.profile)
+        result["paged"] = {
+            "what": "indexer, selection and attention of the same batch on 64-row pages in shuffled "
+                    "order (block tables)",
+            "ms_per_step": p_graph * 1e3 if p_graph else None, "stage_ms": pms,
+            "indexer_frac": idx_bytes / (pms["indexer"] * 1e-3) / HBM_PEAK,
+            "contiguous_stage_ms": {k: stage_ms[k] for k in ("indexer", "select", "attention")},
+        }
+        log(f"paged: {p_graph * 1e3 if p_graph else float('nan'):.3f} ms (no compressor), stages {pms}")
     if not args.no_rescore:
         carried, r_eager, r_graph, rms = run_rescore(torch, d, args.steps, args.warmup, args.profile)
         rb = rescore_bytes(wl, carried)

@@ -179,6 +179,26 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
 #pragma unroll
     for (int j = 0; j < kTilesPerWave / 4; ++j) scv[j] = scales[min(key0 + 64 * j + lane, n - 1)];
   }
+  // paged mode: page id of the wave's tile `lane` (lanes past the last tile take its page),
+  // read before any tile load since the tile addresses depend on it. The wave's tiles span
+  // at most 16 consecutive table entries, read with uniform addresses ahead of every other
+  // memory operation, so they come through the scalar cache (lgkmcnt, not vmcnt)
+  int pgreg = 0;
+  if constexpr (PAGED) {
+    if (live > 0) {
+      const int32_t* trow = a.pages.table + (int64_t)seq * a.pages.stride;
+      const int lp = a.pages.log2_page;
+      const int e0 = key0 >> lp, elast = (n - 1) >> lp;
+      int ent[kTilesPerWave];
+#pragma unroll
+      for (int j = 0; j < kTilesPerWave; ++j) ent[j] = trow[min(e0 + j, elast)];
+      const int mine = ((key0 + 16 * min(lane, kTilesPerWave - 1)) >> lp) - e0;   // 0 .. 15
+      int v = ent[0];
+#pragma unroll
+      for (int j = 1; j < kTilesPerWave; ++j) v = mine == j ? ent[j] : v;
+      pgreg = (int)min(max((int64_t)v, (int64_t)0), a.pages.num_pages - 1);
+    }
+  }
   const uint32_t lds_q = (uint32_t)(uintptr_t)&sh.q[0];
   const uint32_t lds_w = (uint32_t)(uintptr_t)&sh.w[0];
   if (wg_live) {
@@ -190,13 +210,9 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
     if (CAND && wave == 1 && lane < kDWaves * kTilesPerWave * 2 / 4)   // the group's block ids
       to_lds16(a.cand + (int64_t)t * kCandBlocks + chunk0 / 8 + 4 * lane, (uint32_t)(uintptr_t)&sh.ids[0]);
   }
-  // paged mode: page id of the wave's tile `lane` (the first 16 rows past n repeat row n-1),
-  // read before any tile load (their addresses depend on it); the e4m3 scales follow, each
-  // lane's key in the page of its tile
-  int pgreg = 0;
+  // paged mode: the e4m3 scales, each lane's key in the page of its tile
   if constexpr (PAGED) {
     if (live > 0) {
-      pgreg = (int)page_of(a.pages, seq, min(key0 + 16 * min(lane, kTilesPerWave - 1), n - 1));
       if constexpr (FP8) {
         const float* scales = a.scales;
 #pragma unroll
