@@ -262,14 +262,15 @@ sa_status indexer_score(const sa_plan* plan, const sa_queries* q, const sa_cache
   a.cand = nullptr;
   a.group = q->group > 1 ? q->group : 1;
   a.pages = page_table(c);
-  // paged stores: one key stream per query (the chunk and group kernels read contiguous rows)
+  // paged stores: no group kernel; the chunk kernel needs pages of at least one 64-key stage
   if (a.pages.table) a.group = 1;
   // Queries that share a sequence in one call (a prefill chunk) reuse each key tile
   // across many queries; groups of a multi-token decode step share one key stream per
   // group; independent decode queries each stream their own keys.
   // MXFP4 keys: one key stream per query in every case (no chunk or group kernel yet)
   if (a.mxfp4) a.group = 1;
-  const bool prefill = !a.mxfp4 && !a.pages.table && a.group == 1 && c->num_seqs == 1 && q->T > 1;
+  const bool prefill = !a.mxfp4 && (!a.pages.table || c->page_size >= 64) && a.group == 1 &&
+                       c->num_seqs == 1 && q->T > 1;
   SA_REQUIRE(prefill || (q->T + a.group - 1) / a.group <= 65535, SA_EUNSUPPORTED,
              "T = %lld queries in groups of %d over several sequences: at most 65535 groups per call",
              (long long)q->T, (int)a.group);

@@ -736,7 +736,9 @@ __device__ __forceinline__ int pdim(int hh, int s) { return (2 * s + hh) * 8; }
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer resource, 32-bit data (gfx9 family)
 constexpr uint32_t kDrop = 0x80000000u;  // buffer offset past every extent: store dropped
 
-template <bool FP8>
+// PAGED: keys and scales are page pools of at least kPST rows per page, so each stage of
+// 64 keys lies in one page; the chunk's page ids (at most 64) are read once, one per lane.
+template <bool FP8, bool PAGED>
 __global__ __launch_bounds__(kPThreads, 8 / kPWaves) void indexer_prefill_kernel(IndexerArgs a) {
   constexpr int RB = FP8 ? kIdxDim : 2 * kIdxDim;   // key row bytes in HBM
   __shared__ __attribute__((aligned(16))) PrefillShared sh;
@@ -822,6 +824,36 @@ __global__ __launch_bounds__(kPThreads, 8 / kPWaves) void indexer_prefill_kernel
   const float* scales = FP8 ? a.scales + (int64_t)sq * a.scales_seq_stride + k0 : a.w;
   const __amdgpu_buffer_rsrc_t scrs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(scales), (short)0, FP8 ? (klive - k0) * 4 : 0, kRsrcWord3);
+  // paged: page id of table entry (k0 >> lp) + lane (entries past the live keys repeat the last)
+  int pgl = 0;
+  if constexpr (PAGED) {
+    static_assert(kPChunk / kPST <= 64, "one page id per lane");
+    const int lp = a.pages.log2_page;
+    const int e = min((k0 >> lp) + lane, (klive - 1) >> lp);
+    pgl = (int)min(max((int64_t)a.pages.table[(int64_t)sq * a.pages.stride + e], (int64_t)0), a.pages.num_pages - 1);
+  }
+  // buffer resources of stage S: the chunk's (contiguous) or the stage's page (paged); rows
+  // past klive are outside the resource and read zeros
+  auto stage_rsrc = [&](int S, __amdgpu_buffer_rsrc_t& kr, __amdgpu_buffer_rsrc_t& sr, uint32_t& skoff, uint32_t& ssoff) {
+    if constexpr (PAGED) {
+      const int lp = a.pages.log2_page;
+      const int ks = k0 + S * kPST;
+      const int rows = max(0, min(kPST, klive - ks));
+      const int64_t pg = __builtin_amdgcn_readlane(pgl, min((ks >> lp) - (k0 >> lp), 63));
+      const int64_t row0 = (pg << lp) + (ks & ((1 << lp) - 1));
+      kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(a.keys) + row0 * RB),
+                                             (short)0, rows * RB, kRsrcWord3);
+      sr = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(FP8 ? a.scales + row0 : a.w), (short)0,
+                                             FP8 ? rows * 4 : 0, kRsrcWord3);
+      skoff = 0;
+      ssoff = 0;
+    } else {
+      kr = krs;
+      sr = scrs;
+      skoff = (uint32_t)(S * kPST * RB);
+      ssoff = (uint32_t)(S * kPST * 4);
+    }
+  };
 
   // staging, one stage (64 keys) at a time: 16-byte chunk q = tid + kPThreads*h of a stage
   // (h < CPT) is row q / CPR, chunk q % CPR: each wave loads whole rows (contiguous 1 KiB
@@ -842,10 +874,13 @@ __global__ __launch_bounds__(kPThreads, 8 / kPWaves) void indexer_prefill_kernel
     float scale;
   };
   auto fetch = [&](Stage& st, int S) {
+    __amdgpu_buffer_rsrc_t kr, sr;
+    uint32_t skoff, ssoff;
+    stage_rsrc(S, kr, sr, skoff, ssoff);
 #pragma unroll
     for (int h = 0; h < CPT; ++h)
-      st.v[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, kvoff[h] + S * kPST * RB, 0, 0));
-    if (FP8) st.scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(scrs, scoff + S * kPST * 4, 0, 0));
+      st.v[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, kvoff[h] + skoff, 0, 0));
+    if (FP8) st.scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sr, scoff + ssoff, 0, 0));
   };
   auto commit = [&](const Stage& st, int buf) {
 #pragma unroll
@@ -1012,10 +1047,16 @@ hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream
     // blockIdx.x (key chunk) varies fastest, so with a multiple of 8 chunks every XCD
     // keeps the same chunks and their keys stay in its L2.
     dim3 grid((unsigned)((a.E + kPChunk - 1) / kPChunk), (unsigned)((a.T + kQPerWG - 1) / kQPerWG));
-    if (a.fp8)
-      hipLaunchKernelGGL(indexer_prefill_kernel<true>, grid, dim3(kPThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL(indexer_prefill_kernel<false>, grid, dim3(kPThreads), 0, stream, a);
+    if (a.pages.table) {
+      if (a.fp8)
+        hipLaunchKernelGGL((indexer_prefill_kernel<true, true>), grid, dim3(kPThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL((indexer_prefill_kernel<false, true>), grid, dim3(kPThreads), 0, stream, a);
+    } else if (a.fp8) {
+      hipLaunchKernelGGL((indexer_prefill_kernel<true, false>), grid, dim3(kPThreads), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((indexer_prefill_kernel<false, false>), grid, dim3(kPThreads), 0, stream, a);
+    }
   }
   return hipGetLastError();
 }

@@ -89,7 +89,8 @@ def test_paged_decode_matches_contiguous(kd, P):
 
 
 def test_paged_prefill_chunk_runs_per_query_and_matches_oracle():
-    # one sequence, 40 queries: with paged stores the indexer runs one key stream per query
+    # one sequence, 40 queries on 32-row pages: below the chunk kernel's 64-row stage, so
+    # the indexer runs one key stream per query
     wl = W.make_prefill(T=40, offset=5000, ratio=1, key_dtype="bf16", name="paged-prefill", seed=52)
     d = _batch(wl)
     sc, bm, topk, out, lse = _run(d, _paged_cache(d, 32, seed=7))
@@ -100,6 +101,17 @@ def test_paged_prefill_chunk_runs_per_query_and_matches_oracle():
     for t in range(wl.T):
         check_index_row(topk[t], res.idx[t], res.scores[t], 512, f"t={t}")
         check_outputs(o[t], res2.o[t], f"t={t} out")
+
+
+@pytest.mark.parametrize("kd,P", [("bf16", 64), ("fp8", 256)])
+def test_paged_prefill_chunk_kernel_matches_contiguous(kd, P):
+    # pages of at least 64 rows: the chunk kernel reads each 64-key stage from its page;
+    # 300 queries over 20000+ keys (several chunks and stages, a ragged end)
+    wl = W.make_prefill(T=300, offset=20000, ratio=1, key_dtype=kd, name=f"paged-chunk-{kd}", seed=54)
+    d = _batch(wl)
+    res_c = _run(d, d.cache)
+    res_p = _run(d, _paged_cache(d, P, seed=3))
+    _same(d, res_p, res_c)
 
 
 def test_paged_rejects():
