@@ -107,6 +107,15 @@ typedef struct sa_queries {
                               then streams each group's keys once for all its queries. A
                               query whose seq_id differs from its group's first query gets
                               -inf scores. Ignored by the other calls. */
+  const int32_t* runs;     /* host, optional (NULL: none): a ragged batch as num_runs runs of
+                              consecutive queries, runs[i] >= 1 queries each, summing to T;
+                              the queries of a run read one sequence (a prefill chunk, a
+                              decode step with drafted tokens, or one decode query).
+                              indexer_score then launches the chunk kernel for runs of 9 or
+                              more queries, the group kernel for neighbouring runs of one
+                              length in 2..8, and one key stream per query for the rest
+                              (and "group" is ignored). Ignored by the other calls. */
+  int32_t num_runs;
 } sa_queries;
 
 /* Per-sequence stores, all device memory. */

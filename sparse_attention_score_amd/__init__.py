@@ -40,7 +40,8 @@ class sa_params(ctypes.Structure):
 
 class sa_queries(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("seq_id", ctypes.c_void_p), ("pos", ctypes.c_void_p),
-                ("max_visible", ctypes.c_int64), ("group", ctypes.c_int32)]
+                ("max_visible", ctypes.c_int64), ("group", ctypes.c_int32),
+                ("runs", ctypes.c_void_p), ("num_runs", ctypes.c_int32)]
 
 
 class sa_cache(ctypes.Structure):
@@ -162,12 +163,18 @@ class Queries:
     """sa_queries from device int32 tensors seq_id[T], pos[T], a host max_visible and the
     number of consecutive queries that share a sequence (group; 0 = none)."""
 
-    def __init__(self, seq_id: torch.Tensor, pos: torch.Tensor, max_visible: int, group: int = 0):
+    def __init__(self, seq_id: torch.Tensor, pos: torch.Tensor, max_visible: int, group: int = 0,
+                 runs=None):
         _need(seq_id, "seq_id", torch.int32)
         _need(pos, "pos", torch.int32)
-        self._keep = (seq_id, pos)
         self.c = sa_queries(T=seq_id.shape[0], seq_id=seq_id.data_ptr(), pos=pos.data_ptr(),
                             max_visible=int(max_visible), group=int(group))
+        host_runs = None
+        if runs is not None:   # host run lengths of a ragged batch
+            host_runs = (ctypes.c_int32 * len(runs))(*[int(r) for r in runs])
+            self.c.runs = ctypes.cast(host_runs, ctypes.c_void_p)
+            self.c.num_runs = len(runs)
+        self._keep = (seq_id, pos, host_runs)
 
     @property
     def T(self) -> int:

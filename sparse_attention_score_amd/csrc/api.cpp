@@ -95,6 +95,16 @@ sa_status check_queries(const sa_plan* plan, const sa_queries* q) {
              (long long)q->max_visible, (long long)plan->p.max_compressed);
   SA_REQUIRE(q->group >= 0 && q->group <= kMaxGroup, SA_EUNSUPPORTED,
              "queries->group = %d outside [0, %d]", (int)q->group, kMaxGroup);
+  if (q->runs) {
+    SA_REQUIRE(q->num_runs >= 1, SA_EINVAL, "queries->num_runs = %d < 1", (int)q->num_runs);
+    int64_t sum = 0;
+    for (int32_t i = 0; i < q->num_runs; ++i) {
+      SA_REQUIRE(q->runs[i] >= 1, SA_EINVAL, "queries->runs[%d] = %d < 1", (int)i, (int)q->runs[i]);
+      sum += q->runs[i];
+    }
+    SA_REQUIRE(sum == q->T, SA_EINVAL, "queries->runs sum to %lld, not T = %lld", (long long)sum,
+               (long long)q->T);
+  }
   return SA_OK;
 }
 
@@ -217,6 +227,59 @@ sa_status sparse_attn_plan(const sa_params* p, sa_plan** plan, size_t* workspace
 
 void sparse_attn_plan_destroy(sa_plan* plan) { delete plan; }
 
+// A ragged batch (sa_queries.runs): one launch per class of run over each contiguous
+// query range of that class. Runs of 9+ queries go to the chunk kernel (one per run),
+// neighbouring runs of one length in 2..8 to the group kernel, single queries (and runs the
+// store layout keeps off those kernels) to the per-query kernel.
+sa_status indexer_runs(const sa::IndexerArgs& a, const sa_queries* q, const sa_cache* c, const void* q_idx,
+                       const float* w, hipStream_t stream) {
+  const bool chunk_ok = !a.mxfp4 && (!a.pages.table || c->page_size >= 64);
+  const bool group_ok = !a.mxfp4 && !a.pages.table;
+  auto cls = [&](int32_t len) { return len >= 9 && chunk_ok ? 2 : (len >= 2 && len <= 8 && group_ok ? 1 : 0); };
+  // first pass: every launch's grid fits (per-query and group launches index queries in y)
+  {
+    int64_t t0 = 0;
+    for (int32_t i = 0; i < q->num_runs;) {
+      const int k = cls(q->runs[i]);
+      int32_t j = i;
+      int64_t len = 0;
+      while (j < q->num_runs && cls(q->runs[j]) == k && (k != 1 || q->runs[j] == q->runs[i])) len += q->runs[j++];
+      if (k == 2) j = i + 1, len = q->runs[i];
+      const int64_t rows_y = k == 1 ? len / q->runs[i] : len;
+      SA_REQUIRE(k == 2 || rows_y <= 65535, SA_EUNSUPPORTED,
+                 "a range of %lld queries on the per-query or group kernel: at most 65535 per launch", (long long)len);
+      t0 += len;
+      i = j;
+    }
+  }
+  int64_t t0 = 0;
+  for (int32_t i = 0; i < q->num_runs;) {
+    const int k = cls(q->runs[i]);
+    int32_t j = i;
+    int64_t len = 0;
+    if (k == 2) {
+      len = q->runs[i];
+      j = i + 1;
+    } else {
+      while (j < q->num_runs && cls(q->runs[j]) == k && (k != 1 || q->runs[j] == q->runs[i])) len += q->runs[j++];
+    }
+    sa::IndexerArgs b = a;
+    b.seq_id = a.seq_id + t0;
+    b.pos = a.pos + t0;
+    b.T = len;
+    b.q_idx = static_cast<const uint16_t*>(q_idx) + t0 * 16 * 128;
+    b.w = w + t0 * 16;
+    b.scores = a.scores + t0 * a.ld_scores;
+    b.block_max = a.block_max ? a.block_max + t0 * a.ld_block_max : nullptr;
+    b.group = k == 1 ? q->runs[i] : 1;
+    const hipError_t e = sa::launch_indexer(b, k == 2, stream);
+    if (e != hipSuccess) return hip_status(e, "indexer_score launch");
+    t0 += len;
+    i = j;
+  }
+  return ok();
+}
+
 sa_status indexer_score(const sa_plan* plan, const sa_queries* q, const sa_cache* c,
                         const void* q_idx, const float* w, float* scores, int64_t ld_scores,
                         float* block_max, int64_t ld_block_max, void* stream) {
@@ -269,6 +332,7 @@ sa_status indexer_score(const sa_plan* plan, const sa_queries* q, const sa_cache
   // group; independent decode queries each stream their own keys.
   // MXFP4 keys: one key stream per query in every case (no chunk or group kernel yet)
   if (a.mxfp4) a.group = 1;
+  if (q->runs) return indexer_runs(a, q, c, q_idx, w, (hipStream_t)stream);
   const bool prefill = !a.mxfp4 && (!a.pages.table || c->page_size >= 64) && a.group == 1 &&
                        c->num_seqs == 1 && q->T > 1;
   SA_REQUIRE(prefill || (q->T + a.group - 1) / a.group <= 65535, SA_EUNSUPPORTED,

@@ -33,7 +33,8 @@ class DeviceBatch:
         self.seq = torch.from_numpy(wl.seq.astype(np.int32)).to(dev)
         self.pos = torch.from_numpy(wl.pos.astype(np.int32)).to(dev)
         self.max_visible = int(((wl.pos.astype(np.int64) + 1) // wl.ratio).max())
-        self.queries = Queries(self.seq, self.pos, self.max_visible, getattr(wl, "group", 0))
+        self.queries = Queries(self.seq, self.pos, self.max_visible, getattr(wl, "group", 0),
+                               getattr(wl, "runs", None))
         self.q = to_device_bf16(wl.q, dev)
         self.qI = to_device_bf16(wl.qI, dev)
         self.w = torch.from_numpy(wl.w).to(dev)

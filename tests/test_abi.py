@@ -159,6 +159,18 @@ def test_mxfp4_rejects(case):
     assert _indexer(p, q, c) == S.SA_EINVAL, S.lib.sparse_attn_last_error()
 
 
+@pytest.mark.parametrize("runs", [[1, 2], [4, 0], [5]])
+def test_indexer_rejects_bad_runs(runs):
+    # T = 4: runs must be >= 1 each and sum to T
+    p = _plan()
+    q, c = _q(), _c()
+    arr = (ctypes.c_int32 * len(runs))(*runs)
+    q.runs = ctypes.cast(arr, ctypes.c_void_p)
+    q.num_runs = len(runs)
+    assert _indexer(p, q, c) == S.SA_EINVAL
+    assert b"runs" in S.lib.sparse_attn_last_error()
+
+
 def test_select_rejects():
     p = _plan()
     q = _q()

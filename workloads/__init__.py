@@ -177,6 +177,7 @@ class Workload:
     seed: int = 0
     meta: dict = field(default_factory=dict)
     group: int = 0       # consecutive queries that share a sequence (multi-token decode)
+    runs: Optional[list] = None   # ragged batch: lengths of the runs of one sequence each
 
     def visible(self) -> np.ndarray:
         return (self.pos.astype(np.int64) + 1) // self.ratio
@@ -276,6 +277,41 @@ def make_decode_mq(B: int, n_raw, G: int = 6, ratio: int = 2, key_dtype: str = "
     return Workload(name=name, kind="decode", ratio=ratio, key_dtype=key_dtype, B=B, T=T,
                     nc_cap=nc_cap, wcap=wcap, seq=seq, pos=pos, q=q, qI=qI, w=w, C=C, KI=KI,
                     KS=KS, R=R, seed=seed, group=G)
+
+
+def make_ragged(n_raw, lengths, ratio: int = 2, key_dtype: str = "bf16", seed: int = 0,
+                name: str = "ragged") -> Workload:
+    """A ragged batch: sequence b contributes lengths[b] consecutive queries at raw positions
+    n_raw[b] - lengths[b] .. n_raw[b] - 1 (a prefill chunk, a decode step with drafted tokens,
+    or one decode query), in sequence order. Their latents, keys and window rows are already
+    in the stores; the window store holds 128 + max(lengths) rows."""
+    n_raw = np.asarray(n_raw, dtype=np.int64)
+    lengths = np.asarray(lengths, dtype=np.int64)
+    B = len(n_raw)
+    assert len(lengths) == B and np.all(lengths >= 1) and np.all(n_raw >= lengths)
+    T = int(lengths.sum())
+    seq = np.repeat(np.arange(B, dtype=np.int32), lengths)
+    pos = np.concatenate([n_raw[b] - lengths[b] + np.arange(lengths[b]) for b in range(B)]).astype(np.int32)
+    nc_cap = int(max(1, ((pos.astype(np.int64) + 1) // ratio).max()))
+    wcap = WINDOW + int(lengths.max())
+    q = np.empty((T, HEADS, DIM), np.uint16)
+    qI = np.empty((T, IDX_HEADS, IDX_DIM), np.uint16)
+    w = np.empty((T, IDX_HEADS), np.float32)
+    C = np.empty((B, nc_cap, DIM), np.uint16)
+    R = np.empty((B, wcap, DIM), np.uint16)
+    t0 = 0
+    for b in range(B):
+        L = int(lengths[b])
+        q[t0:t0 + L] = normal_bf16(seed, "q-mq", b, (L, HEADS, DIM))
+        qI[t0:t0 + L] = normal_bf16(seed, "qI-mq", b, (L, IDX_HEADS, IDX_DIM))
+        w[t0:t0 + L] = uniform_f32(seed, "w-mq", b, (L, IDX_HEADS))
+        C[b] = normal_bf16(seed, "C", b, (nc_cap, DIM))
+        R[b] = normal_bf16(seed, "R", b, (wcap, DIM))
+        t0 += L
+    KI, KS = _keys(seed, key_dtype, B, nc_cap)
+    return Workload(name=name, kind="decode", ratio=ratio, key_dtype=key_dtype, B=B, T=T,
+                    nc_cap=nc_cap, wcap=wcap, seq=seq, pos=pos, q=q, qI=qI, w=w, C=C, KI=KI,
+                    KS=KS, R=R, seed=seed, runs=[int(x) for x in lengths])
 
 
 def make_prefill(T: int, offset: int, ratio: int = 1, key_dtype: str = "bf16", seed: int = 0,
