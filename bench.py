@@ -15,10 +15,13 @@ the two-stage pass kept (candidate-bounded indexer, selection inside them, atten
 A third times a multi-token decode step: 128 sequences x 6 queries (a verified token and
 5 drafted ones) whose indexer streams each sequence's keys once per group. A fourth times
 the headline decode batch with MXFP4 index keys (the 4-bit indexer cache), and a fifth its
-indexer, selection and attention on paged stores (64-row pages, block tables).
+indexer, selection and attention on paged stores (64-row pages, block tables). A sixth
+times a ragged serving batch (prefill chunks, drafted decode steps and single decode queries
+in one call).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-prefill] [--no-rescore] [--no-multiquery] [--no-mxfp4] [--no-paged]
+                       [--no-ragged]
                        [--no-cpu-baseline] [--profile]
 """
 from __future__ import annotations
@@ -374,6 +377,8 @@ def main():
     ap.add_argument("--mxfp4-workload", default="decode-b128-ctx128k-mxfp4")
     ap.add_argument("--no-mxfp4", action="store_true")
     ap.add_argument("--no-paged", action="store_true")
+    ap.add_argument("--ragged-workload", default="ragged-2x1024+64+16x6-ctx128k-fp8")
+    ap.add_argument("--no-ragged", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--profile", action="store_true", help="timed steps only (for rocprofv3)")
@@ -524,6 +529,32 @@ def main():
         }
         log(f"MXFP4-key decode: {x_s * 1e3:.3f} ms/step, stages {xms}")
         del dx, wx
+        torch.cuda.empty_cache()
+
+    if not args.no_ragged and not args.profile:
+        import sparse_attention_score_amd as S
+        t0 = time.perf_counter()
+        wr = W.make(args.ragged_workload)
+        dr = DeviceBatch(wr)
+        torch.cuda.synchronize()
+        log(f"ragged inputs ready in {time.perf_counter() - t0:.1f}s")
+        r_eager, rms2 = run_batch(torch, dr, max(3, args.steps // 2), args.warmup)
+        r_s, _ = run_graph(torch, dr, max(3, args.steps // 2))
+        flat = S.Queries(dr.seq, dr.pos, dr.max_visible)   # the same batch as independent queries
+        flat_idx = lambda: S.indexer_score(dr.plan, flat, dr.cache, dr.qI, dr.w, dr.scores, dr.block_max)
+        warm_up(torch, [flat_idx], 2, 0.2)
+        ft = Timer(torch, ["indexer"])
+        for _ in range(max(3, args.steps // 4)):
+            ft.step([flat_idx])
+        torch.cuda.synchronize()
+        result["ragged"] = {
+            "workload": args.ragged_workload, "queries": int(wr.T), "runs": len(wr.runs),
+            "ms_per_step": r_s * 1e3, "queries_per_s": wr.T / r_s, "eager_ms_per_step": r_eager * 1e3,
+            "stage_ms": rms2,
+            "indexer_ms_as_independent_queries": ft.mean_ms()["indexer"],
+        }
+        log(f"ragged: {r_s * 1e3:.3f} ms/step, stages {rms2}, indexer without runs {ft.mean_ms()['indexer']:.3f} ms")
+        del dr, wr
         torch.cuda.empty_cache()
 
     if not args.no_prefill and not args.profile:

@@ -365,6 +365,11 @@ MORE_WORKLOADS = {
                                         key_dtype="fp8"),
     # the headline decode batch with the 4-bit indexer cache (MXFP4 keys)
     "decode-b128-ctx128k-mxfp4": dict(kind="decode", B=128, n_raw=131072, ratio=2, key_dtype="mxfp4"),
+    # a ragged serving batch at 128K context: two 1024-query prefill chunks, 64 single decode
+    # queries and 16 decode steps with 5 drafted tokens (2208 queries, 82 sequences)
+    "ragged-2x1024+64+16x6-ctx128k-fp8": dict(kind="ragged", n_raw=[131072] * 82,
+                                              lengths=[1024, 1024] + [1] * 64 + [6] * 16,
+                                              ratio=2, key_dtype="fp8"),
 }
 
 
@@ -375,4 +380,6 @@ def make(name: str, seed: int = 0) -> Workload:
         return make_decode(name=name, seed=seed, **cfg)
     if kind == "decode_mq":
         return make_decode_mq(name=name, seed=seed, **cfg)
+    if kind == "ragged":
+        return make_ragged(name=name, seed=seed, **cfg)
     return make_prefill(name=name, seed=seed, **cfg)
