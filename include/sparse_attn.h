@@ -142,10 +142,10 @@ typedef struct sa_cache {
    * page_size, row r % page_size; the *_seq_stride fields are ignored), and compressed
    * position j of sequence s is pool row block_table[s * block_table_stride + j /
    * page_size] * page_size + j % page_size. The window stays per sequence. Page ids
-   * outside [0, num_pages) are clamped. Supported by indexer_score (bf16 and e4m3 keys;
-   * a one-sequence chunk uses the chunk kernel when pages hold at least 64 rows, every
-   * other batch one key stream per query) and sparse_attn_fwd; indexer_score_cand and
-   * MXFP4 keys return SA_EUNSUPPORTED. */
+   * outside [0, num_pages) are clamped. Supported by indexer_score (bf16 and e4m3 keys,
+   * every kernel; a chunk runs on the chunk kernel only when pages hold at least 64 rows,
+   * else one key stream per query) and sparse_attn_fwd; indexer_score_cand and MXFP4 keys
+   * return SA_EUNSUPPORTED. */
   const int32_t* block_table;    /* device int32 [num_seqs][block_table_stride] or NULL */
   int64_t block_table_stride;    /* >= ceil(compressed_cap / page_size) */
   int32_t page_size;             /* power of two in [16, 2^20] */

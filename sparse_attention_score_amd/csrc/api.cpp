@@ -234,7 +234,7 @@ void sparse_attn_plan_destroy(sa_plan* plan) { delete plan; }
 sa_status indexer_runs(const sa::IndexerArgs& a, const sa_queries* q, const sa_cache* c, const void* q_idx,
                        const float* w, hipStream_t stream) {
   const bool chunk_ok = !a.mxfp4 && (!a.pages.table || c->page_size >= 64);
-  const bool group_ok = !a.mxfp4 && !a.pages.table;
+  const bool group_ok = !a.mxfp4;
   auto cls = [&](int32_t len) { return len >= 9 && chunk_ok ? 2 : (len >= 2 && len <= 8 && group_ok ? 1 : 0); };
   // first pass: every launch's grid fits (per-query and group launches index queries in y)
   {
@@ -325,8 +325,7 @@ sa_status indexer_score(const sa_plan* plan, const sa_queries* q, const sa_cache
   a.cand = nullptr;
   a.group = q->group > 1 ? q->group : 1;
   a.pages = page_table(c);
-  // paged stores: no group kernel; the chunk kernel needs pages of at least one 64-key stage
-  if (a.pages.table) a.group = 1;
+  // paged stores: the chunk kernel needs pages of at least one 64-key stage
   // Queries that share a sequence in one call (a prefill chunk) reuse each key tile
   // across many queries; groups of a multi-token decode step share one key stream per
   // group; independent decode queries each stream their own keys.

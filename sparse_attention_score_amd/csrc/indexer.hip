@@ -521,7 +521,9 @@ constexpr int group_tpw() { return G <= 6 ? 32 : 16; }
 template <int G>
 constexpr int group_keys_per_wg() { return kDWaves * group_tpw<G>() * 16; }
 
-template <bool FP8, int G>
+// PAGED: keys and e4m3 scales are page pools (pages of 16+ rows); each wave reads the page
+// ids of its tiles (one per lane) ahead of its other loads.
+template <bool FP8, int G, bool PAGED>
 __global__ __launch_bounds__(kDThreads, 2) void indexer_group_kernel(IndexerArgs a) {
   using DT = DecodeTile<FP8>;
   constexpr int RB = DT::RB, TB = DT::TB, NK = DT::NK, D = DT::D;
@@ -546,7 +548,15 @@ __global__ __launch_bounds__(kDThreads, 2) void indexer_group_kernel(IndexerArgs
   const int ntiles = key0 < E ? min(TPW, (E - key0 + 15) >> 4) : 0;
   const int live = key0 < nmax ? min(TPW, (nmax - key0 + 15) >> 4) : 0;
   const int sq = nmax > 0 ? seq : 0;   // nmax > 0 implies a valid sequence
-  const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys) + (int64_t)sq * a.keys_seq_stride * (FP8 ? 1 : 2);
+  const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys) +
+                        (PAGED ? 0 : (int64_t)sq * a.keys_seq_stride * (FP8 ? 1 : 2));
+  // paged: page id of the wave's tile `lane` (lanes past the last live tile take its page)
+  int pgreg = 0;
+  if constexpr (PAGED) {
+    static_assert(TPW <= 64, "one tile per lane");
+    if (live > 0)
+      pgreg = (int)page_of(a.pages, sq, min(key0 + 16 * min(lane, TPW - 1), nmax - 1));
+  }
 
   // Head weights, e4m3 row scales (4 consecutive keys per lane per 256) and the A operands, in this
   // order, before the first ring loads: the compiler waits for the A operands at the first
@@ -562,11 +572,15 @@ __global__ __launch_bounds__(kDThreads, 2) void indexer_group_kernel(IndexerArgs
       for (int i = 0; i < 4; ++i) wq[j][i] = a.w[(int64_t)tq * kIdxHeads + 4 * g + i];
     }
     if constexpr (FP8) {
-      const float* scales = a.scales + (int64_t)sq * a.scales_seq_stride;
+      const float* scales = a.scales + (PAGED ? 0 : (int64_t)sq * a.scales_seq_stride);
 #pragma unroll
       for (int k2 = 0; k2 < TPW / 16; ++k2)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sv[k2][e] = scales[min(key0 + 256 * k2 + 4 * lane + e, nmax - 1)];
+        for (int e = 0; e < 4; ++e) {
+          const int x = min(key0 + 256 * k2 + 4 * lane + e, nmax - 1);
+          if constexpr (PAGED) sv[k2][e] = scales[pool_row(a.pages, __shfl(pgreg, (x - key0) >> 4), x)];
+          else sv[k2][e] = scales[x];
+        }
     }
 #pragma unroll
     for (int j = 0; j < G; ++j) {
@@ -588,7 +602,7 @@ __global__ __launch_bounds__(kDThreads, 2) void indexer_group_kernel(IndexerArgs
   const uint32_t ring0 = (uint32_t)(uintptr_t)&ring[wave][0];
   auto issue = [&](int i, bool after_reads) {
     const int k = key0 + 16 * i;
-    const uint8_t* tb = keys + (int64_t)k * RB;
+    const uint8_t* tb = keys + (PAGED ? pool_row(a.pages, __builtin_amdgcn_readlane(pgreg, i), k) : (int64_t)k) * RB;
     const int last = nmax - 1 - k;   // rows past the group's last key repeat that row
     const uint32_t lds = ring0 + (uint32_t)((i & (D - 1)) * TB);
 #pragma unroll
@@ -1007,10 +1021,16 @@ template <int G>
 void launch_group(const IndexerArgs& a, hipStream_t stream) {
   constexpr int KW = group_keys_per_wg<G>();
   dim3 grid((unsigned)((a.E + KW - 1) / KW), (unsigned)((a.T + a.group - 1) / a.group));
-  if (a.fp8)
-    hipLaunchKernelGGL((indexer_group_kernel<true, G>), grid, dim3(kDThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((indexer_group_kernel<false, G>), grid, dim3(kDThreads), 0, stream, a);
+  if (a.pages.table) {
+    if (a.fp8)
+      hipLaunchKernelGGL((indexer_group_kernel<true, G, true>), grid, dim3(kDThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((indexer_group_kernel<false, G, true>), grid, dim3(kDThreads), 0, stream, a);
+  } else if (a.fp8) {
+    hipLaunchKernelGGL((indexer_group_kernel<true, G, false>), grid, dim3(kDThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((indexer_group_kernel<false, G, false>), grid, dim3(kDThreads), 0, stream, a);
+  }
 }
 
 }  // namespace

@@ -114,6 +114,22 @@ def test_paged_prefill_chunk_kernel_matches_contiguous(kd, P):
     _same(d, res_p, res_c)
 
 
+@pytest.mark.parametrize("kind", ["mq", "ragged"])
+def test_paged_group_and_ragged_match_contiguous(kind):
+    # the group kernel (6-query draft steps) and a ragged batch (chunk, group and per-query
+    # launches from one call) on 64-row pages
+    if kind == "mq":
+        wl = W.make_decode_mq(B=3, n_raw=[3001, 40006, 700], G=6, ratio=2, key_dtype="fp8",
+                              name="paged-mq", seed=55)
+    else:
+        wl = W.make_ragged([9000, 3001, 4000, 5000, 700], [20, 1, 6, 6, 1], ratio=2, key_dtype="bf16",
+                           name="paged-ragged", seed=56)
+    d = _batch(wl)
+    res_c = _run(d, d.cache)
+    res_p = _run(d, _paged_cache(d, 64, seed=5))
+    _same(d, res_p, res_c)
+
+
 def test_paged_rejects():
     wl = W.make_decode(B=2, n_raw=300, ratio=2, key_dtype="fp8", name="paged-args",
                        with_compress=False, seed=53)
