@@ -191,6 +191,64 @@ sa::QueryMeta meta(const sa_plan* plan, const sa_queries* q, int64_t num_seqs, i
 
 int64_t round8(int64_t v) { return (v + 7) / 8 * 8; }
 
+// A ragged batch (sa_queries.runs): one launch per class of run over each contiguous
+// query range of that class. Runs of 9+ queries go to the chunk kernel (one launch per
+// run), neighbouring runs of one length in 2..8 to the group kernel, single queries (and
+// runs the store layout keeps off those kernels) to the per-query kernel. The cursor walks
+// the runs without allocating.
+struct RunLaunch {
+  int64_t t0, len;
+  int kind;       // 0 per query, 1 group, 2 chunk
+  int32_t group;  // queries per group (kind 1)
+};
+
+struct RunCursor {
+  const sa_queries* q;
+  bool chunk_ok, group_ok;
+  int32_t i = 0;
+  int64_t t0 = 0;
+  int cls(int32_t len) const {
+    return len >= 9 && chunk_ok ? 2 : (len >= 2 && len <= 8 && group_ok ? 1 : 0);
+  }
+  bool next(RunLaunch& r) {
+    if (i >= q->num_runs) return false;
+    const int k = cls(q->runs[i]);
+    int32_t j = i + 1;
+    int64_t len = q->runs[i];
+    if (k != 2)
+      while (j < q->num_runs && cls(q->runs[j]) == k && (k != 1 || q->runs[j] == q->runs[i])) len += q->runs[j++];
+    r = RunLaunch{t0, len, k, k == 1 ? q->runs[i] : 1};
+    t0 += len;
+    i = j;
+    return true;
+  }
+};
+
+sa_status indexer_runs(const sa::IndexerArgs& a, const sa_queries* q, const sa_cache* c, const void* q_idx,
+                       const float* w, hipStream_t stream) {
+  const bool chunk_ok = !a.mxfp4 && (!a.pages.table || c->page_size >= 64), group_ok = !a.mxfp4;
+  RunLaunch r;
+  // per-query and group launches index queries in grid y
+  for (RunCursor cur{q, chunk_ok, group_ok}; cur.next(r);)
+    SA_REQUIRE(r.kind == 2 || r.len / r.group <= 65535, SA_EUNSUPPORTED,
+               "a range of %lld queries on the per-query or group kernel: at most 65535 per launch",
+               (long long)r.len);
+  for (RunCursor cur{q, chunk_ok, group_ok}; cur.next(r);) {
+    sa::IndexerArgs b = a;
+    b.seq_id = a.seq_id + r.t0;
+    b.pos = a.pos + r.t0;
+    b.T = r.len;
+    b.q_idx = static_cast<const uint16_t*>(q_idx) + r.t0 * 16 * 128;
+    b.w = w + r.t0 * 16;
+    b.scores = a.scores + r.t0 * a.ld_scores;
+    b.block_max = a.block_max ? a.block_max + r.t0 * a.ld_block_max : nullptr;
+    b.group = r.group;
+    const hipError_t e = sa::launch_indexer(b, r.kind == 2, stream);
+    if (e != hipSuccess) return hip_status(e, "indexer_score launch");
+  }
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -226,59 +284,6 @@ sa_status sparse_attn_plan(const sa_params* p, sa_plan** plan, size_t* workspace
 }
 
 void sparse_attn_plan_destroy(sa_plan* plan) { delete plan; }
-
-// A ragged batch (sa_queries.runs): one launch per class of run over each contiguous
-// query range of that class. Runs of 9+ queries go to the chunk kernel (one per run),
-// neighbouring runs of one length in 2..8 to the group kernel, single queries (and runs the
-// store layout keeps off those kernels) to the per-query kernel.
-sa_status indexer_runs(const sa::IndexerArgs& a, const sa_queries* q, const sa_cache* c, const void* q_idx,
-                       const float* w, hipStream_t stream) {
-  const bool chunk_ok = !a.mxfp4 && (!a.pages.table || c->page_size >= 64);
-  const bool group_ok = !a.mxfp4;
-  auto cls = [&](int32_t len) { return len >= 9 && chunk_ok ? 2 : (len >= 2 && len <= 8 && group_ok ? 1 : 0); };
-  // first pass: every launch's grid fits (per-query and group launches index queries in y)
-  {
-    int64_t t0 = 0;
-    for (int32_t i = 0; i < q->num_runs;) {
-      const int k = cls(q->runs[i]);
-      int32_t j = i;
-      int64_t len = 0;
-      while (j < q->num_runs && cls(q->runs[j]) == k && (k != 1 || q->runs[j] == q->runs[i])) len += q->runs[j++];
-      if (k == 2) j = i + 1, len = q->runs[i];
-      const int64_t rows_y = k == 1 ? len / q->runs[i] : len;
-      SA_REQUIRE(k == 2 || rows_y <= 65535, SA_EUNSUPPORTED,
-                 "a range of %lld queries on the per-query or group kernel: at most 65535 per launch", (long long)len);
-      t0 += len;
-      i = j;
-    }
-  }
-  int64_t t0 = 0;
-  for (int32_t i = 0; i < q->num_runs;) {
-    const int k = cls(q->runs[i]);
-    int32_t j = i;
-    int64_t len = 0;
-    if (k == 2) {
-      len = q->runs[i];
-      j = i + 1;
-    } else {
-      while (j < q->num_runs && cls(q->runs[j]) == k && (k != 1 || q->runs[j] == q->runs[i])) len += q->runs[j++];
-    }
-    sa::IndexerArgs b = a;
-    b.seq_id = a.seq_id + t0;
-    b.pos = a.pos + t0;
-    b.T = len;
-    b.q_idx = static_cast<const uint16_t*>(q_idx) + t0 * 16 * 128;
-    b.w = w + t0 * 16;
-    b.scores = a.scores + t0 * a.ld_scores;
-    b.block_max = a.block_max ? a.block_max + t0 * a.ld_block_max : nullptr;
-    b.group = k == 1 ? q->runs[i] : 1;
-    const hipError_t e = sa::launch_indexer(b, k == 2, stream);
-    if (e != hipSuccess) return hip_status(e, "indexer_score launch");
-    t0 += len;
-    i = j;
-  }
-  return ok();
-}
 
 sa_status indexer_score(const sa_plan* plan, const sa_queries* q, const sa_cache* c,
                         const void* q_idx, const float* w, float* scores, int64_t ld_scores,

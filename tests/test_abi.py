@@ -31,6 +31,18 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
+def test_library_exports_only_declared_symbols():
+    import shutil
+    import subprocess
+    if shutil.which("nm") is None:
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    funcs = {ln.split()[-1] for ln in out.splitlines() if len(ln.split()) == 3 and ln.split()[1] == "T"}
+    funcs = {f for f in funcs if not f.startswith("_")}
+    assert funcs == set(_declared()), funcs ^ set(_declared())
+
+
 def _plan(**kw):
     args = dict(ratio=2, key_dtype="bf16", max_queries=8, max_compressed=4096)
     args.update(kw)
