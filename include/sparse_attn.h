@@ -67,9 +67,10 @@ typedef enum sa_key_dtype {
                            indexer_kv_dtype of the recipe's MI355X configurations):
                            [.][64] bytes of FP4 E2M1, element 2i in the low nibble of
                            byte i, plus [.][4] E8M0 scales, scale b for elements
-                           32b .. 32b+31. Key = 2^(scale-127) * element. Scored per
-                           query (indexer_score ignores queries->group and the chunk
-                           kernel for these keys); not supported by indexer_score_cand */
+                           32b .. 32b+31. Key = 2^(scale-127) * element. indexer_score
+                           runs the chunk kernel (one-sequence chunks, ragged runs) or one
+                           key stream per query for these keys, never the group kernel;
+                           not supported by indexer_score_cand or paged stores */
 } sa_key_dtype;
 
 /* Fixed at plan time. The kernels support exactly num_heads 64, latent_dim 512,

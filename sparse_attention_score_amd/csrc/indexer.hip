@@ -750,11 +750,16 @@ __device__ __forceinline__ int pdim(int hh, int s) { return (2 * s + hh) * 8; }
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer resource, 32-bit data (gfx9 family)
 constexpr uint32_t kDrop = 0x80000000u;  // buffer offset past every extent: store dropped
 
-// PAGED: keys and scales are page pools of at least kPST rows per page, so each stage of
-// 64 keys lies in one page; the chunk's page ids (at most 64) are read once, one per lane.
-template <bool FP8, bool PAGED>
+// KF: key format, 0 bf16, 1 e4m3 (row scale applied to the score), 2 MXFP4 (each 16-byte
+// chunk of a 64-byte row is one 32-element block: widened with its E8M0 scale while
+// staging, so the tile holds exact bf16 values). PAGED: keys and scales are page pools of
+// at least kPST rows per page, so each stage of 64 keys lies in one page; the chunk's page
+// ids (at most 64) are read once, one per lane.
+template <int KF, bool PAGED>
 __global__ __launch_bounds__(kPThreads, 8 / kPWaves) void indexer_prefill_kernel(IndexerArgs a) {
-  constexpr int RB = FP8 ? kIdxDim : 2 * kIdxDim;   // key row bytes in HBM
+  constexpr bool FP8 = KF == 1, MX = KF == 2;
+  static_assert(!(MX && PAGED), "MXFP4 keys are read from contiguous stores");
+  constexpr int RB = MX ? kIdxDim / 2 : (FP8 ? kIdxDim : 2 * kIdxDim);   // key row bytes in HBM
   __shared__ __attribute__((aligned(16))) PrefillShared sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int r32 = lane & 31, hh = lane >> 5;
@@ -831,13 +836,17 @@ __global__ __launch_bounds__(kPThreads, 8 / kPWaves) void indexer_prefill_kernel
   // past klive read zeros (their scores are masked), so the loads need no clamping. The
   // whole offset goes in the VGPR operand, which the range check covers.
   const int sq = (seq >= 0 && seq < a.num_seqs) ? seq : 0;
-  const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys) + (int64_t)sq * a.keys_seq_stride * (FP8 ? 1 : 2) +
-                        (int64_t)k0 * RB;
+  const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys) +
+                        (int64_t)sq * a.keys_seq_stride * (KF == 0 ? 2 : 1) + (int64_t)k0 * RB;
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(keys), (short)0, (klive - k0) * RB, kRsrcWord3);
-  const float* scales = FP8 ? a.scales + (int64_t)sq * a.scales_seq_stride + k0 : a.w;
-  const __amdgpu_buffer_rsrc_t scrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(scales), (short)0, FP8 ? (klive - k0) * 4 : 0, kRsrcWord3);
+  // scales: e4m3 fp32 per row; MXFP4 4 E8M0 bytes per row (one dword per row)
+  const int64_t soff = MX ? (int64_t)sq * a.scales_seq_stride + (int64_t)k0 * 4   // bytes (stride in bytes)
+                          : ((int64_t)sq * a.scales_seq_stride + k0) * 4;          // bytes (stride in floats)
+  const float* scales = (FP8 || MX) ? reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(a.scales) + soff)
+                                    : a.w;
+  const __amdgpu_buffer_rsrc_t scrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(scales), (short)0, (FP8 || MX) ? (klive - k0) * 4 : 0, kRsrcWord3);
   // paged: page id of table entry (k0 >> lp) + lane (entries past the live keys repeat the last)
   int pgl = 0;
   if constexpr (PAGED) {
@@ -880,9 +889,12 @@ __global__ __launch_bounds__(kPThreads, 8 / kPWaves) void indexer_prefill_kernel
   for (int h = 0; h < CPT; ++h) {
     const int q = tid + kPThreads * h;
     kvoff[h] = (uint32_t)((q / CPR) * RB + (q % CPR) * 16);
-    ldsoff[h] = (uint32_t)((q / CPR) * kPRS + (q % CPR) * (FP8 ? 32 : 16));
+    ldsoff[h] = (uint32_t)((q / CPR) * kPRS + (q % CPR) * (MX ? 64 : FP8 ? 32 : 16));
   }
-  const uint32_t scoff = tid < kPST ? (uint32_t)tid * 4u : kDrop;
+  // e4m3: thread t < 64 loads row t's scale; MXFP4: every thread the scale dword of its
+  // chunk's row (its block's byte picked at commit)
+  static_assert(!MX || CPT == 1, "one MXFP4 chunk per thread");
+  const uint32_t scoff = MX ? (uint32_t)(tid / CPR) * 4u : (tid < kPST ? (uint32_t)tid * 4u : kDrop);
   struct Stage {
     u32x4 v[CPT];
     float scale;
@@ -894,13 +906,25 @@ __global__ __launch_bounds__(kPThreads, 8 / kPWaves) void indexer_prefill_kernel
 #pragma unroll
     for (int h = 0; h < CPT; ++h)
       st.v[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, kvoff[h] + skoff, 0, 0));
-    if (FP8) st.scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sr, scoff + ssoff, 0, 0));
+    if (FP8 || MX) st.scale = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sr, scoff + ssoff, 0, 0));
   };
   auto commit = [&](const Stage& st, int buf) {
 #pragma unroll
     for (int h = 0; h < CPT; ++h) {
       uint8_t* dst = &sh.tile[buf][ldsoff[h]];
-      if constexpr (FP8) {
+      if constexpr (MX) {
+        // 32 E2M1 elements of block (tid % 4) times its scale: 64 bytes of bf16
+        const float bs = e8m0_scale((__float_as_uint(st.scale) >> (8 * (tid % CPR))) & 0xFFu);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const u32x4 u = {
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(st.v[h][c], bs, 0)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(st.v[h][c], bs, 1)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(st.v[h][c], bs, 2)),
+              __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(st.v[h][c], bs, 3))};
+          *reinterpret_cast<u32x4*>(dst + 16 * c) = u;
+        }
+      } else if constexpr (FP8) {
         uint32_t u[8];
 #pragma unroll
         for (int c = 0; c < 4; ++c) e4m3x4_to_bf16x4(st.v[h][c], u[2 * c], u[2 * c + 1]);
@@ -1036,7 +1060,7 @@ void launch_group(const IndexerArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream) {
-  if (a.mxfp4) {
+  if (a.mxfp4 && !prefill) {
     // every query streams its own keys (the caller routes no other mode here)
     dim3 grid((unsigned)((a.E + kMxKeysPerWG - 1) / kMxKeysPerWG), (unsigned)a.T);
     hipLaunchKernelGGL(indexer_mx_kernel, grid, dim3(kDThreads), 0, stream, a);
@@ -1067,15 +1091,17 @@ hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream
     // blockIdx.x (key chunk) varies fastest, so with a multiple of 8 chunks every XCD
     // keeps the same chunks and their keys stay in its L2.
     dim3 grid((unsigned)((a.E + kPChunk - 1) / kPChunk), (unsigned)((a.T + kQPerWG - 1) / kQPerWG));
-    if (a.pages.table) {
+    if (a.mxfp4) {
+      hipLaunchKernelGGL((indexer_prefill_kernel<2, false>), grid, dim3(kPThreads), 0, stream, a);
+    } else if (a.pages.table) {
       if (a.fp8)
-        hipLaunchKernelGGL((indexer_prefill_kernel<true, true>), grid, dim3(kPThreads), 0, stream, a);
+        hipLaunchKernelGGL((indexer_prefill_kernel<1, true>), grid, dim3(kPThreads), 0, stream, a);
       else
-        hipLaunchKernelGGL((indexer_prefill_kernel<false, true>), grid, dim3(kPThreads), 0, stream, a);
+        hipLaunchKernelGGL((indexer_prefill_kernel<0, true>), grid, dim3(kPThreads), 0, stream, a);
     } else if (a.fp8) {
-      hipLaunchKernelGGL((indexer_prefill_kernel<true, false>), grid, dim3(kPThreads), 0, stream, a);
+      hipLaunchKernelGGL((indexer_prefill_kernel<1, false>), grid, dim3(kPThreads), 0, stream, a);
     } else {
-      hipLaunchKernelGGL((indexer_prefill_kernel<false, false>), grid, dim3(kPThreads), 0, stream, a);
+      hipLaunchKernelGGL((indexer_prefill_kernel<0, false>), grid, dim3(kPThreads), 0, stream, a);
     }
   }
   return hipGetLastError();

@@ -102,9 +102,10 @@ def test_decode_mxfp4_keys(n_raw):
 
 
 def test_mxfp4_keys_in_a_prefill_chunk_and_a_group():
-    # a chunk of one sequence and a multi-token decode batch with MXFP4 keys: both run the
-    # per-query kernel for these keys
+    # chunks of one sequence (the chunk kernel widens E2M1 x scale while staging; several
+    # chunks and stages, a ragged end) and a multi-token decode batch (per-query kernel)
     _e2e(W.make_prefill(T=40, offset=20000, ratio=1, key_dtype="mxfp4", name="prefill-mxfp4", seed=18))
+    _e2e(W.make_prefill(T=150, offset=9001, ratio=2, key_dtype="mxfp4", name="prefill-mxfp4-r2", seed=20))
     _e2e(W.make_decode_mq(B=2, n_raw=[3001, 9000], G=6, ratio=2, key_dtype="mxfp4",
                           name="mq-mxfp4", seed=19), check_scores=True)
 

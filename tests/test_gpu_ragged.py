@@ -19,7 +19,7 @@ def _gpu():
     assert torch.cuda.is_available(), "GPU tests need a ROCm device"
 
 
-@pytest.mark.parametrize("kd", ["bf16", "fp8"])
+@pytest.mark.parametrize("kd", ["bf16", "fp8", "mxfp4"])
 def test_ragged_batch_end_to_end(kd):
     # a 100-query chunk, decode singles, two 6-query draft steps (one group launch), a
     # 20-query chunk, a 3-query step, a 9-query run (chunk kernel); contexts up to 20k
