@@ -301,12 +301,21 @@ class Result:
         self.C_new = {}               # sequence -> fp64 compressed latent written this step
 
 
+def kv_rows_f64(codes: np.ndarray, scales: Optional[np.ndarray]) -> np.ndarray:
+    """Exact latent / window rows: bf16 as stored, or e4m3 code * fp32 row scale (the FP8
+    latent and window caches of the pages, read like the e4m3 index keys)."""
+    if scales is None:
+        return bf16_to_f64(codes)
+    return e4m3_to_f64(codes) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
 def compressed_rows(wl, b: int, n: int, rows: np.ndarray,
                     C_new_bits: Optional[np.ndarray] = None) -> np.ndarray:
     """fp64 values of compressed rows `rows` (< n) of sequence b; the row written this
     step (if any) stands in for row n-1."""
     rows = np.asarray(rows, np.int64)
-    X = bf16_to_f64(wl.C[b, rows])
+    CS = getattr(wl, "CS", None)
+    X = kv_rows_f64(wl.C[b, rows], None if CS is None else CS[b, rows])
     if C_new_bits is not None and n > 0:
         X[rows == n - 1] = bf16_to_f64(C_new_bits)
     return X
@@ -343,7 +352,8 @@ def run_query(wl, t: int, keys_f64: Optional[np.ndarray] = None, C_new: Optional
         new_bits = C_new[b][1]
     rows = compressed_rows(wl, b, n, use, new_bits) if use.size else np.zeros((0, DIM))
     win = window_positions(p)
-    Xw = bf16_to_f64(wl.R[b, win % wl.wcap])
+    RS = getattr(wl, "RS", None)
+    Xw = kv_rows_f64(wl.R[b, win % wl.wcap], None if RS is None else RS[b, win % wl.wcap])
     X = np.concatenate([rows, Xw], axis=0)
     o, lse = attend(bf16_to_f64(wl.q[t]), X)
     return I, cand, idx, o, lse

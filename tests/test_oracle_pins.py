@@ -129,6 +129,26 @@ def test_mxfp4_scores_equal_bf16_scores():
     assert np.array_equal(a, b)
 
 
+def test_fp8_kv_rows_with_power_of_two_scales_equal_bf16_rows():
+    # e4m3 latent and window rows with power-of-two row scales are exact bf16 values: the
+    # attention over them equals the attention over the same rows stored as bf16
+    import workloads as W
+    wl8 = W.make_decode(B=2, n_raw=[1100, 90], ratio=2, key_dtype="bf16", kv_dtype="fp8", seed=3)
+    wl8.CS[:] = 2.0 ** np.round(np.log2(wl8.CS))
+    wl8.RS[:] = 2.0 ** np.round(np.log2(wl8.RS))
+    wlb = W.make_decode(B=2, n_raw=[1100, 90], ratio=2, key_dtype="bf16", seed=3, with_compress=False)
+    for b in range(2):
+        cv = O.kv_rows_f64(wl8.C[b], wl8.CS[b])
+        rv = O.kv_rows_f64(wl8.R[b], wl8.RS[b])
+        wlb.C[b] = torch.from_numpy(cv).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        wlb.R[b] = torch.from_numpy(rv).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(O.bf16_to_f64(wlb.C[b]), cv) and np.array_equal(O.bf16_to_f64(wlb.R[b]), rv)
+    r8, rb = O.run(wl8), O.run(wlb)
+    for t in range(2):
+        assert np.array_equal(r8.idx[t], rb.idx[t])
+        assert np.array_equal(r8.o[t], rb.o[t]) and np.array_equal(r8.lse[t], rb.lse[t])
+
+
 def test_bf16_matches_torch():
     rng = np.random.default_rng(1)
     x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 10 ** rng.uniform(-30, 30, 20000).astype(np.float32),

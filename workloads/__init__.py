@@ -178,6 +178,9 @@ class Workload:
     meta: dict = field(default_factory=dict)
     group: int = 0       # consecutive queries that share a sequence (multi-token decode)
     runs: Optional[list] = None   # ragged batch: lengths of the runs of one sequence each
+    kv_dtype: str = "bf16"        # latents and window: "bf16", or "fp8" (e4m3 codes + row scales)
+    CS: Optional[np.ndarray] = None   # fp8 latents: fp32 row scales [B, nc_cap]
+    RS: Optional[np.ndarray] = None   # fp8 window: fp32 row scales [B, wcap]
 
     def visible(self) -> np.ndarray:
         return (self.pos.astype(np.int64) + 1) // self.ratio
@@ -213,8 +216,10 @@ def _keys(seed, key_dtype, B, nc_cap):
 
 def make_decode(B: int, n_raw, ratio: int = 2, key_dtype: str = "bf16", seed: int = 0,
                 wcap: int = WINDOW, name: str = "decode", nc_cap: Optional[int] = None,
-                with_compress: bool = True) -> Workload:
-    """B sequences, one decode query each at raw position n_raw-1 (per-sequence if an array)."""
+                with_compress: bool = True, kv_dtype: str = "bf16") -> Workload:
+    """B sequences, one decode query each at raw position n_raw-1 (per-sequence if an array).
+    kv_dtype "fp8": latents and window rows are N(0,1) rows quantised to e4m3 with one fp32
+    scale per row (no compressor inputs then: the compressor writes bf16 rows)."""
     n_raw = np.broadcast_to(np.asarray(n_raw, dtype=np.int64), (B,)).copy()
     pos = (n_raw - 1).astype(np.int32)
     vis = (pos.astype(np.int64) + 1) // ratio
@@ -225,15 +230,26 @@ def make_decode(B: int, n_raw, ratio: int = 2, key_dtype: str = "bf16", seed: in
     q = np.empty((T, HEADS, DIM), np.uint16)
     qI = np.empty((T, IDX_HEADS, IDX_DIM), np.uint16)
     w = np.empty((T, IDX_HEADS), np.float32)
-    C = np.empty((B, nc_cap, DIM), np.uint16)
-    R = np.empty((B, wcap, DIM), np.uint16)
+    C = np.empty((B, nc_cap, DIM), np.uint16) if kv_dtype == "bf16" else None
+    R = np.empty((B, wcap, DIM), np.uint16) if kv_dtype == "bf16" else None
     for b in range(B):
         q[b] = normal_bf16(seed, "q", b, (HEADS, DIM))
         qI[b] = normal_bf16(seed, "qI", b, (IDX_HEADS, IDX_DIM))
         w[b] = uniform_f32(seed, "w", b, (IDX_HEADS,))
-        C[b] = normal_bf16(seed, "C", b, (nc_cap, DIM))
-        R[b] = normal_bf16(seed, "R", b, (wcap, DIM))
+        if kv_dtype == "bf16":
+            C[b] = normal_bf16(seed, "C", b, (nc_cap, DIM))
+            R[b] = normal_bf16(seed, "R", b, (wcap, DIM))
     KI, KS = _keys(seed, key_dtype, B, nc_cap)
+    CS = RS = None
+    if kv_dtype == "fp8":
+        C = np.empty((B, nc_cap, DIM), np.uint8)
+        R = np.empty((B, wcap, DIM), np.uint8)
+        CS = np.empty((B, nc_cap), np.float32)
+        RS = np.empty((B, wcap), np.float32)
+        for b in range(B):
+            C[b], CS[b] = normal_e4m3_rows(seed, "C", b, nc_cap, DIM)
+            R[b], RS[b] = normal_e4m3_rows(seed, "R", b, wcap, DIM)
+        with_compress = False
     Xp = Zp = beta = None
     if ratio == 2 and with_compress:
         Xp = np.empty((B, 2, DIM), np.uint16)
@@ -244,7 +260,7 @@ def make_decode(B: int, n_raw, ratio: int = 2, key_dtype: str = "bf16", seed: in
         beta = normal_f32(seed, "beta", 0, (2, DIM))
     return Workload(name=name, kind="decode", ratio=ratio, key_dtype=key_dtype, B=B, T=T,
                     nc_cap=nc_cap, wcap=wcap, seq=seq, pos=pos, q=q, qI=qI, w=w, C=C, KI=KI,
-                    KS=KS, R=R, Xp=Xp, Zp=Zp, beta=beta, seed=seed)
+                    KS=KS, R=R, Xp=Xp, Zp=Zp, beta=beta, seed=seed, kv_dtype=kv_dtype, CS=CS, RS=RS)
 
 
 def make_decode_mq(B: int, n_raw, G: int = 6, ratio: int = 2, key_dtype: str = "bf16",
