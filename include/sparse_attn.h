@@ -76,6 +76,15 @@ typedef enum sa_key_dtype {
 /* Fixed at plan time. The kernels support exactly num_heads 64, latent_dim 512,
  * window 128, topk 512, idx_heads 16, idx_dim 128, block 8, cand_blocks 2048,
  * ratio 1 or 2; anything else returns SA_EUNSUPPORTED. */
+/* Latent and window store element type (the pages' FP8 window cache and 8-bit latents). */
+typedef enum sa_kv_dtype {
+  SA_KV_BF16 = 0,       /* rows of 512 bf16 */
+  SA_KV_FP8_E4M3 = 1    /* rows of 512 OCP E4M3 codes plus one fp32 scale per row:
+                           X = scale * code. Read by sparse_attn_fwd (decoded exactly where
+                           the MFMA operands are built); sparse_attn_compress writes bf16
+                           rows and returns SA_EUNSUPPORTED for these plans */
+} sa_kv_dtype;
+
 typedef struct sa_params {
   int32_t num_heads;
   int32_t latent_dim;
@@ -90,6 +99,7 @@ typedef struct sa_params {
   float softmax_scale;     /* multiplies <q_h, x>; 1/sqrt(512) for this layer */
   int64_t max_queries;     /* largest T of any call made with this plan */
   int64_t max_compressed;  /* largest visible compressed count of any query */
+  int32_t kv_dtype;        /* sa_kv_dtype of the latents and the window (0: bf16) */
 } sa_params;
 
 typedef struct sa_plan sa_plan;
@@ -151,6 +161,14 @@ typedef struct sa_cache {
   int64_t block_table_stride;    /* >= ceil(compressed_cap / page_size) */
   int32_t page_size;             /* power of two in [16, 2^20] */
   int64_t num_pages;             /* pages in each pool, 1 .. 2^31 - 1 */
+  /* e4m3 latents and window (plan kv_dtype SA_KV_FP8_E4M3): latents and window hold 512
+   * codes per row and their *_seq_stride fields count bytes (multiples of 16); the fp32
+   * row scales are latent_scales [num_seqs][compressed_cap] (or one per pool row when
+   * paged) and window_scales [num_seqs][window_cap]. */
+  const float* latent_scales;
+  int64_t latent_scales_seq_stride;  /* >= compressed_cap (ignored when paged) */
+  const float* window_scales;
+  int64_t window_scales_seq_stride;  /* >= window_cap */
 } sa_cache;
 
 /* Validate `params` and create a plan (host memory owned by the library,

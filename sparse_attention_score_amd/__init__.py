@@ -21,6 +21,8 @@ LIB_PATH = os.environ.get("SPARSE_ATTN_LIB") or os.path.join(_PKG, "libsparse_at
 SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_EWORKSPACE, SA_EHIP = 0, 1, 2, 3, 4
 SA_KEY_BF16, SA_KEY_FP8_E4M3, SA_KEY_MXFP4 = 0, 1, 2
 KEY_DTYPES = {"bf16": SA_KEY_BF16, "fp8": SA_KEY_FP8_E4M3, "mxfp4": SA_KEY_MXFP4}
+SA_KV_BF16, SA_KV_FP8_E4M3 = 0, 1
+KV_DTYPES = {"bf16": SA_KV_BF16, "fp8": SA_KV_FP8_E4M3}
 STATUS_NAMES = {0: "SA_OK", 1: "SA_EINVAL", 2: "SA_EUNSUPPORTED", 3: "SA_EWORKSPACE", 4: "SA_EHIP"}
 
 EXPORTS = ("sparse_attn_plan", "sparse_attn_plan_destroy", "sparse_attn_last_error",
@@ -35,7 +37,7 @@ class sa_params(ctypes.Structure):
                 ("block", ctypes.c_int32), ("cand_blocks", ctypes.c_int32),
                 ("ratio", ctypes.c_int32), ("idx_key_dtype", ctypes.c_int32),
                 ("softmax_scale", ctypes.c_float), ("max_queries", ctypes.c_int64),
-                ("max_compressed", ctypes.c_int64)]
+                ("max_compressed", ctypes.c_int64), ("kv_dtype", ctypes.c_int32)]
 
 
 class sa_queries(ctypes.Structure):
@@ -52,7 +54,9 @@ class sa_cache(ctypes.Structure):
                 ("idx_keys", ctypes.c_void_p), ("idx_keys_seq_stride", ctypes.c_int64),
                 ("idx_scales", ctypes.c_void_p), ("idx_scales_seq_stride", ctypes.c_int64),
                 ("block_table", ctypes.c_void_p), ("block_table_stride", ctypes.c_int64),
-                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int64)]
+                ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int64),
+                ("latent_scales", ctypes.c_void_p), ("latent_scales_seq_stride", ctypes.c_int64),
+                ("window_scales", ctypes.c_void_p), ("window_scales_seq_stride", ctypes.c_int64)]
 
 
 class SparseAttnError(RuntimeError):
@@ -128,7 +132,7 @@ class Plan:
 
     def __init__(self, ratio: int, key_dtype: str = "bf16", max_queries: int = 1,
                  max_compressed: int = 0, softmax_scale: float = 1.0 / math.sqrt(512.0),
-                 **dims):
+                 kv_dtype: str = "bf16", **dims):
         p = sa_params(num_heads=dims.get("num_heads", 64), latent_dim=dims.get("latent_dim", 512),
                       window=dims.get("window", 128), topk=dims.get("topk", 512),
                       idx_heads=dims.get("idx_heads", 16), idx_dim=dims.get("idx_dim", 128),
@@ -136,7 +140,7 @@ class Plan:
                       ratio=ratio,
                       idx_key_dtype=KEY_DTYPES[key_dtype],
                       softmax_scale=softmax_scale, max_queries=max_queries,
-                      max_compressed=max_compressed)
+                      max_compressed=max_compressed, kv_dtype=KV_DTYPES[kv_dtype])
         h = ctypes.c_void_p()
         ws = ctypes.c_size_t()
         _check(lib.sparse_attn_plan(ctypes.byref(p), ctypes.byref(h), ctypes.byref(ws)))
@@ -181,6 +185,17 @@ class Queries:
         return self.c.T
 
 
+def _seq_stride(t: torch.Tensor) -> int:
+    """Stride of dim 0 in elements; a single-sequence tensor may carry any stride there (a
+    size-1 dimension), so its row block size is used instead."""
+    if t.shape[0] > 1:
+        return t.stride(0)
+    n = 1
+    for d in t.shape[1:]:
+        n *= d
+    return n
+
+
 class Cache:
     """sa_cache from device tensors: latents [S,cap,512] bf16, window [S,wcap,512] bf16,
     idx_keys [S,cap,128] bf16 or uint8 (e4m3 codes), or uint8 [S,cap,64] (MXFP4 codes);
@@ -189,38 +204,52 @@ class Cache:
 
     def __init__(self, latents=None, window=None, idx_keys=None, idx_scales=None,
                  num_seqs: Optional[int] = None, compressed_cap: Optional[int] = None,
-                 block_table: Optional[torch.Tensor] = None, page_size: int = 0):
+                 block_table: Optional[torch.Tensor] = None, page_size: int = 0,
+                 latent_scales: Optional[torch.Tensor] = None,
+                 window_scales: Optional[torch.Tensor] = None):
         ref = latents if latents is not None else idx_keys
         if num_seqs is None:
             num_seqs = ref.shape[0]
         if compressed_cap is None:
             compressed_cap = ref.shape[1]
         c = sa_cache(num_seqs=num_seqs, compressed_cap=compressed_cap)
+        # latents / window: bf16 rows, or uint8 e4m3 codes with fp32 row scales (strides in
+        # elements of the tensor: bf16 or bytes, as the C ABI counts them)
         if latents is not None:
-            _need(latents, "latents", torch.bfloat16)
-            c.latents, c.latents_seq_stride = latents.data_ptr(), latents.stride(0)
+            if latents.dtype not in (torch.bfloat16, torch.uint8):
+                raise TypeError("latents must be bfloat16 or uint8 (e4m3 codes)")
+            _need(latents, "latents", latents.dtype)
+            c.latents, c.latents_seq_stride = latents.data_ptr(), _seq_stride(latents)
         if window is not None:
-            _need(window, "window", torch.bfloat16)
-            c.window, c.window_seq_stride, c.window_cap = window.data_ptr(), window.stride(0), window.shape[1]
+            if window.dtype not in (torch.bfloat16, torch.uint8):
+                raise TypeError("window must be bfloat16 or uint8 (e4m3 codes)")
+            _need(window, "window", window.dtype)
+            c.window, c.window_seq_stride, c.window_cap = window.data_ptr(), _seq_stride(window), window.shape[1]
+        if latent_scales is not None:
+            _need(latent_scales, "latent_scales", torch.float32)
+            c.latent_scales, c.latent_scales_seq_stride = latent_scales.data_ptr(), _seq_stride(latent_scales)
+        if window_scales is not None:
+            _need(window_scales, "window_scales", torch.float32)
+            c.window_scales, c.window_scales_seq_stride = window_scales.data_ptr(), _seq_stride(window_scales)
         if idx_keys is not None:
             if idx_keys.dtype not in (torch.bfloat16, torch.uint8):
                 raise TypeError("idx_keys must be bfloat16 or uint8 (e4m3 or MXFP4 codes)")
             _need(idx_keys, "idx_keys", idx_keys.dtype)
-            c.idx_keys, c.idx_keys_seq_stride = idx_keys.data_ptr(), idx_keys.stride(0)
+            c.idx_keys, c.idx_keys_seq_stride = idx_keys.data_ptr(), _seq_stride(idx_keys)
         if idx_scales is not None:
             if idx_scales.dtype not in (torch.float32, torch.uint8):
                 raise TypeError("idx_scales must be float32 (e4m3) or uint8 (MXFP4 E8M0)")
             _need(idx_scales, "idx_scales", idx_scales.dtype)
-            c.idx_scales, c.idx_scales_seq_stride = idx_scales.data_ptr(), idx_scales.stride(0)
+            c.idx_scales, c.idx_scales_seq_stride = idx_scales.data_ptr(), _seq_stride(idx_scales)
         if block_table is not None:
             # paged stores: latents [pages*page_size, 512], idx_keys [pages*page_size, 128],
             # idx_scales [pages*page_size] are pools; block_table [num_seqs, pages per seq]
             _need(block_table, "block_table", torch.int32)
             pool = latents if latents is not None else idx_keys
-            c.block_table, c.block_table_stride = block_table.data_ptr(), block_table.stride(0)
+            c.block_table, c.block_table_stride = block_table.data_ptr(), _seq_stride(block_table)
             c.page_size = int(page_size)
             c.num_pages = pool.shape[0] // int(page_size)
-        self._keep = (latents, window, idx_keys, idx_scales, block_table)
+        self._keep = (latents, window, idx_keys, idx_scales, block_table, latent_scales, window_scales)
         self.c = c
 
 

@@ -70,6 +70,7 @@ struct AttnShared {
   u32x4 P[2][kHG][64];                 // P^T operand of each head group per lane, two steps
   float tmax[2][kHeads];               // step-0 maxima per key half / partial normalisers
   float norm[kHeads];                  // final normaliser of each head
+  float rscale[kMaxKeys];              // e4m3 rows: the fp32 scale of every key slot
   int wave_cnt[kAW];
   int redo[kAW];                       // per wave: a score exceeded its reference by > kSafe
   int last;                            // this work-group combines the query's key splits
@@ -119,8 +120,21 @@ __device__ __forceinline__ uint32_t part_off(int unit, int vw, int hh, int h, in
 __device__ __forceinline__ void row_to_lds(const uint16_t* row, uint32_t lds, int lane) {
   to_lds16(row + lane * 8, lds);
 }
+// an e4m3 row (512 bytes): the first half-wave moves it into the first half of the slot
+__device__ __forceinline__ void row8_to_lds(const uint16_t* row, uint32_t lds, int lane) {
+  if (lane < 32) to_lds16(reinterpret_cast<const uint8_t*>(row) + 16 * lane, lds);
+}
+// 4 e4m3 codes -> 4 bf16 (exact), as two packed pairs
+__device__ __forceinline__ uint2 e4m3x4_bf16(uint32_t x) {
+  return uint2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true))};
+}
 
-template <int HS>
+// KV8: the latents and the window are e4m3 rows with one fp32 scale each (X_j = s_j code_j):
+// rows travel as 512 bytes, codes are widened exactly to bf16 where the MFMA operands are
+// built, the raw score of key j is multiplied by s_j, and so is P_j before the values
+// (the normaliser sums the unscaled P).
+template <int HS, bool KV8>
 __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   // HS = 2: the query's heads are split over two work-groups (32 each) that gather the same
   // rows (normally on one XCD, so the second reads them from L2); no key splits then
@@ -195,19 +209,32 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       nsel += sh.wave_cnt[w];
       before += (w < wave) ? sh.wave_cnt[w] : 0;
     }
-    const uint16_t* lat = reinterpret_cast<const uint16_t*>(a.latents);
-    if (a.pages.table) {
-      // paged latents: the row of position j is in page table[seq][j / page] (the only
-      // compiler-visible load before the output; the waits after it are explicit again)
-      if (v) sh.rows[before + incl - 1] = lat + pool_row(a.pages, page_of(a.pages, seq, j), j) * kDim;
-    } else {
-      lat += (int64_t)seq * a.latents_seq_stride;
-      if (v) sh.rows[before + incl - 1] = lat + (int64_t)j * kDim;
+    // global row of each key (and, for e4m3 rows, its scale: compiler-visible loads before
+    // the output, waited for here; the waits after them are explicit again). Strides are in
+    // elements of the store: bf16, or bytes for e4m3 rows.
+    constexpr int RB = KV8 ? kDim : 2 * kDim;   // row bytes
+    const uint8_t* latb = reinterpret_cast<const uint8_t*>(a.latents);
+    if (v) {
+      int64_t off, sidx;
+      if (a.pages.table) {   // paged latents: the row of position j is in page table[seq][j / page]
+        const int64_t r = pool_row(a.pages, page_of(a.pages, seq, j), j);
+        off = r * RB;
+        sidx = r;
+      } else {
+        off = (int64_t)seq * a.latents_seq_stride * (KV8 ? 1 : 2) + (int64_t)j * RB;
+        sidx = (int64_t)seq * a.latent_scales_seq_stride + j;
+      }
+      sh.rows[before + incl - 1] = reinterpret_cast<const uint16_t*>(latb + off);
+      if (KV8) sh.rscale[before + incl - 1] = a.latent_scales[sidx];
     }
     const int u0 = p - kWindow + 1 > 0 ? p - kWindow + 1 : 0;
     const int nwin = p - u0 + 1;
-    const uint16_t* win = reinterpret_cast<const uint16_t*>(a.window) + (int64_t)seq * a.window_seq_stride;
-    if (tid < nwin) sh.rows[nsel + tid] = win + (int64_t)((u0 + tid) % a.window_cap) * kDim;
+    if (tid < nwin) {
+      const int64_t wr = (int64_t)((u0 + tid) % a.window_cap);
+      sh.rows[nsel + tid] = reinterpret_cast<const uint16_t*>(
+          reinterpret_cast<const uint8_t*>(a.window) + (int64_t)seq * a.window_seq_stride * (KV8 ? 1 : 2) + wr * RB);
+      if (KV8) sh.rscale[nsel + tid] = a.window_scales[(int64_t)seq * a.window_scales_seq_stride + wr];
+    }
     m = nsel + nwin;
   }
   __syncthreads();
@@ -236,7 +263,10 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) r[i] = sh.rows[kb + min(step * kKT + wave * kRowsPerWave + i, mk - 1)];
 #pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) row_to_lds(r[i], base + i * kRow, lane);
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      if constexpr (KV8) row8_to_lds(r[i], base + i * kRow, lane);
+      else row_to_lds(r[i], base + i * kRow, lane);
+    }
   };
 
   // ---- score waves: query heads 16(2hp + j) + c as B operands (k-step s: dims
@@ -280,10 +310,25 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + (4 * s + g) * 16);
+        bf16x8 ka;
+        if constexpr (KV8) {   // dims (4s+g)*8 .. +7: 8 code bytes
+          const uint2 b8 = *reinterpret_cast<const uint2*>(krow + (4 * s + g) * 8);
+          const uint2 lo = e4m3x4_bf16(b8.x), hi = e4m3x4_bf16(b8.y);
+          ka = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+        } else {
+          ka = *reinterpret_cast<const bf16x8*>(krow + (4 * s + g) * 16);
+        }
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
           acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j][s], acc[j], 0, 0, 0);
+      }
+      if constexpr (KV8) {   // raw score of key j times s_j (slots past the list: any value, masked)
+        const int k0 = min(kb + step * kKT + 16 * kh + 4 * g, kMaxKeys - 4);
+        const f32x4 rs = *reinterpret_cast<const f32x4*>(&sh.rscale[k0]);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[j][i] *= rs[i];
       }
     };
     // softmax of step `step`: P to LDS buffer step & 1 (keys past mk, and whole steps past
@@ -307,6 +352,12 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
         for (int i = 0; i < 4; ++i) {
           pv[i] = __builtin_amdgcn_exp2f(x[i] - m_ref[j]);
           l_run[j] += pv[i];
+        }
+        if constexpr (KV8) {   // the values are the codes: P_j s_j weighs them
+          const int k0 = min(kb + step * kKT + 16 * kh + 4 * g, kMaxKeys - 4);
+          const f32x4 rs = *reinterpret_cast<const f32x4*>(&sh.rscale[k0]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pv[i] *= rs[i];
         }
         uint32_t* dst = reinterpret_cast<uint32_t*>(&sh.P[step & 1][sgrp(j)][lane]) + 2 * kh;
         dst[0] = pack_bf16x2(pv[0], pv[1]);
@@ -435,7 +486,9 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int key = (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4));
-          const uint2 v = *reinterpret_cast<const uint2*>(T8 + key * kRow + (128 * vw + 64 * hh + 4 * c) * 2);
+          uint2 v;
+          if constexpr (KV8) v = e4m3x4_bf16(*reinterpret_cast<const uint32_t*>(T8 + key * kRow + 128 * vw + 64 * hh + 4 * c));
+          else v = *reinterpret_cast<const uint2*>(T8 + key * kRow + (128 * vw + 64 * hh + 4 * c) * 2);
           R[hh][j][0] = v.x;
           R[hh][j][1] = v.y;
         }
@@ -616,9 +669,15 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   const int hs = attn_head_sets(a.m.T, a.splits);
   const int64_t u8 = (a.m.T * a.splits * hs + 7) / 8;   // work units per XCD
   if (hs == 2)
-    hipLaunchKernelGGL(attn_kernel<2>, dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
+    if (a.kv_fp8)
+      hipLaunchKernelGGL((attn_kernel<2, true>), dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_kernel<2, false>), dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(attn_kernel<1>, dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
+    if (a.kv_fp8)
+      hipLaunchKernelGGL((attn_kernel<1, true>), dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_kernel<1, false>), dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
   return hipGetLastError();
 }
 

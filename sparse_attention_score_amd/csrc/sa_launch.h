@@ -93,6 +93,13 @@ struct AttnArgs {
   float* part_ml;           // [T * splits][64][2] reference (log2 domain) and normaliser
   uint32_t* counters;       // [T]
   PageTable pages;          // latents are a page pool when pages.table is set
+  // e4m3 latents and window: rows of 512 codes (strides above in bytes then), one fp32
+  // scale per row ([seq][cap] / [seq][wcap], or the pool's rows when paged)
+  bool kv_fp8;
+  const float* latent_scales;
+  int64_t latent_scales_seq_stride;
+  const float* window_scales;
+  int64_t window_scales_seq_stride;
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 // Key splits used for T queries, and the partial slots (T * splits) the largest of them

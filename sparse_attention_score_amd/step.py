@@ -28,7 +28,8 @@ class DeviceBatch:
         self.T = wl.T
         self.ratio = wl.ratio
         dev = torch.device(device)
-        self.plan = Plan(ratio=wl.ratio, key_dtype=wl.key_dtype,
+        kv = getattr(wl, "kv_dtype", "bf16")
+        self.plan = Plan(ratio=wl.ratio, key_dtype=wl.key_dtype, kv_dtype=kv,
                          max_queries=max_queries or wl.T, max_compressed=wl.nc_cap)
         self.seq = torch.from_numpy(wl.seq.astype(np.int32)).to(dev)
         self.pos = torch.from_numpy(wl.pos.astype(np.int32)).to(dev)
@@ -38,15 +39,23 @@ class DeviceBatch:
         self.q = to_device_bf16(wl.q, dev)
         self.qI = to_device_bf16(wl.qI, dev)
         self.w = torch.from_numpy(wl.w).to(dev)
-        self.C = to_device_bf16(wl.C, dev)
-        self.R = to_device_bf16(wl.R, dev)
+        self.CS = self.RS = None
+        if kv == "fp8":   # e4m3 latent and window rows with fp32 row scales
+            self.C = torch.from_numpy(np.ascontiguousarray(wl.C)).to(dev)
+            self.R = torch.from_numpy(np.ascontiguousarray(wl.R)).to(dev)
+            self.CS = torch.from_numpy(np.ascontiguousarray(wl.CS)).to(dev)
+            self.RS = torch.from_numpy(np.ascontiguousarray(wl.RS)).to(dev)
+        else:
+            self.C = to_device_bf16(wl.C, dev)
+            self.R = to_device_bf16(wl.R, dev)
         if wl.key_dtype in ("fp8", "mxfp4"):
             self.KI = torch.from_numpy(wl.KI).to(dev)
             self.KS = torch.from_numpy(wl.KS).to(dev)
         else:
             self.KI = to_device_bf16(wl.KI, dev)
             self.KS = None
-        self.cache = Cache(latents=self.C, window=self.R, idx_keys=self.KI, idx_scales=self.KS)
+        self.cache = Cache(latents=self.C, window=self.R, idx_keys=self.KI, idx_scales=self.KS,
+                           latent_scales=self.CS, window_scales=self.RS)
         # compressor inputs for the group each query completes (ratio 2, uniform position)
         self.groups = wl.compress_groups() if hasattr(wl, "compress_groups") else np.zeros(0)
         self.Xp = self.Zp = self.beta = None

@@ -110,6 +110,25 @@ def test_mxfp4_keys_in_a_prefill_chunk_and_a_group():
                           name="mq-mxfp4", seed=19), check_scores=True)
 
 
+@pytest.mark.parametrize("B,n_raw", [(6, [40006, 3001, 2, 130, 1031, 9000]), (40, 5000)])
+def test_fp8_latents_and_window(B, n_raw):
+    # e4m3 latent and window rows with fp32 row scales: 6 queries (key splits), 40 queries
+    # (two head sets), pruning and tiny contexts
+    wl = W.make_decode(B=B, n_raw=n_raw, ratio=2, key_dtype="fp8", kv_dtype="fp8",
+                       name=f"fp8kv-{B}", seed=41)
+    _e2e(wl)
+
+
+def test_fp8_latents_prefill_chunk():
+    # one work-group per query (150 queries), ratio 1
+    wl = W.make_prefill(T=150, offset=3000, ratio=1, key_dtype="bf16", name="fp8kv-prefill", seed=42)
+    import workloads as Wm
+    C, CS = Wm.normal_e4m3_rows(42, "C", 0, wl.nc_cap, 512)
+    R, RS = Wm.normal_e4m3_rows(42, "R", 0, wl.wcap, 512)
+    wl.C, wl.R, wl.CS, wl.RS, wl.kv_dtype = C[None], R[None], CS[None], RS[None], "fp8"
+    _e2e(wl)
+
+
 def test_decode_tiny_contexts():
     # n = 0 (window only), 1, 1, 8, 65 visible compressed latents
     wl = W.make_decode(B=5, n_raw=[1, 2, 3, 17, 130], ratio=2, key_dtype="bf16", name="tiny",
