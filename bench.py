@@ -17,11 +17,11 @@ A third times a multi-token decode step: 128 sequences x 6 queries (a verified t
 the headline decode batch with MXFP4 index keys (the 4-bit indexer cache), and a fifth its
 indexer, selection and attention on paged stores (64-row pages, block tables). A sixth
 times a ragged serving batch (prefill chunks, drafted decode steps and single decode queries
-in one call).
+in one call), and a seventh the headline batch with e4m3 latent and window rows.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-prefill] [--no-rescore] [--no-multiquery] [--no-mxfp4] [--no-paged]
-                       [--no-ragged]
+                       [--no-ragged] [--no-fp8kv]
                        [--no-cpu-baseline] [--profile]
 """
 from __future__ import annotations
@@ -377,6 +377,8 @@ def main():
     ap.add_argument("--mxfp4-workload", default="decode-b128-ctx128k-mxfp4")
     ap.add_argument("--no-mxfp4", action="store_true")
     ap.add_argument("--no-paged", action="store_true")
+    ap.add_argument("--fp8kv-workload", default="decode-b128-ctx128k-fp8kv")
+    ap.add_argument("--no-fp8kv", action="store_true")
     ap.add_argument("--ragged-workload", default="ragged-2x1024+64+16x6-ctx128k-fp8")
     ap.add_argument("--no-ragged", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -529,6 +531,24 @@ def main():
         }
         log(f"MXFP4-key decode: {x_s * 1e3:.3f} ms/step, stages {xms}")
         del dx, wx
+        torch.cuda.empty_cache()
+
+    if not args.no_fp8kv and not args.profile:
+        t0 = time.perf_counter()
+        wk = W.make(args.fp8kv_workload)
+        dk = DeviceBatch(wk)
+        torch.cuda.synchronize()
+        log(f"e4m3-KV decode inputs ready in {time.perf_counter() - t0:.1f}s")
+        k_eager, kms = run_batch(torch, dk, args.steps, args.warmup)
+        k_s, _ = run_graph(torch, dk, args.steps)
+        result["fp8_kv"] = {
+            "workload": args.fp8kv_workload, "queries": int(wk.T),
+            "what": "the headline batch with e4m3 latent and window rows (no compressor: it writes bf16 rows)",
+            "ms_per_step": k_s * 1e3, "queries_per_s": wk.T / k_s, "eager_ms_per_step": k_eager * 1e3,
+            "stage_ms": kms,
+        }
+        log(f"e4m3-KV decode: {k_s * 1e3:.3f} ms/step, stages {kms}")
+        del dk, wk
         torch.cuda.empty_cache()
 
     if not args.no_ragged and not args.profile:

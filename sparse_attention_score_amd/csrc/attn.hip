@@ -71,6 +71,7 @@ struct AttnShared {
   float tmax[2][kHeads];               // step-0 maxima per key half / partial normalisers
   float norm[kHeads];                  // final normaliser of each head
   float rscale[kMaxKeys];              // e4m3 rows: the fp32 scale of every key slot
+  const float* sptr[kMaxKeys];         // e4m3 rows: where each slot's scale lives
   int wave_cnt[kAW];
   int redo[kAW];                       // per wave: a score exceeded its reference by > kSafe
   int last;                            // this work-group combines the query's key splits
@@ -120,6 +121,10 @@ __device__ __forceinline__ uint32_t part_off(int unit, int vw, int hh, int h, in
 __device__ __forceinline__ void row_to_lds(const uint16_t* row, uint32_t lds, int lane) {
   to_lds16(row + lane * 8, lds);
 }
+// 4 bytes per lane to LDS byte lds + 4 * lane (same rules as to_lds16)
+__device__ __forceinline__ void to_lds4(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(src), "{m0}"(lds) : "memory");
+}
 // an e4m3 row (512 bytes): the first half-wave moves it into the first half of the slot
 __device__ __forceinline__ void row8_to_lds(const uint16_t* row, uint32_t lds, int lane) {
   if (lane < 32) to_lds16(reinterpret_cast<const uint8_t*>(row) + 16 * lane, lds);
@@ -131,9 +136,9 @@ __device__ __forceinline__ uint2 e4m3x4_bf16(uint32_t x) {
 }
 
 // KV8: the latents and the window are e4m3 rows with one fp32 scale each (X_j = s_j code_j):
-// rows travel as 512 bytes, codes are widened exactly to bf16 where the MFMA operands are
-// built, the raw score of key j is multiplied by s_j, and so is P_j before the values
-// (the normaliser sums the unscaled P).
+// rows travel as 512 bytes and are widened exactly to bf16 codes in LDS, once per step by
+// the wave that loaded them; the raw score of key j is multiplied by s_j, and so is P_j
+// before the values (the normaliser sums the unscaled P).
 template <int HS, bool KV8>
 __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   // HS = 2: the query's heads are split over two work-groups (32 each) that gather the same
@@ -209,8 +214,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       nsel += sh.wave_cnt[w];
       before += (w < wave) ? sh.wave_cnt[w] : 0;
     }
-    // global row of each key (and, for e4m3 rows, its scale: compiler-visible loads before
-    // the output, waited for here; the waits after them are explicit again). Strides are in
+    // global row of each key (and, for e4m3 rows, where its scale is). Strides are in
     // elements of the store: bf16, or bytes for e4m3 rows.
     constexpr int RB = KV8 ? kDim : 2 * kDim;   // row bytes
     const uint8_t* latb = reinterpret_cast<const uint8_t*>(a.latents);
@@ -225,7 +229,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
         sidx = (int64_t)seq * a.latent_scales_seq_stride + j;
       }
       sh.rows[before + incl - 1] = reinterpret_cast<const uint16_t*>(latb + off);
-      if (KV8) sh.rscale[before + incl - 1] = a.latent_scales[sidx];
+      if (KV8) sh.sptr[before + incl - 1] = a.latent_scales + sidx;
     }
     const int u0 = p - kWindow + 1 > 0 ? p - kWindow + 1 : 0;
     const int nwin = p - u0 + 1;
@@ -233,7 +237,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       const int64_t wr = (int64_t)((u0 + tid) % a.window_cap);
       sh.rows[nsel + tid] = reinterpret_cast<const uint16_t*>(
           reinterpret_cast<const uint8_t*>(a.window) + (int64_t)seq * a.window_seq_stride * (KV8 ? 1 : 2) + wr * RB);
-      if (KV8) sh.rscale[nsel + tid] = a.window_scales[(int64_t)seq * a.window_scales_seq_stride + wr];
+      if (KV8) sh.sptr[nsel + tid] = a.window_scales + (int64_t)seq * a.window_scales_seq_stride + wr;
     }
     m = nsel + nwin;
   }
@@ -268,7 +272,39 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       else row_to_lds(r[i], base + i * kRow, lane);
     }
   };
+  // e4m3 rows: each wave widens the rows it loaded, in place (codes in the first 512 bytes
+  // of a slot become 1 KiB of bf16), after its own wait and before the barrier that hands
+  // the step to the other waves. All of a lane's reads come before its writes, and a
+  // wave's LDS operations run in order, so no code is overwritten before it is read.
+  auto expand = [&](int step) {
+    if constexpr (KV8) {
+      uint8_t* base = sh.tile[step % kBufs] + wave * kRowsPerWave * kRow;
+      u32x4 cv[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {   // 16-code chunk q of row rr (2 per lane: 4 rows x 32)
+        const int ch = lane + 64 * h, rr = ch >> 5, q = ch & 31;
+        cv[h] = *reinterpret_cast<const u32x4*>(base + rr * kRow + 16 * q);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ch = lane + 64 * h, rr = ch >> 5, q = ch & 31;
+        uint2 b[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[e] = e4m3x4_bf16(cv[h][e]);
+        *reinterpret_cast<u32x4*>(base + rr * kRow + 32 * q) = u32x4{b[0].x, b[0].y, b[1].x, b[1].y};
+        *reinterpret_cast<u32x4*>(base + rr * kRow + 32 * q + 16) = u32x4{b[2].x, b[2].y, b[3].x, b[3].y};
+      }
+    }
+  };
 
+  // e4m3 rows: the slots' scales by direct loads (slots past the list read the first
+  // slot's), issued before the first rows so the rows' waits cover them
+  if constexpr (KV8) {
+    for (int i = wave; i < kMaxKeys / 64; i += kAW) {
+      const int slot = 64 * i + lane;
+      to_lds4(sh.sptr[slot < m ? slot : 0], (uint32_t)(uintptr_t)&sh.rscale[64 * i]);
+    }
+  }
   // ---- score waves: query heads 16(2hp + j) + c as B operands (k-step s: dims
   // (4s+g)*8 .. +8), from LDS; steps 0 and 1 are already on their way meanwhile ----
   if (mk > 0) {
@@ -310,14 +346,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
-        bf16x8 ka;
-        if constexpr (KV8) {   // dims (4s+g)*8 .. +7: 8 code bytes
-          const uint2 b8 = *reinterpret_cast<const uint2*>(krow + (4 * s + g) * 8);
-          const uint2 lo = e4m3x4_bf16(b8.x), hi = e4m3x4_bf16(b8.y);
-          ka = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-        } else {
-          ka = *reinterpret_cast<const bf16x8*>(krow + (4 * s + g) * 16);
-        }
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + (4 * s + g) * 16);
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
           acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j][s], acc[j], 0, 0, 0);
@@ -371,6 +400,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
         for (int j = 0; j < kDepth; ++j) issue(j);
       }
       __builtin_amdgcn_s_waitcnt(kWaitLater);   // step 0's rows (steps 1, 2 in flight)
+      expand(0);
       __syncthreads();
       f32x4 acc[NJ];
       scores_raw(0, acc);
@@ -404,6 +434,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       // the buffer of step s-1; the value waves weigh step s meanwhile
       for (int step = 0; step < nsteps; ++step) {
         __builtin_amdgcn_s_waitcnt(kWaitNext);   // step s+1's rows (step s+2's in flight)
+        expand(step + 1);
         __syncthreads();
         issue(step + kDepth);
         scores_raw(step + 1, acc);               // past the last step: P = 0, never read
@@ -486,9 +517,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int key = (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4));
-          uint2 v;
-          if constexpr (KV8) v = e4m3x4_bf16(*reinterpret_cast<const uint32_t*>(T8 + key * kRow + 128 * vw + 64 * hh + 4 * c));
-          else v = *reinterpret_cast<const uint2*>(T8 + key * kRow + (128 * vw + 64 * hh + 4 * c) * 2);
+          const uint2 v = *reinterpret_cast<const uint2*>(T8 + key * kRow + (128 * vw + 64 * hh + 4 * c) * 2);
           R[hh][j][0] = v.x;
           R[hh][j][1] = v.y;
         }
@@ -524,10 +553,12 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
         for (int j = 0; j < kDepth; ++j) issue(j);
       }
       __builtin_amdgcn_s_waitcnt(kWaitLater);
+      expand(0);
       __syncthreads();
       __syncthreads();   // (the score waves' step-0 maxima)
       for (int step = 0; step < nsteps; ++step) {
         __builtin_amdgcn_s_waitcnt(kWaitNext);
+        expand(step + 1);
         __syncthreads();
         issue(step + kDepth);
         values(step);

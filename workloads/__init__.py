@@ -381,6 +381,9 @@ MORE_WORKLOADS = {
                                         key_dtype="fp8"),
     # the headline decode batch with the 4-bit indexer cache (MXFP4 keys)
     "decode-b128-ctx128k-mxfp4": dict(kind="decode", B=128, n_raw=131072, ratio=2, key_dtype="mxfp4"),
+    # the headline decode batch with e4m3 latent and window rows (fp32 row scales)
+    "decode-b128-ctx128k-fp8kv": dict(kind="decode", B=128, n_raw=131072, ratio=2, key_dtype="fp8",
+                                      kv_dtype="fp8"),
     # a ragged serving batch at 128K context: two 1024-query prefill chunks, 64 single decode
     # queries and 16 decode steps with 5 drafted tokens (2208 queries, 82 sequences)
     "ragged-2x1024+64+16x6-ctx128k-fp8": dict(kind="ragged", n_raw=[131072] * 82,
