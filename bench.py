@@ -17,7 +17,8 @@ A third times a multi-token decode step: 128 sequences x 6 queries (a verified t
 the headline decode batch with MXFP4 index keys (the 4-bit indexer cache), and a fifth its
 indexer, selection and attention on paged stores (64-row pages, block tables). A sixth
 times a ragged serving batch (prefill chunks, drafted decode steps and single decode queries
-in one call), and a seventh the headline batch with e4m3 latent and window rows.
+in one call), a seventh the headline batch with e4m3 latent and window rows, and an eighth
+with MXFP4 latent rows and e4m3 window rows.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-prefill] [--no-rescore] [--no-multiquery] [--no-mxfp4] [--no-paged]
@@ -378,7 +379,8 @@ def main():
     ap.add_argument("--no-mxfp4", action="store_true")
     ap.add_argument("--no-paged", action="store_true")
     ap.add_argument("--fp8kv-workload", default="decode-b128-ctx128k-fp8kv")
-    ap.add_argument("--no-fp8kv", action="store_true")
+    ap.add_argument("--fp4kv-workload", default="decode-b128-ctx128k-fp4kv")
+    ap.add_argument("--no-fp8kv", action="store_true", help="skip the e4m3 and MXFP4 latent-row batches")
     ap.add_argument("--ragged-workload", default="ragged-2x1024+64+16x6-ctx128k-fp8")
     ap.add_argument("--no-ragged", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -533,21 +535,23 @@ def main():
         del dx, wx
         torch.cuda.empty_cache()
 
-    if not args.no_fp8kv and not args.profile:
+    kv_cases = [("fp8_kv", args.fp8kv_workload, "e4m3 latent and window rows"),
+                ("mxfp4_kv", args.fp4kv_workload, "MXFP4 latent rows and e4m3 window rows")]
+    for key, name, rows in kv_cases if not args.no_fp8kv and not args.profile else []:
         t0 = time.perf_counter()
-        wk = W.make(args.fp8kv_workload)
+        wk = W.make(name)
         dk = DeviceBatch(wk)
         torch.cuda.synchronize()
-        log(f"e4m3-KV decode inputs ready in {time.perf_counter() - t0:.1f}s")
+        log(f"{key} decode inputs ready in {time.perf_counter() - t0:.1f}s")
         k_eager, kms = run_batch(torch, dk, args.steps, args.warmup)
         k_s, _ = run_graph(torch, dk, args.steps)
-        result["fp8_kv"] = {
-            "workload": args.fp8kv_workload, "queries": int(wk.T),
-            "what": "the headline batch with e4m3 latent and window rows (no compressor: it writes bf16 rows)",
+        result[key] = {
+            "workload": name, "queries": int(wk.T),
+            "what": f"the headline batch with {rows} (no compressor: it writes bf16 rows)",
             "ms_per_step": k_s * 1e3, "queries_per_s": wk.T / k_s, "eager_ms_per_step": k_eager * 1e3,
             "stage_ms": kms,
         }
-        log(f"e4m3-KV decode: {k_s * 1e3:.3f} ms/step, stages {kms}")
+        log(f"{key} decode: {k_s * 1e3:.3f} ms/step, stages {kms}")
         del dk, wk
         torch.cuda.empty_cache()
 

@@ -79,10 +79,16 @@ typedef enum sa_key_dtype {
 /* Latent and window store element type (the pages' FP8 window cache and 8-bit latents). */
 typedef enum sa_kv_dtype {
   SA_KV_BF16 = 0,       /* rows of 512 bf16 */
-  SA_KV_FP8_E4M3 = 1    /* rows of 512 OCP E4M3 codes plus one fp32 scale per row:
+  SA_KV_FP8_E4M3 = 1,   /* rows of 512 OCP E4M3 codes plus one fp32 scale per row:
                            X = scale * code. Read by sparse_attn_fwd (decoded exactly where
                            the MFMA operands are built); sparse_attn_compress writes bf16
                            rows and returns SA_EUNSUPPORTED for these plans */
+  SA_KV_MXFP4 = 2       /* the pages' FP4 compressed state with an FP8 window (DeepSeek-V4
+                           report, the KV cache section): latent rows of OCP MXFP4, 256 bytes
+                           of E2M1 (element 2i in the low nibble of byte i) plus 16 E8M0
+                           block scales (scale b for elements 32b .. 32b+31, X = 2^(scale-127)
+                           * element); window rows e4m3 as for SA_KV_FP8_E4M3. Same calls
+                           and limits as SA_KV_FP8_E4M3 */
 } sa_kv_dtype;
 
 typedef struct sa_params {
@@ -164,9 +170,14 @@ typedef struct sa_cache {
   /* e4m3 latents and window (plan kv_dtype SA_KV_FP8_E4M3): latents and window hold 512
    * codes per row and their *_seq_stride fields count bytes (multiples of 16); the fp32
    * row scales are latent_scales [num_seqs][compressed_cap] (or one per pool row when
-   * paged) and window_scales [num_seqs][window_cap]. */
-  const float* latent_scales;
-  int64_t latent_scales_seq_stride;  /* >= compressed_cap (ignored when paged) */
+   * paged) and window_scales [num_seqs][window_cap].
+   * MXFP4 latents (SA_KV_MXFP4): latents hold 256 bytes per row (latents_seq_stride in
+   * bytes, >= 256 * compressed_cap, a multiple of 16) and latent_scales 16 E8M0 bytes per
+   * row, [num_seqs][compressed_cap][16] or per pool row when paged (16-byte aligned,
+   * latent_scales_seq_stride in bytes); the window is e4m3 as above. */
+  const void* latent_scales;
+  int64_t latent_scales_seq_stride;  /* >= compressed_cap, or >= 16 * compressed_cap and a
+                                        multiple of 16 for MXFP4 (ignored when paged) */
   const float* window_scales;
   int64_t window_scales_seq_stride;  /* >= window_cap */
 } sa_cache;

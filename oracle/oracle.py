@@ -152,9 +152,10 @@ MX_BLOCK = 32
 
 
 def mxfp4_to_f64(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
-    """MXFP4 rows -> fp64 [..., 128]. codes: uint8 [..., 64], element 2i in the low nibble
-    of byte i and element 2i+1 in the high nibble; scales: uint8 E8M0 [..., 4], scale b for
-    elements 32b .. 32b+31. Element value = E8M0 scale * E2M1 element [MX]."""
+    """MXFP4 rows -> fp64 [..., 2B]. codes: uint8 [..., B] (64 for index keys, 256 for
+    latents), element 2i in the low nibble of byte i and element 2i+1 in the high nibble;
+    scales: uint8 E8M0 [..., B / 16], scale b for elements 32b .. 32b+31. Element value =
+    E8M0 scale * E2M1 element [MX]."""
     codes = np.asarray(codes, dtype=np.uint8)
     lo = E2M1_TABLE[codes & 0xF]
     hi = E2M1_TABLE[codes >> 4]
@@ -302,10 +303,14 @@ class Result:
 
 
 def kv_rows_f64(codes: np.ndarray, scales: Optional[np.ndarray]) -> np.ndarray:
-    """Exact latent / window rows: bf16 as stored, or e4m3 code * fp32 row scale (the FP8
-    latent and window caches of the pages, read like the e4m3 index keys)."""
+    """Exact latent / window rows: bf16 as stored, e4m3 code * fp32 row scale (the FP8
+    latent and window caches of the pages, read like the e4m3 index keys), or MXFP4 (the
+    pages' FP4 compressed state: uint8 codes [.., 256] with uint8 E8M0 block scales
+    [.., 16], read like the MXFP4 index keys)."""
     if scales is None:
         return bf16_to_f64(codes)
+    if np.asarray(scales).dtype == np.uint8:
+        return mxfp4_to_f64(codes, scales)
     return e4m3_to_f64(codes) * np.asarray(scales, dtype=np.float64)[..., None]
 
 

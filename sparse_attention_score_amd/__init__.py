@@ -21,8 +21,8 @@ LIB_PATH = os.environ.get("SPARSE_ATTN_LIB") or os.path.join(_PKG, "libsparse_at
 SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_EWORKSPACE, SA_EHIP = 0, 1, 2, 3, 4
 SA_KEY_BF16, SA_KEY_FP8_E4M3, SA_KEY_MXFP4 = 0, 1, 2
 KEY_DTYPES = {"bf16": SA_KEY_BF16, "fp8": SA_KEY_FP8_E4M3, "mxfp4": SA_KEY_MXFP4}
-SA_KV_BF16, SA_KV_FP8_E4M3 = 0, 1
-KV_DTYPES = {"bf16": SA_KV_BF16, "fp8": SA_KV_FP8_E4M3}
+SA_KV_BF16, SA_KV_FP8_E4M3, SA_KV_MXFP4 = 0, 1, 2
+KV_DTYPES = {"bf16": SA_KV_BF16, "fp8": SA_KV_FP8_E4M3, "mxfp4": SA_KV_MXFP4}
 STATUS_NAMES = {0: "SA_OK", 1: "SA_EINVAL", 2: "SA_EUNSUPPORTED", 3: "SA_EWORKSPACE", 4: "SA_EHIP"}
 
 EXPORTS = ("sparse_attn_plan", "sparse_attn_plan_destroy", "sparse_attn_last_error",
@@ -197,7 +197,9 @@ def _seq_stride(t: torch.Tensor) -> int:
 
 
 class Cache:
-    """sa_cache from device tensors: latents [S,cap,512] bf16, window [S,wcap,512] bf16,
+    """sa_cache from device tensors: latents [S,cap,512] bf16 or uint8 (e4m3 codes) or uint8
+    [S,cap,256] (MXFP4 codes), window [S,wcap,512] bf16 or uint8 (e4m3 codes), latent_scales
+    [S,cap] fp32 (e4m3) or uint8 [S,cap,16] (MXFP4 E8M0 scales), window_scales [S,wcap] fp32,
     idx_keys [S,cap,128] bf16 or uint8 (e4m3 codes), or uint8 [S,cap,64] (MXFP4 codes);
     idx_scales [S,cap] fp32 (e4m3), uint8 [S,cap,4] (MXFP4 E8M0 scales) or None.
     Any of them may be None when the call at hand does not read it."""
@@ -226,7 +228,9 @@ class Cache:
             _need(window, "window", window.dtype)
             c.window, c.window_seq_stride, c.window_cap = window.data_ptr(), _seq_stride(window), window.shape[1]
         if latent_scales is not None:
-            _need(latent_scales, "latent_scales", torch.float32)
+            if latent_scales.dtype not in (torch.float32, torch.uint8):
+                raise TypeError("latent_scales must be float32 (e4m3) or uint8 (MXFP4 E8M0)")
+            _need(latent_scales, "latent_scales", latent_scales.dtype)
             c.latent_scales, c.latent_scales_seq_stride = latent_scales.data_ptr(), _seq_stride(latent_scales)
         if window_scales is not None:
             _need(window_scales, "window_scales", torch.float32)

@@ -165,16 +165,25 @@ sa_status check_cache(const sa_plan* plan, const sa_queries* q, const sa_cache* 
   if (latents) {
     SA_REQUIRE(c->latents != nullptr && aligned16(c->latents), SA_EINVAL,
                "cache->latents is NULL or not 16-byte aligned");
-    // strides: bf16 elements, or bytes for e4m3 rows (512 either way per row, 16-byte rows)
-    const bool kv8 = plan->p.kv_dtype == SA_KV_FP8_E4M3;
-    const int64_t smul = kv8 ? 16 : 8;
-    SA_REQUIRE(paged || (c->latents_seq_stride >= c->compressed_cap * 512 && c->latents_seq_stride % smul == 0),
+    // strides: bf16 elements, or bytes for code rows (16-byte rows either way): latent rows
+    // of 512 elements (256 bytes for MXFP4), window rows of 512
+    const bool kv8 = plan->p.kv_dtype != SA_KV_BF16, fp4l = plan->p.kv_dtype == SA_KV_MXFP4;
+    const int64_t smul = kv8 ? 16 : 8, lrow = fp4l ? 256 : 512;
+    SA_REQUIRE(paged || (c->latents_seq_stride >= c->compressed_cap * lrow && c->latents_seq_stride % smul == 0),
                SA_EINVAL, "cache->latents_seq_stride = %lld invalid", (long long)c->latents_seq_stride);
     if (kv8) {
       SA_REQUIRE(c->latent_scales != nullptr && c->window_scales != nullptr, SA_EINVAL,
-                 "cache->latent_scales / window_scales NULL (required for e4m3 latents)");
-      SA_REQUIRE(paged || c->latent_scales_seq_stride >= c->compressed_cap, SA_EINVAL,
-                 "cache->latent_scales_seq_stride = %lld < compressed_cap", (long long)c->latent_scales_seq_stride);
+                 "cache->latent_scales / window_scales NULL (required for e4m3 and MXFP4 latents)");
+      if (fp4l) {
+        SA_REQUIRE(aligned16(c->latent_scales), SA_EINVAL, "cache->latent_scales not 16-byte aligned (MXFP4 latents)");
+        SA_REQUIRE(paged || (c->latent_scales_seq_stride >= 16 * c->compressed_cap &&
+                             c->latent_scales_seq_stride % 16 == 0),
+                   SA_EINVAL, "cache->latent_scales_seq_stride = %lld must be >= 16 * compressed_cap and a multiple of 16",
+                   (long long)c->latent_scales_seq_stride);
+      } else {
+        SA_REQUIRE(paged || c->latent_scales_seq_stride >= c->compressed_cap, SA_EINVAL,
+                   "cache->latent_scales_seq_stride = %lld < compressed_cap", (long long)c->latent_scales_seq_stride);
+      }
       SA_REQUIRE(c->window_scales_seq_stride >= c->window_cap, SA_EINVAL,
                  "cache->window_scales_seq_stride = %lld < window_cap", (long long)c->window_scales_seq_stride);
     }
@@ -278,7 +287,8 @@ sa_status sparse_attn_plan(const sa_params* p, sa_plan** plan, size_t* workspace
   SA_REQUIRE(p->idx_key_dtype == SA_KEY_BF16 || p->idx_key_dtype == SA_KEY_FP8_E4M3 ||
                  p->idx_key_dtype == SA_KEY_MXFP4,
              SA_EUNSUPPORTED, "idx_key_dtype %d unknown", p->idx_key_dtype);
-  SA_REQUIRE(p->kv_dtype == SA_KV_BF16 || p->kv_dtype == SA_KV_FP8_E4M3, SA_EUNSUPPORTED,
+  SA_REQUIRE(p->kv_dtype == SA_KV_BF16 || p->kv_dtype == SA_KV_FP8_E4M3 || p->kv_dtype == SA_KV_MXFP4,
+             SA_EUNSUPPORTED,
              "kv_dtype %d unknown", p->kv_dtype);
   SA_REQUIRE(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f, SA_EINVAL,
              "softmax_scale must be finite and > 0");
@@ -495,7 +505,7 @@ sa_status sparse_attn_fwd(const sa_plan* plan, const sa_queries* q, const sa_cac
   sa::AttnArgs a;
   a.m = meta(plan, q, c->num_seqs, c->compressed_cap);
   a.pages = page_table(c);
-  a.kv_fp8 = plan->p.kv_dtype == SA_KV_FP8_E4M3;
+  a.kv_mode = plan->p.kv_dtype;
   a.latent_scales = c->latent_scales;
   a.latent_scales_seq_stride = c->latent_scales_seq_stride;
   a.window_scales = c->window_scales;
@@ -551,7 +561,7 @@ sa_status sparse_attn_compress(const sa_plan* plan, const void* raw, int64_t raw
   if ((st = check_plan(plan)) != SA_OK) return st;
   const int r = plan->p.ratio;
   SA_REQUIRE(plan->p.kv_dtype == SA_KV_BF16, SA_EUNSUPPORTED,
-             "the compressor writes bf16 rows (plan kv_dtype is e4m3)");
+             "the compressor writes bf16 rows (plan kv_dtype is e4m3 or MXFP4)");
   SA_REQUIRE(G >= 0, SA_EINVAL, "G = %lld < 0", (long long)G);
   SA_REQUIRE(raw && aligned16(raw) && out && aligned16(out), SA_EINVAL,
              "raw / out NULL or not 16-byte aligned");

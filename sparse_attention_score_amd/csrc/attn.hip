@@ -135,12 +135,19 @@ __device__ __forceinline__ uint2 e4m3x4_bf16(uint32_t x) {
                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true))};
 }
 
-// KV8: the latents and the window are e4m3 rows with one fp32 scale each (X_j = s_j code_j):
-// rows travel as 512 bytes and are widened exactly to bf16 codes in LDS, once per step by
-// the wave that loaded them; the raw score of key j is multiplied by s_j, and so is P_j
-// before the values (the normaliser sums the unscaled P).
-template <int HS, bool KV8>
+// a 1.0 that the scale slots of MXFP4 rows (their scales are applied while widening) and
+// of slots past the key list load
+__device__ float g_unit_scale = 1.0f;
+
+// KVM: 0 bf16 rows. 1: the latents and the window are e4m3 rows with one fp32 scale each
+// (X_j = s_j code_j). 2: MXFP4 latents (256 bytes of E2M1 plus 16 E8M0 block scales per
+// row) and an e4m3 window. Code rows travel as they are stored and are widened exactly to
+// bf16 in LDS, once per step by the wave that loaded them (MXFP4 rows with their block
+// scales); the raw score of key j is multiplied by its row scale s_j (1 for MXFP4), and so
+// is P_j before the values (the normaliser sums the unscaled P).
+template <int HS, int KVM>
 __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
+  constexpr bool KV8 = KVM != 0, FP4L = KVM == 2;
   // HS = 2: the query's heads are split over two work-groups (32 each) that gather the same
   // rows (normally on one XCD, so the second reads them from L2); no key splits then
   static_assert(HS == 1 || HS == 2, "one or two head sets");
@@ -202,7 +209,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   __syncthreads();
 
   // ---- key list: selected latents in topk order, then the window ----
-  int m = 0;
+  int m = 0, nlat = 0;   // keys; the first nlat of them are latents
   if (valid_q) {
     const int32_t j = sh.topk[tid];   // kAThreads == kTopK
     const bool v = j >= 0 && j < n;
@@ -214,32 +221,40 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       nsel += sh.wave_cnt[w];
       before += (w < wave) ? sh.wave_cnt[w] : 0;
     }
-    // global row of each key (and, for e4m3 rows, where its scale is). Strides are in
-    // elements of the store: bf16, or bytes for e4m3 rows.
-    constexpr int RB = KV8 ? kDim : 2 * kDim;   // row bytes
+    // global row of each key (and, for code rows, where its scale is: an fp32, or the 16
+    // E8M0 bytes of an MXFP4 row). Strides are in elements of the store: bf16, or bytes.
+    constexpr int LRB = FP4L ? kDim / 2 : (KV8 ? kDim : 2 * kDim);   // latent row bytes
+    constexpr int WRB = KV8 ? kDim : 2 * kDim;                       // window row bytes
     const uint8_t* latb = reinterpret_cast<const uint8_t*>(a.latents);
     if (v) {
       int64_t off, sidx;
       if (a.pages.table) {   // paged latents: the row of position j is in page table[seq][j / page]
         const int64_t r = pool_row(a.pages, page_of(a.pages, seq, j), j);
-        off = r * RB;
+        off = r * LRB;
         sidx = r;
       } else {
-        off = (int64_t)seq * a.latents_seq_stride * (KV8 ? 1 : 2) + (int64_t)j * RB;
-        sidx = (int64_t)seq * a.latent_scales_seq_stride + j;
+        off = (int64_t)seq * a.latents_seq_stride * (KV8 ? 1 : 2) + (int64_t)j * LRB;
+        sidx = FP4L ? -1 : (int64_t)seq * a.latent_scales_seq_stride + j;
       }
       sh.rows[before + incl - 1] = reinterpret_cast<const uint16_t*>(latb + off);
-      if (KV8) sh.sptr[before + incl - 1] = a.latent_scales + sidx;
+      if constexpr (FP4L) {
+        const uint8_t* sb = reinterpret_cast<const uint8_t*>(a.latent_scales) +
+                            (a.pages.table ? sidx * 16 : (int64_t)seq * a.latent_scales_seq_stride + (int64_t)j * 16);
+        sh.sptr[before + incl - 1] = reinterpret_cast<const float*>(sb);
+      } else if constexpr (KV8) {
+        sh.sptr[before + incl - 1] = reinterpret_cast<const float*>(a.latent_scales) + sidx;
+      }
     }
     const int u0 = p - kWindow + 1 > 0 ? p - kWindow + 1 : 0;
     const int nwin = p - u0 + 1;
     if (tid < nwin) {
       const int64_t wr = (int64_t)((u0 + tid) % a.window_cap);
       sh.rows[nsel + tid] = reinterpret_cast<const uint16_t*>(
-          reinterpret_cast<const uint8_t*>(a.window) + (int64_t)seq * a.window_seq_stride * (KV8 ? 1 : 2) + wr * RB);
+          reinterpret_cast<const uint8_t*>(a.window) + (int64_t)seq * a.window_seq_stride * (KV8 ? 1 : 2) + wr * WRB);
       if (KV8) sh.sptr[nsel + tid] = a.window_scales + (int64_t)seq * a.window_scales_seq_stride + wr;
     }
     m = nsel + nwin;
+    nlat = nsel;
   }
   __syncthreads();
 
@@ -268,41 +283,99 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
     for (int i = 0; i < kRowsPerWave; ++i) r[i] = sh.rows[kb + min(step * kKT + wave * kRowsPerWave + i, mk - 1)];
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
-      if constexpr (KV8) row8_to_lds(r[i], base + i * kRow, lane);
-      else row_to_lds(r[i], base + i * kRow, lane);
+      const int idx = kb + min(step * kKT + wave * kRowsPerWave + i, mk - 1);
+      if (FP4L && idx < nlat) {   // 256 code bytes (lanes 0-15) and 16 scale bytes (lane 16)
+        const uint8_t* src = lane < 16 ? reinterpret_cast<const uint8_t*>(r[i]) + 16 * lane
+                                       : reinterpret_cast<const uint8_t*>(sh.sptr[idx]);
+        if (lane <= 16) to_lds16(src, base + i * kRow);
+      } else if constexpr (KV8) {
+        row8_to_lds(r[i], base + i * kRow, lane);
+      } else {
+        row_to_lds(r[i], base + i * kRow, lane);
+      }
     }
   };
   // e4m3 rows: each wave widens the rows it loaded, in place (codes in the first 512 bytes
   // of a slot become 1 KiB of bf16), after its own wait and before the barrier that hands
   // the step to the other waves. All of a lane's reads come before its writes, and a
   // wave's LDS operations run in order, so no code is overwritten before it is read.
+  // e4m3 rows: chunk q (16 codes) of row rr, 2 chunks per lane (4 rows x 32 chunks);
+  // MXFP4 rows: code dword e of block q of row rr, lane 4q + e, with block q's scale byte
+  // (after the 256 code bytes): 8 elements per lane and row, contiguous 16-byte writes.
+  // Every read of a row comes before its first write.
+  auto e4m3_rows = [&](uint8_t* base) {
+    u32x4 cv[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int ch = lane + 64 * h, rr = ch >> 5, q = ch & 31;
+      cv[h] = *reinterpret_cast<const u32x4*>(base + rr * kRow + 16 * q);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int ch = lane + 64 * h, rr = ch >> 5, q = ch & 31;
+      uint2 b[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b[e] = e4m3x4_bf16(cv[h][e]);
+      *reinterpret_cast<u32x4*>(base + rr * kRow + 32 * q) = u32x4{b[0].x, b[0].y, b[1].x, b[1].y};
+      *reinterpret_cast<u32x4*>(base + rr * kRow + 32 * q + 16) = u32x4{b[2].x, b[2].y, b[3].x, b[3].y};
+    }
+  };
+  auto fp4_write = [&](uint8_t* row, uint32_t codes, uint32_t sbyte) {
+    const float bs = e8m0_scale(sbyte);
+    const u32x4 u = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, bs, 0)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, bs, 1)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, bs, 2)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, bs, 3))};
+    *reinterpret_cast<u32x4*>(row + 16 * lane) = u;   // elements 8 lane .. 8 lane + 7
+  };
   auto expand = [&](int step) {
     if constexpr (KV8) {
       uint8_t* base = sh.tile[step % kBufs] + wave * kRowsPerWave * kRow;
-      u32x4 cv[2];
+      if constexpr (!FP4L) {
+        e4m3_rows(base);
+      } else {
+        // list indices of the wave's rows ascend: latents (MXFP4) first, then the window
+        const int r0 = step * kKT + wave * kRowsPerWave;
+        const int first = kb + min(r0, mk - 1), last = kb + min(r0 + kRowsPerWave - 1, mk - 1);
+        if (first >= nlat) {
+          e4m3_rows(base);
+        } else if (last < nlat) {
+          uint32_t cw[kRowsPerWave], sb[kRowsPerWave];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {   // 16-code chunk q of row rr (2 per lane: 4 rows x 32)
-        const int ch = lane + 64 * h, rr = ch >> 5, q = ch & 31;
-        cv[h] = *reinterpret_cast<const u32x4*>(base + rr * kRow + 16 * q);
-      }
+          for (int rr = 0; rr < kRowsPerWave; ++rr) {
+            cw[rr] = *reinterpret_cast<const uint32_t*>(base + rr * kRow + 4 * lane);
+            sb[rr] = base[rr * kRow + kDim / 2 + (lane >> 2)];
+          }
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int ch = lane + 64 * h, rr = ch >> 5, q = ch & 31;
-        uint2 b[4];
+          for (int rr = 0; rr < kRowsPerWave; ++rr) fp4_write(base + rr * kRow, cw[rr], sb[rr]);
+        } else {   // the step where the latents end: row by row
+          for (int rr = 0; rr < kRowsPerWave; ++rr) {
+            uint8_t* row = base + rr * kRow;
+            if (kb + min(r0 + rr, mk - 1) < nlat) {
+              const uint32_t cw = *reinterpret_cast<const uint32_t*>(row + 4 * lane);
+              const uint32_t sb = row[kDim / 2 + (lane >> 2)];
+              fp4_write(row, cw, sb);
+            } else if (lane < 32) {
+              const u32x4 cv = *reinterpret_cast<const u32x4*>(row + 16 * lane);
+              uint2 b[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) b[e] = e4m3x4_bf16(cv[h][e]);
-        *reinterpret_cast<u32x4*>(base + rr * kRow + 32 * q) = u32x4{b[0].x, b[0].y, b[1].x, b[1].y};
-        *reinterpret_cast<u32x4*>(base + rr * kRow + 32 * q + 16) = u32x4{b[2].x, b[2].y, b[3].x, b[3].y};
+              for (int e = 0; e < 4; ++e) b[e] = e4m3x4_bf16(cv[e]);
+              *reinterpret_cast<u32x4*>(row + 32 * lane) = u32x4{b[0].x, b[0].y, b[1].x, b[1].y};
+              *reinterpret_cast<u32x4*>(row + 32 * lane + 16) = u32x4{b[2].x, b[2].y, b[3].x, b[3].y};
+            }
+          }
+        }
       }
     }
   };
 
-  // e4m3 rows: the slots' scales by direct loads (slots past the list read the first
-  // slot's), issued before the first rows so the rows' waits cover them
+  // code rows: the slots' scales by direct loads, issued before the first rows so the
+  // rows' waits cover them
   if constexpr (KV8) {
     for (int i = wave; i < kMaxKeys / 64; i += kAW) {
       const int slot = 64 * i + lane;
-      to_lds4(sh.sptr[slot < m ? slot : 0], (uint32_t)(uintptr_t)&sh.rscale[64 * i]);
+      const float* src = (FP4L && slot < nlat) || slot >= m ? &g_unit_scale : sh.sptr[slot];
+      to_lds4(src, (uint32_t)(uintptr_t)&sh.rscale[64 * i]);
     }
   }
   // ---- score waves: query heads 16(2hp + j) + c as B operands (k-step s: dims
@@ -700,15 +773,19 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   const int hs = attn_head_sets(a.m.T, a.splits);
   const int64_t u8 = (a.m.T * a.splits * hs + 7) / 8;   // work units per XCD
   if (hs == 2)
-    if (a.kv_fp8)
-      hipLaunchKernelGGL((attn_kernel<2, true>), dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
+    if (a.kv_mode == 2)
+      hipLaunchKernelGGL((attn_kernel<2, 2>), dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
+    else if (a.kv_mode == 1)
+      hipLaunchKernelGGL((attn_kernel<2, 1>), dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_kernel<2, false>), dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
+      hipLaunchKernelGGL((attn_kernel<2, 0>), dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
   else
-    if (a.kv_fp8)
-      hipLaunchKernelGGL((attn_kernel<1, true>), dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
+    if (a.kv_mode == 2)
+      hipLaunchKernelGGL((attn_kernel<1, 2>), dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
+    else if (a.kv_mode == 1)
+      hipLaunchKernelGGL((attn_kernel<1, 1>), dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL((attn_kernel<1, false>), dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
+      hipLaunchKernelGGL((attn_kernel<1, 0>), dim3((unsigned)(8 * u8)), dim3(kAThreads), 0, stream, a);
   return hipGetLastError();
 }
 

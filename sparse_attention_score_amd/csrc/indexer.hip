@@ -393,10 +393,6 @@ struct MxShared {
 __device__ __forceinline__ int mx_pos(int r, int q) { return q ^ ((r >> 2) & 3); }
 __device__ __forceinline__ int kdim_mx(int g, int s) { return 32 * g + 8 * s; }
 
-// E8M0 code -> fp32 scale 2^(e-127) (e = 0 is the fp32 subnormal 2^-127, 255 is NaN).
-__device__ __forceinline__ float e8m0_scale(uint32_t e) {
-  return __uint_as_float(e == 0 ? 0x00400000u : (e == 255 ? 0x7FC00000u : e << 23));
-}
 
 __global__ __launch_bounds__(kDThreads) void indexer_mx_kernel(IndexerArgs a) {
   constexpr int RB = kMxRB, TB = 16 * kMxRB, D = kMxD;

@@ -47,6 +47,11 @@ __device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t codes, uint32_t& lo, u
   hi = __builtin_amdgcn_perm(__float_as_uint(f23[1]), __float_as_uint(f23[0]), 0x07060302u);
 }
 
+// E8M0 code -> fp32 scale 2^(e-127) (e = 0 is the fp32 subnormal 2^-127, 255 is NaN).
+__device__ __forceinline__ float e8m0_scale(uint32_t e) {
+  return __uint_as_float(e == 0 ? 0x00400000u : (e == 255 ? 0x7FC00000u : e << 23));
+}
+
 // max(x, 0) as one integer max: negative floats (sign bit set) are negative int32s, and
 // +0, positive floats and +inf keep their bits. Exact for every non-NaN input.
 __device__ __forceinline__ float relu(float x) {

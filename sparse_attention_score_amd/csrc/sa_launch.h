@@ -93,10 +93,12 @@ struct AttnArgs {
   float* part_ml;           // [T * splits][64][2] reference (log2 domain) and normaliser
   uint32_t* counters;       // [T]
   PageTable pages;          // latents are a page pool when pages.table is set
-  // e4m3 latents and window: rows of 512 codes (strides above in bytes then), one fp32
-  // scale per row ([seq][cap] / [seq][wcap], or the pool's rows when paged)
-  bool kv_fp8;
-  const float* latent_scales;
+  // kv_mode 1: e4m3 latents and window, rows of 512 codes (strides above in bytes then),
+  // one fp32 scale per row ([seq][cap] / [seq][wcap], or the pool's rows when paged).
+  // kv_mode 2: MXFP4 latents (256 code bytes per row, latent_scales 16 E8M0 bytes per row,
+  // its stride in bytes) and an e4m3 window.
+  int kv_mode;
+  const void* latent_scales;
   int64_t latent_scales_seq_stride;
   const float* window_scales;
   int64_t window_scales_seq_stride;

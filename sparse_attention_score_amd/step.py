@@ -40,7 +40,7 @@ class DeviceBatch:
         self.qI = to_device_bf16(wl.qI, dev)
         self.w = torch.from_numpy(wl.w).to(dev)
         self.CS = self.RS = None
-        if kv == "fp8":   # e4m3 latent and window rows with fp32 row scales
+        if kv in ("fp8", "mxfp4"):   # code rows with their scales (e4m3 window either way)
             self.C = torch.from_numpy(np.ascontiguousarray(wl.C)).to(dev)
             self.R = torch.from_numpy(np.ascontiguousarray(wl.R)).to(dev)
             self.CS = torch.from_numpy(np.ascontiguousarray(wl.CS)).to(dev)

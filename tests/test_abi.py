@@ -223,3 +223,27 @@ def test_compress_rejects():
     assert lib.sparse_attn_compress(p.handle, 0x1000, 1024, None, 1024, 0x2000, 0x3000, 512, 4, None) == S.SA_EINVAL
     assert lib.sparse_attn_compress(p.handle, 0x1000, 1024, 0x1000, 1024, 0x2000, 0x3000, 512, -1, None) == S.SA_EINVAL
     assert lib.sparse_attn_compress(None, 0x1000, 1024, 0x1000, 1024, 0x2000, 0x3000, 512, 4, None) == S.SA_EINVAL
+
+
+@pytest.mark.parametrize("case", ["no_latent_scales", "no_window_scales", "lat_stride_small",
+                                  "lat_stride_odd", "scale_stride_small", "scale_stride_odd",
+                                  "scales_misaligned"])
+def test_mxfp4_latent_rejects(case):
+    # MXFP4 latent rows: 256 code bytes and 16 E8M0 bytes per row, strides in bytes
+    p = _plan(kv_dtype="mxfp4")
+    q = _q()
+    good = dict(latents_seq_stride=1000 * 256, window_seq_stride=128 * 512,
+                latent_scales=0x70000, latent_scales_seq_stride=1000 * 16,
+                window_scales=0x80000, window_scales_seq_stride=128)
+    bad = {"no_latent_scales": dict(latent_scales=None), "no_window_scales": dict(window_scales=None),
+           "lat_stride_small": dict(latents_seq_stride=999 * 256),
+           "lat_stride_odd": dict(latents_seq_stride=1000 * 256 + 8),
+           "scale_stride_small": dict(latent_scales_seq_stride=999 * 16),
+           "scale_stride_odd": dict(latent_scales_seq_stride=1000 * 16 + 4),
+           "scales_misaligned": dict(latent_scales=0x70004)}[case]
+    c = _c(**{**good, **bad})
+    assert S.lib.sparse_attn_fwd(p.handle, ctypes.byref(q), ctypes.byref(c), 0x40000, 0x50000,
+                                 0x60000, None, None, 0, None) == S.SA_EINVAL
+    assert b"latent" in S.lib.sparse_attn_last_error() or b"window" in S.lib.sparse_attn_last_error()
+    assert S.lib.sparse_attn_compress(p.handle, 0x1000, 1024, 0x1000, 1024, 0x2000, 0x3000, 512, 4,
+                                      None) == S.SA_EUNSUPPORTED

@@ -44,10 +44,10 @@ def _paged_cache(d, P, seed, spare=3):
                 pool[pg * P:pg * P + (r1 - r0)] = x[b, r0:r1]
         return pool
 
-    lat = pool_of(d.C, (512,))
+    lat = pool_of(d.C, tuple(d.C.shape[2:]))
     keys = pool_of(d.KI, (128,))
     scales = pool_of(d.KS, ()) if d.KS is not None else None
-    lscales = pool_of(d.CS, ()) if d.CS is not None else None
+    lscales = pool_of(d.CS, tuple(d.CS.shape[2:])) if d.CS is not None else None
     cache = S.Cache(latents=lat, window=d.R, idx_keys=keys, idx_scales=scales, num_seqs=B,
                     compressed_cap=cap, block_table=table, page_size=P, latent_scales=lscales,
                     window_scales=d.RS)
@@ -132,9 +132,10 @@ def test_paged_group_and_ragged_match_contiguous(kind):
     _same(d, res_p, res_c)
 
 
-def test_paged_fp8_latents_match_contiguous():
-    wl = W.make_decode(B=4, n_raw=[40006, 3000, 1, 35], ratio=2, key_dtype="fp8", kv_dtype="fp8",
-                       name="paged-fp8kv", seed=57)
+@pytest.mark.parametrize("kv", ["fp8", "mxfp4"])
+def test_paged_code_latents_match_contiguous(kv):
+    wl = W.make_decode(B=4, n_raw=[40006, 3000, 1, 35], ratio=2, key_dtype="fp8", kv_dtype=kv,
+                       name=f"paged-{kv}kv", seed=57)
     d = _batch(wl)
     res_c = _run(d, d.cache)
     res_p = _run(d, _paged_cache(d, 64, seed=9))

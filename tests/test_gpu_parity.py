@@ -119,6 +119,24 @@ def test_fp8_latents_and_window(B, n_raw):
     _e2e(wl)
 
 
+@pytest.mark.parametrize("B,n_raw", [(6, [40006, 3001, 2, 130, 1031, 9000]), (40, 5000)])
+def test_mxfp4_latents_fp8_window(B, n_raw):
+    # MXFP4 latent rows (E8M0 scale per 32 elements) with e4m3 window rows: key splits, two
+    # head sets, pruning and tiny contexts
+    wl = W.make_decode(B=B, n_raw=n_raw, ratio=2, key_dtype="fp8", kv_dtype="mxfp4",
+                       name=f"fp4kv-{B}", seed=43)
+    _e2e(wl)
+
+
+def test_mxfp4_latents_prefill_chunk():
+    wl = W.make_prefill(T=150, offset=3000, ratio=1, key_dtype="bf16", name="fp4kv-prefill", seed=44)
+    import workloads as Wm
+    C, CS = Wm.normal_mxfp4_rows(44, "C", 0, wl.nc_cap, 512)
+    R, RS = Wm.normal_e4m3_rows(44, "R", 0, wl.wcap, 512)
+    wl.C, wl.R, wl.CS, wl.RS, wl.kv_dtype = C[None], R[None], CS[None], RS[None], "mxfp4"
+    _e2e(wl)
+
+
 def test_fp8_latents_prefill_chunk():
     # one work-group per query (150 queries), ratio 1
     wl = W.make_prefill(T=150, offset=3000, ratio=1, key_dtype="bf16", name="fp8kv-prefill", seed=42)

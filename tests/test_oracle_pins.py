@@ -149,6 +149,40 @@ def test_fp8_kv_rows_with_power_of_two_scales_equal_bf16_rows():
         assert np.array_equal(r8.o[t], rb.o[t]) and np.array_equal(r8.lse[t], rb.lse[t])
 
 
+def test_mxfp4_latent_rows_equal_bf16_rows():
+    # MXFP4 latent rows (256 bytes, 16 block scales) are exact bf16 values: the attention over
+    # them (e4m3 window with power-of-two row scales) equals the attention over the same rows
+    # stored as bf16. The bf16 rows are built from a per-element decode written here (E2M1
+    # sign, exponent, mantissa fields; one scale per 32 elements), rounded by torch.
+    import workloads as W
+    wl4 = W.make_decode(B=2, n_raw=[1100, 90], ratio=2, key_dtype="bf16", kv_dtype="mxfp4", seed=4)
+    wl4.RS[:] = 2.0 ** np.round(np.log2(wl4.RS))
+    wlb = W.make_decode(B=2, n_raw=[1100, 90], ratio=2, key_dtype="bf16", seed=4, with_compress=False)
+
+    def e2m1(code):
+        s, e, m = code >> 3, (code >> 1) & 3, code & 1
+        v = m * 0.5 if e == 0 else (1 + m / 2) * 2.0 ** (e - 1)
+        return -v if s else v
+
+    for b in range(2):
+        codes, sc = wl4.C[b], wl4.CS[b]
+        assert codes.shape == (wl4.nc_cap, 256) and sc.shape == (wl4.nc_cap, 16)
+        x = np.empty((wl4.nc_cap, 512))
+        for r in range(wl4.nc_cap):
+            for k in range(512):
+                byte = int(codes[r, k // 2])
+                x[r, k] = e2m1(byte >> 4 if k % 2 else byte & 15) * 2.0 ** (int(sc[r, k // 32]) - 127)
+        assert np.array_equal(O.kv_rows_f64(codes, sc), x)
+        wlb.C[b] = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        rv = O.kv_rows_f64(wl4.R[b], wl4.RS[b])
+        wlb.R[b] = torch.from_numpy(rv).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(O.bf16_to_f64(wlb.C[b]), x) and np.array_equal(O.bf16_to_f64(wlb.R[b]), rv)
+    r4, rb = O.run(wl4), O.run(wlb)
+    for t in range(2):
+        assert np.array_equal(r4.idx[t], rb.idx[t])
+        assert np.array_equal(r4.o[t], rb.o[t]) and np.array_equal(r4.lse[t], rb.lse[t])
+
+
 def test_bf16_matches_torch():
     rng = np.random.default_rng(1)
     x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 10 ** rng.uniform(-30, 30, 20000).astype(np.float32),

@@ -178,7 +178,8 @@ class Workload:
     meta: dict = field(default_factory=dict)
     group: int = 0       # consecutive queries that share a sequence (multi-token decode)
     runs: Optional[list] = None   # ragged batch: lengths of the runs of one sequence each
-    kv_dtype: str = "bf16"        # latents and window: "bf16", or "fp8" (e4m3 codes + row scales)
+    kv_dtype: str = "bf16"        # latents and window: "bf16", "fp8" (e4m3 codes + row scales),
+                                  # or "mxfp4" (MXFP4 latents + E8M0 block scales, e4m3 window)
     CS: Optional[np.ndarray] = None   # fp8 latents: fp32 row scales [B, nc_cap]
     RS: Optional[np.ndarray] = None   # fp8 window: fp32 row scales [B, wcap]
 
@@ -219,7 +220,9 @@ def make_decode(B: int, n_raw, ratio: int = 2, key_dtype: str = "bf16", seed: in
                 with_compress: bool = True, kv_dtype: str = "bf16") -> Workload:
     """B sequences, one decode query each at raw position n_raw-1 (per-sequence if an array).
     kv_dtype "fp8": latents and window rows are N(0,1) rows quantised to e4m3 with one fp32
-    scale per row (no compressor inputs then: the compressor writes bf16 rows)."""
+    scale per row (no compressor inputs then: the compressor writes bf16 rows). kv_dtype
+    "mxfp4": N(0,1) latent rows quantised to MXFP4 (E8M0 scale per 32 elements) and e4m3
+    window rows as for "fp8"."""
     n_raw = np.broadcast_to(np.asarray(n_raw, dtype=np.int64), (B,)).copy()
     pos = (n_raw - 1).astype(np.int32)
     vis = (pos.astype(np.int64) + 1) // ratio
@@ -241,13 +244,17 @@ def make_decode(B: int, n_raw, ratio: int = 2, key_dtype: str = "bf16", seed: in
             R[b] = normal_bf16(seed, "R", b, (wcap, DIM))
     KI, KS = _keys(seed, key_dtype, B, nc_cap)
     CS = RS = None
-    if kv_dtype == "fp8":
-        C = np.empty((B, nc_cap, DIM), np.uint8)
+    if kv_dtype in ("fp8", "mxfp4"):
+        fp4 = kv_dtype == "mxfp4"
+        C = np.empty((B, nc_cap, DIM // 2 if fp4 else DIM), np.uint8)
         R = np.empty((B, wcap, DIM), np.uint8)
-        CS = np.empty((B, nc_cap), np.float32)
+        CS = np.empty((B, nc_cap, DIM // 32), np.uint8) if fp4 else np.empty((B, nc_cap), np.float32)
         RS = np.empty((B, wcap), np.float32)
         for b in range(B):
-            C[b], CS[b] = normal_e4m3_rows(seed, "C", b, nc_cap, DIM)
+            if fp4:
+                C[b], CS[b] = normal_mxfp4_rows(seed, "C", b, nc_cap, DIM)
+            else:
+                C[b], CS[b] = normal_e4m3_rows(seed, "C", b, nc_cap, DIM)
             R[b], RS[b] = normal_e4m3_rows(seed, "R", b, wcap, DIM)
         with_compress = False
     Xp = Zp = beta = None
@@ -384,6 +391,9 @@ MORE_WORKLOADS = {
     # the headline decode batch with e4m3 latent and window rows (fp32 row scales)
     "decode-b128-ctx128k-fp8kv": dict(kind="decode", B=128, n_raw=131072, ratio=2, key_dtype="fp8",
                                       kv_dtype="fp8"),
+    # ... and with MXFP4 latent rows (the 4-bit compressed state) and e4m3 window rows
+    "decode-b128-ctx128k-fp4kv": dict(kind="decode", B=128, n_raw=131072, ratio=2, key_dtype="fp8",
+                                      kv_dtype="mxfp4"),
     # a ragged serving batch at 128K context: two 1024-query prefill chunks, 64 single decode
     # queries and 16 decode steps with 5 drafted tokens (2208 queries, 82 sequences)
     "ragged-2x1024+64+16x6-ctx128k-fp8": dict(kind="ragged", n_raw=[131072] * 82,
