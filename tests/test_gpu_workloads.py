@@ -1,4 +1,6 @@
-"""The five measured workloads at full size, in the launch configuration bench.py times.
+"""The measured workloads at full size, in the launch configuration bench.py times: the five
+layer configurations and the further batches bench.py reports (MXFP4 keys, e4m3 and MXFP4
+latent rows, the ragged serving batch; the multi-token batch has its own test).
 
 All queries are checked for properties that hold at any size (selection well-formed,
 block maxima consistent with the scores); a sample of queries per workload is checked
@@ -27,8 +29,27 @@ SAMPLES = {
 }
 
 
+# sampled queries of the further batches (ragged: first and last query of each prefill chunk,
+# single decode queries, the first and last query of a draft step)
+MORE_SAMPLES = {
+    "decode-b128-ctx128k-mxfp4": [0, 127],
+    "decode-b128-ctx128k-fp8kv": [0, 127],
+    "decode-b128-ctx128k-fp4kv": [0, 64, 127],
+    "ragged-2x1024+64+16x6-ctx128k-fp8": [0, 1023, 1024, 2047, 2048, 2111, 2112, 2117, 2207],
+}
+
+
 @pytest.mark.parametrize("name", list(W.WORKLOADS))
 def test_workload_full_size(name):
+    _full_size(name, SAMPLES[name])
+
+
+@pytest.mark.parametrize("name", list(MORE_SAMPLES))
+def test_more_workloads_full_size(name):
+    _full_size(name, MORE_SAMPLES[name])
+
+
+def _full_size(name, samples):
     assert torch.cuda.is_available()
     from sparse_attention_score_amd.step import DeviceBatch
     t0 = time.time()
@@ -54,8 +75,6 @@ def test_workload_full_size(name):
         assert np.all(np.diff(cand[t, :kc]) > 0), t
         # every selected position lies in a kept block
         assert np.all(np.isin(row[:k] // 8, cand[t, :kc])), t
-    o_gpu = None
-    samples = SAMPLES[name]
     keys_cache = {}
     C_new = O.step_compress(wl)
     for t in samples:
