@@ -19,7 +19,7 @@ def _snapshot(d):
 
 
 @pytest.mark.parametrize("name", ["decode-b4-ctx2k", "prefill-small", "ragged-small", "mq-small",
-                                  "mxfp4-small"])
+                                  "mxfp4-small", "fp4kv-small"])
 def test_graph_replays_match_eager(name):
     # ragged-small issues several indexer launches from one call (chunk, group, per-query)
     from sparse_attention_score_amd.step import DeviceBatch
@@ -34,6 +34,10 @@ def test_graph_replays_match_eager(name):
     elif name == "mxfp4-small":
         wl = W.make_decode(B=6, n_raw=[3001, 9000, 700, 40006, 64, 2], ratio=2, key_dtype="mxfp4",
                            name=name, seed=34, with_compress=False)
+    elif name == "fp4kv-small":
+        # MXFP4 latents and e4m3 window rows (key splits: 6 queries)
+        wl = W.make_decode(B=6, n_raw=[3001, 9000, 700, 40006, 64, 2], ratio=2, key_dtype="fp8",
+                           kv_dtype="mxfp4", name=name, seed=35)
     else:
         wl = W.make(name)
     print(f"[case] graph {name} T={wl.T}", flush=True)
