@@ -81,7 +81,8 @@ typedef enum sa_kv_dtype {
   SA_KV_BF16 = 0,       /* rows of 512 bf16 */
   SA_KV_FP8_E4M3 = 1,   /* rows of 512 OCP E4M3 codes plus one fp32 scale per row:
                            X = scale * code. Read by sparse_attn_fwd (decoded exactly where
-                           the MFMA operands are built); sparse_attn_compress writes bf16
+                           the MFMA operands are built) and written by
+                           sparse_attn_compress_codes; sparse_attn_compress writes bf16
                            rows and returns SA_EUNSUPPORTED for these plans */
   SA_KV_MXFP4 = 2       /* the pages' FP4 compressed state with an FP8 window (DeepSeek-V4
                            report, the KV cache section): latent rows of OCP MXFP4, 256 bytes
@@ -294,6 +295,27 @@ sa_status sparse_attn_compress(const sa_plan* plan, const void* raw, int64_t raw
                                const void* gate, int64_t gate_group_stride,
                                const float* slot_bias, void* out, int64_t out_group_stride,
                                int64_t G, void* stream);
+
+/* S0 into code rows: the compressor above, its fp32 result quantised into the e4m3 or MXFP4
+ * latent store of the plan's kv_dtype (the FP8 and FP4 caches of the DeepSeek-V4 report,
+ * KV cache section; bf16 plans return SA_EUNSUPPORTED). raw, gate, slot_bias and their
+ * strides as for sparse_attn_compress. Group g writes its code row at out + g*out_group_stride
+ * and its scales at out_scales + g*scales_group_stride (both strides in bytes):
+ *   SA_KV_FP8_E4M3: 512 e4m3 codes and one fp32 scale s = amax / 448 over the row (1 if the
+ *     row is zero); code = nearest e4m3 of x / s, ties to the even code.
+ *   SA_KV_MXFP4: 256 bytes of E2M1 (element 2i in the low nibble of byte i) and 16 E8M0
+ *     bytes; block b (elements 32b .. 32b+31) has exponent X = floor(log2 amax_b) - 2
+ *     (-127 if the block is zero, clamped to [-127, 127]), stored as X + 127; element =
+ *     nearest E2M1 of x * 2^-X, ties to the even code, saturating at 6.
+ * x is the compressor's fp32 value; divisions are IEEE fp32. out must be 16-byte aligned,
+ * out_group_stride >= the row bytes (512 or 256) and a multiple of 16; out_scales 4-byte
+ * aligned, scales_group_stride >= 4 (e4m3) or 16 (MXFP4) and a multiple of 4. Outputs must
+ * not overlap inputs. */
+sa_status sparse_attn_compress_codes(const sa_plan* plan, const void* raw, int64_t raw_group_stride,
+                                     const void* gate, int64_t gate_group_stride,
+                                     const float* slot_bias, void* out, int64_t out_group_stride,
+                                     void* out_scales, int64_t scales_group_stride, int64_t G,
+                                     void* stream);
 
 #ifdef __cplusplus
 }

@@ -164,6 +164,55 @@ def mxfp4_to_f64(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return elem * np.repeat(sc, MX_BLOCK, axis=-1)
 
 
+E4M3_MAX = 448.0
+_E4M3_POS = E4M3_TABLE[:0x7F]           # codes 0 .. 0x7E: the finite non-negative values, ascending
+_E2M1_POS = E2M1_TABLE[:8]              # codes 0 .. 7: 0, 0.5, 1, 1.5, 2, 3, 4, 6
+
+
+def _nearest_code(mag: np.ndarray, table: np.ndarray) -> np.ndarray:
+    """Code of the nearest value of an ascending table to each magnitude (exact in fp64);
+    a tie goes to the even code, magnitudes past the last value take the last code."""
+    mag = np.asarray(mag, np.float64)
+    hi = np.clip(np.searchsorted(table, mag, side="left"), 1, len(table) - 1)
+    lo = hi - 1
+    dlo, dhi = mag - table[lo], table[hi] - mag
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    return np.where(mag >= table[-1], len(table) - 1, code).astype(np.uint8)
+
+
+def _signed(code: np.ndarray, x: np.ndarray, sign_bit: int) -> np.ndarray:
+    neg = np.signbit(np.asarray(x))
+    return (code | np.where(neg, sign_bit, 0)).astype(np.uint8)
+
+
+def quantize_e4m3_rows(x: np.ndarray):
+    """Rows [.., 512] of compressor values -> (e4m3 codes, fp32 row scales) [OCP FP8]: the value
+    taken in fp32, s = amax / 448 in fp32 (1 for a zero row), code = nearest e4m3 of the fp32
+    quotient x / s, ties to the even code (values past 448 saturate)."""
+    x32 = np.asarray(x, np.float64).astype(np.float32)
+    amax = np.abs(x32).max(axis=-1)
+    s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    y = (x32 / s[..., None]).astype(np.float32)
+    return _signed(_nearest_code(np.abs(y), _E4M3_POS), y, 0x80), s
+
+
+def quantize_mxfp4_rows(x: np.ndarray):
+    """Rows [.., 512] of compressor values -> (MXFP4 codes [.., 256], E8M0 scales [.., 16])
+    [MX]: the value taken in fp32; per block of 32 elements X = floor(log2 amax) - 2 (-127 for a
+    zero block, clamped to [-127, 127]); element = nearest E2M1 of x 2^-X, ties to the even
+    code, saturating at 6; element 2i in the low nibble of byte i; scale byte X + 127."""
+    x32 = np.asarray(x, np.float64).astype(np.float32).astype(np.float64)
+    blocks = x32.reshape(x32.shape[:-1] + (-1, MX_BLOCK))
+    amax = np.abs(blocks).max(axis=-1)
+    _, e = np.frexp(amax)                          # amax = f 2^e, f in [0.5, 1)
+    X = np.where(amax > 0, np.clip(e - 3, -127, 127), -127)
+    y = blocks * np.exp2(-X)[..., None].astype(np.float64)
+    codes = _signed(_nearest_code(np.abs(y), _E2M1_POS), y, 0x8).reshape(x32.shape)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return packed, (X + 127).astype(np.uint8)
+
+
 def index_keys_f64(KI: np.ndarray, KS: Optional[np.ndarray]) -> np.ndarray:
     """Exact index keys: bf16 keys as stored, e4m3 code * fp32 row scale, or MXFP4
     (uint8 codes [.., 64] with uint8 E8M0 block scales [.., 4])."""
@@ -322,18 +371,30 @@ def compressed_rows(wl, b: int, n: int, rows: np.ndarray,
     CS = getattr(wl, "CS", None)
     X = kv_rows_f64(wl.C[b, rows], None if CS is None else CS[b, rows])
     if C_new_bits is not None and n > 0:
-        X[rows == n - 1] = bf16_to_f64(C_new_bits)
+        if isinstance(C_new_bits, tuple):   # a code row: (codes, scales)
+            X[rows == n - 1] = kv_rows_f64(C_new_bits[0][None], C_new_bits[1][None])[0]
+        else:
+            X[rows == n - 1] = bf16_to_f64(C_new_bits)
     return X
 
 
 def step_compress(wl) -> dict:
     """Compressor for the group completed by each sequence's query (ratio 2 decode).
 
-    Returns sequence -> (fp64 value, bf16 bits as stored)."""
+    Returns sequence -> (fp64 value, row as stored): bf16 bits, or (codes, scales) for the
+    e4m3 and MXFP4 latent stores."""
     out = {}
+    kv = getattr(wl, "kv_dtype", "bf16")
     for b in wl.compress_groups():
         v = compress(bf16_to_f64(wl.Xp[b])[None], bf16_to_f64(wl.Zp[b])[None], wl.beta)[0]
-        out[int(b)] = (v, f64_to_bf16(v))
+        if kv == "fp8":
+            c, s = quantize_e4m3_rows(v[None])
+            out[int(b)] = (v, (c[0], s[0]))
+        elif kv == "mxfp4":
+            c, s = quantize_mxfp4_rows(v[None])
+            out[int(b)] = (v, (c[0], s[0]))
+        else:
+            out[int(b)] = (v, f64_to_bf16(v))
     return out
 
 

@@ -27,7 +27,7 @@ STATUS_NAMES = {0: "SA_OK", 1: "SA_EINVAL", 2: "SA_EUNSUPPORTED", 3: "SA_EWORKSP
 
 EXPORTS = ("sparse_attn_plan", "sparse_attn_plan_destroy", "sparse_attn_last_error",
            "sparse_attn_workspace_init", "indexer_score", "select_topk", "indexer_score_cand",
-           "select_topk_cand", "sparse_attn_fwd", "sparse_attn_compress")
+           "select_topk_cand", "sparse_attn_fwd", "sparse_attn_compress", "sparse_attn_compress_codes")
 
 
 class sa_params(ctypes.Structure):
@@ -94,6 +94,8 @@ def _load():
     lib.sparse_attn_fwd.restype = ctypes.c_int
     lib.sparse_attn_compress.argtypes = [vp, vp, i64, vp, i64, vp, vp, i64, i64, vp]
     lib.sparse_attn_compress.restype = ctypes.c_int
+    lib.sparse_attn_compress_codes.argtypes = [vp, vp, i64, vp, i64, vp, vp, i64, vp, i64, i64, vp]
+    lib.sparse_attn_compress_codes.restype = ctypes.c_int
     return lib
 
 
@@ -354,3 +356,23 @@ def sparse_attn_compress(plan: Plan, raw: torch.Tensor, raw_group_stride: int, g
     _check(lib.sparse_attn_compress(plan.handle, _ptr(raw), raw_group_stride, _ptr(gate),
                                     gate_group_stride, _ptr(slot_bias), _ptr(out), out_group_stride,
                                     G, _stream(stream)))
+
+
+def sparse_attn_compress_codes(plan: Plan, raw: torch.Tensor, raw_group_stride: int,
+                               gate: Optional[torch.Tensor], gate_group_stride: int,
+                               slot_bias: Optional[torch.Tensor], out: torch.Tensor, out_group_stride: int,
+                               out_scales: torch.Tensor, scales_group_stride: int, G: int, stream=None):
+    """The compressor into e4m3 or MXFP4 code rows (the plan's kv_dtype). raw / gate strides in
+    bf16 elements; out (uint8) and out_scales (fp32 for e4m3, uint8 for MXFP4) strides in bytes."""
+    for t, name in ((raw, "raw"), (gate, "gate")):
+        if t is not None and (t.dtype != torch.bfloat16 or not t.is_cuda):
+            raise TypeError(f"{name}: expected a bfloat16 device tensor")
+    if out.dtype != torch.uint8 or not out.is_cuda:
+        raise TypeError("out: expected a uint8 device tensor (code bytes)")
+    if out_scales.dtype not in (torch.float32, torch.uint8) or not out_scales.is_cuda:
+        raise TypeError("out_scales: expected a float32 (e4m3) or uint8 (MXFP4) device tensor")
+    if slot_bias is not None:
+        _need(slot_bias, "slot_bias", torch.float32)
+    _check(lib.sparse_attn_compress_codes(plan.handle, _ptr(raw), raw_group_stride, _ptr(gate),
+                                          gate_group_stride, _ptr(slot_bias), _ptr(out), out_group_stride,
+                                          _ptr(out_scales), scales_group_stride, G, _stream(stream)))

@@ -561,7 +561,8 @@ sa_status sparse_attn_compress(const sa_plan* plan, const void* raw, int64_t raw
   if ((st = check_plan(plan)) != SA_OK) return st;
   const int r = plan->p.ratio;
   SA_REQUIRE(plan->p.kv_dtype == SA_KV_BF16, SA_EUNSUPPORTED,
-             "the compressor writes bf16 rows (plan kv_dtype is e4m3 or MXFP4)");
+             "sparse_attn_compress writes bf16 rows (plan kv_dtype is e4m3 or MXFP4: use "
+             "sparse_attn_compress_codes)");
   SA_REQUIRE(G >= 0, SA_EINVAL, "G = %lld < 0", (long long)G);
   SA_REQUIRE(raw && aligned16(raw) && out && aligned16(out), SA_EINVAL,
              "raw / out NULL or not 16-byte aligned");
@@ -586,7 +587,58 @@ sa_status sparse_attn_compress(const sa_plan* plan, const void* raw, int64_t raw
   a.out_stride = out_group_stride;
   a.G = G;
   a.ratio = r;
+  a.kv_mode = 0;
+  a.scales = nullptr;
+  a.scales_stride = 0;
   return hip_status(sa::launch_compress(a, (hipStream_t)stream), "sparse_attn_compress launch");
+}
+
+sa_status sparse_attn_compress_codes(const sa_plan* plan, const void* raw, int64_t raw_group_stride,
+                                     const void* gate, int64_t gate_group_stride,
+                                     const float* slot_bias, void* out, int64_t out_group_stride,
+                                     void* out_scales, int64_t scales_group_stride, int64_t G,
+                                     void* stream) {
+  sa_status st;
+  if ((st = check_plan(plan)) != SA_OK) return st;
+  const int r = plan->p.ratio;
+  const int kv = plan->p.kv_dtype;
+  SA_REQUIRE(kv == SA_KV_FP8_E4M3 || kv == SA_KV_MXFP4, SA_EUNSUPPORTED,
+             "sparse_attn_compress_codes needs a plan with e4m3 or MXFP4 latents (plan kv_dtype is bf16)");
+  SA_REQUIRE(G >= 0 && G <= ((int64_t)1 << 31) - 1, SA_EINVAL, "G = %lld out of range", (long long)G);
+  SA_REQUIRE(raw && aligned16(raw) && out && aligned16(out), SA_EINVAL,
+             "raw / out NULL or not 16-byte aligned");
+  SA_REQUIRE(raw_group_stride >= (int64_t)r * 512 && raw_group_stride % 8 == 0, SA_EINVAL,
+             "raw_group_stride = %lld invalid", (long long)raw_group_stride);
+  const int64_t row = kv == SA_KV_MXFP4 ? 256 : 512, srow = kv == SA_KV_MXFP4 ? 16 : 4;
+  SA_REQUIRE(out_group_stride >= row && out_group_stride % 16 == 0, SA_EINVAL,
+             "out_group_stride = %lld bytes must be >= %lld and a multiple of 16", (long long)out_group_stride,
+             (long long)row);
+  SA_REQUIRE(out_scales && reinterpret_cast<uintptr_t>(out_scales) % 4 == 0, SA_EINVAL,
+             "out_scales NULL or not 4-byte aligned");
+  SA_REQUIRE(scales_group_stride >= srow && scales_group_stride % 4 == 0, SA_EINVAL,
+             "scales_group_stride = %lld bytes must be >= %lld and a multiple of 4",
+             (long long)scales_group_stride, (long long)srow);
+  if (r == 2) {
+    SA_REQUIRE(gate && aligned16(gate) && slot_bias && aligned16(slot_bias), SA_EINVAL,
+               "gate / slot_bias NULL or not 16-byte aligned");
+    SA_REQUIRE(gate_group_stride >= 1024 && gate_group_stride % 8 == 0, SA_EINVAL,
+               "gate_group_stride = %lld invalid", (long long)gate_group_stride);
+  }
+  if (G == 0) return ok();
+  sa::CompressArgs a;
+  a.raw = raw;
+  a.raw_stride = raw_group_stride;
+  a.gate = gate;
+  a.gate_stride = gate_group_stride;
+  a.bias = slot_bias;
+  a.out = out;
+  a.out_stride = out_group_stride;
+  a.G = G;
+  a.ratio = r;
+  a.kv_mode = kv;
+  a.scales = out_scales;
+  a.scales_stride = scales_group_stride;
+  return hip_status(sa::launch_compress(a, (hipStream_t)stream), "sparse_attn_compress_codes launch");
 }
 
 }  // extern "C"

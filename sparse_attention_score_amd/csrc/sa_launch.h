@@ -121,6 +121,11 @@ struct CompressArgs {
   int64_t out_stride;
   int64_t G;
   int32_t ratio;
+  // code rows (kv_mode 1: e4m3 + fp32 row scale, 2: MXFP4 + 16 E8M0 bytes); out_stride and
+  // scales_stride in bytes then
+  int32_t kv_mode;
+  void* scales;
+  int64_t scales_stride;
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t stream);
 

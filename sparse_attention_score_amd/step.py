@@ -9,6 +9,7 @@ import numpy as np
 import torch
 
 from . import (Cache, Plan, Queries, indexer_score, select_topk, sparse_attn_compress,
+               sparse_attn_compress_codes,
                sparse_attn_fwd, workspace_for)
 
 
@@ -85,6 +86,12 @@ class DeviceBatch:
         assert np.all((wl.pos.astype(np.int64) + 1) // 2 == n), "uniform positions required"
         assert len(self.groups) == wl.B and np.array_equal(self.groups, np.arange(wl.B))
         out_view = self.C[:, n - 1]
+        if self.CS is not None:   # code rows: codes into C, scales into CS (strides in bytes)
+            sc_view = self.CS[:, n - 1]
+            sparse_attn_compress_codes(self.plan, self.Xp, 1024, self.Zp, 1024, self.beta, out_view,
+                                       self.C.stride(0), sc_view, self.CS.stride(0) * self.CS.element_size(),
+                                       wl.B, stream=stream)
+            return
         sparse_attn_compress(self.plan, self.Xp, 1024, self.Zp, 1024, self.beta, out_view,
                              self.C.stride(0), wl.B, stream=stream)
 

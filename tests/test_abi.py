@@ -247,3 +247,19 @@ def test_mxfp4_latent_rejects(case):
     assert b"latent" in S.lib.sparse_attn_last_error() or b"window" in S.lib.sparse_attn_last_error()
     assert S.lib.sparse_attn_compress(p.handle, 0x1000, 1024, 0x1000, 1024, 0x2000, 0x3000, 512, 4,
                                       None) == S.SA_EUNSUPPORTED
+
+
+def test_compress_codes_rejects():
+    lib = S.lib
+    args = lambda **k: dict(dict(raw=0x1000, rs=1024, gate=0x1000, gs=1024, bias=0x3000, out=0x4000,
+                                 os=512, sc=0x5000, ss=4, G=4), **k)
+    call = lambda p, a: lib.sparse_attn_compress_codes(p.handle, a["raw"], a["rs"], a["gate"], a["gs"], a["bias"],
+                                                       a["out"], a["os"], a["sc"], a["ss"], a["G"], None)
+    assert call(_plan(), args()) == S.SA_EUNSUPPORTED              # bf16 latents: not a code store
+    p8, p4 = _plan(kv_dtype="fp8"), _plan(kv_dtype="mxfp4")
+    for bad in (dict(raw=None), dict(out=0x4008), dict(os=500), dict(os=496), dict(sc=None), dict(sc=0x5002),
+                dict(ss=2), dict(ss=6), dict(G=-1), dict(gate=None), dict(gs=1000), dict(rs=1000)):
+        assert call(p8, args(**bad)) == S.SA_EINVAL, bad
+    assert call(p4, args(os=240)) == S.SA_EINVAL                   # MXFP4 rows are 256 bytes
+    assert call(p4, args(os=256, ss=12)) == S.SA_EINVAL            # and 16 scale bytes
+    assert call(p8, args(G=0)) == S.SA_OK and call(p4, args(os=256, ss=16, G=0)) == S.SA_OK

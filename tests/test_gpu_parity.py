@@ -421,6 +421,102 @@ def test_compress_standalone_one_ulp():
     assert torch.equal(out1.view(torch.int16).cpu(), Xd.reshape(-1, 512)[:3 * 777].view(torch.int16).cpu())
 
 
+def _grid_step(ref, table):
+    """Spacing of the code grid (ascending non-negative values `table`) at |ref|."""
+    i = np.clip(np.searchsorted(table, np.abs(ref), side="right"), 1, len(table) - 1)
+    return table[i] - table[i - 1]
+
+
+@pytest.mark.parametrize("kv", ["fp8", "mxfp4"])
+def test_compress_codes_against_oracle(kv):
+    # the compressor writing e4m3 (row scale) or MXFP4 (block scales) code rows: 2331 groups,
+    # one all-zero, one with a zero block, one with a huge dynamic range
+    from sparse_attention_score_amd import Plan, sparse_attn_compress_codes
+    from sparse_attention_score_amd.step import to_device_bf16
+    X, Z, beta = W.make_compress_input(B=3, n_raw=2 * 777, seed=52)
+    X = X.reshape(-1, 2, 512)
+    Z = Z.reshape(-1, 2, 512)
+    X[0] = 0
+    X[1, :, 64:96] = 0
+    X[2, :, :256] = O.f64_to_bf16(O.bf16_to_f64(X[2, :, :256]) * 2.0 ** -40)
+    G = X.shape[0]
+    fp4 = kv == "mxfp4"
+    plan = Plan(ratio=2, max_queries=1, max_compressed=1, kv_dtype=kv)
+    Xd, Zd = to_device_bf16(X), to_device_bf16(Z)
+    bd = torch.from_numpy(beta).cuda()
+    rb = 256 if fp4 else 512
+    out = torch.full((G, rb), 0xAB, dtype=torch.uint8, device="cuda")
+    sc = (torch.full((G, 16), 0xAB, dtype=torch.uint8, device="cuda") if fp4
+          else torch.full((G,), float("nan"), dtype=torch.float32, device="cuda"))
+    sparse_attn_compress_codes(plan, Xd, 1024, Zd, 1024, bd, out, rb, sc, 16 if fp4 else 4, G)
+    torch.cuda.synchronize()
+    codes, scales = out.cpu().numpy(), sc.cpu().numpy()
+    ref = O.compress(O.bf16_to_f64(X), O.bf16_to_f64(Z), beta)
+    xs = O.bf16_to_f64(X)
+    slack = 1e-5 * (np.abs(xs[:, 0]) + np.abs(xs[:, 1])) + 1e-30   # fp32 arithmetic vs fp64
+    if fp4:
+        rc, rs = O.quantize_mxfp4_rows(ref)
+        dec = O.mxfp4_to_f64(codes, scales)
+        step = _grid_step(ref / np.repeat(2.0 ** (rs.astype(np.int64) - 127), 32, axis=1), O.E2M1_TABLE[:8])
+        unit = np.repeat(2.0 ** (scales.astype(np.int64) - 127), 32, axis=1)
+        # block exponents agree unless the block's amax sits at a power of two
+        amax = np.abs(ref).reshape(G, 16, 32).max(axis=2)
+        frac = amax / 2.0 ** np.floor(np.log2(np.maximum(amax, 1e-300)))
+        edge = (frac - 1 < 1e-5) | (2 - frac < 2e-5)
+        assert np.all((scales == rs) | edge), "block exponents"
+        assert scales[0].tolist() == [0] * 16 and scales[1, 2] == 0 and not np.any(codes[0])
+        keep = np.repeat(~edge | (amax == 0), 32, axis=1)
+        # values past 6 x 2^X saturate to 6 x 2^X (the MX scale rule leaves |x| 2^-X < 8)
+        y = np.abs(ref) / np.repeat(2.0 ** (rs.astype(np.int64) - 127), 32, axis=1)
+        sat = np.maximum(y - 6, 0)
+    else:
+        rc, rs = O.quantize_e4m3_rows(ref)
+        dec = O.kv_rows_f64(codes, scales)
+        assert np.all(np.abs(scales - rs) <= 1e-6 * rs), "row scales"
+        assert scales[0] == 1.0 and not np.any(codes[0])
+        step = _grid_step(ref / rs[:, None].astype(np.float64), O.E4M3_TABLE[:0x7F])
+        unit = scales[:, None].astype(np.float64)
+        keep = np.ones_like(ref, dtype=bool)
+        sat = np.zeros_like(ref)
+    # every element within half a grid step (plus the fp32 slack) of the exact value; codes
+    # equal the oracle's but for the few values on a rounding boundary
+    err = np.abs(dec - ref)
+    bound = np.maximum(0.5 * step, sat) * unit * (1 + 1e-5) + slack
+    assert np.all((err <= bound)[keep]), f"max {np.max((err / bound)[keep]):.3f}"
+    same = np.mean(codes == rc)
+    print(f"[compress-codes {kv}] code bytes equal to the oracle's: {same:.6f}", flush=True)
+    assert same > 0.999
+    # ratio 1 quantises the raw rows themselves (exact bf16 values): bit for bit the oracle's
+    plan1 = Plan(ratio=1, max_queries=1, max_compressed=1, kv_dtype=kv)
+    out1 = torch.empty((2 * G, rb), dtype=torch.uint8, device="cuda")
+    sc1 = (torch.empty((2 * G, 16), dtype=torch.uint8, device="cuda") if fp4
+           else torch.empty((2 * G,), dtype=torch.float32, device="cuda"))
+    sparse_attn_compress_codes(plan1, Xd, 512, None, 0, None, out1, rb, sc1, 16 if fp4 else 4, 2 * G)
+    torch.cuda.synchronize()
+    raw = O.bf16_to_f64(X).reshape(2 * G, 512)
+    rc1, rs1 = O.quantize_mxfp4_rows(raw) if fp4 else O.quantize_e4m3_rows(raw)
+    assert np.array_equal(out1.cpu().numpy(), rc1) and np.array_equal(sc1.cpu().numpy(), rs1)
+
+
+@pytest.mark.parametrize("kv", ["fp8", "mxfp4"])
+def test_decode_step_with_code_row_compressor(kv):
+    # the whole step on code-row stores: the compressor writes each sequence's new latent as
+    # codes and scales, then indexer, selection and attention run (40 queries at raw position
+    # 9001, each completing a group)
+    wl = W.make_decode(B=40, n_raw=9002, ratio=2, key_dtype="fp8", kv_dtype=kv, compress_codes=True,
+                       name=f"compress-{kv}", seed=53)
+    d, res = _e2e(wl)
+    n = 4501
+    for b in range(40):
+        v, (rc, rs) = res.C_new[b]
+        got_c = d.C[b, n - 1].cpu().numpy()
+        got_s = d.CS[b, n - 1].cpu().numpy()
+        dec = O.kv_rows_f64(got_c[None], got_s[None])[0]
+        ref = O.kv_rows_f64(rc[None], rs[None])[0]
+        assert np.mean(got_c == rc) > 0.99, b
+        assert np.abs(dec - v).max() <= np.abs(ref - v).max() * 1.5 + 1e-6 * np.abs(v).max(), b
+
+
 def test_deterministic_bitwise():
     wl = W.make_decode(B=3, n_raw=2 * 20003, ratio=2, key_dtype="fp8", name="determinism", seed=61)
     d = _run(wl)

@@ -602,3 +602,59 @@ def test_compressor_row_feeds_attention():
     X = np.concatenate([C, O.bf16_to_f64(wl.R[0, np.arange(0, 64) % 128])])
     o, lse = O.attend(q, X)
     assert np.allclose(res.o[0], o, atol=0) and np.allclose(res.lse[0], lse, atol=0)
+
+
+# ------------------------------------------------- quantising the compressor's output rows
+
+def test_e4m3_row_quantiser_matches_torch_cast():
+    # rows whose amax is 448 have scale 1, so the codes are the plain fp32 -> e4m3 cast, which
+    # torch implements independently (nearest, ties to even); include every code's value and
+    # every midpoint between neighbouring codes (ties), negative values and subnormals
+    finite = O.E4M3_TABLE[:0x7F]
+    mids = (finite[:-1] + finite[1:]) / 2
+    rng = np.random.default_rng(5)
+    vals = np.concatenate([finite, mids, rng.uniform(0, 448, 4000), 2.0 ** rng.uniform(-12, 8, 4000)])
+    vals = np.concatenate([vals, -vals])
+    vals = vals[: len(vals) // 511 * 511].reshape(-1, 511)
+    x = np.concatenate([vals, np.full((vals.shape[0], 1), 448.0)], axis=1).astype(np.float32)
+    assert np.array_equal(x.astype(np.float64), np.asarray(x, np.float64))   # exact in fp32
+    codes, s = O.quantize_e4m3_rows(x)
+    assert np.all(s == 1.0)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+
+
+def test_code_row_quantisers_match_the_input_quantisers():
+    # the inputs module quantises with its own C code (same rules): rows of N(0,1) values at
+    # several magnitudes, plus zero rows and blocks
+    import workloads as W
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal((64, 512)) * 10.0 ** rng.uniform(-20, 20, (64, 1))).astype(np.float32)
+    x[3] = 0.0
+    x[5, 64:96] = 0.0
+    c8, s8 = O.quantize_e4m3_rows(x)
+    w8, ws8 = W.quant_e4m3_rows(x)
+    assert np.array_equal(c8, w8) and np.array_equal(s8, ws8)
+    c4, s4 = O.quantize_mxfp4_rows(x)
+    w4, ws4 = W.quant_mxfp4_rows(x)
+    assert np.array_equal(c4, w4) and np.array_equal(s4, ws4)
+    assert s4[3].tolist() == [0] * 16 and s4[5, 2] == 0
+
+
+def test_mxfp4_row_quantiser_round_trip_and_ties():
+    # every E2M1 value times a block scale encodes to itself; midpoints take the even code
+    mags = O.E2M1_TABLE[:8]
+    for X in (-3, 0, 5):
+        blk = np.zeros(32)
+        blk[:8] = mags * 2.0 ** X
+        blk[8:16] = -mags * 2.0 ** X
+        blk[31] = 6 * 2.0 ** X          # amax 6 * 2^X: floor(log2) - 2 = X
+        c, s = O.quantize_mxfp4_rows(np.tile(blk, 16)[None])
+        assert np.all(s == X + 127)
+        assert np.array_equal(O.mxfp4_to_f64(c, s)[0, :32], blk)
+        mid = np.zeros(32)
+        mid[:7] = (mags[:-1] + mags[1:]) / 2 * 2.0 ** X
+        mid[31] = 6 * 2.0 ** X
+        c, s = O.quantize_mxfp4_rows(np.tile(mid, 16)[None])
+        got = O.mxfp4_to_f64(c, s)[0, :7] / 2.0 ** X
+        assert got.tolist() == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]   # ties to codes 0, 2, 2, 4, 4, 6, 6

@@ -217,12 +217,14 @@ def _keys(seed, key_dtype, B, nc_cap):
 
 def make_decode(B: int, n_raw, ratio: int = 2, key_dtype: str = "bf16", seed: int = 0,
                 wcap: int = WINDOW, name: str = "decode", nc_cap: Optional[int] = None,
-                with_compress: bool = True, kv_dtype: str = "bf16") -> Workload:
+                with_compress: bool = True, kv_dtype: str = "bf16",
+                compress_codes: bool = False) -> Workload:
     """B sequences, one decode query each at raw position n_raw-1 (per-sequence if an array).
     kv_dtype "fp8": latents and window rows are N(0,1) rows quantised to e4m3 with one fp32
     scale per row (no compressor inputs then: the compressor writes bf16 rows). kv_dtype
     "mxfp4": N(0,1) latent rows quantised to MXFP4 (E8M0 scale per 32 elements) and e4m3
-    window rows as for "fp8"."""
+    window rows as for "fp8". compress_codes: compressor inputs for code-row stores too (the
+    compressor then writes its group's row as codes and scales)."""
     n_raw = np.broadcast_to(np.asarray(n_raw, dtype=np.int64), (B,)).copy()
     pos = (n_raw - 1).astype(np.int32)
     vis = (pos.astype(np.int64) + 1) // ratio
@@ -256,7 +258,7 @@ def make_decode(B: int, n_raw, ratio: int = 2, key_dtype: str = "bf16", seed: in
             else:
                 C[b], CS[b] = normal_e4m3_rows(seed, "C", b, nc_cap, DIM)
             R[b], RS[b] = normal_e4m3_rows(seed, "R", b, wcap, DIM)
-        with_compress = False
+        with_compress = compress_codes
     Xp = Zp = beta = None
     if ratio == 2 and with_compress:
         Xp = np.empty((B, 2, DIM), np.uint16)
@@ -390,10 +392,10 @@ MORE_WORKLOADS = {
     "decode-b128-ctx128k-mxfp4": dict(kind="decode", B=128, n_raw=131072, ratio=2, key_dtype="mxfp4"),
     # the headline decode batch with e4m3 latent and window rows (fp32 row scales)
     "decode-b128-ctx128k-fp8kv": dict(kind="decode", B=128, n_raw=131072, ratio=2, key_dtype="fp8",
-                                      kv_dtype="fp8"),
+                                      kv_dtype="fp8", compress_codes=True),
     # ... and with MXFP4 latent rows (the 4-bit compressed state) and e4m3 window rows
     "decode-b128-ctx128k-fp4kv": dict(kind="decode", B=128, n_raw=131072, ratio=2, key_dtype="fp8",
-                                      kv_dtype="mxfp4"),
+                                      kv_dtype="mxfp4", compress_codes=True),
     # a ragged serving batch at 128K context: two 1024-query prefill chunks, 64 single decode
     # queries and 16 decode steps with 5 drafted tokens (2208 queries, 82 sequences)
     "ragged-2x1024+64+16x6-ctx128k-fp8": dict(kind="ragged", n_raw=[131072] * 82,
