@@ -70,8 +70,10 @@ struct AttnShared {
   u32x4 P[2][kHG][64];                 // P^T operand of each head group per lane, two steps
   float tmax[2][kHeads];               // step-0 maxima per key half / partial normalisers
   float norm[kHeads];                  // final normaliser of each head
-  float rscale[kMaxKeys];              // e4m3 rows: the fp32 scale of every key slot
-  const float* sptr[kMaxKeys];         // e4m3 rows: where each slot's scale lives
+  float rscale[kMaxKeys];              // code rows: the fp32 row scale of every key slot
+                                       // (1 for MXFP4 rows and slots past the list)
+  const float* sptr[kMaxKeys];         // code rows: where each slot's fp32 scale (e4m3) or
+                                       // 16 E8M0 block scales (MXFP4) live
   int wave_cnt[kAW];
   int redo[kAW];                       // per wave: a score exceeded its reference by > kSafe
   int last;                            // this work-group combines the query's key splits
@@ -295,10 +297,11 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       }
     }
   };
-  // e4m3 rows: each wave widens the rows it loaded, in place (codes in the first 512 bytes
-  // of a slot become 1 KiB of bf16), after its own wait and before the barrier that hands
-  // the step to the other waves. All of a lane's reads come before its writes, and a
-  // wave's LDS operations run in order, so no code is overwritten before it is read.
+  // Code rows: each wave widens the rows it loaded, in place (the codes at the start of a
+  // slot, 512 bytes of e4m3 or 256 + 16 bytes of MXFP4, become 1 KiB of bf16), after its
+  // own wait and before the barrier that hands the step to the other waves. All of a
+  // wave's reads of a row come before its writes to it, and a wave's LDS operations run in
+  // order, so no code is overwritten before it is read.
   // e4m3 rows: chunk q (16 codes) of row rr, 2 chunks per lane (4 rows x 32 chunks);
   // MXFP4 rows: code dword e of block q of row rr, lane 4q + e, with block q's scale byte
   // (after the 256 code bytes): 8 elements per lane and row, contiguous 16-byte writes.
