@@ -2,8 +2,9 @@
 
 Argument marshalling only. Every stage runs in the library's HIP kernels; torch is used
 for device memory and the current stream. The entry points have the names of the C ABI
-(include/sparse_attn.h): sparse_attn_plan, indexer_score, select_topk, sparse_attn_fwd,
-sparse_attn_compress. If the built library is missing, importing this package raises.
+(include/sparse_attn.h): sparse_attn_plan, indexer_score, indexer_score_cand, select_topk,
+select_topk_cand, sparse_attn_fwd, sparse_attn_compress, sparse_attn_compress_codes. If the
+built library is missing, importing this package raises.
 """
 from __future__ import annotations
 
