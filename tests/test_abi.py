@@ -263,3 +263,22 @@ def test_compress_codes_rejects():
     assert call(p4, args(os=240)) == S.SA_EINVAL                   # MXFP4 rows are 256 bytes
     assert call(p4, args(os=256, ss=12)) == S.SA_EINVAL            # and 16 scale bytes
     assert call(p8, args(G=0)) == S.SA_OK and call(p4, args(os=256, ss=16, G=0)) == S.SA_OK
+
+
+def test_plain_c_caller(tmp_path):
+    # the library from C alone: tests/c/abi_host_check.c built with gcc against the header and
+    # the built .so, run on the host (plan creation and argument errors need no GPU)
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    libdir = os.path.join(root, "sparse_attention_score_amd")
+    exe = str(tmp_path / "abi_host_check")
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Werror", os.path.join(root, "tests", "c", "abi_host_check.c"),
+                    "-I", os.path.join(root, "include"), "-L", libdir, "-lsparse_attn",
+                    f"-Wl,-rpath,{libdir}", "-lm", "-o", exe], check=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "abi host checks ok" in r.stdout
