@@ -38,7 +38,11 @@ Readings where the pages are silent (each is also a stated definition):
     1/sqrt(512); output o and natural-log lse per head;
   - compressor: per channel, softmax over the r slots of (gate logit + slot
     bias), then the weighted sum of the slot latents; ratio 1 is the identity;
-    the result is stored as bf16 (round to nearest even).
+    the result is stored as bf16 (round to nearest even), or, for e4m3 and MXFP4
+    latent stores, taken in fp32 and quantised (quantize_e4m3_rows,
+    quantize_mxfp4_rows: nearest code, ties to the even code);
+  - latent and window stores: bf16, e4m3 code x fp32 row scale, or MXFP4
+    (latents only; the window is then e4m3), decoded exactly.
 """
 from __future__ import annotations
 
