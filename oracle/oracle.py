@@ -13,15 +13,16 @@ Sources (the pages):
        into 1 (ratio 2) or 1-to-1 (ratio 1); a 128-position sliding window;
        each retrieving layer picks a top-512 set.
   [P3] "deepseek-ai/DeepSeek-V4.1-Flash" (vLLM recipe, MI355X), Overview, the
-       "Two-tier sparse attention" bullet: every layer attends a 128-token
-       window; compressing layers add latents pooled by a learned softmax gate;
-       an indexer scores those latents and keeps the best 512 per query after
-       a candidate stage that selects 2048 blocks of 8.
+       "Two-tier sparse attention" bullet: a 128-token sliding window in every
+       layer; layers with a compression ratio add compressed latents that a
+       learned softmax gate pools; an indexer ranks them and each query keeps
+       its 512 best, drawn from 2048 candidate blocks of 8 positions.
   [OCP] OCP 8-bit Floating Point Specification (OFP8), E4M3 encoding.
   [MX]  OCP Microscaling Formats (MX) Specification v1.0: MXFP4 = blocks of 32
         FP4 E2M1 elements sharing one E8M0 scale. The pages name the 4-bit
-        indexer cache ("deepseek-ai/DeepSeek-V4.1-Flash" recipe, model table:
-        FP4 indexer cache; both MI355X configurations: indexer_kv_dtype mxfp4).
+        indexer cache ("SGLang and Miles Add Day-0 Support for DeepSeek-V4.1",
+        SGLang Features table, Quantization row: FP4 indexer cache; the recipe's
+        Blackwell TP and DEP section sets indexer_kv_dtype mxfp4).
 
 Readings where the pages are silent (each is also a stated definition):
   - indexer: 16 heads x 128 dims on the query side, one 128-d key per
@@ -402,21 +403,14 @@ def step_compress(wl) -> dict:
     return out
 
 
-def run_query(wl, t: int, keys_f64: Optional[np.ndarray] = None, C_new: Optional[dict] = None,
-              idx_override: Optional[np.ndarray] = None):
-    """The whole path for query t of workload `wl` (see workloads.Workload).
-
-    Returns (scores [n], cand, idx, o [64,512], lse [64]). `idx_override` feeds a
-    given selection into the attention stage instead of the oracle's own.
-    """
+def attend_query(wl, t: int, idx: np.ndarray, C_new: Optional[dict] = None):
+    """S4 alone for query t of workload `wl`: one softmax over the compressed rows `idx`
+    (the row this step's compressor wrote, if any, standing in for row n-1) followed by the
+    window rows of the query's position ([P2], [P3]). Returns (o [64,512], lse [64])."""
     b = int(wl.seq[t])
     p = int(wl.pos[t])
     n = visible_count(p, wl.ratio)
-    if keys_f64 is None:
-        keys_f64 = index_keys_f64(wl.KI[b, :n], None if wl.KS is None else wl.KS[b, :n])
-    I = index_scores(bf16_to_f64(wl.qI[t]), wl.w[t], keys_f64[:n])
-    cand, idx = select(I)
-    use = idx if idx_override is None else np.asarray(idx_override, np.int64)
+    use = np.asarray(idx, np.int64)
     new_bits = None
     if C_new is not None and b in C_new and n > 0:
         new_bits = C_new[b][1]
@@ -425,7 +419,29 @@ def run_query(wl, t: int, keys_f64: Optional[np.ndarray] = None, C_new: Optional
     RS = getattr(wl, "RS", None)
     Xw = kv_rows_f64(wl.R[b, win % wl.wcap], None if RS is None else RS[b, win % wl.wcap])
     X = np.concatenate([rows, Xw], axis=0)
-    o, lse = attend(bf16_to_f64(wl.q[t]), X)
+    return attend(bf16_to_f64(wl.q[t]), X)
+
+
+def index_query(wl, t: int, keys_f64: Optional[np.ndarray] = None) -> np.ndarray:
+    """S1 for query t of workload `wl`: the scores of its n visible compressed positions."""
+    b = int(wl.seq[t])
+    n = visible_count(int(wl.pos[t]), wl.ratio)
+    if keys_f64 is None:
+        keys_f64 = index_keys_f64(wl.KI[b, :n], None if wl.KS is None else wl.KS[b, :n])
+    return index_scores(bf16_to_f64(wl.qI[t]), wl.w[t], keys_f64[:n])
+
+
+def run_query(wl, t: int, keys_f64: Optional[np.ndarray] = None, C_new: Optional[dict] = None,
+              idx_override: Optional[np.ndarray] = None):
+    """The whole path for query t of workload `wl` (see workloads.Workload).
+
+    Returns (scores [n], cand, idx, o [64,512], lse [64]). `idx_override` feeds a
+    given selection into the attention stage instead of the oracle's own.
+    """
+    I = index_query(wl, t, keys_f64)
+    cand, idx = select(I)
+    use = idx if idx_override is None else np.asarray(idx_override, np.int64)
+    o, lse = attend_query(wl, t, use, C_new)
     return I, cand, idx, o, lse
 
 

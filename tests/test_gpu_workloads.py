@@ -1,11 +1,17 @@
 """The measured workloads at full size, in the launch configuration bench.py times: the five
-layer configurations and the further batches bench.py reports (MXFP4 keys, e4m3 and MXFP4
-latent rows, the ragged serving batch; the multi-token batch has its own test).
+layer configurations and the further batches bench.py reports (multi-token decode, MXFP4
+keys, e4m3 and MXFP4 latent rows, the ragged serving batch).
 
-All queries are checked for properties that hold at any size (selection well-formed,
-block maxima consistent with the scores); a sample of queries per workload is checked
-against the fp64 oracle one query at a time (index sets within the tie band, outputs
-within tolerance on the GPU's selection)."""
+Every query of every workload is checked against the fp64 oracle, one query at a time:
+  - indexer scores within 2e-6 of max(|I(j)|, |I_k|) for every visible j, -inf past n;
+  - block maxima bit-equal to the max of the GPU's own scores;
+  - candidate blocks and top-512 positions exact up to the 1e-5 tie band of the k-th score;
+  - outputs against the oracle's attention on the GPU's own selection (end to end), and,
+    for every query whose selection differs from the oracle's inside the tie band, the
+    attention kernel fed the oracle's selection against the oracle's output (stage-isolated);
+  - max |diff| <= 2e-2 and mean |diff| <= 2e-3 per query and over all T x 64 x 512 output
+    elements of the workload (the aggregate is printed), lse within 1e-4.
+One GPU pass per workload serves all its query ranges (cases of up to 1024 queries)."""
 import gc
 import time
 
@@ -15,41 +21,50 @@ import torch
 
 import workloads as W
 from oracle import oracle as O
-from parity_util import (LSE_TOL, SCORE_REL, bf16_dev_to_f64, check_index_row, check_outputs,
-                         kth_score)
+from parity_util import (LSE_TOL, OUT_MAX, OUT_MEAN, SCORE_REL, bf16_dev_to_f64, check_index_row,
+                         check_outputs, kth_score)
 
 pytestmark = pytest.mark.gpu
 
-SAMPLES = {
-    "decode-b4-ctx2k": [0, 1, 2, 3],
-    "decode-b64-ctx32k": [0, 17, 42, 63],
-    "decode-b128-ctx128k-fp8": [0, 77, 127],
-    "prefill-4096-at-61440": [0, 1, 127, 2048, 4094, 4095],
-    "decode-b8-ctx1m-fp8": [0, 7],
-}
+CHUNK = 1024
+NAMES = list(W.WORKLOADS) + list(W.MORE_WORKLOADS)
 
 
-# sampled queries of the further batches (ragged: first and last query of each prefill chunk,
-# single decode queries, the first and last query of a draft step)
-MORE_SAMPLES = {
-    "decode-b128-ctx128k-mxfp4": [0, 127],
-    "decode-b128-ctx128k-fp8kv": [0, 127],
-    "decode-b128-ctx128k-fp4kv": [0, 64, 127],
-    "ragged-2x1024+64+16x6-ctx128k-fp8": [0, 1023, 1024, 2047, 2048, 2111, 2112, 2117, 2207],
-}
+def _num_queries(name):
+    cfg = W.WORKLOADS.get(name) or W.MORE_WORKLOADS[name]
+    kind = cfg["kind"]
+    if kind == "decode":
+        return cfg["B"]
+    if kind == "decode_mq":
+        return cfg["B"] * cfg["G"]
+    if kind == "ragged":
+        return int(sum(cfg["lengths"]))
+    return cfg["T"]
 
 
-@pytest.mark.parametrize("name", list(W.WORKLOADS))
-def test_workload_full_size(name):
-    _full_size(name, SAMPLES[name])
+CASES = [(name, lo, min(lo + CHUNK, _num_queries(name)))
+         for name in NAMES for lo in range(0, _num_queries(name), CHUNK)]
+
+# GPU results of the workload under test (one at a time; the next workload frees them)
+_S = {"name": None}
 
 
-@pytest.mark.parametrize("name", list(MORE_SAMPLES))
-def test_more_workloads_full_size(name):
-    _full_size(name, MORE_SAMPLES[name])
+@pytest.fixture(scope="module", autouse=True)
+def _release():
+    yield
+    _S.clear()
+    _S["name"] = None
+    gc.collect()
+    torch.cuda.empty_cache()
 
 
-def _full_size(name, samples):
+def _state(name):
+    if _S["name"] == name:
+        return _S
+    _S.clear()
+    _S["name"] = None
+    gc.collect()
+    torch.cuda.empty_cache()
     assert torch.cuda.is_available()
     from sparse_attention_score_amd.step import DeviceBatch
     t0 = time.time()
@@ -60,46 +75,75 @@ def _full_size(name, samples):
     d.run()
     torch.cuda.synchronize()
     print(f"[workload] {name}: GPU pass done at {time.time() - t0:.1f}s", flush=True)
-    n = wl.visible()
-    topk = d.topk.cpu().numpy()
-    cand = d.cand.cpu().numpy()
-    # well-formed selection for every query
-    for t in range(wl.T):
-        k = min(512, int(n[t]))
-        row = topk[t]
-        assert np.all(row[:k] >= 0) and np.all(row[k:] == -1), t
-        assert np.all(np.diff(row[:k]) > 0) and row[:k].max(initial=-1) < n[t], t
-        nb = -(-int(n[t]) // 8)
-        kc = min(2048, nb)
-        assert np.all(cand[t, :kc] >= 0) and np.all(cand[t, kc:] == -1), t
-        assert np.all(np.diff(cand[t, :kc]) > 0), t
-        # every selected position lies in a kept block
-        assert np.all(np.isin(row[:k] // 8, cand[t, :kc])), t
-    keys_cache = {}
-    C_new = O.step_compress(wl)
-    for t in samples:
+    _S.update(name=name, wl=wl, d=d, t0=t0, n=wl.visible(),
+              scores=d.scores.cpu().numpy(), block_max=d.block_max.cpu().numpy(),
+              topk=d.topk.cpu().numpy(), cand=d.cand.cpu().numpy(),
+              out=bf16_dev_to_f64(d.out), lse=d.lse.cpu().numpy(),
+              C_new=O.step_compress(wl), keys={}, agg_max=0.0, agg_sum=0.0, agg_count=0,
+              agg_lse=0.0, set_diffs=0, isolated=0)
+    return _S
+
+
+@pytest.mark.parametrize("name,lo,hi", CASES, ids=[f"{c[0]}[{c[1]}:{c[2]}]" for c in CASES])
+def test_workload_every_query(name, lo, hi):
+    s = _state(name)
+    wl, n = s["wl"], s["n"]
+    E = s["d"].E
+    isolated = []
+    for t in range(lo, hi):
         b = int(wl.seq[t])
-        if b not in keys_cache:
+        if b not in s["keys"]:
             nn = int(n[wl.seq == b].max())
-            keys_cache = {b: O.index_keys_f64(wl.KI[b, :nn], None if wl.KS is None else wl.KS[b, :nn])}
-        I, c_ref, i_ref, _, _ = O.run_query(wl, t, keys_cache[b], C_new)
-        got = d.scores[t, :n[t]].cpu().numpy().astype(np.float64)
+            s["keys"] = {b: O.index_keys_f64(wl.KI[b, :nn], None if wl.KS is None else wl.KS[b, :nn])}
+        nt = int(n[t])
+        I = O.index_query(wl, t, s["keys"][b])
+        c_ref, i_ref = O.select(I)
+        # S1: scores and block maxima
+        got = s["scores"][t, :nt].astype(np.float64)
         Ik = kth_score(I, 512)
-        assert np.all(np.abs(got - I) <= SCORE_REL * np.maximum(np.abs(I), abs(Ik))), t
-        bm = d.block_max[t].cpu().numpy()
-        nb = -(-int(n[t]) // 8)
-        g32 = d.scores[t, :nb * 8].cpu().numpy()
-        g32 = np.where(np.arange(nb * 8) < n[t], g32, -np.inf).reshape(nb, 8).max(1)
-        assert np.array_equal(bm[:nb], g32), t
-        check_index_row(topk[t], i_ref, I, 512, f"{name} t={t} topk")
-        check_index_row(cand[t], c_ref, O.block_scores(I), 2048, f"{name} t={t} cand")
-        sel = topk[t][topk[t] >= 0]
-        _, _, _, o_ref, lse_ref = O.run_query(wl, t, keys_cache[b], C_new, idx_override=sel)
-        o = bf16_dev_to_f64(d.out[t])
-        mx, mn = check_outputs(o, o_ref, f"{name} t={t}")
-        assert np.abs(d.lse[t].cpu().numpy() - lse_ref).max() <= LSE_TOL, t
-        print(f"[workload] {name} t={t}: ok (max {mx:.2e} mean {mn:.2e}) at {time.time() - t0:.1f}s",
+        assert np.all(np.abs(got - I) <= SCORE_REL * np.maximum(np.abs(I), abs(Ik))), (name, t)
+        assert np.all(s["scores"][t, nt:E] == -np.inf), (name, t, "scores past n")
+        nb = -(-nt // 8)
+        g32 = np.where(np.arange(nb * 8) < nt, s["scores"][t, :nb * 8], -np.inf).reshape(nb, 8).max(1)
+        assert np.array_equal(s["block_max"][t, :nb], g32), (name, t, "block maxima")
+        # S2, S3
+        s["set_diffs"] += check_index_row(s["topk"][t], i_ref, I, 512, f"{name} t={t} topk") > 0
+        check_index_row(s["cand"][t], c_ref, O.block_scores(I), 2048, f"{name} t={t} cand")
+        kc = min(2048, nb)
+        assert np.all(np.isin(s["topk"][t][:min(512, nt)] // 8, s["cand"][t, :kc])), (name, t, "outside kept blocks")
+        # S4 end to end: the oracle's attention on the GPU's selection
+        sel = s["topk"][t][s["topk"][t] >= 0]
+        o_ref, lse_ref = O.attend_query(wl, t, sel, s["C_new"])
+        check_outputs(s["out"][t], o_ref, f"{name} t={t}")
+        dd = np.abs(s["out"][t] - o_ref)
+        s["agg_max"] = max(s["agg_max"], float(dd.max()))
+        s["agg_sum"] += float(dd.sum())
+        s["agg_count"] += dd.size
+        dl = float(np.abs(s["lse"][t] - lse_ref).max())
+        assert dl <= LSE_TOL, (name, t, dl)
+        s["agg_lse"] = max(s["agg_lse"], dl)
+        if not np.array_equal(sel, i_ref):
+            isolated.append((t, i_ref))
+    # S4 stage-isolated where the selections differ: the kernel on the oracle's selection
+    if isolated:
+        d = s["d"]
+        alt = d.topk.clone()
+        for t, i_ref in isolated:
+            row = np.full(512, -1, np.int32)
+            row[:i_ref.size] = i_ref
+            alt[t] = torch.from_numpy(row).to(alt.device)
+        d.attend(topk=alt)
+        torch.cuda.synchronize()
+        out_alt = bf16_dev_to_f64(d.out)
+        for t, i_ref in isolated:
+            o_ref, _ = O.attend_query(wl, t, i_ref, s["C_new"])
+            check_outputs(out_alt[t], o_ref, f"{name} t={t} stage-isolated")
+        s["isolated"] += len(isolated)
+    mean = s["agg_sum"] / max(1, s["agg_count"])
+    print(f"[workload] {name} queries {lo}..{hi - 1}: ok at {time.time() - s['t0']:.1f}s", flush=True)
+    if hi == _num_queries(name):
+        print(f"[parity] {name}: all {hi} queries; outputs max |d| {s['agg_max']:.3e} mean |d| {mean:.3e} "
+              f"over {s['agg_count']} elements; lse max |d| {s['agg_lse']:.2e}; {s['set_diffs']} queries "
+              f"with a top-512 set differing inside the tie band ({s['isolated']} checked stage-isolated)",
               flush=True)
-    del d, wl, keys_cache
-    gc.collect()
-    torch.cuda.empty_cache()
+    assert s["agg_max"] <= OUT_MAX and mean <= OUT_MEAN
