@@ -63,8 +63,11 @@ typedef enum sa_status {
 typedef enum sa_key_dtype {
   SA_KEY_BF16 = 0,      /* index keys bf16 [.][128] */
   SA_KEY_FP8_E4M3 = 1,  /* index keys e4m3 [.][128] plus one fp32 scale per key */
-  SA_KEY_MXFP4 = 2      /* index keys OCP MXFP4 (the pages' FP4 indexer cache, "mxfp4"
-                           indexer_kv_dtype of the recipe's MI355X configurations):
+  SA_KEY_MXFP4 = 2      /* index keys OCP MXFP4: the FP4 indexer cache ("SGLang and Miles Add
+                           Day-0 Support for DeepSeek-V4.1", SGLang Features table,
+                           Quantization row), set as indexer_kv_dtype mxfp4 in the
+                           "deepseek-ai/DeepSeek-V4.1-Flash" recipe's Blackwell TP and DEP
+                           section:
                            [.][64] bytes of FP4 E2M1, element 2i in the low nibble of
                            byte i, plus [.][4] E8M0 scales, scale b for elements
                            32b .. 32b+31. Key = 2^(scale-127) * element. indexer_score
@@ -75,8 +78,15 @@ typedef enum sa_key_dtype {
 
 /* Fixed at plan time. The kernels support exactly num_heads 64, latent_dim 512,
  * window 128, topk 512, idx_heads 16, idx_dim 128, block 8, cand_blocks 2048,
- * ratio 1 or 2; anything else returns SA_EUNSUPPORTED. */
-/* Latent and window store element type (the pages' FP8 window cache and 8-bit latents). */
+ * ratio 1 or 2, and max_compressed up to 1,048,576 (the pages' 1M-token context on a
+ * 1-to-1 layer: "deepseek-ai/DeepSeek-V4.1-Flash" recipe, Context length; "DeepSeek-V4.1
+ * Flash" Miles docs, section 1: 1-to-1 from layer 20 on); anything else returns
+ * SA_EUNSUPPORTED. */
+/* Latent and window store element type. The pages name an FP8 window cache and FP4
+ * compressed state ("SGLang and Miles Add Day-0 Support for DeepSeek-V4.1", Miles Day-0
+ * Support table, Quantization row), latents trained for FP4 storage ("deepseek-ai/
+ * DeepSeek-V4.1-Flash" recipe, Memory) and --kv-cache-dtype fp8 (same recipe, Blackwell TP
+ * and DEP). bf16 is the precision the layer configurations fix. */
 typedef enum sa_kv_dtype {
   SA_KV_BF16 = 0,       /* rows of 512 bf16 */
   SA_KV_FP8_E4M3 = 1,   /* rows of 512 OCP E4M3 codes plus one fp32 scale per row:
@@ -84,8 +94,8 @@ typedef enum sa_kv_dtype {
                            the MFMA operands are built) and written by
                            sparse_attn_compress_codes; sparse_attn_compress writes bf16
                            rows and returns SA_EUNSUPPORTED for these plans */
-  SA_KV_MXFP4 = 2       /* the pages' FP4 compressed state with an FP8 window (DeepSeek-V4
-                           report, the KV cache section): latent rows of OCP MXFP4, 256 bytes
+  SA_KV_MXFP4 = 2       /* FP4 compressed state beside an FP8 window (the Miles Day-0 Support
+                           table cited above): latent rows of OCP MXFP4, 256 bytes
                            of E2M1 (element 2i in the low nibble of byte i) plus 16 E8M0
                            block scales (scale b for elements 32b .. 32b+31, X = 2^(scale-127)
                            * element); window rows e4m3 as for SA_KV_FP8_E4M3. Same calls
@@ -124,7 +134,8 @@ typedef struct sa_queries {
                               verified token and the drafted tokens after it); indexer_score
                               then streams each group's keys once for all its queries. A
                               query whose seq_id differs from its group's first query gets
-                              -inf scores. Ignored by the other calls. */
+                              -inf scores. sparse_attn_fwd uses it only to check
+                              window_cap (see sa_cache); the other calls ignore it. */
   const int32_t* runs;     /* host, optional (NULL: none): a ragged batch as num_runs runs of
                               consecutive queries, runs[i] >= 1 queries each, summing to T;
                               the queries of a run read one sequence (a prefill chunk, a
@@ -132,7 +143,8 @@ typedef struct sa_queries {
                               indexer_score then launches the chunk kernel for runs of 9 or
                               more queries, the group kernel for neighbouring runs of one
                               length in 2..8, and one key stream per query for the rest
-                              (and "group" is ignored). Ignored by the other calls. */
+                              (and "group" is ignored). sparse_attn_fwd uses it only to
+                              check window_cap; the other calls ignore it. */
   int32_t num_runs;
 } sa_queries;
 
@@ -144,7 +156,14 @@ typedef struct sa_cache {
   int64_t latents_seq_stride;    /* >= compressed_cap * 512 */
   const void* window;            /* bf16 [num_seqs][window_cap][512]; raw position u is row u % window_cap */
   int64_t window_seq_stride;     /* >= window_cap * 512 */
-  int32_t window_cap;            /* >= 128 */
+  int32_t window_cap;            /* >= 128, and >= 127 + s where s is the span of raw
+                                    positions (max - min + 1) of the queries of one
+                                    sequence in a call: a later position's row would
+                                    otherwise overwrite a row an earlier query reads.
+                                    sparse_attn_fwd refuses (SA_EINVAL) what the host can
+                                    see: s >= the longest run, the group size, or T when
+                                    num_seqs is 1 (queries of one sequence in one call
+                                    are at distinct positions) */
   const void* idx_keys;          /* bf16 or e4m3 [num_seqs][compressed_cap][128], or MXFP4
                                     bytes [num_seqs][compressed_cap][64]; 16-byte aligned */
   int64_t idx_keys_seq_stride;   /* in elements of the store (bf16, bytes, bytes):
@@ -215,7 +234,10 @@ const char* sparse_attn_last_error(void);
  *              b's visible scores for b < ceil(n_t/8), -inf for the rest of
  *              the first E/8 entries. ld_block_max >= E/8, a multiple of 4.
  *   ld_scores and ld_block_max must be multiples of 4 (rows start 16-byte
- *   aligned) and at most 2^26. */
+ *   aligned) and at most 2^26.
+ * Launch limits (SA_EUNSUPPORTED beyond them, nothing enqueued): at most 65535
+ * independent queries or groups per call, and at most 65535 * 16 queries in one
+ * one-sequence batch or one run. */
 sa_status indexer_score(const sa_plan* plan, const sa_queries* queries, const sa_cache* cache,
                         const void* q_idx, const float* w, float* scores, int64_t ld_scores,
                         float* block_max, int64_t ld_block_max, void* stream);
@@ -233,7 +255,9 @@ sa_status indexer_score(const sa_plan* plan, const sa_queries* queries, const sa
  *   workspace  device, >= the size reported by sparse_attn_plan; used for the
  *              candidate blocks when cand is NULL and, for queries longer than
  *              65536 positions, for per-part candidate lists (the candidate stage then
- *              runs in two levels over parts of 8192 blocks). */
+ *              runs in two levels over parts of 8192 blocks, 16384 past 524288
+ *              positions). Such long rows allow at most 65535 queries per call
+ *              (SA_EUNSUPPORTED beyond, nothing enqueued). */
 sa_status select_topk(const sa_plan* plan, const sa_queries* queries, const float* scores,
                       int64_t ld_scores, const float* block_max, int64_t ld_block_max,
                       int32_t* cand, int32_t* topk, void* workspace, size_t workspace_bytes,
@@ -297,8 +321,9 @@ sa_status sparse_attn_compress(const sa_plan* plan, const void* raw, int64_t raw
                                int64_t G, void* stream);
 
 /* S0 into code rows: the compressor above, its fp32 result quantised into the e4m3 or MXFP4
- * latent store of the plan's kv_dtype (the FP8 and FP4 caches of the DeepSeek-V4 report,
- * KV cache section; bf16 plans return SA_EUNSUPPORTED). raw, gate, slot_bias and their
+ * latent store of the plan's kv_dtype (the FP8 and FP4 caches named in the Miles Day-0
+ * Support table of "SGLang and Miles Add Day-0 Support for DeepSeek-V4.1"; bf16 plans return
+ * SA_EUNSUPPORTED). raw, gate, slot_bias and their
  * strides as for sparse_attn_compress. Group g writes its code row at out + g*out_group_stride
  * and its scales at out_scales + g*scales_group_stride (both strides in bytes):
  *   SA_KV_FP8_E4M3: 512 e4m3 codes and one fp32 scale s = amax / 448 over the row (1 if the

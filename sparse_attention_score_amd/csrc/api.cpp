@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <new>
 
 #include "../../include/sparse_attn.h"
@@ -34,17 +35,39 @@ sa_status ok() {
   return SA_OK;
 }
 
+// SPARSE_ATTN_LOG=1 in the environment: one line on stderr per accepted call, naming the
+// kernel path and launch shape it takes (read once; host only, nothing on the device).
+bool log_on() {
+  static const bool on = [] {
+    const char* e = std::getenv("SPARSE_ATTN_LOG");
+    return e != nullptr && e[0] != '\0' && e[0] != '0';
+  }();
+  return on;
+}
+
+void log_call(const char* fmt, ...) {
+  if (!log_on()) return;
+  char buf[384];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  std::fprintf(stderr, "[sparse_attn] %s\n", buf);
+}
+
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-constexpr int64_t kMaxVisible = 2048LL * 8 * 32;  // 524288: largest block set a select WG holds
+constexpr int64_t kMaxVisible = 1LL << 20;        // 1,048,576 positions: 131072 blocks, 8 parts
+                                                   // of 16384 for the two-level candidate stage
 constexpr int kMaxGroup = 8;                        // queries per group sharing one key stream
+constexpr int64_t kMaxGridY = 65535;               // grid y holds queries, groups or query tiles
 constexpr int64_t kMaxLd = 1LL << 26;              // row strides of scores / block maxima: two rows
                                                    // stay addressable by 32-bit buffer offsets
 
 size_t cand_bytes(int64_t T) { return (size_t)T * 2048 * sizeof(int32_t); }
 // Part lists of the two-level candidate stage (queries longer than 8192 blocks).
 size_t part_bytes(int64_t T, int64_t max_visible) {
-  const int parts = sa::select_parts(max_visible);
+  const int parts = sa::select_parts(max_visible).parts;
   return parts > 1 ? (size_t)T * parts * 2048 * sizeof(int32_t) : 0;
 }
 
@@ -211,6 +234,19 @@ sa::QueryMeta meta(const sa_plan* plan, const sa_queries* q, int64_t num_seqs, i
 
 int64_t round8(int64_t v) { return (v + 7) / 8 * 8; }
 
+// Fewest distinct positions the queries of one sequence in this call can span, as far as
+// the host knows it: a run's length, a group's size, T for a batch over one sequence.
+int64_t min_window_span(const sa_queries* q, const sa_cache* c) {
+  int64_t span = 1;
+  if (q->runs) {
+    for (int32_t i = 0; i < q->num_runs; ++i) span = q->runs[i] > span ? q->runs[i] : span;
+  } else if (q->group > 1) {
+    span = q->group < q->T ? q->group : q->T;
+  }
+  if (c->num_seqs == 1) span = q->T;
+  return span;
+}
+
 // A ragged batch (sa_queries.runs): one launch per class of run over each contiguous
 // query range of that class. Runs of 9+ queries go to the chunk kernel (one launch per
 // run), neighbouring runs of one length in 2..8 to the group kernel, single queries (and
@@ -249,10 +285,14 @@ sa_status indexer_runs(const sa::IndexerArgs& a, const sa_queries* q, const sa_c
   const bool chunk_ok = !a.pages.table || c->page_size >= 64, group_ok = !a.mxfp4;
   RunLaunch r;
   // per-query and group launches index queries in grid y
-  for (RunCursor cur{q, chunk_ok, group_ok}; cur.next(r);)
-    SA_REQUIRE(r.kind == 2 || r.len / r.group <= 65535, SA_EUNSUPPORTED,
+  for (RunCursor cur{q, chunk_ok, group_ok}; cur.next(r);) {
+    SA_REQUIRE(r.kind == 2 || r.len / r.group <= kMaxGridY, SA_EUNSUPPORTED,
                "a range of %lld queries on the per-query or group kernel: at most 65535 per launch",
                (long long)r.len);
+    SA_REQUIRE(r.kind != 2 || (r.len + sa::kChunkQueriesPerWG - 1) / sa::kChunkQueriesPerWG <= kMaxGridY,
+               SA_EUNSUPPORTED, "a run of %lld queries: at most %lld per run", (long long)r.len,
+               (long long)(kMaxGridY * sa::kChunkQueriesPerWG));
+  }
   for (RunCursor cur{q, chunk_ok, group_ok}; cur.next(r);) {
     sa::IndexerArgs b = a;
     b.seq_id = a.seq_id + r.t0;
@@ -263,6 +303,9 @@ sa_status indexer_runs(const sa::IndexerArgs& a, const sa_queries* q, const sa_c
     b.scores = a.scores + r.t0 * a.ld_scores;
     b.block_max = a.block_max ? a.block_max + r.t0 * a.ld_block_max : nullptr;
     b.group = r.group;
+    log_call("indexer_score run: queries %lld..%lld on the %s kernel%s", (long long)r.t0,
+             (long long)(r.t0 + r.len - 1), r.kind == 2 ? "chunk" : r.kind == 1 ? "group" : "per-query",
+             r.kind == 1 ? " (one key stream per group)" : "");
     const hipError_t e = sa::launch_indexer(b, r.kind == 2, stream);
     if (e != hipSuccess) return hip_status(e, "indexer_score launch");
   }
@@ -361,9 +404,15 @@ sa_status indexer_score(const sa_plan* plan, const sa_queries* q, const sa_cache
   if (a.mxfp4) a.group = 1;
   if (q->runs) return indexer_runs(a, q, c, q_idx, w, (hipStream_t)stream);
   const bool prefill = (!a.pages.table || c->page_size >= 64) && a.group == 1 && c->num_seqs == 1 && q->T > 1;
-  SA_REQUIRE(prefill || (q->T + a.group - 1) / a.group <= 65535, SA_EUNSUPPORTED,
+  SA_REQUIRE(prefill || (q->T + a.group - 1) / a.group <= kMaxGridY, SA_EUNSUPPORTED,
              "T = %lld queries in groups of %d over several sequences: at most 65535 groups per call",
              (long long)q->T, (int)a.group);
+  SA_REQUIRE(!prefill || (q->T + sa::kChunkQueriesPerWG - 1) / sa::kChunkQueriesPerWG <= kMaxGridY,
+             SA_EUNSUPPORTED, "T = %lld queries of one sequence: at most %lld per call", (long long)q->T,
+             (long long)(kMaxGridY * sa::kChunkQueriesPerWG));
+  log_call("indexer_score: T=%lld max_visible=%lld E=%lld keys=%s %s%s kernel, group %d", (long long)q->T,
+           (long long)q->max_visible, (long long)E, a.mxfp4 ? "mxfp4" : a.fp8 ? "e4m3" : "bf16",
+           a.pages.table ? "paged " : "", prefill ? "chunk" : a.group > 1 ? "group" : "per-query", (int)a.group);
   return hip_status(sa::launch_indexer(a, prefill, (hipStream_t)stream), "indexer_score launch");
 }
 
@@ -390,7 +439,7 @@ sa_status indexer_score_cand(const sa_plan* plan, const sa_queries* q, const sa_
   SA_REQUIRE(ld_block_max >= 2048 && ld_block_max % 4 == 0 && ld_block_max <= kMaxLd, SA_EINVAL,
              "ld_block_max = %lld must be >= 2048, <= %lld and a multiple of 4", (long long)ld_block_max,
              (long long)kMaxLd);
-  SA_REQUIRE(q->T <= 65535, SA_EUNSUPPORTED, "T = %lld: at most 65535 queries per call", (long long)q->T);
+  SA_REQUIRE(q->T <= kMaxGridY, SA_EUNSUPPORTED, "T = %lld: at most 65535 queries per call", (long long)q->T);
   sa::IndexerArgs a;
   a.seq_id = q->seq_id;
   a.pos = q->pos;
@@ -415,6 +464,8 @@ sa_status indexer_score_cand(const sa_plan* plan, const sa_queries* q, const sa_
   a.cand = cand;
   a.group = 1;
   a.pages = sa::PageTable{nullptr, 0, 0, 0};
+  log_call("indexer_score_cand: T=%lld, 2048 carried blocks per query, keys=%s", (long long)q->T,
+           a.fp8 ? "e4m3" : "bf16");
   return hip_status(sa::launch_indexer(a, false, (hipStream_t)stream), "indexer_score_cand launch");
 }
 
@@ -444,6 +495,8 @@ sa_status select_topk_cand(const sa_plan* plan, const sa_queries* q, const int32
   a.topk = topk;
   a.part_ids = nullptr;
   a.parts = 1;
+  a.part_blocks = sa::kPartBlocks;
+  log_call("select_topk_cand: T=%lld", (long long)q->T);
   return hip_status(sa::launch_select_cand(a, (hipStream_t)stream), "select_topk_cand launch");
 }
 
@@ -476,6 +529,10 @@ sa_status select_topk(const sa_plan* plan, const sa_queries* q, const float* sco
                sa::kPartBlocks * 8);
     SA_REQUIRE(workspace_bytes >= need, SA_EWORKSPACE, "workspace_bytes = %zu < %zu", workspace_bytes, need);
   }
+  const sa::PartSplit ps = sa::select_parts(q->max_visible);
+  SA_REQUIRE(ps.parts <= 1 || q->T <= kMaxGridY, SA_EUNSUPPORTED,
+             "T = %lld queries longer than %d positions: at most 65535 per call", (long long)q->T,
+             sa::kPartBlocks * 8);
   if (!cand) cand = static_cast<int32_t*>(workspace);
   sa::SelectArgs a;
   // num_seqs / compressed_cap are not known here: the per-query n is capped by max_visible.
@@ -486,7 +543,10 @@ sa_status select_topk(const sa_plan* plan, const sa_queries* q, const float* sco
   a.ld_block_max = ld_block_max;
   a.cand = cand;
   a.topk = topk;
-  a.parts = sa::select_parts(q->max_visible);
+  a.parts = ps.parts;
+  a.part_blocks = ps.part_blocks;
+  log_call("select_topk: T=%lld max_visible=%lld, candidate stage in %d part(s) of %d blocks%s", (long long)q->T,
+           (long long)q->max_visible, ps.parts, ps.part_blocks, cand == workspace ? ", candidates in the workspace" : "");
   a.part_ids = a.parts > 1 ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + cand_bytes(q->T)) : nullptr;
   return hip_status(sa::launch_select(a, (hipStream_t)stream), "select_topk launch");
 }
@@ -502,6 +562,14 @@ sa_status sparse_attn_fwd(const sa_plan* plan, const sa_queries* q, const sa_cac
   SA_REQUIRE(topk && aligned16(topk), SA_EINVAL, "topk NULL or not 16-byte aligned");
   SA_REQUIRE(out && aligned16(out), SA_EINVAL, "out NULL or not 16-byte aligned");
   SA_REQUIRE(lse == nullptr || aligned16(lse), SA_EINVAL, "lse not 16-byte aligned");
+  // The window store is a ring (raw position u in row u % window_cap): the queries of one
+  // sequence in one call need window_cap >= 127 + the positions they span. Checked where
+  // the host knows a lower bound of that span: groups, runs, a one-sequence batch.
+  const int64_t span = min_window_span(q, c);
+  SA_REQUIRE(c->window_cap >= plan->p.window - 1 + span, SA_EINVAL,
+             "cache->window_cap = %d: queries of one sequence spanning %lld positions need >= %lld "
+             "(the window ring would overwrite rows they read)",
+             c->window_cap, (long long)span, (long long)(plan->p.window - 1 + span));
   sa::AttnArgs a;
   a.m = meta(plan, q, c->num_seqs, c->compressed_cap);
   a.pages = page_table(c);
@@ -536,6 +604,9 @@ sa_status sparse_attn_fwd(const sa_plan* plan, const sa_queries* q, const sa_cac
   } else {
     a.splits = 1;
   }
+  log_call("sparse_attn_fwd: T=%lld kv=%s, key list split over %d work-group(s)%s", (long long)q->T,
+           a.kv_mode == 2 ? "mxfp4+e4m3" : a.kv_mode == 1 ? "e4m3" : "bf16", a.splits,
+           a.pages.table ? ", paged latents" : "");
   return hip_status(sa::launch_attn(a, (hipStream_t)stream), "sparse_attn_fwd launch");
 }
 
@@ -577,6 +648,8 @@ sa_status sparse_attn_compress(const sa_plan* plan, const void* raw, int64_t raw
                "gate_group_stride = %lld invalid", (long long)gate_group_stride);
   }
   if (G == 0) return ok();
+  log_call("compressor: %lld groups of %d rows into %s rows", (long long)G, r,
+           plan->p.kv_dtype == SA_KV_MXFP4 ? "mxfp4" : plan->p.kv_dtype == SA_KV_FP8_E4M3 ? "e4m3" : "bf16");
   sa::CompressArgs a;
   a.raw = raw;
   a.raw_stride = raw_group_stride;
@@ -625,6 +698,8 @@ sa_status sparse_attn_compress_codes(const sa_plan* plan, const void* raw, int64
                "gate_group_stride = %lld invalid", (long long)gate_group_stride);
   }
   if (G == 0) return ok();
+  log_call("compressor: %lld groups of %d rows into %s rows", (long long)G, r,
+           plan->p.kv_dtype == SA_KV_MXFP4 ? "mxfp4" : plan->p.kv_dtype == SA_KV_FP8_E4M3 ? "e4m3" : "bf16");
   sa::CompressArgs a;
   a.raw = raw;
   a.raw_stride = raw_group_stride;

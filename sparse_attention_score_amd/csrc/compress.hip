@@ -9,7 +9,8 @@
 // Elementwise and HBM-bound: each thread handles 8 channels of one group with 16-byte
 // loads and stores; arithmetic in fp32, output rounded to bf16 (nearest even).
 //
-// Code rows (the FP8 and FP4 caches, DeepSeek-V4 report, KV cache section): one wave per
+// Code rows (the FP8 and FP4 caches of "SGLang and Miles Add Day-0 Support for DeepSeek-V4.1",
+// Miles Day-0 Support table, Quantization row): one wave per
 // group quantises the fp32 row it computed. e4m3: scale s = amax / 448 over the row (1 for
 // an all-zero row), code = nearest e4m3 of x / s (ties to the even code). MXFP4: per block of
 // 32 channels, E8M0 exponent X = floor(log2 amax) - 2 (-127 for an all-zero block, clamped

@@ -727,6 +727,7 @@ constexpr int kPWaves = SA_P_WAVES;
 constexpr int kPThreads = 64 * kPWaves;
 constexpr int kPairsPerWave = 2;
 constexpr int kQPerWG = kPWaves * kPairsPerWave * 2;   // 16 queries
+static_assert(kQPerWG == kChunkQueriesPerWG, "the host sizes the chunk grid with this");
 constexpr int kPKT = 32;                                // keys per tile
 constexpr int kPChunk = SA_P_CHUNK;                     // keys per work-group (4096: 3 % faster than 2048)
 constexpr int kPST = 2 * kPKT;                          // keys per LDS stage (two tiles)

@@ -52,8 +52,12 @@ struct IndexerArgs {
   PageTable pages;          // keys and scales are page pools when pages.table is set
 };
 hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream);
+// Queries per work-group of the chunk kernel (its grid holds ceil(T / this) in y).
+constexpr int kChunkQueriesPerWG = 16;
 
-constexpr int kPartBlocks = 8192;   // blocks per part of the two-level candidate stage
+constexpr int kPartBlocks = 8192;   // blocks per part of the two-level candidate stage (rows of
+                                    // up to 8 parts; longer rows use parts of twice that)
+constexpr int kMaxParts = 8;        // part lists the second level holds (8 x 2048 block ids)
 
 struct SelectArgs {
   QueryMeta m;
@@ -65,9 +69,14 @@ struct SelectArgs {
   int32_t* topk;            // [T][512]
   int32_t* part_ids;        // [T][parts][2048] workspace, used when parts > 1
   int parts;                // select_parts(m.max_visible)
+  int part_blocks;          // blocks per part (kPartBlocks or 2 * kPartBlocks)
 };
-// Parts of the candidate stage for queries of up to max_visible positions (1: one level).
-int select_parts(int64_t max_visible);
+// Parts of the candidate stage for queries of up to max_visible positions (parts 1: one
+// level), and their size in blocks.
+struct PartSplit {
+  int parts, part_blocks;
+};
+PartSplit select_parts(int64_t max_visible);
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream);
 // Candidate mode: top-512 positions inside carried candidate blocks (a.cand is the input,
 // scores / block_max in slot order as the candidate-mode indexer writes them).

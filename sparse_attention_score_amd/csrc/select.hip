@@ -13,9 +13,10 @@
 // pile onto a few bins. Then every element with key > v is kept, plus the lowest-id
 // elements with key == v until k are taken; work-group prefix sums place the kept ids in
 // ascending order.
-// Above 8192 blocks S2 runs in two levels: parts of 8192 blocks each keep their own best
-// 2048 (a block among the best 2048 of the union is among the best 2048 of its part, with
-// the same order), then one work-group per query selects among the survivors.
+// Above 8192 blocks S2 runs in two levels: parts of 8192 blocks (16384 for rows past 65536
+// blocks, so at most 8 parts up to 1,048,576 positions) each keep their own best 2048 (a
+// block among the best 2048 of the union is among the best 2048 of its part, with the same
+// order), then one work-group per query selects among the survivors.
 #include "sa_device.h"
 #include "sa_launch.h"
 
@@ -541,11 +542,12 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
 template <int NT, int EPT>
 __global__ __launch_bounds__(NT) void select_part_kernel(SelectArgs a) {
   __shared__ SelShared sh;
+  static_assert(NT * EPT == kPartBlocks || NT * EPT == 2 * kPartBlocks, "one part per work-group");
   const int t = blockIdx.y, p = blockIdx.x;
   const int64_t n = visible_n(a.m, t);
   const int nb = (int)((n + kBlock - 1) / kBlock);
-  const int b0 = p * kPartBlocks;
-  const int b1 = min(nb, b0 + kPartBlocks);
+  const int b0 = p * (NT * EPT);
+  const int b1 = min(nb, b0 + NT * EPT);
   int32_t* out = a.part_ids + ((int64_t)t * a.parts + p) * kCandBlocks;
   if (b1 - b0 <= kCandBlocks) {
     for (int i = threadIdx.x; i < kCandBlocks; i += NT) out[i] = b0 + i < b1 ? b0 + i : -1;
@@ -723,8 +725,14 @@ hipError_t launch_select_nt(const SelectArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((select_kernel<NT, kPartBlocks / NT>), grid, dim3(NT), 0, stream, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((select_part_kernel<NT, kPartBlocks / NT>), dim3((unsigned)a.parts, (unsigned)a.m.T),
-                     dim3(NT), 0, stream, a);
+  const dim3 pgrid((unsigned)a.parts, (unsigned)a.m.T);
+  if (a.part_blocks == kPartBlocks)
+    hipLaunchKernelGGL((select_part_kernel<NT, kPartBlocks / NT>), pgrid, dim3(NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL((select_part_kernel<NT, 2 * kPartBlocks / NT>), pgrid, dim3(NT), 0, stream, a);
+  // the merge reads the part lists: enqueue it only if the part launch was accepted
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int per_thread = a.parts * kCandBlocks / NT;
   if (per_thread <= 16 * 256 / NT)
     hipLaunchKernelGGL((select_merge_kernel<NT, 16 * 256 / NT>), grid, dim3(NT), 0, stream, a);
@@ -737,9 +745,11 @@ hipError_t launch_select_nt(const SelectArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-int select_parts(int64_t max_visible) {
+PartSplit select_parts(int64_t max_visible) {
   const int64_t nb = (max_visible + kBlock - 1) / kBlock;
-  return nb <= kPartBlocks ? 1 : (int)((nb + kPartBlocks - 1) / kPartBlocks);
+  if (nb <= kPartBlocks) return {1, kPartBlocks};
+  const int size = nb <= (int64_t)kMaxParts * kPartBlocks ? kPartBlocks : 2 * kPartBlocks;
+  return {(int)((nb + size - 1) / size), size};
 }
 
 hipError_t launch_select_cand(const SelectArgs& a, hipStream_t stream) {

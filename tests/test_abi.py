@@ -57,7 +57,7 @@ def _plan(**kw):
     (dict(cand_blocks=1024), S.SA_EUNSUPPORTED),
     (dict(max_queries=0), S.SA_EINVAL),
     (dict(max_compressed=-1), S.SA_EINVAL),
-    (dict(max_compressed=524289), S.SA_EUNSUPPORTED),
+    (dict(max_compressed=(1 << 20) + 1), S.SA_EUNSUPPORTED),
     (dict(softmax_scale=float("nan")), S.SA_EINVAL),
     (dict(softmax_scale=0.0), S.SA_EINVAL),
 ])
@@ -90,6 +90,70 @@ def test_plan_workspace_and_last_error_reset(mq):
     p = _plan(max_queries=mq)
     assert p.workspace_bytes == _expected_workspace(mq)
     assert S.lib.sparse_attn_last_error() == b""
+
+
+@pytest.mark.parametrize("maxc,parts", [(65536, 1), (65544, 2), (524288, 8), (524296, 5),
+                                         (1 << 20, 8)])
+def test_plan_accepts_long_rows(maxc, parts):
+    # ratio-1 layers at the pages' 1,048,576-token context: rows up to 2^20 positions. Rows
+    # past 8192 blocks run the candidate stage over parts (8192 blocks, or 16384 past 65536
+    # blocks), whose 2048-id lists live in the select area of the workspace.
+    mq = 3
+    p = _plan(ratio=1, key_dtype="fp8", max_queries=mq, max_compressed=maxc)
+    nb = (maxc + 7) // 8
+    size = 8192 if nb <= 8 * 8192 else 16384
+    expect = 1 if nb <= 8192 else -(-nb // size)
+    assert expect == parts
+    extra = mq * parts * 2048 * 4 if parts > 1 else 0
+    a256 = lambda b: (b + 255) // 256 * 256
+    select = mq * 2048 * 4 + extra
+    counters = a256(select)
+    ml = counters + a256(4 * mq)
+    o = ml + a256(4 * mq * 64 * 2 * 4)
+    assert p.workspace_bytes == o + 4 * mq * 64 * 512 * 4
+
+
+def test_select_refuses_grid_overflow():
+    # parts in grid x, queries in grid y: rows longer than 65536 positions take at most 65535
+    # queries per call (refused on the host, nothing enqueued)
+    p = _plan(ratio=1, max_queries=70000, max_compressed=1 << 20)
+    q = _q(T=65536, max_visible=65544)
+    st = S.lib.select_topk(p.handle, ctypes.byref(q), 0x60000, 65544, None, 0, 0x80000, 0xA0000,
+                           0x90000, 1 << 40, None)
+    assert st == S.SA_EUNSUPPORTED and b"65535" in S.lib.sparse_attn_last_error()
+
+
+def test_indexer_refuses_chunk_grid_overflow():
+    # the chunk kernel holds ceil(T / 16) query tiles in grid y
+    T = 65535 * 16 + 1
+    p = _plan(ratio=1, max_queries=T, max_compressed=4096)
+    q = _q(T=T, max_visible=100)
+    c = _c(num_seqs=1)
+    assert _indexer(p, q, c) == S.SA_EUNSUPPORTED
+    arr = (ctypes.c_int32 * 1)(T)
+    q.runs = ctypes.cast(arr, ctypes.c_void_p)
+    q.num_runs = 1
+    assert _indexer(p, q, c) == S.SA_EUNSUPPORTED
+    assert b"per run" in S.lib.sparse_attn_last_error()
+
+
+@pytest.mark.parametrize("case,wcap", [("group6", 132), ("runs3-7", 133), ("one_seq_T4", 130)])
+def test_attn_refuses_aliasing_window_ring(case, wcap):
+    # window rows live at u % window_cap: queries of one sequence spanning s positions need
+    # window_cap >= 127 + s, or later positions overwrite rows earlier queries read
+    p = _plan(max_queries=16)
+    q, c = _q(T=10 if case != "one_seq_T4" else 4), _c(window_cap=wcap, window_seq_stride=wcap * 512)
+    if case == "group6":
+        q.group = 6
+    if case == "runs3-7":
+        arr = (ctypes.c_int32 * 2)(3, 7)
+        q.runs = ctypes.cast(arr, ctypes.c_void_p)
+        q.num_runs = 2
+    if case == "one_seq_T4":
+        c.num_seqs = 1
+    st = S.lib.sparse_attn_fwd(p.handle, ctypes.byref(q), ctypes.byref(c), 0x40000, 0x50000,
+                               0x60000, None, None, 0, None)
+    assert st == S.SA_EINVAL and b"window_cap" in S.lib.sparse_attn_last_error()
 
 
 def test_workspace_init_checks():

@@ -32,8 +32,14 @@ def test_c_program_runs_the_decode_path(tmp_path):
                           ("win", wl.R, np.uint16), ("keys", wl.KI, np.uint16)):
         np.ascontiguousarray(arr, dtype=dt).tofile(tmp_path / f"{name}.bin")
     print(f"[case] {wl.name} via {EXE}", flush=True)
-    r = subprocess.run([EXE, str(tmp_path)], capture_output=True, text=True, timeout=120)
+    # SPARSE_ATTN_LOG=1: one line per accepted call on stderr, naming the path taken
+    r = subprocess.run([EXE, str(tmp_path)], capture_output=True, text=True, timeout=120,
+                       env=dict(os.environ, SPARSE_ATTN_LOG="1"))
     assert r.returncode == 0, r.stderr
+    log = [ln for ln in r.stderr.splitlines() if ln.startswith("[sparse_attn] ")]
+    assert any(ln.startswith("[sparse_attn] indexer_score: T=4 ") and "per-query kernel" in ln for ln in log), log
+    assert any(ln.startswith("[sparse_attn] select_topk: T=4 ") for ln in log), log
+    assert any(ln.startswith("[sparse_attn] sparse_attn_fwd: T=4 ") for ln in log), log
     topk = np.fromfile(tmp_path / "topk.bin", dtype=np.int32).reshape(T, 512)
     out = np.fromfile(tmp_path / "out.bin", dtype=np.uint16).reshape(T, 64, 512)
     lse = np.fromfile(tmp_path / "lse.bin", dtype=np.float32).reshape(T, 64)

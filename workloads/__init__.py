@@ -396,6 +396,9 @@ MORE_WORKLOADS = {
     # ... and with MXFP4 latent rows (the 4-bit compressed state) and e4m3 window rows
     "decode-b128-ctx128k-fp4kv": dict(kind="decode", B=128, n_raw=131072, ratio=2, key_dtype="fp8",
                                       kv_dtype="mxfp4", compress_codes=True),
+    # a 1-to-1 layer (the ratio of the pages' layers from 20 on) at the 1,048,576-token context:
+    # every position is a compressed latent, 131072 blocks of 8
+    "decode-b2-ctx1m-r1-fp8": dict(kind="decode", B=2, n_raw=1048576, ratio=1, key_dtype="fp8"),
     # a ragged serving batch at 128K context: two 1024-query prefill chunks, 64 single decode
     # queries and 16 decode steps with 5 drafted tokens (2208 queries, 82 sequences)
     "ragged-2x1024+64+16x6-ctx128k-fp8": dict(kind="ragged", n_raw=[131072] * 82,
