@@ -308,6 +308,22 @@ sa_status sparse_attn_fwd(const sa_plan* plan, const sa_queries* queries, const 
                           const void* q, const int32_t* topk, void* out, float* lse,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* sparse_attn_fwd for callers that cannot allocate device memory or pass a workspace
+ * (code under HIP graph capture, serving loops that forbid allocation). Same arguments,
+ * checks, results and limits as sparse_attn_fwd with a workspace of the plan's size;
+ * batches of at most 32 queries keep their key-split state in a fixed array of
+ * 16.1 MiB that the library holds on each GPU it runs on until the process ends,
+ * instead of a workspace (larger batches use no scratch memory). The call allocates and
+ * frees nothing: it enqueues a kernel that zeroes the array's per-query counters and the
+ * attention kernel on `stream`. Calls that overlap on one GPU (other streams, other
+ * threads) share the array and race; serialise them. The first call on each GPU looks up
+ * that GPU's copy of the array (hipGetSymbolAddress) and must not run under graph capture.
+ * SA_EUNSUPPORTED if a batch's key splits would not fit the array; SA_EHIP if the lookup
+ * or a launch fails. */
+sa_status sparse_attn_fwd_noalloc(const sa_plan* plan, const sa_queries* queries, const sa_cache* cache,
+                                  const void* q, const int32_t* topk, void* out, float* lse,
+                                  void* stream);
+
 /* S0. Softmax-gate compressor over G groups of `ratio` raw latents.
  * Group g reads raw rows raw + g*raw_group_stride + k*512 and gate logits
  * gate + g*gate_group_stride + k*512 (k < ratio, bf16), and writes

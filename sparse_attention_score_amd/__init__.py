@@ -3,7 +3,8 @@
 Argument marshalling only. Every stage runs in the library's HIP kernels; torch is used
 for device memory and the current stream. The entry points have the names of the C ABI
 (include/sparse_attn.h): sparse_attn_plan, indexer_score, indexer_score_cand, select_topk,
-select_topk_cand, sparse_attn_fwd, sparse_attn_compress, sparse_attn_compress_codes. If the
+select_topk_cand, sparse_attn_fwd, sparse_attn_fwd_noalloc, sparse_attn_compress,
+sparse_attn_compress_codes. If the
 built library is missing, importing this package raises.
 """
 from __future__ import annotations
@@ -28,7 +29,8 @@ STATUS_NAMES = {0: "SA_OK", 1: "SA_EINVAL", 2: "SA_EUNSUPPORTED", 3: "SA_EWORKSP
 
 EXPORTS = ("sparse_attn_plan", "sparse_attn_plan_destroy", "sparse_attn_last_error",
            "sparse_attn_workspace_init", "indexer_score", "select_topk", "indexer_score_cand",
-           "select_topk_cand", "sparse_attn_fwd", "sparse_attn_compress", "sparse_attn_compress_codes")
+           "select_topk_cand", "sparse_attn_fwd", "sparse_attn_fwd_noalloc", "sparse_attn_compress",
+           "sparse_attn_compress_codes")
 
 
 class sa_params(ctypes.Structure):
@@ -93,6 +95,9 @@ def _load():
     lib.sparse_attn_fwd.argtypes = [vp, ctypes.POINTER(sa_queries), ctypes.POINTER(sa_cache), vp, vp,
                                     vp, vp, vp, sz, vp]
     lib.sparse_attn_fwd.restype = ctypes.c_int
+    lib.sparse_attn_fwd_noalloc.argtypes = [vp, ctypes.POINTER(sa_queries), ctypes.POINTER(sa_cache), vp, vp,
+                                            vp, vp, vp]
+    lib.sparse_attn_fwd_noalloc.restype = ctypes.c_int
     lib.sparse_attn_compress.argtypes = [vp, vp, i64, vp, i64, vp, vp, i64, i64, vp]
     lib.sparse_attn_compress.restype = ctypes.c_int
     lib.sparse_attn_compress_codes.argtypes = [vp, vp, i64, vp, i64, vp, vp, i64, vp, i64, i64, vp]
@@ -341,6 +346,18 @@ def sparse_attn_fwd(plan: Plan, queries: Queries, cache: Cache, q: torch.Tensor,
     _check(lib.sparse_attn_fwd(plan.handle, ctypes.byref(queries.c), ctypes.byref(cache.c), _ptr(q),
                                _ptr(topk), _ptr(out), _ptr(lse), _ptr(workspace), ws_bytes,
                                _stream(stream)))
+
+
+def sparse_attn_fwd_noalloc(plan: Plan, queries: Queries, cache: Cache, q: torch.Tensor, topk: torch.Tensor,
+                            out: torch.Tensor, lse: Optional[torch.Tensor] = None, stream=None):
+    """sparse_attn_fwd without a workspace: key-split state in the library's fixed per-GPU array."""
+    _need(q, "q", torch.bfloat16)
+    _need(topk, "topk", torch.int32)
+    _need(out, "out", torch.bfloat16)
+    if lse is not None:
+        _need(lse, "lse", torch.float32)
+    _check(lib.sparse_attn_fwd_noalloc(plan.handle, ctypes.byref(queries.c), ctypes.byref(cache.c), _ptr(q),
+                                       _ptr(topk), _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def sparse_attn_compress(plan: Plan, raw: torch.Tensor, raw_group_stride: int, gate: Optional[torch.Tensor],

@@ -312,6 +312,49 @@ sa_status indexer_runs(const sa::IndexerArgs& a, const sa_queries* q, const sa_c
   return ok();
 }
 
+// Checks shared by the attention entry points; fills every field but the key-split state.
+sa_status attn_args(const sa_plan* plan, const sa_queries* q, const sa_cache* c, const void* qv,
+                    const int32_t* topk, void* out, float* lse, sa::AttnArgs& a) {
+  sa_status st;
+  if ((st = check_plan(plan)) != SA_OK) return st;
+  if ((st = check_queries(plan, q)) != SA_OK) return st;
+  if ((st = check_cache(plan, q, c, false, true)) != SA_OK) return st;
+  SA_REQUIRE(qv && aligned16(qv), SA_EINVAL, "q NULL or not 16-byte aligned");
+  SA_REQUIRE(topk && aligned16(topk), SA_EINVAL, "topk NULL or not 16-byte aligned");
+  SA_REQUIRE(out && aligned16(out), SA_EINVAL, "out NULL or not 16-byte aligned");
+  SA_REQUIRE(lse == nullptr || aligned16(lse), SA_EINVAL, "lse not 16-byte aligned");
+  // The window store is a ring (raw position u in row u % window_cap): the queries of one
+  // sequence in one call need window_cap >= 127 + the positions they span. Checked where
+  // the host knows a lower bound of that span: groups, runs, a one-sequence batch.
+  const int64_t span = min_window_span(q, c);
+  SA_REQUIRE(c->window_cap >= plan->p.window - 1 + span, SA_EINVAL,
+             "cache->window_cap = %d: queries of one sequence spanning %lld positions need >= %lld "
+             "(the window ring would overwrite rows they read)",
+             c->window_cap, (long long)span, (long long)(plan->p.window - 1 + span));
+  a.m = meta(plan, q, c->num_seqs, c->compressed_cap);
+  a.pages = page_table(c);
+  a.kv_mode = plan->p.kv_dtype;
+  a.latent_scales = c->latent_scales;
+  a.latent_scales_seq_stride = c->latent_scales_seq_stride;
+  a.window_scales = c->window_scales;
+  a.window_scales_seq_stride = c->window_scales_seq_stride;
+  a.q = qv;
+  a.topk = topk;
+  a.latents = c->latents;
+  a.latents_seq_stride = c->latents_seq_stride;
+  a.window = c->window;
+  a.window_seq_stride = c->window_seq_stride;
+  a.window_cap = c->window_cap;
+  a.scale = plan->p.softmax_scale;
+  a.out = out;
+  a.lse = lse;
+  a.splits = 1;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  a.counters = nullptr;
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -554,47 +597,13 @@ sa_status select_topk(const sa_plan* plan, const sa_queries* q, const float* sco
 sa_status sparse_attn_fwd(const sa_plan* plan, const sa_queries* q, const sa_cache* c,
                           const void* qv, const int32_t* topk, void* out, float* lse,
                           void* workspace, size_t workspace_bytes, void* stream) {
-  sa_status st;
-  if ((st = check_plan(plan)) != SA_OK) return st;
-  if ((st = check_queries(plan, q)) != SA_OK) return st;
-  if ((st = check_cache(plan, q, c, false, true)) != SA_OK) return st;
-  SA_REQUIRE(qv && aligned16(qv), SA_EINVAL, "q NULL or not 16-byte aligned");
-  SA_REQUIRE(topk && aligned16(topk), SA_EINVAL, "topk NULL or not 16-byte aligned");
-  SA_REQUIRE(out && aligned16(out), SA_EINVAL, "out NULL or not 16-byte aligned");
-  SA_REQUIRE(lse == nullptr || aligned16(lse), SA_EINVAL, "lse not 16-byte aligned");
-  // The window store is a ring (raw position u in row u % window_cap): the queries of one
-  // sequence in one call need window_cap >= 127 + the positions they span. Checked where
-  // the host knows a lower bound of that span: groups, runs, a one-sequence batch.
-  const int64_t span = min_window_span(q, c);
-  SA_REQUIRE(c->window_cap >= plan->p.window - 1 + span, SA_EINVAL,
-             "cache->window_cap = %d: queries of one sequence spanning %lld positions need >= %lld "
-             "(the window ring would overwrite rows they read)",
-             c->window_cap, (long long)span, (long long)(plan->p.window - 1 + span));
   sa::AttnArgs a;
-  a.m = meta(plan, q, c->num_seqs, c->compressed_cap);
-  a.pages = page_table(c);
-  a.kv_mode = plan->p.kv_dtype;
-  a.latent_scales = c->latent_scales;
-  a.latent_scales_seq_stride = c->latent_scales_seq_stride;
-  a.window_scales = c->window_scales;
-  a.window_scales_seq_stride = c->window_scales_seq_stride;
-  a.q = qv;
-  a.topk = topk;
-  a.latents = c->latents;
-  a.latents_seq_stride = c->latents_seq_stride;
-  a.window = c->window;
-  a.window_seq_stride = c->window_seq_stride;
-  a.window_cap = c->window_cap;
-  a.scale = plan->p.softmax_scale;
-  a.out = out;
-  a.lse = lse;
+  sa_status st;
+  if ((st = attn_args(plan, q, c, qv, topk, out, lse, a)) != SA_OK) return st;
   // key splits need the plan's whole workspace (its counters zeroed once by
   // sparse_attn_workspace_init); without it every query runs in one work-group
   const WsLayout wl = ws_layout(plan->p);
   a.splits = sa::attn_splits(q->T);
-  a.part_o = nullptr;
-  a.part_ml = nullptr;
-  a.counters = nullptr;
   if (a.splits > 1 && workspace != nullptr && aligned16(workspace) && workspace_bytes >= wl.total &&
       q->T * a.splits <= wl.units) {
     char* ws = static_cast<char*>(workspace);
@@ -608,6 +617,33 @@ sa_status sparse_attn_fwd(const sa_plan* plan, const sa_queries* q, const sa_cac
            a.kv_mode == 2 ? "mxfp4+e4m3" : a.kv_mode == 1 ? "e4m3" : "bf16", a.splits,
            a.pages.table ? ", paged latents" : "");
   return hip_status(sa::launch_attn(a, (hipStream_t)stream), "sparse_attn_fwd launch");
+}
+
+sa_status sparse_attn_fwd_noalloc(const sa_plan* plan, const sa_queries* q, const sa_cache* c,
+                                  const void* qv, const int32_t* topk, void* out, float* lse,
+                                  void* stream) {
+  sa::AttnArgs a;
+  sa_status st;
+  if ((st = attn_args(plan, q, c, qv, topk, out, lse, a)) != SA_OK) return st;
+  a.splits = sa::attn_splits(q->T);
+  if (a.splits > 1) {
+    SA_REQUIRE(q->T * a.splits <= sa::kScratchUnits, SA_EUNSUPPORTED,
+               "sparse_attn_fwd_noalloc: %lld queries in %d key splits exceed the fixed scratch "
+               "(%lld partial slots)", (long long)q->T, a.splits, (long long)sa::kScratchUnits);
+    sa::AttnScratch s;
+    hipError_t e = sa::attn_scratch(s);
+    if (e != hipSuccess) return hip_status(e, "sparse_attn_fwd_noalloc scratch address");
+    a.counters = s.counters;
+    a.part_ml = s.part_ml;
+    a.part_o = s.part_o;
+    // the counters must start at zero: cleared by a kernel on the caller's stream
+    e = sa::launch_zero_u32(s.counters, q->T, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, "sparse_attn_fwd_noalloc counter reset launch");
+  }
+  log_call("sparse_attn_fwd_noalloc: T=%lld kv=%s, key list split over %d work-group(s)%s", (long long)q->T,
+           a.kv_mode == 2 ? "mxfp4+e4m3" : a.kv_mode == 1 ? "e4m3" : "bf16", a.splits,
+           a.splits > 1 ? " (fixed scratch)" : "");
+  return hip_status(sa::launch_attn(a, (hipStream_t)stream), "sparse_attn_fwd_noalloc launch");
 }
 
 sa_status sparse_attn_workspace_init(const sa_plan* plan, void* workspace, size_t workspace_bytes,

@@ -32,6 +32,9 @@
 // query's 64 heads over two work-groups instead, which need no combining: both gather the
 // same rows, and as neighbours in the grid they normally share an XCD, so the second
 // read comes from its L2.
+#include <atomic>
+#include <mutex>
+
 #include "sa_device.h"
 #include "sa_launch.h"
 
@@ -44,7 +47,7 @@ constexpr int kVW = kAW - kSW;
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer resource, 32-bit data (gfx9 family)
 constexpr int kCoherent = 16;            // buffer cache policy sc1: device-scope coherent
 constexpr int64_t kAttnPartBytesO = 64 * 512 * 4;   // one partial O
-constexpr int kMaxSplits = 4;
+constexpr int kMaxSplits = kMaxAttnSplits;
 constexpr int kAThreads = 64 * kAW;
 constexpr int kHG = 4;              // head groups of 16
 constexpr int kKT = 32;             // keys per step
@@ -811,6 +814,53 @@ hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n);
   return hipGetLastError();
+}
+
+}  // namespace sa
+
+// Key-split state for callers that cannot allocate (sparse_attn_fwd_noalloc): one fixed
+// array per GPU instead of a workspace. Layout: [kScratchQueries u32 counters, padded to
+// 256 B][kScratchUnits x 64 x 2 fp32 partial references and normalisers][kScratchUnits
+// partial outputs of 128 KiB]. Host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device (attn_scratch below).
+namespace {
+constexpr size_t kScratchMlOff = 256;
+constexpr size_t kScratchOOff = kScratchMlOff + (size_t)sa::kScratchUnits * 64 * 2 * sizeof(float);
+constexpr size_t kScratchBytes = kScratchOOff + (size_t)sa::kScratchUnits * 64 * 512 * sizeof(float);
+static_assert(sa::kScratchQueries * sizeof(uint32_t) <= kScratchMlOff, "counters fit before the partials");
+static_assert(kScratchOOff % 256 == 0, "partial outputs 256-byte aligned");
+constexpr int kScratchDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace sa {
+
+hipError_t attn_scratch(AttnScratch& s) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+  static std::atomic<uint8_t*> ptrs[kScratchDevices] = {};
+  static std::mutex mu;
+  uint8_t* base = ptrs[dev].load(std::memory_order_acquire);
+  if (base == nullptr) {
+    std::lock_guard<std::mutex> lock(mu);
+    base = ptrs[dev].load(std::memory_order_relaxed);
+    if (base == nullptr) {
+      void* p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // this device's copy of the array
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      base = static_cast<uint8_t*>(p);
+      ptrs[dev].store(base, std::memory_order_release);
+    }
+  }
+  s.counters = reinterpret_cast<uint32_t*>(base);
+  s.part_ml = reinterpret_cast<float*>(base + kScratchMlOff);
+  s.part_o = reinterpret_cast<float*>(base + kScratchOOff);
+  s.bytes = kScratchBytes;
+  return hipSuccess;
 }
 
 }  // namespace sa

@@ -119,6 +119,19 @@ int attn_splits(int64_t T);
 int64_t attn_max_units(int64_t max_queries);
 // Zero n 32-bit words (a kernel, so the call may be captured in a graph).
 hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t stream);
+// Key-split state in a fixed per-GPU array (for callers that cannot allocate): counters,
+// partial references / normalisers and partial outputs for up to kScratchQueries queries of
+// kMaxAttnSplits work-groups each, on the current device.
+constexpr int kScratchQueries = 32;
+constexpr int kMaxAttnSplits = 4;
+constexpr int64_t kScratchUnits = (int64_t)kScratchQueries * kMaxAttnSplits;
+struct AttnScratch {
+  uint32_t* counters;       // [kScratchQueries]
+  float* part_ml;           // [kScratchUnits][64][2]
+  float* part_o;            // [kScratchUnits][64][512]
+  size_t bytes;
+};
+hipError_t attn_scratch(AttnScratch& s);
 
 struct CompressArgs {
   const void* raw;

@@ -279,6 +279,24 @@ def test_attn_rejects():
                                0x70004, None, 0, None) == S.SA_EINVAL
 
 
+def test_attn_noalloc_rejects():
+    # the same host checks as sparse_attn_fwd, before any HIP call (no scratch lookup)
+    p = _plan()
+    q = _q()
+    lib = S.lib
+    for c in (_c(window_cap=127), _c(latents=None), _c(window=None)):
+        assert lib.sparse_attn_fwd_noalloc(p.handle, ctypes.byref(q), ctypes.byref(c), 0x40000, 0x50000,
+                                           0x60000, None, None) == S.SA_EINVAL
+    c = _c()
+    assert lib.sparse_attn_fwd_noalloc(None, ctypes.byref(q), ctypes.byref(c), 0x40000, 0x50000, 0x60000,
+                                       None, None) == S.SA_EINVAL
+    assert lib.sparse_attn_fwd_noalloc(p.handle, ctypes.byref(q), ctypes.byref(c), None, 0x50000, 0x60000,
+                                       None, None) == S.SA_EINVAL
+    assert lib.sparse_attn_fwd_noalloc(p.handle, ctypes.byref(q), ctypes.byref(c), 0x40000, 0x50000, 0x60000,
+                                       0x70004, None) == S.SA_EINVAL
+    assert S.lib.sparse_attn_last_error()
+
+
 def test_compress_rejects():
     p = _plan()
     lib = S.lib
