@@ -18,12 +18,19 @@ the headline decode batch with MXFP4 index keys (the 4-bit indexer cache), and a
 indexer, selection and attention on paged stores (64-row pages, block tables). A sixth
 times a ragged serving batch (prefill chunks, drafted decode steps and single decode queries
 in one call), a seventh the headline batch with e4m3 latent and window rows, and an eighth
-with MXFP4 latent rows and e4m3 window rows.
+with MXFP4 latent rows and e4m3 window rows. The other layer configurations get one object
+each: the 4-query batch at 2K context (latency), the 64-query batch at 32K context (warm, and
+cold: two copies of its stores used in turn, 2 x 319 MB against the 256 MiB last-level cache),
+the 8-query batch at 1M context, and a 1-to-1 layer at 1M context (2 queries, 2^20 positions
+each). The compressor alone runs over the raw context of the 64-query batch (64 x 32768 raw
+latents into 64 x 16384 compressed ones).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                        [--no-prefill] [--no-rescore] [--no-multiquery] [--no-mxfp4] [--no-paged]
-                       [--no-ragged] [--no-fp8kv]
-                       [--no-cpu-baseline] [--profile]
+                       [--no-ragged] [--no-fp8kv] [--no-configs] [--no-compress]
+                       [--only LEG[,LEG...]] [--no-cpu-baseline] [--profile]
+Legs for --only: paged, rescore, multiquery, mxfp4, fp8kv, ragged, prefill, c1, c2, c5, r1m,
+compress, cpu (the headline decode batch always runs: it is the reported value).
 """
 from __future__ import annotations
 
@@ -51,26 +58,31 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_decode-b128-ctx128k-fp8_t
 RESCORE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_cand_decode-b128-ctx128k-fp8_traffic.json")
 GROUP_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_group_decode-mq6-b128-ctx128k-fp8_traffic.json")
 MX_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_mx_decode-b128-ctx128k-mxfp4_traffic.json")
+CONFIG_TRAFFIC_FILES = {"decode-b64-ctx32k": os.path.join(ROOT, "profiles", "indexer_decode-b64-ctx32k_traffic.json"),
+                        "decode-b8-ctx1m-fp8": os.path.join(ROOT, "profiles", "indexer_decode-b8-ctx1m-fp8_traffic.json")}
+COMPRESS_SOURCES = ("sparse_attention_score_amd/csrc/compress.hip", "sparse_attention_score_amd/csrc/sa_device.h",
+                    "sparse_attention_score_amd/csrc/sa_launch.h")
+COMPRESS_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compress_raw-64x32768_traffic.json")
 COPY_BYTES = 1 << 30
 
 
-def indexer_source_hash() -> str:
+def indexer_source_hash(sources=INDEXER_SOURCES) -> str:
     h = hashlib.sha256()
-    for f in INDEXER_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def stored_traffic(workload: str, path: str = TRAFFIC_FILE):
-    """HBM bytes per indexer launch from the committed rocprofv3 counter summary, or None if
-    there is none for this workload or the indexer source changed since it was taken."""
+def stored_traffic(workload: str, path: str = TRAFFIC_FILE, sources=INDEXER_SOURCES):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None if there is
+    none for this workload or the kernel's sources changed since it was taken."""
     try:
         with open(path) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("workload") != workload or d.get("source_sha256") != indexer_source_hash():
+    if d.get("workload") != workload or d.get("source_sha256") != indexer_source_hash(sources):
         return None
     return d.get("traffic_bytes_per_launch")
 
@@ -388,6 +400,98 @@ def cpu_baseline(wl, budget_s=20.0, max_queries=None):
     return done / dt, done, dt, cores
 
 
+def run_alternating(torch, ds, steps):
+    """Plain launches back to back, each step on the next of `ds` (copies of one batch in
+    separate memory) in turn, so no step finds the previous step's stores in cache.
+    Returns seconds per step."""
+    fns = [[d.compress, d.index, d.select, d.attend] for d in ds]
+    for i in range(3 * len(ds)):
+        for f in fns[i % len(ds)]:
+            f()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for f in fns[i % len(ds)]:
+            f()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def config_leg(torch, name, steps, warmup, profile, cold=False, log=None):
+    """One layer configuration: eager steps with stage events, then the faster of graph
+    replays and plain back-to-back launches; with `cold`, a second copy of the batch's stores
+    and plain launches alternating between the two copies."""
+    import workloads as W
+    from sparse_attention_score_amd.step import DeviceBatch
+    t0 = time.perf_counter()
+    wl = W.make(name)
+    d = DeviceBatch(wl)
+    torch.cuda.synchronize()
+    if log:
+        log(f"{name} inputs ready in {time.perf_counter() - t0:.1f}s")
+    eager_s, ms = run_batch(torch, d, steps, warmup, 0.0 if profile else 0.5)
+    best_s, timing = (eager_s, "eager launches with events around every stage") if profile else \
+        best_step(torch, d, steps)
+    ib, sb = indexer_bytes(wl), step_bytes(wl)
+    out = {"workload": name, "queries": int(wl.T), "ms_per_step": best_s * 1e3,
+           "queries_per_s": wl.T / best_s, "tokens_per_s": wl.T / best_s, "timing": timing,
+           "eager_ms_per_step": eager_s * 1e3, "stage_ms": ms,
+           "algorithmic_bytes_per_step": sb, "hbm_frac": sb / best_s / HBM_PEAK,
+           "indexer": {"bound": "hbm", "achieved": ib / (ms["indexer"] * 1e-3) / 1e9,
+                       "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                       "frac": ib / (ms["indexer"] * 1e-3) / HBM_PEAK,
+                       "algorithmic_bytes_per_launch": ib, "avg_launch_ms": ms["indexer"],
+                       "traffic": stored_traffic(name, CONFIG_TRAFFIC_FILES[name]) if name in CONFIG_TRAFFIC_FILES
+                       else None}}
+    if cold and not profile:
+        d2 = DeviceBatch(wl)
+        torch.cuda.synchronize()
+        cold_s = run_alternating(torch, [d, d2], steps)
+        out["cold"] = {"ms_per_step": cold_s * 1e3, "queries_per_s": wl.T / cold_s,
+                       "hbm_frac": sb / cold_s / HBM_PEAK,
+                       "timing": "plain launches back to back, alternating between two copies of the stores"}
+        out["warm"] = {"ms_per_step": best_s * 1e3, "queries_per_s": wl.T / best_s,
+                       "hbm_frac": sb / best_s / HBM_PEAK, "timing": timing}
+        del d2
+    del d, wl
+    torch.cuda.empty_cache()
+    return out
+
+
+def compress_leg(torch, steps, profile, B=64, n_raw=32768):
+    """The compressor alone (sparse_attn_compress, ratio 2) over B x n_raw raw latents and
+    gate logits into B x n_raw/2 compressed rows, one launch over all groups; HIP events on
+    the launch stream. Algorithmic bytes per group: two raw rows and two gate rows in,
+    one row out (bf16)."""
+    import sparse_attention_score_amd as S
+    import workloads as W
+    from sparse_attention_score_amd.step import to_device_bf16
+    X, Z, beta = W.make_compress_input(B, n_raw)
+    Xd, Zd = to_device_bf16(X), to_device_bf16(Z)
+    del X, Z
+    bd = torch.from_numpy(beta).cuda()
+    G = B * (n_raw // 2)
+    out = torch.empty((G, 512), dtype=torch.bfloat16, device="cuda")
+    plan = S.Plan(ratio=2, key_dtype="bf16", max_queries=1, max_compressed=n_raw // 2)
+    fn = lambda: S.sparse_attn_compress(plan, Xd, 1024, Zd, 1024, bd, out, 512, G)  # noqa: E731
+    warm_up(torch, [fn], 3, 0.0 if profile else 0.3)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = float(G * (2 * 2 * 512 * 2 + 512 * 2))
+    del Xd, Zd, out
+    torch.cuda.empty_cache()
+    return {"what": f"sparse_attn_compress over {B} x {n_raw} raw latents ({G} groups, one launch)",
+            "groups": G, "ms_per_launch": ms, "bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9,
+            "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / HBM_PEAK,
+            "algorithmic_bytes_per_launch": nbytes,
+            "traffic": stored_traffic(f"compress raw {B} x {n_raw}", COMPRESS_TRAFFIC_FILE, COMPRESS_SOURCES)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -407,10 +511,29 @@ def main():
     ap.add_argument("--no-fp8kv", action="store_true", help="skip the e4m3 and MXFP4 latent-row batches")
     ap.add_argument("--ragged-workload", default="ragged-2x1024+64+16x6-ctx128k-fp8")
     ap.add_argument("--no-ragged", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other layer configurations")
+    ap.add_argument("--no-compress", action="store_true")
+    ap.add_argument("--only", default=None, help="comma-separated legs to run besides the headline batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--profile", action="store_true", help="timed steps only (for rocprofv3)")
     args = ap.parse_args()
+    LEGS = ("paged", "rescore", "multiquery", "mxfp4", "fp8kv", "ragged", "prefill", "c1", "c2", "c5", "r1m",
+            "compress", "cpu")
+    if args.only is not None:
+        keep = set(x for x in args.only.split(",") if x)
+        unknown = keep - set(LEGS)
+        if unknown:
+            ap.error(f"unknown legs {sorted(unknown)}; known: {', '.join(LEGS)}")
+        for leg in LEGS:
+            if leg not in keep:
+                setattr(args, {"multiquery": "no_multiquery", "cpu": "no_cpu_baseline", "c1": "skip_c1",
+                               "c2": "skip_c2", "c5": "skip_c5", "r1m": "skip_r1m"}.get(leg, f"no_{leg}"), True)
+    for leg in ("c1", "c2", "c5", "r1m"):
+        if args.no_configs:
+            setattr(args, f"skip_{leg}", True)
+        elif not hasattr(args, f"skip_{leg}"):
+            setattr(args, f"skip_{leg}", False)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
@@ -616,14 +739,15 @@ def main():
         del dr, wr
         torch.cuda.empty_cache()
 
-    if not args.no_prefill and not args.profile:
+    if not args.no_prefill:
         t0 = time.perf_counter()
         wp = W.make(args.prefill_workload)
         dp = DeviceBatch(wp)
         torch.cuda.synchronize()
         log(f"prefill inputs ready in {time.perf_counter() - t0:.1f}s")
-        sp_eager, sms = run_batch(torch, dp, max(3, args.steps // 2), args.warmup)
-        sp, p_timing = best_step(torch, dp, max(3, args.steps // 2))
+        sp_eager, sms = run_batch(torch, dp, max(3, args.steps // 2), args.warmup, 0.0 if args.profile else 0.5)
+        sp, p_timing = (sp_eager, "eager launches with events around every stage") if args.profile else \
+            best_step(torch, dp, max(3, args.steps // 2))
         fi, fa = step_flops(wp)
         result["prefill"] = {
             "workload": args.prefill_workload, "ms_per_chunk": sp * 1e3, "tokens_per_s": wp.T / sp,
@@ -636,6 +760,21 @@ def main():
         log(f"prefill: {sp * 1e3:.3f} ms/chunk, stages {sms}")
         del dp, wp
         torch.cuda.empty_cache()
+
+    for key, name, cold, skip in (("c1_latency", "decode-b4-ctx2k", False, args.skip_c1),
+                                  ("c2", "decode-b64-ctx32k", True, args.skip_c2),
+                                  ("c5", "decode-b8-ctx1m-fp8", False, args.skip_c5),
+                                  ("long_r1", "decode-b2-ctx1m-r1-fp8", False, args.skip_r1m)):
+        if skip:
+            continue
+        result[key] = config_leg(torch, name, args.steps, args.warmup, args.profile, cold=cold, log=log)
+        log(f"{key}: {result[key]['ms_per_step']:.4f} ms/step, stages {result[key]['stage_ms']}"
+            + (f", cold {result[key]['cold']['ms_per_step']:.4f} ms" if "cold" in result[key] else ""))
+
+    if not args.no_compress:
+        result["compress"] = compress_leg(torch, args.steps, args.profile)
+        log(f"compress: {result['compress']['ms_per_launch']:.4f} ms/launch, "
+            f"{result['compress']['achieved']:.0f} GB/s")
 
     if not args.no_cpu_baseline and not args.profile:
         qps, done, dt, cores = cpu_baseline(wl, args.cpu_budget)
