@@ -68,7 +68,7 @@ size_t cand_bytes(int64_t T) { return (size_t)T * 2048 * sizeof(int32_t); }
 // Part lists of the two-level candidate stage (queries longer than 8192 blocks).
 size_t part_bytes(int64_t T, int64_t max_visible) {
   const int parts = sa::select_parts(max_visible).parts;
-  return parts > 1 ? (size_t)T * parts * 2048 * sizeof(int32_t) : 0;
+  return parts > 1 ? (size_t)T * parts * 2048 * (sizeof(int32_t) + sizeof(uint32_t)) : 0;   // ids, keys
 }
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
@@ -537,6 +537,7 @@ sa_status select_topk_cand(const sa_plan* plan, const sa_queries* q, const int32
   a.cand = const_cast<int32_t*>(cand);   // read only in this mode
   a.topk = topk;
   a.part_ids = nullptr;
+  a.part_keys = nullptr;
   a.parts = 1;
   a.part_blocks = sa::kPartBlocks;
   log_call("select_topk_cand: T=%lld", (long long)q->T);
@@ -591,6 +592,7 @@ sa_status select_topk(const sa_plan* plan, const sa_queries* q, const float* sco
   log_call("select_topk: T=%lld max_visible=%lld, candidate stage in %d part(s) of %d blocks%s", (long long)q->T,
            (long long)q->max_visible, ps.parts, ps.part_blocks, cand == workspace ? ", candidates in the workspace" : "");
   a.part_ids = a.parts > 1 ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + cand_bytes(q->T)) : nullptr;
+  a.part_keys = a.parts > 1 ? reinterpret_cast<uint32_t*>(a.part_ids + (size_t)q->T * a.parts * 2048) : nullptr;
   return hip_status(sa::launch_select(a, (hipStream_t)stream), "select_topk launch");
 }
 

@@ -68,6 +68,7 @@ struct SelectArgs {
   int32_t* cand;            // [T][2048]
   int32_t* topk;            // [T][512]
   int32_t* part_ids;        // [T][parts][2048] workspace, used when parts > 1
+  uint32_t* part_keys;      // [T][parts][2048] order-preserving block maxima of part_ids
   int parts;                // select_parts(m.max_visible)
   int part_blocks;          // blocks per part (kPartBlocks or 2 * kPartBlocks)
 };

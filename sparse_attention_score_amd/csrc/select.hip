@@ -46,6 +46,7 @@ struct SelShared {
   int32_t cid[kMaxSel][kColl];
   int32_t stage[kCandBlocks + kTopK] __attribute__((aligned(16)));   // kept ids before they go out
 };
+static_assert(kBins >= kCandBlocks, "the histogram doubles as key staging once the threshold is known");
 
 __device__ __forceinline__ int64_t visible_n(const QueryMeta& m, int t) {
   int seq = m.seq_id[t], pos = m.pos[t];
@@ -246,7 +247,7 @@ __device__ __forceinline__ uint32_t kth_key(const uint32_t (&key)[EPT], const Id
 // thread's.
 template <int NT, int EPT, class Ids>
 __device__ __forceinline__ void select_and_emit(const uint32_t (&key)[EPT], const Ids& I, int k, SelShared& sh,
-                                int32_t* out) {
+                                int32_t* out, uint32_t* kout) {
   int take_eq;
   const uint32_t v = kth_key<NT, EPT, Ids>(key, I, k, sh, take_eq);
   int gt = 0, eq = 0;
@@ -270,7 +271,10 @@ __device__ __forceinline__ void select_and_emit(const uint32_t (&key)[EPT], cons
       keep = seen_eq < my_eq;
       ++seen_eq;
     }
-    if (keep && off < k) out[off++] = I.id(e);
+    if (keep && off < k) {
+      if (kout) kout[off] = key[e];
+      out[off++] = I.id(e);
+    }
   }
 }
 
@@ -284,7 +288,7 @@ __device__ __forceinline__ void select_and_emit(const uint32_t (&key)[EPT], cons
 // path above.
 template <int NT, int EPT, int NS, class Ids>
 __device__ __forceinline__ void multi_select(const uint32_t (&key)[EPT], const Ids& I, const int (&k)[NS],
-                             int32_t* const (&out)[NS], SelShared& sh) {
+                             int32_t* const (&out)[NS], SelShared& sh, uint32_t* kout0 = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
@@ -315,7 +319,7 @@ __device__ __forceinline__ void multi_select(const uint32_t (&key)[EPT], const I
   }
   if (!fast) {
 #pragma unroll
-    for (int q = 0; q < NS; ++q) select_and_emit<NT, EPT, Ids>(key, I, k[q], sh, out[q]);
+    for (int q = 0; q < NS; ++q) select_and_emit<NT, EPT, Ids>(key, I, k[q], sh, out[q], q == 0 ? kout0 : nullptr);
     return;
   }
   // collect the threshold bins' elements
@@ -417,7 +421,10 @@ __device__ __forceinline__ void multi_select(const uint32_t (&key)[EPT], const I
 #pragma unroll
     for (int q = 0; q < NS; ++q)
       if ((key[e] > v[q] || (key[e] == v[q] && I.id(e) <= vi[q])) && off[q] < k[q])
+      {
+        if (q == 0 && kout0) sh.hist[off[q]] = key[e];   // the histogram is no longer read
         sh.stage[sbase[q] + off[q]++] = I.id(e);
+      }
   }
   __syncthreads();
   // exactly k[q] ids were kept (the k-th element exists); k and the outputs are 16-byte aligned
@@ -425,6 +432,9 @@ __device__ __forceinline__ void multi_select(const uint32_t (&key)[EPT], const I
   for (int q = 0; q < NS; ++q)
     for (int i = 4 * tid; i < k[q]; i += 4 * NT)
       *reinterpret_cast<int4*>(out[q] + i) = *reinterpret_cast<const int4*>(&sh.stage[sbase[q] + i]);
+  if (kout0)
+    for (int i = 4 * tid; i < k[0]; i += 4 * NT)
+      *reinterpret_cast<uint4*>(kout0 + i) = *reinterpret_cast<const uint4*>(&sh.hist[i]);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -537,8 +547,9 @@ __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
 }
 
 // Two-level S2, first level: work-group (t, p) keeps the best 2048 of blocks
-// [p*kPartBlocks, (p+1)*kPartBlocks) and writes their ids ascending to its part list
-// (-1 after the last).
+// [p * size, (p + 1) * size) and writes their ids ascending to its part list (-1 after the
+// last), with each block's key (its order-preserving block max) beside it, so the second
+// level reads its elements contiguously instead of gathering block maxima.
 template <int NT, int EPT>
 __global__ __launch_bounds__(NT) void select_part_kernel(SelectArgs a) {
   __shared__ SelShared sh;
@@ -548,9 +559,15 @@ __global__ __launch_bounds__(NT) void select_part_kernel(SelectArgs a) {
   const int nb = (int)((n + kBlock - 1) / kBlock);
   const int b0 = p * (NT * EPT);
   const int b1 = min(nb, b0 + NT * EPT);
-  int32_t* out = a.part_ids + ((int64_t)t * a.parts + p) * kCandBlocks;
+  const int64_t li = ((int64_t)t * a.parts + p) * kCandBlocks;
+  int32_t* out = a.part_ids + li;
+  uint32_t* kout = a.part_keys + li;
   if (b1 - b0 <= kCandBlocks) {
-    for (int i = threadIdx.x; i < kCandBlocks; i += NT) out[i] = b0 + i < b1 ? b0 + i : -1;
+    for (int i = threadIdx.x; i < kCandBlocks; i += NT) {
+      const bool v = b0 + i < b1;
+      out[i] = v ? b0 + i : -1;
+      kout[i] = v ? order_key(block_value(a, t, n, b0 + i)) : 0u;
+    }
     return;
   }
   uint32_t key[EPT];
@@ -558,21 +575,26 @@ __global__ __launch_bounds__(NT) void select_part_kernel(SelectArgs a) {
   load_block_keys<EPT>(a, t, n, I, key);
   const int ks[1] = {kCandBlocks};
   int32_t* const outs[1] = {out};
-  multi_select<NT, EPT, 1>(key, I, ks, outs, sh);
+  multi_select<NT, EPT, 1>(key, I, ks, outs, sh, kout);
 }
 
-// Two-level S2, second level: the union of a query's part lists (ids ascending part after
-// part) holds its best 2048 blocks; select them and the 512 core blocks, then S3.
+// Two-level S2, second level, in two work-groups per query: the union of the query's part
+// lists (ids ascending part after part, keys beside them) holds its best 2048 blocks.
+// Role 0 selects them into cand; role 1 selects the best 512 (the core blocks) and then
+// the top-512 positions inside them (S3), independently of role 0.
 template <int NT, int EPT>
 __global__ __launch_bounds__(NT) void select_merge_kernel(SelectArgs a) {
   __shared__ SelShared sh;
   __shared__ __attribute__((aligned(16))) int32_t core[kTopK];
-  const int t = blockIdx.x;
+  const int role = blockIdx.x, t = blockIdx.y;
   const int64_t n = visible_n(a.m, t);
   const int nb = (int)((n + kBlock - 1) / kBlock);
   int32_t* cand = a.cand + (int64_t)t * kCandBlocks;
   if (nb <= kCandBlocks) {
-    for (int i = threadIdx.x; i < kCandBlocks; i += NT) cand[i] = i < nb ? i : -1;
+    if (role == 0) {
+      for (int i = threadIdx.x; i < kCandBlocks; i += NT) cand[i] = i < nb ? i : -1;
+      return;
+    }
     if (nb <= kTopK) {
       for (int i = threadIdx.x; i < kTopK; i += NT) core[i] = i < nb ? i : -1;
     } else {
@@ -586,35 +608,38 @@ __global__ __launch_bounds__(NT) void select_merge_kernel(SelectArgs a) {
       multi_select<NT, E, 1>(key, I, ks, outs, sh);
     }
   } else {
-    const int32_t* lists = a.part_ids + (int64_t)t * a.parts * kCandBlocks;
+    const int64_t l0 = (int64_t)t * a.parts * kCandBlocks;
+    const int32_t* lists = a.part_ids + l0;
+    const uint32_t* lkeys = a.part_keys + l0;
     const int total = a.parts * kCandBlocks;
     uint32_t key[EPT];
     ListIds<EPT> I;
-    // a thread's EPT entries are contiguous and 16-byte aligned (total is a multiple of 16):
-    // all id loads first, then all block-value loads, so each set is one round trip
+    // a thread's EPT entries are contiguous and 16-byte aligned (total is a multiple of 16)
     static_assert(EPT % 4 == 0, "whole 16-byte loads");
 #pragma unroll
     for (int q = 0; q < EPT / 4; ++q) {
       const int i = (int)threadIdx.x * EPT + 4 * q;
-      const int4 v = i < total ? *reinterpret_cast<const int4*>(lists + i) : int4{-1, -1, -1, -1};
+      const bool in = i < total;
+      const int4 v = in ? *reinterpret_cast<const int4*>(lists + i) : int4{-1, -1, -1, -1};
+      const uint4 kv = in ? *reinterpret_cast<const uint4*>(lkeys + i) : uint4{0u, 0u, 0u, 0u};
       I.ids[4 * q] = v.x;
       I.ids[4 * q + 1] = v.y;
       I.ids[4 * q + 2] = v.z;
       I.ids[4 * q + 3] = v.w;
+      key[4 * q] = kv.x;
+      key[4 * q + 1] = kv.y;
+      key[4 * q + 2] = kv.z;
+      key[4 * q + 3] = kv.w;
     }
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) I.valid[e] = I.ids[e] >= 0;
-    if (a.block_max) {
-      const float* bm = a.block_max + (int64_t)t * a.ld_block_max;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) key[e] = I.valid[e] ? order_key(bm[I.ids[e]]) : 0u;
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) key[e] = I.valid[e] ? order_key(block_value(a, t, n, I.ids[e])) : 0u;
+    for (int e = 0; e < EPT; ++e) {
+      I.valid[e] = I.ids[e] >= 0;
+      key[e] = I.valid[e] ? key[e] : 0u;
     }
-    const int ks[2] = {kCandBlocks, kTopK};
-    int32_t* const outs[2] = {cand, core};
-    multi_select<NT, EPT, 2>(key, I, ks, outs, sh);
+    const int ks[1] = {role == 0 ? kCandBlocks : kTopK};
+    int32_t* const outs[1] = {role == 0 ? cand : core};
+    multi_select<NT, EPT, 1>(key, I, ks, outs, sh);
+    if (role == 0) return;
   }
   __syncthreads();
   select_core<NT>(a, t, n, core, sh);
@@ -733,13 +758,14 @@ hipError_t launch_select_nt(const SelectArgs& a, hipStream_t stream) {
   // the merge reads the part lists: enqueue it only if the part launch was accepted
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const dim3 mgrid(2u, (unsigned)a.m.T);   // role, query
   const int per_thread = a.parts * kCandBlocks / NT;
   if (per_thread <= 16 * 256 / NT)
-    hipLaunchKernelGGL((select_merge_kernel<NT, 16 * 256 / NT>), grid, dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((select_merge_kernel<NT, 16 * 256 / NT>), mgrid, dim3(NT), 0, stream, a);
   else if (per_thread <= 32 * 256 / NT)
-    hipLaunchKernelGGL((select_merge_kernel<NT, 32 * 256 / NT>), grid, dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((select_merge_kernel<NT, 32 * 256 / NT>), mgrid, dim3(NT), 0, stream, a);
   else
-    hipLaunchKernelGGL((select_merge_kernel<NT, 64 * 256 / NT>), grid, dim3(NT), 0, stream, a);
+    hipLaunchKernelGGL((select_merge_kernel<NT, 64 * 256 / NT>), mgrid, dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -104,7 +104,7 @@ def test_plan_accepts_long_rows(maxc, parts):
     size = 8192 if nb <= 8 * 8192 else 16384
     expect = 1 if nb <= 8192 else -(-nb // size)
     assert expect == parts
-    extra = mq * parts * 2048 * 4 if parts > 1 else 0
+    extra = mq * parts * 2048 * 8 if parts > 1 else 0   # ids and keys
     a256 = lambda b: (b + 255) // 256 * 256
     select = mq * 2048 * 4 + extra
     counters = a256(select)
