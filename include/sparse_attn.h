@@ -207,7 +207,7 @@ typedef struct sa_cache {
  * receives the device workspace size that select_topk and sparse_attn_fwd
  * need for T = max_queries; concurrent calls need separate workspaces.
  * A workspace holds a select area (scratch between calls) and an attention
- * area (used by batches of at most 32 queries) whose per-query counters must
+ * area (used by batches of at most 32 queries) whose counters must
  * be zero before a call: zero them once with sparse_attn_workspace_init after
  * allocating; every sparse_attn_fwd call leaves them zero again. */
 sa_status sparse_attn_plan(const sa_params* params, sa_plan** plan, size_t* workspace_bytes);
@@ -299,11 +299,13 @@ sa_status select_topk_cand(const sa_plan* plan, const sa_queries* queries, const
  *          scaled logits (max + log of the normaliser)
  *   workspace  device or NULL. With T <= 32 and a workspace of the plan's
  *          size (counters zeroed, see sparse_attn_workspace_init), each query's
- *          key list is split over 4 work-groups whose partial softmax results
- *          are combined at the end (the probabilities are rounded to bf16
- *          against each part's own reference, so the output may differ from
- *          the unsplit one by that rounding; it is the same for every call);
- *          otherwise one work-group takes each query. */
+ *          key list is split over 4 work-groups per head set (two head sets for
+ *          T <= 16) whose
+ *          partial softmax results are combined at the end (the probabilities are
+ *          rounded to bf16 against each part's own reference, so the output may
+ *          differ from the unsplit one by that rounding; it is the same for every
+ *          call); otherwise the query's heads are taken by one work-group, or by
+ *          two (33 to 128 queries). */
 sa_status sparse_attn_fwd(const sa_plan* plan, const sa_queries* queries, const sa_cache* cache,
                           const void* q, const int32_t* topk, void* out, float* lse,
                           void* workspace, size_t workspace_bytes, void* stream);

@@ -85,7 +85,7 @@ WsLayout ws_layout(const sa_params& p) {
   w.select_bytes = cand_bytes(p.max_queries) + part_bytes(p.max_queries, p.max_compressed);
   w.units = sa::attn_max_units(p.max_queries);
   w.counters_off = align256(w.select_bytes);
-  w.ml_off = w.counters_off + align256((size_t)p.max_queries * sizeof(uint32_t));
+  w.ml_off = w.counters_off + align256((size_t)p.max_queries * 2 * sizeof(uint32_t));   // per (query, head set)
   w.o_off = w.ml_off + align256((size_t)w.units * 64 * 2 * sizeof(float));
   w.total = w.units > 0 ? w.o_off + (size_t)w.units * 64 * 512 * sizeof(float) : w.select_bytes;
   return w;
@@ -629,7 +629,7 @@ sa_status sparse_attn_fwd_noalloc(const sa_plan* plan, const sa_queries* q, cons
   if ((st = attn_args(plan, q, c, qv, topk, out, lse, a)) != SA_OK) return st;
   a.splits = sa::attn_splits(q->T);
   if (a.splits > 1) {
-    SA_REQUIRE(q->T * a.splits <= sa::kScratchUnits, SA_EUNSUPPORTED,
+    SA_REQUIRE(q->T * a.splits <= sa::kScratchUnits && q->T <= sa::kScratchQueries, SA_EUNSUPPORTED,
                "sparse_attn_fwd_noalloc: %lld queries in %d key splits exceed the fixed scratch "
                "(%lld partial slots)", (long long)q->T, a.splits, (long long)sa::kScratchUnits);
     sa::AttnScratch s;
@@ -639,7 +639,7 @@ sa_status sparse_attn_fwd_noalloc(const sa_plan* plan, const sa_queries* q, cons
     a.part_ml = s.part_ml;
     a.part_o = s.part_o;
     // the counters must start at zero: cleared by a kernel on the caller's stream
-    e = sa::launch_zero_u32(s.counters, q->T, (hipStream_t)stream);
+    e = sa::launch_zero_u32(s.counters, 2 * q->T, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, "sparse_attn_fwd_noalloc counter reset launch");
   }
   log_call("sparse_attn_fwd_noalloc: T=%lld kv=%s, key list split over %d work-group(s)%s", (long long)q->T,
@@ -658,7 +658,7 @@ sa_status sparse_attn_workspace_init(const sa_plan* plan, void* workspace, size_
   const WsLayout wl = ws_layout(plan->p);
   if (wl.units == 0) return ok();
   uint32_t* counters = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + wl.counters_off);
-  return hip_status(sa::launch_zero_u32(counters, plan->p.max_queries, (hipStream_t)stream),
+  return hip_status(sa::launch_zero_u32(counters, 2 * plan->p.max_queries, (hipStream_t)stream),
                     "sparse_attn_workspace_init launch");
 }
 

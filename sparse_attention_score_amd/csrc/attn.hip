@@ -154,7 +154,8 @@ template <int HS, int KVM>
 __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   constexpr bool KV8 = KVM != 0, FP4L = KVM == 2;
   // HS = 2: the query's heads are split over two work-groups (32 each) that gather the same
-  // rows (normally on one XCD, so the second reads them from L2); no key splits then
+  // rows (normally on one XCD, so the second reads them from L2); with key splits as well,
+  // each (query, split) unit is two such work-groups, each owning its half of the heads
   static_assert(HS == 1 || HS == 2, "one or two head sets");
   constexpr int NJ = 2 / HS;          // head groups per score wave
   constexpr int NV = kHG / HS;        // head groups per value wave
@@ -162,9 +163,9 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) AttnShared sh;
   // work-group -> query: ids are dealt round-robin over the 8 XCDs, so XCD x gets the
   // contiguous query range x*Q8 .. x*Q8+Q8-1 (neighbouring queries share window rows).
-  // With key splits the unit is (query, split), split fastest, so the splits of a query
-  // normally share an XCD.
-  const int T = (int)a.m.T, S = HS == 1 ? a.splits : 1, U = T * S * HS;
+  // With key splits the unit is (query, split), split fastest (after the head set), so the
+  // work-groups of a query normally share an XCD.
+  const int T = (int)a.m.T, S = a.splits, U = T * S * HS;
   const int u8 = (U + 7) >> 3;
   const int uw = (blockIdx.x & 7) * u8 + (blockIdx.x >> 3);
   if ((int)(blockIdx.x >> 3) >= u8 || uw >= U) return;
@@ -676,20 +677,20 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       }
       return;
     }
-    // partial O of this split, in the lanes' own order (every instruction: 1 KB of lines)
-    if constexpr (HS == 1) {
+    // partial O of this split's head groups, in the lanes' own order (every instruction:
+    // 1 KB of lines); a unit holds all 64 heads, each head set writes its own groups
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int h = 0; h < kHG; ++h)
+      for (int h = 0; h < NV; ++h)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const u32x4 v = __builtin_bit_cast(u32x4, f32x4{O[hh][h][0][i], O[hh][h][1][i], O[hh][h][2][i], O[hh][h][3][i]});
-            __builtin_amdgcn_raw_buffer_store_b128(v, part_rsrc(a, U), part_off(u, vw, hh, h, i) + lane * 16, 0, kCoherent);
-          }
-    }
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 v = __builtin_bit_cast(u32x4, f32x4{O[hh][h][0][i], O[hh][h][1][i], O[hh][h][2][i], O[hh][h][3][i]});
+          __builtin_amdgcn_raw_buffer_store_b128(v, part_rsrc(a, T * S), part_off(u, vw, hh, vgrp(h), i) + lane * 16, 0,
+                                                 kCoherent);
+        }
   }
-  if constexpr (HS == 1) {
+  {
 
   // ---- key splits: the last work-group of the query to finish combines the partials ----
   // The softmax of the whole key list from the splits' partial ones: with M the largest
@@ -699,17 +700,18 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   // raised only after every store of the work-group has completed.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's partial is device-visible
   __syncthreads();
-  if (tid == 0) sh.last = atomicAdd(&a.counters[t], 1u) == (uint32_t)(S - 1);
+  // one counter per (query, head set)
+  if (tid == 0) sh.last = atomicAdd(&a.counters[t * HS + hs], 1u) == (uint32_t)(S - 1);
   __syncthreads();
   if (!sh.last) return;
-  if (tid == 0) a.counters[t] = 0u;   // every split of this call has counted: ready for the next
-  // every wave combines one slice: dims 128cv + 64chh .. +63 of all heads
+  if (tid == 0) a.counters[t * HS + hs] = 0u;   // every split of this call has counted: ready for the next
+  // every wave combines one slice: dims 128cv + 64chh .. +63 of the head set's heads
   const int cv = wave & 3, chh = wave >> 2;
   const int u0 = t * S;
-  float wgt[kHG][kMaxSplits], Lsum[kHG], Mx[kHG];
+  float wgt[NV][kMaxSplits], Lsum[NV], Mx[NV];
 #pragma unroll
-  for (int h = 0; h < kHG; ++h) {
-    const int head = 16 * h + c;
+  for (int h = 0; h < NV; ++h) {
+    const int head = 16 * vgrp(h) + c;
     float mref[kMaxSplits], lsp[kMaxSplits];
 #pragma unroll
     for (int s2 = 0; s2 < kMaxSplits; ++s2) {
@@ -730,26 +732,26 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
     Mx[h] = M;
   }
   // sum over the splits in split order (the same bits whichever work-group combines)
-  f32x4 acc[kHG][4];
+  f32x4 acc[NV][4];
 #pragma unroll
   for (int s2 = 0; s2 < kMaxSplits; ++s2) {
     if (s2 >= S) break;
     asm volatile("" ::: "memory");   // one split's loads in flight at a time (registers)
-    f32x4 v[kHG][4];
+    f32x4 v[NV][4];
 #pragma unroll
-    for (int h = 0; h < kHG; ++h)
+    for (int h = 0; h < NV; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         v[h][i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                part_rsrc(a, U), part_off(u0 + s2, cv, chh, h, i) + lane * 16, 0, kCoherent));
+            part_rsrc(a, T * S), part_off(u0 + s2, cv, chh, vgrp(h), i) + lane * 16, 0, kCoherent));
 #pragma unroll
-    for (int h = 0; h < kHG; ++h)
+    for (int h = 0; h < NV; ++h)
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[h][i] = s2 == 0 ? wgt[h][0] * v[h][i] : acc[h][i] + wgt[h][s2] * v[h][i];
   }
 #pragma unroll
-  for (int h = 0; h < kHG; ++h) {
-    const int head = 16 * h + c;
+  for (int h = 0; h < NV; ++h) {
+    const int head = 16 * vgrp(h) + c;
     const float inv = 1.0f / Lsum[h];
     uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + ((int64_t)t * kHeads + head) * kDim + 128 * cv + 64 * chh;
 #pragma unroll
@@ -761,7 +763,7 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
     }
     if (a.lse && wave == 0 && g == 0) a.lse[(int64_t)t * kHeads + head] = (Mx[h] + __log2f(Lsum[h])) * kLn2;
   }
-  }   // HS == 1
+  }
 }
 
 __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
@@ -771,9 +773,11 @@ __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
 
 }  // namespace
 
-// Batches of 33 to 128 queries (fewer work-groups than CUs) split each query's heads over
-// two work-groups; smaller ones split its keys instead (splits > 1), larger ones neither.
-int attn_head_sets(int64_t T, int splits) { return splits == 1 && T > 32 && T <= 128 ? 2 : 1; }
+// Work-groups per query for batches with fewer queries than CUs: up to 16 queries split each
+// query's heads over two work-groups and its keys over four (8 per query), 17 to 32 split
+// the keys over four, 33 to 128 only the heads over two (key splits as well measured no
+// faster for 64 queries: 19.8 against 19.3 us); larger batches take one work-group per query.
+int attn_head_sets(int64_t T, int splits) { return (T <= 16 && splits > 1) || (T > 32 && T <= 128) ? 2 : 1; }
 
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   const int hs = attn_head_sets(a.m.T, a.splits);
@@ -795,9 +799,9 @@ hipError_t launch_attn(const AttnArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Small batches (at most 32 queries, an eighth of the CUs): a query's keys are spread over
-// kMaxSplits work-groups (the last to finish reads the others' partials). With more
-// queries the partial traffic costs about what the shorter key lists save.
+// Small batches (at most 32 queries): a query's keys are spread over kMaxSplits work-groups
+// (the last to finish for each head set reads the others' partials). With more queries the
+// partial traffic costs about what the shorter key lists save.
 int attn_splits(int64_t T) { return T <= 32 ? kMaxSplits : 1; }
 
 int64_t attn_max_units(int64_t max_queries) {
@@ -819,15 +823,15 @@ hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t stream) {
 }  // namespace sa
 
 // Key-split state for callers that cannot allocate (sparse_attn_fwd_noalloc): one fixed
-// array per GPU instead of a workspace. Layout: [kScratchQueries u32 counters, padded to
-// 256 B][kScratchUnits x 64 x 2 fp32 partial references and normalisers][kScratchUnits
+// array per GPU instead of a workspace. Layout: [kScratchCounters u32 counters, padded to
+// 512 B][kScratchUnits x 64 x 2 fp32 partial references and normalisers][kScratchUnits
 // partial outputs of 128 KiB]. Host code reaches it only through the address
 // hipGetSymbolAddress returns for the current device (attn_scratch below).
 namespace {
-constexpr size_t kScratchMlOff = 256;
+constexpr size_t kScratchMlOff = 512;
 constexpr size_t kScratchOOff = kScratchMlOff + (size_t)sa::kScratchUnits * 64 * 2 * sizeof(float);
 constexpr size_t kScratchBytes = kScratchOOff + (size_t)sa::kScratchUnits * 64 * 512 * sizeof(float);
-static_assert(sa::kScratchQueries * sizeof(uint32_t) <= kScratchMlOff, "counters fit before the partials");
+static_assert(sa::kScratchCounters * sizeof(uint32_t) <= kScratchMlOff, "counters fit before the partials");
 static_assert(kScratchOOff % 256 == 0, "partial outputs 256-byte aligned");
 constexpr int kScratchDevices = 64;
 }  // namespace

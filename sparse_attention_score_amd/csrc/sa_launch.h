@@ -115,19 +115,22 @@ struct AttnArgs {
 };
 hipError_t launch_attn(const AttnArgs& a, hipStream_t stream);
 // Key splits used for T queries, and the partial slots (T * splits) the largest of them
-// needs for any T up to max_queries.
+// needs for any T up to max_queries. Split batches keep one counter per (query, head set):
+// 2 * T at most.
 int attn_splits(int64_t T);
 int64_t attn_max_units(int64_t max_queries);
 // Zero n 32-bit words (a kernel, so the call may be captured in a graph).
 hipError_t launch_zero_u32(uint32_t* p, int64_t n, hipStream_t stream);
 // Key-split state in a fixed per-GPU array (for callers that cannot allocate): counters,
-// partial references / normalisers and partial outputs for up to kScratchQueries queries of
-// kMaxAttnSplits work-groups each, on the current device.
+// partial references / normalisers and partial outputs of every batch that splits its keys
+// (at most kScratchQueries queries, at most kScratchUnits (query, split) units), on the
+// current device.
 constexpr int kScratchQueries = 32;
 constexpr int kMaxAttnSplits = 4;
-constexpr int64_t kScratchUnits = (int64_t)kScratchQueries * kMaxAttnSplits;
+constexpr int64_t kScratchUnits = 128;
+constexpr int kScratchCounters = 2 * kScratchQueries;   // one per (query, head set)
 struct AttnScratch {
-  uint32_t* counters;       // [kScratchQueries]
+  uint32_t* counters;       // [kScratchCounters]
   float* part_ml;           // [kScratchUnits][64][2]
   float* part_o;            // [kScratchUnits][64][512]
   size_t bytes;

@@ -30,6 +30,7 @@ constexpr int kBins = 2048;
 
 constexpr int kMaxSel = 2;      // selections sharing one histogram (candidate and core blocks)
 constexpr int kColl = 256;      // most elements of a threshold bin the fast path collects
+constexpr int kTwoRoleQueries = 256;   // batches up to this size run two work-groups per query
 
 struct SelShared {
   uint32_t hist[kBins];
@@ -514,32 +515,39 @@ __device__ __forceinline__ void load_block_keys(const SelectArgs& a, int t, int6
   }
 }
 
-// S2 + S3 in one work-group of NT threads per query, for at most NT * EPT blocks.
-template <int NT, int EPT>
+// S2 + S3 for at most NT * EPT blocks per query. ROLES = 1: one work-group of NT threads
+// per query selects the candidate and core blocks together, then the top-512 positions.
+// ROLES = 2 (batches of few queries, where the latency of one query is the kernel time):
+// two work-groups per query work independently, role 0 selecting the 2048 candidate
+// blocks and role 1 the 512 core blocks and then the top-512 positions.
+template <int NT, int EPT, int ROLES>
 __global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
   __shared__ SelShared sh;
   __shared__ __attribute__((aligned(16))) int32_t core[kTopK];
-  const int t = blockIdx.x;
+  const int role = ROLES == 1 ? -1 : (int)blockIdx.x;
+  const int t = ROLES == 1 ? blockIdx.x : blockIdx.y;
   const int64_t n = visible_n(a.m, t);
   const int nb = (int)((n + kBlock - 1) / kBlock);
   int32_t* cand = a.cand + (int64_t)t * kCandBlocks;
 
-  if (nb <= kCandBlocks)
+  if (role != 1 && nb <= kCandBlocks)
     for (int i = threadIdx.x; i < kCandBlocks; i += NT) cand[i] = i < nb ? i : -1;
-  if (nb <= kTopK) {
+  if (role == 0 && nb <= kCandBlocks) return;
+  if (role != 0 && nb <= kTopK) {
     for (int i = threadIdx.x; i < kTopK; i += NT) core[i] = i < nb ? i : -1;
   } else {
     uint32_t key[EPT];
     const ContigIds<EPT> I{(int)threadIdx.x * EPT, nb};
     load_block_keys<EPT>(a, t, n, I, key);
-    if (nb > kCandBlocks) {
+    if (role == -1 && nb > kCandBlocks) {
       const int ks[2] = {kCandBlocks, kTopK};
       int32_t* const outs[2] = {cand, core};
       multi_select<NT, EPT, 2>(key, I, ks, outs, sh);
     } else {
-      const int ks[1] = {kTopK};
-      int32_t* const outs[1] = {core};
+      const int ks[1] = {role == 0 ? kCandBlocks : kTopK};
+      int32_t* const outs[1] = {role == 0 ? cand : core};
       multi_select<NT, EPT, 1>(key, I, ks, outs, sh);
+      if (role == 0) return;
     }
   }
   __syncthreads();
@@ -742,12 +750,22 @@ hipError_t launch_select_nt(const SelectArgs& a, hipStream_t stream) {
   // blocks per thread: a multiple of 4 (16-byte loads), at least 4
   constexpr int E1 = 2048 / NT < 4 ? 4 : 2048 / NT, E2 = 4096 / NT < 4 ? 4 : 4096 / NT;
   if (a.parts <= 1) {
+    if (a.m.T <= kTwoRoleQueries) {   // two work-groups per query
+      const dim3 g2(2u, (unsigned)a.m.T);
+      if (nbmax <= NT * E1)
+        hipLaunchKernelGGL((select_kernel<NT, E1, 2>), g2, dim3(NT), 0, stream, a);
+      else if (nbmax <= NT * E2)
+        hipLaunchKernelGGL((select_kernel<NT, E2, 2>), g2, dim3(NT), 0, stream, a);
+      else
+        hipLaunchKernelGGL((select_kernel<NT, kPartBlocks / NT, 2>), g2, dim3(NT), 0, stream, a);
+      return hipGetLastError();
+    }
     if (nbmax <= NT * E1)
-      hipLaunchKernelGGL((select_kernel<NT, E1>), grid, dim3(NT), 0, stream, a);
+      hipLaunchKernelGGL((select_kernel<NT, E1, 1>), grid, dim3(NT), 0, stream, a);
     else if (nbmax <= NT * E2)
-      hipLaunchKernelGGL((select_kernel<NT, E2>), grid, dim3(NT), 0, stream, a);
+      hipLaunchKernelGGL((select_kernel<NT, E2, 1>), grid, dim3(NT), 0, stream, a);
     else
-      hipLaunchKernelGGL((select_kernel<NT, kPartBlocks / NT>), grid, dim3(NT), 0, stream, a);
+      hipLaunchKernelGGL((select_kernel<NT, kPartBlocks / NT, 1>), grid, dim3(NT), 0, stream, a);
     return hipGetLastError();
   }
   const dim3 pgrid((unsigned)a.parts, (unsigned)a.m.T);

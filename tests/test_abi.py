@@ -69,7 +69,7 @@ def test_plan_rejects(kw, status):
 
 
 def _splits(T):
-    # key splits of the attention for T queries: 4 work-groups per query for T <= 32
+    # key splits of the attention for T queries: 4 work-groups per head set for T <= 32
     return 4 if T <= 32 else 1
 
 
@@ -80,7 +80,7 @@ def _expected_workspace(max_queries):
     if units == 0:
         return select
     counters = a256(select)
-    ml = counters + a256(4 * max_queries)
+    ml = counters + a256(8 * max_queries)        # one counter per (query, head set)
     o = ml + a256(units * 64 * 2 * 4)
     return o + units * 64 * 512 * 4
 
@@ -108,7 +108,7 @@ def test_plan_accepts_long_rows(maxc, parts):
     a256 = lambda b: (b + 255) // 256 * 256
     select = mq * 2048 * 4 + extra
     counters = a256(select)
-    ml = counters + a256(4 * mq)
+    ml = counters + a256(8 * mq)
     o = ml + a256(4 * mq * 64 * 2 * 4)
     assert p.workspace_bytes == o + 4 * mq * 64 * 512 * 4
 

@@ -1,7 +1,7 @@
 """sparse_attn_fwd_noalloc (key-split state in the library's fixed per-GPU array, no
 workspace) against sparse_attn_fwd with a workspace, through the C ABI: two calls in a row,
-the second on a smaller batch (the array keeps the first call's contents), then a batch
-large enough to use no scratch at all. Outputs must meet the parity bar against the
+the second on a smaller batch (the array keeps the first call's contents), a batch whose
+heads are split over two work-groups, then a batch large enough to use no scratch at all. Outputs must meet the parity bar against the
 existing entry point (max |diff| <= 2e-2, mean <= 2e-3, lse within 1e-4); the two run the
 same kernels with the same splits, so they are also expected to agree bit for bit."""
 import numpy as np
@@ -47,11 +47,14 @@ def _compare(d, what):
 
 def test_noalloc_matches_workspace_entry_point():
     assert torch.cuda.is_available()
-    print("[noalloc] T=20 then T=5 (key splits in the fixed array), then T=40 (no splits)", flush=True)
+    print("[noalloc] T=20 then T=5 (key splits in the fixed array; T=5 also splits its heads), T=40 and "
+          "T=100 (no splits)", flush=True)
     d1 = _batch(20, [131072] * 10 + [9001] * 5 + [700, 64, 2, 1, 300], seed=91)
     _compare(d1, "first call")
     d2 = _batch(5, [40000, 1030, 3, 65536, 2048], seed=92, key_dtype="bf16")
     _compare(d2, "second call, smaller batch")
     _compare(d1, "third call, the first batch again")
     d3 = _batch(40, 6000, seed=93)
-    _compare(d3, "batch above the split size")
+    _compare(d3, "head sets without key splits")
+    d4 = _batch(100, 3000, seed=94)
+    _compare(d4, "batch above the split size")
