@@ -502,6 +502,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-rescore", action="store_true")
     ap.add_argument("--mq-workload", default="decode-mq6-b128-ctx128k-fp8")
+    ap.add_argument("--mq-mxfp4-workload", default="decode-mq6-b128-ctx128k-mxfp4")
     ap.add_argument("--no-multiquery", action="store_true")
     ap.add_argument("--mxfp4-workload", default="decode-b128-ctx128k-mxfp4")
     ap.add_argument("--no-mxfp4", action="store_true")
@@ -638,9 +639,11 @@ def main():
     del d
     torch.cuda.empty_cache()
 
-    if not args.no_multiquery:
+    mq_legs = [] if args.no_multiquery else [("multi_query", args.mq_workload, GROUP_TRAFFIC_FILE),
+                                              ("multi_query_mxfp4", args.mq_mxfp4_workload, None)]
+    for mq_key, mq_name, mq_traffic in mq_legs:
         t0 = time.perf_counter()
-        wm = W.make(args.mq_workload)
+        wm = W.make(mq_name)
         dm = DeviceBatch(wm)
         torch.cuda.synchronize()
         log(f"multi-token decode inputs ready in {time.perf_counter() - t0:.1f}s")
@@ -649,20 +652,20 @@ def main():
         gb = group_indexer_bytes(wm)
         fi, fa = step_flops(wm)
         mi_s = mms["indexer"] * 1e-3
-        result["multi_query"] = {
-            "workload": args.mq_workload, "queries": int(wm.T), "group": int(wm.group),
+        result[mq_key] = {
+            "workload": mq_name, "queries": int(wm.T), "group": int(wm.group),
             "ms_per_step": m_s * 1e3, "queries_per_s": wm.T / m_s,
             "eager_ms_per_step": m_eager * 1e3,
             "timing": m_timing,
             "stage_ms": mms,
             "indexer": {"bound": "hbm", "achieved": gb / mi_s / 1e9, "peak": HBM_PEAK / 1e9,
                         "unit": "GB/s", "frac": gb / mi_s / HBM_PEAK,
-                        "traffic": stored_traffic(args.mq_workload, GROUP_TRAFFIC_FILE),
+                        "traffic": stored_traffic(mq_name, mq_traffic) if mq_traffic else None,
                         "algorithmic_bytes_per_launch": gb, "avg_launch_ms": mms["indexer"],
                         "key_bytes_per_query": gb / wm.T,
                         "mfma_tflop": fi / 1e12, "mfma_frac": fi / mi_s / BF16_PEAK},
         }
-        log(f"multi-token decode: {m_s * 1e3:.3f} ms/step, stages {mms}")
+        log(f"{mq_key}: {m_s * 1e3:.3f} ms/step, stages {mms}")
         del dm, wm
         torch.cuda.empty_cache()
 

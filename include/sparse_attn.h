@@ -71,9 +71,10 @@ typedef enum sa_key_dtype {
                            [.][64] bytes of FP4 E2M1, element 2i in the low nibble of
                            byte i, plus [.][4] E8M0 scales, scale b for elements
                            32b .. 32b+31. Key = 2^(scale-127) * element. indexer_score
-                           runs the chunk kernel (one-sequence chunks, ragged runs) or one
-                           key stream per query for these keys, never the group kernel;
-                           not supported by indexer_score_cand or paged stores */
+                           runs the chunk kernel (one-sequence chunks, ragged runs), the
+                           group kernel (groups, runs of 2 to 8 queries) or one key stream
+                           per query for these keys; not supported by indexer_score_cand or
+                           paged stores */
 } sa_key_dtype;
 
 /* Fixed at plan time. The kernels support exactly num_heads 64, latent_dim 512,

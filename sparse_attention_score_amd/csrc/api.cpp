@@ -282,7 +282,7 @@ struct RunCursor {
 
 sa_status indexer_runs(const sa::IndexerArgs& a, const sa_queries* q, const sa_cache* c, const void* q_idx,
                        const float* w, hipStream_t stream) {
-  const bool chunk_ok = !a.pages.table || c->page_size >= 64, group_ok = !a.mxfp4;
+  const bool chunk_ok = !a.pages.table || c->page_size >= 64, group_ok = true;
   RunLaunch r;
   // per-query and group launches index queries in grid y
   for (RunCursor cur{q, chunk_ok, group_ok}; cur.next(r);) {
@@ -443,8 +443,6 @@ sa_status indexer_score(const sa_plan* plan, const sa_queries* q, const sa_cache
   // Queries that share a sequence in one call (a prefill chunk) reuse each key tile
   // across many queries; groups of a multi-token decode step share one key stream per
   // group; independent decode queries each stream their own keys.
-  // MXFP4 keys: no group kernel (one key stream per query, or the chunk kernel)
-  if (a.mxfp4) a.group = 1;
   if (q->runs) return indexer_runs(a, q, c, q_idx, w, (hipStream_t)stream);
   const bool prefill = (!a.pages.table || c->page_size >= 64) && a.group == 1 && c->num_seqs == 1 && q->T > 1;
   SA_REQUIRE(prefill || (q->T + a.group - 1) / a.group <= kMaxGridY, SA_EUNSUPPORTED,

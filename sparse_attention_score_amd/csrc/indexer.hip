@@ -714,6 +714,158 @@ __global__ __launch_bounds__(kDThreads, 2) void indexer_group_kernel(IndexerArgs
   }
 }
 
+// Grouped decode with MXFP4 keys: the grouped kernel's key stream, head sums and stores
+// with the MXFP4 kernel's tiles. A 16-key tile is one 1 KB load (64-byte rows); lane (c, g)
+// takes 32-dim block g of key c (its chunk at mx_pos(c, g)) and widens it with that key's
+// E8M0 block scale into the four B operands, so each query's arithmetic is the MXFP4
+// kernel's and its scores are the same bits. The block scales of the wave's keys arrive in
+// LDS by direct loads ahead of the A operands.
+constexpr int kGMxD = 8;   // MXFP4 tiles in flight per wave
+template <int G>
+struct GroupMxShared {
+  uint8_t ring[kDWaves][kGMxD * 16 * kMxRB];
+  uint8_t scale[kDWaves][group_tpw<G>() * 16 * 4];
+};
+
+template <int G>
+__global__ __launch_bounds__(kDThreads, 2) void indexer_group_mx_kernel(IndexerArgs a) {
+  constexpr int RB = kMxRB, TB = 16 * kMxRB, D = kGMxD;
+  constexpr int TPW = group_tpw<G>();
+  constexpr int N4 = G / 4, N2 = (G % 4) / 2;
+  static_assert(TB == 1024, "one load instruction per tile");
+  static_assert(G >= 2 && G <= 8 && G % 2 == 0, "groups of 2, 4, 6 or 8 queries");
+  static_assert((D & (D - 1)) == 0 && D <= TPW && D <= 63, "ring depth");
+  static_assert(TPW % 4 == 0, "64 scales per load");
+  __shared__ __attribute__((aligned(16))) GroupMxShared<G> sh;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int c = lane & 15, g = lane >> 4;
+  const int E = (int)a.E, T = (int)a.T;
+  const int t0 = blockIdx.y * a.group;
+  const int gs = min(a.group, T - t0);
+  const int key0 = blockIdx.x * group_keys_per_wg<G>() + wave * TPW * 16;
+  const int seq = a.seq_id[t0];
+  auto n_of = [&](int j) { return j < gs && a.seq_id[t0 + j] == seq ? query_n(a, t0 + j) : 0; };
+  int nmax = 0;
+  for (int j = 0; j < gs; ++j) nmax = max(nmax, n_of(j));
+  const int ntiles = key0 < E ? min(TPW, (E - key0 + 15) >> 4) : 0;
+  const int live = key0 < nmax ? min(TPW, (nmax - key0 + 15) >> 4) : 0;
+  const int sq = nmax > 0 ? seq : 0;
+  const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys) + (int64_t)sq * a.keys_seq_stride;
+  const uint8_t* scales = reinterpret_cast<const uint8_t*>(a.scales) + (int64_t)sq * a.scales_seq_stride;
+
+  // head weights, then the wave's block scales (direct loads, one key's 4 bytes per lane),
+  // then the A operands: the compiler's wait for the A operands at the first MFMA covers
+  // the scales and the first D tiles (loads complete in order)
+  float wq[G][4];
+  bf16x8 qa[G][4];
+  if (live > 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int tq = t0 + min(j, gs - 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wq[j][i] = a.w[(int64_t)tq * kIdxHeads + 4 * g + i];
+    }
+#pragma unroll
+    for (int j = 0; j < TPW / 4; ++j)
+      to_lds4(scales + (int64_t)min(key0 + 64 * j + lane, nmax - 1) * 4,
+              (uint32_t)(uintptr_t)&sh.scale[wave][256 * j]);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int tq = t0 + min(j, gs - 1);
+      const uint16_t* row = reinterpret_cast<const uint16_t*>(a.q_idx) + ((int64_t)tq * kIdxHeads + c) * kIdxDim;
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) qa[j][s2] = *reinterpret_cast<const bf16x8*>(row + kdim_mx(g, s2));
+    }
+  }
+  // tile load: lane -> row lane / 4, position lane % 4 holds chunk mx_pos(row, position)
+  const int rr = lane >> 2, qq = mx_pos(rr, lane & 3);
+  const uint32_t ring0 = (uint32_t)(uintptr_t)&sh.ring[wave][0];
+  auto issue = [&](int i, bool after_reads) {
+    const int k = key0 + 16 * i;
+    const uint8_t* src = keys + (int64_t)min(k + rr, nmax - 1) * RB + qq * 16;   // rows past nmax repeat
+    const uint32_t lds = ring0 + (uint32_t)((i & (D - 1)) * TB);
+    if (after_reads) to_lds16_after_reads(src, lds);
+    else to_lds16(src, lds);
+  };
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+    if (u < live) issue(u, false);
+
+  const uint32_t roff = (uint32_t)(c * RB + mx_pos(c, g) * 16);
+  float r4[TPW][N4 > 0 ? N4 : 1];
+  float r2[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    if (i < live) {
+      if (i + D - 1 < live) __builtin_amdgcn_s_waitcnt(waitcnt_vm(D - 1));   // tile i landed
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      const uint8_t* tile = sh.ring[wave] + (i & (D - 1)) * TB;
+      const u32x4 K = *reinterpret_cast<const u32x4*>(tile + roff);
+      const float sc = e8m0_scale(sh.scale[wave][(16 * i + c) * 4 + g]);
+      if (i + D < live) issue(i + D, true);
+      bf16x8 b[4];
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const u32x4 u = {
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(K[s2], sc, 0)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(K[s2], sc, 1)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(K[s2], sc, 2)),
+            __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(K[s2], sc, 3))};
+        b[s2] = __builtin_bit_cast(bf16x8, u);
+      }
+      float p[G];
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j][s2], b[s2], acc, 0, 0, 0);
+        float v = wq[j][0] * relu(acc[0]);
+        v = fmaf(wq[j][1], relu(acc[1]), v);
+        v = fmaf(wq[j][2], relu(acc[2]), v);
+        p[j] = fmaf(wq[j][3], relu(acc[3]), v);
+      }
+      auto sw16 = [](float x, float y) {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      };
+#pragma unroll
+      for (int h = 0; h < N4; ++h) {
+        const float ab = sw16(p[4 * h], p[4 * h + 1]);
+        const float cd = sw16(p[4 * h + 2], p[4 * h + 3]);
+        auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(ab), __float_as_uint(cd), false, false);
+        r4[i][h] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      }
+      if constexpr (N2 > 0) r2[i] = add_xor32(sw16(p[4 * N4], p[4 * N4 + 1]));
+    }
+  }
+
+  // ---- scores and block maxima: per tile, 16 keys of four queries per store ----
+  int jq4[N4 > 0 ? N4 : 1], nl4[N4 > 0 ? N4 : 1];
+#pragma unroll
+  for (int h = 0; h < N4; ++h) {
+    jq4[h] = 4 * h + g;
+    nl4[h] = n_of(jq4[h]);
+  }
+  const int jq2 = 4 * N4 + (g & 1);
+  const int nl2 = N2 > 0 ? n_of(jq2) : 0;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    if (i >= ntiles) break;
+    const int k = key0 + 16 * i + c;
+    auto put = [&](float v, int jq, bool mine) {
+      const float m = max8_lanes(v);
+      if (mine && jq < gs && k < E) {
+        const int64_t tq = t0 + jq;
+        a.scores[tq * a.ld_scores + k] = v;
+        if (a.block_max && (c & 7) == 0) a.block_max[tq * a.ld_block_max + (k >> 3)] = m;
+      }
+    };
+#pragma unroll
+    for (int h = 0; h < N4; ++h) put(i < live && k < nl4[h] ? r4[i][h] : neg_inf(), jq4[h], true);
+    if constexpr (N2 > 0) put(i < live && k < nl2 ? r2[i] : neg_inf(), jq2, g < 2);
+  }
+}
+
 // ======================================================================================
 // Prefill
 // ======================================================================================
@@ -1042,6 +1194,10 @@ template <int G>
 void launch_group(const IndexerArgs& a, hipStream_t stream) {
   constexpr int KW = group_keys_per_wg<G>();
   dim3 grid((unsigned)((a.E + KW - 1) / KW), (unsigned)((a.T + a.group - 1) / a.group));
+  if (a.mxfp4) {   // contiguous stores only (the host refuses paged MXFP4 keys)
+    hipLaunchKernelGGL((indexer_group_mx_kernel<G>), grid, dim3(kDThreads), 0, stream, a);
+    return;
+  }
   if (a.pages.table) {
     if (a.fp8)
       hipLaunchKernelGGL((indexer_group_kernel<true, G, true>), grid, dim3(kDThreads), 0, stream, a);
@@ -1057,8 +1213,8 @@ void launch_group(const IndexerArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream) {
-  if (a.mxfp4 && !prefill) {
-    // every query streams its own keys (the caller routes no other mode here)
+  if (a.mxfp4 && !prefill && a.group <= 1) {
+    // every query streams its own keys
     dim3 grid((unsigned)((a.E + kMxKeysPerWG - 1) / kMxKeysPerWG), (unsigned)a.T);
     hipLaunchKernelGGL(indexer_mx_kernel, grid, dim3(kDThreads), 0, stream, a);
   } else if (a.group > 1 && !a.cand) {

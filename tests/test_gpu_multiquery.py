@@ -41,7 +41,7 @@ def _same_bits(a, b, E, what):
     assert np.array_equal(a[:, :E].view(np.uint32), b[:, :E].view(np.uint32)), what
 
 
-@pytest.mark.parametrize("kd", ["bf16", "fp8"])
+@pytest.mark.parametrize("kd", ["bf16", "fp8", "mxfp4"])
 def test_multiquery_decode_end_to_end(kd):
     # 3 sequences x 6 queries (positions n_raw-6 .. n_raw-1), ragged contexts; the
     # longest prunes blocks in the candidate stage
@@ -68,12 +68,14 @@ def test_multiquery_decode_end_to_end(kd):
     _same_bits(g_bm, u_bm, d.E // 8, "block maxima")
 
 
-@pytest.mark.parametrize("G", [2, 3, 5, 7, 8])
-def test_multiquery_group_sizes_bitwise(G):
+@pytest.mark.parametrize("kd", ["fp8", "mxfp4"])
+@pytest.mark.parametrize("G", [2, 3, 5, 6, 7, 8])
+def test_multiquery_group_sizes_bitwise(G, kd):
     # group sizes that run in the next even kernel size (masked extra queries) and the
-    # largest; short contexts so every group has keys past some queries' n
-    wl = W.make_decode_mq(B=3, n_raw=[70, 2500, 9001], G=G, ratio=2, key_dtype="fp8",
-                          name=f"mq{G}", seed=32 + G)
+    # largest; short contexts so every group has keys past some queries' n. MXFP4 keys:
+    # the grouped MXFP4 kernel against the per-query MXFP4 kernel.
+    wl = W.make_decode_mq(B=3, n_raw=[70, 2500, 9001], G=G, ratio=2, key_dtype=kd,
+                          name=f"mq{G}-{kd}", seed=32 + G)
     d = _batch(wl)
     g_sc, g_bm = _scores(d, G)
     u_sc, u_bm = _scores(d, 0)

@@ -388,6 +388,10 @@ WORKLOADS = {
 MORE_WORKLOADS = {
     "decode-mq6-b128-ctx128k-fp8": dict(kind="decode_mq", B=128, n_raw=131072, G=6, ratio=2,
                                         key_dtype="fp8"),
+    # the multi-token step with the 4-bit indexer cache: each sequence's MXFP4 keys streamed
+    # once for its 6 queries
+    "decode-mq6-b128-ctx128k-mxfp4": dict(kind="decode_mq", B=128, n_raw=131072, G=6, ratio=2,
+                                          key_dtype="mxfp4"),
     # the headline decode batch with the 4-bit indexer cache (MXFP4 keys)
     "decode-b128-ctx128k-mxfp4": dict(kind="decode", B=128, n_raw=131072, ratio=2, key_dtype="mxfp4"),
     # the headline decode batch with e4m3 latent and window rows (fp32 row scales)
