@@ -73,8 +73,7 @@ typedef enum sa_key_dtype {
                            32b .. 32b+31. Key = 2^(scale-127) * element. indexer_score
                            runs the chunk kernel (one-sequence chunks, ragged runs), the
                            group kernel (groups, runs of 2 to 8 queries) or one key stream
-                           per query for these keys; not supported by indexer_score_cand or
-                           paged stores */
+                           per query for these keys, on contiguous or paged stores */
 } sa_key_dtype;
 
 /* Fixed at plan time. The kernels support exactly num_heads 64, latent_dim 512,
@@ -180,10 +179,11 @@ typedef struct sa_cache {
    * page_size, row r % page_size; the *_seq_stride fields are ignored), and compressed
    * position j of sequence s is pool row block_table[s * block_table_stride + j /
    * page_size] * page_size + j % page_size. The window stays per sequence. Page ids
-   * outside [0, num_pages) are clamped. Supported by indexer_score (bf16 and e4m3 keys,
-   * every kernel; a chunk runs on the chunk kernel only when pages hold at least 64 rows,
-   * else one key stream per query) and sparse_attn_fwd; indexer_score_cand and MXFP4 keys
-   * return SA_EUNSUPPORTED. */
+   * outside [0, num_pages) are clamped. Supported by indexer_score (bf16, e4m3 and MXFP4
+   * keys, every kernel; a chunk runs on the chunk kernel only when pages hold at least 64
+   * rows, else one key stream per query) and sparse_attn_fwd; indexer_score_cand returns
+   * SA_EUNSUPPORTED. MXFP4 key pools: idx_keys [num_pages * page_size][64] bytes and
+   * idx_scales [num_pages * page_size][4] bytes. */
   const int32_t* block_table;    /* device int32 [num_seqs][block_table_stride] or NULL */
   int64_t block_table_stride;    /* >= ceil(compressed_cap / page_size) */
   int32_t page_size;             /* power of two in [16, 2^20] */

@@ -169,11 +169,10 @@ sa_status check_cache(const sa_plan* plan, const sa_queries* q, const sa_cache* 
     const int64_t rowunits = mx ? 64 : 128;
     SA_REQUIRE(paged || (c->idx_keys_seq_stride >= c->compressed_cap * rowunits && c->idx_keys_seq_stride % rowmul == 0),
                SA_EINVAL, "cache->idx_keys_seq_stride = %lld invalid", (long long)c->idx_keys_seq_stride);
-    SA_REQUIRE(!(paged && mx), SA_EUNSUPPORTED, "paged stores support bf16 and e4m3 index keys only");
     if (mx) {
       SA_REQUIRE(c->idx_scales != nullptr && reinterpret_cast<uintptr_t>(c->idx_scales) % 4 == 0, SA_EINVAL,
                  "cache->idx_scales is NULL or not 4-byte aligned (required for MXFP4 keys)");
-      SA_REQUIRE(c->idx_scales_seq_stride >= c->compressed_cap * 4 && c->idx_scales_seq_stride % 4 == 0,
+      SA_REQUIRE(paged || (c->idx_scales_seq_stride >= c->compressed_cap * 4 && c->idx_scales_seq_stride % 4 == 0),
                  SA_EINVAL, "cache->idx_scales_seq_stride = %lld must be >= 4 * compressed_cap and a multiple of 4",
                  (long long)c->idx_scales_seq_stride);
     }

@@ -394,8 +394,12 @@ __device__ __forceinline__ int mx_pos(int r, int q) { return q ^ ((r >> 2) & 3);
 __device__ __forceinline__ int kdim_mx(int g, int s) { return 32 * g + 8 * s; }
 
 
+// PAGED: keys and block scales are page pools (pages of 16+ rows, so a 16-key tile lies in
+// one page); the wave's page ids, one per lane and tile, are read before its other loads.
+template <bool PAGED>
 __global__ __launch_bounds__(kDThreads) void indexer_mx_kernel(IndexerArgs a) {
   constexpr int RB = kMxRB, TB = 16 * kMxRB, D = kMxD;
+  static_assert(!PAGED || kMxTPW <= 64, "one page id per lane");
   static_assert(TB == 1024, "one load instruction per tile");
   __shared__ __attribute__((aligned(16))) MxShared sh;
   const int t = blockIdx.y;
@@ -411,8 +415,19 @@ __global__ __launch_bounds__(kDThreads) void indexer_mx_kernel(IndexerArgs a) {
   float* srow = a.scores + (int64_t)t * a.ld_scores;
   float* brow = a.block_max ? a.block_max + (int64_t)t * a.ld_block_max : nullptr;
   const int seq = a.seq_id[t];
-  const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys) + (int64_t)seq * a.keys_seq_stride;
-  const uint8_t* scales = reinterpret_cast<const uint8_t*>(a.scales) + (int64_t)seq * a.scales_seq_stride;
+  const int sq = n > 0 ? seq : 0;   // n > 0 implies a valid sequence
+  const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys) + (PAGED ? 0 : (int64_t)sq * a.keys_seq_stride);
+  const uint8_t* scales = reinterpret_cast<const uint8_t*>(a.scales) + (PAGED ? 0 : (int64_t)sq * a.scales_seq_stride);
+  // paged: page id of the wave's tile `lane` (lanes past the last live tile take its page)
+  int pgreg = 0;
+  if constexpr (PAGED) {
+    if (live > 0) pgreg = (int)page_of(a.pages, sq, min(key0 + 16 * min(lane, kMxTPW - 1), n - 1));
+  }
+  // store row of key x (x < n) of this wave
+  auto krow = [&](int x) -> int64_t {
+    if constexpr (PAGED) return pool_row(a.pages, __shfl(pgreg, (x - key0) >> 4), x);
+    else return x;
+  };
 
   const uint32_t lds_q = (uint32_t)(uintptr_t)&sh.q[0];
   const uint32_t lds_w = (uint32_t)(uintptr_t)&sh.w[0];
@@ -425,7 +440,7 @@ __global__ __launch_bounds__(kDThreads) void indexer_mx_kernel(IndexerArgs a) {
   if (live > 0) {
 #pragma unroll
     for (int j = 0; j < kMxTPW / 4; ++j)
-      to_lds4(scales + (int64_t)min(key0 + 64 * j + lane, n - 1) * 4,
+      to_lds4(scales + krow(min(key0 + 64 * j + lane, n - 1)) * 4,
               (uint32_t)(uintptr_t)&sh.scale[wave][256 * j]);
   }
 
@@ -434,8 +449,11 @@ __global__ __launch_bounds__(kDThreads) void indexer_mx_kernel(IndexerArgs a) {
   const uint32_t ring0 = (uint32_t)(uintptr_t)&sh.ring[wave][0];
   auto issue = [&](int i, bool after_reads) {
     const int k = key0 + 16 * i;
-    const int row = min(k + rr, n - 1);
-    const uint8_t* src = keys + (int64_t)row * RB + qq * 16;
+    // rows past n repeat row n-1 (same page: a tile never crosses one)
+    int64_t row;
+    if constexpr (PAGED) row = pool_row(a.pages, __builtin_amdgcn_readlane(pgreg, i), k) + min(rr, n - 1 - k);
+    else row = min(k + rr, n - 1);
+    const uint8_t* src = keys + row * RB + qq * 16;
     const uint32_t lds = ring0 + (uint32_t)((i & (D - 1)) * TB);
     if (after_reads) to_lds16_after_reads(src, lds);
     else to_lds16(src, lds);
@@ -727,7 +745,7 @@ struct GroupMxShared {
   uint8_t scale[kDWaves][group_tpw<G>() * 16 * 4];
 };
 
-template <int G>
+template <int G, bool PAGED>
 __global__ __launch_bounds__(kDThreads, 2) void indexer_group_mx_kernel(IndexerArgs a) {
   constexpr int RB = kMxRB, TB = 16 * kMxRB, D = kGMxD;
   constexpr int TPW = group_tpw<G>();
@@ -750,8 +768,19 @@ __global__ __launch_bounds__(kDThreads, 2) void indexer_group_mx_kernel(IndexerA
   const int ntiles = key0 < E ? min(TPW, (E - key0 + 15) >> 4) : 0;
   const int live = key0 < nmax ? min(TPW, (nmax - key0 + 15) >> 4) : 0;
   const int sq = nmax > 0 ? seq : 0;
-  const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys) + (int64_t)sq * a.keys_seq_stride;
-  const uint8_t* scales = reinterpret_cast<const uint8_t*>(a.scales) + (int64_t)sq * a.scales_seq_stride;
+  const uint8_t* keys = reinterpret_cast<const uint8_t*>(a.keys) + (PAGED ? 0 : (int64_t)sq * a.keys_seq_stride);
+  const uint8_t* scales = reinterpret_cast<const uint8_t*>(a.scales) + (PAGED ? 0 : (int64_t)sq * a.scales_seq_stride);
+  // paged: page id of the wave's tile `lane` (lanes past the last live tile take its page),
+  // read before every other load
+  int pgreg = 0;
+  if constexpr (PAGED) {
+    static_assert(TPW <= 64, "one page id per lane");
+    if (live > 0) pgreg = (int)page_of(a.pages, sq, min(key0 + 16 * min(lane, TPW - 1), nmax - 1));
+  }
+  auto krow = [&](int x) -> int64_t {
+    if constexpr (PAGED) return pool_row(a.pages, __shfl(pgreg, (x - key0) >> 4), x);
+    else return x;
+  };
 
   // head weights, then the wave's block scales (direct loads, one key's 4 bytes per lane),
   // then the A operands: the compiler's wait for the A operands at the first MFMA covers
@@ -767,7 +796,7 @@ __global__ __launch_bounds__(kDThreads, 2) void indexer_group_mx_kernel(IndexerA
     }
 #pragma unroll
     for (int j = 0; j < TPW / 4; ++j)
-      to_lds4(scales + (int64_t)min(key0 + 64 * j + lane, nmax - 1) * 4,
+      to_lds4(scales + krow(min(key0 + 64 * j + lane, nmax - 1)) * 4,
               (uint32_t)(uintptr_t)&sh.scale[wave][256 * j]);
 #pragma unroll
     for (int j = 0; j < G; ++j) {
@@ -782,7 +811,11 @@ __global__ __launch_bounds__(kDThreads, 2) void indexer_group_mx_kernel(IndexerA
   const uint32_t ring0 = (uint32_t)(uintptr_t)&sh.ring[wave][0];
   auto issue = [&](int i, bool after_reads) {
     const int k = key0 + 16 * i;
-    const uint8_t* src = keys + (int64_t)min(k + rr, nmax - 1) * RB + qq * 16;   // rows past nmax repeat
+    // rows past nmax repeat row nmax-1 (same page: a tile never crosses one)
+    int64_t row;
+    if constexpr (PAGED) row = pool_row(a.pages, __builtin_amdgcn_readlane(pgreg, i), k) + min(rr, nmax - 1 - k);
+    else row = min(k + rr, nmax - 1);
+    const uint8_t* src = keys + row * RB + qq * 16;
     const uint32_t lds = ring0 + (uint32_t)((i & (D - 1)) * TB);
     if (after_reads) to_lds16_after_reads(src, lds);
     else to_lds16(src, lds);
@@ -901,13 +934,12 @@ constexpr uint32_t kDrop = 0x80000000u;  // buffer offset past every extent: sto
 
 // KF: key format, 0 bf16, 1 e4m3 (row scale applied to the score), 2 MXFP4 (each 16-byte
 // chunk of a 64-byte row is one 32-element block: widened with its E8M0 scale while
-// staging, so the tile holds exact bf16 values). PAGED: keys and scales are page pools of
-// at least kPST rows per page, so each stage of 64 keys lies in one page; the chunk's page
-// ids (at most 64) are read once, one per lane.
+// staging, so the tile holds exact bf16 values). PAGED: keys and scales (e4m3 or MXFP4) are
+// page pools of at least kPST rows per page, so each stage of 64 keys lies in one page; the
+// chunk's page ids (at most 64) are read once, one per lane.
 template <int KF, bool PAGED>
 __global__ __launch_bounds__(kPThreads, 8 / kPWaves) void indexer_prefill_kernel(IndexerArgs a) {
   constexpr bool FP8 = KF == 1, MX = KF == 2;
-  static_assert(!(MX && PAGED), "MXFP4 keys are read from contiguous stores");
   constexpr int RB = MX ? kIdxDim / 2 : (FP8 ? kIdxDim : 2 * kIdxDim);   // key row bytes in HBM
   __shared__ __attribute__((aligned(16))) PrefillShared sh;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -1015,8 +1047,11 @@ __global__ __launch_bounds__(kPThreads, 8 / kPWaves) void indexer_prefill_kernel
       const int64_t row0 = (pg << lp) + (ks & ((1 << lp) - 1));
       kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(a.keys) + row0 * RB),
                                              (short)0, rows * RB, kRsrcWord3);
-      sr = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(FP8 ? a.scales + row0 : a.w), (short)0,
-                                             FP8 ? rows * 4 : 0, kRsrcWord3);
+      // one dword per row: the fp32 scale (e4m3) or the 4 E8M0 bytes (MXFP4)
+      sr = __builtin_amdgcn_make_buffer_rsrc(
+          (FP8 || MX) ? const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(a.scales) + row0 * 4)
+                      : reinterpret_cast<uint8_t*>(const_cast<float*>(a.w)),
+          (short)0, (FP8 || MX) ? rows * 4 : 0, kRsrcWord3);
       skoff = 0;
       ssoff = 0;
     } else {
@@ -1194,8 +1229,11 @@ template <int G>
 void launch_group(const IndexerArgs& a, hipStream_t stream) {
   constexpr int KW = group_keys_per_wg<G>();
   dim3 grid((unsigned)((a.E + KW - 1) / KW), (unsigned)((a.T + a.group - 1) / a.group));
-  if (a.mxfp4) {   // contiguous stores only (the host refuses paged MXFP4 keys)
-    hipLaunchKernelGGL((indexer_group_mx_kernel<G>), grid, dim3(kDThreads), 0, stream, a);
+  if (a.mxfp4) {
+    if (a.pages.table)
+      hipLaunchKernelGGL((indexer_group_mx_kernel<G, true>), grid, dim3(kDThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((indexer_group_mx_kernel<G, false>), grid, dim3(kDThreads), 0, stream, a);
     return;
   }
   if (a.pages.table) {
@@ -1216,7 +1254,10 @@ hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream
   if (a.mxfp4 && !prefill && a.group <= 1) {
     // every query streams its own keys
     dim3 grid((unsigned)((a.E + kMxKeysPerWG - 1) / kMxKeysPerWG), (unsigned)a.T);
-    hipLaunchKernelGGL(indexer_mx_kernel, grid, dim3(kDThreads), 0, stream, a);
+    if (a.pages.table)
+      hipLaunchKernelGGL((indexer_mx_kernel<true>), grid, dim3(kDThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((indexer_mx_kernel<false>), grid, dim3(kDThreads), 0, stream, a);
   } else if (a.group > 1 && !a.cand) {
     // the smallest even group size that holds a.group (extra queries are masked)
     if (a.group <= 2) launch_group<2>(a, stream);
@@ -1245,7 +1286,10 @@ hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream
     // keeps the same chunks and their keys stay in its L2.
     dim3 grid((unsigned)((a.E + kPChunk - 1) / kPChunk), (unsigned)((a.T + kQPerWG - 1) / kQPerWG));
     if (a.mxfp4) {
-      hipLaunchKernelGGL((indexer_prefill_kernel<2, false>), grid, dim3(kPThreads), 0, stream, a);
+      if (a.pages.table)
+        hipLaunchKernelGGL((indexer_prefill_kernel<2, true>), grid, dim3(kPThreads), 0, stream, a);
+      else
+        hipLaunchKernelGGL((indexer_prefill_kernel<2, false>), grid, dim3(kPThreads), 0, stream, a);
     } else if (a.pages.table) {
       if (a.fp8)
         hipLaunchKernelGGL((indexer_prefill_kernel<1, true>), grid, dim3(kPThreads), 0, stream, a);

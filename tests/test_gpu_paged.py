@@ -45,8 +45,8 @@ def _paged_cache(d, P, seed, spare=3):
         return pool
 
     lat = pool_of(d.C, tuple(d.C.shape[2:]))
-    keys = pool_of(d.KI, (128,))
-    scales = pool_of(d.KS, ()) if d.KS is not None else None
+    keys = pool_of(d.KI, tuple(d.KI.shape[2:]))      # 128 bf16 / e4m3, or 64 MXFP4 bytes
+    scales = pool_of(d.KS, tuple(d.KS.shape[2:])) if d.KS is not None else None   # fp32, or 4 E8M0 bytes
     lscales = pool_of(d.CS, tuple(d.CS.shape[2:])) if d.CS is not None else None
     cache = S.Cache(latents=lat, window=d.R, idx_keys=keys, idx_scales=scales, num_seqs=B,
                     compressed_cap=cap, block_table=table, page_size=P, latent_scales=lscales,
@@ -79,7 +79,7 @@ def _same(d, res_p, res_c):
     assert torch.equal(lp.view(torch.int32), lc.view(torch.int32)), "lse"
 
 
-@pytest.mark.parametrize("kd,P", [("fp8", 16), ("fp8", 256), ("bf16", 64)])
+@pytest.mark.parametrize("kd,P", [("fp8", 16), ("fp8", 256), ("bf16", 64), ("mxfp4", 16), ("mxfp4", 128)])
 def test_paged_decode_matches_contiguous(kd, P):
     # n = 20003 (pruning, ragged last block), 1500, 0 (window only), 17
     wl = W.make_decode(B=4, n_raw=[40006, 3000, 1, 35], ratio=2, key_dtype=kd,
@@ -105,7 +105,7 @@ def test_paged_prefill_chunk_runs_per_query_and_matches_oracle():
         check_outputs(o[t], res2.o[t], f"t={t} out")
 
 
-@pytest.mark.parametrize("kd,P", [("bf16", 64), ("fp8", 256)])
+@pytest.mark.parametrize("kd,P", [("bf16", 64), ("fp8", 256), ("mxfp4", 64)])
 def test_paged_prefill_chunk_kernel_matches_contiguous(kd, P):
     # pages of at least 64 rows: the chunk kernel reads each 64-key stage from its page;
     # 300 queries over 20000+ keys (several chunks and stages, a ragged end)
@@ -116,16 +116,17 @@ def test_paged_prefill_chunk_kernel_matches_contiguous(kd, P):
     _same(d, res_p, res_c)
 
 
-@pytest.mark.parametrize("kind", ["mq", "ragged"])
+@pytest.mark.parametrize("kind", ["mq", "ragged", "mq-mxfp4", "ragged-mxfp4"])
 def test_paged_group_and_ragged_match_contiguous(kind):
     # the group kernel (6-query draft steps) and a ragged batch (chunk, group and per-query
-    # launches from one call) on 64-row pages
-    if kind == "mq":
-        wl = W.make_decode_mq(B=3, n_raw=[3001, 40006, 700], G=6, ratio=2, key_dtype="fp8",
-                              name="paged-mq", seed=55)
+    # launches from one call) on 64-row pages, with e4m3 / bf16 and with MXFP4 keys
+    mx = kind.endswith("mxfp4")
+    if kind.startswith("mq"):
+        wl = W.make_decode_mq(B=3, n_raw=[3001, 40006, 700], G=6, ratio=2, key_dtype="mxfp4" if mx else "fp8",
+                              name=f"paged-{kind}", seed=55)
     else:
-        wl = W.make_ragged([9000, 3001, 4000, 5000, 700], [20, 1, 6, 6, 1], ratio=2, key_dtype="bf16",
-                           name="paged-ragged", seed=56)
+        wl = W.make_ragged([9000, 3001, 4000, 5000, 700], [20, 1, 6, 6, 1], ratio=2,
+                           key_dtype="mxfp4" if mx else "bf16", name=f"paged-{kind}", seed=56)
     d = _batch(wl)
     res_c = _run(d, d.cache)
     res_p = _run(d, _paged_cache(d, 64, seed=5))
