@@ -73,7 +73,8 @@ typedef enum sa_key_dtype {
                            32b .. 32b+31. Key = 2^(scale-127) * element. indexer_score
                            runs the chunk kernel (one-sequence chunks, ragged runs), the
                            group kernel (groups, runs of 2 to 8 queries) or one key stream
-                           per query for these keys, on contiguous or paged stores */
+                           per query for these keys, on contiguous or paged stores;
+                           indexer_score_cand takes them on contiguous stores */
 } sa_key_dtype;
 
 /* Fixed at plan time. The kernels support exactly num_heads 64, latent_dim 512,
@@ -268,7 +269,8 @@ sa_status select_topk(const sa_plan* plan, const sa_queries* queries, const floa
  * earlier layer's candidate stage kept; the pages' candidate stage selecting 2048 blocks of
  * 8, "deepseek-ai/DeepSeek-V4.1-Flash" recipe, Overview, two-tier sparse attention bullet).
  * S1 over the visible positions of the carried blocks only, with this query's own index
- * heads and weights; one stream of 1 KB (e4m3) or 2 KB (bf16) blocks per query.
+ * heads and weights; one stream of 2 KB (bf16), 1 KB (e4m3) or 512-byte (MXFP4) blocks per
+ * query.
  *   cand       device int32 [T][2048]: carried block ids, ascending, -1 after the last
  *              (the layout select_topk writes); 16-byte aligned. An entry outside
  *              [0, ceil(n_t / 8)) is an empty slot (its entries are -inf).

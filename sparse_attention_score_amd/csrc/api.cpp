@@ -463,8 +463,6 @@ sa_status indexer_score_cand(const sa_plan* plan, const sa_queries* q, const sa_
   if ((st = check_plan(plan)) != SA_OK) return st;
   if ((st = check_queries(plan, q)) != SA_OK) return st;
   if ((st = check_cache(plan, q, c, true, false)) != SA_OK) return st;
-  SA_REQUIRE(plan->p.idx_key_dtype != SA_KEY_MXFP4, SA_EUNSUPPORTED,
-             "candidate-bounded re-scoring supports bf16 and e4m3 index keys only");
   SA_REQUIRE(c->block_table == nullptr, SA_EUNSUPPORTED,
              "candidate-bounded re-scoring reads contiguous stores only");
   SA_REQUIRE(q_idx && aligned16(q_idx) && w && aligned16(w), SA_EINVAL,
@@ -505,7 +503,7 @@ sa_status indexer_score_cand(const sa_plan* plan, const sa_queries* q, const sa_
   a.group = 1;
   a.pages = sa::PageTable{nullptr, 0, 0, 0};
   log_call("indexer_score_cand: T=%lld, 2048 carried blocks per query, keys=%s", (long long)q->T,
-           a.fp8 ? "e4m3" : "bf16");
+           a.mxfp4 ? "mxfp4" : a.fp8 ? "e4m3" : "bf16");
   return hip_status(sa::launch_indexer(a, false, (hipStream_t)stream), "indexer_score_cand launch");
 }
 

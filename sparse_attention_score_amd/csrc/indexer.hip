@@ -386,6 +386,7 @@ struct MxShared {
   float stage[kDWaves][kMxTPW * 16];
   uint16_t q[kIdxHeads * kIdxDim];
   float w[kIdxHeads];
+  int32_t ids[kDWaves * kMxTPW * 2];         // candidate mode: the work-group's block ids
 };
 
 // Position of chunk q (block q) of row r in LDS: rotated by r/4 so that the 16 rows' reads
@@ -394,12 +395,16 @@ __device__ __forceinline__ int mx_pos(int r, int q) { return q ^ ((r >> 2) & 3);
 __device__ __forceinline__ int kdim_mx(int g, int s) { return 32 * g + 8 * s; }
 
 
-// PAGED: keys and block scales are page pools (pages of 16+ rows, so a 16-key tile lies in
-// one page); the wave's page ids, one per lane and tile, are read before its other loads.
-template <bool PAGED>
+// MODE kPaged: keys and block scales are page pools (pages of 16+ rows, so a 16-key tile
+// lies in one page); the wave's page ids, one per lane and tile, are read before its other
+// loads. MODE kCand: candidate-bounded re-scoring as in the decode kernel; a tile is two
+// slots (blocks of 8 rows), each load instruction reads both, and the block scales of each
+// slot's rows are loaded once the ids are in.
+template <int MODE>
 __global__ __launch_bounds__(kDThreads) void indexer_mx_kernel(IndexerArgs a) {
   constexpr int RB = kMxRB, TB = 16 * kMxRB, D = kMxD;
-  static_assert(!PAGED || kMxTPW <= 64, "one page id per lane");
+  constexpr bool CAND = MODE == kCand, PAGED = MODE == kPaged;
+  static_assert(kMxTPW * 2 <= 64, "one page id or one slot per lane");
   static_assert(TB == 1024, "one load instruction per tile");
   __shared__ __attribute__((aligned(16))) MxShared sh;
   const int t = blockIdx.y;
@@ -410,8 +415,8 @@ __global__ __launch_bounds__(kDThreads) void indexer_mx_kernel(IndexerArgs a) {
   const int key0 = chunk0 + wave * kMxTPW * 16;
   const int n = query_n(a, t);
   const int ntiles = key0 < E ? min(kMxTPW, (E - key0 + 15) >> 4) : 0;
-  const int chunk_live = chunk0 < n ? min(kDWaves * kMxTPW, (n - chunk0 + 15) >> 4) : 0;
-  const int live = min(max(chunk_live - wave * kMxTPW, 0), kMxTPW);
+  const int chunk_live = CAND ? (n > 0 ? 1 : 0) : (chunk0 < n ? min(kDWaves * kMxTPW, (n - chunk0 + 15) >> 4) : 0);
+  int live = CAND ? 0 : min(max(chunk_live - wave * kMxTPW, 0), kMxTPW);
   float* srow = a.scores + (int64_t)t * a.ld_scores;
   float* brow = a.block_max ? a.block_max + (int64_t)t * a.ld_block_max : nullptr;
   const int seq = a.seq_id[t];
@@ -435,9 +440,37 @@ __global__ __launch_bounds__(kDThreads) void indexer_mx_kernel(IndexerArgs a) {
     const uint8_t* qb = reinterpret_cast<const uint8_t*>(a.q_idx) + (int64_t)t * kIdxHeads * kIdxDim * 2;
     to_lds16(qb + 1024 * wave + 16 * lane, lds_q + 1024 * wave);
     if (wave == 0 && lane < kIdxHeads / 4) to_lds16(a.w + (int64_t)t * kIdxHeads + 4 * lane, lds_w);
+    if (CAND && wave == 1) {   // the work-group's 256 block ids (1 KB)
+      static_assert(kDWaves * kMxTPW * 2 == 256, "one 16-byte load per lane");
+      to_lds16(a.cand + (int64_t)t * kCandBlocks + chunk0 / 8 + 4 * lane, (uint32_t)(uintptr_t)&sh.ids[0]);
+    }
   }
+  // candidate mode: block id of the wave's slot `lane` (slot 2i + h is half h of tile i). A
+  // slot is valid when its block holds a visible position; the wave loads tiles up to its
+  // last valid slot, and invalid slots among them read row n - 1 and are masked.
+  constexpr int kSlots = 2 * kMxTPW;
+  const int nbv = (n + 7) >> 3;
+  auto valid_id = [&](int id) { return id >= 0 && id < nbv; };
+  int idreg = -1;
+  if constexpr (CAND) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    asm volatile("s_barrier" ::: "memory");
+    if (chunk_live > 0) idreg = sh.ids[kSlots * wave + lane];
+    const uint64_t vm = __ballot(valid_id(idreg));
+    live = vm ? (64 - __builtin_clzll(vm) + 1) >> 1 : 0;
+  }
+  // row of entry e (0 .. 16 kMxTPW - 1) of the wave in candidate mode
+  auto cand_row = [&](int id, int e) { return valid_id(id) ? min(8 * id + (e & 7), n - 1) : n - 1; };
   // the wave's block scales, one key (4 bytes) per lane and load (rows past n repeat row n-1)
-  if (live > 0) {
+  if constexpr (CAND) {
+    if (live > 0) {
+#pragma unroll
+      for (int j = 0; j < kMxTPW / 4; ++j) {
+        const int id = sh.ids[kSlots * wave + 8 * j + (lane >> 3)];
+        to_lds4(scales + (int64_t)cand_row(id, lane) * 4, (uint32_t)(uintptr_t)&sh.scale[wave][256 * j]);
+      }
+    }
+  } else if (live > 0) {
 #pragma unroll
     for (int j = 0; j < kMxTPW / 4; ++j)
       to_lds4(scales + krow(min(key0 + 64 * j + lane, n - 1)) * 4,
@@ -451,7 +484,11 @@ __global__ __launch_bounds__(kDThreads) void indexer_mx_kernel(IndexerArgs a) {
     const int k = key0 + 16 * i;
     // rows past n repeat row n-1 (same page: a tile never crosses one)
     int64_t row;
-    if constexpr (PAGED) row = pool_row(a.pages, __builtin_amdgcn_readlane(pgreg, i), k) + min(rr, n - 1 - k);
+    if constexpr (CAND) {   // lanes 0-31 load slot 2i, lanes 32-63 slot 2i + 1 (uniform lane reads)
+      const int id0 = __builtin_amdgcn_readlane(idreg, 2 * i), id1 = __builtin_amdgcn_readlane(idreg, 2 * i + 1);
+      row = cand_row(rr >= 8 ? id1 : id0, rr);
+    }
+    else if constexpr (PAGED) row = pool_row(a.pages, __builtin_amdgcn_readlane(pgreg, i), k) + min(rr, n - 1 - k);
     else row = min(k + rr, n - 1);
     const uint8_t* src = keys + row * RB + qq * 16;
     const uint32_t lds = ring0 + (uint32_t)((i & (D - 1)) * TB);
@@ -506,7 +543,12 @@ __global__ __launch_bounds__(kDThreads) void indexer_mx_kernel(IndexerArgs a) {
   for (int j = 0; j < kMxTPW / 4; ++j) {
     const int k = key0 + 64 * j + lane;
     if (64 * j >= 16 * ntiles) break;
-    const float v = k < n ? stage[64 * j + lane] : neg_inf();
+    bool ok = k < n;
+    if constexpr (CAND) {
+      const int id = chunk_live > 0 ? sh.ids[kSlots * wave + 8 * j + (lane >> 3)] : -1;
+      ok = valid_id(id) && 8 * id + (lane & 7) < n;   // valid slots all lie in the loaded tiles
+    }
+    const float v = ok ? stage[64 * j + lane] : neg_inf();
     const float m = max8_lanes(v);
     if (k < E) {
       srow[k] = v;
@@ -1254,10 +1296,12 @@ hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream
   if (a.mxfp4 && !prefill && a.group <= 1) {
     // every query streams its own keys
     dim3 grid((unsigned)((a.E + kMxKeysPerWG - 1) / kMxKeysPerWG), (unsigned)a.T);
-    if (a.pages.table)
-      hipLaunchKernelGGL((indexer_mx_kernel<true>), grid, dim3(kDThreads), 0, stream, a);
+    if (a.cand)
+      hipLaunchKernelGGL((indexer_mx_kernel<kCand>), grid, dim3(kDThreads), 0, stream, a);
+    else if (a.pages.table)
+      hipLaunchKernelGGL((indexer_mx_kernel<kPaged>), grid, dim3(kDThreads), 0, stream, a);
     else
-      hipLaunchKernelGGL((indexer_mx_kernel<false>), grid, dim3(kDThreads), 0, stream, a);
+      hipLaunchKernelGGL((indexer_mx_kernel<kPlain>), grid, dim3(kDThreads), 0, stream, a);
   } else if (a.group > 1 && !a.cand) {
     // the smallest even group size that holds a.group (extra queries are masked)
     if (a.group <= 2) launch_group<2>(a, stream);

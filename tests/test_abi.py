@@ -228,9 +228,11 @@ def test_mxfp4_rejects(case):
     if case == "scale_stride": c.idx_scales_seq_stride = 3999
     if case == "key_stride": c.idx_keys_seq_stride = 999 * 64
     if case == "cand":
+        # re-scoring takes MXFP4 keys, but only from contiguous stores: refused on pages
+        c.block_table, c.block_table_stride, c.page_size, c.num_pages = 0xA0000, 63, 16, 300
         st = S.lib.indexer_score_cand(p.handle, ctypes.byref(q), ctypes.byref(c), 0x40000, 0x50000,
                                       0x80000, 0x60000, 16384, 0x90000, 2048, None)
-        assert st == S.SA_EUNSUPPORTED
+        assert st == S.SA_EUNSUPPORTED and b"contiguous" in S.lib.sparse_attn_last_error()
         return
     assert _indexer(p, q, c) == S.SA_EINVAL, S.lib.sparse_attn_last_error()
 

@@ -101,7 +101,7 @@ def _random_sets(rng, n_per_query, sizes):
     return rows
 
 
-@pytest.mark.parametrize("kd", ["bf16", "fp8"])
+@pytest.mark.parametrize("kd", ["bf16", "fp8", "mxfp4"])
 def test_rescore_own_candidates_match_two_stage(kd):
     # n = 20003 (2501 blocks, 2048 carried), 1500, 65000 (8125 blocks), 9
     wl = W.make_decode(B=4, n_raw=[40006, 3000, 130001, 18], ratio=2, key_dtype=kd,
@@ -126,7 +126,7 @@ def test_rescore_own_candidates_match_two_stage(kd):
     _check_query(wl, t, cand[t], sc[t], bm[t], tk[t], _keys(wl, int(wl.seq[t]), int(wl.visible()[t])))
 
 
-@pytest.mark.parametrize("kd", ["bf16", "fp8"])
+@pytest.mark.parametrize("kd", ["bf16", "fp8", "mxfp4"])
 def test_rescore_carried_sets_vs_oracle(kd):
     # carried sets from another layer: random block subsets of every size class, including
     # blocks past the visible ones and more than 512 slots (the slot pre-selection runs)
@@ -143,11 +143,12 @@ def test_rescore_carried_sets_vs_oracle(kd):
         _check_query(wl, t, rows[t], sc[t], bm[t], tk[t], _keys(wl, int(wl.seq[t]), n))
 
 
-def test_rescore_edge_cases():
+@pytest.mark.parametrize("kd", ["fp8", "mxfp4"])
+def test_rescore_edge_cases(kd):
     # n = 0 (no keys), 1, 8, 9, 17; sets: empty, ids past the visible blocks only,
     # a single partly visible block, every block, a full row of ids past the end
-    wl = W.make_decode(B=6, n_raw=[1, 2, 16, 18, 34, 34], ratio=2, key_dtype="fp8",
-                       name="rescore-edges", with_compress=False, seed=24)
+    wl = W.make_decode(B=6, n_raw=[1, 2, 16, 18, 34, 34], ratio=2, key_dtype=kd,
+                       name=f"rescore-edges-{kd}", with_compress=False, seed=24)
     n = wl.visible()
     rows = np.full((wl.T, CAND), -1, np.int32)
     rows[0, :3] = [0, 1, 2]                 # n = 0: every slot empty
