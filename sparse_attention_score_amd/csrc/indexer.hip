@@ -132,6 +132,22 @@ __device__ __forceinline__ void to_lds4(const void* src, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" :: "v"(src), "{m0}"(lds) : "memory");
 }
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// Register values loaded before a loop of direct loads: the compiler counts only its own
+// loads, so a wait it places before a later use (in every unrolled tile whose guard it cannot
+// resolve) would also hold for the direct loads in flight and drain the ring. Passing the
+// values through an empty asm makes that asm their last definition: the compiler waits for
+// their loads once, there, and never again.
+template <class T>
+__device__ __forceinline__ void settle(T& v) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 16, "a dword or a 16-byte vector");
+  if constexpr (sizeof(T) == 4) {
+    asm volatile("" : "+v"(v));
+  } else {
+    u32x4 x = __builtin_bit_cast(u32x4, v);
+    asm volatile("" : "+v"(x));
+    v = __builtin_bit_cast(T, x);
+  }
+}
 
 // Modes. kPlain: each query's keys are contiguous rows of its sequence. kCand (candidate-
 // bounded re-scoring): the score row is in slot order, entry 8i + r belonging to position
@@ -648,6 +664,19 @@ __global__ __launch_bounds__(kDThreads, 2) void indexer_group_kernel(IndexerArgs
     }
   }
 
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      settle(wq[j][i]);
+      settle(qa[j][i]);
+    }
+  }
+#pragma unroll
+  for (int k2 = 0; k2 < TPW / 16; ++k2)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) settle(sv[k2][e]);
+
   int rr[NK], qq[NK];
 #pragma unroll
   for (int j = 0; j < NK; ++j) {
@@ -846,6 +875,14 @@ __global__ __launch_bounds__(kDThreads, 2) void indexer_group_mx_kernel(IndexerA
       const uint16_t* row = reinterpret_cast<const uint16_t*>(a.q_idx) + ((int64_t)tq * kIdxHeads + c) * kIdxDim;
 #pragma unroll
       for (int s2 = 0; s2 < 4; ++s2) qa[j][s2] = *reinterpret_cast<const bf16x8*>(row + kdim_mx(g, s2));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      settle(wq[j][i]);
+      settle(qa[j][i]);
     }
   }
   // tile load: lane -> row lane / 4, position lane % 4 holds chunk mx_pos(row, position)

@@ -37,14 +37,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
-// Four OCP e4m3 codes (one dword) -> four bf16 values in two dwords. Exact: every
-// e4m3 value is a bf16 value, so the fp32 result of the hardware conversion
-// is truncated to its upper half.
+// Four OCP e4m3 codes (one dword) -> four bf16 values in two dwords, codes 0-1 in the
+// first (code 0 in its low half), 2-3 in the second. Exact: every e4m3 value, subnormals
+// included, is a bf16 value, so the hardware's scaled conversion with scale 1 returns it
+// unchanged (one instruction per pair of codes).
 __device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t codes, uint32_t& lo, uint32_t& hi) {
-  auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(codes, false);
-  auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(codes, true);
-  lo = __builtin_amdgcn_perm(__float_as_uint(f01[1]), __float_as_uint(f01[0]), 0x07060302u);
-  hi = __builtin_amdgcn_perm(__float_as_uint(f23[1]), __float_as_uint(f23[0]), 0x07060302u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, false));
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, true));
 }
 
 // E8M0 code -> fp32 scale 2^(e-127) (e = 0 is the fp32 subnormal 2^-127, 255 is NaN).
