@@ -630,9 +630,33 @@ __global__ __launch_bounds__(kDThreads, 2) void indexer_group_kernel(IndexerArgs
       pgreg = (int)page_of(a.pages, sq, min(key0 + 16 * min(lane, TPW - 1), nmax - 1));
   }
 
-  // Head weights, e4m3 row scales (4 consecutive keys per lane per 256) and the A operands, in this
-  // order, before the first ring loads: the compiler waits for the A operands at the first
-  // MFMA, which then also covers the first D tiles (loads complete in order).
+  int rr[NK], qq[NK];
+#pragma unroll
+  for (int j = 0; j < NK; ++j) {
+    const int r = j * (64 / DT::CPR) + lane / DT::CPR;
+    rr[j] = r;
+    qq[j] = DT::pos(r, lane % DT::CPR);
+  }
+  const uint32_t ring0 = (uint32_t)(uintptr_t)&ring[wave][0];
+  auto issue = [&](int i, bool after_reads) {
+    const int k = key0 + 16 * i;
+    const uint8_t* tb = keys + (PAGED ? pool_row(a.pages, __builtin_amdgcn_readlane(pgreg, i), k) : (int64_t)k) * RB;
+    const int last = nmax - 1 - k;   // rows past the group's last key repeat that row
+    const uint32_t lds = ring0 + (uint32_t)((i & (D - 1)) * TB);
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const uint8_t* src = tb + (min(rr[j], last) * RB + qq[j] * 16);
+      if (j == 0 && after_reads) to_lds16_after_reads(src, lds + 1024 * j);
+      else to_lds16(src, lds + 1024 * j);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+    if (u < live) issue(u, false);
+
+  // Head weights, e4m3 row scales (4 consecutive keys per lane per 256) and the A operands,
+  // after the first D tiles' loads (their latencies overlap); waiting for them (settle)
+  // then also covers those tiles, as loads complete in order.
   float wq[G][4];
   float sv[TPW / 16][4] = {};
   bf16x8 qa[G][4];
@@ -676,30 +700,6 @@ __global__ __launch_bounds__(kDThreads, 2) void indexer_group_kernel(IndexerArgs
   for (int k2 = 0; k2 < TPW / 16; ++k2)
 #pragma unroll
     for (int e = 0; e < 4; ++e) settle(sv[k2][e]);
-
-  int rr[NK], qq[NK];
-#pragma unroll
-  for (int j = 0; j < NK; ++j) {
-    const int r = j * (64 / DT::CPR) + lane / DT::CPR;
-    rr[j] = r;
-    qq[j] = DT::pos(r, lane % DT::CPR);
-  }
-  const uint32_t ring0 = (uint32_t)(uintptr_t)&ring[wave][0];
-  auto issue = [&](int i, bool after_reads) {
-    const int k = key0 + 16 * i;
-    const uint8_t* tb = keys + (PAGED ? pool_row(a.pages, __builtin_amdgcn_readlane(pgreg, i), k) : (int64_t)k) * RB;
-    const int last = nmax - 1 - k;   // rows past the group's last key repeat that row
-    const uint32_t lds = ring0 + (uint32_t)((i & (D - 1)) * TB);
-#pragma unroll
-    for (int j = 0; j < NK; ++j) {
-      const uint8_t* src = tb + (min(rr[j], last) * RB + qq[j] * 16);
-      if (j == 0 && after_reads) to_lds16_after_reads(src, lds + 1024 * j);
-      else to_lds16(src, lds + 1024 * j);
-    }
-  };
-#pragma unroll
-  for (int u = 0; u < D; ++u)
-    if (u < live) issue(u, false);
 
   uint32_t roff[NK];
 #pragma unroll
@@ -853,37 +853,14 @@ __global__ __launch_bounds__(kDThreads, 2) void indexer_group_mx_kernel(IndexerA
     else return x;
   };
 
-  // head weights, then the wave's block scales (direct loads, one key's 4 bytes per lane),
-  // then the A operands: the compiler's wait for the A operands at the first MFMA covers
-  // the scales and the first D tiles (loads complete in order)
-  float wq[G][4];
-  bf16x8 qa[G][4];
+  // the wave's block scales (direct loads, one key's 4 bytes per lane), then the first D
+  // tiles, then the head weights and the A operands; waiting for those (settle) covers
+  // everything before them, as loads complete in order
   if (live > 0) {
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const int tq = t0 + min(j, gs - 1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) wq[j][i] = a.w[(int64_t)tq * kIdxHeads + 4 * g + i];
-    }
 #pragma unroll
     for (int j = 0; j < TPW / 4; ++j)
       to_lds4(scales + krow(min(key0 + 64 * j + lane, nmax - 1)) * 4,
               (uint32_t)(uintptr_t)&sh.scale[wave][256 * j]);
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const int tq = t0 + min(j, gs - 1);
-      const uint16_t* row = reinterpret_cast<const uint16_t*>(a.q_idx) + ((int64_t)tq * kIdxHeads + c) * kIdxDim;
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) qa[j][s2] = *reinterpret_cast<const bf16x8*>(row + kdim_mx(g, s2));
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < G; ++j) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      settle(wq[j][i]);
-      settle(qa[j][i]);
-    }
   }
   // tile load: lane -> row lane / 4, position lane % 4 holds chunk mx_pos(row, position)
   const int rr = lane >> 2, qq = mx_pos(rr, lane & 3);
@@ -902,6 +879,32 @@ __global__ __launch_bounds__(kDThreads, 2) void indexer_group_mx_kernel(IndexerA
 #pragma unroll
   for (int u = 0; u < D; ++u)
     if (u < live) issue(u, false);
+
+  float wq[G][4];
+  bf16x8 qa[G][4];
+  if (live > 0) {
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int tq = t0 + min(j, gs - 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wq[j][i] = a.w[(int64_t)tq * kIdxHeads + 4 * g + i];
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const int tq = t0 + min(j, gs - 1);
+      const uint16_t* row = reinterpret_cast<const uint16_t*>(a.q_idx) + ((int64_t)tq * kIdxHeads + c) * kIdxDim;
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) qa[j][s2] = *reinterpret_cast<const bf16x8*>(row + kdim_mx(g, s2));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      settle(wq[j][i]);
+      settle(qa[j][i]);
+    }
+  }
 
   const uint32_t roff = (uint32_t)(c * RB + mx_pos(c, g) * 16);
   float r4[TPW][N4 > 0 ? N4 : 1];
