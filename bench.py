@@ -219,8 +219,8 @@ def run_batch(torch, d, steps, warmup, min_warm_s=0.5):
 
 def run_plain(torch, d, steps):
     """`steps` eager steps launched back to back on one stream (no events between stages),
-    bracketed by device synchronisation."""
-    fns = [d.compress, d.index, d.select, d.attend]
+    bracketed by device synchronisation; the compressor rides in the indexer's launch."""
+    fns = d.step_fns()
     for _ in range(3):
         for f in fns:
             f()
@@ -404,7 +404,7 @@ def run_alternating(torch, ds, steps):
     """Plain launches back to back, each step on the next of `ds` (copies of one batch in
     separate memory) in turn, so no step finds the previous step's stores in cache.
     Returns seconds per step."""
-    fns = [[d.compress, d.index, d.select, d.attend] for d in ds]
+    fns = [d.step_fns() for d in ds]
     for i in range(3 * len(ds)):
         for f in fns[i % len(ds)]:
             f()

@@ -244,6 +244,37 @@ sa_status indexer_score(const sa_plan* plan, const sa_queries* queries, const sa
                         const void* q_idx, const float* w, float* scores, int64_t ld_scores,
                         float* block_max, int64_t ld_block_max, void* stream);
 
+/* S0 + S1 in one launch (a decode step compresses the group each query completes, the
+ * softmax-gate pooling of "deepseek-ai/DeepSeek-V4.1-Flash" recipe, Overview, two-tier
+ * sparse attention bullet, and scores the index keys of that same bullet's indexer).
+ * The compressor's work-groups ride in the indexer's grid (extra rows after the queries'),
+ * so the step needs one launch fewer. A job holds the arguments of sparse_attn_compress
+ * (bf16 plans) or of sparse_attn_compress_codes (e4m3 and MXFP4 plans), with their meaning
+ * and rules; out_scales and scales_group_stride are read for code-row plans only. */
+typedef struct sa_compress_job {
+  const void* raw;
+  int64_t raw_group_stride;
+  const void* gate;
+  int64_t gate_group_stride;
+  const float* slot_bias;
+  void* out;
+  int64_t out_group_stride;
+  void* out_scales;
+  int64_t scales_group_stride;
+  int64_t G;
+} sa_compress_job;
+
+/* Results: those of the compressor with *job's arguments followed by indexer_score with
+ * the others, on `stream`, with the same checks and errors (nothing is enqueued when any
+ * check fails). The job's outputs must not overlap anything the indexer reads or writes.
+ * job NULL or job->G = 0: indexer_score. Ragged batches (sa_queries.runs) take the job in
+ * their first launch; a job whose rows would not fit the grid, or a batch with no visible
+ * keys, runs it in a launch of its own, first. */
+sa_status indexer_score_compress(const sa_plan* plan, const sa_queries* queries, const sa_cache* cache,
+                                 const void* q_idx, const float* w, float* scores, int64_t ld_scores,
+                                 float* block_max, int64_t ld_block_max, const sa_compress_job* job,
+                                 void* stream);
+
 /* S2 + S3. Candidate blocks, then the top-512 positions inside them.
  *   scores, ld_scores      as written by indexer_score (same limits on the strides)
  *   block_max              as written by indexer_score, or NULL (then the block

@@ -2,10 +2,10 @@
 
 Argument marshalling only. Every stage runs in the library's HIP kernels; torch is used
 for device memory and the current stream. The entry points have the names of the C ABI
-(include/sparse_attn.h): sparse_attn_plan, indexer_score, indexer_score_cand, select_topk,
-select_topk_cand, sparse_attn_fwd, sparse_attn_fwd_noalloc, sparse_attn_compress,
-sparse_attn_compress_codes. If the
-built library is missing, importing this package raises.
+(include/sparse_attn.h): sparse_attn_plan, indexer_score, indexer_score_compress,
+indexer_score_cand, select_topk, select_topk_cand, sparse_attn_fwd, sparse_attn_fwd_noalloc,
+sparse_attn_compress, sparse_attn_compress_codes. If the built library is missing, importing
+this package raises.
 """
 from __future__ import annotations
 
@@ -30,7 +30,7 @@ STATUS_NAMES = {0: "SA_OK", 1: "SA_EINVAL", 2: "SA_EUNSUPPORTED", 3: "SA_EWORKSP
 EXPORTS = ("sparse_attn_plan", "sparse_attn_plan_destroy", "sparse_attn_last_error",
            "sparse_attn_workspace_init", "indexer_score", "select_topk", "indexer_score_cand",
            "select_topk_cand", "sparse_attn_fwd", "sparse_attn_fwd_noalloc", "sparse_attn_compress",
-           "sparse_attn_compress_codes")
+           "sparse_attn_compress_codes", "indexer_score_compress")
 
 
 class sa_params(ctypes.Structure):
@@ -68,6 +68,13 @@ class SparseAttnError(RuntimeError):
         self.status = status
 
 
+class sa_compress_job(ctypes.Structure):
+    _fields_ = [("raw", ctypes.c_void_p), ("raw_group_stride", ctypes.c_int64),
+                ("gate", ctypes.c_void_p), ("gate_group_stride", ctypes.c_int64),
+                ("slot_bias", ctypes.c_void_p), ("out", ctypes.c_void_p), ("out_group_stride", ctypes.c_int64),
+                ("out_scales", ctypes.c_void_p), ("scales_group_stride", ctypes.c_int64), ("G", ctypes.c_int64)]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
@@ -102,6 +109,9 @@ def _load():
     lib.sparse_attn_compress.restype = ctypes.c_int
     lib.sparse_attn_compress_codes.argtypes = [vp, vp, i64, vp, i64, vp, vp, i64, vp, i64, i64, vp]
     lib.sparse_attn_compress_codes.restype = ctypes.c_int
+    lib.indexer_score_compress.argtypes = [vp, ctypes.POINTER(sa_queries), ctypes.POINTER(sa_cache), vp, vp,
+                                           vp, i64, vp, i64, ctypes.POINTER(sa_compress_job), vp]
+    lib.indexer_score_compress.restype = ctypes.c_int
     return lib
 
 
@@ -156,6 +166,7 @@ class Plan:
         self.params = p
         self.workspace_bytes = ws.value
         self.key_dtype = key_dtype
+        self.kv_dtype = kv_dtype
         self.ratio = ratio
 
     def __del__(self, _destroy=lib.sparse_attn_plan_destroy):
@@ -276,6 +287,50 @@ def indexer_score(plan: Plan, queries: Queries, cache: Cache, q_idx: torch.Tenso
                              _ptr(q_idx), _ptr(w), _ptr(scores), scores.stride(0),
                              _ptr(block_max), 0 if block_max is None else block_max.stride(0),
                              _stream(stream)))
+
+
+class CompressJob:
+    """A compressor job for indexer_score_compress: the arguments of sparse_attn_compress (bf16
+    plans; strides in bf16 elements) or sparse_attn_compress_codes (code-row plans: out and
+    out_scales strides in bytes). Tensors are passed as base pointers and kept alive here."""
+
+    def __init__(self, raw: torch.Tensor, raw_group_stride: int, gate: Optional[torch.Tensor],
+                 gate_group_stride: int, slot_bias: Optional[torch.Tensor], out: torch.Tensor,
+                 out_group_stride: int, G: int, out_scales: Optional[torch.Tensor] = None,
+                 scales_group_stride: int = 0):
+        for t, name in ((raw, "raw"), (gate, "gate")):
+            if t is not None and (t.dtype != torch.bfloat16 or not t.is_cuda):
+                raise TypeError(f"{name}: expected a bfloat16 device tensor")
+        if not out.is_cuda or out.dtype not in (torch.bfloat16, torch.uint8):
+            raise TypeError("out: expected a bfloat16 (bf16 rows) or uint8 (code rows) device tensor")
+        if slot_bias is not None:
+            _need(slot_bias, "slot_bias", torch.float32)
+        if out_scales is not None and (out_scales.dtype not in (torch.float32, torch.uint8) or not out_scales.is_cuda):
+            raise TypeError("out_scales: expected a float32 (e4m3) or uint8 (MXFP4) device tensor")
+        j = sa_compress_job()
+        j.raw, j.raw_group_stride = _ptr(raw), raw_group_stride
+        j.gate, j.gate_group_stride = _ptr(gate), gate_group_stride
+        j.slot_bias = _ptr(slot_bias)
+        j.out, j.out_group_stride = _ptr(out), out_group_stride
+        j.out_scales, j.scales_group_stride = _ptr(out_scales), scales_group_stride
+        j.G = G
+        self._keep = (raw, gate, slot_bias, out, out_scales)
+        self.c = j
+
+
+def indexer_score_compress(plan: Plan, queries: Queries, cache: Cache, q_idx: torch.Tensor, w: torch.Tensor,
+                           scores: torch.Tensor, block_max: Optional[torch.Tensor], job: Optional[CompressJob],
+                           stream=None):
+    """indexer_score with a compressor job in the same launch (job None: indexer_score)."""
+    _need(q_idx, "q_idx", torch.bfloat16)
+    _need(w, "w", torch.float32)
+    _need(scores, "scores", torch.float32)
+    if block_max is not None:
+        _need(block_max, "block_max", torch.float32)
+    _check(lib.indexer_score_compress(plan.handle, ctypes.byref(queries.c), ctypes.byref(cache.c),
+                                      _ptr(q_idx), _ptr(w), _ptr(scores), scores.stride(0),
+                                      _ptr(block_max), 0 if block_max is None else block_max.stride(0),
+                                      None if job is None else ctypes.byref(job.c), _stream(stream)))
 
 
 def indexer_score_cand(plan: Plan, queries: Queries, cache: Cache, q_idx: torch.Tensor,

@@ -294,6 +294,7 @@ sa_status indexer_runs(const sa::IndexerArgs& a, const sa_queries* q, const sa_c
   }
   for (RunCursor cur{q, chunk_ok, group_ok}; cur.next(r);) {
     sa::IndexerArgs b = a;
+    if (r.t0 > 0) b.cj.G = 0;   // a compressor job rides in the first launch only
     b.seq_id = a.seq_id + r.t0;
     b.pos = a.pos + r.t0;
     b.T = r.len;
@@ -354,6 +355,124 @@ sa_status attn_args(const sa_plan* plan, const sa_queries* q, const sa_cache* c,
   return ok();
 }
 
+// Checks of a compressor job (the arguments of sparse_attn_compress for bf16 plans, of
+// sparse_attn_compress_codes for code-row plans); fills a.
+sa_status compress_args(const sa_plan* plan, const void* raw, int64_t raw_group_stride, const void* gate,
+                        int64_t gate_group_stride, const float* slot_bias, void* out, int64_t out_group_stride,
+                        void* out_scales, int64_t scales_group_stride, int64_t G, sa::CompressArgs& a) {
+  const int r = plan->p.ratio;
+  const int kv = plan->p.kv_dtype;
+  SA_REQUIRE(G >= 0 && G <= ((int64_t)1 << 31) - 1, SA_EINVAL, "G = %lld out of range", (long long)G);
+  SA_REQUIRE(raw && aligned16(raw) && out && aligned16(out), SA_EINVAL,
+             "raw / out NULL or not 16-byte aligned");
+  SA_REQUIRE(raw_group_stride >= (int64_t)r * 512 && raw_group_stride % 8 == 0, SA_EINVAL,
+             "raw_group_stride = %lld invalid", (long long)raw_group_stride);
+  if (kv == SA_KV_BF16) {
+    SA_REQUIRE(out_group_stride >= 512 && out_group_stride % 8 == 0, SA_EINVAL,
+               "out_group_stride = %lld invalid", (long long)out_group_stride);
+  } else {
+    const int64_t row = kv == SA_KV_MXFP4 ? 256 : 512, srow = kv == SA_KV_MXFP4 ? 16 : 4;
+    SA_REQUIRE(out_group_stride >= row && out_group_stride % 16 == 0, SA_EINVAL,
+               "out_group_stride = %lld bytes must be >= %lld and a multiple of 16", (long long)out_group_stride,
+               (long long)row);
+    SA_REQUIRE(out_scales && reinterpret_cast<uintptr_t>(out_scales) % 4 == 0, SA_EINVAL,
+               "out_scales NULL or not 4-byte aligned");
+    SA_REQUIRE(scales_group_stride >= srow && scales_group_stride % 4 == 0, SA_EINVAL,
+               "scales_group_stride = %lld bytes must be >= %lld and a multiple of 4",
+               (long long)scales_group_stride, (long long)srow);
+  }
+  if (r == 2) {
+    SA_REQUIRE(gate && aligned16(gate) && slot_bias && aligned16(slot_bias), SA_EINVAL,
+               "gate / slot_bias NULL or not 16-byte aligned");
+    SA_REQUIRE(gate_group_stride >= 1024 && gate_group_stride % 8 == 0, SA_EINVAL,
+               "gate_group_stride = %lld invalid", (long long)gate_group_stride);
+  }
+  if (G > 0)
+    log_call("compressor: %lld groups of %d rows into %s rows", (long long)G, r,
+             kv == SA_KV_MXFP4 ? "mxfp4" : kv == SA_KV_FP8_E4M3 ? "e4m3" : "bf16");
+  a.raw = raw;
+  a.raw_stride = raw_group_stride;
+  a.gate = gate;
+  a.gate_stride = gate_group_stride;
+  a.bias = slot_bias;
+  a.out = out;
+  a.out_stride = out_group_stride;
+  a.G = G;
+  a.ratio = r;
+  a.kv_mode = kv;
+  a.scales = kv == SA_KV_BF16 ? nullptr : out_scales;
+  a.scales_stride = kv == SA_KV_BF16 ? 0 : scales_group_stride;
+  return ok();
+}
+
+// indexer_score, with an optional compressor job (already checked) riding in its launch.
+sa_status indexer_common(const sa_plan* plan, const sa_queries* q, const sa_cache* c, const void* q_idx,
+                         const float* w, float* scores, int64_t ld_scores, float* block_max,
+                         int64_t ld_block_max, const sa::CompressArgs* cj, void* stream) {
+  sa_status st;
+  if ((st = check_plan(plan)) != SA_OK) return st;
+  if ((st = check_queries(plan, q)) != SA_OK) return st;
+  if ((st = check_cache(plan, q, c, true, false)) != SA_OK) return st;
+  SA_REQUIRE(q_idx && aligned16(q_idx) && w && aligned16(w), SA_EINVAL,
+             "q_idx / w NULL or not 16-byte aligned");
+  SA_REQUIRE(scores && aligned16(scores), SA_EINVAL, "scores NULL or not 16-byte aligned");
+  const int64_t E = round8(q->max_visible);
+  SA_REQUIRE(ld_scores >= E && ld_scores % 4 == 0 && ld_scores <= kMaxLd, SA_EINVAL,
+             "ld_scores = %lld must be >= %lld (max_visible rounded up to 8), <= %lld and a multiple of 4",
+             (long long)ld_scores, (long long)E, (long long)kMaxLd);
+  if (block_max) {
+    SA_REQUIRE(aligned16(block_max), SA_EINVAL, "block_max not 16-byte aligned");
+    SA_REQUIRE(ld_block_max >= E / 8 && ld_block_max % 4 == 0 && ld_block_max <= kMaxLd, SA_EINVAL,
+               "ld_block_max = %lld must be >= %lld, <= %lld and a multiple of 4",
+               (long long)ld_block_max, (long long)(E / 8), (long long)kMaxLd);
+  }
+  if (E == 0) {
+    if (!cj) return ok();
+    return hip_status(sa::launch_compress(*cj, (hipStream_t)stream), "indexer_score_compress launch");
+  }
+  sa::IndexerArgs a;
+  a.seq_id = q->seq_id;
+  a.pos = q->pos;
+  a.T = q->T;
+  a.max_visible = q->max_visible;
+  a.num_seqs = c->num_seqs;
+  a.compressed_cap = c->compressed_cap;
+  a.ratio = plan->p.ratio;
+  a.fp8 = plan->p.idx_key_dtype == SA_KEY_FP8_E4M3;
+  a.mxfp4 = plan->p.idx_key_dtype == SA_KEY_MXFP4;
+  a.q_idx = q_idx;
+  a.w = w;
+  a.keys = c->idx_keys;
+  a.keys_seq_stride = c->idx_keys_seq_stride;
+  a.scales = static_cast<const float*>(c->idx_scales);
+  a.scales_seq_stride = c->idx_scales_seq_stride;
+  a.scores = scores;
+  a.ld_scores = ld_scores;
+  a.block_max = block_max;
+  a.ld_block_max = ld_block_max;
+  a.E = E;
+  a.cand = nullptr;
+  a.group = q->group > 1 ? q->group : 1;
+  a.pages = page_table(c);
+  if (cj) a.cj = *cj;   // its work-groups join the (first) indexer launch
+  // paged stores: the chunk kernel needs pages of at least one 64-key stage
+  // Queries that share a sequence in one call (a prefill chunk) reuse each key tile
+  // across many queries; groups of a multi-token decode step share one key stream per
+  // group; independent decode queries each stream their own keys.
+  if (q->runs) return indexer_runs(a, q, c, q_idx, w, (hipStream_t)stream);
+  const bool prefill = (!a.pages.table || c->page_size >= 64) && a.group == 1 && c->num_seqs == 1 && q->T > 1;
+  SA_REQUIRE(prefill || (q->T + a.group - 1) / a.group <= kMaxGridY, SA_EUNSUPPORTED,
+             "T = %lld queries in groups of %d over several sequences: at most 65535 groups per call",
+             (long long)q->T, (int)a.group);
+  SA_REQUIRE(!prefill || (q->T + sa::kChunkQueriesPerWG - 1) / sa::kChunkQueriesPerWG <= kMaxGridY,
+             SA_EUNSUPPORTED, "T = %lld queries of one sequence: at most %lld per call", (long long)q->T,
+             (long long)(kMaxGridY * sa::kChunkQueriesPerWG));
+  log_call("indexer_score: T=%lld max_visible=%lld E=%lld keys=%s %s%s kernel, group %d", (long long)q->T,
+           (long long)q->max_visible, (long long)E, a.mxfp4 ? "mxfp4" : a.fp8 ? "e4m3" : "bf16",
+           a.pages.table ? "paged " : "", prefill ? "chunk" : a.group > 1 ? "group" : "per-query", (int)a.group);
+  return hip_status(sa::launch_indexer(a, prefill, (hipStream_t)stream), "indexer_score launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -396,64 +515,7 @@ void sparse_attn_plan_destroy(sa_plan* plan) { delete plan; }
 sa_status indexer_score(const sa_plan* plan, const sa_queries* q, const sa_cache* c,
                         const void* q_idx, const float* w, float* scores, int64_t ld_scores,
                         float* block_max, int64_t ld_block_max, void* stream) {
-  sa_status st;
-  if ((st = check_plan(plan)) != SA_OK) return st;
-  if ((st = check_queries(plan, q)) != SA_OK) return st;
-  if ((st = check_cache(plan, q, c, true, false)) != SA_OK) return st;
-  SA_REQUIRE(q_idx && aligned16(q_idx) && w && aligned16(w), SA_EINVAL,
-             "q_idx / w NULL or not 16-byte aligned");
-  SA_REQUIRE(scores && aligned16(scores), SA_EINVAL, "scores NULL or not 16-byte aligned");
-  const int64_t E = round8(q->max_visible);
-  SA_REQUIRE(ld_scores >= E && ld_scores % 4 == 0 && ld_scores <= kMaxLd, SA_EINVAL,
-             "ld_scores = %lld must be >= %lld (max_visible rounded up to 8), <= %lld and a multiple of 4",
-             (long long)ld_scores, (long long)E, (long long)kMaxLd);
-  if (block_max) {
-    SA_REQUIRE(aligned16(block_max), SA_EINVAL, "block_max not 16-byte aligned");
-    SA_REQUIRE(ld_block_max >= E / 8 && ld_block_max % 4 == 0 && ld_block_max <= kMaxLd, SA_EINVAL,
-               "ld_block_max = %lld must be >= %lld, <= %lld and a multiple of 4",
-               (long long)ld_block_max, (long long)(E / 8), (long long)kMaxLd);
-  }
-  if (E == 0) return ok();
-  sa::IndexerArgs a;
-  a.seq_id = q->seq_id;
-  a.pos = q->pos;
-  a.T = q->T;
-  a.max_visible = q->max_visible;
-  a.num_seqs = c->num_seqs;
-  a.compressed_cap = c->compressed_cap;
-  a.ratio = plan->p.ratio;
-  a.fp8 = plan->p.idx_key_dtype == SA_KEY_FP8_E4M3;
-  a.mxfp4 = plan->p.idx_key_dtype == SA_KEY_MXFP4;
-  a.q_idx = q_idx;
-  a.w = w;
-  a.keys = c->idx_keys;
-  a.keys_seq_stride = c->idx_keys_seq_stride;
-  a.scales = static_cast<const float*>(c->idx_scales);
-  a.scales_seq_stride = c->idx_scales_seq_stride;
-  a.scores = scores;
-  a.ld_scores = ld_scores;
-  a.block_max = block_max;
-  a.ld_block_max = ld_block_max;
-  a.E = E;
-  a.cand = nullptr;
-  a.group = q->group > 1 ? q->group : 1;
-  a.pages = page_table(c);
-  // paged stores: the chunk kernel needs pages of at least one 64-key stage
-  // Queries that share a sequence in one call (a prefill chunk) reuse each key tile
-  // across many queries; groups of a multi-token decode step share one key stream per
-  // group; independent decode queries each stream their own keys.
-  if (q->runs) return indexer_runs(a, q, c, q_idx, w, (hipStream_t)stream);
-  const bool prefill = (!a.pages.table || c->page_size >= 64) && a.group == 1 && c->num_seqs == 1 && q->T > 1;
-  SA_REQUIRE(prefill || (q->T + a.group - 1) / a.group <= kMaxGridY, SA_EUNSUPPORTED,
-             "T = %lld queries in groups of %d over several sequences: at most 65535 groups per call",
-             (long long)q->T, (int)a.group);
-  SA_REQUIRE(!prefill || (q->T + sa::kChunkQueriesPerWG - 1) / sa::kChunkQueriesPerWG <= kMaxGridY,
-             SA_EUNSUPPORTED, "T = %lld queries of one sequence: at most %lld per call", (long long)q->T,
-             (long long)(kMaxGridY * sa::kChunkQueriesPerWG));
-  log_call("indexer_score: T=%lld max_visible=%lld E=%lld keys=%s %s%s kernel, group %d", (long long)q->T,
-           (long long)q->max_visible, (long long)E, a.mxfp4 ? "mxfp4" : a.fp8 ? "e4m3" : "bf16",
-           a.pages.table ? "paged " : "", prefill ? "chunk" : a.group > 1 ? "group" : "per-query", (int)a.group);
-  return hip_status(sa::launch_indexer(a, prefill, (hipStream_t)stream), "indexer_score launch");
+  return indexer_common(plan, q, c, q_idx, w, scores, ld_scores, block_max, ld_block_max, nullptr, stream);
 }
 
 sa_status indexer_score_cand(const sa_plan* plan, const sa_queries* q, const sa_cache* c,
@@ -663,39 +725,14 @@ sa_status sparse_attn_compress(const sa_plan* plan, const void* raw, int64_t raw
                                int64_t G, void* stream) {
   sa_status st;
   if ((st = check_plan(plan)) != SA_OK) return st;
-  const int r = plan->p.ratio;
   SA_REQUIRE(plan->p.kv_dtype == SA_KV_BF16, SA_EUNSUPPORTED,
              "sparse_attn_compress writes bf16 rows (plan kv_dtype is e4m3 or MXFP4: use "
              "sparse_attn_compress_codes)");
-  SA_REQUIRE(G >= 0, SA_EINVAL, "G = %lld < 0", (long long)G);
-  SA_REQUIRE(raw && aligned16(raw) && out && aligned16(out), SA_EINVAL,
-             "raw / out NULL or not 16-byte aligned");
-  SA_REQUIRE(raw_group_stride >= (int64_t)r * 512 && raw_group_stride % 8 == 0, SA_EINVAL,
-             "raw_group_stride = %lld invalid", (long long)raw_group_stride);
-  SA_REQUIRE(out_group_stride >= 512 && out_group_stride % 8 == 0, SA_EINVAL,
-             "out_group_stride = %lld invalid", (long long)out_group_stride);
-  if (r == 2) {
-    SA_REQUIRE(gate && aligned16(gate) && slot_bias && aligned16(slot_bias), SA_EINVAL,
-               "gate / slot_bias NULL or not 16-byte aligned");
-    SA_REQUIRE(gate_group_stride >= 1024 && gate_group_stride % 8 == 0, SA_EINVAL,
-               "gate_group_stride = %lld invalid", (long long)gate_group_stride);
-  }
-  if (G == 0) return ok();
-  log_call("compressor: %lld groups of %d rows into %s rows", (long long)G, r,
-           plan->p.kv_dtype == SA_KV_MXFP4 ? "mxfp4" : plan->p.kv_dtype == SA_KV_FP8_E4M3 ? "e4m3" : "bf16");
   sa::CompressArgs a;
-  a.raw = raw;
-  a.raw_stride = raw_group_stride;
-  a.gate = gate;
-  a.gate_stride = gate_group_stride;
-  a.bias = slot_bias;
-  a.out = out;
-  a.out_stride = out_group_stride;
-  a.G = G;
-  a.ratio = r;
-  a.kv_mode = 0;
-  a.scales = nullptr;
-  a.scales_stride = 0;
+  if ((st = compress_args(plan, raw, raw_group_stride, gate, gate_group_stride, slot_bias, out, out_group_stride,
+                          nullptr, 0, G, a)) != SA_OK)
+    return st;
+  if (G == 0) return ok();
   return hip_status(sa::launch_compress(a, (hipStream_t)stream), "sparse_attn_compress launch");
 }
 
@@ -706,47 +743,30 @@ sa_status sparse_attn_compress_codes(const sa_plan* plan, const void* raw, int64
                                      void* stream) {
   sa_status st;
   if ((st = check_plan(plan)) != SA_OK) return st;
-  const int r = plan->p.ratio;
-  const int kv = plan->p.kv_dtype;
-  SA_REQUIRE(kv == SA_KV_FP8_E4M3 || kv == SA_KV_MXFP4, SA_EUNSUPPORTED,
+  SA_REQUIRE(plan->p.kv_dtype == SA_KV_FP8_E4M3 || plan->p.kv_dtype == SA_KV_MXFP4, SA_EUNSUPPORTED,
              "sparse_attn_compress_codes needs a plan with e4m3 or MXFP4 latents (plan kv_dtype is bf16)");
-  SA_REQUIRE(G >= 0 && G <= ((int64_t)1 << 31) - 1, SA_EINVAL, "G = %lld out of range", (long long)G);
-  SA_REQUIRE(raw && aligned16(raw) && out && aligned16(out), SA_EINVAL,
-             "raw / out NULL or not 16-byte aligned");
-  SA_REQUIRE(raw_group_stride >= (int64_t)r * 512 && raw_group_stride % 8 == 0, SA_EINVAL,
-             "raw_group_stride = %lld invalid", (long long)raw_group_stride);
-  const int64_t row = kv == SA_KV_MXFP4 ? 256 : 512, srow = kv == SA_KV_MXFP4 ? 16 : 4;
-  SA_REQUIRE(out_group_stride >= row && out_group_stride % 16 == 0, SA_EINVAL,
-             "out_group_stride = %lld bytes must be >= %lld and a multiple of 16", (long long)out_group_stride,
-             (long long)row);
-  SA_REQUIRE(out_scales && reinterpret_cast<uintptr_t>(out_scales) % 4 == 0, SA_EINVAL,
-             "out_scales NULL or not 4-byte aligned");
-  SA_REQUIRE(scales_group_stride >= srow && scales_group_stride % 4 == 0, SA_EINVAL,
-             "scales_group_stride = %lld bytes must be >= %lld and a multiple of 4",
-             (long long)scales_group_stride, (long long)srow);
-  if (r == 2) {
-    SA_REQUIRE(gate && aligned16(gate) && slot_bias && aligned16(slot_bias), SA_EINVAL,
-               "gate / slot_bias NULL or not 16-byte aligned");
-    SA_REQUIRE(gate_group_stride >= 1024 && gate_group_stride % 8 == 0, SA_EINVAL,
-               "gate_group_stride = %lld invalid", (long long)gate_group_stride);
-  }
-  if (G == 0) return ok();
-  log_call("compressor: %lld groups of %d rows into %s rows", (long long)G, r,
-           plan->p.kv_dtype == SA_KV_MXFP4 ? "mxfp4" : plan->p.kv_dtype == SA_KV_FP8_E4M3 ? "e4m3" : "bf16");
   sa::CompressArgs a;
-  a.raw = raw;
-  a.raw_stride = raw_group_stride;
-  a.gate = gate;
-  a.gate_stride = gate_group_stride;
-  a.bias = slot_bias;
-  a.out = out;
-  a.out_stride = out_group_stride;
-  a.G = G;
-  a.ratio = r;
-  a.kv_mode = kv;
-  a.scales = out_scales;
-  a.scales_stride = scales_group_stride;
+  if ((st = compress_args(plan, raw, raw_group_stride, gate, gate_group_stride, slot_bias, out, out_group_stride,
+                          out_scales, scales_group_stride, G, a)) != SA_OK)
+    return st;
+  if (G == 0) return ok();
   return hip_status(sa::launch_compress(a, (hipStream_t)stream), "sparse_attn_compress_codes launch");
+}
+
+sa_status indexer_score_compress(const sa_plan* plan, const sa_queries* q, const sa_cache* c,
+                                 const void* q_idx, const float* w, float* scores, int64_t ld_scores,
+                                 float* block_max, int64_t ld_block_max, const sa_compress_job* job,
+                                 void* stream) {
+  sa_status st;
+  if ((st = check_plan(plan)) != SA_OK) return st;
+  if (job == nullptr || job->G == 0)
+    return indexer_common(plan, q, c, q_idx, w, scores, ld_scores, block_max, ld_block_max, nullptr, stream);
+  sa::CompressArgs cj;
+  if ((st = compress_args(plan, job->raw, job->raw_group_stride, job->gate, job->gate_group_stride, job->slot_bias,
+                          job->out, job->out_group_stride, job->out_scales, job->scales_group_stride, job->G,
+                          cj)) != SA_OK)
+    return st;
+  return indexer_common(plan, q, c, q_idx, w, scores, ld_scores, block_max, ld_block_max, &cj, stream);
 }
 
 }  // extern "C"

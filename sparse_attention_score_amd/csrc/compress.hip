@@ -1,195 +1,20 @@
-// S0 softmax-gate compressor on gfx950.
-//
-// For each group of r raw latents (r = 2 in the compressing layers that collapse two
-// positions into one, "DeepSeek-V4.1 Flash" Miles docs, section 1) and each channel c:
-//   pi_k = softmax_k(gate[k][c] + bias[k][c]),   out[c] = sum_k pi_k * raw[k][c]
-// (latents "pooled by a learned softmax gate", vLLM recipe, Overview, two-tier sparse
-// attention bullet). Ratio 1 is the identity copy.
-//
-// Elementwise and HBM-bound: each thread handles 8 channels of one group with 16-byte
-// loads and stores; arithmetic in fp32, output rounded to bf16 (nearest even).
-//
-// Code rows (the FP8 and FP4 caches of "SGLang and Miles Add Day-0 Support for DeepSeek-V4.1",
-// Miles Day-0 Support table, Quantization row): one wave per
-// group quantises the fp32 row it computed. e4m3: scale s = amax / 448 over the row (1 for
-// an all-zero row), code = nearest e4m3 of x / s (ties to the even code). MXFP4: per block of
-// 32 channels, E8M0 exponent X = floor(log2 amax) - 2 (-127 for an all-zero block, clamped
-// to [-127, 127]), element = nearest E2M1 of x * 2^-X (ties to the even code, saturating at
-// 6). Divisions are IEEE fp32.
-#include "sa_device.h"
-#include "sa_launch.h"
+// S0 softmax-gate compressor kernels on gfx950: one launch over all groups. The per-group
+// arithmetic (and its sources) is in sa_compress.h, which the indexer kernels share when a
+// compressor job rides in their launch.
+#include "sa_compress.h"
 
 namespace sa {
 namespace {
 
-constexpr int kCThreads = 256;
-constexpr int kChunks = kDim / 8;  // 64 chunks of 8 channels per group
-
-__global__ __launch_bounds__(kCThreads) void compress2_kernel(CompressArgs a) {
-  const int64_t total = a.G * kChunks;
-  for (int64_t item = (int64_t)blockIdx.x * kCThreads + threadIdx.x; item < total;
-       item += (int64_t)gridDim.x * kCThreads) {
-    const int64_t grp = item / kChunks;
-    const int ch = (int)(item % kChunks) * 8;
-    const uint16_t* x = reinterpret_cast<const uint16_t*>(a.raw) + grp * a.raw_stride + ch;
-    const uint16_t* z = reinterpret_cast<const uint16_t*>(a.gate) + grp * a.gate_stride + ch;
-    const u32x4 x0 = *reinterpret_cast<const u32x4*>(x);
-    const u32x4 x1 = *reinterpret_cast<const u32x4*>(x + kDim);
-    const u32x4 z0 = *reinterpret_cast<const u32x4*>(z);
-    const u32x4 z1 = *reinterpret_cast<const u32x4*>(z + kDim);
-    const float* b0 = a.bias + ch;
-    const float* b1 = a.bias + kDim + ch;
-    u32x4 o;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      float r[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int cc = 2 * w + h;
-        const float xa = h ? bf16_hi(x0[w]) : bf16_lo(x0[w]);
-        const float xb = h ? bf16_hi(x1[w]) : bf16_lo(x1[w]);
-        const float a0 = (h ? bf16_hi(z0[w]) : bf16_lo(z0[w])) + b0[cc];
-        const float a1 = (h ? bf16_hi(z1[w]) : bf16_lo(z1[w])) + b1[cc];
-        // pi_0 = 1 / (1 + exp(a1 - a0)); out = xb + pi_0 * (xa - xb)
-        const float e = __builtin_amdgcn_exp2f((a1 - a0) * 1.4426950408889634f);
-        const float p0 = 1.0f / (1.0f + e);
-        r[h] = fmaf(p0, xa - xb, xb);
-      }
-      o[w] = pack_bf16x2(r[0], r[1]);
-    }
-    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + grp * a.out_stride + ch) = o;
-  }
-}
-
-__global__ __launch_bounds__(kCThreads) void copy1_kernel(CompressArgs a) {
-  const int64_t total = a.G * kChunks;
-  for (int64_t item = (int64_t)blockIdx.x * kCThreads + threadIdx.x; item < total;
-       item += (int64_t)gridDim.x * kCThreads) {
-    const int64_t grp = item / kChunks;
-    const int ch = (int)(item % kChunks) * 8;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.raw) +
-                                                    grp * a.raw_stride + ch);
-    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.out) + grp * a.out_stride + ch) = v;
-  }
-}
-
-// Nearest OCP e4m3 code of y (|y| clamped to 448, ties to the even code), y's sign kept.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fminf(fabsf(y), 448.0f);
-  if (a < 0.015625f) return sign | (uint32_t)__builtin_rintf(a * 512.0f);   // subnormals: 2^-9 steps
-  int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;                   // floor(log2 a)
-  float m = __builtin_rintf(__builtin_ldexpf(a, 3 - e));                       // 8 .. 16
-  if (m >= 16.0f) {
-    m = 8.0f;
-    e += 1;
-  }
-  const uint32_t code = ((uint32_t)(e + 7) << 3) | ((uint32_t)m - 8u);
-  return sign | (code < 0x7Eu ? code : 0x7Eu);
-}
-
-// Nearest FP4 E2M1 code of y (0, 0.5, 1, 1.5, 2, 3, 4, 6; ties to the even code; saturating).
-__device__ __forceinline__ uint32_t e2m1_code(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 28) & 0x8u;
-  const float a = fabsf(y);
-  uint32_t c;
-  if (a < 2.0f) c = (uint32_t)__builtin_rintf(2.0f * a);      // steps of 0.5: codes 0..4
-  else if (a < 4.0f) c = (uint32_t)__builtin_rintf(a) + 2u;   // steps of 1: codes 4..6
-  else if (a < 6.0f) c = a > 5.0f ? 7u : 6u;                  // 4 or 6 (5 ties to 4)
-  else c = 7u;
-  return sign | c;
-}
-
-__device__ __forceinline__ float wave_max(float v, int width) {
-  for (int o = 1; o < width; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
-// One wave per group: lane l computes channels 8l .. 8l+7 (the bf16 kernel's arithmetic,
-// kept in fp32) and quantises them.
-template <int KVM, int R>
-__global__ __launch_bounds__(kCThreads) void compress_codes_kernel(CompressArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t grp = (int64_t)blockIdx.x * (kCThreads / 64) + (threadIdx.x >> 6);
-  if (grp >= a.G) return;
-  const int ch = 8 * lane;
-  const uint16_t* x = reinterpret_cast<const uint16_t*>(a.raw) + grp * a.raw_stride + ch;
-  const u32x4 x0 = *reinterpret_cast<const u32x4*>(x);
-  float r[8];
-  if constexpr (R == 2) {
-    const u32x4 x1 = *reinterpret_cast<const u32x4*>(x + kDim);
-    const uint16_t* z = reinterpret_cast<const uint16_t*>(a.gate) + grp * a.gate_stride + ch;
-    const u32x4 z0 = *reinterpret_cast<const u32x4*>(z);
-    const u32x4 z1 = *reinterpret_cast<const u32x4*>(z + kDim);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int w = k >> 1, h = k & 1;
-      const float xa = h ? bf16_hi(x0[w]) : bf16_lo(x0[w]);
-      const float xb = h ? bf16_hi(x1[w]) : bf16_lo(x1[w]);
-      const float a0 = (h ? bf16_hi(z0[w]) : bf16_lo(z0[w])) + a.bias[ch + k];
-      const float a1 = (h ? bf16_hi(z1[w]) : bf16_lo(z1[w])) + a.bias[kDim + ch + k];
-      const float e = __builtin_amdgcn_exp2f((a1 - a0) * 1.4426950408889634f);
-      r[k] = fmaf(1.0f / (1.0f + e), xa - xb, xb);
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) r[k] = (k & 1) ? bf16_hi(x0[k >> 1]) : bf16_lo(x0[k >> 1]);
-  }
-  float amax = 0.0f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(r[k]));
-  uint8_t* out = reinterpret_cast<uint8_t*>(a.out) + grp * a.out_stride;
-  uint8_t* sc = reinterpret_cast<uint8_t*>(a.scales) + grp * a.scales_stride;
-  if constexpr (KVM == 1) {
-    amax = wave_max(amax, 64);
-    const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      lo |= e4m3_code(r[k] / s) << (8 * k);
-      hi |= e4m3_code(r[k + 4] / s) << (8 * k);
-    }
-    *reinterpret_cast<uint2*>(out + ch) = uint2{lo, hi};
-    if (lane == 0) *reinterpret_cast<float*>(sc) = s;
-  } else {
-    amax = wave_max(amax, 4);   // the block: lanes 4b .. 4b+3
-    int X = -127;
-    if (amax > 0.0f) {
-      int e;
-      frexpf(amax, &e);        // amax = f 2^e, f in [0.5, 1): floor(log2 amax) = e - 1
-      X = min(max(e - 3, -127), 127);
-    }
-    uint32_t packed = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) packed |= e2m1_code(__builtin_ldexpf(r[k], -X)) << (4 * k);
-    *reinterpret_cast<uint32_t*>(out + 4 * lane) = packed;
-    if ((lane & 3) == 0) sc[lane >> 2] = (uint8_t)(X + 127);
-  }
+__global__ __launch_bounds__(kCThreads) void compress_kernel(CompressArgs a) {
+  compress_blocks(a, blockIdx.x, gridDim.x);
 }
 
 }  // namespace
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t stream) {
-  if (a.kv_mode != 0) {   // one wave per group
-    const int64_t blocks = (a.G + kCThreads / 64 - 1) / (kCThreads / 64);
-    if (a.kv_mode == 1 && a.ratio == 2)
-      hipLaunchKernelGGL((compress_codes_kernel<1, 2>), dim3((unsigned)blocks), dim3(kCThreads), 0, stream, a);
-    else if (a.kv_mode == 1)
-      hipLaunchKernelGGL((compress_codes_kernel<1, 1>), dim3((unsigned)blocks), dim3(kCThreads), 0, stream, a);
-    else if (a.ratio == 2)
-      hipLaunchKernelGGL((compress_codes_kernel<2, 2>), dim3((unsigned)blocks), dim3(kCThreads), 0, stream, a);
-    else
-      hipLaunchKernelGGL((compress_codes_kernel<2, 1>), dim3((unsigned)blocks), dim3(kCThreads), 0, stream, a);
-    return hipGetLastError();
-  }
-  const int64_t items = a.G * kChunks;
-  int64_t blocks = (items + kCThreads - 1) / kCThreads;
-  if (blocks > 256 * 64) blocks = 256 * 64;   // grid-stride beyond 64 work-groups per CU
-  if (blocks < 1) blocks = 1;
-  if (a.ratio == 2)
-    hipLaunchKernelGGL(compress2_kernel, dim3((unsigned)blocks), dim3(kCThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(copy1_kernel, dim3((unsigned)blocks), dim3(kCThreads), 0, stream, a);
+  const int64_t blocks = compress_blocks_wanted(a);
+  hipLaunchKernelGGL(compress_kernel, dim3((unsigned)blocks), dim3(kCThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -22,6 +22,7 @@
 // work-group in padded LDS rows (prefetched two tiles ahead through registers) and read by
 // every wave; each wave holds two query pairs. A lane's 16 results are 8 heads of each of
 // the two queries for one key, so the head sum is in-lane plus one 32-lane swap.
+#include "sa_compress.h"
 #include "sa_device.h"
 #include "sa_launch.h"
 
@@ -149,6 +150,15 @@ __device__ __forceinline__ void settle(T& v) {
   }
 }
 
+// A compressor job riding in an indexer launch: work-groups of the grid rows from
+// a.cj_row0 on run it (all indexer kernels have the compressor's 256 threads) and return.
+__device__ __forceinline__ bool run_compress_rows(const IndexerArgs& a) {
+  if (a.cj.G == 0 || (int)blockIdx.y < a.cj_row0) return false;
+  compress_blocks(a.cj, (int64_t)(blockIdx.y - a.cj_row0) * gridDim.x + blockIdx.x,
+                  (int64_t)(gridDim.y - a.cj_row0) * gridDim.x);
+  return true;
+}
+
 // Modes. kPlain: each query's keys are contiguous rows of its sequence. kCand (candidate-
 // bounded re-scoring): the score row is in slot order, entry 8i + r belonging to position
 // 8 cand[i] + r of the query's carried candidate blocks (ascending, -1 padded); a tile of 16
@@ -159,6 +169,7 @@ enum DecodeMode { kPlain = 0, kCand = 1, kPaged = 2 };
 
 template <bool FP8, int MODE>
 __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a) {
+  if (run_compress_rows(a)) return;
   constexpr bool CAND = MODE == kCand, PAGED = MODE == kPaged;
   using DT = DecodeTile<FP8>;
   constexpr int RB = DT::RB, TB = DT::TB, NK = DT::NK, D = DT::D;
@@ -418,6 +429,7 @@ __device__ __forceinline__ int kdim_mx(int g, int s) { return 32 * g + 8 * s; }
 // slot's rows are loaded once the ids are in.
 template <int MODE>
 __global__ __launch_bounds__(kDThreads) void indexer_mx_kernel(IndexerArgs a) {
+  if (run_compress_rows(a)) return;
   constexpr int RB = kMxRB, TB = 16 * kMxRB, D = kMxD;
   constexpr bool CAND = MODE == kCand, PAGED = MODE == kPaged;
   static_assert(kMxTPW * 2 <= 64, "one page id or one slot per lane");
@@ -597,6 +609,7 @@ constexpr int group_keys_per_wg() { return kDWaves * group_tpw<G>() * 16; }
 // ids of its tiles (one per lane) ahead of its other loads.
 template <bool FP8, int G, bool PAGED>
 __global__ __launch_bounds__(kDThreads, 2) void indexer_group_kernel(IndexerArgs a) {
+  if (run_compress_rows(a)) return;
   using DT = DecodeTile<FP8>;
   constexpr int RB = DT::RB, TB = DT::TB, NK = DT::NK, D = DT::D;
   constexpr int TPW = group_tpw<G>();
@@ -818,6 +831,7 @@ struct GroupMxShared {
 
 template <int G, bool PAGED>
 __global__ __launch_bounds__(kDThreads, 2) void indexer_group_mx_kernel(IndexerArgs a) {
+  if (run_compress_rows(a)) return;
   constexpr int RB = kMxRB, TB = 16 * kMxRB, D = kGMxD;
   constexpr int TPW = group_tpw<G>();
   constexpr int N4 = G / 4, N2 = (G % 4) / 2;
@@ -1021,6 +1035,7 @@ constexpr uint32_t kDrop = 0x80000000u;  // buffer offset past every extent: sto
 // chunk's page ids (at most 64) are read once, one per lane.
 template <int KF, bool PAGED>
 __global__ __launch_bounds__(kPThreads, 8 / kPWaves) void indexer_prefill_kernel(IndexerArgs a) {
+  if (run_compress_rows(a)) return;
   constexpr bool FP8 = KF == 1, MX = KF == 2;
   constexpr int RB = MX ? kIdxDim / 2 : (FP8 ? kIdxDim : 2 * kIdxDim);   // key row bytes in HBM
   __shared__ __attribute__((aligned(16))) PrefillShared sh;
@@ -1307,82 +1322,112 @@ __global__ __launch_bounds__(kPThreads, 8 / kPWaves) void indexer_prefill_kernel
   epilogue(1, acc1, kprev, scprev);
 }
 
+static_assert(kDThreads == kCThreads && kPThreads == kCThreads, "compressor jobs need 256-thread work-groups");
+
+// The grid of an indexer launch with the compressor job's rows appended (b.cj_row0 set).
+dim3 with_job_rows(dim3 g, IndexerArgs& b) {
+  if (b.cj.G > 0) {
+    b.cj_row0 = (int32_t)g.y;
+    g.y += (unsigned)((compress_blocks_wanted(b.cj) + g.x - 1) / g.x);
+  }
+  return g;
+}
+
 template <int G>
-void launch_group(const IndexerArgs& a, hipStream_t stream) {
+void launch_group(IndexerArgs& b, hipStream_t stream) {
   constexpr int KW = group_keys_per_wg<G>();
-  dim3 grid((unsigned)((a.E + KW - 1) / KW), (unsigned)((a.T + a.group - 1) / a.group));
-  if (a.mxfp4) {
-    if (a.pages.table)
-      hipLaunchKernelGGL((indexer_group_mx_kernel<G, true>), grid, dim3(kDThreads), 0, stream, a);
+  const dim3 grid = with_job_rows(dim3((unsigned)((b.E + KW - 1) / KW), (unsigned)((b.T + b.group - 1) / b.group)), b);
+  if (b.mxfp4) {
+    if (b.pages.table)
+      hipLaunchKernelGGL((indexer_group_mx_kernel<G, true>), grid, dim3(kDThreads), 0, stream, b);
     else
-      hipLaunchKernelGGL((indexer_group_mx_kernel<G, false>), grid, dim3(kDThreads), 0, stream, a);
+      hipLaunchKernelGGL((indexer_group_mx_kernel<G, false>), grid, dim3(kDThreads), 0, stream, b);
     return;
   }
-  if (a.pages.table) {
-    if (a.fp8)
-      hipLaunchKernelGGL((indexer_group_kernel<true, G, true>), grid, dim3(kDThreads), 0, stream, a);
+  if (b.pages.table) {
+    if (b.fp8)
+      hipLaunchKernelGGL((indexer_group_kernel<true, G, true>), grid, dim3(kDThreads), 0, stream, b);
     else
-      hipLaunchKernelGGL((indexer_group_kernel<false, G, true>), grid, dim3(kDThreads), 0, stream, a);
-  } else if (a.fp8) {
-    hipLaunchKernelGGL((indexer_group_kernel<true, G, false>), grid, dim3(kDThreads), 0, stream, a);
+      hipLaunchKernelGGL((indexer_group_kernel<false, G, true>), grid, dim3(kDThreads), 0, stream, b);
+  } else if (b.fp8) {
+    hipLaunchKernelGGL((indexer_group_kernel<true, G, false>), grid, dim3(kDThreads), 0, stream, b);
   } else {
-    hipLaunchKernelGGL((indexer_group_kernel<false, G, false>), grid, dim3(kDThreads), 0, stream, a);
+    hipLaunchKernelGGL((indexer_group_kernel<false, G, false>), grid, dim3(kDThreads), 0, stream, b);
   }
+}
+
+// Grid rows (y) the launch puts the queries in, before any job rows (the dispatch below).
+unsigned query_rows(const IndexerArgs& a, bool prefill) {
+  if (a.mxfp4 && !prefill && a.group <= 1) return (unsigned)a.T;
+  if (a.group > 1 && !a.cand) return (unsigned)((a.T + a.group - 1) / a.group);
+  if (!prefill) return (unsigned)a.T;
+  return (unsigned)((a.T + kQPerWG - 1) / kQPerWG);
 }
 
 }  // namespace
 
 hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream) {
-  if (a.mxfp4 && !prefill && a.group <= 1) {
+  IndexerArgs b = a;
+  if (b.cj.G > 0) {
+    // the job's rows must fit the grid's y limit beside the queries' rows (the narrowest
+    // grid of any kernel here has one work-group per row); otherwise it runs on its own,
+    // first, on the same stream
+    if ((int64_t)query_rows(a, prefill) + compress_blocks_wanted(b.cj) > 65535) {
+      const hipError_t e = launch_compress(b.cj, stream);
+      if (e != hipSuccess) return e;
+      b.cj.G = 0;
+    }
+  }
+  if (b.mxfp4 && !prefill && b.group <= 1) {
     // every query streams its own keys
-    dim3 grid((unsigned)((a.E + kMxKeysPerWG - 1) / kMxKeysPerWG), (unsigned)a.T);
-    if (a.cand)
-      hipLaunchKernelGGL((indexer_mx_kernel<kCand>), grid, dim3(kDThreads), 0, stream, a);
-    else if (a.pages.table)
-      hipLaunchKernelGGL((indexer_mx_kernel<kPaged>), grid, dim3(kDThreads), 0, stream, a);
+    const dim3 grid = with_job_rows(dim3((unsigned)((b.E + kMxKeysPerWG - 1) / kMxKeysPerWG), (unsigned)b.T), b);
+    if (b.cand)
+      hipLaunchKernelGGL((indexer_mx_kernel<kCand>), grid, dim3(kDThreads), 0, stream, b);
+    else if (b.pages.table)
+      hipLaunchKernelGGL((indexer_mx_kernel<kPaged>), grid, dim3(kDThreads), 0, stream, b);
     else
-      hipLaunchKernelGGL((indexer_mx_kernel<kPlain>), grid, dim3(kDThreads), 0, stream, a);
-  } else if (a.group > 1 && !a.cand) {
-    // the smallest even group size that holds a.group (extra queries are masked)
-    if (a.group <= 2) launch_group<2>(a, stream);
-    else if (a.group <= 4) launch_group<4>(a, stream);
-    else if (a.group <= 6) launch_group<6>(a, stream);
-    else launch_group<8>(a, stream);
+      hipLaunchKernelGGL((indexer_mx_kernel<kPlain>), grid, dim3(kDThreads), 0, stream, b);
+  } else if (b.group > 1 && !b.cand) {
+    // the smallest even group size that holds b.group (extra queries are masked)
+    if (b.group <= 2) launch_group<2>(b, stream);
+    else if (b.group <= 4) launch_group<4>(b, stream);
+    else if (b.group <= 6) launch_group<6>(b, stream);
+    else launch_group<8>(b, stream);
   } else if (!prefill) {
-    dim3 grid((unsigned)((a.E + kKeysPerWG - 1) / kKeysPerWG), (unsigned)a.T);
-    if (a.cand) {
-      if (a.fp8)
-        hipLaunchKernelGGL((indexer_decode_kernel<true, kCand>), grid, dim3(kDThreads), 0, stream, a);
+    const dim3 grid = with_job_rows(dim3((unsigned)((b.E + kKeysPerWG - 1) / kKeysPerWG), (unsigned)b.T), b);
+    if (b.cand) {
+      if (b.fp8)
+        hipLaunchKernelGGL((indexer_decode_kernel<true, kCand>), grid, dim3(kDThreads), 0, stream, b);
       else
-        hipLaunchKernelGGL((indexer_decode_kernel<false, kCand>), grid, dim3(kDThreads), 0, stream, a);
-    } else if (a.pages.table) {
-      if (a.fp8)
-        hipLaunchKernelGGL((indexer_decode_kernel<true, kPaged>), grid, dim3(kDThreads), 0, stream, a);
+        hipLaunchKernelGGL((indexer_decode_kernel<false, kCand>), grid, dim3(kDThreads), 0, stream, b);
+    } else if (b.pages.table) {
+      if (b.fp8)
+        hipLaunchKernelGGL((indexer_decode_kernel<true, kPaged>), grid, dim3(kDThreads), 0, stream, b);
       else
-        hipLaunchKernelGGL((indexer_decode_kernel<false, kPaged>), grid, dim3(kDThreads), 0, stream, a);
-    } else if (a.fp8) {
-      hipLaunchKernelGGL((indexer_decode_kernel<true, kPlain>), grid, dim3(kDThreads), 0, stream, a);
+        hipLaunchKernelGGL((indexer_decode_kernel<false, kPaged>), grid, dim3(kDThreads), 0, stream, b);
+    } else if (b.fp8) {
+      hipLaunchKernelGGL((indexer_decode_kernel<true, kPlain>), grid, dim3(kDThreads), 0, stream, b);
     } else {
-      hipLaunchKernelGGL((indexer_decode_kernel<false, kPlain>), grid, dim3(kDThreads), 0, stream, a);
+      hipLaunchKernelGGL((indexer_decode_kernel<false, kPlain>), grid, dim3(kDThreads), 0, stream, b);
     }
   } else {
     // blockIdx.x (key chunk) varies fastest, so with a multiple of 8 chunks every XCD
     // keeps the same chunks and their keys stay in its L2.
-    dim3 grid((unsigned)((a.E + kPChunk - 1) / kPChunk), (unsigned)((a.T + kQPerWG - 1) / kQPerWG));
-    if (a.mxfp4) {
-      if (a.pages.table)
-        hipLaunchKernelGGL((indexer_prefill_kernel<2, true>), grid, dim3(kPThreads), 0, stream, a);
+    const dim3 grid = with_job_rows(dim3((unsigned)((b.E + kPChunk - 1) / kPChunk), (unsigned)((b.T + kQPerWG - 1) / kQPerWG)), b);
+    if (b.mxfp4) {
+      if (b.pages.table)
+        hipLaunchKernelGGL((indexer_prefill_kernel<2, true>), grid, dim3(kPThreads), 0, stream, b);
       else
-        hipLaunchKernelGGL((indexer_prefill_kernel<2, false>), grid, dim3(kPThreads), 0, stream, a);
-    } else if (a.pages.table) {
-      if (a.fp8)
-        hipLaunchKernelGGL((indexer_prefill_kernel<1, true>), grid, dim3(kPThreads), 0, stream, a);
+        hipLaunchKernelGGL((indexer_prefill_kernel<2, false>), grid, dim3(kPThreads), 0, stream, b);
+    } else if (b.pages.table) {
+      if (b.fp8)
+        hipLaunchKernelGGL((indexer_prefill_kernel<1, true>), grid, dim3(kPThreads), 0, stream, b);
       else
-        hipLaunchKernelGGL((indexer_prefill_kernel<0, true>), grid, dim3(kPThreads), 0, stream, a);
-    } else if (a.fp8) {
-      hipLaunchKernelGGL((indexer_prefill_kernel<1, false>), grid, dim3(kPThreads), 0, stream, a);
+        hipLaunchKernelGGL((indexer_prefill_kernel<0, true>), grid, dim3(kPThreads), 0, stream, b);
+    } else if (b.fp8) {
+      hipLaunchKernelGGL((indexer_prefill_kernel<1, false>), grid, dim3(kPThreads), 0, stream, b);
     } else {
-      hipLaunchKernelGGL((indexer_prefill_kernel<0, false>), grid, dim3(kPThreads), 0, stream, a);
+      hipLaunchKernelGGL((indexer_prefill_kernel<0, false>), grid, dim3(kPThreads), 0, stream, b);
     }
   }
   return hipGetLastError();

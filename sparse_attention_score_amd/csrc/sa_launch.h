@@ -26,6 +26,22 @@ struct QueryMeta {
   int32_t ratio;
 };
 
+struct CompressArgs {
+  const void* raw;
+  int64_t raw_stride;
+  const void* gate;
+  int64_t gate_stride;
+  const float* bias;        // [ratio][512]
+  void* out;
+  int64_t out_stride;
+  int64_t G;
+  int32_t ratio;
+  // code rows (kv_mode 1: e4m3 + fp32 row scale, 2: MXFP4 + 16 E8M0 bytes); out_stride and
+  // scales_stride in bytes then
+  int32_t kv_mode;
+  void* scales;
+  int64_t scales_stride;
+};
 struct IndexerArgs {
   const int32_t* seq_id;
   const int32_t* pos;
@@ -50,6 +66,10 @@ struct IndexerArgs {
   const int32_t* cand;      // candidate mode: [T][2048] carried block ids, else null
   int32_t group;            // > 1: queries g*group .. g*group+group-1 share a sequence (<= 8)
   PageTable pages;          // keys and scales are page pools when pages.table is set
+  // A compressor job (cj.G > 0) that rides in the launch: work-groups in grid rows from
+  // cj_row0 on (set by the launcher) run it instead of indexer work.
+  CompressArgs cj{};
+  int32_t cj_row0 = 0;
 };
 hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream);
 // Queries per work-group of the chunk kernel (its grid holds ceil(T / this) in y).
@@ -137,22 +157,6 @@ struct AttnScratch {
 };
 hipError_t attn_scratch(AttnScratch& s);
 
-struct CompressArgs {
-  const void* raw;
-  int64_t raw_stride;
-  const void* gate;
-  int64_t gate_stride;
-  const float* bias;        // [ratio][512]
-  void* out;
-  int64_t out_stride;
-  int64_t G;
-  int32_t ratio;
-  // code rows (kv_mode 1: e4m3 + fp32 row scale, 2: MXFP4 + 16 E8M0 bytes); out_stride and
-  // scales_stride in bytes then
-  int32_t kv_mode;
-  void* scales;
-  int64_t scales_stride;
-};
 hipError_t launch_compress(const CompressArgs& a, hipStream_t stream);
 
 }  // namespace sa

@@ -1,6 +1,6 @@
-"""One pass of the hot path over a batch: compressor (if a group completes), indexer,
-candidate + top-512 selection, gather attention. Allocation and call order only; every
-stage runs in the library's kernels through the C ABI."""
+"""One pass of the hot path over a batch: compressor (if a group completes) and indexer in
+one launch, candidate + top-512 selection, gather attention. Allocation and call order only;
+every stage runs in the library's kernels through the C ABI."""
 from __future__ import annotations
 
 from typing import Optional
@@ -8,9 +8,8 @@ from typing import Optional
 import numpy as np
 import torch
 
-from . import (Cache, Plan, Queries, indexer_score, select_topk, sparse_attn_compress,
-               sparse_attn_compress_codes,
-               sparse_attn_fwd, workspace_for)
+from . import (Cache, CompressJob, Plan, Queries, indexer_score, indexer_score_compress, select_topk,
+               sparse_attn_compress, sparse_attn_compress_codes, sparse_attn_fwd, workspace_for)
 
 
 def to_device_bf16(bits: np.ndarray, device="cuda") -> torch.Tensor:
@@ -95,9 +94,40 @@ class DeviceBatch:
         sparse_attn_compress(self.plan, self.Xp, 1024, self.Zp, 1024, self.beta, out_view,
                              self.C.stride(0), wl.B, stream=stream)
 
+    def compress_job(self) -> Optional[CompressJob]:
+        """The compress() call's arguments as a job for indexer_score_compress (None without
+        compressor inputs)."""
+        if not len(self.groups):
+            return None
+        if getattr(self, "_job", None) is None:
+            wl = self.wl
+            n = (int(wl.pos[0]) + 1) // 2
+            assert np.all((wl.pos.astype(np.int64) + 1) // 2 == n), "uniform positions required"
+            assert len(self.groups) == wl.B and np.array_equal(self.groups, np.arange(wl.B))
+            out_view = self.C[:, n - 1]
+            if self.CS is not None:
+                self._job = CompressJob(self.Xp, 1024, self.Zp, 1024, self.beta, out_view, self.C.stride(0), wl.B,
+                                        self.CS[:, n - 1], self.CS.stride(0) * self.CS.element_size())
+            else:
+                self._job = CompressJob(self.Xp, 1024, self.Zp, 1024, self.beta, out_view, self.C.stride(0), wl.B)
+        return self._job
+
     def index(self, stream=None):
         indexer_score(self.plan, self.queries, self.cache, self.qI, self.w, self.scores,
                       self.block_max, stream=stream)
+
+    def index_compress(self, stream=None):
+        """compress() and index() in one launch (the compressor's work-groups ride in the
+        indexer's grid)."""
+        indexer_score_compress(self.plan, self.queries, self.cache, self.qI, self.w, self.scores,
+                               self.block_max, self.compress_job(), stream=stream)
+
+    def step_fns(self, fused: bool = True):
+        """The launches of one step: the compressor in the indexer's launch (fused) or as a
+        launch of its own."""
+        if fused:
+            return [self.index_compress, self.select, self.attend]
+        return [self.compress, self.index, self.select, self.attend]
 
     def select(self, stream=None, use_block_max=True):
         select_topk(self.plan, self.queries, self.scores, self.block_max if use_block_max else None,
@@ -109,14 +139,12 @@ class DeviceBatch:
                         self.topk if topk is None else topk, self.out, self.lse,
                         workspace=self.workspace if split else None, stream=stream)
 
-    def run(self, stream=None):
-        self.compress(stream)
-        self.index(stream)
-        self.select(stream)
-        self.attend(stream)
+    def run(self, stream=None, fused: bool = True):
+        for f in self.step_fns(fused):
+            f(stream)
 
     def capture(self):
-        """One whole step (the four stage launches) captured in a HIP graph. The library
+        """One whole step (its three launches) captured in a HIP graph. The library
         enqueues kernels only (no allocation, copy, memset or synchronisation), so every
         launch is recorded; replaying the graph re-runs the step on the same buffers."""
         torch.cuda.synchronize()

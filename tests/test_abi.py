@@ -349,6 +349,47 @@ def test_compress_codes_rejects():
     assert call(p8, args(G=0)) == S.SA_OK and call(p4, args(os=256, ss=16, G=0)) == S.SA_OK
 
 
+def _job(**k):
+    a = dict(raw=0x1000, raw_group_stride=1024, gate=0x1000, gate_group_stride=1024, slot_bias=0x3000,
+             out=0x4000, out_group_stride=512, out_scales=None, scales_group_stride=0, G=4)
+    a.update(k)
+    return S.sa_compress_job(**a)
+
+
+def _index_compress(p, q, c, job, ld=104):
+    return S.lib.indexer_score_compress(p.handle, ctypes.byref(q), ctypes.byref(c), 0x40000, 0x50000, 0x60000, ld,
+                                        None, 0, None if job is None else ctypes.byref(job), None)
+
+
+@pytest.mark.parametrize("bad", [dict(raw=None), dict(raw_group_stride=1000), dict(gate=None),
+                                 dict(gate_group_stride=1000), dict(slot_bias=None), dict(out=0x4008),
+                                 dict(out_group_stride=500), dict(G=-1)])
+def test_indexer_compress_rejects_bad_job(bad):
+    # the job's checks are the compressor's; a refused call enqueues nothing
+    assert _index_compress(_plan(), _q(), _c(), _job(**bad)) == S.SA_EINVAL, S.lib.sparse_attn_last_error()
+
+
+def test_indexer_compress_code_rows_job():
+    # code-row plans check the scales of the job like sparse_attn_compress_codes
+    p8 = _plan(kv_dtype="fp8")
+    c8 = _c(latent_scales=0x70000, latent_scales_seq_stride=1000, window_scales=0x80000,
+            window_scales_seq_stride=128)
+    assert _index_compress(p8, _q(), c8, _job(out_scales=None)) == S.SA_EINVAL
+    assert _index_compress(p8, _q(), c8, _job(out_scales=0x5002, scales_group_stride=4)) == S.SA_EINVAL
+    assert _index_compress(p8, _q(), c8, _job(out_scales=0x5000, scales_group_stride=2)) == S.SA_EINVAL
+
+
+def test_indexer_compress_checks_the_indexer_too():
+    # a good job does not lift the indexer's own checks; no job or G = 0 is indexer_score
+    q = _q()
+    q.seq_id = None
+    assert _index_compress(_plan(), q, _c(), _job()) == S.SA_EINVAL
+    assert _index_compress(_plan(), _q(), _c(), _job(), ld=100) == S.SA_EINVAL
+    assert _index_compress(_plan(), _q(), _c(idx_keys=None), None) == S.SA_EINVAL
+    assert _index_compress(_plan(), _q(), _c(idx_keys=None), _job(G=0)) == S.SA_EINVAL
+    assert b"idx_keys" in S.lib.sparse_attn_last_error() or S.lib.sparse_attn_last_error()
+
+
 def test_plain_c_caller(tmp_path):
     # the library from C alone: tests/c/abi_host_check.c built with gcc against the header and
     # the built .so, run on the host (plan creation and argument errors need no GPU)
