@@ -520,8 +520,13 @@ __device__ __forceinline__ void load_block_keys(const SelectArgs& a, int t, int6
 // ROLES = 2 (batches of few queries, where the latency of one query is the kernel time):
 // two work-groups per query work independently, role 0 selecting the 2048 candidate
 // blocks and role 1 the 512 core blocks and then the top-512 positions.
+// 512-thread work-groups (large batches) are held to 80 registers so that three fit a CU
+// beside each other (six waves per SIMD instead of four): the phases of one query are short
+// and latency-bound, and a third work-group hides more of them (prefill chunk: 183 -> 153
+// us, though the 8192-block variant then keeps a few values in scratch).
 template <int NT, int EPT, int ROLES>
-__global__ __launch_bounds__(NT) void select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 512 ? 6 : 1, 8)))
+void select_kernel(SelectArgs a) {
   __shared__ SelShared sh;
   __shared__ __attribute__((aligned(16))) int32_t core[kTopK];
   const int role = ROLES == 1 ? -1 : (int)blockIdx.x;
