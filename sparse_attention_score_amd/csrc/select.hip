@@ -808,9 +808,10 @@ hipError_t launch_select_cand(const SelectArgs& a, hipStream_t stream) {
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t stream) {
   // few queries: one large work-group each (the latency of a query is the kernel time);
-  // many queries: 512-thread work-groups, two or more per CU (measured against 256 and
-  // 1024 threads on a 4096-query chunk: 193 us against 258 and 292)
-  return a.m.T < 1024 ? launch_select_nt<1024>(a, stream) : launch_select_nt<512>(a, stream);
+  // many queries: 512-thread work-groups, three per CU (measured against 256 and 1024
+  // threads on a 4096-query chunk: 193 us against 258 and 292 at two per CU; 768 queries
+  // of a multi-token step: 31 us against 50 with 1024 threads)
+  return a.m.T < 512 ? launch_select_nt<1024>(a, stream) : launch_select_nt<512>(a, stream);
 }
 
 }  // namespace sa
