@@ -53,15 +53,15 @@ LATENT_ROW = 512 * 2
 
 
 INDEXER_SOURCES = ("sparse_attention_score_amd/csrc/indexer.hip", "sparse_attention_score_amd/csrc/sa_device.h",
-                   "sparse_attention_score_amd/csrc/sa_launch.h")
+                   "sparse_attention_score_amd/csrc/sa_launch.h", "sparse_attention_score_amd/csrc/sa_compress.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_decode-b128-ctx128k-fp8_traffic.json")
 RESCORE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_cand_decode-b128-ctx128k-fp8_traffic.json")
 GROUP_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_group_decode-mq6-b128-ctx128k-fp8_traffic.json")
 MX_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_mx_decode-b128-ctx128k-mxfp4_traffic.json")
 CONFIG_TRAFFIC_FILES = {"decode-b64-ctx32k": os.path.join(ROOT, "profiles", "indexer_decode-b64-ctx32k_traffic.json"),
                         "decode-b8-ctx1m-fp8": os.path.join(ROOT, "profiles", "indexer_decode-b8-ctx1m-fp8_traffic.json")}
-COMPRESS_SOURCES = ("sparse_attention_score_amd/csrc/compress.hip", "sparse_attention_score_amd/csrc/sa_device.h",
-                    "sparse_attention_score_amd/csrc/sa_launch.h")
+COMPRESS_SOURCES = ("sparse_attention_score_amd/csrc/compress.hip", "sparse_attention_score_amd/csrc/sa_compress.h",
+                    "sparse_attention_score_amd/csrc/sa_device.h", "sparse_attention_score_amd/csrc/sa_launch.h")
 COMPRESS_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compress_raw-64x32768_traffic.json")
 COPY_BYTES = 1 << 30
 
