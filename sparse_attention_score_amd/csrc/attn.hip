@@ -134,10 +134,30 @@ __device__ __forceinline__ void to_lds4(const void* src, uint32_t lds) {
 __device__ __forceinline__ void row8_to_lds(const uint16_t* row, uint32_t lds, int lane) {
   if (lane < 32) to_lds16(reinterpret_cast<const uint8_t*>(row) + 16 * lane, lds);
 }
-// 4 e4m3 codes -> 4 bf16 (exact), as two packed pairs
-__device__ __forceinline__ uint2 e4m3x4_bf16(uint32_t x) {
-  return uint2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false)),
-               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true))};
+// e4m3 codes 2w, 2w+1 of a dword -> two bf16 (exact), packed (code 2w in the low half)
+template <bool W>
+__device__ __forceinline__ uint32_t e4m3_pair(uint32_t x) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, W));
+}
+// E2M1 elements 2b, 2b+1 of a dword (byte b) times an E8M0 scale -> two bf16 (exact)
+template <int B>
+__device__ __forceinline__ uint32_t fp4_pair(uint32_t x, float scale) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, scale, B));
+}
+// 8 e4m3 codes (two dwords) -> bf16x8
+__device__ __forceinline__ bf16x8 e4m3x8(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(bf16x8, u32x4{e4m3_pair<false>(lo), e4m3_pair<true>(lo), e4m3_pair<false>(hi),
+                                          e4m3_pair<true>(hi)});
+}
+// 8 E2M1 elements (one dword) with their block's scale -> bf16x8
+__device__ __forceinline__ bf16x8 fp4x8(uint32_t x, float scale) {
+  return __builtin_bit_cast(bf16x8, u32x4{fp4_pair<0>(x, scale), fp4_pair<1>(x, scale), fp4_pair<2>(x, scale),
+                                          fp4_pair<3>(x, scale)});
+}
+// An E8M0 byte -> its fp32 scale 2^(e-127) (e = 0: the fp32 subnormal 2^-127; codes here
+// are at most 254, the encoder's range)
+__device__ __forceinline__ float e8m0_f32(uint32_t e) {
+  return __uint_as_float(e == 0 ? 0x00400000u : e << 23);
 }
 
 // a 1.0 that the scale slots of MXFP4 rows (their scales are applied while widening) and
@@ -146,10 +166,13 @@ __device__ float g_unit_scale = 1.0f;
 
 // KVM: 0 bf16 rows. 1: the latents and the window are e4m3 rows with one fp32 scale each
 // (X_j = s_j code_j). 2: MXFP4 latents (256 bytes of E2M1 plus 16 E8M0 block scales per
-// row) and an e4m3 window. Code rows travel as they are stored and are widened exactly to
-// bf16 in LDS, once per step by the wave that loaded them (MXFP4 rows with their block
-// scales); the raw score of key j is multiplied by its row scale s_j (1 for MXFP4), and so
-// is P_j before the values (the normaliser sums the unscaled P).
+// row) and an e4m3 window. Code rows travel and stay in LDS as they are stored (half or a
+// quarter of a bf16 row's bytes) and are widened exactly to bf16 in registers as the MFMA
+// operands are read (MXFP4 elements with their block scales); the raw score of key j is
+// multiplied by its row scale s_j (1 for MXFP4), and so is P_j before the values (the
+// normaliser sums the unscaled P). Score waves of code rows take dims 128g + 8s .. +7 of
+// their key in k-step s (the query operands in the same order), so a lane's four k-steps
+// 4t .. 4t+3 read 32 consecutive dims: one MXFP4 block, one scale.
 template <int HS, int KVM>
 __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   constexpr bool KV8 = KVM != 0, FP4L = KVM == 2;
@@ -301,81 +324,6 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       }
     }
   };
-  // Code rows: each wave widens the rows it loaded, in place (the codes at the start of a
-  // slot, 512 bytes of e4m3 or 256 + 16 bytes of MXFP4, become 1 KiB of bf16), after its
-  // own wait and before the barrier that hands the step to the other waves. All of a
-  // wave's reads of a row come before its writes to it, and a wave's LDS operations run in
-  // order, so no code is overwritten before it is read.
-  // e4m3 rows: chunk q (16 codes) of row rr, 2 chunks per lane (4 rows x 32 chunks);
-  // MXFP4 rows: code dword e of block q of row rr, lane 4q + e, with block q's scale byte
-  // (after the 256 code bytes): 8 elements per lane and row, contiguous 16-byte writes.
-  // Every read of a row comes before its first write.
-  auto e4m3_rows = [&](uint8_t* base) {
-    u32x4 cv[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int ch = lane + 64 * h, rr = ch >> 5, q = ch & 31;
-      cv[h] = *reinterpret_cast<const u32x4*>(base + rr * kRow + 16 * q);
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int ch = lane + 64 * h, rr = ch >> 5, q = ch & 31;
-      uint2 b[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) b[e] = e4m3x4_bf16(cv[h][e]);
-      *reinterpret_cast<u32x4*>(base + rr * kRow + 32 * q) = u32x4{b[0].x, b[0].y, b[1].x, b[1].y};
-      *reinterpret_cast<u32x4*>(base + rr * kRow + 32 * q + 16) = u32x4{b[2].x, b[2].y, b[3].x, b[3].y};
-    }
-  };
-  auto fp4_write = [&](uint8_t* row, uint32_t codes, uint32_t sbyte) {
-    const float bs = e8m0_scale(sbyte);
-    const u32x4 u = {__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, bs, 0)),
-                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, bs, 1)),
-                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, bs, 2)),
-                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, bs, 3))};
-    *reinterpret_cast<u32x4*>(row + 16 * lane) = u;   // elements 8 lane .. 8 lane + 7
-  };
-  auto expand = [&](int step) {
-    if constexpr (KV8) {
-      uint8_t* base = sh.tile[step % kBufs] + wave * kRowsPerWave * kRow;
-      if constexpr (!FP4L) {
-        e4m3_rows(base);
-      } else {
-        // list indices of the wave's rows ascend: latents (MXFP4) first, then the window
-        const int r0 = step * kKT + wave * kRowsPerWave;
-        const int first = kb + min(r0, mk - 1), last = kb + min(r0 + kRowsPerWave - 1, mk - 1);
-        if (first >= nlat) {
-          e4m3_rows(base);
-        } else if (last < nlat) {
-          uint32_t cw[kRowsPerWave], sb[kRowsPerWave];
-#pragma unroll
-          for (int rr = 0; rr < kRowsPerWave; ++rr) {
-            cw[rr] = *reinterpret_cast<const uint32_t*>(base + rr * kRow + 4 * lane);
-            sb[rr] = base[rr * kRow + kDim / 2 + (lane >> 2)];
-          }
-#pragma unroll
-          for (int rr = 0; rr < kRowsPerWave; ++rr) fp4_write(base + rr * kRow, cw[rr], sb[rr]);
-        } else {   // the step where the latents end: row by row
-          for (int rr = 0; rr < kRowsPerWave; ++rr) {
-            uint8_t* row = base + rr * kRow;
-            if (kb + min(r0 + rr, mk - 1) < nlat) {
-              const uint32_t cw = *reinterpret_cast<const uint32_t*>(row + 4 * lane);
-              const uint32_t sb = row[kDim / 2 + (lane >> 2)];
-              fp4_write(row, cw, sb);
-            } else if (lane < 32) {
-              const u32x4 cv = *reinterpret_cast<const u32x4*>(row + 16 * lane);
-              uint2 b[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) b[e] = e4m3x4_bf16(cv[e]);
-              *reinterpret_cast<u32x4*>(row + 32 * lane) = u32x4{b[0].x, b[0].y, b[1].x, b[1].y};
-              *reinterpret_cast<u32x4*>(row + 32 * lane + 16) = u32x4{b[2].x, b[2].y, b[3].x, b[3].y};
-            }
-          }
-        }
-      }
-    }
-  };
-
   // code rows: the slots' scales by direct loads, issued before the first rows so the
   // rows' waits cover them
   if constexpr (KV8) {
@@ -407,7 +355,8 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       const uint8_t* qrow = reinterpret_cast<const uint8_t*>(&sh.tile[0][0]) + 2 * kKT * kRow +
                             (16 * sgrp(j) + c) * kRow;
 #pragma unroll
-      for (int s = 0; s < 16; ++s) qb[j][s] = *reinterpret_cast<const bf16x8*>(qrow + (4 * s + g) * 16);
+      for (int s = 0; s < 16; ++s)
+        qb[j][s] = *reinterpret_cast<const bf16x8*>(qrow + (KV8 ? (128 * g + 8 * s) * 2 : (4 * s + g) * 16));
     }
     __syncthreads();   // every wave holds its query heads: tile 2 may take step 2's rows
     if (mk > 0) issue(2);
@@ -424,12 +373,59 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       const uint8_t* krow = sh.tile[step % kBufs] + (16 * kh + c) * kRow;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 16; ++s) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(krow + (4 * s + g) * 16);
+      auto mma = [&](int s, const bf16x8& ka) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
           acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j][s], acc[j], 0, 0, 0);
+      };
+      if constexpr (!KV8) {
+#pragma unroll
+        for (int s = 0; s < 16; ++s) mma(s, *reinterpret_cast<const bf16x8*>(krow + (4 * s + g) * 16));
+      } else {
+        // code rows widened here: k-steps 4t .. 4t+3 take dims 128g + 32t .. +31 of the
+        // lane's key. MXFP4 latents and e4m3 window rows share a step only where the latents
+        // end; slots past the list repeat the last key, in its format.
+        const int k0 = step * kKT + 16 * kh;
+        const bool all8 = !FP4L || kb + min(k0, mk - 1) >= nlat;
+        const bool all4 = FP4L && kb + min(k0 + 15, mk - 1) < nlat;
+        auto e4m3_t = [&](int t) {   // 32 codes of dims 128g + 32t ..
+          const u32x4 e0 = *reinterpret_cast<const u32x4*>(krow + 128 * g + 32 * t);
+          const u32x4 e1 = *reinterpret_cast<const u32x4*>(krow + 128 * g + 32 * t + 16);
+          return [=](int u) { return u < 2 ? e4m3x8(e0[2 * u], e0[2 * u + 1]) : e4m3x8(e1[2 * u - 4], e1[2 * u - 3]); };
+        };
+        auto fp4_t = [&](int t, uint32_t sc4) {   // block 4g + t: 16 code bytes and its scale
+          const u32x4 f = *reinterpret_cast<const u32x4*>(krow + 64 * g + 16 * t);
+          const float bs = e8m0_f32((sc4 >> (8 * t)) & 0xFFu);
+          return [=](int u) { return fp4x8(f[u], bs); };
+        };
+        if (all8) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const auto k8 = e4m3_t(t);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) mma(4 * t + u, k8(u));
+          }
+        } else {
+          // scales of blocks 4g .. 4g+3 of the lane's key (after its 256 code bytes)
+          const uint32_t sc4 = *reinterpret_cast<const uint32_t*>(krow + kDim / 2 + 4 * g);
+          if (all4) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const auto k4 = fp4_t(t, sc4);
+#pragma unroll
+              for (int u = 0; u < 4; ++u) mma(4 * t + u, k4(u));
+            }
+          } else {
+            const bool mine4 = kb + min(k0 + c, mk - 1) < nlat;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const auto k8 = e4m3_t(t);
+              const auto k4 = fp4_t(t, sc4);
+#pragma unroll
+              for (int u = 0; u < 4; ++u) mma(4 * t + u, mine4 ? k4(u) : k8(u));
+            }
+          }
+        }
       }
       if constexpr (KV8) {   // raw score of key j times s_j (slots past the list: any value, masked)
         const int k0 = min(kb + step * kKT + 16 * kh + 4 * g, kMaxKeys - 4);
@@ -480,7 +476,6 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
         for (int j = 0; j < kDepth; ++j) issue(j);
       }
       __builtin_amdgcn_s_waitcnt(kWaitLater);   // step 0's rows (steps 1, 2 in flight)
-      expand(0);
       __syncthreads();
       f32x4 acc[NJ];
       scores_raw(0, acc);
@@ -514,7 +509,6 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       // the buffer of step s-1; the value waves weigh step s meanwhile
       for (int step = 0; step < nsteps; ++step) {
         __builtin_amdgcn_s_waitcnt(kWaitNext);   // step s+1's rows (step s+2's in flight)
-        expand(step + 1);
         __syncthreads();
         issue(step + kDepth);
         scores_raw(step + 1, acc);               // past the last step: P = 0, never read
@@ -590,17 +584,59 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       bf16x8 pb[NV];
 #pragma unroll
       for (int h = 0; h < NV; ++h) pb[h] = __builtin_bit_cast(bf16x8, sh.P[step & 1][vgrp(h)][lane]);
-      // key slot j of half hh: dims 128vw + 64hh + 4c .. +3 (two dwords)
+      // key slot j of half hh: dims 128vw + 64hh + 4c .. +3 (two dwords of bf16 pairs;
+      // code rows are widened to them here)
       uint32_t R[2][8][2];
+      auto key_of = [&](int j) { return (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4)); };
+      auto bf16_R = [&](int hh, int j) {
+        const uint2 v = *reinterpret_cast<const uint2*>(T8 + key_of(j) * kRow + (128 * vw + 64 * hh + 4 * c) * 2);
+        R[hh][j][0] = v.x;
+        R[hh][j][1] = v.y;
+      };
+      auto e4m3_R = [&](int hh, int j) {   // 4 codes
+        const uint32_t x = *reinterpret_cast<const uint32_t*>(T8 + key_of(j) * kRow + 128 * vw + 64 * hh + 4 * c);
+        return uint2{e4m3_pair<false>(x), e4m3_pair<true>(x)};
+      };
+      auto fp4_R = [&](int hh, int j) {    // 4 E2M1 elements (2 bytes) and their block's scale
+        const uint8_t* row = T8 + key_of(j) * kRow;
+        const uint32_t x = *reinterpret_cast<const uint16_t*>(row + 64 * vw + 32 * hh + 2 * c);
+        const float bs = e8m0_f32(row[kDim / 2 + 4 * vw + 2 * hh + (c >> 3)]);
+        return uint2{fp4_pair<0>(x, bs), fp4_pair<1>(x, bs)};
+      };
+      if constexpr (!KV8) {
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int key = (j < 4) ? (4 * g + j) : (16 + 4 * g + (j - 4));
-          const uint2 v = *reinterpret_cast<const uint2*>(T8 + key * kRow + (128 * vw + 64 * hh + 4 * c) * 2);
+          for (int j = 0; j < 8; ++j) bf16_R(hh, j);
+      } else {
+        const int k0 = step * kKT;
+        const bool all8 = !FP4L || kb + min(k0, mk - 1) >= nlat;
+        const bool all4 = FP4L && kb + min(k0 + kKT - 1, mk - 1) < nlat;
+        auto put = [&](int hh, int j, uint2 v) {
           R[hh][j][0] = v.x;
           R[hh][j][1] = v.y;
+        };
+        if (all8) {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) put(hh, j, e4m3_R(hh, j));
+        } else if (all4) {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) put(hh, j, fp4_R(hh, j));
+        } else {   // the step where the latents end: each key slot its own format
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const bool lat = kb + min(k0 + key_of(j), mk - 1) < nlat;
+              const uint2 a = e4m3_R(hh, j), b = fp4_R(hh, j);
+              put(hh, j, lat ? b : a);
+            }
         }
+      }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
@@ -633,12 +669,10 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
         for (int j = 0; j < kDepth; ++j) issue(j);
       }
       __builtin_amdgcn_s_waitcnt(kWaitLater);
-      expand(0);
       __syncthreads();
       __syncthreads();   // (the score waves' step-0 maxima)
       for (int step = 0; step < nsteps; ++step) {
         __builtin_amdgcn_s_waitcnt(kWaitNext);
-        expand(step + 1);
         __syncthreads();
         issue(step + kDepth);
         values(step);
