@@ -1229,9 +1229,15 @@ __global__ __launch_bounds__(kPThreads, 8 / kPWaves) void indexer_prefill_kernel
   // Epilogue of pair p for the tile at key k: ReLU and head weights in-lane over the
   // lane's 8 heads of each query, one 32-lane swap to finish both 16-head sums, key scale,
   // mask past the query's n, block max over 8 lanes, two stores.
+  // The tile's key offset goes in the stores' scalar offset; the lane-dependent parts
+  // (row, key within the tile, the lanes that store block maxima) are fixed, and the
+  // masks compare the tile's first key with per-lane limits computed once.
   const uint32_t sbase = soff_hh + (uint32_t)r32 * 4u;
-  const uint32_t bbase = boff_hh + (uint32_t)(r32 >> 3) * 4u;
-  const bool bstore = (lane & 7) == 0;
+  const uint32_t bbase = (lane & 7) == 0 ? boff_hh + (uint32_t)(r32 >> 3) * 4u : kDrop;
+  const int kend_l = kend - r32;   // key k of lane r32 is this chunk's while k < kend_l
+  int nvis_l[kPairsPerWave];       // ... and visible to the lane's query while k < nvis_l
+#pragma unroll
+  for (int p = 0; p < kPairsPerWave; ++p) nvis_l[p] = nl[p] - r32;
   auto epilogue = [&](int p, const f32x16& acc, int k, float sc) {
     float x = wt[p][0][0] * relu(acc[0]);
     float y = wt[p][1][0] * relu(acc[8]);
@@ -1245,13 +1251,12 @@ __global__ __launch_bounds__(kPThreads, 8 / kPWaves) void indexer_prefill_kernel
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
     float v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
     if (FP8) v *= sc;
-    v = r32 < nl[p] - k ? v : neg_inf();
+    v = k < nvis_l[p] ? v : neg_inf();
     const float m = max8_lanes(v);
-    const bool in = r32 < kend - k;            // keys of later chunks belong to other WGs
-    const uint32_t so = in ? sbase + (uint32_t)k * 4u : kDrop;
-    const uint32_t bo = in && bstore ? bbase + (uint32_t)(k >> 3) * 4u : kDrop;
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srs[p], so, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), brs[p], bo, 0, 0);
+    const bool in = k < kend_l;                // keys of later chunks belong to other WGs
+    // a dropped store's vector offset alone is past every extent
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), srs[p], in ? sbase : kDrop, k * 4, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m), brs[p], in ? bbase : kDrop, (k >> 3) * 4, 0);
   };
 
   // One tile: B operands of the next tile are read from LDS while this one's MFMAs run.
