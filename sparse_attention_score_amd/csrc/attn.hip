@@ -26,7 +26,10 @@
 //           P^T with A = V^T built from LDS rows by byte permutes (8 keys x 1 dim per lane),
 //           each value element read from LDS once per step, and B = P^T of each head group.
 // The values of step s and the scores of step s+1 are independent and run in the same
-// loop iteration, with one barrier per step.
+// loop iteration, with one barrier per step. Each wave requests its rows of step s+3 after
+// its MFMAs of the iteration are issued: the operand reads start right at the barrier, and
+// the 32 direct loads of a step, which the CU's load path takes one at a time, queue while
+// the matrix cores work.
 // Small batches spread each query's key list over kMaxSplits work-groups; the last to
 // finish combines their partial results. Mid-size batches (33 to 128 queries) split each
 // query's 64 heads over two work-groups instead, which need no combining: both gather the
@@ -378,7 +381,25 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
         for (int j = 0; j < NJ; ++j)
           acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qb[j][s], acc[j], 0, 0, 0);
       };
-      if constexpr (!KV8) {
+      if constexpr (!KV8 && NJ == 2) {
+        // six operand reads ahead of the MFMAs that use them (the compiler's own order
+        // keeps two in flight)
+        constexpr int kAhead = 6;
+        __builtin_amdgcn_sched_barrier(0);
+        bf16x8 kr[16];
+#pragma unroll
+        for (int s = 0; s < 16; ++s) kr[s] = *reinterpret_cast<const bf16x8*>(krow + (4 * s + g) * 16);
+#pragma unroll
+        for (int s = 0; s < 16; ++s) mma(s, kr[s]);
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);   // LDS reads
+#pragma unroll
+        for (int i = 0; i < 16 - kAhead; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, NJ, 0);     // MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NJ * kAhead, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      } else if constexpr (!KV8) {
 #pragma unroll
         for (int s = 0; s < 16; ++s) mma(s, *reinterpret_cast<const bf16x8*>(krow + (4 * s + g) * 16));
       } else {
@@ -510,8 +531,8 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       for (int step = 0; step < nsteps; ++step) {
         __builtin_amdgcn_s_waitcnt(kWaitNext);   // step s+1's rows (step s+2's in flight)
         __syncthreads();
-        issue(step + kDepth);
         scores_raw(step + 1, acc);               // past the last step: P = 0, never read
+        issue(step + kDepth);                    // (queues while the MFMAs run)
         softmax(step + 1, acc);
       }
       __builtin_amdgcn_s_waitcnt(kWaitAll);   // no row load may outlive the pass (or the LDS)
@@ -674,8 +695,8 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       for (int step = 0; step < nsteps; ++step) {
         __builtin_amdgcn_s_waitcnt(kWaitNext);
         __syncthreads();
-        issue(step + kDepth);
         values(step);
+        issue(step + kDepth);
       }
       __builtin_amdgcn_s_waitcnt(kWaitAll);
       if (pass == 1) break;

@@ -27,14 +27,13 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
-// Round fp32 to bf16 (nearest, ties to even). Inputs here are finite.
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// Two fp32 -> two bf16 (nearest, ties to even; lo in the low half) by one v_cvt_pk_bf16_f32.
+// The kernels run with fp32 denormals kept and round-to-nearest-even, so the conversion is
+// the exact rounding of each value, denormals included. Inputs here are finite.
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_v){lo, hi}, bf16x2_v));
 }
 
 // Four OCP e4m3 codes (one dword) -> four bf16 values in two dwords, codes 0-1 in the
