@@ -529,6 +529,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(NT == 512 ? 
 void select_kernel(SelectArgs a) {
   __shared__ SelShared sh;
   __shared__ __attribute__((aligned(16))) int32_t core[kTopK];
+  // one work-group doing both stages keeps the candidate list in LDS until the end: a
+  // barrier after global stores waits for them to complete (~10 us per query under load)
+  __shared__ __attribute__((aligned(16))) int32_t cand_lds[ROLES == 1 ? kCandBlocks : 4];
   const int role = ROLES == 1 ? -1 : (int)blockIdx.x;
   const int t = ROLES == 1 ? blockIdx.x : blockIdx.y;
   const int64_t n = visible_n(a.m, t);
@@ -546,7 +549,7 @@ void select_kernel(SelectArgs a) {
     load_block_keys<EPT>(a, t, n, I, key);
     if (role == -1 && nb > kCandBlocks) {
       const int ks[2] = {kCandBlocks, kTopK};
-      int32_t* const outs[2] = {cand, core};
+      int32_t* const outs[2] = {cand_lds, core};
       multi_select<NT, EPT, 2>(key, I, ks, outs, sh);
     } else {
       const int ks[1] = {role == 0 ? kCandBlocks : kTopK};
@@ -557,6 +560,9 @@ void select_kernel(SelectArgs a) {
   }
   __syncthreads();
   select_core<NT>(a, t, n, core, sh);
+  if (ROLES == 1 && nb > kCandBlocks)
+    for (int i = 4 * threadIdx.x; i < kCandBlocks; i += 4 * NT)
+      *reinterpret_cast<int4*>(cand + i) = *reinterpret_cast<const int4*>(&cand_lds[i]);
 }
 
 // Two-level S2, first level: work-group (t, p) keeps the best 2048 of blocks
