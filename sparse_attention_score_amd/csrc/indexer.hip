@@ -1071,22 +1071,23 @@ __global__ __launch_bounds__(kPThreads, 8 / kPWaves) void indexer_prefill_kernel
   }
   if (nsteps == 0) return;
 
-  // A operands and head weights of the wave's two query pairs.
+  // A operands and head weights of the wave's two query pairs. Row r of a pair's A operand
+  // is head 4 (r / 8) + r % 4 of the pair's query (r / 4) % 2, so that in the 32x32 result
+  // (lane (r32, hh) holds rows 8 (i / 4) + 4 hh + i % 4, i = 0..15) a lane's 16 values are
+  // heads 0..15 of query hh of the pair for key r32, and each lane finishes its head sum.
   bf16x8 qa[kPairsPerWave][8];
-  float wt[kPairsPerWave][2][8];
+  float wt[kPairsPerWave][16];
 #pragma unroll
   for (int p = 0; p < kPairsPerWave; ++p) {
-    const int jq = 2 * p + (r32 >> 4);
+    const int jq = 2 * p + ((r32 >> 2) & 1);
+    const int head = 4 * (r32 >> 3) + (r32 & 3);
     const int tq = min(q0 + 4 * wave + jq, T - 1);
-    const uint16_t* row = reinterpret_cast<const uint16_t*>(a.q_idx) + ((int64_t)tq * kIdxHeads + (r32 & 15)) * kIdxDim;
+    const uint16_t* row = reinterpret_cast<const uint16_t*>(a.q_idx) + ((int64_t)tq * kIdxHeads + head) * kIdxDim;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qa[p][s] = *reinterpret_cast<const bf16x8*>(row + pdim(hh, s));
+    const int tw = min(q0 + 4 * wave + 2 * p + hh, T - 1);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int tw = min(q0 + 4 * wave + 2 * p + j, T - 1);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) wt[p][j][i] = a.w[(int64_t)tw * kIdxHeads + 8 * (i >> 2) + 4 * hh + (i & 3)];
-    }
+    for (int i = 0; i < 16; ++i) wt[p][i] = a.w[(int64_t)tw * kIdxHeads + i];
   }
 
   // Outputs. After the head sum of pair p, lanes 0-31 hold query 2p's score of key r32 and
@@ -1226,9 +1227,9 @@ __global__ __launch_bounds__(kPThreads, 8 / kPWaves) void indexer_prefill_kernel
     sc = FP8 ? sh.scale[buf][row] : 1.f;
   };
 
-  // Epilogue of pair p for the tile at key k: ReLU and head weights in-lane over the
-  // lane's 8 heads of each query, one 32-lane swap to finish both 16-head sums, key scale,
-  // mask past the query's n, block max over 8 lanes, two stores.
+  // Epilogue of pair p for the tile at key k: ReLU and head weights in-lane over the lane's
+  // 16 heads (heads in order), key scale, mask past the query's n, block max over 8 lanes,
+  // two stores.
   // The tile's key offset goes in the stores' scalar offset; the lane-dependent parts
   // (row, key within the tile, the lanes that store block maxima) are fixed, and the
   // masks compare the tile's first key with per-lane limits computed once.
@@ -1239,17 +1240,9 @@ __global__ __launch_bounds__(kPThreads, 8 / kPWaves) void indexer_prefill_kernel
 #pragma unroll
   for (int p = 0; p < kPairsPerWave; ++p) nvis_l[p] = nl[p] - r32;
   auto epilogue = [&](int p, const f32x16& acc, int k, float sc) {
-    float x = wt[p][0][0] * relu(acc[0]);
-    float y = wt[p][1][0] * relu(acc[8]);
+    float v = wt[p][0] * relu(acc[0]);
 #pragma unroll
-    for (int ii = 1; ii < 8; ++ii) {
-      x = fmaf(wt[p][0][ii], relu(acc[ii]), x);
-      y = fmaf(wt[p][1][ii], relu(acc[8 + ii]), y);
-    }
-    // lanes 32-63 of x trade places with lanes 0-31 of y: the low half then adds its own
-    // and the high half's partial of query 2p, the high half both partials of query 2p+1
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-    float v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    for (int i = 1; i < 16; ++i) v = fmaf(wt[p][i], relu(acc[i]), v);
     if (FP8) v *= sc;
     v = k < nvis_l[p] ? v : neg_inf();
     const float m = max8_lanes(v);
