@@ -551,12 +551,24 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       }
       softmax(0, acc);
       // one barrier per step makes visible the P of step s, the rows of step s+1 and frees
-      // the buffer of step s-1; the value waves weigh step s meanwhile
-      for (int step = 0; step < nsteps; ++step) {
+      // the buffer of step s-1; the value waves weigh step s meanwhile. Steps past the last
+      // are not requested (their tiles' stale rows only meet masked scores): the last
+      // kDepth steps run in a loop of their own without requests (a branch around the
+      // request would split the step's code, which the compiler interleaves), and once no
+      // later step is in flight the wait is for all.
+      int step = 0;
+      for (; step < nsteps - kDepth; ++step) {
         __builtin_amdgcn_s_waitcnt(kWaitNext);   // step s+1's rows (step s+2's in flight)
         __syncthreads();
-        scores_raw(step + 1, acc);               // past the last step: P = 0, never read
+        scores_raw(step + 1, acc);
         issue(step + kDepth);                    // (queues while the MFMAs run)
+        softmax(step + 1, acc);
+      }
+      for (; step < nsteps; ++step) {
+        if (step == 0 || step + 2 < nsteps) __builtin_amdgcn_s_waitcnt(kWaitNext);
+        else __builtin_amdgcn_s_waitcnt(kWaitAll);
+        __syncthreads();
+        scores_raw(step + 1, acc);               // past the last step: P = 0, never read
         softmax(step + 1, acc);
       }
       __builtin_amdgcn_s_waitcnt(kWaitAll);   // no row load may outlive the pass (or the LDS)
@@ -716,11 +728,18 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       __builtin_amdgcn_s_waitcnt(kWaitLater);
       __syncthreads();
       __syncthreads();   // (the score waves' step-0 maxima)
-      for (int step = 0; step < nsteps; ++step) {
+      int step = 0;
+      for (; step < nsteps - kDepth; ++step) {
         __builtin_amdgcn_s_waitcnt(kWaitNext);
         __syncthreads();
         values(step);
         issue(step + kDepth);
+      }
+      for (; step < nsteps; ++step) {
+        if (step == 0 || step + 2 < nsteps) __builtin_amdgcn_s_waitcnt(kWaitNext);
+        else __builtin_amdgcn_s_waitcnt(kWaitAll);
+        __syncthreads();
+        values(step);
       }
       __builtin_amdgcn_s_waitcnt(kWaitAll);
       if (pass == 1) break;
