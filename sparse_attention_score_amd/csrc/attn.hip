@@ -219,10 +219,11 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   }
 
   // Key list order. bf16 rows with one work-group per query (large batches): the window
-  // first, then the selected latents in topk order, so the first steps' rows (window rows
-  // need no selection) are requested before the selection has arrived (prefill chunk 494 ->
-  // 484 us). Otherwise the latents first: smaller batches measured 1-4 % slower with the
-  // window first, and code rows' format switch and scale loads assume latents first.
+  // first, then the selected latents in topk order; the first steps then gather window
+  // rows, which neighbouring queries share and the L2 mostly holds, so the pipeline fills
+  // sooner (prefill chunk 475 -> 456 us). Otherwise the latents first: smaller batches
+  // measured 1-4 % slower with the window first, and code rows' format switch and scale
+  // loads assume latents first.
   const bool wf = !KV8 && HS == 1 && S == 1;
   const int u0 = p - kWindow + 1 > 0 ? p - kWindow + 1 : 0;
   const int nwin = valid_q ? p - u0 + 1 : 0;
@@ -234,40 +235,13 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
                                              (int64_t)seq * a.window_seq_stride * (KV8 ? 1 : 2) + wr * WRB);
   };
 
-  // ---- tile loader: wave w moves rows 4w..4w+3 of a step, slots kb_ + min(32 step + r,
-  // last). Rows past the key list repeat the last real row (finite data; their scores are
-  // masked), so every wave issues exactly kRowsPerWave loads per step and the wait counts
-  // are constants.
-  const uint32_t tile0 = (uint32_t)(uintptr_t)&sh.tile[0][0];
-  int m = 0, nlat = 0;   // keys; code rows: the first nlat of them are latents
-  auto issue_at = [&](int step, int kb_, int last) {
-    const uint32_t base = tile0 + (uint32_t)((step % kBufs) * (kKT * kRow) + wave * kRowsPerWave * kRow);
-    const uint16_t* r[kRowsPerWave];
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) r[i] = sh.rows[kb_ + min(step * kKT + wave * kRowsPerWave + i, last)];
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-      const int idx = kb_ + min(step * kKT + wave * kRowsPerWave + i, last);
-      if (FP4L && idx < nlat) {   // 256 code bytes (lanes 0-15) and 16 scale bytes (lane 16)
-        const uint8_t* src = lane < 16 ? reinterpret_cast<const uint8_t*>(r[i]) + 16 * lane
-                                       : reinterpret_cast<const uint8_t*>(sh.sptr[idx]);
-        if (lane <= 16) to_lds16(src, base + i * kRow);
-      } else if constexpr (KV8) {
-        row8_to_lds(r[i], base + i * kRow, lane);
-      } else {
-        row_to_lds(r[i], base + i * kRow, lane);
-      }
-    }
-  };
-
   // ---- the selection (2 KB) and the query (64 KB) by direct loads: the selection into its
   // own LDS array, the query's 64 heads into tiles 2 and 3 (one padded row per head) until
-  // step 2's rows replace it; then, window first, the rows of the steps that hold only
-  // window rows (at most two: tiles 0 and 1). Every load the kernel makes
-  // before its output is one of these, so all waits are explicit vmcnt counts. ----
+  // step 2's rows replace it. Every load the kernel makes before its output is one of these,
+  // so all waits are explicit vmcnt counts. ----
+  const uint32_t tile0 = (uint32_t)(uintptr_t)&sh.tile[0][0];
   const uint32_t qlds = tile0 + (uint32_t)(2 * kKT * kRow);
   static_assert(kBufs >= 4 && kHeads <= 2 * kKT, "the query needs two tiles");
-  const int early = wf ? min(2, nwin / kKT) : 0;   // uniform: steps requested early
   if (valid_q) {
     if (wave < 2) {   // 256 entries per wave
       const int32_t* src = a.topk + (int64_t)t * kTopK + 256 * wave + 4 * lane;
@@ -279,20 +253,12 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
       const int head = (kHeads / HS) * hs + kQPW * wave + i;
       to_lds16(qt + head * kDim + 8 * lane, qlds + head * kRow);
     }
-    if (wf && tid < nwin) sh.rows[tid] = window_row(tid);
-  }
-  if (early > 0) {
-    __syncthreads();   // the window's row pointers
-    for (int e = 0; e < early; ++e) issue_at(e, 0, nwin - 1);
-  }
-  if (valid_q) {
-    if (early == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kQPW + 2 * kRowsPerWave));   // the selection
-    else if (early == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kQPW + kRowsPerWave));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kQPW));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kQPW));   // the selection (query loads in flight)
   }
   __syncthreads();
 
   // ---- key list ----
+  int m = 0, nlat = 0;   // keys; code rows: the first nlat of them are latents
   if (valid_q) {
     const int32_t j = sh.topk[tid];   // kAThreads == kTopK
     const bool v = j >= 0 && j < n;
@@ -327,9 +293,10 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
         sh.sptr[before + incl - 1] = reinterpret_cast<const float*>(a.latent_scales) + sidx;
       }
     }
-    if (!wf && tid < nwin) {
-      sh.rows[nsel + tid] = window_row(tid);
-      if (KV8) sh.sptr[nsel + tid] = a.window_scales + (int64_t)seq * a.window_scales_seq_stride + (u0 + tid) % a.window_cap;
+    if (tid < nwin) {
+      const int ws = wf ? tid : nsel + tid;   // the window's slot
+      sh.rows[ws] = window_row(tid);
+      if (KV8) sh.sptr[ws] = a.window_scales + (int64_t)seq * a.window_scales_seq_stride + (u0 + tid) % a.window_cap;
     }
     m = nsel + nwin;
     nlat = nsel;
@@ -351,7 +318,28 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   const int kb = st0 * kKT;
   const int mk = min(m, st1 * kKT) - kb;   // 0 for a split without a step
 
-  auto issue = [&](int step) { issue_at(step, kb, mk - 1); };
+  // ---- tile loader: wave w moves rows 4w..4w+3 of a step. Rows past the key list repeat
+  // the last real row (finite data; their scores are masked), so every wave issues exactly
+  // kRowsPerWave loads per step and the wait counts are constants.
+  auto issue = [&](int step) {
+    const uint32_t base = tile0 + (uint32_t)((step % kBufs) * (kKT * kRow) + wave * kRowsPerWave * kRow);
+    const uint16_t* r[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) r[i] = sh.rows[kb + min(step * kKT + wave * kRowsPerWave + i, mk - 1)];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int idx = kb + min(step * kKT + wave * kRowsPerWave + i, mk - 1);
+      if (FP4L && idx < nlat) {   // 256 code bytes (lanes 0-15) and 16 scale bytes (lane 16)
+        const uint8_t* src = lane < 16 ? reinterpret_cast<const uint8_t*>(r[i]) + 16 * lane
+                                       : reinterpret_cast<const uint8_t*>(sh.sptr[idx]);
+        if (lane <= 16) to_lds16(src, base + i * kRow);
+      } else if constexpr (KV8) {
+        row8_to_lds(r[i], base + i * kRow, lane);
+      } else {
+        row_to_lds(r[i], base + i * kRow, lane);
+      }
+    }
+  };
   // code rows: the slots' scales by direct loads, issued before the first rows so the
   // rows' waits cover them
   if constexpr (KV8) {
@@ -364,7 +352,8 @@ __global__ __launch_bounds__(kAThreads, 1) void attn_kernel(AttnArgs a) {
   // ---- score waves: query heads 16(2hp + j) + c as B operands (k-step s: dims
   // (4s+g)*8 .. +8), from LDS; steps 0 and 1 are already on their way meanwhile ----
   if (mk > 0) {
-    for (int e = early; e < 2; ++e) issue(e);
+    issue(0);
+    issue(1);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kRowsPerWave));   // the query (steps 0, 1 in flight)
   } else {
     __builtin_amdgcn_s_waitcnt(kWaitAll);
