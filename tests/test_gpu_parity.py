@@ -248,6 +248,14 @@ def test_prefill_small_ratio1():
     _e2e(wl)
 
 
+def test_prefill_from_position_zero():
+    # more than 128 queries (one work-group per query, window first in the key list) from
+    # raw position 0: short windows (fewer than one step of rows for the first 31 queries),
+    # key lists of one step, every visible latent selected, then the full window
+    _e2e(W.make_prefill(T=300, offset=0, ratio=1, key_dtype="bf16", name="prefill-from-zero", seed=19))
+    _e2e(W.make_prefill(T=160, offset=5, ratio=2, key_dtype="bf16", name="prefill-from-five-r2", seed=21))
+
+
 def test_prefill_prunes_ratio1():
     wl = W.make_prefill(T=40, offset=20000, ratio=1, key_dtype="bf16", name="prefill-prune", seed=12)
     _e2e(wl)
