@@ -197,6 +197,37 @@ def test_attention_late_dominant_keys():
         assert np.abs(lse1[t] - res2.lse[t]).max() <= LSE_TOL * 10
 
 
+def test_attention_large_batch_redo_and_invalid():
+    """A batch of 600 short-context queries (one work-group per query, window rows first in
+    the key list; key lists of 1 to 20 steps): every 7th has two heads dominated by its window
+    rows (the redo pass), and every 50th is invalid (raw position -1: zero output, lse =
+    -inf, between valid ones)."""
+    rng = np.random.default_rng(83)
+    B = 600
+    n_raw = [int(x) for x in rng.integers(3, 1500, size=B)]
+    wl = W.make_decode(B=B, n_raw=n_raw, ratio=2, key_dtype="bf16", name="large-batch",
+                       with_compress=False, seed=83)
+    dom = np.arange(0, B, 7)
+    wl.R[dom] = O.f64_to_bf16(0.5 + 0.25 * rng.standard_normal(wl.R[dom].shape))
+    for h in (5, 37):
+        wl.q[dom, h, :] = O.f64_to_bf16(np.full((len(dom), wl.q.shape[2]), 8.0))
+    bad = np.arange(3, B, 50)
+    wl.pos[bad] = -1
+    d = _run(wl)
+    good = [t for t in range(B) if t not in set(bad.tolist())]
+    topk = d.topk.cpu().numpy()
+    res = O.run(wl, queries=good, idx_override={t: topk[t][topk[t] >= 0] for t in good})
+    o = bf16_dev_to_f64(d.out)
+    lse = d.lse.cpu().numpy()
+    for t in good:
+        check_outputs(o[t], res.o[t], f"large batch t={t}")
+        assert np.abs(lse[t] - res.lse[t]).max() <= LSE_TOL * 10, f"t={t} lse"
+    for t in bad:
+        assert np.all(o[t] == 0) and np.all(np.isneginf(lse[t])), f"invalid query {t}"
+    dd = o[dom][:, [5, 37], :]
+    assert np.all(dd > -0.5) and np.all(dd < 1.5), "dominated heads must be the window rows' mixture"
+
+
 def test_attention_key_splits_match_one_group_per_query():
     """A small batch spreads each query's key list over several work-groups and the last
     to finish combines their partial softmax results: the same output as one work-group per
