@@ -327,15 +327,38 @@ def test_select_exact_on_given_scores_with_ties():
             assert np.array_equal(cand[t][cand[t] >= 0], c_ref), t
 
 
-@pytest.mark.parametrize("T,n_lo,n_hi", [(1040, 16500, 24000), (6, 66000, 140000)])
+@pytest.mark.parametrize("T,n_lo,n_hi", [(1040, 16500, 24000), (6, 66000, 140000), (520, 66000, 70000)])
 def test_select_many_queries_and_long_rows(T, n_lo, n_hi):
     """Selection alone on given fp32 scores with ties: 1040 queries (the small-work-group
     kernels used for large batches) and rows past 65536 positions (the two-level candidate
-    stage), against the oracle's selection on the same values; exact integer results."""
-    from sparse_attention_score_amd import Plan, Queries, select_topk
+    stage, with few and with many queries), against the oracle's selection on the same
+    values; exact integer results."""
     rng = np.random.default_rng(23 + T)
     n = rng.integers(n_lo, n_hi, T)
     n[0] = n_hi   # one row at the maximum
+    _select_given_scores(n, rng, levels=200)
+
+
+@pytest.mark.parametrize("rows,levels", [
+    # parts of 8192 blocks: a last part of 13 blocks (100 positions, all kept), of 300 blocks
+    # (2400 positions, every block a core block), of 500 blocks, and a long row
+    ([65636, 67936, 135072, 300000], 200),
+    # parts of 16384 blocks (rows past 65536 blocks): a last part of 2 blocks, the longest rows
+    ([524304, 700000, 1 << 20], 200),
+    # every score equal: the lowest positions and blocks win in every part and overall
+    ([70000, 200000], 1),
+])
+def test_select_two_level_edges(rows, levels):
+    """The two-level selection's part boundaries: parts whose visible positions are at most
+    512, parts of at most 512 blocks, 16384-block parts, and all-equal scores; exact against
+    the oracle's selection on the same fp32 values."""
+    rng = np.random.default_rng(len(rows) + levels)
+    _select_given_scores(np.array(rows, np.int64), rng, levels=levels, every=True)
+
+
+def _select_given_scores(n, rng, levels, every=False):
+    from sparse_attention_score_amd import Plan, Queries, select_topk
+    T = len(n)
     E = int(-(-n.max() // 8) * 8)
     plan = Plan(ratio=1, max_queries=T, max_compressed=int(n.max()))
     seq = torch.zeros(T, dtype=torch.int32, device="cuda")
@@ -343,7 +366,7 @@ def test_select_many_queries_and_long_rows(T, n_lo, n_hi):
     qs = Queries(seq, pos, int(n.max()))
     S = np.full((T, E), -np.inf, np.float32)
     for t in range(T):
-        S[t, :n[t]] = rng.integers(0, 200, n[t]).astype(np.float32) * np.float32(0.5)
+        S[t, :n[t]] = rng.integers(0, levels, n[t]).astype(np.float32) * np.float32(0.5)
     scores = torch.from_numpy(S).cuda()
     bm_np = np.full((T, (E // 8 + 3) // 4 * 4), -np.inf, np.float32)
     for t in range(T):
@@ -360,7 +383,7 @@ def test_select_many_queries_and_long_rows(T, n_lo, n_hi):
         select_topk(plan, qs, scores, block_max if use_bm else None, topk, cand=cand, workspace=ws)
         torch.cuda.synchronize()
         tk, cd = topk.cpu().numpy(), cand.cpu().numpy()
-        for t in range(0, T, max(1, T // 40)):
+        for t in range(0, T, 1 if every else max(1, T // 40)):
             c_ref, i_ref = O.select(S[t, :n[t]].astype(np.float64))
             assert np.array_equal(tk[t][tk[t] >= 0], i_ref), (use_bm, t)
             assert np.array_equal(cd[t][cd[t] >= 0], c_ref), (use_bm, t)
