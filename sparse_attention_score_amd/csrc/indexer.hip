@@ -8,8 +8,8 @@
 //
 // Block maxima (blocks of 8 positions) are taken in registers with DPP.
 //
-// Decode (every query has its own key stream, HBM-bound): each wave streams 16 tiles of 16
-// keys from HBM straight into its own LDS ring (kDepth tiles in flight, no registers held;
+// Decode (every query has its own key stream, HBM-bound): each wave streams 32 KB of keys
+// (16 e4m3 or 8 bf16 tiles of 16 keys) from HBM straight into its own LDS ring (kDepth tiles in flight, no registers held;
 // every load instruction moves 1 KB of whole rows). v_mfma_f32_16x16x32_bf16 then takes the
 // 16 heads of the query as rows (A, in registers) and the tile's 16 keys as columns (B, from
 // LDS). In the 16x16 result each lane holds heads 4g..4g+3 (g = lane/16) of key lane%16:
@@ -46,16 +46,12 @@ __device__ __forceinline__ int query_n(const IndexerArgs& a, int t) {
 // ======================================================================================
 // Decode
 // ======================================================================================
-#ifndef SA_IDX_TPW
-#define SA_IDX_TPW 16
-#endif
 #ifndef SA_IDX_DEPTH
 #define SA_IDX_DEPTH 8
 #endif
 constexpr int kDWaves = 4;
 constexpr int kDThreads = 64 * kDWaves;
-constexpr int kTilesPerWave = SA_IDX_TPW;
-constexpr int kKeysPerWG = kDWaves * kTilesPerWave * 16;
+constexpr int kTilesPerWave = 16;                  // most tiles of one wave (e4m3 keys)
 constexpr int kRingBytes = SA_IDX_DEPTH * 16 * kIdxDim;   // per wave: kDepth e4m3 tiles
 
 // Decode key tiles (16 keys) travel HBM -> LDS by direct loads (no registers): each load
@@ -167,12 +163,22 @@ __device__ __forceinline__ bool run_compress_rows(const IndexerArgs& a) {
 // multiple of 16 positions), whose id each wave reads from the block table up front.
 enum DecodeMode { kPlain = 0, kCand = 1, kPaged = 2 };
 
+// Tiles per wave: the same 32 KB of key rows per wave in either format (16 e4m3 tiles or 8
+// bf16 tiles). Fewer, longer waves measured slower with e4m3 keys (8 or 32 tiles: 202-226
+// against 180 us on 128 queries at 64K keys); with bf16 keys 8 tiles beat 16 (64 queries at
+// 16K keys 45.7 -> 44.4 us, 4 queries at 1K keys 10.4 -> 9.0 us). Candidate mode keeps 16
+// (a wave's two block ids per tile fill its 32 lanes).
+template <bool FP8, int MODE>
+constexpr int decode_tpw() { return FP8 || MODE == kCand ? kTilesPerWave : kTilesPerWave / 2; }
+
 template <bool FP8, int MODE>
 __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a) {
   if (run_compress_rows(a)) return;
   constexpr bool CAND = MODE == kCand, PAGED = MODE == kPaged;
   using DT = DecodeTile<FP8>;
   constexpr int RB = DT::RB, TB = DT::TB, NK = DT::NK, D = DT::D;
+  constexpr int TPW = decode_tpw<FP8, MODE>();
+  static_assert(TPW % 4 == 0 && TPW <= kTilesPerWave, "whole 64-key stores; shared arrays sized for the most");
   static_assert((D & (D - 1)) == 0 && D >= 2, "ring depth must be a power of two");
   static_assert(D * NK <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) DecodeShared sh;
@@ -180,16 +186,16 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int c = lane & 15, g = lane >> 4;
   const int E = (int)a.E;
-  const int chunk0 = blockIdx.x * kKeysPerWG;
-  const int key0 = chunk0 + wave * kTilesPerWave * 16;   // the keys this wave stores
+  const int chunk0 = blockIdx.x * (kDWaves * TPW * 16);
+  const int key0 = chunk0 + wave * TPW * 16;   // the keys this wave stores
   const int n = query_n(a, t);
-  const int ntiles = key0 < E ? min(kTilesPerWave, (E - key0 + 15) >> 4) : 0;
+  const int ntiles = key0 < E ? min(TPW, (E - key0 + 15) >> 4) : 0;
   // tiles of the group's chunk below n, and this wave's share of them (candidate mode:
   // decided once the block ids are in)
   const int chunk_live = CAND ? (n > 0 ? 1 : 0)
-                              : (chunk0 < n ? min(kDWaves * kTilesPerWave, (n - chunk0 + 15) >> 4) : 0);
-  int live = CAND ? 0 : min(max(chunk_live - wave * kTilesPerWave, 0), kTilesPerWave);
-  auto tile_of = [&](int i) { return wave * kTilesPerWave + i; };
+                              : (chunk0 < n ? min(kDWaves * TPW, (n - chunk0 + 15) >> 4) : 0);
+  int live = CAND ? 0 : min(max(chunk_live - wave * TPW, 0), TPW);
+  auto tile_of = [&](int i) { return wave * TPW + i; };
   const bool wg_live = chunk_live > 0;
 
   float* srow = a.scores + (int64_t)t * a.ld_scores;
@@ -200,11 +206,11 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
 
   // e4m3 row scales of the keys this lane stores at the end (issued first: the loads
   // complete in order, so the row waits below also cover them)
-  float scv[kTilesPerWave / 4] = {};
+  float scv[TPW / 4] = {};
   if (FP8 && MODE == kPlain && key0 < n) {   // (a query without keys may have no valid sequence)
     const float* scales = a.scales + (int64_t)seq * a.scales_seq_stride;
 #pragma unroll
-    for (int j = 0; j < kTilesPerWave / 4; ++j) scv[j] = scales[min(key0 + 64 * j + lane, n - 1)];
+    for (int j = 0; j < TPW / 4; ++j) scv[j] = scales[min(key0 + 64 * j + lane, n - 1)];
   }
   // paged mode: page id of the wave's tile `lane` (lanes past the last tile take its page),
   // read before any tile load since the tile addresses depend on it. The wave's tiles span
@@ -216,13 +222,13 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
       const int32_t* trow = a.pages.table + (int64_t)seq * a.pages.stride;
       const int lp = a.pages.log2_page;
       const int e0 = key0 >> lp, elast = (n - 1) >> lp;
-      int ent[kTilesPerWave];
+      int ent[TPW];
 #pragma unroll
-      for (int j = 0; j < kTilesPerWave; ++j) ent[j] = trow[min(e0 + j, elast)];
-      const int mine = ((key0 + 16 * min(lane, kTilesPerWave - 1)) >> lp) - e0;   // 0 .. 15
+      for (int j = 0; j < TPW; ++j) ent[j] = trow[min(e0 + j, elast)];
+      const int mine = ((key0 + 16 * min(lane, TPW - 1)) >> lp) - e0;   // 0 .. 15
       int v = ent[0];
 #pragma unroll
-      for (int j = 1; j < kTilesPerWave; ++j) v = mine == j ? ent[j] : v;
+      for (int j = 1; j < TPW; ++j) v = mine == j ? ent[j] : v;
       pgreg = (int)min(max((int64_t)v, (int64_t)0), a.pages.num_pages - 1);
     }
   }
@@ -234,7 +240,7 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
     const uint8_t* qb = reinterpret_cast<const uint8_t*>(a.q_idx) + (int64_t)t * kIdxHeads * kIdxDim * 2;
     to_lds16(qb + 1024 * wave + 16 * lane, lds_q + 1024 * wave);
     if (wave == 0 && lane < kIdxHeads / 4) to_lds16(a.w + (int64_t)t * kIdxHeads + 4 * lane, lds_w);
-    if (CAND && wave == 1 && lane < kDWaves * kTilesPerWave * 2 / 4)   // the group's block ids
+    if (CAND && wave == 1 && lane < kDWaves * TPW * 2 / 4)   // the group's block ids
       to_lds16(a.cand + (int64_t)t * kCandBlocks + chunk0 / 8 + 4 * lane, (uint32_t)(uintptr_t)&sh.ids[0]);
   }
   // paged mode: the e4m3 scales, each lane's key in the page of its tile
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
       if constexpr (FP8) {
         const float* scales = a.scales;
 #pragma unroll
-        for (int j = 0; j < kTilesPerWave / 4; ++j) {
+        for (int j = 0; j < TPW / 4; ++j) {
           const int x = min(key0 + 64 * j + lane, n - 1);
           const int pg = __shfl(pgreg, (x - key0) >> 4);
           scv[j] = scales[pool_row(a.pages, pg, x)];
@@ -255,8 +261,8 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
   // slot is valid when its block holds a visible position (0 <= id < ceil(n / 8), compared
   // without forming 8 id); the wave loads tiles up to its last valid slot, and invalid
   // slots among them read row n - 1 and are masked.
-  static_assert(2 * kTilesPerWave <= 64, "one slot per lane");
-  constexpr int kSlots = 2 * kTilesPerWave;   // candidate blocks per wave
+  static_assert(2 * TPW <= 64, "one slot per lane");
+  constexpr int kSlots = 2 * TPW;   // candidate blocks per wave
   const int nbv = (n + 7) >> 3;
   auto valid_id = [&](int id) { return id >= 0 && id < nbv; };
   int idreg = -1;
@@ -269,7 +275,7 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
     if (FP8 && live > 0) {
       const float* scales = a.scales + (int64_t)seq * a.scales_seq_stride;
 #pragma unroll
-      for (int j = 0; j < kTilesPerWave / 4; ++j) {
+      for (int j = 0; j < TPW / 4; ++j) {
         const int id = sh.ids[kSlots * wave + 8 * j + (lane >> 3)];
         scv[j] = valid_id(id) ? scales[min(8 * id + (lane & 7), n - 1)] : 0.f;
       }
@@ -337,7 +343,7 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
       const int q = FP8 ? g + 4 * i : 4 * i + g;
       roff[i] = (uint32_t)(c * RB + DT::pos(c, q) * 16);
     }
-    float* stage = &sh.stage[0][0];
+    float* stage = sh.stage[wave];   // row stride: the most tiles of a wave
     for (int i = 0; i < live; ++i) {
       if (i + D - 1 < live) __builtin_amdgcn_s_waitcnt(waitcnt_vm((D - 1) * NK));   // tile i landed
       else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -352,14 +358,14 @@ __global__ __launch_bounds__(kDThreads) void indexer_decode_kernel(IndexerArgs a
       v = fmaf(wq[2], relu(acc[2]), v);
       v = fmaf(wq[3], relu(acc[3]), v);
       v = add_xor32(add_xor16(v));
-      if (lane < 16) stage[16 * tile_of(i) + lane] = v;
+      if (lane < 16) stage[16 * i + lane] = v;
     }
   }
 
   // ---- scores and block maxima of the wave's keys: 64 consecutive keys per store ----
   const float* stage = sh.stage[wave];
 #pragma unroll
-  for (int j = 0; j < kTilesPerWave / 4; ++j) {
+  for (int j = 0; j < TPW / 4; ++j) {
     const int k = key0 + 64 * j + lane;
     if (64 * j >= 16 * ntiles) break;
     float v = neg_inf();
@@ -1392,7 +1398,9 @@ hipError_t launch_indexer(const IndexerArgs& a, bool prefill, hipStream_t stream
     else if (b.group <= 6) launch_group<6>(b, stream);
     else launch_group<8>(b, stream);
   } else if (!prefill) {
-    const dim3 grid = with_job_rows(dim3((unsigned)((b.E + kKeysPerWG - 1) / kKeysPerWG), (unsigned)b.T), b);
+    const int kpw = kDWaves * 16 * (b.cand ? decode_tpw<true, kCand>()
+                                           : b.fp8 ? decode_tpw<true, kPlain>() : decode_tpw<false, kPlain>());
+    const dim3 grid = with_job_rows(dim3((unsigned)((b.E + kpw - 1) / kpw), (unsigned)b.T), b);
     if (b.cand) {
       if (b.fp8)
         hipLaunchKernelGGL((indexer_decode_kernel<true, kCand>), grid, dim3(kDThreads), 0, stream, b);
