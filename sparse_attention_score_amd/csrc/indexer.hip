@@ -9,19 +9,20 @@
 // Block maxima (blocks of 8 positions) are taken in registers with DPP.
 //
 // Decode (every query has its own key stream, HBM-bound): each wave streams 32 KB of keys
-// (16 e4m3 or 8 bf16 tiles of 16 keys) from HBM straight into its own LDS ring (kDepth tiles in flight, no registers held;
-// every load instruction moves 1 KB of whole rows). v_mfma_f32_16x16x32_bf16 then takes the
-// 16 heads of the query as rows (A, in registers) and the tile's 16 keys as columns (B, from
-// LDS). In the 16x16 result each lane holds heads 4g..4g+3 (g = lane/16) of key lane%16:
-// ReLU and head weights in-lane, then two row-swap adds finish the 16-head sum. The k order
-// inside an MFMA is free (A and B use the same one). Scores are staged in LDS and written
-// at the end with their row scales and block maxima, 64 consecutive keys per store.
+// (16 e4m3 or 8 bf16 tiles of 16 keys) from HBM straight into its own LDS ring (kDepth
+// tiles in flight, no registers held; every load instruction moves 1 KB of whole rows).
+// v_mfma_f32_16x16x32_bf16 then takes the 16 heads of the query as rows (A, in registers)
+// and the tile's 16 keys as columns (B, from LDS). In the 16x16 result each lane holds
+// heads 4g..4g+3 (g = lane/16) of key lane%16: ReLU and head weights in-lane, then two
+// row-swap adds finish the 16-head sum. The k order inside an MFMA is free (A and B use the
+// same one). Scores are staged in LDS and written at the end with their row scales and
+// block maxima, 64 consecutive keys per store.
 //
 // Prefill (a chunk of queries shares one key stream, MFMA-bound): v_mfma_f32_32x32x16_bf16
 // with two queries x 16 heads as rows and 32 keys as columns. Key tiles are staged once per
 // work-group in padded LDS rows (prefetched two tiles ahead through registers) and read by
-// every wave; each wave holds two query pairs. A lane's 16 results are 8 heads of each of
-// the two queries for one key, so the head sum is in-lane plus one 32-lane swap.
+// every wave; each wave holds two query pairs. The A rows are ordered so that a lane's 16
+// results are the 16 heads of one query for one key: the head sum finishes in-lane.
 #include "sa_compress.h"
 #include "sa_device.h"
 #include "sa_launch.h"
