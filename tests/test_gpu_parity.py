@@ -110,10 +110,11 @@ def test_mxfp4_keys_in_a_prefill_chunk_and_a_group():
                           name="mq-mxfp4", seed=19), check_scores=True)
 
 
-@pytest.mark.parametrize("B,n_raw", [(6, [40006, 3001, 2, 130, 1031, 9000]), (40, 5000)])
+@pytest.mark.parametrize("B,n_raw", [(6, [40006, 3001, 2, 130, 1031, 9000]), (40, 5000), (20, 3000)])
 def test_fp8_latents_and_window(B, n_raw):
-    # e4m3 latent and window rows with fp32 row scales: 6 queries (key splits), 40 queries
-    # (two head sets), pruning and tiny contexts
+    # e4m3 latent and window rows with fp32 row scales: 6 queries (key splits, two head
+    # sets), 20 queries (key splits, one head set), 40 queries (two head sets), pruning and
+    # tiny contexts
     wl = W.make_decode(B=B, n_raw=n_raw, ratio=2, key_dtype="fp8", kv_dtype="fp8",
                        name=f"fp8kv-{B}", seed=41)
     _e2e(wl)
@@ -264,6 +265,18 @@ def test_attention_key_splits_match_one_group_per_query():
             assert np.abs(l_s[t] - res.lse[t]).max() <= LSE_TOL
 
 
+@pytest.mark.parametrize("B", [17, 32])
+def test_attention_key_splits_one_head_set(B):
+    """17 to 32 queries: each key list is spread over four work-groups that hold all 64
+    heads (one head set); the last to finish combines the four partials of every head."""
+    rng = np.random.default_rng(85 + B)
+    n_raw = [int(x) for x in rng.integers(3, 6000, size=B)]
+    n_raw[0] = 2   # a one-key list beside longer ones
+    wl = W.make_decode(B=B, n_raw=n_raw, ratio=2, key_dtype="bf16", name=f"splits-{B}",
+                       with_compress=False, seed=85 + B)
+    _e2e(wl)
+
+
 def test_attention_head_sets():
     """33 to 128 queries: each query's heads are split over two work-groups (32 heads each).
     Ragged contexts, both key dtypes' paths share this kernel; bf16 keys here."""
@@ -327,12 +340,14 @@ def test_select_exact_on_given_scores_with_ties():
             assert np.array_equal(cand[t][cand[t] >= 0], c_ref), t
 
 
-@pytest.mark.parametrize("T,n_lo,n_hi", [(1040, 16500, 24000), (6, 66000, 140000), (520, 66000, 70000)])
+@pytest.mark.parametrize("T,n_lo,n_hi", [(1040, 16500, 24000), (300, 16500, 60000), (6, 66000, 140000),
+                                         (520, 66000, 70000)])
 def test_select_many_queries_and_long_rows(T, n_lo, n_hi):
     """Selection alone on given fp32 scores with ties: 1040 queries (the small-work-group
-    kernels used for large batches) and rows past 65536 positions (the two-level candidate
-    stage, with few and with many queries), against the oracle's selection on the same
-    values; exact integer results."""
+    kernels used for large batches), 300 queries (one large work-group per query doing both
+    stages), and rows past 65536 positions (the two-level candidate stage, with few and with
+    many queries), against the oracle's selection on the same values; exact integer
+    results."""
     rng = np.random.default_rng(23 + T)
     n = rng.integers(n_lo, n_hi, T)
     n[0] = n_hi   # one row at the maximum
